@@ -1,0 +1,166 @@
+"""ctypes wrapper over the plain C oracle (oracle.c).
+
+TEST INFRASTRUCTURE ONLY: imported by the tests, by the smoke check and by the
+benchmark's CPU-baseline leg, never by the product library. Argument
+marshalling only; every computation happens in oracle.c.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_SO = os.path.join(_HERE, "liboracle.so")
+
+MISS, EXACT, CONTAINED, INVALID = 0, 1, 2, 3
+OK, EINVAL, ERANGE, ENOSPC = 0, 1, 2, 3
+
+
+def build() -> str:
+    """Compile liboracle.so with the host C compiler (single-threaded, -O2)."""
+    cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-Wall", "-Wextra",
+           "-o", _SO, _SRC]
+    subprocess.run(cmd, check=True)
+    return _SO
+
+
+_lib_handle = None
+_u64p = ctypes.POINTER(ctypes.c_uint64)
+_u32p = ctypes.POINTER(ctypes.c_uint32)
+_i32p = ctypes.POINTER(ctypes.c_int32)
+_u8p = ctypes.POINTER(ctypes.c_uint8)
+
+
+def _lib():
+    global _lib_handle
+    if _lib_handle is None:
+        if not os.path.exists(_SO):
+            build()
+        lib = ctypes.CDLL(_SO)
+        u64, u32 = ctypes.c_uint64, ctypes.c_uint32
+        lib.orc_mr_lookup.argtypes = [_u64p, _u64p, _u32p, u64, ctypes.c_uint,
+                                      _u64p, _u64p, u64, u64,
+                                      _i32p, _u32p, _u8p, _u64p, _u64p]
+        lib.orc_mr_lookup.restype = None
+        lib.orc_build_prp.argtypes = [_u64p, u64, _u64p, _u64p, u64, u64, _u64p, u64,
+                                      _u64p, _u64p, _u8p, _u64p]
+        lib.orc_build_prp.restype = None
+        lib.orc_partition.argtypes = [_u32p, u64, u32, _u32p, _u64p, _u64p]
+        lib.orc_partition.restype = None
+        lib.orc_reg_create.argtypes = [ctypes.c_uint]
+        lib.orc_reg_create.restype = ctypes.c_void_p
+        lib.orc_reg_destroy.argtypes = [ctypes.c_void_p]
+        lib.orc_reg_destroy.restype = None
+        lib.orc_reg_register.argtypes = [ctypes.c_void_p, u64, u64]
+        lib.orc_reg_register.restype = u64
+        lib.orc_reg_deregister.argtypes = [ctypes.c_void_p, u64]
+        lib.orc_reg_deregister.restype = ctypes.c_int
+        lib.orc_reg_refs.argtypes = [ctypes.c_void_p, u64]
+        lib.orc_reg_refs.restype = ctypes.c_int64
+        lib.orc_reg_count.argtypes = [ctypes.c_void_p]
+        lib.orc_reg_count.restype = u64
+        lib.orc_reg_capacity.argtypes = [ctypes.c_void_p]
+        lib.orc_reg_capacity.restype = u64
+        lib.orc_reg_export.argtypes = [ctypes.c_void_p, _u64p, _u64p, _u64p, u64]
+        lib.orc_reg_export.restype = u64
+        _lib_handle = lib
+    return _lib_handle
+
+
+def _p(a, t):
+    if a is None:
+        return ctypes.cast(None, t)
+    assert a.flags["C_CONTIGUOUS"]
+    return a.ctypes.data_as(t)
+
+
+def _u64(a):
+    return np.ascontiguousarray(a, dtype=np.uint64)
+
+
+def _u32(a):
+    return np.ascontiguousarray(a, dtype=np.uint32)
+
+
+def mr_lookup(start, end, lkey, off, length, va_base=0, page_shift=12):
+    start, end, off, length = _u64(start), _u64(end), _u64(off), _u64(length)
+    lkey = _u32(lkey)
+    n = off.shape[0]
+    out = dict(handle=np.empty(n, np.int32), lkey=np.empty(n, np.uint32),
+               kind=np.empty(n, np.uint8), rbase=np.empty(n, np.uint64),
+               rend=np.empty(n, np.uint64))
+    _lib().orc_mr_lookup(_p(start, _u64p), _p(end, _u64p), _p(lkey, _u32p),
+                         start.shape[0], page_shift, _p(off, _u64p), _p(length, _u64p),
+                         n, va_base, _p(out["handle"], _i32p), _p(out["lkey"], _u32p),
+                         _p(out["kind"], _u8p), _p(out["rbase"], _u64p),
+                         _p(out["rend"], _u64p))
+    return out
+
+
+def build_prp(lut, off, length, list_bus_base, pool_pages, pool=None):
+    """Runs O2. `pool` is None (lists not written), True (allocate a zeroed
+    u64[pool_pages][512]) or a caller-owned u64 array of that shape."""
+    lut, off, length = _u64(lut), _u64(off), _u64(length)
+    n = off.shape[0]
+    if pool is True:
+        pool = np.zeros((pool_pages, 512), dtype=np.uint64)
+    if pool is not None:
+        assert pool.dtype == np.uint64 and pool.size >= pool_pages * 512
+    out = dict(prp1=np.empty(n, np.uint64), prp2=np.empty(n, np.uint64),
+               status=np.empty(n, np.uint8))
+    total = np.zeros(1, np.uint64)
+    _lib().orc_build_prp(_p(lut, _u64p), lut.shape[0], _p(off, _u64p), _p(length, _u64p),
+                         n, list_bus_base, _p(pool, _u64p), pool_pages,
+                         _p(out["prp1"], _u64p), _p(out["prp2"], _u64p),
+                         _p(out["status"], _u8p), _p(total, _u64p))
+    out["total"] = int(total[0])
+    out["pool"] = pool
+    return out
+
+
+def partition(qid, nqueues):
+    qid = _u32(qid)
+    n = qid.shape[0]
+    perm = np.empty(n, np.uint32)
+    qoff = np.empty(nqueues + 2, np.uint64)
+    ninv = np.zeros(1, np.uint64)
+    _lib().orc_partition(_p(qid, _u32p), n, nqueues, _p(perm, _u32p), _p(qoff, _u64p),
+                         _p(ninv, _u64p))
+    return dict(perm=perm, qoff=qoff, n_invalid=int(ninv[0]))
+
+
+class Registry:
+    """Refcounted registration cache (O4)."""
+
+    def __init__(self, page_shift=12):
+        self._h = _lib().orc_reg_create(page_shift)
+
+    def __del__(self):
+        if getattr(self, "_h", None):
+            _lib().orc_reg_destroy(self._h)
+            self._h = None
+
+    def register(self, addr, size):
+        return int(_lib().orc_reg_register(self._h, addr, size))
+
+    def deregister(self, handle):
+        return int(_lib().orc_reg_deregister(self._h, handle))
+
+    def refs(self, handle):
+        return int(_lib().orc_reg_refs(self._h, handle))
+
+    def count(self):
+        return int(_lib().orc_reg_count(self._h))
+
+    def capacity(self):
+        return int(_lib().orc_reg_capacity(self._h))
+
+    def table(self):
+        k = self.count()
+        s, e, h = (np.empty(k, np.uint64) for _ in range(3))
+        _lib().orc_reg_export(self._h, _p(s, _u64p), _p(e, _u64p), _p(h, _u64p), k)
+        return s, e, h

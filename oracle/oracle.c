@@ -1,0 +1,340 @@
+/*
+ * oracle.c - plain, single-threaded CPU reference (TEST INFRASTRUCTURE ONLY).
+ *
+ * Only the tests, the smoke check and the benchmark's CPU-baseline leg load
+ * this file's library. It shares nothing with the GPU library. Each function
+ * follows the steps of the passage it cites, in that order, with no blocking,
+ * fusion or reordering; exact 128-bit arithmetic is used wherever a 64-bit
+ * intermediate could wrap, so that a reader can check it by eye.
+ *
+ * Parity status of each function is recorded beside it ("pinned by ...").
+ */
+#include "oracle.h"
+
+#include <stdlib.h>
+#include <string.h>
+
+typedef unsigned __int128 u128;
+
+/* ------------------------------------------------------------------------
+ * O1  Page-rounded containment lookup.
+ *
+ * [NCCL-26] "IB Backend MR Cache": a range is first widened to whole system
+ * pages -- the base is the address with the in-page bits cleared, and the page
+ * count is (address + size - base + page - 1) / page -- and the cache is then
+ * searched by address; an existing region that fully contains the widened
+ * range is a hit and is reused, a partial overlap is not a hit. The
+ * "Communicator User Registration Cache" section applies the same floor/cover
+ * rounding before its containment test.
+ *
+ * Readings: the region id in the sorted table is the handle (-1 = miss); the
+ * exact/contained distinction is made on the rounded bounds; a zero-length
+ * range, or one whose end or rounded end does not fit in 64 bits, is INVALID.
+ *
+ * Pinned by: the four-row rounding table printed in "IB Backend MR Cache"; the
+ * register sequence of "真实 ncclCommRegister 语义实验" replayed on O4 and
+ * looked up here; brute-force containment scans over every region.
+ * ------------------------------------------------------------------------ */
+void orc_mr_lookup(const uint64_t *start, const uint64_t *end, const uint32_t *lkey,
+                   uint64_t nregions, unsigned page_shift,
+                   const uint64_t *off, const uint64_t *len, uint64_t n, uint64_t va_base,
+                   int32_t *handle, uint32_t *lkey_out, uint8_t *kind,
+                   uint64_t *rbase, uint64_t *rend)
+{
+    const uint64_t page = 1ull << page_shift;
+    for (uint64_t i = 0; i < n; ++i) {
+        handle[i] = -1;
+        lkey_out[i] = 0;
+        kind[i] = ORC_MISS;
+        rbase[i] = 0;
+        rend[i] = 0;
+
+        /* Absolute address of the range, and validity. */
+        u128 a_wide = (u128)va_base + off[i];
+        uint64_t size = len[i];
+        if (size == 0 || a_wide + size > (u128)UINT64_MAX) {
+            kind[i] = ORC_INVALID;
+            continue;
+        }
+        uint64_t a = (uint64_t)a_wide;
+
+        /* Round down the base, count the covering pages, round up the end. */
+        uint64_t base = a & ~(page - 1);
+        u128 pages = ((u128)a + size - base + page - 1) / page;
+        u128 end_wide = (u128)base + pages * page;
+        if (end_wide > (u128)UINT64_MAX) {
+            kind[i] = ORC_INVALID;
+            continue;
+        }
+        uint64_t top = (uint64_t)end_wide;
+        rbase[i] = base;
+        rend[i] = top;
+
+        /* The only region that can contain [base, top) in a sorted,
+         * non-overlapping table is the last one starting at or below base:
+         * binary search for the count of starts <= base. */
+        uint64_t lo = 0, hi = nregions;
+        while (lo < hi) {
+            uint64_t mid = lo + (hi - lo) / 2;
+            if (start[mid] <= base) lo = mid + 1;
+            else hi = mid;
+        }
+        if (lo == 0) continue;                 /* no region starts at or below */
+        uint64_t r = lo - 1;
+        if (top <= end[r]) {                   /* full containment: a hit */
+            handle[i] = (int32_t)r;
+            lkey_out[i] = lkey[r];
+            kind[i] = (base == start[r] && top == end[r]) ? ORC_EXACT : ORC_CONTAINED;
+        }                                      /* partial overlap or disjoint: miss */
+    }
+}
+
+/* ------------------------------------------------------------------------
+ * O2  GPU-page table -> NVMe PRP entries and chained PRP lists.
+ *
+ * [UPCIE] introduction: GPU memory is resolved once into a table holding one
+ * physical address per 64 KiB GPU page; at submission PRP entries are formed
+ * at 4 KiB granularity from the 4 KiB sub-page offsets inside each 64 KiB
+ * entry. "Limitations": one list page holds 512 entries, so PRP1 plus one
+ * list page reaches 513 x 4 KiB; that backend does not chain.
+ * [NVMe] PRP rules (not on the pages): PRP1 is the first page's address with
+ * the byte offset; PRP2 is 0 for a one-page transfer, the second page's
+ * address for two pages, and otherwise the bus address of a PRP list; when a
+ * list needs more entries than a page holds, the last entry of each
+ * non-final list page points to the next list page.
+ *
+ * Readings: the physical address of heap byte x is table[x >> 16] plus
+ * (x & 0xFFFF); list pages are handed out in request order from a running
+ * counter (an exclusive prefix of the per-request page counts); a request
+ * refused for lack of pool pages still advances the counter, so the refused
+ * set is a suffix and *total is the capacity the batch needs; a request with
+ * zero length, an offset that is not a multiple of 4 (PRP1 must be dword
+ * aligned), or an end that wraps is EINVAL; one that ends past the heap is
+ * ERANGE. Refused requests get PRP1 = PRP2 = 0 and write no list entries.
+ *
+ * Pinned by: a byte-walk brute force over tiny heaps (every 4 KiB physical
+ * page the bytes of the request touch, in order, against PRP1/PRP2/list
+ * chain), the identity-table special case (the textbook contiguous PRP list),
+ * the 513-page single-list limit from "Limitations", and chain-walk checks of
+ * list sizes around every multiple of 511. Chaining itself follows [NVMe];
+ * no page prints a chained example.
+ * ------------------------------------------------------------------------ */
+static uint64_t phys_of(const uint64_t *lut, uint64_t x)
+{
+    return lut[x >> 16] + (x & 0xFFFFull);
+}
+
+void orc_build_prp(const uint64_t *lut, uint64_t lut_entries,
+                   const uint64_t *off, const uint64_t *len, uint64_t n,
+                   uint64_t list_bus_base, uint64_t *pool, uint64_t pool_pages,
+                   uint64_t *prp1, uint64_t *prp2, uint8_t *status, uint64_t *total)
+{
+    const u128 heap = (u128)lut_entries << 16;
+    uint64_t next_slot = 0;                       /* running list-page counter */
+
+    for (uint64_t i = 0; i < n; ++i) {
+        const uint64_t o = off[i], size = len[i];
+        prp1[i] = 0;
+        prp2[i] = 0;
+        status[i] = ORC_OK;
+
+        /* 1. Validate. */
+        if (size == 0 || (o % 4) != 0 || (u128)o + size > (u128)UINT64_MAX) {
+            status[i] = ORC_EINVAL;
+            continue;
+        }
+        if ((u128)o + size > heap) {
+            status[i] = ORC_ERANGE;
+            continue;
+        }
+
+        /* 2. Number of 4 KiB pages the byte range touches. */
+        uint64_t npages = (uint64_t)(((u128)(o & 4095) + size + 4095) >> 12);
+        uint64_t page0 = o & ~4095ull;            /* heap offset of page 0 */
+
+        /* 3./5. PRP1, then PRP2 by page count. */
+        if (npages == 1) {
+            prp1[i] = phys_of(lut, o);
+            prp2[i] = 0;
+            continue;
+        }
+        if (npages == 2) {
+            prp1[i] = phys_of(lut, o);
+            prp2[i] = phys_of(lut, page0 + 4096);
+            continue;
+        }
+        uint64_t entries = npages - 1;                    /* pages 1 .. n-1 */
+        uint64_t lpages = (entries - 1 + 510) / 511;      /* ceil((entries-1)/511) */
+        uint64_t slot = next_slot;
+        next_slot += lpages;                              /* 7. advance, refused or not */
+        if ((u128)slot + lpages > pool_pages) {
+            status[i] = ORC_ENOSPC;
+            continue;
+        }
+        prp1[i] = phys_of(lut, o);
+        prp2[i] = list_bus_base + slot * 4096;
+
+        /* 4./6. Fill the list pages in order; a full non-final page gets a
+         * pointer to the next page in its last entry. */
+        if (pool) {
+            uint64_t t = 0, pos = 0;
+            for (uint64_t k = 1; k < npages; ++k) {
+                if (pos == 511 && t + 1 < lpages) {
+                    pool[(slot + t) * 512 + 511] = list_bus_base + (slot + t + 1) * 4096;
+                    ++t;
+                    pos = 0;
+                }
+                pool[(slot + t) * 512 + pos] = phys_of(lut, page0 + 4096 * k);
+                ++pos;
+            }
+        }
+    }
+    *total = next_slot;
+}
+
+/* ------------------------------------------------------------------------
+ * O3  Stable split of requests by destination queue.
+ *
+ * A plain counting split: count each bucket, take the exclusive prefix as the
+ * bucket starts, then place the request indices in increasing order behind a
+ * per-bucket cursor, so that equal queue ids keep their original order.
+ * [MORI] groups a wave's lanes by destination before issuing and reserves
+ * queue slots per group; the order of equal keys is not stated there, and the
+ * reading here is stable (ties by original index). Queue ids >= nqueues go to
+ * an overflow bucket after the valid ones.
+ *
+ * Pinned by: a library stable sort of the indices by queue id.
+ * ------------------------------------------------------------------------ */
+void orc_partition(const uint32_t *qid, uint64_t n, uint32_t nqueues,
+                   uint32_t *perm, uint64_t *qoff, uint64_t *n_invalid)
+{
+    const uint64_t nb = (uint64_t)nqueues + 1;
+    uint64_t *cursor = (uint64_t *)calloc(nb, sizeof(uint64_t));
+    for (uint64_t i = 0; i < n; ++i) {
+        uint64_t b = qid[i] < nqueues ? qid[i] : nqueues;
+        cursor[b]++;
+    }
+    qoff[0] = 0;
+    for (uint64_t b = 0; b < nb; ++b) qoff[b + 1] = qoff[b] + cursor[b];
+    *n_invalid = cursor[nqueues];
+    for (uint64_t b = 0; b < nb; ++b) cursor[b] = qoff[b];
+    for (uint64_t i = 0; i < n; ++i) {
+        uint64_t b = qid[i] < nqueues ? qid[i] : nqueues;
+        perm[cursor[b]++] = (uint32_t)i;
+    }
+    free(cursor);
+}
+
+/* ------------------------------------------------------------------------
+ * O4  Registration cache with reference counts.
+ *
+ * [NCCL-26] "Communicator User Registration Cache": register rounds the range
+ * to whole pages; if an existing record fully contains it, its count goes up
+ * and its handle is returned; otherwise a new record is inserted in sorted
+ * position. "IB Backend MR Cache": deregister drops the count and frees the
+ * record at zero; a handle not in the cache is an error; the record array
+ * grows from 0 to 32 and then doubles (32 -> 64 -> 128).
+ *
+ * Readings: a handle is a record id that is never reused (so a stale handle
+ * is always detected); records are kept sorted by start, a new record goes
+ * after existing records with the same start; when several records contain a
+ * range, the first in sorted order is reused.
+ *
+ * Pinned by: the 8 MiB register/deregister sequence of
+ * "真实 ncclCommRegister 语义实验" and the capacity growth sequence.
+ * ------------------------------------------------------------------------ */
+typedef struct {
+    uint64_t start, end, id;
+    int64_t refs;
+} orc_record;
+
+struct orc_registry {
+    uint64_t page;
+    uint64_t count, capacity, next_id;
+    orc_record *rec;
+};
+
+orc_registry *orc_reg_create(unsigned page_shift)
+{
+    orc_registry *g = (orc_registry *)calloc(1, sizeof(*g));
+    g->page = 1ull << page_shift;
+    g->next_id = 1;
+    return g;
+}
+
+void orc_reg_destroy(orc_registry *g)
+{
+    if (!g) return;
+    free(g->rec);
+    free(g);
+}
+
+uint64_t orc_reg_register(orc_registry *g, uint64_t addr, uint64_t size)
+{
+    if (size == 0 || (u128)addr + size > (u128)UINT64_MAX) return 0;
+    uint64_t base = addr & ~(g->page - 1);
+    u128 pages = ((u128)addr + size - base + g->page - 1) / g->page;
+    u128 top_wide = (u128)base + pages * g->page;
+    if (top_wide > (u128)UINT64_MAX) return 0;
+    uint64_t top = (uint64_t)top_wide;
+
+    for (uint64_t k = 0; k < g->count; ++k) {
+        if (g->rec[k].start <= base && top <= g->rec[k].end) {
+            g->rec[k].refs++;
+            return g->rec[k].id;
+        }
+    }
+    if (g->count == g->capacity) {
+        uint64_t cap = g->capacity == 0 ? 32 : 2 * g->capacity;
+        g->rec = (orc_record *)realloc(g->rec, cap * sizeof(orc_record));
+        g->capacity = cap;
+    }
+    uint64_t pos = 0;
+    while (pos < g->count && g->rec[pos].start <= base) ++pos;
+    memmove(&g->rec[pos + 1], &g->rec[pos], (g->count - pos) * sizeof(orc_record));
+    g->rec[pos].start = base;
+    g->rec[pos].end = top;
+    g->rec[pos].id = g->next_id++;
+    g->rec[pos].refs = 1;
+    g->count++;
+    return g->rec[pos].id;
+}
+
+static int64_t find_record(const orc_registry *g, uint64_t handle)
+{
+    for (uint64_t k = 0; k < g->count; ++k)
+        if (g->rec[k].id == handle) return (int64_t)k;
+    return -1;
+}
+
+int orc_reg_deregister(orc_registry *g, uint64_t handle)
+{
+    int64_t k = find_record(g, handle);
+    if (k < 0) return -1;
+    if (--g->rec[k].refs == 0) {
+        memmove(&g->rec[k], &g->rec[k + 1], (g->count - (uint64_t)k - 1) * sizeof(orc_record));
+        g->count--;
+    }
+    return 0;
+}
+
+int64_t orc_reg_refs(const orc_registry *g, uint64_t handle)
+{
+    int64_t k = find_record(g, handle);
+    return k < 0 ? -1 : g->rec[k].refs;
+}
+
+uint64_t orc_reg_count(const orc_registry *g) { return g->count; }
+uint64_t orc_reg_capacity(const orc_registry *g) { return g->capacity; }
+
+uint64_t orc_reg_export(const orc_registry *g, uint64_t *start, uint64_t *end,
+                        uint64_t *handle, uint64_t max)
+{
+    uint64_t k = 0;
+    for (; k < g->count && k < max; ++k) {
+        start[k] = g->rec[k].start;
+        end[k] = g->rec[k].end;
+        handle[k] = g->rec[k].id;
+    }
+    return k;
+}

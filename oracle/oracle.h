@@ -1,0 +1,94 @@
+/*
+ * oracle.h - plain, single-threaded CPU reference for batched DMA-descriptor
+ * building.
+ *
+ * TEST INFRASTRUCTURE ONLY. This is the checker the GPU library is compared
+ * against; it is not part of the product. Only the tests, the smoke check and
+ * the benchmark's CPU-baseline leg may load it. It shares no code, header,
+ * table or helper with the GPU library, and the GPU library never calls it.
+ *
+ * Sources (web pages; cited by title and section):
+ *   [NCCL-26]  "NCCL 专家课程 26：GPUDirect RDMA、DMA-BUF、MR 与注册缓存"
+ *              (blog.cptz.space), sections "IB Backend MR Cache",
+ *              "Communicator User Registration Cache" and
+ *              "真实 ncclCommRegister 语义实验".
+ *   [UPCIE]    xNVMe "uPCIe CUDA" backend (xnvme.io), introduction,
+ *              "Memory Architecture" and "Limitations".
+ *   [MORI]     "mori通信库分析(一)——对称内存RDMA数据发送过程", the
+ *              thread-scope put kernel and the warp-level WQE reservation.
+ *   [NVMe]     NVM Express Base Specification, PRP entry / PRP list rules
+ *              (not on the pages; used where they stop).
+ *
+ * Every function computes one fully determined result; see oracle.c for the
+ * step-by-step definitions and the readings taken where the pages are silent.
+ */
+#ifndef DMADESC_ORACLE_H
+#define DMADESC_ORACLE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Lookup outcome per request. */
+enum { ORC_MISS = 0, ORC_EXACT = 1, ORC_CONTAINED = 2, ORC_INVALID = 3 };
+
+/* PRP build status per request. */
+enum { ORC_OK = 0, ORC_EINVAL = 1, ORC_ERANGE = 2, ORC_ENOSPC = 3 };
+
+/*
+ * O1: page-rounded containment lookup of each request range in a sorted,
+ * non-overlapping region table [start[r], end[r]).
+ * Outputs per request: handle (region index, -1 on miss/invalid), lkey
+ * (0 on miss/invalid), kind, rounded base and rounded end (0/0 on invalid).
+ */
+void orc_mr_lookup(const uint64_t *start, const uint64_t *end, const uint32_t *lkey,
+                   uint64_t nregions, unsigned page_shift,
+                   const uint64_t *off, const uint64_t *len, uint64_t n, uint64_t va_base,
+                   int32_t *handle, uint32_t *lkey_out, uint8_t *kind,
+                   uint64_t *rbase, uint64_t *rend);
+
+/*
+ * O2: 64 KiB GPU-page table -> 4 KiB NVMe PRP1/PRP2 and chained PRP lists.
+ * pool (may be NULL: lists are then not written) is u64[pool_pages][512];
+ * list page s has bus address list_bus_base + 4096*s. *total receives the
+ * number of list pages the batch needs (including those refused with ENOSPC).
+ */
+void orc_build_prp(const uint64_t *lut, uint64_t lut_entries,
+                   const uint64_t *off, const uint64_t *len, uint64_t n,
+                   uint64_t list_bus_base, uint64_t *pool, uint64_t pool_pages,
+                   uint64_t *prp1, uint64_t *prp2, uint8_t *status, uint64_t *total);
+
+/*
+ * O3: stable split of request indices by queue id. Queue ids >= nqueues go to
+ * an overflow bucket nqueues. qoff has nqueues+2 entries: bucket b occupies
+ * perm[qoff[b] .. qoff[b+1]). *n_invalid = size of the overflow bucket.
+ */
+void orc_partition(const uint32_t *qid, uint64_t n, uint32_t nqueues,
+                   uint32_t *perm, uint64_t *qoff, uint64_t *n_invalid);
+
+/*
+ * O4: host registration cache with reference counts ([NCCL-26]).
+ * Handles are positive record ids, never reused; 0 is never a handle.
+ */
+typedef struct orc_registry orc_registry;
+orc_registry *orc_reg_create(unsigned page_shift);
+void orc_reg_destroy(orc_registry *g);
+/* Returns the handle (> 0), or 0 for a zero-length or wrapping range. */
+uint64_t orc_reg_register(orc_registry *g, uint64_t addr, uint64_t size);
+/* Returns 0 on success, -1 for a handle that names no live record. */
+int orc_reg_deregister(orc_registry *g, uint64_t handle);
+/* Reference count of a live record, or -1. */
+int64_t orc_reg_refs(const orc_registry *g, uint64_t handle);
+uint64_t orc_reg_count(const orc_registry *g);
+uint64_t orc_reg_capacity(const orc_registry *g);
+/* Copies the live records in sorted order (start, end, handle); returns count. */
+uint64_t orc_reg_export(const orc_registry *g, uint64_t *start, uint64_t *end,
+                        uint64_t *handle, uint64_t max);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DMADESC_ORACLE_H */

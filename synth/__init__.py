@@ -1,0 +1,115 @@
+"""Seeded synthetic workloads for the batched DMA-descriptor path.
+
+Thin ctypes wrapper over ``synth.c``. It only draws inputs (GPU-page
+physical-address table, registered-region table, SoA request batch); it holds
+none of the method's arithmetic, so both the CPU oracle and the GPU library
+can consume what it returns.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "synth.c")
+_SO = os.path.join(_HERE, "libsynth.so")
+
+WORKLOADS = {"tiny": 1, "small": 2, "large": 3, "mrheavy": 4, "mixed": 5}
+
+HEAP_VA_BASE = 0x0000700000000000
+PHYS_BASE = 0x0000200000000000
+LIST_BUS_BASE = 0x0000100000000000
+
+
+class _Shape(ctypes.Structure):
+    _fields_ = [
+        ("n", ctypes.c_uint64),
+        ("lut_entries", ctypes.c_uint64),
+        ("regions", ctypes.c_uint64),
+        ("nqueues", ctypes.c_uint32),
+        ("page_shift", ctypes.c_uint32),
+        ("va_base", ctypes.c_uint64),
+        ("list_bus_base", ctypes.c_uint64),
+        ("default_seed", ctypes.c_uint64),
+    ]
+
+
+def build() -> str:
+    """Compile libsynth.so with the host C compiler."""
+    cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-Wall", "-Wextra",
+           "-o", _SO, _SRC, "-lm"]
+    subprocess.run(cmd, check=True)
+    return _SO
+
+
+_lib_handle = None
+
+
+def _lib():
+    global _lib_handle
+    if _lib_handle is None:
+        if not os.path.exists(_SO):
+            build()
+        lib = ctypes.CDLL(_SO)
+        p64 = ctypes.POINTER(ctypes.c_uint64)
+        p32 = ctypes.POINTER(ctypes.c_uint32)
+        lib.synth_shape_of.argtypes = [ctypes.c_int, ctypes.POINTER(_Shape)]
+        lib.synth_shape_of.restype = ctypes.c_int
+        lib.synth_splitmix64.argtypes = [ctypes.c_uint64, ctypes.c_uint64, p64]
+        lib.synth_splitmix64.restype = None
+        lib.synth_fill.argtypes = [ctypes.c_int, ctypes.c_uint64, ctypes.c_uint64,
+                                   p64, p64, p64, p32, p64, p64, p32]
+        lib.synth_fill.restype = ctypes.c_int
+        _lib_handle = lib
+    return _lib_handle
+
+
+def _ptr(a, ctype):
+    if a is None:
+        return ctypes.cast(None, ctypes.POINTER(ctype))
+    return a.ctypes.data_as(ctypes.POINTER(ctype))
+
+
+def shape(name: str) -> dict:
+    s = _Shape()
+    if _lib().synth_shape_of(WORKLOADS[name], ctypes.byref(s)) != 0:
+        raise ValueError(name)
+    return {f: getattr(s, f) for f, _ in _Shape._fields_}
+
+
+def splitmix64(seed: int, k: int) -> np.ndarray:
+    out = np.empty(k, dtype=np.uint64)
+    _lib().synth_splitmix64(seed, k, _ptr(out, ctypes.c_uint64))
+    return out
+
+
+def generate(name: str, n: int | None = None, seed: int = 0) -> dict:
+    """Draws workload `name` with `n` requests (default: the workload's own
+    count). Returns a dict with the shape fields and the arrays ``lut``,
+    ``rstart``, ``rend``, ``rlkey``, ``off``, ``len``, ``qid`` (empty arrays
+    where the workload has none)."""
+    sh = shape(name)
+    if n is None:
+        n = sh["n"]
+    P, R = sh["lut_entries"], sh["regions"]
+    lut = np.empty(P, dtype=np.uint64)
+    rstart = np.empty(R, dtype=np.uint64)
+    rend = np.empty(R, dtype=np.uint64)
+    rlkey = np.empty(R, dtype=np.uint32)
+    off = np.empty(n, dtype=np.uint64)
+    ln = np.empty(n, dtype=np.uint64)
+    qid = np.empty(n, dtype=np.uint32)
+    rc = _lib().synth_fill(WORKLOADS[name], seed, n,
+                           _ptr(lut, ctypes.c_uint64), _ptr(rstart, ctypes.c_uint64),
+                           _ptr(rend, ctypes.c_uint64), _ptr(rlkey, ctypes.c_uint32),
+                           _ptr(off, ctypes.c_uint64), _ptr(ln, ctypes.c_uint64),
+                           _ptr(qid, ctypes.c_uint32))
+    if rc != 0:
+        raise RuntimeError(f"synth_fill({name}) failed")
+    out = dict(sh)
+    out.update(name=name, n=n, lut=lut, rstart=rstart, rend=rend, rlkey=rlkey,
+               off=off, len=ln, qid=qid)
+    return out

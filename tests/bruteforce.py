@@ -1,0 +1,101 @@
+"""Independent brute-force definitions used to pin the oracle.
+
+These restate what the results must be in a different form from the oracle:
+integer floor/ceil instead of masks, a scan over every region instead of a
+binary search, a walk over every byte of a request instead of page arithmetic,
+a chain walk that follows pointers instead of slot arithmetic, and a library
+stable sort instead of a counting split. Pure Python / numpy, small inputs only.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+MISS, EXACT, CONTAINED, INVALID = 0, 1, 2, 3
+U64_MAX = (1 << 64) - 1
+
+
+def round_bounds(a: int, size: int, page: int):
+    """Whole pages covering [a, a+size): floor of the start, ceiling of the end."""
+    lo = (a // page) * page
+    hi = -(-(a + size) // page) * page
+    return lo, hi
+
+
+def lookup(start, end, lkey, off, length, va_base=0, page_shift=12):
+    """Containment lookup by scanning every region for one that holds the
+    rounded range."""
+    page = 1 << page_shift
+    start = [int(x) for x in start]
+    end = [int(x) for x in end]
+    res = []
+    for o, ln in zip(off, length):
+        a, size = va_base + int(o), int(ln)
+        if size == 0 or a > U64_MAX or a + size > U64_MAX:
+            res.append((-1, 0, INVALID, 0, 0))
+            continue
+        lo, hi = round_bounds(a, size, page)
+        if hi > U64_MAX:
+            res.append((-1, 0, INVALID, 0, 0))
+            continue
+        hit = None
+        for r, (s, e) in enumerate(zip(start, end)):
+            if s <= lo and hi <= e:
+                hit = r
+                break
+        if hit is None:
+            res.append((-1, 0, MISS, lo, hi))
+        else:
+            k = EXACT if (lo == start[hit] and hi == end[hit]) else CONTAINED
+            res.append((hit, int(lkey[hit]), k, lo, hi))
+    return res
+
+
+def phys_bytes(lut: np.ndarray, x: np.ndarray) -> np.ndarray:
+    """Physical address of heap bytes x: the 64 KiB GPU page's physical
+    address plus the byte's position inside that GPU page."""
+    x = x.astype(np.uint64)
+    return lut[x // np.uint64(65536)] + x % np.uint64(65536)
+
+
+def touched_pages(lut: np.ndarray, off: int, size: int):
+    """Walks every byte of [off, off+size) and returns (physical address of the
+    first byte, physical 4 KiB page addresses touched, in order, no repeats)."""
+    x = np.arange(off, off + size, dtype=np.uint64)
+    ph = phys_bytes(lut, x)
+    pg = ph // np.uint64(4096)
+    keep = np.ones(pg.shape[0], dtype=bool)
+    keep[1:] = pg[1:] != pg[:-1]
+    return int(ph[0]), [int(p) * 4096 for p in pg[keep]]
+
+
+def chain_walk(pool: np.ndarray, bus: int, prp2: int, count: int):
+    """Follows an NVMe PRP list from PRP2 and returns (the `count` data
+    entries, the list slots visited). In a list page, the last entry is a
+    pointer to the next list page whenever more than one entry remains."""
+    rel = prp2 - bus
+    assert rel >= 0 and rel % 4096 == 0, "PRP2 does not name a list page"
+    slot = rel // 4096
+    slots = [slot]
+    entries = []
+    pos = 0
+    while len(entries) < count:
+        if pos == 511 and count - len(entries) > 1:
+            nxt = int(pool[slot, 511]) - bus
+            assert nxt >= 0 and nxt % 4096 == 0, "chain pointer does not name a list page"
+            slot = nxt // 4096
+            slots.append(slot)
+            pos = 0
+            continue
+        entries.append(int(pool[slot, pos]))
+        pos += 1
+    return entries, slots
+
+
+def stable_split(qid: np.ndarray, nqueues: int):
+    """Stable sort of request indices by bucket (ids >= nqueues share the
+    overflow bucket) and bucket starts from a histogram."""
+    b = np.minimum(qid.astype(np.int64), nqueues)
+    perm = np.argsort(b, kind="stable").astype(np.uint32)
+    counts = np.bincount(b, minlength=nqueues + 1)
+    qoff = np.concatenate([[0], np.cumsum(counts)]).astype(np.uint64)
+    return perm, qoff, int(counts[nqueues])

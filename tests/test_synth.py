@@ -1,0 +1,67 @@
+"""The seeded input generator: reproducible, and shaped as the workloads say."""
+import numpy as np
+import pytest
+
+import synth
+
+
+def test_splitmix64_published_outputs():
+    # First outputs of SplitMix64 seeded with 0, as published with the
+    # algorithm's reference implementation.
+    assert [int(x) for x in synth.splitmix64(0, 3)] == [
+        0xE220A8397B1DCDAF, 0x6E789E6AA1B965F4, 0x06C45D188009454F]
+
+
+@pytest.mark.parametrize("name", list(synth.WORKLOADS))
+def test_reproducible_and_prefix_stable(name):
+    a = synth.generate(name, n=3000)
+    b = synth.generate(name, n=3000)
+    c = synth.generate(name, n=1000)
+    for k in ("lut", "rstart", "rend", "rlkey", "off", "len", "qid"):
+        assert np.array_equal(a[k], b[k])
+    for k in ("off", "len", "qid"):
+        assert np.array_equal(a[k][:1000], c[k])
+    d = synth.generate(name, n=1000, seed=12345)
+    assert not np.array_equal(d["off"], c["off"])
+
+
+@pytest.mark.parametrize("name", list(synth.WORKLOADS))
+def test_shapes(name):
+    d = synth.generate(name, n=20000)
+    P, R = d["lut_entries"], d["regions"]
+    if P:
+        lut = d["lut"]
+        assert (lut % 65536 == 0).all()
+        frames = (lut - synth.PHYS_BASE) // 65536
+        assert np.array_equal(np.sort(frames), np.arange(P, dtype=np.uint64))
+        heap = P * 65536
+        assert (d["off"] + d["len"] <= heap).all()
+    if R:
+        s, e = d["rstart"], d["rend"]
+        assert (s % 4096 == 0).all() and (e % 4096 == 0).all()
+        assert (s < e).all() and (s[1:] >= e[:-1]).all()
+        assert (d["rlkey"] != 0).all()
+    assert (d["len"] > 0).all()
+    if name in ("large", "mixed"):
+        assert (d["off"] % 4 == 0).all()
+    if name in ("tiny", "small"):
+        assert (d["off"] % 512 == 0).all()
+    if d["nqueues"]:
+        assert (d["qid"] < d["nqueues"]).all()
+
+
+def test_mixed_distributions():
+    d = synth.generate("mixed", n=200000)
+    ln = d["len"]
+    assert ln.min() >= 512 and ln.max() <= 1 << 20 and (ln % 512 == 0).all()
+    frac0 = (d["qid"] == 0).mean()
+    assert 0.23 < frac0 < 0.27           # Zipf(1.1) over 64: queue 0 ~ 25%
+    w = np.arange(1, 65, dtype=float) ** -1.1
+    assert abs((d["qid"] == 63).mean() - w[-1] / w.sum()) < 0.001
+
+
+def test_large_lengths():
+    d = synth.generate("large", n=50000)
+    ln = d["len"]
+    assert ln.min() >= 32 * 4096 and ln.max() <= 2048 * 4096 and (ln % 4096 == 0).all()
+    assert (d["qid"] < 16).all()
