@@ -1,0 +1,241 @@
+#!/usr/bin/env python3
+"""Benchmark: batched DMA-descriptor building on one MI355X.
+
+One step = the whole hot path over one batch: page-rounded MR lookup, PRP
+build (PRP1/PRP2 + chained lists) and stable split by queue, three calls on
+one stream, over the 16,777,216-request Mixed workload (256 GiB heap of
+4,194,304 GPU pages, 4,096 regions, log-uniform 512 B - 1 MiB requests,
+Zipf(1.1) over 64 queues). Inputs are resident in HBM before timing starts.
+
+Prints ONE JSON line. `value` is requests per second (millions) over the
+timed steps; `roofline` describes the dominant call (the PRP build):
+algorithmic bytes of one launch / its mean duration from HIP events recorded
+on the stream it runs on. `cpu_baseline` times the single-threaded oracle on a
+bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, AMD public specification
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_build_prp_mixed.json")
+PRP_SOURCES = ["build_prp.hip", "dd_device.hpp"]
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="mixed",
+                    choices=["tiny", "small", "large", "mixed"])
+    ap.add_argument("--cpu-sample", type=int, default=1 << 21,
+                    help="requests of the workload the oracle is timed on")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="minimum CPU time spent timing the oracle")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run a plain 1 GiB device copy (for counter scaling) and exit")
+    return ap.parse_args()
+
+
+def prp_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in PRP_SOURCES:
+        with open(os.path.join(ROOT, "memory_dma_descriptor_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def algorithmic_bytes(d, np):
+    """Bytes each call must move, each column once (per-request figures:
+    lookup 16 read + 25 written; PRP 16 read + 8 per GPU page touched, 17
+    written + 8 per list entry or chain pointer; split 4 read + 4 written)."""
+    off, ln = d["off"], d["len"]
+    n = off.shape[0]
+    heap = np.uint64(d["lut_entries"]) * np.uint64(65536)
+    valid = (ln > 0) & (off % 4 == 0) & (off + ln <= heap) & (off + ln >= off)
+    pages = np.where(valid, ((off & np.uint64(4095)) + ln + np.uint64(4095)) >> np.uint64(12), 0)
+    frames = np.where(valid, ((off + ln - np.uint64(1)) >> np.uint64(16)) - (off >> np.uint64(16)) + np.uint64(1), 0)
+    lists = pages >= 3
+    m = np.where(lists, pages - 1, 0).astype(np.float64)
+    lp = np.where(lists, (pages - 2 + 510) // 511, 0).astype(np.float64)
+    entries = float((m + lp - np.where(lists, 1.0, 0.0)).sum())
+    lookup = n * (16 + 25) + d["regions"] * 20
+    prp = n * (16 + 17) + 8 * float(frames.sum()) + 8 * entries
+    split = n * 8
+    return dict(lookup=float(lookup), build_prp=float(prp), partition=float(split),
+                list_entries=entries, prp_entries=float(pages.astype(np.float64).sum()))
+
+
+def cpu_baseline(name, sample, min_seconds):
+    import numpy as np
+
+    import oracle
+    import synth
+    d = synth.generate(name, n=sample)
+    bus = d["list_bus_base"]
+    total = oracle.build_prp(d["lut"], d["off"], d["len"], bus, 0)["total"]
+    pool = np.ones((max(total, 1), 512), dtype=np.uint64)      # pre-faulted, reused
+    old = os.sched_getaffinity(0)
+    cpu = min(old)
+    os.sched_setaffinity(0, {cpu})
+    try:
+        reps, spent = 0, 0.0
+        while spent < min_seconds:
+            t0 = time.perf_counter()
+            if d["regions"]:
+                oracle.mr_lookup(d["rstart"], d["rend"], d["rlkey"], d["off"], d["len"],
+                                 va_base=d["va_base"])
+            oracle.build_prp(d["lut"], d["off"], d["len"], bus, total, pool=pool)
+            oracle.partition(d["qid"], d["nqueues"])
+            spent += time.perf_counter() - t0
+            reps += 1
+    finally:
+        os.sched_setaffinity(0, old)
+    return {"value": round(sample * reps / spent / 1e6, 4), "unit": "M req/s", "cores": 1,
+            "kind": "oracle",
+            "sample": (f"first {sample:,} requests of the {name} workload, lookup + PRP build "
+                       f"(lists into a pre-faulted host pool) + split, single thread pinned "
+                       f"to one core, {reps} repetitions, {spent:.1f} s"),
+            "host_cores": os.cpu_count()}
+
+
+def copy_calibration():
+    import torch
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty(n, dtype=torch.uint8, device="cuda")
+    src.fill_(1)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": n, "launches": 3}), flush=True)
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this build runs on exactly one GPU (requests are independent; "
+              "see the sharding design); use --gpus 1", file=sys.stderr, flush=True)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    if args.copy_calibration:
+        copy_calibration()
+        return
+
+    import memory_dma_descriptor_amd as dd
+    import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    d = synth.generate(args.workload)
+    n, nq = d["n"], d["nqueues"]
+    bus = d["list_bus_base"]
+    up = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)  # noqa: E731
+    rs, re_, rk = up(d["rstart"]), up(d["rend"]), up(d["rlkey"])
+    off, ln, qid, lut = up(d["off"]), up(d["len"]), up(d["qid"]), up(d["lut"])
+
+    # Capacity query: with an empty pool the call still reports the pages
+    # the batch needs.
+    empty = torch.empty((0, 512), dtype=torch.uint64, device=dev)
+    probe = dd.build_prp(lut, off, ln, bus, empty)
+    torch.cuda.synchronize()
+    pool_pages = int(probe["total_pages"].cpu()[0])
+    pool = torch.empty((pool_pages, 512), dtype=torch.uint64, device=dev)
+
+    lk_out = prp_out = sp_out = None
+    ws_prp = torch.empty(max(dd.workspace_bytes(dd.OP_BUILD_PRP, n), 1), dtype=torch.uint8, device=dev)
+    ws_sp = torch.empty(max(dd.workspace_bytes(dd.OP_PARTITION, n, max(nq, 1)), 1),
+                        dtype=torch.uint8, device=dev)
+
+    def step():
+        nonlocal lk_out, prp_out, sp_out
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        ev[0].record()
+        if d["regions"]:
+            lk_out = dd.mr_lookup(rs, re_, rk, off, ln, va_base=d["va_base"], out=lk_out)
+        ev[1].record()
+        prp_out = dd.build_prp(lut, off, ln, bus, pool, out=prp_out, ws=ws_prp)
+        ev[2].record()
+        if nq:
+            sp_out = dd.partition_by_queue(qid, nq, out=sp_out, ws=ws_sp)
+        ev[3].record()
+        return ev
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = []
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        events.append(step())
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    calls = ["mr_lookup", "build_prp", "partition_by_queue"]
+    per_call = {c: float(np.mean([e[k].elapsed_time(e[k + 1]) for e in events]))
+                for k, c in enumerate(calls)}
+    status = prp_out["status"].cpu().numpy()
+    ab = algorithmic_bytes(d, np)
+    step_bytes = ab["lookup"] * bool(d["regions"]) + ab["build_prp"] + ab["partition"] * bool(nq)
+    ms = elapsed / args.steps * 1e3
+    prp_ms = per_call["build_prp"]
+    achieved = ab["build_prp"] / (prp_ms * 1e-3) / 1e9
+
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+        if rec.get("source_sha256") == prp_source_hash() and rec.get("workload") == args.workload:
+            traffic = rec.get("traffic_bytes_per_launch")
+
+    result = {
+        "metric": "descriptor requests/sec (M/s) + achieved HBM GB/s vs MI355X peak",
+        "value": round(n * args.steps / elapsed / 1e6, 3),
+        "unit": "M req/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "u64",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "requests": n, "lut_entries": d["lut_entries"],
+                   "regions": d["regions"], "nqueues": nq, "list_pages": pool_pages,
+                   "calls": "mr_lookup + build_prp + partition_by_queue, one stream"},
+        "roofline": {"bound": "hbm", "kernel": "dmadesc_build_prp (count + scan + emit)",
+                     "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
+                     "algorithmic_bytes_per_launch": ab["build_prp"],
+                     "mean_launch_ms": round(prp_ms, 4)},
+        "per_call_ms": {k: round(v, 4) for k, v in per_call.items()},
+        "step_algorithmic_gbs": round(step_bytes / (ms * 1e-3) / 1e9, 1),
+        "step_frac_of_peak": round(step_bytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+        "prp_entries_per_s": round(ab["prp_entries"] * args.steps / elapsed, 1),
+        "refused_requests": int((status != 0).sum()),
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(args.workload, min(args.cpu_sample, n),
+                                              args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

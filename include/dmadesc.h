@@ -1,0 +1,198 @@
+/*
+ * dmadesc.h - batched DMA-descriptor building on AMD Instinct MI355X (gfx950).
+ *
+ * Three data-parallel operations turn a batch of I/O requests against GPU
+ * device memory into DMA descriptors:
+ *
+ *   dmadesc_mr_lookup          page-rounded containment lookup of each request
+ *                              range in a table of registered memory regions
+ *   dmadesc_build_prp          64 KiB GPU-page physical-address table -> 4 KiB
+ *                              NVMe PRP1/PRP2 and chained PRP lists
+ *   dmadesc_partition_by_queue stable split of the requests by destination queue
+ *
+ * Sources (web pages, cited by title and section):
+ *   [NCCL-26] "NCCL 专家课程 26：GPUDirect RDMA、DMA-BUF、MR 与注册缓存",
+ *             sections "IB Backend MR Cache" and
+ *             "Communicator User Registration Cache".
+ *   [UPCIE]   xNVMe "uPCIe CUDA" backend: introduction, "Memory Architecture",
+ *             "Choosing the GPU and Heap Sizes", "Limitations".
+ *   [MORI]    "mori通信库分析(一)——对称内存RDMA数据发送过程": the thread-scope
+ *             put kernel (ballot / find-first-set / shuffle grouping of lanes by
+ *             destination) and the warp-level WQE slot reservation.
+ *   [CUFRAMES] "Синхронизация: stream sync, не CUDA events": data written on a
+ *             stream is visible to others once that stream is synchronized.
+ *   [NVMe]    NVM Express Base Specification PRP rules (not on the pages).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Every pointer argument is caller-owned DEVICE memory on the current HIP
+ *    device unless marked "host". The library allocates nothing, keeps no
+ *    state between calls and retains no pointer after returning.
+ *  - Every call is asynchronous on `stream` (a hipStream_t; NULL = the
+ *    device's null stream). Outputs are valid once the caller synchronizes
+ *    that stream or orders later work behind it on the same stream
+ *    ([CUFRAMES]). Calls on distinct streams with distinct buffers may run
+ *    concurrently; calls that share a workspace must be ordered.
+ *  - Return value: 0 on success, or a negative errno value. On error nothing
+ *    is launched and no output is touched:
+ *      -EINVAL  null pointer where one is required, n >= 2^32, a parameter
+ *               out of range (stated per call), workspace too small;
+ *      -EIO     the HIP runtime refused a kernel launch.
+ *    Errors in individual requests are not call errors: they are reported
+ *    per request in an output column (stated per call).
+ *  - All arithmetic is exact unsigned 64-bit integer arithmetic; outputs are
+ *    bit-for-bit deterministic (no atomics decide any output position).
+ *  - `ws` is a caller-owned device workspace of at least
+ *    dmadesc_workspace_bytes(op, n, param) bytes (256-byte aligned). Its
+ *    contents on entry are ignored and on return are unspecified.
+ */
+#ifndef DMADESC_H
+#define DMADESC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Lookup outcome per request (column `kind` of dmadesc_mr_lookup). */
+enum dmadesc_kind {
+    DMADESC_MISS = 0,      /* no region contains the rounded range               */
+    DMADESC_EXACT = 1,     /* the rounded range equals a region                  */
+    DMADESC_CONTAINED = 2, /* the rounded range lies inside a region             */
+    DMADESC_INVALID = 3    /* zero length, or the range / rounded end wraps 2^64 */
+};
+
+/* PRP build status per request (column `status` of dmadesc_build_prp). */
+enum dmadesc_prp_status {
+    DMADESC_PRP_OK = 0,
+    DMADESC_PRP_EINVAL = 1, /* len == 0, off not a multiple of 4, or off+len wraps */
+    DMADESC_PRP_ERANGE = 2, /* off + len > lut_entries * 64 KiB (past the heap)     */
+    DMADESC_PRP_ENOSPC = 3  /* the request's list pages pass pool_pages            */
+};
+
+/* Operation codes for dmadesc_workspace_bytes. */
+enum dmadesc_op {
+    DMADESC_OP_MR_LOOKUP = 1,
+    DMADESC_OP_BUILD_PRP = 2,
+    DMADESC_OP_PARTITION = 3
+};
+
+/* Largest nqueues dmadesc_partition_by_queue accepts. */
+#define DMADESC_MAX_QUEUES 256u
+
+/*
+ * dmadesc_mr_lookup - page-rounded containment lookup.
+ *
+ * Defined by [NCCL-26] "IB Backend MR Cache": a range is widened to whole
+ * pages (base = address with the in-page bits cleared; page count =
+ * (address + size - base + page - 1) / page) and a registered region that
+ * fully contains the widened range is a hit; a partial overlap is a miss.
+ * "Communicator User Registration Cache" applies the same floor/cover
+ * rounding before its containment test; exact and contained ranges reuse the
+ * region's handle.
+ *
+ * Region table (device arrays, `nregions` entries, nregions < 2^31): sorted
+ * by start, non-overlapping (end[r] <= start[r+1]), start[r] < end[r]; end is
+ * exclusive. Abutting regions are allowed. A table that breaks these rules
+ * gives unspecified (but memory-safe) results.
+ *   reg_start  u64[nregions]   region start address
+ *   reg_end    u64[nregions]   region end address (exclusive)
+ *   reg_lkey   u32[nregions]   local key returned on a hit
+ * Requests: absolute address a = va_base + off[i], length len[i].
+ *   page_shift  log2 of the page size, 12..30 (12 = 4 KiB), else -EINVAL
+ * Outputs (u = per request, n entries each):
+ *   handle  i32  region index on a hit, -1 on MISS / INVALID
+ *   lkey    u32  reg_lkey[handle] on a hit, 0 otherwise
+ *   kind    u8   enum dmadesc_kind; EXACT iff both rounded bounds equal the
+ *                region's bounds
+ *   rbase   u64  rounded base (0 when INVALID)
+ *   rend    u64  rounded end, exclusive (0 when INVALID)
+ * Workspace: none (ws may be NULL).
+ */
+int dmadesc_mr_lookup(const uint64_t *reg_start, const uint64_t *reg_end,
+                      const uint32_t *reg_lkey, uint32_t nregions, uint32_t page_shift,
+                      const uint64_t *off, const uint64_t *len, uint64_t n, uint64_t va_base,
+                      int32_t *handle, uint32_t *lkey, uint8_t *kind,
+                      uint64_t *rbase, uint64_t *rend,
+                      void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * dmadesc_build_prp - GPU-page table -> NVMe PRP1/PRP2 and chained PRP lists.
+ *
+ * Defined by [UPCIE] introduction: one physical address per 64 KiB GPU page,
+ * and PRP entries at 4 KiB granularity from the sub-page offsets inside each
+ * 64 KiB entry; "Limitations": a list page holds 512 entries. Chaining follows
+ * [NVMe]: the last entry of every non-final list page points to the next one.
+ *
+ *   lut          u64[lut_entries]  physical address of GPU page k (heap bytes
+ *                [k*64 KiB, (k+1)*64 KiB)); lut_entries < 2^48, else -EINVAL.
+ *                The physical address of heap byte x is lut[x>>16] + (x&0xFFFF).
+ *   off, len     u64[n]            request heap offset and length in bytes
+ *   list_bus_base                  bus address of list page 0; must be a
+ *                                  multiple of 4096, else -EINVAL
+ *   list_pool    u64[pool_pages][512]  list pages; page s has bus address
+ *                                  list_bus_base + 4096*s. Only entries the
+ *                                  batch needs are written; entries past a
+ *                                  request's last entry in its final page and
+ *                                  pages >= *total_pages are not touched.
+ *   prp1, prp2   u64[n]            PRP1: physical address of the first byte.
+ *                                  PRP2: 0 for one 4 KiB page, the second
+ *                                  page's address for two, else the bus
+ *                                  address of the request's first list page.
+ *   status       u8[n]             enum dmadesc_prp_status; any non-OK request
+ *                                  gets prp1 = prp2 = 0 and no list entries.
+ *   total_pages  u64 (device scalar) list pages the whole batch needs: the
+ *                                  sum over requests not EINVAL/ERANGE. List
+ *                                  pages are handed out in request order, so
+ *                                  ENOSPC requests form a suffix of the
+ *                                  list-using requests and a pool of
+ *                                  *total_pages pages serves them all.
+ * Per request, with pages p = ((off & 4095) + len + 4095) >> 12, entries
+ * m = p - 1 and, for p >= 3, list pages L = ceil((m - 1) / 511).
+ * Workspace: dmadesc_workspace_bytes(DMADESC_OP_BUILD_PRP, n, 0).
+ */
+int dmadesc_build_prp(const uint64_t *lut, uint64_t lut_entries,
+                      const uint64_t *off, const uint64_t *len, uint64_t n,
+                      uint64_t list_bus_base, uint64_t *list_pool, uint64_t pool_pages,
+                      uint64_t *prp1, uint64_t *prp2, uint8_t *status,
+                      uint64_t *total_pages,
+                      void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * dmadesc_partition_by_queue - stable split of request indices by queue id.
+ *
+ * [MORI] groups a wave's lanes by destination with ballot / find-first-set /
+ * shuffle and reserves queue slots once per group; here every queue's
+ * requests are placed contiguously, in increasing request index.
+ *   qid       u32[n]           destination queue of each request
+ *   nqueues   1..DMADESC_MAX_QUEUES, else -EINVAL
+ *   perm      u32[n]           request indices grouped by queue; queue q's
+ *                              requests are perm[qoff[q] .. qoff[q+1]) in
+ *                              increasing index order
+ *   qoff      u64[nqueues + 2] bucket starts; bucket nqueues holds, in order,
+ *                              the requests whose qid >= nqueues; qoff[nqueues+1] = n
+ *   n_invalid u64 (device scalar) size of that overflow bucket
+ * Workspace: dmadesc_workspace_bytes(DMADESC_OP_PARTITION, n, nqueues).
+ */
+int dmadesc_partition_by_queue(const uint32_t *qid, uint64_t n, uint32_t nqueues,
+                               uint32_t *perm, uint64_t *qoff, uint64_t *n_invalid,
+                               void *ws, size_t ws_bytes, void *stream);
+
+/* Workspace bytes needed by `op` for n requests (`param` = nqueues for
+ * DMADESC_OP_PARTITION, ignored otherwise). Returns 0 for an unknown op or
+ * for an op that needs none. Host-only; launches nothing. */
+size_t dmadesc_workspace_bytes(int op, uint64_t n, uint32_t param);
+
+/* Static description of a return code (host-only). */
+const char *dmadesc_strerror(int err);
+
+/* Library ABI version (host-only). */
+int dmadesc_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DMADESC_H */

@@ -1,0 +1,174 @@
+"""dmadesc: batched DMA-descriptor building on AMD MI355X (gfx950).
+
+Thin binding over the C ABI of libdmadesc.so (include/dmadesc.h): argument
+marshalling only. Every step runs in the library's HIP kernels; PyTorch only
+provides device memory and the current stream. There is no CPU fallback: if
+the library cannot be loaded, importing the functions raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+from . import _build
+
+__all__ = ["mr_lookup", "build_prp", "partition_by_queue", "workspace_bytes",
+           "DmadescError", "lib", "LIB_PATH", "MAX_QUEUES",
+           "MISS", "EXACT", "CONTAINED", "INVALID",
+           "PRP_OK", "PRP_EINVAL", "PRP_ERANGE", "PRP_ENOSPC"]
+
+LIB_PATH = _build.LIB
+MAX_QUEUES = 256
+OP_MR_LOOKUP, OP_BUILD_PRP, OP_PARTITION = 1, 2, 3
+MISS, EXACT, CONTAINED, INVALID = 0, 1, 2, 3
+PRP_OK, PRP_EINVAL, PRP_ERANGE, PRP_ENOSPC = 0, 1, 2, 3
+
+_P = ctypes.c_void_p
+_U64 = ctypes.c_uint64
+_U32 = ctypes.c_uint32
+_SIZE = ctypes.c_size_t
+
+_EXPORTS = {
+    "dmadesc_mr_lookup": ([_P, _P, _P, _U32, _U32, _P, _P, _U64, _U64,
+                           _P, _P, _P, _P, _P, _P, _SIZE, _P], ctypes.c_int),
+    "dmadesc_build_prp": ([_P, _U64, _P, _P, _U64, _U64, _P, _U64,
+                           _P, _P, _P, _P, _P, _SIZE, _P], ctypes.c_int),
+    "dmadesc_partition_by_queue": ([_P, _U64, _U32, _P, _P, _P, _P, _SIZE, _P],
+                                   ctypes.c_int),
+    "dmadesc_workspace_bytes": ([ctypes.c_int, _U64, _U32], _SIZE),
+    "dmadesc_strerror": ([ctypes.c_int], ctypes.c_char_p),
+    "dmadesc_version": ([], ctypes.c_int),
+}
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Loads libdmadesc.so (building it in-tree first if it was never built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            _build.build()
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (args, res) in _EXPORTS.items():
+            fn = getattr(handle, name)
+            fn.argtypes = args
+            fn.restype = res
+        _lib = handle
+    return _lib
+
+
+class DmadescError(RuntimeError):
+    def __init__(self, func: str, rc: int):
+        msg = lib().dmadesc_strerror(rc).decode()
+        super().__init__(f"{func} returned {rc}: {msg}")
+        self.rc = rc
+
+
+def _check(func: str, rc: int) -> None:
+    if rc != 0:
+        raise DmadescError(func, rc)
+
+
+def _dev(t: torch.Tensor, dtype: torch.dtype, name: str, n: int | None = None) -> int:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name}: expected a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name}: must be a device tensor, got {t.device}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    if n is not None and t.numel() != n:
+        raise ValueError(f"{name}: expected {n} elements, got {t.numel()}")
+    return t.data_ptr() if t.numel() else 0
+
+
+def _stream(device: torch.device, stream) -> int:
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    return s.cuda_stream
+
+
+def workspace_bytes(op: int, n: int, param: int = 0) -> int:
+    return int(lib().dmadesc_workspace_bytes(op, n, param))
+
+
+def _workspace(op: int, n: int, param: int, device, ws):
+    need = workspace_bytes(op, n, param)
+    if ws is None:
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=device)
+    if ws.numel() < need:
+        raise ValueError(f"workspace needs {need} bytes, got {ws.numel()}")
+    return ws
+
+
+def mr_lookup(reg_start: torch.Tensor, reg_end: torch.Tensor, reg_lkey: torch.Tensor,
+              off: torch.Tensor, length: torch.Tensor, va_base: int = 0,
+              page_shift: int = 12, out: dict | None = None, stream=None) -> dict:
+    """Page-rounded containment lookup; returns dict(handle, lkey, kind, rbase, rend)."""
+    n, r = off.numel(), reg_start.numel()
+    dev = off.device
+    if out is None:
+        out = dict(handle=torch.empty(n, dtype=torch.int32, device=dev),
+                   lkey=torch.empty(n, dtype=torch.uint32, device=dev),
+                   kind=torch.empty(n, dtype=torch.uint8, device=dev),
+                   rbase=torch.empty(n, dtype=torch.uint64, device=dev),
+                   rend=torch.empty(n, dtype=torch.uint64, device=dev))
+    rc = lib().dmadesc_mr_lookup(
+        _dev(reg_start, torch.uint64, "reg_start", r), _dev(reg_end, torch.uint64, "reg_end", r),
+        _dev(reg_lkey, torch.uint32, "reg_lkey", r), r, page_shift,
+        _dev(off, torch.uint64, "off", n), _dev(length, torch.uint64, "len", n), n, va_base,
+        _dev(out["handle"], torch.int32, "handle", n), _dev(out["lkey"], torch.uint32, "lkey", n),
+        _dev(out["kind"], torch.uint8, "kind", n), _dev(out["rbase"], torch.uint64, "rbase", n),
+        _dev(out["rend"], torch.uint64, "rend", n), None, 0, _stream(dev, stream))
+    _check("dmadesc_mr_lookup", rc)
+    return out
+
+
+def build_prp(lut: torch.Tensor, off: torch.Tensor, length: torch.Tensor,
+              list_bus_base: int, pool: torch.Tensor, out: dict | None = None,
+              ws: torch.Tensor | None = None, stream=None) -> dict:
+    """GPU-page table -> PRP1/PRP2/status and chained lists in `pool`
+    (u64[pool_pages, 512]); returns dict(prp1, prp2, status, total_pages)."""
+    n = off.numel()
+    dev = off.device
+    if pool.dim() != 2 or pool.shape[1] != 512:
+        raise ValueError("pool must have shape [pool_pages, 512]")
+    if out is None:
+        out = dict(prp1=torch.empty(n, dtype=torch.uint64, device=dev),
+                   prp2=torch.empty(n, dtype=torch.uint64, device=dev),
+                   status=torch.empty(n, dtype=torch.uint8, device=dev),
+                   total_pages=torch.empty(1, dtype=torch.uint64, device=dev))
+    ws = _workspace(OP_BUILD_PRP, n, 0, dev, ws)
+    rc = lib().dmadesc_build_prp(
+        _dev(lut, torch.uint64, "lut"), lut.numel(),
+        _dev(off, torch.uint64, "off", n), _dev(length, torch.uint64, "len", n), n,
+        list_bus_base, _dev(pool, torch.uint64, "pool"), pool.shape[0],
+        _dev(out["prp1"], torch.uint64, "prp1", n), _dev(out["prp2"], torch.uint64, "prp2", n),
+        _dev(out["status"], torch.uint8, "status", n),
+        _dev(out["total_pages"], torch.uint64, "total_pages", 1),
+        ws.data_ptr(), ws.numel(), _stream(dev, stream))
+    _check("dmadesc_build_prp", rc)
+    return out
+
+
+def partition_by_queue(qid: torch.Tensor, nqueues: int, out: dict | None = None,
+                       ws: torch.Tensor | None = None, stream=None) -> dict:
+    """Stable split by queue id; returns dict(perm, qoff, n_invalid)."""
+    n = qid.numel()
+    dev = qid.device
+    if out is None:
+        out = dict(perm=torch.empty(n, dtype=torch.uint32, device=dev),
+                   qoff=torch.empty(nqueues + 2, dtype=torch.uint64, device=dev),
+                   n_invalid=torch.empty(1, dtype=torch.uint64, device=dev))
+    ws = _workspace(OP_PARTITION, n, nqueues, dev, ws)
+    rc = lib().dmadesc_partition_by_queue(
+        _dev(qid, torch.uint32, "qid", n), n, nqueues,
+        _dev(out["perm"], torch.uint32, "perm", n),
+        _dev(out["qoff"], torch.uint64, "qoff", nqueues + 2),
+        _dev(out["n_invalid"], torch.uint64, "n_invalid", 1),
+        ws.data_ptr(), ws.numel(), _stream(dev, stream))
+    _check("dmadesc_partition_by_queue", rc)
+    return out

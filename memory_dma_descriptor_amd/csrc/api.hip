@@ -1,0 +1,98 @@
+// api.hip - the C ABI of libdmadesc: argument validation, workspace sizing
+// and kernel launches. Every check here runs on the host before anything is
+// launched, so a rejected call touches no memory and needs no GPU.
+#include <errno.h>
+
+#include "dd_internal.h"
+#include "dmadesc.h"
+
+namespace {
+
+constexpr uint64_t kMaxN = 1ull << 32;           // indices are u32
+constexpr uint64_t kMaxLutEntries = 1ull << 48;  // heap < 2^64 bytes
+
+int launched(hipError_t e) { return e == hipSuccess ? 0 : -EIO; }
+
+}  // namespace
+
+extern "C" {
+
+int dmadesc_version(void) { return 1; }
+
+const char *dmadesc_strerror(int err)
+{
+    switch (err) {
+    case 0: return "success";
+    case -EINVAL: return "invalid argument (null pointer, size or parameter out of range, or workspace too small)";
+    case -EIO: return "the HIP runtime refused a kernel launch";
+    default: return "unknown error";
+    }
+}
+
+size_t dmadesc_workspace_bytes(int op, uint64_t n, uint32_t param)
+{
+    switch (op) {
+    case DMADESC_OP_MR_LOOKUP: return 0;
+    case DMADESC_OP_BUILD_PRP: return dd::ws_build_prp(n);
+    case DMADESC_OP_PARTITION:
+        if (param == 0 || param > DMADESC_MAX_QUEUES) return 0;
+        return dd::ws_partition(n, param);
+    default: return 0;
+    }
+}
+
+int dmadesc_mr_lookup(const uint64_t *reg_start, const uint64_t *reg_end,
+                      const uint32_t *reg_lkey, uint32_t nregions, uint32_t page_shift,
+                      const uint64_t *off, const uint64_t *len, uint64_t n, uint64_t va_base,
+                      int32_t *handle, uint32_t *lkey, uint8_t *kind,
+                      uint64_t *rbase, uint64_t *rend,
+                      void *ws, size_t ws_bytes, void *stream)
+{
+    (void)ws;
+    (void)ws_bytes;
+    if (page_shift < 12 || page_shift > 30) return -EINVAL;
+    if (n >= kMaxN || nregions >= (1u << 31)) return -EINVAL;
+    if (nregions > 0 && (!reg_start || !reg_end || !reg_lkey)) return -EINVAL;
+    if (n == 0) return 0;
+    if (!off || !len || !handle || !lkey || !kind || !rbase || !rend) return -EINVAL;
+    dd::LookupArgs a{reg_start, reg_end, reg_lkey, nregions, page_shift, off, len, n, va_base,
+                     handle, lkey, kind, rbase, rend};
+    return launched(dd::launch_mr_lookup(a, static_cast<hipStream_t>(stream)));
+}
+
+int dmadesc_build_prp(const uint64_t *lut, uint64_t lut_entries,
+                      const uint64_t *off, const uint64_t *len, uint64_t n,
+                      uint64_t list_bus_base, uint64_t *list_pool, uint64_t pool_pages,
+                      uint64_t *prp1, uint64_t *prp2, uint8_t *status,
+                      uint64_t *total_pages,
+                      void *ws, size_t ws_bytes, void *stream)
+{
+    if (n >= kMaxN || lut_entries >= kMaxLutEntries) return -EINVAL;
+    if (list_bus_base & 4095u) return -EINVAL;
+    if (!total_pages) return -EINVAL;
+    if (lut_entries > 0 && !lut) return -EINVAL;
+    if (pool_pages > 0 && !list_pool) return -EINVAL;
+    if (pool_pages > (~0ull >> 12)) return -EINVAL;          // pool byte size fits 64 bits
+    if (n > 0 && (!off || !len || !prp1 || !prp2 || !status)) return -EINVAL;
+    const size_t need = dd::ws_build_prp(n);
+    if (need > 0 && (!ws || ws_bytes < need)) return -EINVAL;
+    dd::PrpArgs a{lut, lut_entries, off, len, n, list_bus_base, list_pool, pool_pages,
+                  prp1, prp2, status, total_pages, ws};
+    return launched(dd::launch_build_prp(a, static_cast<hipStream_t>(stream)));
+}
+
+int dmadesc_partition_by_queue(const uint32_t *qid, uint64_t n, uint32_t nqueues,
+                               uint32_t *perm, uint64_t *qoff, uint64_t *n_invalid,
+                               void *ws, size_t ws_bytes, void *stream)
+{
+    if (nqueues == 0 || nqueues > DMADESC_MAX_QUEUES) return -EINVAL;
+    if (n >= kMaxN) return -EINVAL;
+    if (!qoff || !n_invalid) return -EINVAL;
+    if (n > 0 && (!qid || !perm)) return -EINVAL;
+    const size_t need = dd::ws_partition(n, nqueues);
+    if (n > 0 && (!ws || ws_bytes < need)) return -EINVAL;
+    dd::SplitArgs a{qid, n, nqueues, perm, qoff, n_invalid, ws};
+    return launched(dd::launch_partition(a, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,54 @@
+// dd_internal.h - launchers behind the C ABI (host side). The public entry
+// points in api.hip validate arguments and then call these.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace dd {
+
+struct LookupArgs {
+    const uint64_t *reg_start, *reg_end;
+    const uint32_t *reg_lkey;
+    uint32_t nregions, page_shift;
+    const uint64_t *off, *len;
+    uint64_t n, va_base;
+    int32_t *handle;
+    uint32_t *lkey;
+    uint8_t *kind;
+    uint64_t *rbase, *rend;
+};
+
+struct PrpArgs {
+    const uint64_t *lut;
+    uint64_t lut_entries;
+    const uint64_t *off, *len;
+    uint64_t n, list_bus_base;
+    uint64_t *pool;
+    uint64_t pool_pages;
+    uint64_t *prp1, *prp2;
+    uint8_t *status;
+    uint64_t *total_pages;
+    void *ws;
+};
+
+struct SplitArgs {
+    const uint32_t *qid;
+    uint64_t n;
+    uint32_t nqueues;
+    uint32_t *perm;
+    uint64_t *qoff, *n_invalid;
+    void *ws;
+};
+
+hipError_t launch_mr_lookup(const LookupArgs &a, hipStream_t s);
+hipError_t launch_build_prp(const PrpArgs &a, hipStream_t s);
+hipError_t launch_partition(const SplitArgs &a, hipStream_t s);
+
+size_t ws_build_prp(uint64_t n);
+size_t ws_partition(uint64_t n, uint32_t nqueues);
+
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+}  // namespace dd

@@ -1,0 +1,145 @@
+"""Shared helpers for the GPU parity tests: run the C-ABI library through its
+binding and compare with the oracle, column by column, bit for bit."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import memory_dma_descriptor_amd as dd
+import oracle
+
+CANARY = 0xCCCC_CCCC_CCCC_CCCC
+CANARY_I64 = np.uint64(CANARY).astype(np.int64).item()
+
+
+def dev(a: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def host(t: torch.Tensor) -> np.ndarray:
+    return t.cpu().numpy()
+
+
+def say(msg: str) -> None:
+    print(msg, flush=True)
+
+
+# ----------------------------------------------------------------- lookup ---
+
+def gpu_lookup(start, end, lkey, off, ln, va_base=0, page_shift=12):
+    out = dd.mr_lookup(dev(np.asarray(start, np.uint64)), dev(np.asarray(end, np.uint64)),
+                       dev(np.asarray(lkey, np.uint32)), dev(np.asarray(off, np.uint64)),
+                       dev(np.asarray(ln, np.uint64)), va_base=va_base, page_shift=page_shift)
+    torch.cuda.synchronize()
+    return {k: host(v) for k, v in out.items()}
+
+
+def assert_lookup_equal(o, g, ctx=""):
+    for k in ("handle", "lkey", "kind", "rbase", "rend"):
+        if not np.array_equal(o[k], g[k]):
+            bad = np.nonzero(o[k] != g[k])[0]
+            raise AssertionError(f"{ctx} lookup column {k}: {bad.size} mismatches, first at "
+                                 f"{bad[0]}: oracle {o[k][bad[0]]} gpu {g[k][bad[0]]}")
+
+
+def check_lookup(start, end, lkey, off, ln, va_base=0, page_shift=12, ctx=""):
+    o = oracle.mr_lookup(start, end, lkey, off, ln, va_base=va_base, page_shift=page_shift)
+    g = gpu_lookup(start, end, lkey, off, ln, va_base=va_base, page_shift=page_shift)
+    assert_lookup_equal(o, g, ctx)
+    return o, g
+
+
+# -------------------------------------------------------------------- PRP ---
+
+def gpu_prp(lut, off, ln, bus, pool_pages):
+    """Runs dmadesc_build_prp on a canary-filled pool; returns (outputs as
+    numpy, the device pool)."""
+    pool = torch.empty((pool_pages, 512), dtype=torch.uint64, device="cuda")
+    pool.view(torch.int64).fill_(CANARY_I64)
+    out = dd.build_prp(dev(np.asarray(lut, np.uint64)), dev(np.asarray(off, np.uint64)),
+                       dev(np.asarray(ln, np.uint64)), bus, pool)
+    torch.cuda.synchronize()
+    g = {k: host(v) for k, v in out.items()}
+    g["total"] = int(g.pop("total_pages")[0])
+    return g, pool
+
+
+def assert_prp_columns_equal(o, g, ctx=""):
+    for k in ("prp1", "prp2", "status"):
+        if not np.array_equal(o[k], g[k]):
+            bad = np.nonzero(o[k] != g[k])[0]
+            raise AssertionError(f"{ctx} PRP column {k}: {bad.size} mismatches, first at "
+                                 f"{bad[0]}: oracle {o[k][bad[0]]:#x} gpu {g[k][bad[0]]:#x}")
+    assert o["total"] == g["total"], (ctx, o["total"], g["total"])
+
+
+def check_prp_full(lut, off, ln, bus, pool_pages, ctx=""):
+    """Whole-pool comparison: both pools start as canary, so equal pools mean
+    the GPU wrote exactly the oracle's entries and nothing else."""
+    o_pool = np.full((pool_pages, 512), CANARY, dtype=np.uint64)
+    o = oracle.build_prp(lut, off, ln, bus, pool_pages, pool=o_pool)
+    g, pool = gpu_prp(lut, off, ln, bus, pool_pages)
+    assert_prp_columns_equal(o, g, ctx)
+    gp = host(pool)
+    if not np.array_equal(o_pool, gp):
+        bad = np.argwhere(o_pool != gp)
+        s, p = bad[0]
+        raise AssertionError(f"{ctx} pool: {len(bad)} mismatching entries, first at page {s} "
+                             f"entry {p}: oracle {o_pool[s, p]:#x} gpu {gp[s, p]:#x}")
+    return o, g
+
+
+def check_prp_sampled(lut, off, ln, bus, pool_pages, sample, ctx=""):
+    """Full-size check: every PRP1/PRP2/status and the total against the
+    oracle run without a pool; list pages of `sample` requests against the
+    oracle run on each request alone at its slot; pool pages past the total
+    untouched."""
+    o = oracle.build_prp(lut, off, ln, bus, pool_pages, pool=None)
+    g, pool = gpu_prp(lut, off, ln, bus, pool_pages)
+    assert_prp_columns_equal(o, g, ctx)
+    lists = [int(i) for i in sample
+             if g["status"][i] == 0 and g["prp2"][i] >= bus
+             and (g["prp2"][i] - bus) // 4096 < min(pool_pages, g["total"])
+             and (ln[i] + (off[i] % 4096) + 4095) // 4096 >= 3]
+    slots, want = [], []
+    for i in lists:
+        slot = (int(g["prp2"][i]) - bus) // 4096
+        one = oracle.build_prp(lut, off[i:i + 1], ln[i:i + 1], bus + slot * 4096,
+                               pool_pages - slot, pool=None)
+        lp = one["total"]
+        page = np.full((lp, 512), CANARY, dtype=np.uint64)
+        oracle.build_prp(lut, off[i:i + 1], ln[i:i + 1], bus + slot * 4096, lp, pool=page)
+        slots.extend(range(slot, slot + lp))
+        want.append(page)
+    if slots:
+        idx = torch.tensor(slots, dtype=torch.int64, device="cuda")
+        got = host(pool.view(torch.int64)[idx]).view(np.uint64)
+        want = np.concatenate(want)
+        if not np.array_equal(got, want):
+            bad = np.argwhere(got != want)
+            raise AssertionError(f"{ctx} sampled list pages: {len(bad)} mismatches")
+    tail = pool.view(torch.int64)[min(g["total"], pool_pages):]
+    assert bool((tail == CANARY_I64).all()), f"{ctx}: pool pages past the total were written"
+    return o, g, len(lists)
+
+
+# ------------------------------------------------------------------ split ---
+
+def gpu_split(qid, nq):
+    out = dd.partition_by_queue(dev(np.asarray(qid, np.uint32)), nq)
+    torch.cuda.synchronize()
+    g = {k: host(v) for k, v in out.items()}
+    g["n_invalid"] = int(g["n_invalid"][0])
+    return g
+
+
+def check_split(qid, nq, ctx=""):
+    o = oracle.partition(qid, nq)
+    g = gpu_split(qid, nq)
+    for k in ("perm", "qoff"):
+        if not np.array_equal(o[k], g[k]):
+            bad = np.nonzero(o[k] != g[k])[0]
+            raise AssertionError(f"{ctx} split column {k}: {bad.size} mismatches, first at "
+                                 f"{bad[0]}: oracle {o[k][bad[0]]} gpu {g[k][bad[0]]}")
+    assert o["n_invalid"] == g["n_invalid"], ctx
+    return o, g

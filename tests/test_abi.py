@@ -1,0 +1,110 @@
+"""The C-ABI library: loads, exports what include/dmadesc.h declares, and
+rejects bad arguments on the host (these calls return before any GPU work,
+so they run without a GPU)."""
+import ctypes
+import errno
+import os
+import re
+
+import pytest
+
+import memory_dma_descriptor_amd as dd
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    names = set()
+    for fn in os.listdir(os.path.join(ROOT, "include")):
+        if fn.endswith(".h"):
+            src = open(os.path.join(ROOT, "include", fn), encoding="utf-8").read()
+            src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+            names |= set(re.findall(r"\b(dmadesc_\w+)\s*\(", src))
+    return names
+
+
+def test_exports_every_declared_symbol():
+    names = _declared()
+    assert {"dmadesc_mr_lookup", "dmadesc_build_prp", "dmadesc_partition_by_queue"} <= names
+    lib = ctypes.CDLL(dd.LIB_PATH)
+    for n in sorted(names):
+        assert hasattr(lib, n), n
+
+
+def test_version_and_strerror():
+    lib = dd.lib()
+    assert lib.dmadesc_version() == 1
+    assert b"invalid" in lib.dmadesc_strerror(-errno.EINVAL)
+    assert lib.dmadesc_strerror(0) == b"success"
+
+
+def test_workspace_sizes():
+    ws = dd.workspace_bytes
+    assert ws(dd.OP_MR_LOOKUP, 1 << 20) == 0
+    assert ws(dd.OP_BUILD_PRP, 0) == 0
+    assert ws(dd.OP_BUILD_PRP, 1) == 256
+    assert ws(dd.OP_BUILD_PRP, 16 << 20) >= (16 << 20) // 256 * 8
+    assert ws(dd.OP_PARTITION, 100, 0) == 0            # nqueues 0 is invalid
+    assert ws(dd.OP_PARTITION, 100, 257) == 0          # above the maximum
+    assert ws(dd.OP_PARTITION, 16 << 20, 64) >= 65 * (16 << 20) // 2048 * 4
+    assert ws(99, 10, 0) == 0
+
+
+EINVAL = -errno.EINVAL
+NULL = None
+
+# The probes below pass dummy pointers that host validation must reject. They
+# run only where no GPU is visible, so a validation bug can never turn one of
+# them into a launch on a real device.
+import torch  # noqa: E402
+
+no_gpu_only = pytest.mark.skipif(torch.cuda.device_count() > 0,
+                                 reason="dummy-pointer probes run only without a GPU")
+P = 0x1000   # a non-null pointer value never dereferenced: every call below is
+             # rejected by host validation before anything is launched
+
+
+@no_gpu_only
+def test_lookup_rejects_bad_arguments():
+    f = dd.lib().dmadesc_mr_lookup
+    ok = [P, P, P, 4, 12, P, P, 8, 0, P, P, P, P, P, NULL, 0, NULL]
+    for k, bad in [(4, 11), (4, 31), (7, 1 << 32), (3, 1 << 31), (0, NULL), (5, NULL),
+                   (9, NULL), (13, NULL)]:
+        args = list(ok)
+        args[k] = bad
+        assert f(*args) == EINVAL, (k, bad)
+
+
+@no_gpu_only
+def test_build_prp_rejects_bad_arguments():
+    f = dd.lib().dmadesc_build_prp
+    ok = [P, 16, P, P, 8, 0x10000, P, 4, P, P, P, P, P, 1 << 20, NULL]
+    for k, bad in [(5, 0x10008), (1, 1 << 48), (4, 1 << 32), (11, NULL), (0, NULL),
+                   (6, NULL), (2, NULL), (8, NULL), (12, NULL), (13, 8)]:
+        args = list(ok)
+        args[k] = bad
+        assert f(*args) == EINVAL, (k, bad)
+
+
+@no_gpu_only
+def test_partition_rejects_bad_arguments():
+    f = dd.lib().dmadesc_partition_by_queue
+    ok = [P, 100, 4, P, P, P, P, 1 << 20, NULL]
+    for k, bad in [(2, 0), (2, 257), (1, 1 << 32), (4, NULL), (5, NULL), (0, NULL),
+                   (3, NULL), (6, NULL), (7, 16)]:
+        args = list(ok)
+        args[k] = bad
+        assert f(*args) == EINVAL, (k, bad)
+
+
+def test_empty_lookup_is_a_no_op():
+    # n == 0 with valid parameters launches nothing and succeeds.
+    f = dd.lib().dmadesc_mr_lookup
+    assert f(NULL, NULL, NULL, 0, 12, NULL, NULL, 0, 0, NULL, NULL, NULL, NULL, NULL,
+             NULL, 0, NULL) == 0
+
+
+@pytest.mark.parametrize("name", ["mr_lookup", "build_prp", "partition_by_queue"])
+def test_binding_names_match_abi(name):
+    assert callable(getattr(dd, name))
+    assert f"dmadesc_{name}" in _declared()
