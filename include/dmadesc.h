@@ -132,11 +132,15 @@ int dmadesc_mr_lookup(const uint64_t *reg_start, const uint64_t *reg_end,
  *   off, len     u64[n]            request heap offset and length in bytes
  *   list_bus_base                  bus address of list page 0; must be a
  *                                  multiple of 4096, else -EINVAL
- *   list_pool    u64[pool_pages][512]  list pages; page s has bus address
- *                                  list_bus_base + 4096*s. Only entries the
- *                                  batch needs are written; entries past a
- *                                  request's last entry in its final page and
- *                                  pages >= *total_pages are not touched.
+ *   list_pool    u64[pool_pages][512], 16-byte aligned (else -EINVAL): list
+ *                                  pages; page s has bus address
+ *                                  list_bus_base + 4096*s. Entries the batch
+ *                                  needs are written; after a request's last
+ *                                  entry, words up to the next multiple of 16
+ *                                  words of its final list page may be
+ *                                  written (with 0; a controller never reads
+ *                                  them); every other word, and every page
+ *                                  >= *total_pages, is left untouched.
  *   prp1, prp2   u64[n]            PRP1: physical address of the first byte.
  *                                  PRP2: 0 for one 4 KiB page, the second
  *                                  page's address for two, else the bus
@@ -151,7 +155,10 @@ int dmadesc_mr_lookup(const uint64_t *reg_start, const uint64_t *reg_end,
  *                                  *total_pages pages serves them all.
  * Per request, with pages p = ((off & 4095) + len + 4095) >> 12, entries
  * m = p - 1 and, for p >= 3, list pages L = ceil((m - 1) / 511).
- * Workspace: dmadesc_workspace_bytes(DMADESC_OP_BUILD_PRP, n, 0).
+ * Workspace: dmadesc_workspace_bytes(DMADESC_OP_BUILD_PRP, n, 0); its
+ * first 8 bytes hold, on return, a block counter and a count of bounded
+ * waits that expired (always 0 when blocks make progress; read it after
+ * synchronizing to check).
  */
 int dmadesc_build_prp(const uint64_t *lut, uint64_t lut_entries,
                       const uint64_t *off, const uint64_t *len, uint64_t n,

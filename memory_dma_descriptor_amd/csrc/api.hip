@@ -72,6 +72,7 @@ int dmadesc_build_prp(const uint64_t *lut, uint64_t lut_entries,
     if (!total_pages) return -EINVAL;
     if (lut_entries > 0 && !lut) return -EINVAL;
     if (pool_pages > 0 && !list_pool) return -EINVAL;
+    if (reinterpret_cast<uintptr_t>(list_pool) & 15u) return -EINVAL;    // 16-byte stores
     if (pool_pages > (~0ull >> 12)) return -EINVAL;          // pool byte size fits 64 bits
     if (n > 0 && (!off || !len || !prp1 || !prp2 || !status)) return -EINVAL;
     const size_t need = dd::ws_build_prp(n);

@@ -8,31 +8,71 @@
 // the last entry of every non-final list page points to the next list page,
 // so a non-final page carries 511 data entries and the final one up to 512.
 //
-// Three kernels, stream-ordered, no atomics:
-//   k_prp_count  one lane per request: validity and list pages L; per-block sum
-//   k_prp_scan   one workgroup: exclusive scan of the block sums -> first list
-//                page of every block, and the batch total
-//   k_prp_emit   per block of 256 requests: PRP1/PRP2/status, then the list
-//                entries, load-balanced over entries (not requests): the
-//                block's data entries form one index space that all 256 lanes
-//                walk in steps of 256, each lane finding its request by a
-//                binary search over the per-request entry offsets in LDS. The
-//                table entries the block needs are staged in LDS once per
-//                window of kWin GPU pages (each request's pages form one
-//                contiguous run of the table), so every entry reads LDS, not
-//                global memory.
+// One pass, one kernel (after a small workspace-clearing kernel):
+//
+//  * Request phase, 2048 requests per block, item k of thread t being request
+//    block_base + 256 k + t (so every column load is contiguous per wave):
+//    validity, 4 KiB page count, list pages L. List pages are handed out in
+//    request order by a device-wide exclusive scan done in the same pass
+//    with decoupled look-back: each block publishes its aggregate, then
+//    reads its predecessors' published values until it meets an inclusive
+//    prefix. Block order comes from an atomic ticket, so a block only ever
+//    waits on blocks that are already running; waits are bounded.
+//  * Because a request's list pages are consecutive slots, its written
+//    entries (data entries plus chain pointers) are ONE contiguous run of
+//    E = m + L - 1 words starting at word 512 * slot of the pool: word q of
+//    the run is the chain pointer when q % 512 == 511 on a non-final page,
+//    else data entry j = q - q / 512. No division is needed anywhere.
+//  * List phase, per wave and per item round: the wave's 64 consecutive
+//    requests of that round are emitted in groups
+//    of 4 consecutive words (32 bytes), load-balanced over groups, not
+//    requests: lane k of each step takes group c + k, finds its request by a
+//    6-step search over the wave's group offsets in LDS, and writes its 4
+//    words with two 16-byte stores. Four consecutive 4 KiB pages lie in at
+//    most two 64 KiB GPU pages, so each group reads at most two table
+//    entries; a wave's 64 groups read one short run of the table per
+//    request, which the L1/L2 serve.
 #include "dd_device.hpp"
 #include "dd_internal.h"
 
 namespace dd {
 namespace {
 
-constexpr int kTile = 256;        // requests per block (= threads)
-constexpr int kScanThreads = 1024;
-constexpr int kScanItems = 16;
-constexpr int kWin = 2048;        // GPU pages staged per window (16 KiB LDS)
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / kWave;
+constexpr int kItems = 4;                     // requests per thread
+constexpr int kTile = kThreads * kItems;      // requests per block
+// A request's list run is written in whole units of kPadWords words (a
+// multiple of 4 dividing 512, so padding never leaves the request's final
+// list page); words past the last entry are written as 0.
+constexpr uint64_t kPadWords = 16;
+// GPU pages of the table staged in LDS per wave and round (4 KiB).
+constexpr int kTileFrames = 512;
+constexpr uint64_t kFlagAgg = 1ull << 62;     // status word: aggregate published
+constexpr uint64_t kFlagInc = 2ull << 62;     // status word: inclusive prefix published
+constexpr uint64_t kValue = (1ull << 62) - 1;
+constexpr uint32_t kMaxPolls = 1u << 22;      // bounded wait (about seconds)
 
 enum : uint8_t { kOk = 0, kEinval = 1, kErange = 2, kEnospc = 3 };
+
+// Workspace layout: a 256-byte header, then one status word per block.
+struct Header {
+    uint32_t ticket;     // next block order
+    uint32_t timeouts;   // look-back waits that hit the bound (never expected)
+};
+constexpr size_t kHeaderBytes = 256;
+
+typedef uint64_t u64x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint64_t load_status(const uint64_t *p)
+{
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ void store_status(uint64_t *p, uint64_t v)
+{
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
 // Status and 4 KiB page count of one request.
 __device__ __forceinline__ uint8_t decode(uint64_t o, uint64_t l, uint64_t heap,
@@ -45,168 +85,222 @@ __device__ __forceinline__ uint8_t decode(uint64_t o, uint64_t l, uint64_t heap,
     return kOk;
 }
 
-// List pages of a request with `pages` 4 KiB pages: entries m = pages - 1,
-// pages L = ceil((m - 1) / 511) when pages >= 3.
-__device__ __forceinline__ uint64_t list_pages(uint64_t pages)
+// Exclusive prefix of the list pages of all blocks before `b` (called by one
+// whole wave; lane k inspects block b-1-k of the current window).
+__device__ uint64_t look_back(uint64_t *status, int64_t b, uint32_t *timeouts)
 {
-    return pages >= 3 ? (pages - 2 + 510) / 511 : 0;
-}
-
-__global__ __launch_bounds__(kTile) void k_prp_count(
-    const uint64_t *__restrict__ off, const uint64_t *__restrict__ len, uint64_t n,
-    uint64_t heap, uint64_t *__restrict__ partial)
-{
-    __shared__ uint64_t wsum[kTile / kWave];
-    const uint64_t i = (uint64_t)blockIdx.x * kTile + threadIdx.x;
-    uint64_t lp = 0;
-    if (i < n) {
-        uint64_t pages;
-        if (decode(off[i], len[i], heap, pages) == kOk) lp = list_pages(pages);
-    }
-    lp = wave_sum(lp);
-    if (lane() == 0) wsum[wave()] = lp;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        uint64_t s = 0;
-        for (int k = 0; k < kTile / kWave; ++k) s += wsum[k];
-        partial[blockIdx.x] = s;
-    }
-}
-
-// Single workgroup: in-place exclusive scan of partial[0..nb), total -> *total.
-__global__ __launch_bounds__(kScanThreads) void k_prp_scan(
-    uint64_t *__restrict__ partial, uint64_t nb, uint64_t *__restrict__ total)
-{
-    __shared__ uint64_t scratch[kScanThreads / kWave];
-    uint64_t carry = 0;
-    for (uint64_t base = 0; base < nb; base += (uint64_t)kScanThreads * kScanItems) {
-        const uint64_t b0 = base + (uint64_t)threadIdx.x * kScanItems;
-        uint64_t v[kScanItems];
-        uint64_t s = 0;
-#pragma unroll
-        for (int k = 0; k < kScanItems; ++k) {
-            v[k] = (b0 + k < nb) ? partial[b0 + k] : 0;
-            s += v[k];
+    const int ln = lane();
+    uint64_t excl = 0;
+    int64_t top = b - 1;
+    uint32_t polls = 0;
+    for (;;) {
+        const int64_t idx = top - ln;
+        uint64_t s = idx >= 0 ? load_status(status + idx) : kFlagInc;   // before block 0: 0
+        while (__ballot((s >> 62) == 0) != 0) {
+            if (++polls > kMaxPolls) {
+                if (ln == 0) atomicAdd(timeouts, 1u);
+                return excl;
+            }
+            __builtin_amdgcn_s_sleep(2);
+            if ((s >> 62) == 0) s = load_status(status + idx);
         }
-        uint64_t chunk;
-        uint64_t run = carry + block_excl_scan<kScanThreads>(s, scratch, &chunk);
-#pragma unroll
-        for (int k = 0; k < kScanItems; ++k) {
-            if (b0 + k < nb) partial[b0 + k] = run;
-            run += v[k];
+        const uint64_t inc = __ballot((s >> 62) == 2);
+        if (inc != 0) {
+            const int first = __ffsll((unsigned long long)inc) - 1;   // nearest inclusive
+            excl += wave_sum(ln <= first ? (s & kValue) : 0ull);
+            return excl;
         }
-        carry += chunk;
+        excl += wave_sum(s & kValue);
+        top -= kWave;
     }
-    if (threadIdx.x == 0) *total = carry;
 }
 
-__global__ __launch_bounds__(kTile) void k_prp_emit(
+__global__ void k_prp_clear(uint64_t *ws_words, uint64_t words)
+{
+    for (uint64_t k = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; k < words;
+         k += (uint64_t)gridDim.x * blockDim.x)
+        ws_words[k] = 0;
+}
+
+// Per-wave table of one round of 64 requests, in LDS.
+struct RoundTable {
+    uint64_t goff[kWave + 1];   // exclusive prefix of 4-word groups
+    uint64_t foff[kWave + 1];   // exclusive prefix of staged GPU pages
+    uint64_t xb[kWave];         // heap offset of data entry 0 (4 KiB page 1)
+    uint64_t word[kWave];       // first pool word (512 * slot)
+    uint64_t ent[kWave];        // words holding entries or pointers (m + L - 1)
+    uint64_t plim[kWave];       // 512 * (L - 1): chain pointers lie below this
+    uint64_t lut[kTileFrames];  // staged table entries of the round's requests
+};
+
+__device__ __forceinline__ void wave_sync_lds()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Writes the list runs of the wave's 64 requests of one round. Lane k's
+// request is described by (xb, word, ent, lp); ent == 0 for no list.
+__device__ __forceinline__ void emit_round(RoundTable &T, uint64_t xb, uint64_t word, uint64_t ent,
+                                           uint64_t lp, uint64_t last_frame,
+                                           const uint64_t *__restrict__ lut,
+                                           uint64_t *__restrict__ pool, uint64_t bus)
+{
+    const int ln = lane();
+    const uint64_t groups = ((ent + kPadWords - 1) / kPadWords) * (kPadWords / 4);
+    const uint64_t ginc = wave_incl_scan(groups);
+    const uint64_t gtot = __shfl(ginc, kWave - 1, kWave);
+    if (gtot == 0) return;                                   // uniform per wave
+    const uint64_t frames = ent ? last_frame - (xb >> 16) + 1 : 0;
+    const uint64_t finc = wave_incl_scan(frames);
+    const uint64_t ftot = __shfl(finc, kWave - 1, kWave);
+    const bool staged = ftot <= (uint64_t)kTileFrames;      // uniform per wave
+    T.goff[ln] = ginc - groups;
+    T.foff[ln] = finc - frames;
+    if (ln == kWave - 1) {
+        T.goff[kWave] = ginc;
+        T.foff[kWave] = finc;
+    }
+    T.xb[ln] = xb;
+    T.word[ln] = word;
+    T.ent[ln] = ent;
+    T.plim[ln] = lp ? (lp - 1) << 9 : 0;
+    wave_sync_lds();
+    if (staged) {
+        // Each request's data entries read one contiguous run of the table.
+        for (uint64_t j = ln; j < ftot; j += kWave) {
+            const int r = owner_of<kWave>(T.foff, j);
+            T.lut[j] = lut[(T.xb[r] >> 16) + (j - T.foff[r])];
+        }
+        wave_sync_lds();
+    }
+    for (uint64_t g = ln; g < gtot; g += kWave) {
+        const int r = owner_of<kWave>(T.goff, g);
+        const uint64_t q = (g - T.goff[r]) << 2;             // first word of the group
+        const uint64_t e = T.ent[r];
+        const uint64_t page = q >> 9;
+        const uint64_t w0 = T.word[r];
+        const uint64_t xr = T.xb[r];
+        const uint64_t x0 = xr + ((q - page) << 12);         // data entry q - page
+        const bool has_ptr = ((q & 511u) == 508u) && (q < T.plim[r]);
+        const uint64_t left = e > q ? e - q : 0;             // 0 for a padding-only group
+        const uint32_t nd = has_ptr ? 3u : (uint32_t)(left < 4 ? left : 4);
+        const uint64_t f = x0 >> 16;
+        const bool two = nd && (((x0 + ((uint64_t)(nd - 1) << 12)) >> 16) != f);
+        uint64_t l0 = 0, l1 = 0;
+        if (nd) {
+            if (staged) {
+                const uint64_t fs = T.foff[r] + f - (xr >> 16);
+                l0 = T.lut[fs];
+                l1 = two ? T.lut[fs + 1] : l0;
+            } else {
+                l0 = lut[f];
+                l1 = two ? lut[f + 1] : l0;
+            }
+        }
+        uint64_t v[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const uint64_t x = x0 + ((uint64_t)k << 12);
+            const uint64_t d = (((x >> 16) != f) ? l1 : l0) + (x & 0xFFFFu);
+            v[k] = (uint32_t)k < nd ? d : 0;                 // padding words are 0
+        }
+        if (has_ptr) v[3] = bus + (((w0 >> 9) + page + 1) << 12);
+        uint64_t *dst = pool + w0 + q;
+        *reinterpret_cast<u64x2 *>(dst) = u64x2{v[0], v[1]};
+        *reinterpret_cast<u64x2 *>(dst + 2) = u64x2{v[2], v[3]};
+    }
+    wave_sync_lds();                                         // the next round rewrites T
+}
+
+__global__ __launch_bounds__(kThreads, 4) void k_prp_build(
     const uint64_t *__restrict__ lut, uint64_t heap,
     const uint64_t *__restrict__ off, const uint64_t *__restrict__ len, uint64_t n,
-    uint64_t bus, uint64_t *__restrict__ pool, uint64_t pool_pages,
+    uint64_t nblocks, uint64_t bus, uint64_t *__restrict__ pool, uint64_t pool_pages,
     uint64_t *__restrict__ prp1, uint64_t *__restrict__ prp2,
-    uint8_t *__restrict__ status, const uint64_t *__restrict__ block_slot)
+    uint8_t *__restrict__ status, uint64_t *__restrict__ total,
+    Header *__restrict__ hdr, uint64_t *__restrict__ bstat)
 {
-    __shared__ uint64_t s_moff[kTile + 1];   // exclusive prefix of data entries
-    __shared__ uint64_t s_foff[kTile + 1];   // exclusive prefix of staged GPU pages
-    __shared__ uint64_t s_pb[kTile];         // heap offset of the request's 4 KiB page 0
-    __shared__ uint64_t s_slot[kTile];       // first list page
-    __shared__ uint64_t s_lp[kTile];         // list pages
-    __shared__ uint64_t s_lut[kWin];
-    __shared__ uint64_t s_red[kTile / kWave];
-    __shared__ uint64_t s_bound[2];
+    __shared__ uint64_t s_red[kWaves];
+    __shared__ uint64_t s_bid, s_excl;
+    __shared__ RoundTable s_round[kWaves];
 
-    const int t = threadIdx.x;
-    const uint64_t i = (uint64_t)blockIdx.x * kTile + t;
+    const int t = threadIdx.x, w = wave(), ln = lane();
+    if (t == 0) s_bid = atomicAdd(&hdr->ticket, 1u);
+    __syncthreads();
+    const uint64_t b = s_bid;
+    const uint64_t base = b * kTile;
 
-    uint64_t o = 0, l = 0, pages = 0;
-    uint8_t st = kEinval;
-    if (i < n) {
-        o = off[i];
-        l = len[i];
-        st = decode(o, l, heap, pages);
+    // ---- request phase: item k of thread t is request base + k*256 + t ----
+    uint64_t o[kItems], l[kItems], pre[kItems];
+#pragma unroll
+    for (int k = 0; k < kItems; ++k) {
+        const uint64_t i = base + (uint64_t)k * kThreads + t;
+        o[k] = i < n ? off[i] : 0;
+        l[k] = i < n ? len[i] : 0;                   // len 0 decodes as invalid
     }
-    const uint64_t lp = (st == kOk) ? list_pages(pages) : 0;
-    uint64_t lp_tot;
-    const uint64_t slot = block_slot[blockIdx.x] + block_excl_scan<kTile>(lp, s_red, &lp_tot);
-    if (lp != 0 && slot + lp > pool_pages) st = kEnospc;     // refused; still took its slots
-    const bool lists = (st == kOk) && lp != 0;
-
-    const uint64_t pb = o & ~4095ull;
-    const uint64_t fa = (pb + 4096) >> 16;                    // GPU page of 4 KiB page 1
-    const uint64_t m = lists ? pages - 1 : 0;
-    const uint64_t fr = lists ? ((o + l - 1) >> 16) - fa + 1 : 0;
-    uint64_t m_tot, f_tot;
-    const uint64_t moff = block_excl_scan<kTile>(m, s_red, &m_tot);
-    const uint64_t foff = block_excl_scan<kTile>(fr, s_red, &f_tot);
-    s_moff[t] = moff;
-    s_foff[t] = foff;
-    if (t == 0) {
-        s_moff[kTile] = m_tot;
-        s_foff[kTile] = f_tot;
-    }
-    s_pb[t] = pb;
-    s_slot[t] = slot;
-    s_lp[t] = lp;
-
-    if (i < n) {
-        uint64_t p1 = 0, p2 = 0;
-        if (st == kOk) {
-            p1 = lut[o >> 16] + (o & 0xFFFFu);
-            if (pages == 2) {
-                const uint64_t x = pb + 4096;
-                p2 = lut[x >> 16] + (x & 0xFFFFu);
-            } else if (pages >= 3) {
-                p2 = bus + slot * 4096;
-            }
+    // PRP1, a two-page PRP2 and the status do not depend on the list pages,
+    // so they are written before the scan and overlap it. A request later
+    // refused for lack of pool pages is rewritten below.
+#pragma unroll
+    for (int k = 0; k < kItems; ++k) {
+        const uint64_t i = base + (uint64_t)k * kThreads + t;
+        uint64_t pages;
+        const uint8_t st = decode(o[k], l[k], heap, pages);
+        const uint64_t x = (o[k] & ~4095ull) + 4096;
+        if (i < n) {
+            prp1[i] = st == kOk ? lut[o[k] >> 16] + (o[k] & 0xFFFFu) : 0;
+            if (pages < 3) prp2[i] = (st == kOk && pages == 2) ? lut[x >> 16] + (x & 0xFFFFu) : 0;
+            status[i] = st;
         }
-        prp1[i] = p1;
-        prp2[i] = p2;
-        status[i] = st;
+    }
+    uint64_t agg = 0;
+#pragma unroll
+    for (int k = 0; k < kItems; ++k) {
+        uint64_t pages;
+        const uint8_t st = decode(o[k], l[k], heap, pages);
+        const uint64_t lp = (st == kOk && pages >= 3) ? (pages - 2 + 510) / 511 : 0;
+        uint64_t tot;
+        pre[k] = agg + block_excl_scan<kThreads>(lp, s_red, &tot);
+        agg += tot;
+    }
+    if (w == 0) {
+        uint64_t excl = 0;
+        if (b == 0) {
+            if (ln == 0) store_status(bstat, kFlagInc | agg);
+        } else {
+            if (ln == 0) store_status(bstat + b, kFlagAgg | agg);
+            excl = look_back(bstat, (int64_t)b, &hdr->timeouts);
+            if (ln == 0) store_status(bstat + b, kFlagInc | (excl + agg));
+        }
+        if (ln == 0) {
+            s_excl = excl;
+            if (b == nblocks - 1) *total = excl + agg;
+        }
     }
     __syncthreads();
-    if (m_tot == 0) return;                                    // uniform
+    const uint64_t excl = s_excl;
 
-    for (uint64_t w0 = 0; w0 < f_tot; w0 += kWin) {
-        const uint64_t wn = (f_tot - w0 < (uint64_t)kWin) ? f_tot - w0 : (uint64_t)kWin;
-        // Stage the table entries of GPU-page positions [w0, w0 + wn).
-        for (uint64_t j = t; j < wn; j += kTile) {
-            const uint64_t g = w0 + j;
-            const int r = owner_of<kTile>(s_foff, g);
-            s_lut[j] = lut[((s_pb[r] + 4096) >> 16) + (g - s_foff[r])];
-        }
-        // Entry range whose GPU pages fall in this window: first entry at or
-        // after GPU-page position w0 and w0 + kWin.
-        if (t < 2) {
-            const uint64_t g = w0 + (t ? (uint64_t)kWin : 0);
-            uint64_t e = m_tot;
-            if (g < f_tot) {
-                const int r = owner_of<kTile>(s_foff, g);
-                const uint64_t frame = ((s_pb[r] + 4096) >> 16) + (g - s_foff[r]);
-                const uint64_t start = frame << 16;
-                const uint64_t j = (start <= s_pb[r] + 4096) ? 0 : (start - s_pb[r]) / 4096 - 1;
-                e = s_moff[r] + j;
+#pragma unroll 1
+    for (int k = 0; k < kItems; ++k) {
+        const uint64_t i = base + (uint64_t)k * kThreads + t;
+        uint64_t pages;
+        uint8_t st = decode(o[k], l[k], heap, pages);
+        const uint64_t lp = (st == kOk && pages >= 3) ? (pages - 2 + 510) / 511 : 0;
+        const uint64_t slot = excl + pre[k];
+        if (lp != 0 && slot + lp > pool_pages) st = kEnospc;   // refused; its slots stay taken
+        if (i < n && lp != 0) {
+            prp2[i] = st == kOk ? bus + (slot << 12) : 0;
+            if (st == kEnospc) {
+                prp1[i] = 0;
+                status[i] = kEnospc;
             }
-            s_bound[t] = e;
         }
-        __syncthreads();
-        const uint64_t e_hi = s_bound[1];
-        for (uint64_t e = s_bound[0] + t; e < e_hi; e += kTile) {
-            const int r = owner_of<kTile>(s_moff, e);
-            const uint64_t j = e - s_moff[r];                   // data entry j = page j+1
-            const uint64_t pb_r = s_pb[r];
-            const uint64_t x = pb_r + 4096 * (j + 1);
-            const uint64_t g = s_foff[r] + (x >> 16) - ((pb_r + 4096) >> 16);
-            const uint64_t v = s_lut[g - w0] + (x & 0xFFFFu);
-            const uint64_t lp_r = s_lp[r];
-            uint64_t tp = j / 511;
-            if (tp > lp_r - 1) tp = lp_r - 1;
-            const uint64_t pos = j - 511 * tp;
-            const uint64_t sl = s_slot[r] + tp;
-            pool[sl * 512 + pos] = v;
-            if (pos == 510 && tp + 1 < lp_r) pool[sl * 512 + 511] = bus + (sl + 1) * 4096;
-        }
-        __syncthreads();
+        const bool lists = (st == kOk) && lp != 0;
+        emit_round(s_round[w], (o[k] & ~4095ull) + 4096, slot << 9,
+                   lists ? (pages - 1) + (lp - 1) : 0, lists ? lp : 0,
+                   (o[k] + l[k] - 1) >> 16, lut, pool, bus);
     }
 }
 
@@ -214,26 +308,30 @@ __global__ __launch_bounds__(kTile) void k_prp_emit(
 
 size_t ws_build_prp(uint64_t n)
 {
+    if (n == 0) return 0;
     const uint64_t nb = (n + kTile - 1) / kTile;
-    return align256(nb * sizeof(uint64_t));
+    return align256(kHeaderBytes + nb * sizeof(uint64_t));
 }
 
 hipError_t launch_build_prp(const PrpArgs &a, hipStream_t s)
 {
     const uint64_t heap = a.lut_entries << 16;
     const uint64_t nb = (a.n + kTile - 1) / kTile;
-    uint64_t *partial = static_cast<uint64_t *>(a.ws);
-    if (nb > 0) {
-        hipLaunchKernelGGL(k_prp_count, dim3((unsigned)nb), dim3(kTile), 0, s,
-                           a.off, a.len, a.n, heap, partial);
+    if (nb == 0) {
+        // Nothing to build; the batch needs no list pages.
+        hipLaunchKernelGGL(k_prp_clear, dim3(1), dim3(64), 0, s, a.total_pages, (uint64_t)1);
+        return hipGetLastError();
     }
-    hipLaunchKernelGGL(k_prp_scan, dim3(1), dim3(kScanThreads), 0, s, partial, nb,
-                       a.total_pages);
-    if (nb > 0) {
-        hipLaunchKernelGGL(k_prp_emit, dim3((unsigned)nb), dim3(kTile), 0, s,
-                           a.lut, heap, a.off, a.len, a.n, a.list_bus_base, a.pool,
-                           a.pool_pages, a.prp1, a.prp2, a.status, partial);
-    }
+    Header *hdr = static_cast<Header *>(a.ws);
+    uint64_t *bstat = reinterpret_cast<uint64_t *>(static_cast<char *>(a.ws) + kHeaderBytes);
+    const uint64_t words = kHeaderBytes / sizeof(uint64_t) + nb;
+    uint64_t cblocks = (words + 255) / 256;
+    if (cblocks > 1024) cblocks = 1024;
+    hipLaunchKernelGGL(k_prp_clear, dim3((unsigned)cblocks), dim3(256), 0, s,
+                       static_cast<uint64_t *>(a.ws), words);
+    hipLaunchKernelGGL(k_prp_build, dim3((unsigned)nb), dim3(kThreads), 0, s,
+                       a.lut, heap, a.off, a.len, a.n, nb, a.list_bus_base, a.pool,
+                       a.pool_pages, a.prp1, a.prp2, a.status, a.total_pages, hdr, bstat);
     return hipGetLastError();
 }
 

@@ -10,6 +10,37 @@ import oracle
 
 CANARY = 0xCCCC_CCCC_CCCC_CCCC
 CANARY_I64 = np.uint64(CANARY).astype(np.int64).item()
+# The library may write the words after a request's last list entry, up to
+# the next multiple of PAD_WORDS words inside that request's final list page
+# (their contents are unspecified); every other pool word it must leave alone.
+PAD_WORDS = 16
+
+
+def padding_spans(prp2, status, off, ln, bus, slot_base=0):
+    """(page, first word, end word) of the words after each list's last entry
+    that the library may write, from the oracle's PRP2 and status."""
+    off = np.asarray(off, np.uint64)
+    ln = np.asarray(ln, np.uint64)
+    pages = ((off & np.uint64(4095)) + ln + np.uint64(4095)) >> np.uint64(12)
+    sel = np.nonzero((status == 0) & (pages >= 3))[0]
+    spans = []
+    for i in sel:
+        m = int(pages[i]) - 1
+        lp = (m - 1 + 510) // 511
+        final_words = m - 511 * (lp - 1)
+        end = min(512, -(-final_words // PAD_WORDS) * PAD_WORDS)
+        if end > final_words:
+            page = (int(prp2[i]) - bus) // 4096 + lp - 1 - slot_base
+            spans.append((page, final_words, end))
+    return spans
+
+
+def mask_padding(a, b, spans):
+    """Makes the padding words of both pools equal before they are compared."""
+    for page, lo, hi in spans:
+        if 0 <= page < a.shape[0]:
+            a[page, lo:hi] = 0
+            b[page, lo:hi] = 0
 
 
 def dev(a: np.ndarray) -> torch.Tensor:
@@ -56,11 +87,18 @@ def gpu_prp(lut, off, ln, bus, pool_pages):
     numpy, the device pool)."""
     pool = torch.empty((pool_pages, 512), dtype=torch.uint64, device="cuda")
     pool.view(torch.int64).fill_(CANARY_I64)
+    n = len(off)
+    ws = torch.full((max(dd.workspace_bytes(dd.OP_BUILD_PRP, n), 8),), 0xAB,
+                    dtype=torch.uint8, device="cuda")
     out = dd.build_prp(dev(np.asarray(lut, np.uint64)), dev(np.asarray(off, np.uint64)),
-                       dev(np.asarray(ln, np.uint64)), bus, pool)
+                       dev(np.asarray(ln, np.uint64)), bus, pool, ws=ws)
     torch.cuda.synchronize()
     g = {k: host(v) for k, v in out.items()}
     g["total"] = int(g.pop("total_pages")[0])
+    if n:
+        # workspace header: blocks that ran, and bounded waits that expired
+        blocks, timeouts = host(ws[:8]).view(np.uint32)
+        assert 1 <= blocks <= n and timeouts == 0, (blocks, timeouts)
     return g, pool
 
 
@@ -81,6 +119,7 @@ def check_prp_full(lut, off, ln, bus, pool_pages, ctx=""):
     g, pool = gpu_prp(lut, off, ln, bus, pool_pages)
     assert_prp_columns_equal(o, g, ctx)
     gp = host(pool)
+    mask_padding(o_pool, gp, padding_spans(o["prp2"], o["status"], off, ln, bus))
     if not np.array_equal(o_pool, gp):
         bad = np.argwhere(o_pool != gp)
         s, p = bad[0]
@@ -101,7 +140,7 @@ def check_prp_sampled(lut, off, ln, bus, pool_pages, sample, ctx=""):
              if g["status"][i] == 0 and g["prp2"][i] >= bus
              and (g["prp2"][i] - bus) // 4096 < min(pool_pages, g["total"])
              and (ln[i] + (off[i] % 4096) + 4095) // 4096 >= 3]
-    slots, want = [], []
+    slots, want, spans = [], [], []
     for i in lists:
         slot = (int(g["prp2"][i]) - bus) // 4096
         one = oracle.build_prp(lut, off[i:i + 1], ln[i:i + 1], bus + slot * 4096,
@@ -109,12 +148,16 @@ def check_prp_sampled(lut, off, ln, bus, pool_pages, sample, ctx=""):
         lp = one["total"]
         page = np.full((lp, 512), CANARY, dtype=np.uint64)
         oracle.build_prp(lut, off[i:i + 1], ln[i:i + 1], bus + slot * 4096, lp, pool=page)
+        spans += [(pg + len(slots), lo, hi) for pg, lo, hi in
+                  padding_spans(one["prp2"], one["status"], off[i:i + 1], ln[i:i + 1],
+                                bus + slot * 4096)]
         slots.extend(range(slot, slot + lp))
         want.append(page)
     if slots:
         idx = torch.tensor(slots, dtype=torch.int64, device="cuda")
         got = host(pool.view(torch.int64)[idx]).view(np.uint64)
         want = np.concatenate(want)
+        mask_padding(got, want, spans)
         if not np.array_equal(got, want):
             bad = np.argwhere(got != want)
             raise AssertionError(f"{ctx} sampled list pages: {len(bad)} mismatches")

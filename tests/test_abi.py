@@ -42,8 +42,8 @@ def test_workspace_sizes():
     ws = dd.workspace_bytes
     assert ws(dd.OP_MR_LOOKUP, 1 << 20) == 0
     assert ws(dd.OP_BUILD_PRP, 0) == 0
-    assert ws(dd.OP_BUILD_PRP, 1) == 256
-    assert ws(dd.OP_BUILD_PRP, 16 << 20) >= (16 << 20) // 256 * 8
+    assert ws(dd.OP_BUILD_PRP, 1) == 512                # header + one block word
+    assert ws(dd.OP_BUILD_PRP, 16 << 20) >= 256 + (16 << 20) // 2048 * 8
     assert ws(dd.OP_PARTITION, 100, 0) == 0            # nqueues 0 is invalid
     assert ws(dd.OP_PARTITION, 100, 257) == 0          # above the maximum
     assert ws(dd.OP_PARTITION, 16 << 20, 64) >= 65 * (16 << 20) // 2048 * 4
@@ -80,7 +80,7 @@ def test_build_prp_rejects_bad_arguments():
     f = dd.lib().dmadesc_build_prp
     ok = [P, 16, P, P, 8, 0x10000, P, 4, P, P, P, P, P, 1 << 20, NULL]
     for k, bad in [(5, 0x10008), (1, 1 << 48), (4, 1 << 32), (11, NULL), (0, NULL),
-                   (6, NULL), (2, NULL), (8, NULL), (12, NULL), (13, 8)]:
+                   (6, NULL), (6, P + 8), (2, NULL), (8, NULL), (12, NULL), (13, 8)]:
         args = list(ok)
         args[k] = bad
         assert f(*args) == EINVAL, (k, bad)

@@ -84,7 +84,9 @@ def test_mixed_three_calls_one_stream():
     g = {k: gc.host(v) for k, v in pr.items()}
     g["total"] = int(g.pop("total_pages")[0])
     gc.assert_prp_columns_equal(o_p, g, "mixed/stream")
-    assert np.array_equal(gc.host(pool), o_pool)
+    gp = gc.host(pool)
+    gc.mask_padding(o_pool, gp, gc.padding_spans(o_p["prp2"], o_p["status"], d["off"], d["len"], BUS))
+    assert np.array_equal(gp, o_pool)
     assert np.array_equal(gc.host(sp["perm"]), o_s["perm"])
     assert np.array_equal(gc.host(sp["qoff"]), o_s["qoff"])
 
@@ -278,3 +280,6 @@ def test_binding_rejects_bad_arguments():
         dd.build_prp(z, z, z, 0x1008, pool)
     with pytest.raises(dd.DmadescError):
         dd.mr_lookup(z, z, gc.dev(np.zeros(4, np.uint32)), z, z, page_shift=11)
+    skewed = torch.empty(2 * 512 + 1, dtype=torch.uint64, device="cuda")[1:].view(2, 512)
+    with pytest.raises(dd.DmadescError):                 # pool not 16-byte aligned
+        dd.build_prp(z, z, z, 0x1000, skewed)
