@@ -133,6 +133,28 @@ struct RoundTable {
     uint64_t lut[kTileFrames];  // staged table entries of the round's requests
 };
 
+// Compact round table for rounds whose lists are all shorter than 2^24
+// words: every offset inside a list then fits 32-bit arithmetic.
+constexpr uint64_t kFastWords = 1ull << 24;
+struct ReqRec {                 // 32 bytes, read with two 16-byte LDS loads
+    uint64_t word;              // first pool word (512 * slot)
+    uint64_t f0;                // GPU page holding data entry 0
+    uint32_t ent;               // words holding entries or pointers
+    uint32_t plim;              // 512 * (L - 1): chain pointers lie below this
+    uint32_t fbase;             // staged-tile index of GPU page f0
+    uint32_t ph;                // 4 KiB page of data entry 0 within GPU page f0
+};
+struct FastTable {
+    uint32_t goff[kWave + 1];   // exclusive prefix of 4-word groups
+    uint32_t foff[kWave + 1];   // exclusive prefix of staged GPU pages
+    ReqRec rec[kWave];
+    uint64_t lut[kTileFrames];
+};
+union RoundLds {
+    RoundTable wide;
+    FastTable fast;
+};
+
 __device__ __forceinline__ void wave_sync_lds()
 {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -142,7 +164,7 @@ __device__ __forceinline__ void wave_sync_lds()
 
 // Writes the list runs of the wave's 64 requests of one round. Lane k's
 // request is described by (xb, word, ent, lp); ent == 0 for no list.
-__device__ __forceinline__ void emit_round(RoundTable &T, uint64_t xb, uint64_t word, uint64_t ent,
+__device__ __forceinline__ void emit_round_wide(RoundTable &T, uint64_t xb, uint64_t word, uint64_t ent,
                                            uint64_t lp, uint64_t last_frame,
                                            const uint64_t *__restrict__ lut,
                                            uint64_t *__restrict__ pool, uint64_t bus)
@@ -214,6 +236,132 @@ __device__ __forceinline__ void emit_round(RoundTable &T, uint64_t xb, uint64_t 
     wave_sync_lds();                                         // the next round rewrites T
 }
 
+// Writes one group of a fast round. Data entry j of a request lies in GPU
+// page f0 + ((ph + j) >> 4) at in-page offset ((ph + j) & 15) * 4 KiB.
+template <bool kStaged>
+__device__ __forceinline__ void fast_group(const FastTable &T, uint32_t g, int r,
+                                           const uint64_t *__restrict__ lut,
+                                           uint64_t *__restrict__ pool, uint64_t bus)
+{
+    const ReqRec R = T.rec[r];
+    const uint32_t q = (g - T.goff[r]) << 2;                 // first word of the group
+    const uint32_t page = q >> 9;
+    const uint32_t j0 = q - page;                            // its data entry
+    const bool has_ptr = ((q & 511u) == 508u) && (q < R.plim);
+    const uint32_t left = R.ent > q ? R.ent - q : 0;         // 0 for a padding-only group
+    const uint32_t nd = has_ptr ? 3u : (left < 4u ? left : 4u);
+    const uint32_t t0 = R.ph + j0;
+    const uint32_t fi = t0 >> 4, u = t0 & 15u;
+    uint64_t l0 = 0, l1 = 0;
+    if (nd) {
+        const bool two = (u + nd - 1u) >= 16u;
+        if (kStaged) {
+            l0 = T.lut[R.fbase + fi];
+            l1 = two ? T.lut[R.fbase + fi + 1] : l0;
+        } else {
+            l0 = lut[R.f0 + fi];
+            l1 = two ? lut[R.f0 + fi + 1] : l0;
+        }
+    }
+    uint64_t v[4];
+#pragma unroll
+    for (uint32_t k = 0; k < 4; ++k) {
+        const uint32_t wk = u + k;
+        const uint64_t d = (wk >= 16u ? l1 : l0) + (uint64_t)((wk & 15u) << 12);
+        v[k] = k < nd ? d : 0;                               // padding words are 0
+    }
+    if (has_ptr) v[3] = bus + (((R.word >> 9) + page + 1) << 12);
+    uint64_t *dst = pool + R.word + q;
+    *reinterpret_cast<u64x2 *>(dst) = u64x2{v[0], v[1]};
+    *reinterpret_cast<u64x2 *>(dst + 2) = u64x2{v[2], v[3]};
+}
+
+// Writes the groups of a fast round, two per lane per step: groups g and
+// g + 64 are searched in lockstep so that their LDS reads overlap.
+template <bool kStaged>
+__device__ __forceinline__ void fast_groups(const FastTable &T, uint32_t gtot,
+                                            const uint64_t *__restrict__ lut,
+                                            uint64_t *__restrict__ pool, uint64_t bus)
+{
+    const uint32_t ln = lane();
+    for (uint32_t c = 0; c < gtot; c += 2 * kWave) {
+        const uint32_t ga = c + ln, gb = c + kWave + ln;
+        const uint32_t ka = ga < gtot ? ga : gtot - 1;       // clamped search keys
+        const uint32_t kb = gb < gtot ? gb : gtot - 1;
+        int ra = 0, rb = 0;
+#pragma unroll
+        for (int step = kWave / 2; step > 0; step >>= 1) {
+            const uint32_t pa = T.goff[ra + step], pbv = T.goff[rb + step];
+            ra = (pa <= ka) ? ra + step : ra;
+            rb = (pbv <= kb) ? rb + step : rb;
+        }
+        if (ga < gtot) fast_group<kStaged>(T, ga, ra, lut, pool, bus);
+        if (gb < gtot) fast_group<kStaged>(T, gb, rb, lut, pool, bus);
+    }
+}
+
+__device__ __forceinline__ void emit_round_fast(FastTable &T, uint64_t xb, uint64_t word,
+                                                uint32_t ent, uint64_t lp, uint64_t last_frame,
+                                                const uint64_t *__restrict__ lut,
+                                                uint64_t *__restrict__ pool, uint64_t bus)
+{
+    const int ln = lane();
+    const uint32_t groups = ((ent + (uint32_t)kPadWords - 1) / (uint32_t)kPadWords) *
+                            (uint32_t)(kPadWords / 4);
+    const uint32_t ginc = wave_incl_scan(groups);
+    const uint32_t gtot = __shfl(ginc, kWave - 1, kWave);
+    if (gtot == 0) return;                                   // uniform per wave
+    const uint64_t f0 = xb >> 16;
+    const uint32_t frames = ent ? (uint32_t)(last_frame - f0 + 1) : 0;
+    const uint32_t finc = wave_incl_scan(frames);
+    const uint32_t ftot = __shfl(finc, kWave - 1, kWave);
+    T.goff[ln] = ginc - groups;
+    T.foff[ln] = finc - frames;
+    if (ln == kWave - 1) {
+        T.goff[kWave] = ginc;
+        T.foff[kWave] = finc;
+    }
+    T.rec[ln] = ReqRec{word, f0, ent, lp ? (uint32_t)((lp - 1) << 9) : 0u, finc - frames,
+                       (uint32_t)((xb >> 12) & 15u)};
+    wave_sync_lds();
+    if (ftot <= (uint32_t)kTileFrames) {
+        // Four reads in flight per lane before any lands in LDS.
+        for (uint32_t j0 = 0; j0 < ftot; j0 += 4 * kWave) {
+            uint64_t v[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const uint32_t j = j0 + u * kWave + ln;
+                const uint32_t jj = j < ftot ? j : 0;
+                const int r = owner_of<kWave>(T.foff, jj);
+                v[u] = lut[T.rec[r].f0 + (jj - T.foff[r])];
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const uint32_t j = j0 + u * kWave + ln;
+                if (j < ftot) T.lut[j] = v[u];
+            }
+        }
+        wave_sync_lds();
+        fast_groups<true>(T, gtot, lut, pool, bus);
+    } else {
+        fast_groups<false>(T, gtot, lut, pool, bus);
+    }
+    wave_sync_lds();                                         // the next round rewrites T
+}
+
+// Writes the list runs of the wave's 64 requests of one round (lane k: one
+// request; ent == 0 for no list).
+__device__ __forceinline__ void emit_round(RoundLds &T, uint64_t xb, uint64_t word, uint64_t ent,
+                                           uint64_t lp, uint64_t last_frame,
+                                           const uint64_t *__restrict__ lut,
+                                           uint64_t *__restrict__ pool, uint64_t bus)
+{
+    if (__ballot(ent >= kFastWords) == 0)
+        emit_round_fast(T.fast, xb, word, (uint32_t)ent, lp, last_frame, lut, pool, bus);
+    else
+        emit_round_wide(T.wide, xb, word, ent, lp, last_frame, lut, pool, bus);
+}
+
 __global__ __launch_bounds__(kThreads, 4) void k_prp_build(
     const uint64_t *__restrict__ lut, uint64_t heap,
     const uint64_t *__restrict__ off, const uint64_t *__restrict__ len, uint64_t n,
@@ -224,7 +372,7 @@ __global__ __launch_bounds__(kThreads, 4) void k_prp_build(
 {
     __shared__ uint64_t s_red[kWaves];
     __shared__ uint64_t s_bid, s_excl;
-    __shared__ RoundTable s_round[kWaves];
+    __shared__ RoundLds s_round[kWaves];
 
     const int t = threadIdx.x, w = wave(), ln = lane();
     if (t == 0) s_bid = atomicAdd(&hdr->ticket, 1u);
@@ -242,17 +390,47 @@ __global__ __launch_bounds__(kThreads, 4) void k_prp_build(
     }
     // PRP1, a two-page PRP2 and the status do not depend on the list pages,
     // so they are written before the scan and overlap it. A request later
-    // refused for lack of pool pages is rewritten below.
+    // refused for lack of pool pages is rewritten below. The table reads are
+    // branch-free (index 0 stands in for a request that needs none) so that
+    // all of them are in flight together.
+    if (heap != 0) {
+        uint64_t i1[kItems], i2[kItems], v1[kItems], v2[kItems];
 #pragma unroll
-    for (int k = 0; k < kItems; ++k) {
-        const uint64_t i = base + (uint64_t)k * kThreads + t;
-        uint64_t pages;
-        const uint8_t st = decode(o[k], l[k], heap, pages);
-        const uint64_t x = (o[k] & ~4095ull) + 4096;
-        if (i < n) {
-            prp1[i] = st == kOk ? lut[o[k] >> 16] + (o[k] & 0xFFFFu) : 0;
-            if (pages < 3) prp2[i] = (st == kOk && pages == 2) ? lut[x >> 16] + (x & 0xFFFFu) : 0;
-            status[i] = st;
+        for (int k = 0; k < kItems; ++k) {
+            uint64_t pages;
+            const uint8_t st = decode(o[k], l[k], heap, pages);
+            const uint64_t x = (o[k] & ~4095ull) + 4096;
+            i1[k] = st == kOk ? o[k] >> 16 : 0;
+            i2[k] = (st == kOk && pages == 2) ? x >> 16 : 0;
+        }
+#pragma unroll
+        for (int k = 0; k < kItems; ++k) {
+            v1[k] = lut[i1[k]];
+            v2[k] = lut[i2[k]];
+        }
+#pragma unroll
+        for (int k = 0; k < kItems; ++k) {
+            const uint64_t i = base + (uint64_t)k * kThreads + t;
+            uint64_t pages;
+            const uint8_t st = decode(o[k], l[k], heap, pages);
+            if (i < n) {
+                prp1[i] = st == kOk ? v1[k] + (o[k] & 0xFFFFu) : 0;
+                if (pages < 3) prp2[i] = (st == kOk && pages == 2) ?
+                    v2[k] + (((o[k] & ~4095ull) + 4096) & 0xFFFFu) : 0;
+                status[i] = st;
+            }
+        }
+    } else {
+#pragma unroll
+        for (int k = 0; k < kItems; ++k) {                  // no heap: every request is ERANGE
+            const uint64_t i = base + (uint64_t)k * kThreads + t;
+            uint64_t pages;
+            const uint8_t st = decode(o[k], l[k], heap, pages);
+            if (i < n) {
+                prp1[i] = 0;
+                prp2[i] = 0;
+                status[i] = st;
+            }
         }
     }
     uint64_t agg = 0;

@@ -7,13 +7,20 @@
 // is a hit (exact when both bounds coincide); partial overlap is a miss.
 //
 // Layout: one lane per request over structure-of-arrays columns, so each
-// column load/store of a wave is one contiguous 64-element run. Every block
-// first stages a splitter array -- every S-th region start, S a power of two
-// chosen so at most kMaxSplitters fit in LDS -- then each lane does a
-// branch-free binary search over the splitters in LDS followed by one over
-// the <= S starts of the selected run in global memory (L2-resident: the
-// whole table is at most a few MiB). Blocks loop over the batch so the
-// splitter staging is paid once per block, not per 256 requests.
+// column load/store of a wave is one contiguous 64-element run. Two kernels:
+//
+//  * k_lookup_lds, for tables that fit in LDS (20 bytes per region; MI355X
+//    has 160 KiB of LDS per CU): every block copies the whole table into
+//    LDS once and then answers requests in a grid-stride loop; the search
+//    and the start/end/lkey reads of the chosen region are all LDS reads, so
+//    no random global gathers reach the texture address unit.
+//  * k_lookup_split, for larger tables: every block stages every S-th
+//    region start (S a power of two, at most kMaxSplitters splitters = 64 KiB)
+//    in LDS; a lane searches the splitters in LDS, then the <= S starts of the
+//    selected run in global memory (the table is L2-resident).
+//
+// Both searches are branch-free: the trip count depends only on the length
+// searched, so lanes of a wave never diverge in them.
 #include "dd_device.hpp"
 #include "dd_internal.h"
 
@@ -21,10 +28,10 @@ namespace dd {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kThreadsLds = 512;
 constexpr uint32_t kMaxSplitters = 8192;   // 64 KiB of LDS
 
-// Index of the last element <= key in a[0..cnt), given a[0] <= key; the trip
-// count depends only on cnt, so lanes with equal cnt never diverge.
+// Index of the last element <= key in a[0..cnt), given a[0] <= key.
 template <typename Ptr>
 __device__ __forceinline__ uint64_t last_le(Ptr a, uint64_t cnt, uint64_t key)
 {
@@ -37,7 +44,73 @@ __device__ __forceinline__ uint64_t last_le(Ptr a, uint64_t cnt, uint64_t key)
     return idx;
 }
 
-__global__ __launch_bounds__(kThreads) void k_mr_lookup(
+// Validity and page-rounded bounds of one request; returns false for
+// INVALID (empty, start wraps, end wraps, or rounded end wraps).
+__device__ __forceinline__ bool round_range(uint64_t va_base, uint64_t o, uint64_t l,
+                                            uint64_t in_page, uint64_t &lo, uint64_t &hi)
+{
+    const uint64_t a = va_base + o;
+    const uint64_t last = a + l - 1;
+    const bool bad = (l == 0) | (a < va_base) | (l > ~a) | ((last | in_page) == ~0ull);
+    lo = bad ? 0 : (a & ~in_page);             // page floor of the start
+    hi = bad ? 0 : (last | in_page) + 1;       // page cover of the end
+    return !bad;
+}
+
+__device__ __forceinline__ void put(uint64_t i, int32_t h, uint32_t key, uint8_t kd,
+                                    uint64_t lo, uint64_t hi, int32_t *__restrict__ handle,
+                                    uint32_t *__restrict__ lkey, uint8_t *__restrict__ kind,
+                                    uint64_t *__restrict__ rbase, uint64_t *__restrict__ rend)
+{
+    handle[i] = h;
+    lkey[i] = key;
+    kind[i] = kd;
+    rbase[i] = lo;
+    rend[i] = hi;
+}
+
+__global__ __launch_bounds__(kThreadsLds) void k_lookup_lds(
+    const uint64_t *__restrict__ rs, const uint64_t *__restrict__ re,
+    const uint32_t *__restrict__ rk, uint32_t nregions, uint32_t page_shift,
+    const uint64_t *__restrict__ off, const uint64_t *__restrict__ len,
+    uint64_t n, uint64_t va_base,
+    int32_t *__restrict__ handle, uint32_t *__restrict__ lkey,
+    uint8_t *__restrict__ kind, uint64_t *__restrict__ rbase,
+    uint64_t *__restrict__ rend)
+{
+    extern __shared__ uint64_t lds[];
+    uint64_t *s_start = lds;
+    uint64_t *s_end = lds + nregions;
+    uint32_t *s_key = reinterpret_cast<uint32_t *>(lds + 2 * (uint64_t)nregions);
+    for (uint32_t k = threadIdx.x; k < nregions; k += kThreadsLds) {
+        s_start[k] = rs[k];
+        s_end[k] = re[k];
+        s_key[k] = rk[k];
+    }
+    __syncthreads();
+
+    const uint64_t in_page = (1ull << page_shift) - 1;
+    const uint64_t stride = (uint64_t)gridDim.x * kThreadsLds;
+    for (uint64_t i = (uint64_t)blockIdx.x * kThreadsLds + threadIdx.x; i < n; i += stride) {
+        uint64_t lo, hi;
+        const bool ok = round_range(va_base, off[i], len[i], in_page, lo, hi);
+        int32_t h = -1;
+        uint32_t key = 0;
+        uint8_t kd = ok ? 0 : 3;                 // MISS : INVALID
+        if (ok && nregions > 0 && s_start[0] <= lo) {
+            const uint32_t r = (uint32_t)last_le(s_start, nregions, lo);
+            const uint64_t e = s_end[r];
+            if (hi <= e) {
+                h = (int32_t)r;
+                key = s_key[r];
+                kd = (lo == s_start[r] && hi == e) ? 1 : 2;   // EXACT : CONTAINED
+            }
+        }
+        put(i, h, key, kd, lo, hi, handle, lkey, kind, rbase, rend);
+    }
+}
+
+__global__ __launch_bounds__(kThreads) void k_lookup_split(
     const uint64_t *__restrict__ rs, const uint64_t *__restrict__ re,
     const uint32_t *__restrict__ rk, uint32_t nregions,
     uint32_t split_shift, uint32_t nsplit, uint32_t page_shift,
@@ -56,41 +129,25 @@ __global__ __launch_bounds__(kThreads) void k_mr_lookup(
     const uint64_t run = 1ull << split_shift;
     const uint64_t stride = (uint64_t)gridDim.x * kThreads;
     for (uint64_t i = (uint64_t)blockIdx.x * kThreads + threadIdx.x; i < n; i += stride) {
-        const uint64_t o = off[i], l = len[i];
-        const uint64_t a = va_base + o;
+        uint64_t lo, hi;
+        const bool ok = round_range(va_base, off[i], len[i], in_page, lo, hi);
         int32_t h = -1;
         uint32_t key = 0;
-        uint8_t kd = 0;        // MISS
-        uint64_t lo = 0, hi = 0;
-
-        // Invalid: empty, start wraps, end wraps, or rounded end wraps.
-        bool bad = (l == 0) | (a < va_base) | (l > ~a);
-        const uint64_t last = a + l - 1;
-        bad |= ((last | in_page) == ~0ull);
-        if (bad) {
-            kd = 3;            // INVALID
-        } else {
-            lo = a & ~in_page;             // page floor of the start
-            hi = (last | in_page) + 1;     // page cover of the end
-            if (nsplit > 0 && spl[0] <= lo) {
-                const uint64_t c = last_le(spl, nsplit, lo);      // splitter run
-                const uint64_t b0 = c << split_shift;
-                const uint64_t left = (uint64_t)nregions - b0;
-                const uint64_t cnt = left < run ? left : run;
-                const uint64_t r = b0 + last_le(rs + b0, cnt, lo); // last start <= lo
-                const uint64_t e = re[r];
-                if (hi <= e) {
-                    h = (int32_t)r;
-                    key = rk[r];
-                    kd = (lo == rs[r] && hi == e) ? 1 : 2;   // EXACT : CONTAINED
-                }
+        uint8_t kd = ok ? 0 : 3;                 // MISS : INVALID
+        if (ok && nsplit > 0 && spl[0] <= lo) {
+            const uint64_t c = last_le(spl, nsplit, lo);         // splitter run
+            const uint64_t b0 = c << split_shift;
+            const uint64_t left = (uint64_t)nregions - b0;
+            const uint64_t cnt = left < run ? left : run;
+            const uint64_t r = b0 + last_le(rs + b0, cnt, lo);   // last start <= lo
+            const uint64_t e = re[r];
+            if (hi <= e) {
+                h = (int32_t)r;
+                key = rk[r];
+                kd = (lo == rs[r] && hi == e) ? 1 : 2;   // EXACT : CONTAINED
             }
         }
-        handle[i] = h;
-        lkey[i] = key;
-        kind[i] = kd;
-        rbase[i] = lo;
-        rend[i] = hi;
+        put(i, h, key, kd, lo, hi, handle, lkey, kind, rbase, rend);
     }
 }
 
@@ -98,12 +155,35 @@ __global__ __launch_bounds__(kThreads) void k_mr_lookup(
 
 hipError_t launch_mr_lookup(const LookupArgs &a, hipStream_t s)
 {
+    int dev = 0, cus = 0, lds_max = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e == hipSuccess)
+        e = hipDeviceGetAttribute(&lds_max, hipDeviceAttributeSharedMemPerBlockOptin, dev);
+    if (e != hipSuccess) return e;
+
+    const size_t table_bytes = (size_t)a.nregions * 20;
+    if (table_bytes <= (size_t)lds_max / 2) {
+        // Two blocks per CU share its LDS; each answers a grid-stride share.
+        const size_t bytes = table_bytes;
+        e = hipFuncSetAttribute(reinterpret_cast<const void *>(k_lookup_lds),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+        if (e != hipSuccess) return e;
+        uint64_t blocks = (a.n + kThreadsLds - 1) / kThreadsLds;
+        const uint64_t cap = 2ull * (uint64_t)cus;
+        if (blocks > cap) blocks = cap;
+        hipLaunchKernelGGL(k_lookup_lds, dim3((unsigned)blocks), dim3(kThreadsLds), bytes, s,
+                           a.reg_start, a.reg_end, a.reg_lkey, a.nregions, a.page_shift,
+                           a.off, a.len, a.n, a.va_base, a.handle, a.lkey, a.kind, a.rbase,
+                           a.rend);
+        return hipGetLastError();
+    }
     uint32_t shift = 0;
     while (((uint64_t)a.nregions + (1ull << shift) - 1) >> shift > kMaxSplitters) ++shift;
     const uint32_t nsplit = (uint32_t)(((uint64_t)a.nregions + (1ull << shift) - 1) >> shift);
     uint64_t blocks = (a.n + kThreads - 1) / kThreads;
     if (blocks > 2048) blocks = 2048;
-    hipLaunchKernelGGL(k_mr_lookup, dim3((unsigned)blocks), dim3(kThreads),
+    hipLaunchKernelGGL(k_lookup_split, dim3((unsigned)blocks), dim3(kThreads),
                        (size_t)nsplit * sizeof(uint64_t), s,
                        a.reg_start, a.reg_end, a.reg_lkey, a.nregions, shift, nsplit,
                        a.page_shift, a.off, a.len, a.n, a.va_base,

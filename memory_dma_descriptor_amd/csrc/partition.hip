@@ -7,16 +7,22 @@
 // which ballots the lanes that share a destination and lets one of them act
 // for the group, and of its warp-level WQE reservation, where one lane
 // reserves for the whole group and the others take consecutive slots by
-// their rank. Here the group of each lane comes from one ballot per key bit
-// (a lane matches when it agrees on every bit), its rank is the popcount of
-// the group below it, and the lowest lane of each group publishes the count;
-// a scan over (queue, block, item-round, wave) in that order turns counts
-// into positions, which keeps equal keys in index order. No atomic decides a
-// position, so the output is deterministic.
+// their rank. Here each lane learns the lanes sharing its queue id from one
+// ballot per key bit (a lane matches when it agrees on every bit), its rank is
+// the popcount of that group below it, and the lowest lane of the group bumps
+// a wave-private running counter by the group size; scans over (bucket,
+// block) and over the waves of a block turn counts into positions. No atomic
+// decides a position, so the output is deterministic.
 //
-// Kernels: k_split_hist (per-block bucket counts, bucket-major),
-// k_split_rowscan (one block per bucket: exclusive scan over blocks),
-// k_split_scatter (bucket bases, intra-block ranks, perm writes).
+// A block owns kTile consecutive requests; wave w of it owns the kWaveItems
+// consecutive requests [w * kWaveItems, (w + 1) * kWaveItems) of the tile,
+// read as kItems rounds of 64 consecutive requests, so equal ids meet in
+// (wave, round, lane) order -- request order.
+//
+// Kernels: k_split_hist (per-block bucket counts, block-major),
+// k_split_colscan (one block per bucket: exclusive scan over blocks),
+// k_split_scatter (ranks, a block-local stable sort in LDS, then perm written
+// as contiguous runs, one per bucket, so stores coalesce).
 #include "dd_device.hpp"
 #include "dd_internal.h"
 #include "dmadesc.h"
@@ -25,18 +31,28 @@ namespace dd {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kItems = 8;                       // requests per thread
-constexpr int kTile = kThreads * kItems;        // requests per block
 constexpr int kWaves = kThreads / kWave;
+constexpr int kItems = 16;                      // requests per thread
+constexpr int kWaveItems = kWave * kItems;      // requests per wave
+constexpr int kTile = kThreads * kItems;        // requests per block
 constexpr int kMaxBuckets = DMADESC_MAX_QUEUES + 1;
+constexpr int kBucketSlots = 2 * kThreads;      // >= kMaxBuckets, two per thread
 
 __device__ __forceinline__ int key_bits(uint32_t nq)
 {
     return 32 - __clz(nq);                       // bits of the largest bucket id
 }
 
+__device__ __forceinline__ uint32_t bucket_of(const uint32_t *__restrict__ qid, uint64_t i,
+                                              uint64_t n, uint32_t nq)
+{
+    if (i >= n) return 0;
+    const uint32_t q = qid[i];
+    return q < nq ? q : nq;
+}
+
 __global__ __launch_bounds__(kThreads) void k_split_hist(
-    const uint32_t *__restrict__ qid, uint64_t n, uint32_t nq, uint64_t nb,
+    const uint32_t *__restrict__ qid, uint64_t n, uint32_t nq,
     uint32_t *__restrict__ counts)
 {
     __shared__ uint32_t h[kMaxBuckets];
@@ -44,112 +60,138 @@ __global__ __launch_bounds__(kThreads) void k_split_hist(
     for (uint32_t b = threadIdx.x; b < nbk; b += kThreads) h[b] = 0;
     __syncthreads();
     const int nbits = key_bits(nq);
-    const uint64_t base = (uint64_t)blockIdx.x * kTile;
+    const uint64_t base = (uint64_t)blockIdx.x * kTile + (uint64_t)wave() * kWaveItems + lane();
     const uint64_t below = __lanemask_lt();
+    uint32_t b[kItems];
+#pragma unroll
+    for (int k = 0; k < kItems; ++k) b[k] = bucket_of(qid, base + (uint64_t)k * kWave, n, nq);
 #pragma unroll
     for (int k = 0; k < kItems; ++k) {
-        const uint64_t i = base + (uint64_t)k * kThreads + threadIdx.x;
-        const bool on = i < n;
-        uint32_t b = 0;
-        if (on) {
-            const uint32_t q = qid[i];
-            b = q < nq ? q : nq;
-        }
-        const uint64_t m = match_key(b, on, nbits, __ballot(on));
-        if (on && (m & below) == 0) atomicAdd(&h[b], (uint32_t)__popcll(m));
+        const bool on = base + (uint64_t)k * kWave < n;
+        const uint64_t m = match_key(b[k], on, nbits, __ballot(on));
+        if (on && (m & below) == 0) atomicAdd(&h[b[k]], (uint32_t)__popcll(m));
     }
     __syncthreads();
-    for (uint32_t b = threadIdx.x; b < nbk; b += kThreads) counts[(uint64_t)b * nb + blockIdx.x] = h[b];
+    uint32_t *row = counts + (uint64_t)blockIdx.x * nbk;       // block-major
+    for (uint32_t k = threadIdx.x; k < nbk; k += kThreads) row[k] = h[k];
 }
 
-// One block per bucket: exclusive scan of that bucket's per-block counts.
-__global__ __launch_bounds__(kThreads) void k_split_rowscan(
-    uint32_t *__restrict__ counts, uint64_t nb, uint64_t *__restrict__ rowtotal)
+// One block per bucket: in-place exclusive scan of that bucket's per-block
+// counts (a column of the block-major matrix) and the bucket total.
+__global__ __launch_bounds__(kThreads) void k_split_colscan(
+    uint32_t *__restrict__ counts, uint64_t nb, uint32_t nbk, uint64_t *__restrict__ total)
 {
     __shared__ uint64_t scratch[kWaves];
-    uint32_t *row = counts + (uint64_t)blockIdx.x * nb;
+    const uint32_t col = blockIdx.x;
     const uint64_t seg = (nb + kThreads - 1) / kThreads;
     const uint64_t b0 = (uint64_t)threadIdx.x * seg;
     const uint64_t b1 = (b0 + seg < nb) ? b0 + seg : nb;
     uint64_t s = 0;
-    for (uint64_t b = b0; b < b1; ++b) s += row[b];
+    for (uint64_t k = b0; k < b1; ++k) s += counts[k * nbk + col];
     uint64_t tot;
     uint64_t run = block_excl_scan<kThreads>(s, scratch, &tot);
-    for (uint64_t b = b0; b < b1; ++b) {
-        const uint32_t c = row[b];
-        row[b] = (uint32_t)run;
+    for (uint64_t k = b0; k < b1; ++k) {
+        const uint32_t c = counts[k * nbk + col];
+        counts[k * nbk + col] = (uint32_t)run;
         run += c;
     }
-    if (threadIdx.x == 0) rowtotal[blockIdx.x] = tot;
+    if (threadIdx.x == 0) total[col] = tot;
 }
 
 __global__ __launch_bounds__(kThreads) void k_split_scatter(
-    const uint32_t *__restrict__ qid, uint64_t n, uint32_t nq, uint64_t nb,
-    const uint32_t *__restrict__ counts, const uint64_t *__restrict__ rowtotal,
+    const uint32_t *__restrict__ qid, uint64_t n, uint32_t nq,
+    const uint32_t *__restrict__ offs, const uint64_t *__restrict__ total,
     uint32_t *__restrict__ perm, uint64_t *__restrict__ qoff,
     uint64_t *__restrict__ n_invalid)
 {
-    __shared__ uint64_t s_base[kMaxBuckets];
-    __shared__ uint32_t s_cnt[kItems * kWaves][kMaxBuckets];
+    __shared__ uint64_t s_scr[kWaves];
+    __shared__ uint32_t s_wcnt[kWaves][kMaxBuckets];   // running, then prefix, per wave
+    __shared__ uint32_t s_lstart[kBucketSlots];        // bucket start in the block's sorted tile
+    __shared__ uint64_t s_gpos[kBucketSlots];          // bucket start in perm for this block
+    __shared__ uint32_t s_sorted[kTile];               // request indices, block-local stable order
+    __shared__ uint16_t s_sbkt[kTile];                 // their buckets
+
     const uint32_t nbk = nq + 1;
-    const int t = threadIdx.x, w = wave();
+    const int t = threadIdx.x, w = wave(), ln = lane();
+    for (uint32_t b = ln; b < nbk; b += kWave) s_wcnt[w][b] = 0;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
-    for (uint32_t b = t; b < nbk; b += kThreads) s_base[b] = rowtotal[b];
-    for (int kw = 0; kw < kItems * kWaves; ++kw)
-        for (uint32_t b = t; b < nbk; b += kThreads) s_cnt[kw][b] = 0;
-    __syncthreads();
-    if (t == 0) {                                  // bucket starts over the whole batch
-        uint64_t run = 0;
-        for (uint32_t b = 0; b < nbk; ++b) {
-            const uint64_t c = s_base[b];
-            s_base[b] = run;
-            run += c;
-        }
-    }
-    __syncthreads();
-    if (blockIdx.x == 0) {
-        for (uint32_t b = t; b < nbk; b += kThreads) qoff[b] = s_base[b];
-        if (t == 0) {
-            qoff[nbk] = n;
-            *n_invalid = rowtotal[nq];
-        }
-    }
-
+    // Wave-private stable ranks: round k of wave w covers 64 consecutive requests.
     const int nbits = key_bits(nq);
-    const uint64_t base = (uint64_t)blockIdx.x * kTile;
+    const uint64_t tile = (uint64_t)blockIdx.x * kTile;
+    const uint64_t base = tile + (uint64_t)w * kWaveItems + ln;
     const uint64_t below = __lanemask_lt();
-    uint32_t bkt[kItems], rank[kItems];
+    uint32_t b[kItems], rank[kItems];
+#pragma unroll
+    for (int k = 0; k < kItems; ++k) b[k] = bucket_of(qid, base + (uint64_t)k * kWave, n, nq);
 #pragma unroll
     for (int k = 0; k < kItems; ++k) {
-        const uint64_t i = base + (uint64_t)k * kThreads + t;
-        const bool on = i < n;
-        uint32_t b = 0;
-        if (on) {
-            const uint32_t q = qid[i];
-            b = q < nq ? q : nq;
-        }
-        const uint64_t m = match_key(b, on, nbits, __ballot(on));
-        const uint32_t r = (uint32_t)__popcll(m & below);
-        if (on && r == 0) s_cnt[k * kWaves + w][b] = (uint32_t)__popcll(m);
-        bkt[k] = b;
-        rank[k] = r;
+        const bool on = base + (uint64_t)k * kWave < n;
+        const uint64_t m = match_key(b[k], on, nbits, __ballot(on));
+        const uint32_t before = s_wcnt[w][b[k]];
+        rank[k] = before + (uint32_t)__popcll(m & below);
+        __builtin_amdgcn_wave_barrier();
+        if (on && (m & below) == 0) s_wcnt[w][b[k]] = before + (uint32_t)__popcll(m);
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
     __syncthreads();
-    // Positions: bucket start + this block's offset in the bucket + earlier
-    // (item-round, wave) groups of this block.
-    for (uint32_t b = t; b < nbk; b += kThreads) {
-        uint64_t run = s_base[b] + counts[(uint64_t)b * nb + blockIdx.x];
-        for (int kw = 0; kw < kItems * kWaves; ++kw) {
-            const uint32_t c = s_cnt[kw][b];
-            s_cnt[kw][b] = (uint32_t)run;
-            run += c;
+
+    // Per bucket: waves' prefix inside the block, the block's total, and the
+    // bucket's start in perm (all buckets' totals scanned across the block).
+    uint64_t pair_tot[2] = {0, 0}, pair_off[2] = {0, 0};
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const uint32_t bk = 2 * t + h;
+        if (bk < nbk) {
+            uint32_t run = 0;
+#pragma unroll
+            for (int ww = 0; ww < kWaves; ++ww) {
+                const uint32_t c = s_wcnt[ww][bk];
+                s_wcnt[ww][bk] = run;
+                run += c;
+            }
+            pair_tot[h] = run;                           // this block's count in bucket bk
+            pair_off[h] = total[bk];                     // whole batch's count in bucket bk
         }
     }
+    uint64_t ltot, gtot;
+    const uint64_t lex = block_excl_scan<kThreads>(pair_tot[0] + pair_tot[1], s_scr, &ltot);
+    const uint64_t gex = block_excl_scan<kThreads>(pair_off[0] + pair_off[1], s_scr, &gtot);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const uint32_t bk = 2 * t + h;
+        if (bk < nbk) {
+            const uint64_t gbase = gex + (h ? pair_off[0] : 0);
+            s_lstart[bk] = (uint32_t)(lex + (h ? pair_tot[0] : 0));
+            s_gpos[bk] = gbase + offs[(uint64_t)blockIdx.x * nbk + bk];
+            if (blockIdx.x == 0) qoff[bk] = gbase;
+        }
+    }
+    if (blockIdx.x == 0 && t == 0) {
+        qoff[nbk] = n;
+        *n_invalid = total[nq];
+    }
     __syncthreads();
+
+    // Block-local stable order in LDS, then perm written run by run.
 #pragma unroll
     for (int k = 0; k < kItems; ++k) {
-        const uint64_t i = base + (uint64_t)k * kThreads + t;
-        if (i < n) perm[s_cnt[k * kWaves + w][bkt[k]] + rank[k]] = (uint32_t)i;
+        const uint64_t i = base + (uint64_t)k * kWave;
+        if (i < n) {
+            const uint32_t sidx = s_lstart[b[k]] + s_wcnt[w][b[k]] + rank[k];
+            s_sorted[sidx] = (uint32_t)i;
+            s_sbkt[sidx] = (uint16_t)b[k];
+        }
+    }
+    __syncthreads();
+    const uint64_t cnt = n - tile < (uint64_t)kTile ? n - tile : (uint64_t)kTile;
+    for (uint32_t j = t; j < cnt; j += kThreads) {
+        const uint32_t bk = s_sbkt[j];
+        perm[s_gpos[bk] + (j - s_lstart[bk])] = s_sorted[j];
     }
 }
 
@@ -176,16 +218,16 @@ hipError_t launch_partition(const SplitArgs &a, hipStream_t s)
         return hipGetLastError();
     }
     const uint64_t nb = (a.n + kTile - 1) / kTile;
+    const uint32_t nbk = a.nqueues + 1;
     uint32_t *counts = static_cast<uint32_t *>(a.ws);
-    uint64_t *rowtotal = reinterpret_cast<uint64_t *>(
-        static_cast<char *>(a.ws) + align256((uint64_t)(a.nqueues + 1) * nb * sizeof(uint32_t)));
+    uint64_t *total = reinterpret_cast<uint64_t *>(
+        static_cast<char *>(a.ws) + align256((uint64_t)nbk * nb * sizeof(uint32_t)));
     hipLaunchKernelGGL(k_split_hist, dim3((unsigned)nb), dim3(kThreads), 0, s,
-                       a.qid, a.n, a.nqueues, nb, counts);
-    hipLaunchKernelGGL(k_split_rowscan, dim3(a.nqueues + 1), dim3(kThreads), 0, s,
-                       counts, nb, rowtotal);
+                       a.qid, a.n, a.nqueues, counts);
+    hipLaunchKernelGGL(k_split_colscan, dim3(nbk), dim3(kThreads), 0, s,
+                       counts, nb, nbk, total);
     hipLaunchKernelGGL(k_split_scatter, dim3((unsigned)nb), dim3(kThreads), 0, s,
-                       a.qid, a.n, a.nqueues, nb, counts, rowtotal, a.perm, a.qoff,
-                       a.n_invalid);
+                       a.qid, a.n, a.nqueues, counts, total, a.perm, a.qoff, a.n_invalid);
     return hipGetLastError();
 }
 

@@ -42,12 +42,15 @@ def test_workspace_sizes():
     ws = dd.workspace_bytes
     assert ws(dd.OP_MR_LOOKUP, 1 << 20) == 0
     assert ws(dd.OP_BUILD_PRP, 0) == 0
-    assert ws(dd.OP_BUILD_PRP, 1) == 512                # header + one block word
-    assert ws(dd.OP_BUILD_PRP, 16 << 20) >= 256 + (16 << 20) // 2048 * 8
     assert ws(dd.OP_PARTITION, 100, 0) == 0            # nqueues 0 is invalid
     assert ws(dd.OP_PARTITION, 100, 257) == 0          # above the maximum
-    assert ws(dd.OP_PARTITION, 16 << 20, 64) >= 65 * (16 << 20) // 2048 * 4
     assert ws(99, 10, 0) == 0
+    for op, q in ((dd.OP_BUILD_PRP, 0), (dd.OP_PARTITION, 64)):
+        sizes = [ws(op, n, q) for n in (1, 1000, 1 << 16, 1 << 20, 16 << 20, (1 << 32) - 1)]
+        assert all(x % 256 == 0 and x > 0 for x in sizes), sizes
+        assert sizes == sorted(sizes), sizes
+        assert sizes[-1] < 1 << 32, sizes                 # small next to the batch itself
+    assert ws(dd.OP_PARTITION, 1 << 20, 256) > ws(dd.OP_PARTITION, 1 << 20, 1)
 
 
 EINVAL = -errno.EINVAL

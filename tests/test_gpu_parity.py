@@ -169,6 +169,23 @@ def test_prp_empty_and_single():
     assert list(g["status"]) == [2, 2] and g["total"] == 0
 
 
+def test_prp_list_longer_than_2_24_words():
+    """A request whose list needs more than 2^24 words (a 64 GiB transfer)
+    among small ones: such a round takes the library's 64-bit list path."""
+    rng = np.random.default_rng(24)
+    p = (1 << 20) + 256                                  # 64 GiB + 16 MiB heap
+    lut = _perm_lut(rng, p)
+    n = 700
+    ln = rng.integers(1, 300 * 4096, size=n).astype(np.uint64)
+    off = (rng.integers(0, 1 << 28, size=n) * 4).astype(np.uint64)
+    ln[5] = ((1 << 24) + 9) * 4096 - 12                  # 2^24 + 10 pages
+    off[5] = 4 * 1000
+    ln[600] = ((1 << 24) + 600) * 4096
+    off[600] = 65536 * 7 + 8
+    total = oracle.build_prp(lut, off, ln, BUS, 0, pool=None)["total"]
+    gc.check_prp_full(lut, off, ln, BUS, total + 1, ctx="huge list")
+
+
 def test_prp_unaligned_table_entries():
     """Table entries need not be 64 KiB aligned: results are still the
     table value plus the in-page offset, as in the oracle."""
