@@ -45,6 +45,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a plain 1 GiB device copy (for counter scaling) and exit")
+    ap.add_argument("--list-write-floor", action="store_true",
+                    help="time a library scatter that writes the same 128-byte list lines "
+                         "as the PRP build (its layout's write floor) and exit")
     return ap.parse_args()
 
 
@@ -123,6 +126,47 @@ def copy_calibration():
     print(json.dumps({"copy_calibration_bytes": n, "launches": 3}), flush=True)
 
 
+def list_write_floor(name, steps):
+    """Writes exactly the 128-byte lines the PRP build writes for `name` (each
+    list run padded to whole lines at the head of its list pages) with
+    torch's index_fill_, a plain library scatter, and reports its rate. This
+    bounds what any kernel can reach for the list writes of that layout."""
+    import numpy as np
+    import torch
+
+    import synth
+    d = synth.generate(name)
+    off, ln = d["off"], d["len"]
+    heap = np.uint64(d["lut_entries"]) * np.uint64(65536)
+    valid = (ln > 0) & (off % 4 == 0) & (off + ln <= heap)
+    pages = np.where(valid, ((off & np.uint64(4095)) + ln + np.uint64(4095)) >> np.uint64(12), 0)
+    lists = pages >= 3
+    lp = np.where(lists, (pages - 2 + 510) // 511, 0).astype(np.int64)
+    ent = np.where(lists, pages - 1 + lp - 1, 0).astype(np.int64)
+    slot = np.cumsum(lp) - lp
+    nl = (ent + 15) // 16
+    first = np.repeat(slot * 32, nl)
+    within = np.arange(int(nl.sum())) - np.repeat(np.cumsum(nl) - nl, nl)
+    dev = torch.device("cuda:0")
+    idx = torch.from_numpy(first + within).to(dev)
+    pool = torch.empty((int(lp.sum()) * 32, 16), dtype=torch.int64, device=dev)
+    pool.index_fill_(0, idx, 7)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        pool.index_fill_(0, idx, 7)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    nbytes = int(nl.sum()) * 128
+    print(json.dumps({"list_write_floor": {"workload": name, "lines": int(nl.sum()),
+                                           "bytes": nbytes, "ms": round(ms, 4),
+                                           "gbs": round(nbytes / ms / 1e6, 1),
+                                           "method": "torch index_fill_ of the 128-byte list lines"}}),
+          flush=True)
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -136,6 +180,9 @@ def main():
 
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.list_write_floor:
+        list_write_floor(args.workload, min(args.steps, 20))
         return
 
     import memory_dma_descriptor_amd as dd
@@ -220,7 +267,7 @@ def main():
         "config": {"workload": args.workload, "requests": n, "lut_entries": d["lut_entries"],
                    "regions": d["regions"], "nqueues": nq, "list_pages": pool_pages,
                    "calls": "mr_lookup + build_prp + partition_by_queue, one stream"},
-        "roofline": {"bound": "hbm", "kernel": "dmadesc_build_prp (count + scan + emit)",
+        "roofline": {"bound": "hbm", "kernel": "dmadesc_build_prp (k_prp_clear + k_prp_build)",
                      "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
                      "algorithmic_bytes_per_launch": ab["build_prp"],

@@ -29,6 +29,7 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kThreadsLds = 512;
+constexpr int kPerLane = 4;                  // requests per lane per trip (LDS kernel)
 constexpr uint32_t kMaxSplitters = 8192;   // 64 KiB of LDS
 
 // Index of the last element <= key in a[0..cnt), given a[0] <= key.
@@ -89,24 +90,38 @@ __global__ __launch_bounds__(kThreadsLds) void k_lookup_lds(
     }
     __syncthreads();
 
+    // Each lane takes kPerLane requests per trip (striped, so every column
+    // load stays contiguous per wave); all their loads are issued before any
+    // search so that memory latency overlaps.
     const uint64_t in_page = (1ull << page_shift) - 1;
-    const uint64_t stride = (uint64_t)gridDim.x * kThreadsLds;
-    for (uint64_t i = (uint64_t)blockIdx.x * kThreadsLds + threadIdx.x; i < n; i += stride) {
-        uint64_t lo, hi;
-        const bool ok = round_range(va_base, off[i], len[i], in_page, lo, hi);
-        int32_t h = -1;
-        uint32_t key = 0;
-        uint8_t kd = ok ? 0 : 3;                 // MISS : INVALID
-        if (ok && nregions > 0 && s_start[0] <= lo) {
-            const uint32_t r = (uint32_t)last_le(s_start, nregions, lo);
-            const uint64_t e = s_end[r];
-            if (hi <= e) {
-                h = (int32_t)r;
-                key = s_key[r];
-                kd = (lo == s_start[r] && hi == e) ? 1 : 2;   // EXACT : CONTAINED
-            }
+    const uint64_t span = (uint64_t)kThreadsLds * kPerLane;
+    for (uint64_t c = (uint64_t)blockIdx.x * span; c < n; c += (uint64_t)gridDim.x * span) {
+        uint64_t o[kPerLane], l[kPerLane];
+#pragma unroll
+        for (int k = 0; k < kPerLane; ++k) {
+            const uint64_t i = c + (uint64_t)k * kThreadsLds + threadIdx.x;
+            o[k] = i < n ? off[i] : 0;
+            l[k] = i < n ? len[i] : 0;
         }
-        put(i, h, key, kd, lo, hi, handle, lkey, kind, rbase, rend);
+#pragma unroll
+        for (int k = 0; k < kPerLane; ++k) {
+            const uint64_t i = c + (uint64_t)k * kThreadsLds + threadIdx.x;
+            uint64_t lo, hi;
+            const bool ok = round_range(va_base, o[k], l[k], in_page, lo, hi);
+            int32_t h = -1;
+            uint32_t key = 0;
+            uint8_t kd = ok ? 0 : 3;             // MISS : INVALID
+            if (ok && nregions > 0 && s_start[0] <= lo) {
+                const uint32_t r = (uint32_t)last_le(s_start, nregions, lo);
+                const uint64_t e = s_end[r];
+                if (hi <= e) {
+                    h = (int32_t)r;
+                    key = s_key[r];
+                    kd = (lo == s_start[r] && hi == e) ? 1 : 2;   // EXACT : CONTAINED
+                }
+            }
+            if (i < n) put(i, h, key, kd, lo, hi, handle, lkey, kind, rbase, rend);
+        }
     }
 }
 
@@ -169,7 +184,7 @@ hipError_t launch_mr_lookup(const LookupArgs &a, hipStream_t s)
         e = hipFuncSetAttribute(reinterpret_cast<const void *>(k_lookup_lds),
                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
         if (e != hipSuccess) return e;
-        uint64_t blocks = (a.n + kThreadsLds - 1) / kThreadsLds;
+        uint64_t blocks = (a.n + (uint64_t)kThreadsLds * kPerLane - 1) / ((uint64_t)kThreadsLds * kPerLane);
         const uint64_t cap = 2ull * (uint64_t)cus;
         if (blocks > cap) blocks = cap;
         hipLaunchKernelGGL(k_lookup_lds, dim3((unsigned)blocks), dim3(kThreadsLds), bytes, s,

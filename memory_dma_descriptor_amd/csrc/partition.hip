@@ -59,18 +59,14 @@ __global__ __launch_bounds__(kThreads) void k_split_hist(
     const uint32_t nbk = nq + 1;
     for (uint32_t b = threadIdx.x; b < nbk; b += kThreads) h[b] = 0;
     __syncthreads();
-    const int nbits = key_bits(nq);
+    // Counts only (no ranks), so plain LDS atomics suffice here.
     const uint64_t base = (uint64_t)blockIdx.x * kTile + (uint64_t)wave() * kWaveItems + lane();
-    const uint64_t below = __lanemask_lt();
     uint32_t b[kItems];
 #pragma unroll
     for (int k = 0; k < kItems; ++k) b[k] = bucket_of(qid, base + (uint64_t)k * kWave, n, nq);
 #pragma unroll
-    for (int k = 0; k < kItems; ++k) {
-        const bool on = base + (uint64_t)k * kWave < n;
-        const uint64_t m = match_key(b[k], on, nbits, __ballot(on));
-        if (on && (m & below) == 0) atomicAdd(&h[b[k]], (uint32_t)__popcll(m));
-    }
+    for (int k = 0; k < kItems; ++k)
+        if (base + (uint64_t)k * kWave < n) atomicAdd(&h[b[k]], 1u);
     __syncthreads();
     uint32_t *row = counts + (uint64_t)blockIdx.x * nbk;       // block-major
     for (uint32_t k = threadIdx.x; k < nbk; k += kThreads) row[k] = h[k];
