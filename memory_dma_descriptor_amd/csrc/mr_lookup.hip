@@ -30,6 +30,10 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kThreadsLds = 512;
 constexpr int kPerLane = 4;                  // requests per lane per trip (LDS kernel)
+
+typedef uint64_t u64x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 constexpr uint32_t kMaxSplitters = 8192;   // 64 KiB of LDS
 
 // Index of the last element <= key in a[0..cnt), given a[0] <= key.
@@ -77,7 +81,7 @@ __global__ __launch_bounds__(kThreadsLds) void k_lookup_lds(
     uint64_t n, uint64_t va_base,
     int32_t *__restrict__ handle, uint32_t *__restrict__ lkey,
     uint8_t *__restrict__ kind, uint64_t *__restrict__ rbase,
-    uint64_t *__restrict__ rend)
+    uint64_t *__restrict__ rend, bool aligned)
 {
     extern __shared__ uint64_t lds[];
     uint64_t *s_start = lds;
@@ -90,37 +94,66 @@ __global__ __launch_bounds__(kThreadsLds) void k_lookup_lds(
     }
     __syncthreads();
 
-    // Each lane takes kPerLane requests per trip (striped, so every column
-    // load stays contiguous per wave); all their loads are issued before any
-    // search so that memory latency overlaps.
+    // Each lane takes kPerLane consecutive requests per trip, so every column
+    // moves through 16- to 32-byte accesses per lane (kind as one dword,
+    // handle and lkey as 16 bytes, rbase and rend as 32 bytes) while a wave's
+    // accesses stay contiguous; all loads are issued before any search.
     const uint64_t in_page = (1ull << page_shift) - 1;
     const uint64_t span = (uint64_t)kThreadsLds * kPerLane;
     for (uint64_t c = (uint64_t)blockIdx.x * span; c < n; c += (uint64_t)gridDim.x * span) {
+        const uint64_t i0 = c + (uint64_t)threadIdx.x * kPerLane;
+        if (i0 >= n) break;
+        const bool whole = aligned && i0 + kPerLane <= n;
         uint64_t o[kPerLane], l[kPerLane];
+        if (whole) {
+            const u64x2 oa = *reinterpret_cast<const u64x2 *>(off + i0);
+            const u64x2 ob = *reinterpret_cast<const u64x2 *>(off + i0 + 2);
+            const u64x2 la = *reinterpret_cast<const u64x2 *>(len + i0);
+            const u64x2 lb = *reinterpret_cast<const u64x2 *>(len + i0 + 2);
+            o[0] = oa.x; o[1] = oa.y; o[2] = ob.x; o[3] = ob.y;
+            l[0] = la.x; l[1] = la.y; l[2] = lb.x; l[3] = lb.y;
+        } else {
 #pragma unroll
-        for (int k = 0; k < kPerLane; ++k) {
-            const uint64_t i = c + (uint64_t)k * kThreadsLds + threadIdx.x;
-            o[k] = i < n ? off[i] : 0;
-            l[k] = i < n ? len[i] : 0;
+            for (int k = 0; k < kPerLane; ++k) {
+                o[k] = i0 + k < n ? off[i0 + k] : 0;
+                l[k] = i0 + k < n ? len[i0 + k] : 0;
+            }
         }
+        int32_t h[kPerLane];
+        uint32_t key[kPerLane];
+        uint8_t kd[kPerLane];
+        uint64_t lo[kPerLane], hi[kPerLane];
 #pragma unroll
         for (int k = 0; k < kPerLane; ++k) {
-            const uint64_t i = c + (uint64_t)k * kThreadsLds + threadIdx.x;
-            uint64_t lo, hi;
-            const bool ok = round_range(va_base, o[k], l[k], in_page, lo, hi);
-            int32_t h = -1;
-            uint32_t key = 0;
-            uint8_t kd = ok ? 0 : 3;             // MISS : INVALID
-            if (ok && nregions > 0 && s_start[0] <= lo) {
-                const uint32_t r = (uint32_t)last_le(s_start, nregions, lo);
+            const bool ok = round_range(va_base, o[k], l[k], in_page, lo[k], hi[k]);
+            h[k] = -1;
+            key[k] = 0;
+            kd[k] = ok ? 0 : 3;                  // MISS : INVALID
+            if (ok && nregions > 0 && s_start[0] <= lo[k]) {
+                const uint32_t r = (uint32_t)last_le(s_start, nregions, lo[k]);
                 const uint64_t e = s_end[r];
-                if (hi <= e) {
-                    h = (int32_t)r;
-                    key = s_key[r];
-                    kd = (lo == s_start[r] && hi == e) ? 1 : 2;   // EXACT : CONTAINED
+                if (hi[k] <= e) {
+                    h[k] = (int32_t)r;
+                    key[k] = s_key[r];
+                    kd[k] = (lo[k] == s_start[r] && hi[k] == e) ? 1 : 2;   // EXACT : CONTAINED
                 }
             }
-            if (i < n) put(i, h, key, kd, lo, hi, handle, lkey, kind, rbase, rend);
+        }
+        if (whole) {
+            *reinterpret_cast<i32x4 *>(handle + i0) = i32x4{h[0], h[1], h[2], h[3]};
+            *reinterpret_cast<u32x4 *>(lkey + i0) = u32x4{key[0], key[1], key[2], key[3]};
+            *reinterpret_cast<uint32_t *>(kind + i0) =
+                (uint32_t)kd[0] | ((uint32_t)kd[1] << 8) | ((uint32_t)kd[2] << 16) |
+                ((uint32_t)kd[3] << 24);
+            *reinterpret_cast<u64x2 *>(rbase + i0) = u64x2{lo[0], lo[1]};
+            *reinterpret_cast<u64x2 *>(rbase + i0 + 2) = u64x2{lo[2], lo[3]};
+            *reinterpret_cast<u64x2 *>(rend + i0) = u64x2{hi[0], hi[1]};
+            *reinterpret_cast<u64x2 *>(rend + i0 + 2) = u64x2{hi[2], hi[3]};
+        } else {
+#pragma unroll
+            for (int k = 0; k < kPerLane; ++k)
+                if (i0 + k < n) put(i0 + k, h[k], key[k], kd[k], lo[k], hi[k], handle, lkey, kind,
+                                    rbase, rend);
         }
     }
 }
@@ -187,10 +220,15 @@ hipError_t launch_mr_lookup(const LookupArgs &a, hipStream_t s)
         uint64_t blocks = (a.n + (uint64_t)kThreadsLds * kPerLane - 1) / ((uint64_t)kThreadsLds * kPerLane);
         const uint64_t cap = 2ull * (uint64_t)cus;
         if (blocks > cap) blocks = cap;
+        // Columns that allow 16-byte accesses (4-byte for kind) take the
+        // vector path; any other alignment is served element by element.
+        auto al = [](const void *p, uintptr_t m) { return (reinterpret_cast<uintptr_t>(p) & m) == 0; };
+        const bool aligned = al(a.off, 15) && al(a.len, 15) && al(a.handle, 15) &&
+                             al(a.lkey, 15) && al(a.kind, 3) && al(a.rbase, 15) && al(a.rend, 15);
         hipLaunchKernelGGL(k_lookup_lds, dim3((unsigned)blocks), dim3(kThreadsLds), bytes, s,
                            a.reg_start, a.reg_end, a.reg_lkey, a.nregions, a.page_shift,
                            a.off, a.len, a.n, a.va_base, a.handle, a.lkey, a.kind, a.rbase,
-                           a.rend);
+                           a.rend, aligned);
         return hipGetLastError();
     }
     uint32_t shift = 0;

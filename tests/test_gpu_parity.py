@@ -254,6 +254,31 @@ def test_lookup_invalid_and_va_base():
     gc.check_lookup(start, end, lkey, off, ln, page_shift=30, ctx="shift30")
 
 
+def test_lookup_unaligned_columns():
+    """Columns that start 8 bytes (1 byte for kind) past an aligned address take
+    the element-by-element path and must give the same answers."""
+    rng = np.random.default_rng(41)
+    start, end = _table(rng, 1000)
+    lkey = rng.integers(1, 1 << 32, size=1000, dtype=np.uint64).astype(np.uint32)
+    off, ln = _queries(rng, start, end, 5003)
+    n = off.shape[0]
+    o = oracle.mr_lookup(start, end, lkey, off, ln)
+    def shift(a):
+        buf = torch.empty(a.numel() + 1, dtype=a.dtype, device="cuda")
+        buf[1:].copy_(a)
+        return buf[1:]
+
+    out = dict(handle=torch.empty(n + 1, dtype=torch.int32, device="cuda")[1:],
+               lkey=torch.empty(n + 1, dtype=torch.uint32, device="cuda")[1:],
+               kind=torch.empty(n + 1, dtype=torch.uint8, device="cuda")[1:],
+               rbase=torch.empty(n + 1, dtype=torch.uint64, device="cuda")[1:],
+               rend=torch.empty(n + 1, dtype=torch.uint64, device="cuda")[1:])
+    dd.mr_lookup(gc.dev(start), gc.dev(end), gc.dev(lkey), shift(gc.dev(off)), shift(gc.dev(ln)),
+                 out=out)
+    torch.cuda.synchronize()
+    gc.assert_lookup_equal(o, {k: gc.host(v) for k, v in out.items()}, "unaligned")
+
+
 def test_lookup_register_sequence_table():
     base = 0x7F00_0000_0000
     reg = oracle.Registry(12)
