@@ -51,6 +51,11 @@ def _lib():
         lib.orc_build_prp.restype = None
         lib.orc_partition.argtypes = [_u32p, u64, u32, _u32p, _u64p, _u64p]
         lib.orc_partition.restype = None
+        lib.orc_emit_sqe.argtypes = [_u32p, _u64p, u32, _u8p, _u64p, _u64p, _u64p, _u64p, u64,
+                                     ctypes.c_uint8, u32, ctypes.c_uint,
+                                     ctypes.POINTER(_u8p), _u32p, _u32p, _u32p, _u64p, _u32p,
+                                     _u32p]
+        lib.orc_emit_sqe.restype = None
         lib.orc_reg_create.argtypes = [ctypes.c_uint]
         lib.orc_reg_create.restype = ctypes.c_void_p
         lib.orc_reg_destroy.argtypes = [ctypes.c_void_p]
@@ -131,6 +136,34 @@ def partition(qid, nqueues):
     _lib().orc_partition(_p(qid, _u32p), n, nqueues, _p(perm, _u32p), _p(qoff, _u64p),
                          _p(ninv, _u64p))
     return dict(perm=perm, qoff=qoff, n_invalid=int(ninv[0]))
+
+
+def emit_sqe(perm, qoff, status, length, slba, prp1, prp2, rings, depth, free_slots,
+             tail, cursor, slot=None, opcode=0x02, nsid=1, lba_shift=9):
+    """Runs O5 for one call. `rings` is a list of u8[depth[q], 64] arrays (or
+    None for a refused queue), updated in place. Returns dict(tail, cursor,
+    placed, slot) with new arrays; `slot` (u32[n]) is copied first when given,
+    else starts as all 0xFFFFFFFF."""
+    perm, qoff = _u32(perm), _u64(qoff)
+    status = np.ascontiguousarray(status, dtype=np.uint8)
+    length, slba, prp1, prp2 = _u64(length), _u64(slba), _u64(prp1), _u64(prp2)
+    nq = len(rings)
+    depth, free_slots = _u32(depth), _u32(free_slots)
+    tail, cursor = _u32(tail).copy(), _u64(cursor).copy()
+    n = length.shape[0]
+    slot = (np.full(n, 0xFFFFFFFF, np.uint32) if slot is None else _u32(slot).copy())
+    placed = np.zeros(nq, np.uint32)
+    ring_ptrs = (_u8p * max(nq, 1))()
+    for q, r in enumerate(rings):
+        if r is not None:
+            assert r.dtype == np.uint8 and r.flags["C_CONTIGUOUS"] and r.size >= int(depth[q]) * 64
+            ring_ptrs[q] = r.ctypes.data_as(_u8p)
+    _lib().orc_emit_sqe(_p(perm, _u32p), _p(qoff, _u64p), nq, _p(status, _u8p),
+                        _p(length, _u64p), _p(slba, _u64p), _p(prp1, _u64p), _p(prp2, _u64p),
+                        n, opcode, nsid, lba_shift, ring_ptrs, _p(depth, _u32p),
+                        _p(free_slots, _u32p), _p(tail, _u32p), _p(cursor, _u64p),
+                        _p(placed, _u32p), _p(slot, _u32p))
+    return dict(tail=tail, cursor=cursor, placed=placed, slot=slot)
 
 
 class Registry:

@@ -226,6 +226,94 @@ void orc_partition(const uint32_t *qid, uint64_t n, uint32_t nqueues,
 }
 
 /* ------------------------------------------------------------------------
+ * O5  NVMe submission entries per queue.
+ *
+ * [UPCIE] "GPU-Resident Queue API": a kernel on the GPU fills the submission
+ * queue itself, one 64-byte entry per command, written as four 16-byte stores.
+ * [MORI] warp-level WQE reservation: the lanes bound for one queue take
+ * consecutive slots starting at that queue's tail, and the tail then moves on
+ * by their number. The entry layout is the NVMe common command format [NVMe]
+ * (not on the pages): dword 0 = opcode (bits 7:0), fused operation and PRP
+ * data transfer (bits 15:8, zero), command identifier (bits 31:16); dword 1 =
+ * namespace id; dwords 2-5 = 0 (no metadata pointer); dwords 6-7 = PRP1;
+ * dwords 8-9 = PRP2; dwords 10-11 = starting LBA; dword 12 bits 15:0 = number
+ * of logical blocks minus one; dwords 13-15 = 0. A queue of depth D holds at
+ * most D - 1 entries, and D is at most 65536.
+ *
+ * Readings: a queue's entries follow the stable split order (request order);
+ * the command identifier is the ring slot; a call consumes a window of each
+ * bucket no longer than the free slots, so a batch larger than the rings
+ * drains over several calls; a consumed request that cannot be expressed
+ * (PRP not OK, length not a whole number of blocks, more than 65536 blocks) is
+ * skipped without a slot, so the ring never holds a hole.
+ *
+ * Pinned by: entries rebuilt field by field with Python's struct module from
+ * the NVMe field table, and a replay of every queue as a Python deque fed
+ * from a NumPy stable sort, over several calls that drain a batch.
+ * ------------------------------------------------------------------------ */
+static void put_le32(uint8_t *p, uint32_t v)
+{
+    p[0] = (uint8_t)v;
+    p[1] = (uint8_t)(v >> 8);
+    p[2] = (uint8_t)(v >> 16);
+    p[3] = (uint8_t)(v >> 24);
+}
+
+static void put_le64(uint8_t *p, uint64_t v)
+{
+    put_le32(p, (uint32_t)v);
+    put_le32(p + 4, (uint32_t)(v >> 32));
+}
+
+void orc_emit_sqe(const uint32_t *perm, const uint64_t *qoff, uint32_t nqueues,
+                  const uint8_t *status, const uint64_t *len, const uint64_t *slba,
+                  const uint64_t *prp1, const uint64_t *prp2, uint64_t n,
+                  uint8_t opcode, uint32_t nsid, unsigned lba_shift,
+                  uint8_t *const *ring, const uint32_t *depth, const uint32_t *free_slots,
+                  uint32_t *tail, uint64_t *cursor, uint32_t *placed, uint32_t *slot)
+{
+    const uint64_t block = 1ull << lba_shift;
+    for (uint32_t q = 0; q < nqueues; ++q) {
+        placed[q] = 0;
+        const uint32_t d = depth[q];
+        if (ring[q] == NULL || d < 2 || d > 65536 || tail[q] >= d) continue;   /* refused */
+
+        /* The window: the next entries of bucket q, no more than the ring takes. */
+        const uint64_t size = qoff[q + 1] - qoff[q];
+        const uint64_t left = cursor[q] < size ? size - cursor[q] : 0;
+        uint64_t room = free_slots[q] < d - 1 ? free_slots[q] : d - 1;
+        const uint64_t w = room < left ? room : left;
+
+        uint32_t k = 0;
+        for (uint64_t j = 0; j < w; ++j) {
+            const uint32_t i = perm[qoff[q] + cursor[q] + j];
+            if (i >= n) continue;                 /* not a request of this batch */
+            const uint64_t blocks = len[i] / block;
+            const int placeable = status[i] == ORC_OK && len[i] % block == 0 &&
+                                  blocks >= 1 && blocks <= 65536;
+            if (!placeable) {
+                slot[i] = UINT32_MAX;
+                continue;
+            }
+            const uint32_t s = (tail[q] + k) % d;
+            ++k;
+            slot[i] = s;
+            uint8_t *e = ring[q] + (uint64_t)s * 64;
+            memset(e, 0, 64);
+            put_le32(e + 0, (uint32_t)opcode | (s << 16));
+            put_le32(e + 4, nsid);
+            put_le64(e + 24, prp1[i]);
+            put_le64(e + 32, prp2[i]);
+            put_le64(e + 40, slba[i]);
+            put_le32(e + 48, (uint32_t)(blocks - 1));
+        }
+        placed[q] = k;
+        tail[q] = (tail[q] + k) % d;
+        cursor[q] += w;
+    }
+}
+
+/* ------------------------------------------------------------------------
  * O4  Registration cache with reference counts.
  *
  * [NCCL-26] "Communicator User Registration Cache": register rounds the range

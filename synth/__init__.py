@@ -22,6 +22,8 @@ WORKLOADS = {"tiny": 1, "small": 2, "large": 3, "mrheavy": 4, "mixed": 5}
 HEAP_VA_BASE = 0x0000700000000000
 PHYS_BASE = 0x0000200000000000
 LIST_BUS_BASE = 0x0000100000000000
+NS_BLOCKS = 1 << 40
+SLBA_STREAM = 0x51BA51BA51BA51BA
 
 
 class _Shape(ctypes.Structure):
@@ -63,6 +65,8 @@ def _lib():
         lib.synth_fill.argtypes = [ctypes.c_int, ctypes.c_uint64, ctypes.c_uint64,
                                    p64, p64, p64, p32, p64, p64, p32]
         lib.synth_fill.restype = ctypes.c_int
+        lib.synth_fill_slba.argtypes = [ctypes.c_int, ctypes.c_uint64, ctypes.c_uint64, p64]
+        lib.synth_fill_slba.restype = ctypes.c_int
         _lib_handle = lib
     return _lib_handle
 
@@ -112,4 +116,13 @@ def generate(name: str, n: int | None = None, seed: int = 0) -> dict:
     out = dict(sh)
     out.update(name=name, n=n, lut=lut, rstart=rstart, rend=rend, rlkey=rlkey,
                off=off, len=ln, qid=qid)
+    return out
+
+
+def slba(name: str, n: int, seed: int = 0) -> np.ndarray:
+    """Starting logical block of each of `n` requests of workload `name`
+    (uniform over the namespace, room left for a 65536-block command)."""
+    out = np.empty(n, dtype=np.uint64)
+    if _lib().synth_fill_slba(WORKLOADS[name], seed, n, _ptr(out, ctypes.c_uint64)) != 0:
+        raise ValueError(name)
     return out

@@ -209,3 +209,12 @@ int synth_fill(int w, uint64_t seed, uint64_t n,
     }
     return 0;
 }
+
+int synth_fill_slba(int w, uint64_t seed, uint64_t n, uint64_t *slba)
+{
+    synth_shape sh;
+    if (synth_shape_of(w, &sh) != 0) return -1;
+    rng_t r = { (seed ? seed : sh.default_seed) ^ SYNTH_SLBA_STREAM };
+    for (uint64_t i = 0; i < n; ++i) slba[i] = below(&r, SYNTH_NS_BLOCKS - 65536 + 1);
+    return 0;
+}

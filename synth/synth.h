@@ -73,6 +73,17 @@ int synth_fill(int workload, uint64_t seed, uint64_t n,
                uint64_t *lut, uint64_t *rstart, uint64_t *rend, uint32_t *rlkey,
                uint64_t *off, uint64_t *len, uint32_t *qid);
 
+/*
+ * Starting logical block of each request for the submission-entry stage:
+ * uniform over a namespace of SYNTH_NS_BLOCKS blocks, leaving room for the
+ * largest command (65536 blocks). Drawn from a stream of its own (the
+ * workload's seed xor SYNTH_SLBA_STREAM), so it does not disturb the arrays of
+ * synth_fill. Returns 0, or -1 for an unknown workload.
+ */
+#define SYNTH_NS_BLOCKS     (1ull << 40)
+#define SYNTH_SLBA_STREAM   0x51BA51BA51BA51BAull
+int synth_fill_slba(int workload, uint64_t seed, uint64_t n, uint64_t *slba);
+
 #ifdef __cplusplus
 }
 #endif

@@ -99,3 +99,37 @@ def stable_split(qid: np.ndarray, nqueues: int):
     counts = np.bincount(b, minlength=nqueues + 1)
     qoff = np.concatenate([[0], np.cumsum(counts)]).astype(np.uint64)
     return perm, qoff, int(counts[nqueues])
+
+
+# NVMe common command format, little endian: opcode, flags, command id,
+# namespace id, CDW2-3, metadata pointer, PRP1, PRP2, starting LBA (CDW10-11),
+# CDW12 (number of blocks minus one in bits 15:0, flags above), CDW13-15.
+SQE_FORMAT = "<BBHI8s8sQQQHH12s"
+
+
+def pack_sqe(opcode: int, cid: int, nsid: int, prp1: int, prp2: int, slba: int,
+             nlb0: int) -> bytes:
+    """One 64-byte submission entry laid out field by field."""
+    import struct
+    return struct.pack(SQE_FORMAT, opcode, 0, cid, nsid, bytes(8), bytes(8), prp1, prp2,
+                       slba, nlb0, 0, bytes(12))
+
+
+def unpack_sqe(raw: bytes) -> dict:
+    import struct
+    f = struct.unpack(SQE_FORMAT, bytes(raw))
+    return dict(opcode=f[0], flags=f[1], cid=f[2], nsid=f[3], cdw2_3=f[4], mptr=f[5],
+                prp1=f[6], prp2=f[7], slba=f[8], nlb0=f[9], cdw12_hi=f[10], rest=f[11])
+
+
+def queue_feed(qid, status, length, lba_shift, q):
+    """Request indices of queue q in request order, with whether each can be
+    expressed as one command (PRP built, whole blocks, 1..65536 blocks)."""
+    idx = np.flatnonzero(np.asarray(qid) == q)
+    block = 1 << lba_shift
+    out = []
+    for i in idx:
+        ln = int(length[i])
+        ok = int(status[i]) == 0 and ln > 0 and ln % block == 0 and ln // block <= 65536
+        out.append((int(i), ok))
+    return out
