@@ -10,18 +10,25 @@
  *                              NVMe PRP1/PRP2 and chained PRP lists
  *   dmadesc_partition_by_queue stable split of the requests by destination queue
  *
+ * and one stage after them:
+ *
+ *   dmadesc_emit_sqe           64-byte NVMe submission entries in per-queue
+ *                              rings, one window of the split per call
+ *
  * Sources (web pages, cited by title and section):
  *   [NCCL-26] "NCCL 专家课程 26：GPUDirect RDMA、DMA-BUF、MR 与注册缓存",
  *             sections "IB Backend MR Cache" and
  *             "Communicator User Registration Cache".
  *   [UPCIE]   xNVMe "uPCIe CUDA" backend: introduction, "Memory Architecture",
- *             "Choosing the GPU and Heap Sizes", "Limitations".
+ *             "Choosing the GPU and Heap Sizes", "GPU-Resident Queue API",
+ *             "Limitations".
  *   [MORI]    "mori通信库分析(一)——对称内存RDMA数据发送过程": the thread-scope
  *             put kernel (ballot / find-first-set / shuffle grouping of lanes by
  *             destination) and the warp-level WQE slot reservation.
  *   [CUFRAMES] "Синхронизация: stream sync, не CUDA events": data written on a
  *             stream is visible to others once that stream is synchronized.
- *   [NVMe]    NVM Express Base Specification PRP rules (not on the pages).
+ *   [NVMe]    NVM Express Base Specification: PRP rules, the common command
+ *             format of a submission entry, queue sizes (not on the pages).
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -76,11 +83,16 @@ enum dmadesc_prp_status {
 enum dmadesc_op {
     DMADESC_OP_MR_LOOKUP = 1,
     DMADESC_OP_BUILD_PRP = 2,
-    DMADESC_OP_PARTITION = 3
+    DMADESC_OP_PARTITION = 3,
+    DMADESC_OP_EMIT_SQE = 4
 };
 
-/* Largest nqueues dmadesc_partition_by_queue accepts. */
+/* Largest nqueues dmadesc_partition_by_queue and dmadesc_emit_sqe accept. */
 #define DMADESC_MAX_QUEUES 256u
+
+/* Deepest submission ring (NVMe queue size limit); also the row stride of
+ * dmadesc_emit_sqe's req_of_slot. */
+#define DMADESC_SQ_MAX_DEPTH 65536u
 
 /*
  * dmadesc_mr_lookup - page-rounded containment lookup.
@@ -187,8 +199,67 @@ int dmadesc_partition_by_queue(const uint32_t *qid, uint64_t n, uint32_t nqueues
                                uint32_t *perm, uint64_t *qoff, uint64_t *n_invalid,
                                void *ws, size_t ws_bytes, void *stream);
 
+/*
+ * dmadesc_emit_sqe - NVMe submission entries per queue, one window per call.
+ *
+ * [UPCIE] "GPU-Resident Queue API": a kernel fills the submission queue with
+ * 64-byte entries, each written as four 16-byte stores that the L2 merges
+ * before they leave the GPU. [MORI] warp-level WQE reservation: the requests
+ * bound for one queue take consecutive slots from its tail, which then moves
+ * on by their number. Entry layout [NVMe]: dword 0 = opcode | command id << 16
+ * (fused and PRP/SGL bits 0), dword 1 = nsid, dwords 2-5 = 0, dwords 6-9 =
+ * PRP1, PRP2, dwords 10-11 = starting LBA, dword 12 = blocks - 1 (bits 15:0),
+ * dwords 13-15 = 0. The command id is the ring slot.
+ *
+ * Inputs (device unless noted):
+ *   perm, qoff   the output of dmadesc_partition_by_queue for these n
+ *                requests with the same nqueues (qoff: nqueues + 2 entries)
+ *   status       u8[n]  dmadesc_build_prp's status
+ *   len, slba    u64[n] byte length (as given to dmadesc_build_prp) and
+ *                starting logical block of each request
+ *   prp1, prp2   u64[n] dmadesc_build_prp's outputs
+ *   opcode       0..255 (host), e.g. 0x02 read, 0x01 write, else -EINVAL
+ *   nsid         namespace id (host)
+ *   lba_shift    log2 of the logical block size, 9..16 (host), else -EINVAL
+ *   ring         u64[nqueues] device address of queue q's ring of depth[q]
+ *                64-byte entries
+ *   depth        u32[nqueues] ring size in entries
+ *   free_slots   u32[nqueues] slots the caller allows this call to fill
+ * In/out:
+ *   tail         u32[nqueues] next slot to fill; advanced mod depth[q]
+ *   cursor       u64[nqueues] entries of bucket q consumed by earlier calls;
+ *                advanced by this call's window
+ * Outputs:
+ *   placed       u32[nqueues] entries written into ring q by this call
+ *   req_of_slot  u32[nqueues * DMADESC_SQ_MAX_DEPTH] or NULL: for every slot s
+ *                this call fills in ring q, entry q * 65536 + s receives the
+ *                request index (to map a completion's command id back)
+ * Per queue q: the queue is refused (nothing read, consumed or written, tail
+ * and cursor unchanged, placed[q] = 0) when ring[q] is 0 or not 64-byte
+ * aligned, depth[q] is outside [2, 65536] or tail[q] >= depth[q]. Otherwise
+ * the call consumes W = min(free_slots[q], depth[q] - 1, bucket size -
+ * cursor[q]) entries of bucket q after the first cursor[q]; in that order,
+ * every consumed request that is placeable -- status OK and len a positive
+ * multiple of 2^lba_shift of at most 65536 blocks -- gets the next slot from
+ * tail[q]; the others are consumed without a slot, so the ring holds no hole.
+ * Calls with cursor carried over drain a batch larger than the rings. The
+ * overflow bucket (qid >= nqueues) is never consumed. Slots outside the ones
+ * filled, and req_of_slot entries for them, are not written. Outputs must not
+ * overlap inputs (tail and cursor are updated in place). Memory safety needs
+ * perm/qoff to come from the split of these n requests and each ring and
+ * req_of_slot to have the stated size.
+ * Workspace: dmadesc_workspace_bytes(DMADESC_OP_EMIT_SQE, n, nqueues).
+ */
+int dmadesc_emit_sqe(const uint32_t *perm, const uint64_t *qoff, uint32_t nqueues,
+                     const uint8_t *status, const uint64_t *len, const uint64_t *slba,
+                     const uint64_t *prp1, const uint64_t *prp2, uint64_t n,
+                     uint32_t opcode, uint32_t nsid, uint32_t lba_shift,
+                     const uint64_t *ring, const uint32_t *depth, const uint32_t *free_slots,
+                     uint32_t *tail, uint64_t *cursor, uint32_t *placed,
+                     uint32_t *req_of_slot, void *ws, size_t ws_bytes, void *stream);
+
 /* Workspace bytes needed by `op` for n requests (`param` = nqueues for
- * DMADESC_OP_PARTITION, ignored otherwise). Returns 0 for an unknown op or
+ * DMADESC_OP_PARTITION and DMADESC_OP_EMIT_SQE, ignored otherwise). Returns 0 for an unknown op or
  * for an op that needs none. Host-only; launches nothing. */
 size_t dmadesc_workspace_bytes(int op, uint64_t n, uint32_t param);
 

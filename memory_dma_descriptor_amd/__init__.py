@@ -14,14 +14,16 @@ import torch
 
 from . import _build
 
-__all__ = ["mr_lookup", "build_prp", "partition_by_queue", "workspace_bytes",
-           "DmadescError", "lib", "LIB_PATH", "MAX_QUEUES",
+__all__ = ["mr_lookup", "build_prp", "partition_by_queue", "emit_sqe", "ring_addresses",
+           "workspace_bytes", "DmadescError", "lib", "LIB_PATH", "MAX_QUEUES",
+           "SQ_MAX_DEPTH",
            "MISS", "EXACT", "CONTAINED", "INVALID",
            "PRP_OK", "PRP_EINVAL", "PRP_ERANGE", "PRP_ENOSPC"]
 
 LIB_PATH = _build.LIB
 MAX_QUEUES = 256
-OP_MR_LOOKUP, OP_BUILD_PRP, OP_PARTITION = 1, 2, 3
+SQ_MAX_DEPTH = 65536
+OP_MR_LOOKUP, OP_BUILD_PRP, OP_PARTITION, OP_EMIT_SQE = 1, 2, 3, 4
 MISS, EXACT, CONTAINED, INVALID = 0, 1, 2, 3
 PRP_OK, PRP_EINVAL, PRP_ERANGE, PRP_ENOSPC = 0, 1, 2, 3
 
@@ -37,6 +39,8 @@ _EXPORTS = {
                            _P, _P, _P, _P, _P, _SIZE, _P], ctypes.c_int),
     "dmadesc_partition_by_queue": ([_P, _U64, _U32, _P, _P, _P, _P, _SIZE, _P],
                                    ctypes.c_int),
+    "dmadesc_emit_sqe": ([_P, _P, _U32, _P, _P, _P, _P, _P, _U64, _U32, _U32, _U32,
+                          _P, _P, _P, _P, _P, _P, _P, _P, _SIZE, _P], ctypes.c_int),
     "dmadesc_workspace_bytes": ([ctypes.c_int, _U64, _U32], _SIZE),
     "dmadesc_strerror": ([ctypes.c_int], ctypes.c_char_p),
     "dmadesc_version": ([], ctypes.c_int),
@@ -172,3 +176,45 @@ def partition_by_queue(qid: torch.Tensor, nqueues: int, out: dict | None = None,
         ws.data_ptr(), ws.numel(), _stream(dev, stream))
     _check("dmadesc_partition_by_queue", rc)
     return out
+
+
+def ring_addresses(rings, device=None) -> torch.Tensor:
+    """u64 device tensor of ring base addresses (None -> 0, a refused queue)
+    from a list of device tensors holding depth x 64 bytes each."""
+    addrs = [0 if r is None else r.data_ptr() for r in rings]
+    if device is None:
+        device = next(r.device for r in rings if r is not None)
+    return torch.tensor(addrs, dtype=torch.int64).view(torch.uint64).to(device)
+
+
+def emit_sqe(perm: torch.Tensor, qoff: torch.Tensor, status: torch.Tensor,
+             length: torch.Tensor, slba: torch.Tensor, prp1: torch.Tensor,
+             prp2: torch.Tensor, ring: torch.Tensor, depth: torch.Tensor,
+             free_slots: torch.Tensor, tail: torch.Tensor, cursor: torch.Tensor,
+             placed: torch.Tensor | None = None, req_of_slot: torch.Tensor | None = None,
+             opcode: int = 0x02, nsid: int = 1, lba_shift: int = 9,
+             ws: torch.Tensor | None = None, stream=None) -> dict:
+    """NVMe submission entries for one window of each queue's bucket.
+    `ring` holds each queue's ring address (see ring_addresses); `tail` and
+    `cursor` are updated in place. Returns dict(placed, tail, cursor,
+    req_of_slot)."""
+    n = status.numel()
+    nq = ring.numel()
+    dev = status.device
+    if placed is None:
+        placed = torch.empty(nq, dtype=torch.uint32, device=dev)
+    rid = 0
+    if req_of_slot is not None:
+        rid = _dev(req_of_slot, torch.uint32, "req_of_slot", nq * SQ_MAX_DEPTH)
+    ws = _workspace(OP_EMIT_SQE, n, nq, dev, ws)
+    rc = lib().dmadesc_emit_sqe(
+        _dev(perm, torch.uint32, "perm", n), _dev(qoff, torch.uint64, "qoff", nq + 2), nq,
+        _dev(status, torch.uint8, "status", n), _dev(length, torch.uint64, "len", n),
+        _dev(slba, torch.uint64, "slba", n), _dev(prp1, torch.uint64, "prp1", n),
+        _dev(prp2, torch.uint64, "prp2", n), n, opcode, nsid, lba_shift,
+        _dev(ring, torch.uint64, "ring", nq), _dev(depth, torch.uint32, "depth", nq),
+        _dev(free_slots, torch.uint32, "free_slots", nq), _dev(tail, torch.uint32, "tail", nq),
+        _dev(cursor, torch.uint64, "cursor", nq), _dev(placed, torch.uint32, "placed", nq),
+        rid, ws.data_ptr(), ws.numel(), _stream(dev, stream))
+    _check("dmadesc_emit_sqe", rc)
+    return dict(placed=placed, tail=tail, cursor=cursor, req_of_slot=req_of_slot)

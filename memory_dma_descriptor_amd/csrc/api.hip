@@ -37,6 +37,9 @@ size_t dmadesc_workspace_bytes(int op, uint64_t n, uint32_t param)
     case DMADESC_OP_PARTITION:
         if (param == 0 || param > DMADESC_MAX_QUEUES) return 0;
         return dd::ws_partition(n, param);
+    case DMADESC_OP_EMIT_SQE:
+        if (param == 0 || param > DMADESC_MAX_QUEUES) return 0;
+        return dd::ws_emit_sqe(param);
     default: return 0;
     }
 }
@@ -94,6 +97,25 @@ int dmadesc_partition_by_queue(const uint32_t *qid, uint64_t n, uint32_t nqueues
     if (n > 0 && (!ws || ws_bytes < need)) return -EINVAL;
     dd::SplitArgs a{qid, n, nqueues, perm, qoff, n_invalid, ws};
     return launched(dd::launch_partition(a, static_cast<hipStream_t>(stream)));
+}
+
+int dmadesc_emit_sqe(const uint32_t *perm, const uint64_t *qoff, uint32_t nqueues,
+                     const uint8_t *status, const uint64_t *len, const uint64_t *slba,
+                     const uint64_t *prp1, const uint64_t *prp2, uint64_t n,
+                     uint32_t opcode, uint32_t nsid, uint32_t lba_shift,
+                     const uint64_t *ring, const uint32_t *depth, const uint32_t *free_slots,
+                     uint32_t *tail, uint64_t *cursor, uint32_t *placed,
+                     uint32_t *req_of_slot, void *ws, size_t ws_bytes, void *stream)
+{
+    if (nqueues == 0 || nqueues > DMADESC_MAX_QUEUES) return -EINVAL;
+    if (n >= kMaxN || opcode > 0xFFu || lba_shift < 9 || lba_shift > 16) return -EINVAL;
+    if (!qoff || !ring || !depth || !free_slots || !tail || !cursor || !placed) return -EINVAL;
+    if (n > 0 && (!perm || !status || !len || !slba || !prp1 || !prp2)) return -EINVAL;
+    const size_t need = dd::ws_emit_sqe(nqueues);
+    if (!ws || ws_bytes < need) return -EINVAL;
+    dd::SqeArgs a{perm, qoff, nqueues, status, len, slba, prp1, prp2, n, opcode, nsid, lba_shift,
+                  ring, depth, free_slots, tail, cursor, placed, req_of_slot, ws};
+    return launched(dd::launch_emit_sqe(a, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

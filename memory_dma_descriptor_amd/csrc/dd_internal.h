@@ -42,12 +42,30 @@ struct SplitArgs {
     void *ws;
 };
 
+struct SqeArgs {
+    const uint32_t *perm;
+    const uint64_t *qoff;
+    uint32_t nqueues;
+    const uint8_t *status;
+    const uint64_t *len, *slba, *prp1, *prp2;
+    uint64_t n;
+    uint32_t opcode, nsid, lba_shift;
+    const uint64_t *ring;
+    const uint32_t *depth, *free_slots;
+    uint32_t *tail;
+    uint64_t *cursor;
+    uint32_t *placed, *req_of_slot;
+    void *ws;
+};
+
 hipError_t launch_mr_lookup(const LookupArgs &a, hipStream_t s);
 hipError_t launch_build_prp(const PrpArgs &a, hipStream_t s);
 hipError_t launch_partition(const SplitArgs &a, hipStream_t s);
+hipError_t launch_emit_sqe(const SqeArgs &a, hipStream_t s);
 
 size_t ws_build_prp(uint64_t n);
 size_t ws_partition(uint64_t n, uint32_t nqueues);
+size_t ws_emit_sqe(uint32_t nqueues);
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 

@@ -139,11 +139,11 @@ def partition(qid, nqueues):
 
 
 def emit_sqe(perm, qoff, status, length, slba, prp1, prp2, rings, depth, free_slots,
-             tail, cursor, slot=None, opcode=0x02, nsid=1, lba_shift=9):
+             tail, cursor, req_of_slot=None, opcode=0x02, nsid=1, lba_shift=9):
     """Runs O5 for one call. `rings` is a list of u8[depth[q], 64] arrays (or
-    None for a refused queue), updated in place. Returns dict(tail, cursor,
-    placed, slot) with new arrays; `slot` (u32[n]) is copied first when given,
-    else starts as all 0xFFFFFFFF."""
+    None for a refused queue) and `req_of_slot` a u32[nqueues, 65536] array
+    (or None); both are updated in place. Returns dict(tail, cursor, placed)
+    with new arrays."""
     perm, qoff = _u32(perm), _u64(qoff)
     status = np.ascontiguousarray(status, dtype=np.uint8)
     length, slba, prp1, prp2 = _u64(length), _u64(slba), _u64(prp1), _u64(prp2)
@@ -151,8 +151,9 @@ def emit_sqe(perm, qoff, status, length, slba, prp1, prp2, rings, depth, free_sl
     depth, free_slots = _u32(depth), _u32(free_slots)
     tail, cursor = _u32(tail).copy(), _u64(cursor).copy()
     n = length.shape[0]
-    slot = (np.full(n, 0xFFFFFFFF, np.uint32) if slot is None else _u32(slot).copy())
     placed = np.zeros(nq, np.uint32)
+    if req_of_slot is not None:
+        assert req_of_slot.dtype == np.uint32 and req_of_slot.size >= nq * 65536
     ring_ptrs = (_u8p * max(nq, 1))()
     for q, r in enumerate(rings):
         if r is not None:
@@ -162,8 +163,8 @@ def emit_sqe(perm, qoff, status, length, slba, prp1, prp2, rings, depth, free_sl
                         _p(length, _u64p), _p(slba, _u64p), _p(prp1, _u64p), _p(prp2, _u64p),
                         n, opcode, nsid, lba_shift, ring_ptrs, _p(depth, _u32p),
                         _p(free_slots, _u32p), _p(tail, _u32p), _p(cursor, _u64p),
-                        _p(placed, _u32p), _p(slot, _u32p))
-    return dict(tail=tail, cursor=cursor, placed=placed, slot=slot)
+                        _p(placed, _u32p), _p(req_of_slot, _u32p))
+    return dict(tail=tail, cursor=cursor, placed=placed)
 
 
 class Registry:

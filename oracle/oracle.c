@@ -245,7 +245,9 @@ void orc_partition(const uint32_t *qid, uint64_t n, uint32_t nqueues,
  * bucket no longer than the free slots, so a batch larger than the rings
  * drains over several calls; a consumed request that cannot be expressed
  * (PRP not OK, length not a whole number of blocks, more than 65536 blocks) is
- * skipped without a slot, so the ring never holds a hole.
+ * skipped without a slot, so the ring never holds a hole; the request index
+ * of every filled slot is recorded beside the ring, which is what turns a
+ * completion's command identifier back into a request.
  *
  * Pinned by: entries rebuilt field by field with Python's struct module from
  * the NVMe field table, and a replay of every queue as a Python deque fed
@@ -270,7 +272,7 @@ void orc_emit_sqe(const uint32_t *perm, const uint64_t *qoff, uint32_t nqueues,
                   const uint64_t *prp1, const uint64_t *prp2, uint64_t n,
                   uint8_t opcode, uint32_t nsid, unsigned lba_shift,
                   uint8_t *const *ring, const uint32_t *depth, const uint32_t *free_slots,
-                  uint32_t *tail, uint64_t *cursor, uint32_t *placed, uint32_t *slot)
+                  uint32_t *tail, uint64_t *cursor, uint32_t *placed, uint32_t *req_of_slot)
 {
     const uint64_t block = 1ull << lba_shift;
     for (uint32_t q = 0; q < nqueues; ++q) {
@@ -291,13 +293,10 @@ void orc_emit_sqe(const uint32_t *perm, const uint64_t *qoff, uint32_t nqueues,
             const uint64_t blocks = len[i] / block;
             const int placeable = status[i] == ORC_OK && len[i] % block == 0 &&
                                   blocks >= 1 && blocks <= 65536;
-            if (!placeable) {
-                slot[i] = UINT32_MAX;
-                continue;
-            }
+            if (!placeable) continue;
             const uint32_t s = (tail[q] + k) % d;
             ++k;
-            slot[i] = s;
+            if (req_of_slot) req_of_slot[(uint64_t)q * 65536 + s] = i;
             uint8_t *e = ring[q] + (uint64_t)s * 64;
             memset(e, 0, 64);
             put_le32(e + 0, (uint32_t)opcode | (s << 16));

@@ -79,17 +79,17 @@ void orc_partition(const uint32_t *qid, uint64_t n, uint32_t nqueues,
  * (left = bucket size - cursor[q], or 0). In bucket order, each consumed
  * request that is placeable (status OK; length a positive multiple of
  * 2^lba_shift of at most 65536 blocks) takes ring slot (tail[q] + k) % depth[q]
- * for k = 0, 1, ... and gets a 64-byte entry there; slot[i] = that slot, or
- * UINT32_MAX for a consumed request that is not placeable. Requests not
- * consumed keep their slot[] value. Afterwards placed[q] = k, tail[q] =
- * (tail[q] + k) % depth[q] and cursor[q] += W. ring[q] is u8[depth[q]][64].
+ * for k = 0, 1, ... and gets a 64-byte entry there, and
+ * req_of_slot[q * 65536 + slot] (if req_of_slot is not NULL) receives its
+ * request index. Afterwards placed[q] = k, tail[q] = (tail[q] + k) % depth[q]
+ * and cursor[q] += W. ring[q] is u8[depth[q]][64].
  */
 void orc_emit_sqe(const uint32_t *perm, const uint64_t *qoff, uint32_t nqueues,
                   const uint8_t *status, const uint64_t *len, const uint64_t *slba,
                   const uint64_t *prp1, const uint64_t *prp2, uint64_t n,
                   uint8_t opcode, uint32_t nsid, unsigned lba_shift,
                   uint8_t *const *ring, const uint32_t *depth, const uint32_t *free_slots,
-                  uint32_t *tail, uint64_t *cursor, uint32_t *placed, uint32_t *slot);
+                  uint32_t *tail, uint64_t *cursor, uint32_t *placed, uint32_t *req_of_slot);
 
 /*
  * O4: host registration cache with reference counts ([NCCL-26]).

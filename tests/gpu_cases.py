@@ -186,3 +186,95 @@ def check_split(qid, nq, ctx=""):
                                  f"{bad[0]}: oracle {o[k][bad[0]]} gpu {g[k][bad[0]]}")
     assert o["n_invalid"] == g["n_invalid"], ctx
     return o, g
+
+
+# ------------------------------------------------------ submission entries ---
+
+RING_FILL = 0xEE
+RID_FILL = 0xA5A5A5A5
+
+
+class SqeRig:
+    """Rings, request maps, tails and cursors of both sides for a series of
+    dmadesc_emit_sqe calls. `refuse` queues get ring address 0 (None for the
+    oracle); `misalign` queues get a ring address 16 bytes into a buffer that
+    has room for a whole ring past it (so even a wrong write stays inside it)."""
+
+    def __init__(self, depth, tail, refuse=(), misalign=(), req_map=True):
+        self.depth = np.asarray(depth, np.uint32)
+        nq = self.depth.size
+        self.nq = nq
+        # GPU buffers leave room for slots up to tail + depth, so that even a
+        # queue the library should refuse for its tail could not be written
+        # outside its buffer.
+        rows = [max(int(d), 1) for d in self.depth]
+        grow = [rows[q] + int(np.asarray(tail)[q]) for q in range(nq)]
+        self.o_rings = [None if (q in refuse or q in misalign)
+                        else np.full((rows[q], 64), RING_FILL, np.uint8) for q in range(nq)]
+        self.g_bufs = [torch.full((grow[q] * 64 + 64,), RING_FILL, dtype=torch.uint8,
+                                  device="cuda") for q in range(nq)]
+        addrs = []
+        for q in range(nq):
+            p = self.g_bufs[q].data_ptr()
+            assert p % 256 == 0
+            addrs.append(0 if q in refuse else (p + 16 if q in misalign else p))
+        self.g_ring = torch.tensor(addrs, dtype=torch.int64).view(torch.uint64).cuda()
+        self.o_tail = np.asarray(tail, np.uint32).copy()
+        self.o_cursor = np.zeros(nq, np.uint64)
+        self.g_tail = dev(self.o_tail.copy())
+        self.g_cursor = dev(self.o_cursor.copy())
+        self.g_depth = dev(self.depth)
+        self.o_rid = self.g_rid = None
+        if req_map:
+            self.o_rid = np.full((nq, 65536), RID_FILL, np.uint32)
+            self.g_rid = dev(np.full(nq * 65536, RID_FILL, np.uint32))
+
+    def call(self, o_in, g_in, free, lba_shift=9, opcode=0x02, nsid=1, ctx=""):
+        """o_in / g_in: dict(perm, qoff, status, len, slba, prp1, prp2) as numpy
+        arrays (oracle) and device tensors (GPU). Compares every output."""
+        free = np.asarray(free, np.uint32)
+        say(f"emit_sqe {ctx}: nq={self.nq} n={o_in['len'].size} lba_shift={lba_shift}")
+        o = oracle.emit_sqe(o_in["perm"], o_in["qoff"], o_in["status"], o_in["len"],
+                            o_in["slba"], o_in["prp1"], o_in["prp2"], self.o_rings,
+                            self.depth, free, self.o_tail, self.o_cursor,
+                            req_of_slot=self.o_rid, opcode=opcode, nsid=nsid,
+                            lba_shift=lba_shift)
+        g = dd.emit_sqe(g_in["perm"], g_in["qoff"], g_in["status"], g_in["len"],
+                        g_in["slba"], g_in["prp1"], g_in["prp2"], self.g_ring, self.g_depth,
+                        dev(free), self.g_tail, self.g_cursor, req_of_slot=self.g_rid,
+                        opcode=opcode, nsid=nsid, lba_shift=lba_shift)
+        torch.cuda.synchronize()
+        self.o_tail, self.o_cursor = o["tail"], o["cursor"]
+        for k, want, got in (("placed", o["placed"], host(g["placed"])),
+                             ("tail", o["tail"], host(self.g_tail)),
+                             ("cursor", o["cursor"], host(self.g_cursor))):
+            if not np.array_equal(want, got):
+                bad = np.nonzero(want != got)[0]
+                raise AssertionError(f"{ctx} {k}: queues {bad[:8].tolist()}: oracle "
+                                     f"{want[bad[:8]].tolist()} gpu {got[bad[:8]].tolist()}")
+        for q in range(self.nq):
+            gb = host(self.g_bufs[q])
+            if self.o_rings[q] is None:
+                assert (gb == RING_FILL).all(), f"{ctx} refused queue {q} was written"
+                continue
+            ob = self.o_rings[q].reshape(-1)
+            if not np.array_equal(gb[:ob.size], ob):
+                bad = np.nonzero(gb[:ob.size] != ob)[0]
+                raise AssertionError(f"{ctx} ring {q}: {bad.size} bytes differ, first in "
+                                     f"slot {bad[0] // 64} byte {bad[0] % 64}")
+            assert (gb[ob.size:] == RING_FILL).all(), f"{ctx} ring {q} written past its end"
+        if self.o_rid is not None:
+            gr = host(self.g_rid).reshape(self.nq, 65536)
+            if not np.array_equal(gr, self.o_rid):
+                bad = np.argwhere(gr != self.o_rid)
+                raise AssertionError(f"{ctx} req_of_slot: {len(bad)} differ, first {bad[0]}")
+        return o
+
+
+def sqe_inputs(perm, qoff, status, ln, slba, prp1, prp2):
+    """The same emission inputs as numpy (oracle) and device tensors (GPU)."""
+    o = dict(perm=np.asarray(perm, np.uint32), qoff=np.asarray(qoff, np.uint64),
+             status=np.asarray(status, np.uint8), len=np.asarray(ln, np.uint64),
+             slba=np.asarray(slba, np.uint64), prp1=np.asarray(prp1, np.uint64),
+             prp2=np.asarray(prp2, np.uint64))
+    return o, {k: dev(v) for k, v in o.items()}

@@ -25,7 +25,8 @@ def _declared():
 
 def test_exports_every_declared_symbol():
     names = _declared()
-    assert {"dmadesc_mr_lookup", "dmadesc_build_prp", "dmadesc_partition_by_queue"} <= names
+    assert {"dmadesc_mr_lookup", "dmadesc_build_prp", "dmadesc_partition_by_queue",
+            "dmadesc_emit_sqe"} <= names
     lib = ctypes.CDLL(dd.LIB_PATH)
     for n in sorted(names):
         assert hasattr(lib, n), n
@@ -51,6 +52,11 @@ def test_workspace_sizes():
         assert sizes == sorted(sizes), sizes
         assert sizes[-1] < 1 << 32, sizes                 # small next to the batch itself
     assert ws(dd.OP_PARTITION, 1 << 20, 256) > ws(dd.OP_PARTITION, 1 << 20, 1)
+    # Submission entries: a count per (queue, tile); independent of the batch.
+    assert ws(dd.OP_EMIT_SQE, 100, 0) == 0 and ws(dd.OP_EMIT_SQE, 100, 257) == 0
+    e = [ws(dd.OP_EMIT_SQE, n, q) for q in (1, 64, 256) for n in (0, 1 << 24)]
+    assert all(x % 256 == 0 and x > 0 for x in e) and e[0] == e[1] and e[2] < e[4]
+    assert e[-1] <= 1 << 20
 
 
 EINVAL = -errno.EINVAL
@@ -100,6 +106,19 @@ def test_partition_rejects_bad_arguments():
         assert f(*args) == EINVAL, (k, bad)
 
 
+@no_gpu_only
+def test_emit_sqe_rejects_bad_arguments():
+    f = dd.lib().dmadesc_emit_sqe
+    ok = [P, P, 4, P, P, P, P, P, 8, 2, 1, 9, P, P, P, P, P, P, NULL, P, 1 << 20, NULL]
+    for k, bad in [(2, 0), (2, 257), (8, 1 << 32), (9, 256), (11, 8), (11, 17),
+                   (1, NULL), (12, NULL), (13, NULL), (14, NULL), (15, NULL), (16, NULL),
+                   (17, NULL), (0, NULL), (3, NULL), (4, NULL), (5, NULL), (6, NULL),
+                   (7, NULL), (19, NULL), (20, 16)]:
+        args = list(ok)
+        args[k] = bad
+        assert f(*args) == EINVAL, (k, bad)
+
+
 def test_empty_lookup_is_a_no_op():
     # n == 0 with valid parameters launches nothing and succeeds.
     f = dd.lib().dmadesc_mr_lookup
@@ -107,7 +126,8 @@ def test_empty_lookup_is_a_no_op():
              NULL, 0, NULL) == 0
 
 
-@pytest.mark.parametrize("name", ["mr_lookup", "build_prp", "partition_by_queue"])
+@pytest.mark.parametrize("name", ["mr_lookup", "build_prp", "partition_by_queue",
+                                  "emit_sqe"])
 def test_binding_names_match_abi(name):
     assert callable(getattr(dd, name))
     assert f"dmadesc_{name}" in _declared()

@@ -1,0 +1,216 @@
+"""GPU parity of dmadesc_emit_sqe with the oracle's O5: every ring byte
+(filled slots and untouched ones), the request map, placed counts, tails and
+cursors, bit for bit, over single calls, chained calls that drain a batch, and
+the whole path (PRP build -> split -> entries) at scaled and full size."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import memory_dma_descriptor_amd as dd
+import oracle
+import synth
+from tests import gpu_cases as gc
+
+pytestmark = pytest.mark.gpu
+
+
+def _columns(rng, n, nq, lba_shift=9, bad_p=0.1, max_blocks=300):
+    qid = rng.integers(0, nq + 1, n).astype(np.uint32)              # nq: out of range
+    ln = (rng.integers(1, max_blocks + 1, n).astype(np.uint64) << np.uint64(lba_shift))
+    odd = rng.random(n) < bad_p / 3
+    ln[odd] += np.uint64(4)                                          # not whole blocks
+    status = np.where(rng.random(n) < bad_p / 3, 3, 0).astype(np.uint8)
+    status[rng.random(n) < bad_p / 6] = 1
+    prp1 = rng.integers(0, 1 << 62, n, dtype=np.uint64)
+    prp2 = rng.integers(0, 1 << 62, n, dtype=np.uint64)
+    slba = rng.integers(0, 1 << 62, n, dtype=np.uint64)
+    return qid, status, ln, slba, prp1, prp2
+
+
+def _inputs(qid, nq, status, ln, slba, prp1, prp2):
+    """Oracle inputs from the oracle's split, GPU inputs from the GPU's split."""
+    o_split = oracle.partition(qid, nq)
+    g_split = dd.partition_by_queue(gc.dev(qid), nq)
+    o, _ = gc.sqe_inputs(o_split["perm"], o_split["qoff"], status, ln, slba, prp1, prp2)
+    _, g = gc.sqe_inputs(o_split["perm"], o_split["qoff"], status, ln, slba, prp1, prp2)
+    g["perm"], g["qoff"] = g_split["perm"], g_split["qoff"]
+    return o, g
+
+
+@pytest.mark.parametrize("nq,n,seed", [(1, 1, 1), (1, 5000, 2), (3, 7000, 3), (16, 70_001, 4),
+                                       (64, 200_000, 5), (256, 300_000, 6)])
+def test_one_call(nq, n, seed):
+    rng = np.random.default_rng(seed)
+    qid, *cols = _columns(rng, n, nq)
+    o, g = _inputs(qid, nq, *cols)
+    depth = rng.choice([2, 3, 1024, 1025, 2049, 4096, 65536], nq).astype(np.uint32)
+    tail = (rng.integers(0, 1 << 30, nq) % depth).astype(np.uint32)
+    rig = gc.SqeRig(depth, tail)
+    free = rng.integers(0, 70_000, nq).astype(np.uint32)             # some above depth - 1
+    rig.call(o, g, free, ctx=f"one call nq={nq} n={n}")
+
+
+def test_windows_on_tile_edges():
+    # One queue per window length around multiples of the 1024-entry tile.
+    lens = [1, 1023, 1024, 1025, 2047, 2048, 2049, 65535]
+    nq = len(lens)
+    qid = np.concatenate([np.full(k + 3, q, np.uint32) for q, k in enumerate(lens)])
+    rng = np.random.default_rng(7)
+    qid = qid[rng.permutation(qid.size)]
+    n = qid.size
+    status = np.zeros(n, np.uint8)
+    ln = np.full(n, 4096, np.uint64)
+    ln[rng.random(n) < 0.05] = 100                                   # a few skipped
+    cols = (status, ln, rng.integers(0, 1 << 40, n, dtype=np.uint64),
+            rng.integers(0, 1 << 48, n, dtype=np.uint64), rng.integers(0, 1 << 48, n, dtype=np.uint64))
+    o, g = _inputs(qid, nq, *cols)
+    depth = np.full(nq, 65536, np.uint32)
+    tail = rng.integers(0, 65536, nq).astype(np.uint32)
+    rig = gc.SqeRig(depth, tail)
+    rig.call(o, g, np.array(lens, np.uint32), ctx="tile edges")
+    rig.call(o, g, np.full(nq, 65535, np.uint32), ctx="tile edges, rest")
+
+
+def test_refused_queues():
+    rng = np.random.default_rng(8)
+    nq, n = 8, 20_000
+    qid, *cols = _columns(rng, n, nq)
+    o, g = _inputs(qid, nq, *cols)
+    depth = np.array([64, 1, 65537, 64, 64, 64, 0, 65536], np.uint32)
+    tail = np.array([5, 0, 0, 64, 70, 3, 0, 65535], np.uint32)       # 3, 4: tail >= depth
+    rig = gc.SqeRig(depth, tail, refuse=(1, 2, 3, 4, 5, 6), misalign=(5,))
+    # refuse covers every queue the oracle must see as refused; queue 5 is
+    # refused by its misaligned address alone (its depth and tail are valid).
+    addrs = rig.g_ring.cpu().view(torch.int64)
+    addrs[5] = rig.g_bufs[5].data_ptr() + 16
+    for q in (1, 2, 3, 4):
+        addrs[q] = rig.g_bufs[q].data_ptr()                          # valid address, bad state
+    rig.g_ring.copy_(addrs.view(torch.uint64).cuda())
+    rig.call(o, g, np.full(nq, 1000, np.uint32), ctx="refused")
+
+
+@pytest.mark.parametrize("lba_shift", [9, 12, 16])
+def test_block_limits(lba_shift):
+    blk = 1 << lba_shift
+    rng = np.random.default_rng(lba_shift)
+    n = 4000
+    qid = rng.integers(0, 4, n).astype(np.uint32)
+    blocks = rng.choice([1, 2, 65535, 65536, 65537, 70000], n).astype(np.uint64)
+    ln = blocks * np.uint64(blk)
+    ln[rng.random(n) < 0.05] = np.uint64(0)
+    ln[rng.random(n) < 0.05] += np.uint64(blk // 2)
+    status = np.zeros(n, np.uint8)
+    cols = (status, ln, rng.integers(0, 1 << 50, n, dtype=np.uint64),
+            rng.integers(0, 1 << 50, n, dtype=np.uint64), rng.integers(0, 1 << 50, n, dtype=np.uint64))
+    o, g = _inputs(qid, 4, *cols)
+    rig = gc.SqeRig(np.full(4, 4096, np.uint32), np.array([0, 1, 4094, 4095], np.uint32))
+    rig.call(o, g, np.full(4, 4095, np.uint32), lba_shift=lba_shift, opcode=0x01,
+             nsid=0xFFFFFFFF, ctx=f"block limits shift={lba_shift}")
+
+
+def test_drain_over_many_calls():
+    rng = np.random.default_rng(10)
+    nq, n = 6, 60_000
+    qid, *cols = _columns(rng, n, nq, bad_p=0.2)
+    o, g = _inputs(qid, nq, *cols)
+    depth = np.array([2, 17, 1024, 1500, 4096, 65536], np.uint32)
+    rig = gc.SqeRig(depth, rng.integers(0, 1 << 20, nq).astype(np.uint32) % depth)
+    sizes = np.diff(o["qoff"])[:nq]
+    calls = 0
+    while (rig.o_cursor < sizes).any():
+        # Between calls the controller fetched part of each ring.
+        free = (rng.integers(0, 1 << 20, nq) % depth).astype(np.uint32)
+        if calls < 3 or calls % 50 == 0:
+            rig.call(o, g, free, ctx=f"drain call {calls}")
+        else:                                                      # checked less often
+            oo = oracle.emit_sqe(o["perm"], o["qoff"], o["status"], o["len"], o["slba"],
+                                 o["prp1"], o["prp2"], rig.o_rings, rig.depth, free,
+                                 rig.o_tail, rig.o_cursor, req_of_slot=rig.o_rid)
+            dd.emit_sqe(g["perm"], g["qoff"], g["status"], g["len"], g["slba"], g["prp1"],
+                        g["prp2"], rig.g_ring, rig.g_depth, gc.dev(free), rig.g_tail,
+                        rig.g_cursor, req_of_slot=rig.g_rid)
+            rig.o_tail, rig.o_cursor = oo["tail"], oo["cursor"]
+        calls += 1
+        assert calls < 20_000
+    rig.call(o, g, np.full(nq, 1, np.uint32), ctx="drained")          # nothing left
+    assert (rig.o_cursor == sizes).all()
+
+
+def test_without_request_map_and_empty_batch():
+    rng = np.random.default_rng(11)
+    qid, *cols = _columns(rng, 3000, 5)
+    o, g = _inputs(qid, 5, *cols)
+    rig = gc.SqeRig(np.full(5, 512, np.uint32), np.arange(5, dtype=np.uint32), req_map=False)
+    rig.call(o, g, np.full(5, 511, np.uint32), ctx="no request map")
+    qid, *cols = _columns(rng, 0, 5)
+    o, g = _inputs(qid, 5, *cols)
+    rig = gc.SqeRig(np.full(5, 512, np.uint32), np.arange(5, dtype=np.uint32))
+    rig.call(o, g, np.full(5, 511, np.uint32), ctx="empty batch")
+
+
+def _path_inputs(name, n=None):
+    """The whole path on both sides: PRPs, split, and the LBA column."""
+    d = synth.generate(name, n=n)
+    n, nq = d["n"], d["nqueues"]
+    slba = synth.slba(name, n)
+    # A pool large enough for every list: lists not written by the oracle.
+    o_prp = oracle.build_prp(d["lut"], d["off"], d["len"], d["list_bus_base"], 1 << 50)
+    total = o_prp["total"]
+    g_lut, g_off, g_len = gc.dev(d["lut"]), gc.dev(d["off"]), gc.dev(d["len"])
+    pool = torch.empty((max(total, 1), 512), dtype=torch.uint64, device="cuda")
+    g_prp = dd.build_prp(g_lut, g_off, g_len, d["list_bus_base"], pool)
+    assert int(gc.host(g_prp["total_pages"])[0]) == total
+    o_split = oracle.partition(d["qid"], nq)
+    g_split = dd.partition_by_queue(gc.dev(d["qid"]), nq)
+    o = dict(perm=o_split["perm"], qoff=o_split["qoff"], status=o_prp["status"],
+             len=d["len"], slba=slba, prp1=o_prp["prp1"], prp2=o_prp["prp2"])
+    g = dict(perm=g_split["perm"], qoff=g_split["qoff"], status=g_prp["status"], len=g_len,
+             slba=gc.dev(slba), prp1=g_prp["prp1"], prp2=g_prp["prp2"])
+    return d, o, g, pool
+
+
+@pytest.mark.parametrize("name,n", [("tiny", None), ("small", 300_000), ("large", None),
+                                    ("mixed", 1 << 20)])
+def test_path_scaled(name, n):
+    d, o, g, _pool = _path_inputs(name, n)
+    nq = d["nqueues"]
+    rng = np.random.default_rng(12)
+    rig = gc.SqeRig(np.full(nq, 65536, np.uint32), rng.integers(0, 65536, nq).astype(np.uint32))
+    rig.call(o, g, np.full(nq, 65535, np.uint32), ctx=f"path {name} call 1")
+    rig.call(o, g, rng.integers(0, 65536, nq).astype(np.uint32), ctx=f"path {name} call 2")
+
+
+def test_path_mixed_full_size():
+    d, o, g, pool = _path_inputs("mixed")
+    del pool
+    nq = d["nqueues"]
+    tail = np.random.default_rng(13).integers(0, 65536, nq).astype(np.uint32)
+    rig = gc.SqeRig(np.full(nq, 65536, np.uint32), tail)
+    out = rig.call(o, g, np.full(nq, 65535, np.uint32), ctx="path mixed full")
+    assert int(out["placed"].sum()) > 3_000_000
+
+
+def test_binding_rejects_bad_arguments():
+    rng = np.random.default_rng(14)
+    qid, *cols = _columns(rng, 100, 2)
+    o, g = _inputs(qid, 2, *cols)
+    rig = gc.SqeRig(np.full(2, 8, np.uint32), np.zeros(2, np.uint32))
+    free = gc.dev(np.full(2, 7, np.uint32))
+    args = [g["perm"], g["qoff"], g["status"], g["len"], g["slba"], g["prp1"], g["prp2"],
+            rig.g_ring, rig.g_depth, free, rig.g_tail, rig.g_cursor]
+    with pytest.raises(dd.DmadescError):
+        dd.emit_sqe(*args, lba_shift=8)
+    with pytest.raises(dd.DmadescError):
+        dd.emit_sqe(*args, opcode=256)
+    bad = list(args)
+    bad[3] = g["len"].view(torch.int64)
+    with pytest.raises(TypeError):
+        dd.emit_sqe(*bad)
+    bad = list(args)
+    bad[1] = g["qoff"][:2]
+    with pytest.raises(ValueError):
+        dd.emit_sqe(*bad)
+    torch.cuda.synchronize()
+    assert (gc.host(rig.g_cursor) == 0).all()

@@ -43,9 +43,12 @@ def test_entry_layout_matches_struct_packing():
              slba=np.array([7, 0xFF_FFFF_FFFF, 0], np.uint64))
     perm, qoff = _split(b["qid"], 1)
     ring = np.full((8, 64), 0xAB, np.uint8)
+    rid = np.full((1, 65536), NONE, np.uint32)
     out = oracle.emit_sqe(perm, qoff, b["status"], b["length"], b["slba"], b["prp1"],
-                          b["prp2"], [ring], [8], [7], [6], [0], opcode=0x02, nsid=0x11223344)
-    assert out["slot"].tolist() == [6, 7, 0]
+                          b["prp2"], [ring], [8], [7], [6], [0], req_of_slot=rid,
+                          opcode=0x02, nsid=0x11223344)
+    assert rid[0, [6, 7, 0]].tolist() == [0, 1, 2]
+    assert (np.delete(rid[0], [6, 7, 0]) == NONE).all()
     assert out["tail"].tolist() == [1] and out["cursor"].tolist() == [3]
     assert out["placed"].tolist() == [3]
     for i, s in enumerate([6, 7, 0]):
@@ -60,7 +63,7 @@ def test_entry_layout_matches_struct_packing():
 
 def _replay(b, nq, rings, depth, free, tail, cursor, lba_shift=9, opcode=2, nsid=1):
     """The expected result of one call, queue by queue, as deques."""
-    slot = {}
+    slot = {}                                             # (queue, slot) -> request
     tail, cursor = list(tail), list(cursor)
     placed = [0] * nq
     for q in range(nq):
@@ -77,11 +80,10 @@ def _replay(b, nq, rings, depth, free, tail, cursor, lba_shift=9, opcode=2, nsid
             i, ok = feed.popleft()
             took += 1
             if not ok:
-                slot[i] = NONE
                 continue
             s = (int(tail[q]) + placed[q]) % d
             placed[q] += 1
-            slot[i] = s
+            slot[(q, s)] = i
             rings[q][s] = np.frombuffer(bf.pack_sqe(
                 opcode, s, nsid, int(b["prp1"][i]), int(b["prp2"][i]), int(b["slba"][i]),
                 int(b["length"][i]) // (1 << lba_shift) - 1), np.uint8)
@@ -104,13 +106,14 @@ def test_one_call_matches_deque_replay(nq, n, seed):
     want_rings = [r.copy() for r in got_rings]
     if nq > 2:
         got_rings[2] = want_rings[2] = None               # refused queue
+    rid = np.full((nq, 65536), NONE, np.uint32)
     out = oracle.emit_sqe(perm, qoff, b["status"], b["length"], b["slba"], b["prp1"],
-                          b["prp2"], got_rings, depth, free, tail, cursor)
+                          b["prp2"], got_rings, depth, free, tail, cursor, req_of_slot=rid)
     slot, wtail, wcursor, wplaced = _replay(b, nq, want_rings, depth, free, tail, cursor)
-    want_slot = np.full(n, NONE, np.uint32)
-    for i, s in slot.items():
-        want_slot[i] = s
-    np.testing.assert_array_equal(out["slot"], want_slot)
+    want_rid = np.full((nq, 65536), NONE, np.uint32)
+    for (q, s), i in slot.items():
+        want_rid[q, s] = i
+    np.testing.assert_array_equal(rid, want_rid)
     assert out["tail"].tolist() == wtail
     assert out["cursor"].tolist() == wcursor
     assert out["placed"].tolist() == wplaced
@@ -131,12 +134,16 @@ def test_refused_queues_and_block_limits(lba_shift):
     depth = np.array([1, 65537, 4, 4, 65536], np.uint32)
     tail = np.array([0, 0, 4, 3, 65535], np.uint32)       # queue 2: tail == depth
     rings = [np.zeros((max(int(d), 1), 64), np.uint8) for d in depth]
+    rid = np.full((5, 65536), NONE, np.uint32)
     out = oracle.emit_sqe(perm, qoff, b["status"], b["length"], b["slba"], b["prp1"],
-                          b["prp2"], rings, depth, [9] * 5, tail, [0] * 5, lba_shift=lba_shift)
+                          b["prp2"], rings, depth, [9] * 5, tail, [0] * 5, req_of_slot=rid,
+                          lba_shift=lba_shift)
     assert out["placed"].tolist() == [0, 0, 0, 1, 1]
     assert out["cursor"].tolist() == [0, 0, 0, 1, 2]
     assert out["tail"].tolist() == [0, 0, 4, 0, 0]
-    assert out["slot"].tolist() == [NONE, NONE, NONE, 3, NONE, 65535]
+    assert (rid[:3] == NONE).all()
+    assert rid[3, 3] == 3 and rid[4, 65535] == 5
+    assert (rid != NONE).sum() == 2
     assert bf.unpack_sqe(rings[4][65535])["nlb0"] == 65535
 
 
@@ -150,31 +157,29 @@ def test_drain_places_every_expressible_request_once_in_order():
     cursor = np.zeros(nq, np.uint64)
     rings = [np.zeros((int(d), 64), np.uint8) for d in depth]
     seen = [[] for _ in range(nq)]
-    expect_slot = np.full(n, 0x12345678, np.uint32)
-    slot = expect_slot.copy()
+    rid = np.full((nq, 65536), NONE, np.uint32)
     for _ in range(2000):
         prev_tail = tail.copy()
         # The controller has fetched everything: the whole ring is free.
         out = oracle.emit_sqe(perm, qoff, b["status"], b["length"], b["slba"], b["prp1"],
-                              b["prp2"], rings, depth, depth - 1, tail, cursor, slot=slot)
+                              b["prp2"], rings, depth, depth - 1, tail, cursor,
+                              req_of_slot=rid)
         for q in range(nq):
+            assert out["placed"][q] <= depth[q] - 1
             for k in range(int(out["placed"][q])):
                 s = (int(prev_tail[q]) + k) % int(depth[q])
                 f = bf.unpack_sqe(rings[q][s])
                 assert f["cid"] == s
-                seen[q].append((f["prp1"], f["slba"], f["nlb0"]))
-        tail, cursor, slot = out["tail"], out["cursor"], out["slot"]
+                i = int(rid[q, s])
+                assert f["prp1"] == int(b["prp1"][i])
+                seen[q].append((i, f["slba"], f["nlb0"]))
+        tail, cursor = out["tail"], out["cursor"]
         if (cursor == np.diff(qoff)[:nq]).all():
             break
     for q in range(nq):
         feed = bf.queue_feed(b["qid"], b["status"], b["length"], 9, q)
-        want = [(int(b["prp1"][i]), int(b["slba"][i]), int(b["length"][i]) // 512 - 1)
-                for i, ok in feed if ok]
+        want = [(i, int(b["slba"][i]), int(b["length"][i]) // 512 - 1) for i, ok in feed if ok]
         assert seen[q] == want
-    bad = [i for q in range(nq) for i, ok in bf.queue_feed(b["qid"], b["status"],
-                                                             b["length"], 9, q) if not ok]
-    assert (slot[bad] == NONE).all()
-    assert (slot[b["qid"] == nq] == 0x12345678).all()     # out-of-range queue: never consumed
 
 
 def test_empty_batch_and_zero_free():
