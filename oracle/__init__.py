@@ -49,6 +49,8 @@ def _lib():
         lib.orc_build_prp.argtypes = [_u64p, u64, _u64p, _u64p, u64, u64, _u64p, u64,
                                       _u64p, _u64p, _u8p, _u64p]
         lib.orc_build_prp.restype = None
+        lib.orc_build_prp_packed.argtypes = lib.orc_build_prp.argtypes
+        lib.orc_build_prp_packed.restype = None
         lib.orc_partition.argtypes = [_u32p, u64, u32, _u32p, _u64p, _u64p]
         lib.orc_partition.restype = None
         lib.orc_emit_sqe.argtypes = [_u32p, _u64p, u32, _u8p, _u64p, _u64p, _u64p, _u64p, u64,
@@ -122,6 +124,26 @@ def build_prp(lut, off, length, list_bus_base, pool_pages, pool=None):
                          n, list_bus_base, _p(pool, _u64p), pool_pages,
                          _p(out["prp1"], _u64p), _p(out["prp2"], _u64p),
                          _p(out["status"], _u8p), _p(total, _u64p))
+    out["total"] = int(total[0])
+    out["pool"] = pool
+    return out
+
+
+def build_prp_packed(lut, off, length, list_bus_base, pool_pages, pool=None):
+    """Runs O2p (packed lists); arguments and result as build_prp."""
+    lut, off, length = _u64(lut), _u64(off), _u64(length)
+    n = off.shape[0]
+    if pool is True:
+        pool = np.zeros((pool_pages, 512), dtype=np.uint64)
+    if pool is not None:
+        assert pool.dtype == np.uint64 and pool.size >= pool_pages * 512
+    out = dict(prp1=np.empty(n, np.uint64), prp2=np.empty(n, np.uint64),
+               status=np.empty(n, np.uint8))
+    total = np.zeros(1, np.uint64)
+    _lib().orc_build_prp_packed(_p(lut, _u64p), lut.shape[0], _p(off, _u64p),
+                                _p(length, _u64p), n, list_bus_base, _p(pool, _u64p),
+                                pool_pages, _p(out["prp1"], _u64p), _p(out["prp2"], _u64p),
+                                _p(out["status"], _u8p), _p(total, _u64p))
     out["total"] = int(total[0])
     out["pool"] = pool
     return out

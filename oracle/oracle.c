@@ -193,6 +193,103 @@ void orc_build_prp(const uint64_t *lut, uint64_t lut_entries,
 }
 
 /* ------------------------------------------------------------------------
+ * O2p  The same PRP entries with packed lists.
+ *
+ * [NVMe] (not on the pages): the PRP list pointer carried in a command may
+ * name any qword of a page, not only its start; a list then runs to the end
+ * of that page, and when more than one entry is still needed there, the
+ * page's last entry points to the start of the next list page. Everything
+ * else -- which entries a request needs, PRP1, and PRP2 for one- and
+ * two-page requests -- is O2 unchanged.
+ *
+ * Readings: lists are laid back to back in request order in "data slots",
+ * 511 to a page (words 0..510), so a request's list starts where the
+ * previous one ended; word 511 of a page belongs to the request that owns the
+ * page's last data slot and holds a pointer, that request's final entry (when
+ * exactly one remains; the slot that entry would have taken, word 0 of the
+ * next page, is then 0) or 0 (its list ended in word 510). A refused request
+ * writes nothing.
+ *
+ * Pinned by: NVMe chain walks from each PRP2 (with its offset) against the
+ * byte walk of the request, disjointness of all requests' words, the dense
+ * page count, and hand-built layouts around page ends.
+ * ------------------------------------------------------------------------ */
+static uint64_t slot_word(u128 d)
+{
+    return (uint64_t)(d + d / 511);
+}
+
+void orc_build_prp_packed(const uint64_t *lut, uint64_t lut_entries,
+                          const uint64_t *off, const uint64_t *len, uint64_t n,
+                          uint64_t list_bus_base, uint64_t *pool, uint64_t pool_pages,
+                          uint64_t *prp1, uint64_t *prp2, uint8_t *status, uint64_t *total)
+{
+    const u128 heap = (u128)lut_entries << 16;
+    const u128 capacity = (u128)pool_pages * 511;   /* data slots in the pool */
+    u128 next = 0;                                  /* running data-slot counter */
+
+    for (uint64_t i = 0; i < n; ++i) {
+        const uint64_t o = off[i], size = len[i];
+        prp1[i] = 0;
+        prp2[i] = 0;
+        status[i] = ORC_OK;
+
+        /* Validation, page count, PRP1 and short PRP2: as in O2. */
+        if (size == 0 || (o % 4) != 0 || (u128)o + size > (u128)UINT64_MAX) {
+            status[i] = ORC_EINVAL;
+            continue;
+        }
+        if ((u128)o + size > heap) {
+            status[i] = ORC_ERANGE;
+            continue;
+        }
+        uint64_t npages = (uint64_t)(((u128)(o & 4095) + size + 4095) >> 12);
+        uint64_t page0 = o & ~4095ull;
+        if (npages == 1) {
+            prp1[i] = phys_of(lut, o);
+            continue;
+        }
+        if (npages == 2) {
+            prp1[i] = phys_of(lut, o);
+            prp2[i] = phys_of(lut, page0 + 4096);
+            continue;
+        }
+
+        /* Data slots of this request's entries. */
+        const uint64_t m = npages - 1;
+        const u128 first = next;
+        next += m;
+        if (first + m > capacity) {
+            status[i] = ORC_ENOSPC;
+            continue;
+        }
+        prp1[i] = phys_of(lut, o);
+        prp2[i] = list_bus_base + 8 * slot_word(first);
+        if (pool == NULL) continue;
+
+        for (uint64_t k = 0; k < m; ++k) {
+            const u128 d = first + k;
+            const uint64_t entry = phys_of(lut, page0 + 4096 * (k + 1));
+            if (k >= 1 && d % 511 == 0) {
+                /* The list enters a new page at entry k: the last word of the
+                 * page before is a pointer, or this final entry itself. */
+                const uint64_t last = slot_word(d) - 1;              /* word 511 */
+                if (k == m - 1) {
+                    pool[last] = entry;
+                    pool[slot_word(d)] = 0;
+                    continue;
+                }
+                pool[last] = list_bus_base + 4096 * (uint64_t)(d / 511);
+            }
+            pool[slot_word(d)] = entry;
+        }
+        const u128 end = first + m - 1;
+        if (end % 511 == 510) pool[slot_word(end) + 1] = 0;          /* word 511 unused */
+    }
+    *total = (uint64_t)((next + 510) / 511);
+}
+
+/* ------------------------------------------------------------------------
  * O3  Stable split of requests by destination queue.
  *
  * A plain counting split: count each bucket, take the exclusive prefix as the

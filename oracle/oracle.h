@@ -61,6 +61,23 @@ void orc_build_prp(const uint64_t *lut, uint64_t lut_entries,
                    uint64_t *prp1, uint64_t *prp2, uint8_t *status, uint64_t *total);
 
 /*
+ * O2p: the same PRP entries with the lists packed back to back. List entries
+ * are numbered by data slots: request i with m = pages - 1 >= 2 entries takes
+ * slots [D, D + m), D = running count of earlier requests' entries (refused
+ * ones included). A pool page holds data slots 511 p .. 511 p + 510 in words
+ * 0..510; slot d lies in word d + floor(d / 511). PRP2 = list_bus_base +
+ * 8 * word(D). Word 511 of a page is set by the request owning the page's
+ * last data slot: a pointer to the next page if two or more of its entries
+ * remain, its final entry if exactly one remains (the next page's word 0 is
+ * then 0), and 0 if its list ended in word 510. ENOSPC when D + m >
+ * 511 * pool_pages. *total = ceil(all entries / 511) pages.
+ */
+void orc_build_prp_packed(const uint64_t *lut, uint64_t lut_entries,
+                          const uint64_t *off, const uint64_t *len, uint64_t n,
+                          uint64_t list_bus_base, uint64_t *pool, uint64_t pool_pages,
+                          uint64_t *prp1, uint64_t *prp2, uint8_t *status, uint64_t *total);
+
+/*
  * O3: stable split of request indices by queue id. Queue ids >= nqueues go to
  * an overflow bucket nqueues. qoff has nqueues+2 entries: bucket b occupies
  * perm[qoff[b] .. qoff[b+1]). *n_invalid = size of the overflow bucket.

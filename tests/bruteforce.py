@@ -68,16 +68,19 @@ def touched_pages(lut: np.ndarray, off: int, size: int):
     return int(ph[0]), [int(p) * 4096 for p in pg[keep]]
 
 
-def chain_walk(pool: np.ndarray, bus: int, prp2: int, count: int):
+def chain_walk(pool: np.ndarray, bus: int, prp2: int, count: int, allow_offset=False):
     """Follows an NVMe PRP list from PRP2 and returns (the `count` data
     entries, the list slots visited). In a list page, the last entry is a
-    pointer to the next list page whenever more than one entry remains."""
+    pointer to the next list page whenever more than one entry remains. With
+    allow_offset, PRP2 may point to any qword of its page (the NVMe rule for
+    the list pointer in a command); chain pointers must name a page start."""
     rel = prp2 - bus
-    assert rel >= 0 and rel % 4096 == 0, "PRP2 does not name a list page"
+    assert rel >= 0 and rel % 8 == 0, "PRP2 is not a qword address in the pool"
+    assert allow_offset or rel % 4096 == 0, "PRP2 does not name a list page"
     slot = rel // 4096
     slots = [slot]
     entries = []
-    pos = 0
+    pos = (rel % 4096) // 8
     while len(entries) < count:
         if pos == 511 and count - len(entries) > 1:
             nxt = int(pool[slot, 511]) - bus
