@@ -8,6 +8,8 @@
  *                              range in a table of registered memory regions
  *   dmadesc_build_prp          64 KiB GPU-page physical-address table -> 4 KiB
  *                              NVMe PRP1/PRP2 and chained PRP lists
+ *   dmadesc_build_prp_packed   the same entries with the lists packed back to
+ *                              back (qword-offset list pointers)
  *   dmadesc_partition_by_queue stable split of the requests by destination queue
  *
  * and one stage after them:
@@ -178,6 +180,41 @@ int dmadesc_build_prp(const uint64_t *lut, uint64_t lut_entries,
                       uint64_t *prp1, uint64_t *prp2, uint8_t *status,
                       uint64_t *total_pages,
                       void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * dmadesc_build_prp_packed - dmadesc_build_prp with packed PRP lists.
+ *
+ * [NVMe] (not on the pages) lets the PRP list pointer carried in a command
+ * (PRP2) name any qword of a page; the list then runs to the end of that page
+ * and, when more than one entry is still needed there, the page's last entry
+ * points to the start of the next list page. Lists are therefore laid back to
+ * back: the pool is a run of list pages of 511 data slots each (words
+ * 0..510); request i with m = pages - 1 >= 2 list entries takes data slots
+ * [D, D + m), where D is the sum of m over all earlier list requests
+ * (refused ones included), and slot d lies in pool word d + floor(d / 511).
+ * Everything else is as in dmadesc_build_prp (same arguments, statuses,
+ * PRP1, and PRP2 of one- and two-page requests), except:
+ *   PRP2 (lists)   list_bus_base + 8 * word(D)
+ *   word 511 of a list page: written by the request that owns the page's
+ *                  last data slot -- the bus address of the next page when
+ *                  two or more of its entries remain; its final entry when
+ *                  exactly one remains (word 0 of the next page is then 0);
+ *                  0 when its list ended in word 510
+ *   ENOSPC         D + m > 511 * pool_pages (refused requests are a suffix)
+ *   *total_pages   ceil(sum of m over all list requests / 511)
+ *   padding        none: the library writes exactly the words of non-refused
+ *                  lists and the zero words above, every other pool word stays
+ *   extra check    (16 * lut_entries + 2) * n >= 2^62 -> -EINVAL
+ * A batch's lists fill about (entries / 511) pages instead of one page or
+ * more per list, and are written as one dense stream.
+ * Workspace: dmadesc_workspace_bytes(DMADESC_OP_BUILD_PRP, n, 0).
+ */
+int dmadesc_build_prp_packed(const uint64_t *lut, uint64_t lut_entries,
+                             const uint64_t *off, const uint64_t *len, uint64_t n,
+                             uint64_t list_bus_base, uint64_t *list_pool, uint64_t pool_pages,
+                             uint64_t *prp1, uint64_t *prp2, uint8_t *status,
+                             uint64_t *total_pages,
+                             void *ws, size_t ws_bytes, void *stream);
 
 /*
  * dmadesc_partition_by_queue - stable split of request indices by queue id.

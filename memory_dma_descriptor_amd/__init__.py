@@ -14,7 +14,8 @@ import torch
 
 from . import _build
 
-__all__ = ["mr_lookup", "build_prp", "partition_by_queue", "emit_sqe", "ring_addresses",
+__all__ = ["mr_lookup", "build_prp", "build_prp_packed", "partition_by_queue", "emit_sqe",
+           "ring_addresses",
            "workspace_bytes", "DmadescError", "lib", "LIB_PATH", "MAX_QUEUES",
            "SQ_MAX_DEPTH",
            "MISS", "EXACT", "CONTAINED", "INVALID",
@@ -37,6 +38,8 @@ _EXPORTS = {
                            _P, _P, _P, _P, _P, _P, _SIZE, _P], ctypes.c_int),
     "dmadesc_build_prp": ([_P, _U64, _P, _P, _U64, _U64, _P, _U64,
                            _P, _P, _P, _P, _P, _SIZE, _P], ctypes.c_int),
+    "dmadesc_build_prp_packed": ([_P, _U64, _P, _P, _U64, _U64, _P, _U64,
+                                  _P, _P, _P, _P, _P, _SIZE, _P], ctypes.c_int),
     "dmadesc_partition_by_queue": ([_P, _U64, _U32, _P, _P, _P, _P, _SIZE, _P],
                                    ctypes.c_int),
     "dmadesc_emit_sqe": ([_P, _P, _U32, _P, _P, _P, _P, _P, _U64, _U32, _U32, _U32,
@@ -133,9 +136,10 @@ def mr_lookup(reg_start: torch.Tensor, reg_end: torch.Tensor, reg_lkey: torch.Te
 
 def build_prp(lut: torch.Tensor, off: torch.Tensor, length: torch.Tensor,
               list_bus_base: int, pool: torch.Tensor, out: dict | None = None,
-              ws: torch.Tensor | None = None, stream=None) -> dict:
+              ws: torch.Tensor | None = None, stream=None, packed: bool = False) -> dict:
     """GPU-page table -> PRP1/PRP2/status and chained lists in `pool`
-    (u64[pool_pages, 512]); returns dict(prp1, prp2, status, total_pages)."""
+    (u64[pool_pages, 512]); returns dict(prp1, prp2, status, total_pages).
+    packed=True calls dmadesc_build_prp_packed (lists back to back)."""
     n = off.numel()
     dev = off.device
     if pool.dim() != 2 or pool.shape[1] != 512:
@@ -146,7 +150,8 @@ def build_prp(lut: torch.Tensor, off: torch.Tensor, length: torch.Tensor,
                    status=torch.empty(n, dtype=torch.uint8, device=dev),
                    total_pages=torch.empty(1, dtype=torch.uint64, device=dev))
     ws = _workspace(OP_BUILD_PRP, n, 0, dev, ws)
-    rc = lib().dmadesc_build_prp(
+    fn = lib().dmadesc_build_prp_packed if packed else lib().dmadesc_build_prp
+    rc = fn(
         _dev(lut, torch.uint64, "lut"), lut.numel(),
         _dev(off, torch.uint64, "off", n), _dev(length, torch.uint64, "len", n), n,
         list_bus_base, _dev(pool, torch.uint64, "pool"), pool.shape[0],
@@ -154,8 +159,16 @@ def build_prp(lut: torch.Tensor, off: torch.Tensor, length: torch.Tensor,
         _dev(out["status"], torch.uint8, "status", n),
         _dev(out["total_pages"], torch.uint64, "total_pages", 1),
         ws.data_ptr(), ws.numel(), _stream(dev, stream))
-    _check("dmadesc_build_prp", rc)
+    _check("dmadesc_build_prp_packed" if packed else "dmadesc_build_prp", rc)
     return out
+
+
+def build_prp_packed(lut: torch.Tensor, off: torch.Tensor, length: torch.Tensor,
+                     list_bus_base: int, pool: torch.Tensor, out: dict | None = None,
+                     ws: torch.Tensor | None = None, stream=None) -> dict:
+    """dmadesc_build_prp_packed: the same PRP entries, lists back to back."""
+    return build_prp(lut, off, length, list_bus_base, pool, out=out, ws=ws, stream=stream,
+                     packed=True)
 
 
 def partition_by_queue(qid: torch.Tensor, nqueues: int, out: dict | None = None,

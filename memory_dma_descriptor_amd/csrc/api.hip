@@ -13,6 +13,31 @@ constexpr uint64_t kMaxLutEntries = 1ull << 48;  // heap < 2^64 bytes
 
 int launched(hipError_t e) { return e == hipSuccess ? 0 : -EIO; }
 
+int build_prp_common(const uint64_t *lut, uint64_t lut_entries, const uint64_t *off,
+                     const uint64_t *len, uint64_t n, uint64_t list_bus_base,
+                     uint64_t *list_pool, uint64_t pool_pages, uint64_t *prp1, uint64_t *prp2,
+                     uint8_t *status, uint64_t *total_pages, void *ws, size_t ws_bytes,
+                     void *stream, bool packed)
+{
+    if (n >= kMaxN || lut_entries >= kMaxLutEntries) return -EINVAL;
+    if (list_bus_base & 4095u) return -EINVAL;
+    if (!total_pages) return -EINVAL;
+    if (lut_entries > 0 && !lut) return -EINVAL;
+    if (pool_pages > 0 && !list_pool) return -EINVAL;
+    if (reinterpret_cast<uintptr_t>(list_pool) & 15u) return -EINVAL;    // 16-byte stores
+    if (pool_pages > (~0ull >> 12)) return -EINVAL;          // pool byte size fits 64 bits
+    // The scan carries 62-bit counts: every request has at most 16 lut_entries
+    // + 1 list entries, so n of them must stay below 2^62.
+    if (packed && (unsigned __int128)(lut_entries * 16 + 2) * n >= ((unsigned __int128)1 << 62))
+        return -EINVAL;
+    if (n > 0 && (!off || !len || !prp1 || !prp2 || !status)) return -EINVAL;
+    const size_t need = dd::ws_build_prp(n);
+    if (need > 0 && (!ws || ws_bytes < need)) return -EINVAL;
+    dd::PrpArgs a{lut, lut_entries, off, len, n, list_bus_base, list_pool, pool_pages,
+                  prp1, prp2, status, total_pages, ws, packed};
+    return launched(dd::launch_build_prp(a, static_cast<hipStream_t>(stream)));
+}
+
 }  // namespace
 
 extern "C" {
@@ -70,19 +95,19 @@ int dmadesc_build_prp(const uint64_t *lut, uint64_t lut_entries,
                       uint64_t *total_pages,
                       void *ws, size_t ws_bytes, void *stream)
 {
-    if (n >= kMaxN || lut_entries >= kMaxLutEntries) return -EINVAL;
-    if (list_bus_base & 4095u) return -EINVAL;
-    if (!total_pages) return -EINVAL;
-    if (lut_entries > 0 && !lut) return -EINVAL;
-    if (pool_pages > 0 && !list_pool) return -EINVAL;
-    if (reinterpret_cast<uintptr_t>(list_pool) & 15u) return -EINVAL;    // 16-byte stores
-    if (pool_pages > (~0ull >> 12)) return -EINVAL;          // pool byte size fits 64 bits
-    if (n > 0 && (!off || !len || !prp1 || !prp2 || !status)) return -EINVAL;
-    const size_t need = dd::ws_build_prp(n);
-    if (need > 0 && (!ws || ws_bytes < need)) return -EINVAL;
-    dd::PrpArgs a{lut, lut_entries, off, len, n, list_bus_base, list_pool, pool_pages,
-                  prp1, prp2, status, total_pages, ws};
-    return launched(dd::launch_build_prp(a, static_cast<hipStream_t>(stream)));
+    return build_prp_common(lut, lut_entries, off, len, n, list_bus_base, list_pool, pool_pages,
+                            prp1, prp2, status, total_pages, ws, ws_bytes, stream, false);
+}
+
+int dmadesc_build_prp_packed(const uint64_t *lut, uint64_t lut_entries,
+                             const uint64_t *off, const uint64_t *len, uint64_t n,
+                             uint64_t list_bus_base, uint64_t *list_pool, uint64_t pool_pages,
+                             uint64_t *prp1, uint64_t *prp2, uint8_t *status,
+                             uint64_t *total_pages,
+                             void *ws, size_t ws_bytes, void *stream)
+{
+    return build_prp_common(lut, lut_entries, off, len, n, list_bus_base, list_pool, pool_pages,
+                            prp1, prp2, status, total_pages, ws, ws_bytes, stream, true);
 }
 
 int dmadesc_partition_by_queue(const uint32_t *qid, uint64_t n, uint32_t nqueues,

@@ -32,6 +32,20 @@
 //    most two 64 KiB GPU pages, so each group reads at most two table
 //    entries; a wave's 64 groups read one short run of the table per
 //    request, which the L1/L2 serve.
+//
+// Packed layout (the same kernel, kPacked = true): lists lie back to back in
+// data slots, 511 to a page (words 0..510); a request's list starts where the
+// previous one ended, and PRP2 may carry that qword offset, as NVMe allows for
+// the list pointer in a command. The scan hands out data slots (entries)
+// instead of pages, and a wave writes the words of its 64 consecutive
+// requests as one range [word(S), word(E)) of the pool: aligned 4-word groups,
+// each word's owner found by a search over the requests' first slots. Word
+// 511 of a page is written by the owner of the page's last slot: a chain
+// pointer when two or more of its entries remain, its final entry when one
+// remains (the next page's word 0 is then 0), else 0. The list writes become
+// one dense stream instead of one short run per 4 KiB list page.
+#include <type_traits>
+
 #include "dd_device.hpp"
 #include "dd_internal.h"
 
@@ -362,6 +376,165 @@ __device__ __forceinline__ void emit_round(RoundLds &T, uint64_t xb, uint64_t wo
         emit_round_wide(T.wide, xb, word, ent, lp, last_frame, lut, pool, bus);
 }
 
+// Per-wave table of one round of 64 requests for the packed layout. T holds
+// slot offsets relative to the round's first slot S: 32-bit when the round
+// spans fewer than 2^31 slots, else 64-bit.
+template <typename T>
+struct PackTab {
+    T start[kWave + 1];         // first data slot of each request, - S (clamped to E - S)
+    T foff[kWave + 1];          // exclusive prefix of staged GPU pages
+    T m[kWave];                 // list entries (0: none)
+    uint64_t f0[kWave];         // GPU page holding data entry 0
+    uint32_t ph[kWave];         // 4 KiB page of data entry 0 within GPU page f0
+    uint64_t lut[kTileFrames];
+};
+union PackLds {
+    PackTab<uint32_t> fast;
+    PackTab<uint64_t> wide;
+};
+
+// Writes the aligned 4-word groups covering pool words [wlo, whi) of one
+// packed round; words outside the range belong to other rounds.
+template <typename T, bool kStaged>
+__device__ __forceinline__ void pack_groups(const PackTab<T> &P, uint64_t S, uint64_t wlo,
+                                            uint64_t whi, const uint64_t *__restrict__ lut,
+                                            uint64_t *__restrict__ pool, uint64_t bus)
+{
+    const uint64_t ghi = (whi + 3) >> 2;
+    for (uint64_t G = (wlo >> 2) + lane(); G < ghi; G += kWave) {
+        const uint64_t w0 = G << 2;
+        uint64_t v[4];
+        bool all = true;
+        int r = -1;
+        T st = 0, mm = 0;
+        uint64_t f0 = 0;
+        uint32_t ph = 0;
+        T fb = 0;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const uint64_t w = w0 + k;
+            v[k] = 0;
+            if (w < wlo || w >= whi) {
+                all = false;
+                continue;
+            }
+            const uint64_t pg = w >> 9;
+            const uint32_t o = (uint32_t)(w & 511u);
+            // Word 511 is decided by the owner of the page's last slot.
+            const T rel = (T)(pg * 511 + (o == 511u ? 510u : o) - S);
+            const int r0 = r;
+            if (r < 0) r = owner_of<kWave>(P.start, rel);
+            else
+                while (P.start[r + 1] <= rel) ++r;
+            if (r != r0) {
+                st = P.start[r];
+                mm = P.m[r];
+                f0 = P.f0[r];
+                ph = P.ph[r];
+                fb = P.foff[r];
+            }
+            const T j = rel - st;                            // entry at this slot
+            T e = j;                                         // entry to write, if any
+            bool data = true;
+            if (o == 511u) {
+                const T rem = mm - j - 1;                    // entries after the slot
+                if (rem >= 2) {
+                    v[k] = bus + ((pg + 1) << 12);           // chain pointer
+                    data = false;
+                } else if (rem == 1) {
+                    e = mm - 1;                              // the final entry moves up
+                } else {
+                    data = false;                            // list ended in word 510
+                }
+            } else if (o == 0u && j > 0 && j == mm - 1) {
+                data = false;                                // vacated by the final entry
+            }
+            if (data) {
+                const T t0 = (T)ph + e;
+                const T fi = t0 >> 4;
+                const uint64_t l = kStaged ? P.lut[fb + fi] : lut[f0 + fi];
+                v[k] = l + ((uint64_t)(t0 & 15u) << 12);
+            }
+        }
+        uint64_t *dst = pool + w0;
+        if (all) {
+            *reinterpret_cast<u64x2 *>(dst) = u64x2{v[0], v[1]};
+            *reinterpret_cast<u64x2 *>(dst + 2) = u64x2{v[2], v[3]};
+        } else {
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                if (w0 + k >= wlo && w0 + k < whi) dst[k] = v[k];
+        }
+    }
+}
+
+template <typename T>
+__device__ __forceinline__ void emit_packed_t(PackTab<T> &P, uint64_t d, uint64_t m,
+                                              uint64_t S, uint64_t E, uint64_t xb,
+                                              uint64_t last_frame,
+                                              const uint64_t *__restrict__ lut,
+                                              uint64_t *__restrict__ pool, uint64_t bus)
+{
+    const int ln = lane();
+    const uint64_t frames = m ? last_frame - (xb >> 16) + 1 : 0;
+    const uint64_t finc = wave_incl_scan(frames);
+    const uint64_t ftot = __shfl(finc, kWave - 1, kWave);
+    const uint64_t rs = d - S < E - S ? d - S : E - S;       // d >= S for every lane
+    P.start[ln] = (T)rs;
+    P.foff[ln] = (T)(finc - frames);
+    P.m[ln] = (T)m;
+    P.f0[ln] = xb >> 16;
+    P.ph[ln] = (uint32_t)((xb >> 12) & 15u);
+    if (ln == kWave - 1) {
+        P.start[kWave] = (T)(E - S);
+        P.foff[kWave] = (T)finc;
+    }
+    wave_sync_lds();
+    const uint64_t wlo = S + S / 511, whi = E + E / 511;
+    if (ftot <= (uint64_t)kTileFrames) {
+        for (uint32_t j0 = 0; j0 < (uint32_t)ftot; j0 += 4 * kWave) {
+            uint64_t v[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const uint32_t j = j0 + u * kWave + ln;
+                const T jj = j < ftot ? (T)j : (T)0;
+                const int r = owner_of<kWave>(P.foff, jj);
+                v[u] = lut[P.f0[r] + (jj - P.foff[r])];
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const uint32_t j = j0 + u * kWave + ln;
+                if (j < ftot) P.lut[j] = v[u];
+            }
+        }
+        wave_sync_lds();
+        pack_groups<T, true>(P, S, wlo, whi, lut, pool, bus);
+    } else {
+        pack_groups<T, false>(P, S, wlo, whi, lut, pool, bus);
+    }
+    wave_sync_lds();                                         // the next round rewrites P
+}
+
+// Writes the packed words of the wave's 64 requests of one round (lane k: one
+// request with list entries m from data slot d; m == 0 for no list).
+__device__ __forceinline__ void emit_round_packed(PackLds &L, uint64_t d, uint64_t m,
+                                                  uint64_t xb, uint64_t last_frame,
+                                                  const uint64_t *__restrict__ lut,
+                                                  uint64_t *__restrict__ pool, uint64_t bus)
+{
+    const uint64_t has = __ballot(m != 0);
+    if (has == 0) return;                                    // uniform per wave
+    const int first = __ffsll((unsigned long long)has) - 1;
+    const int last = 63 - __clzll((unsigned long long)has);
+    const uint64_t S = __shfl(d, first, kWave);
+    const uint64_t E = __shfl(d + m, last, kWave);
+    if (E - S < (1ull << 31))
+        emit_packed_t<uint32_t>(L.fast, d, m, S, E, xb, last_frame, lut, pool, bus);
+    else
+        emit_packed_t<uint64_t>(L.wide, d, m, S, E, xb, last_frame, lut, pool, bus);
+}
+
+template <bool kPacked>
 __global__ __launch_bounds__(kThreads, 4) void k_prp_build(
     const uint64_t *__restrict__ lut, uint64_t heap,
     const uint64_t *__restrict__ off, const uint64_t *__restrict__ len, uint64_t n,
@@ -372,7 +545,7 @@ __global__ __launch_bounds__(kThreads, 4) void k_prp_build(
 {
     __shared__ uint64_t s_red[kWaves];
     __shared__ uint64_t s_bid, s_excl;
-    __shared__ RoundLds s_round[kWaves];
+    __shared__ typename std::conditional<kPacked, PackLds, RoundLds>::type s_round[kWaves];
 
     const int t = threadIdx.x, w = wave(), ln = lane();
     if (t == 0) s_bid = atomicAdd(&hdr->ticket, 1u);
@@ -433,14 +606,16 @@ __global__ __launch_bounds__(kThreads, 4) void k_prp_build(
             }
         }
     }
+    // Scanned per request: list pages (page layout) or list entries (packed).
     uint64_t agg = 0;
 #pragma unroll
     for (int k = 0; k < kItems; ++k) {
         uint64_t pages;
         const uint8_t st = decode(o[k], l[k], heap, pages);
-        const uint64_t lp = (st == kOk && pages >= 3) ? (pages - 2 + 510) / 511 : 0;
+        const uint64_t cnt = (st == kOk && pages >= 3)
+                                 ? (kPacked ? pages - 1 : (pages - 2 + 510) / 511) : 0;
         uint64_t tot;
-        pre[k] = agg + block_excl_scan<kThreads>(lp, s_red, &tot);
+        pre[k] = agg + block_excl_scan<kThreads>(cnt, s_red, &tot);
         agg += tot;
     }
     if (w == 0) {
@@ -454,31 +629,38 @@ __global__ __launch_bounds__(kThreads, 4) void k_prp_build(
         }
         if (ln == 0) {
             s_excl = excl;
-            if (b == nblocks - 1) *total = excl + agg;
+            if (b == nblocks - 1) *total = kPacked ? (excl + agg + 510) / 511 : excl + agg;
         }
     }
     __syncthreads();
     const uint64_t excl = s_excl;
 
+    const uint64_t cap = kPacked ? pool_pages * 511 : pool_pages;   // slots of the pool
 #pragma unroll 1
     for (int k = 0; k < kItems; ++k) {
         const uint64_t i = base + (uint64_t)k * kThreads + t;
         uint64_t pages;
         uint8_t st = decode(o[k], l[k], heap, pages);
-        const uint64_t lp = (st == kOk && pages >= 3) ? (pages - 2 + 510) / 511 : 0;
+        const uint64_t cnt = (st == kOk && pages >= 3)
+                                 ? (kPacked ? pages - 1 : (pages - 2 + 510) / 511) : 0;
         const uint64_t slot = excl + pre[k];
-        if (lp != 0 && slot + lp > pool_pages) st = kEnospc;   // refused; its slots stay taken
-        if (i < n && lp != 0) {
-            prp2[i] = st == kOk ? bus + (slot << 12) : 0;
+        if (cnt != 0 && slot + cnt > cap) st = kEnospc;      // refused; its slots stay taken
+        if (i < n && cnt != 0) {
+            const uint64_t list = kPacked ? bus + 8 * (slot + slot / 511) : bus + (slot << 12);
+            prp2[i] = st == kOk ? list : 0;
             if (st == kEnospc) {
                 prp1[i] = 0;
                 status[i] = kEnospc;
             }
         }
-        const bool lists = (st == kOk) && lp != 0;
-        emit_round(s_round[w], (o[k] & ~4095ull) + 4096, slot << 9,
-                   lists ? (pages - 1) + (lp - 1) : 0, lists ? lp : 0,
-                   (o[k] + l[k] - 1) >> 16, lut, pool, bus);
+        const bool lists = (st == kOk) && cnt != 0;
+        const uint64_t xb = (o[k] & ~4095ull) + 4096;
+        const uint64_t last_frame = (o[k] + l[k] - 1) >> 16;
+        if constexpr (kPacked)
+            emit_round_packed(s_round[w], slot, lists ? cnt : 0, xb, last_frame, lut, pool, bus);
+        else
+            emit_round(s_round[w], xb, slot << 9, lists ? (pages - 1) + (cnt - 1) : 0,
+                       lists ? cnt : 0, last_frame, lut, pool, bus);
     }
 }
 
@@ -507,9 +689,14 @@ hipError_t launch_build_prp(const PrpArgs &a, hipStream_t s)
     if (cblocks > 1024) cblocks = 1024;
     hipLaunchKernelGGL(k_prp_clear, dim3((unsigned)cblocks), dim3(256), 0, s,
                        static_cast<uint64_t *>(a.ws), words);
-    hipLaunchKernelGGL(k_prp_build, dim3((unsigned)nb), dim3(kThreads), 0, s,
-                       a.lut, heap, a.off, a.len, a.n, nb, a.list_bus_base, a.pool,
-                       a.pool_pages, a.prp1, a.prp2, a.status, a.total_pages, hdr, bstat);
+    if (a.packed)
+        hipLaunchKernelGGL(k_prp_build<true>, dim3((unsigned)nb), dim3(kThreads), 0, s,
+                           a.lut, heap, a.off, a.len, a.n, nb, a.list_bus_base, a.pool,
+                           a.pool_pages, a.prp1, a.prp2, a.status, a.total_pages, hdr, bstat);
+    else
+        hipLaunchKernelGGL(k_prp_build<false>, dim3((unsigned)nb), dim3(kThreads), 0, s,
+                           a.lut, heap, a.off, a.len, a.n, nb, a.list_bus_base, a.pool,
+                           a.pool_pages, a.prp1, a.prp2, a.status, a.total_pages, hdr, bstat);
     return hipGetLastError();
 }
 

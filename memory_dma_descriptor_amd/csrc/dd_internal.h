@@ -31,6 +31,7 @@ struct PrpArgs {
     uint8_t *status;
     uint64_t *total_pages;
     void *ws;
+    bool packed;          // lists back to back (dmadesc_build_prp_packed)
 };
 
 struct SplitArgs {

@@ -13,15 +13,25 @@
 // before, and ballots inside the tile. No atomic decides a slot, so the rings
 // are deterministic.
 //
-// Layout: block (t, q) owns positions [t * kTile, (t + 1) * kTile) of queue
-// q's window. A window is shorter than the deepest ring (65536 entries), so
-// kTilesPerQueue blocks cover any window; blocks past the window's end return
-// at once. Round k of a block covers kThreads consecutive positions, wave w
-// the 64 positions [k * kThreads + 64 w, ...), so lanes meet positions in
-// (round, wave, lane) order -- the window's order.
+// Layout: tile g = 64 q + t owns positions [t * kTile, (t + 1) * kTile) of
+// queue q's window. A window is shorter than the deepest ring (65536 entries),
+// so kTilesPerQueue tiles cover any window. Round k of a tile covers kThreads
+// consecutive positions, wave w the 64 positions [k * kThreads + 64 w, ...),
+// so lanes meet positions in (round, wave, lane) order -- the window's order.
 //
-// Kernels: k_sqe_count (placeable requests per tile), k_sqe_emit (slots,
-// entries, request map), k_sqe_finish (placed counts, tails and cursors).
+// Schedule: a queue's window is a sparse, increasing run of request indices,
+// so the gathers of one tile touch many cache lines that tiles of other
+// queues touch as well. Launched queue by queue, the resident tiles would
+// span the whole batch and re-read each line from HBM once per queue; instead
+// the non-empty tiles are ordered by their first request index, and block b of
+// the two passes takes the b-th tile of that order, so the resident tiles
+// sweep the batch together and share its lines in the caches. The order only
+// affects speed: a slot depends on the per-tile counts, never on which block
+// ran first.
+//
+// Kernels: k_sqe_order (tile order), k_sqe_count (placeable requests per
+// tile), k_sqe_emit (slots, entries, request map), k_sqe_finish (placed
+// counts, tails and cursors).
 #include "dd_device.hpp"
 #include "dd_internal.h"
 #include "dmadesc.h"
@@ -34,7 +44,18 @@ constexpr int kWaves = kThreads / kWave;
 constexpr int kRounds = 4;
 constexpr uint32_t kTile = kThreads * kRounds;                  // window positions per block
 constexpr uint32_t kTilesPerQueue = DMADESC_SQ_MAX_DEPTH / kTile;
-static_assert(kTilesPerQueue <= kWave, "a wave sums the tile counts of one queue");
+static_assert(kTilesPerQueue == 64, "tile ids are 64 q + t");
+constexpr int kOrderThreads = 1024;
+constexpr uint32_t kBins = 4096;                 // tile-order buckets over the batch
+constexpr int kBinsPerThread = kBins / kOrderThreads;
+constexpr int kMaxTiles = DMADESC_MAX_QUEUES * kTilesPerQueue;
+
+// Workspace: per-tile counts, the tile order, and the number of non-empty tiles.
+struct SqeWs {
+    uint32_t *counts;     // [nq * 64]
+    uint32_t *order;      // [nq * 64]
+    uint32_t *ntiles;     // scalar
+};
 
 struct Window {
     uint64_t start;     // position in perm of the window's first entry
@@ -70,13 +91,78 @@ __device__ __forceinline__ bool placeable(uint8_t st, uint64_t len, uint32_t shi
            (len >> shift) <= 65536u;
 }
 
-__global__ __launch_bounds__(kThreads) void k_sqe_count(SqeArgs a, uint32_t *__restrict__ counts)
+// One block: counting sort of the non-empty tiles by the bucket of their first
+// request index (bucket = index * kBins / n). Ties in a bucket take the order
+// of the LDS atomics; only the schedule depends on it.
+__global__ __launch_bounds__(kOrderThreads) void k_sqe_order(SqeArgs a, SqeWs ws)
+{
+    __shared__ uint64_t s_start[DMADESC_MAX_QUEUES];
+    __shared__ uint32_t s_w[DMADESC_MAX_QUEUES];
+    __shared__ uint32_t s_bin[kBins];
+    __shared__ uint32_t s_scr[kOrderThreads / kWave];
+    const uint32_t nq = a.nqueues, ntile = nq * kTilesPerQueue;
+    for (uint32_t q = threadIdx.x; q < nq; q += kOrderThreads) {
+        const Window win = window_of(a, q);
+        s_start[q] = win.start;
+        s_w[q] = win.w;
+    }
+    for (uint32_t b = threadIdx.x; b < kBins; b += kOrderThreads) s_bin[b] = 0;
+    __syncthreads();
+    // Each thread owns tiles threadIdx.x + k * kOrderThreads.
+    constexpr int kPer = kMaxTiles / kOrderThreads;
+    uint32_t bin[kPer];
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+        const uint32_t g = threadIdx.x + k * kOrderThreads;
+        bin[k] = UINT32_MAX;
+        if (g < ntile) {
+            const uint32_t q = g / kTilesPerQueue, lo = (g % kTilesPerQueue) * kTile;
+            if (lo < s_w[q]) {
+                const uint64_t first = a.perm[s_start[q] + lo];
+                bin[k] = (uint32_t)(first * kBins / a.n);   // first < n, so bin < kBins
+                atomicAdd(&s_bin[bin[k]], 1u);
+            }
+        }
+    }
+    __syncthreads();
+    uint32_t v[kBinsPerThread], sum = 0;
+#pragma unroll
+    for (int k = 0; k < kBinsPerThread; ++k) {
+        v[k] = s_bin[threadIdx.x * kBinsPerThread + k];
+        sum += v[k];
+    }
+    uint32_t total;
+    uint32_t run = block_excl_scan<kOrderThreads>(sum, s_scr, &total);
+#pragma unroll
+    for (int k = 0; k < kBinsPerThread; ++k) {
+        s_bin[threadIdx.x * kBinsPerThread + k] = run;
+        run += v[k];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < kPer; ++k)
+        if (bin[k] != UINT32_MAX)
+            ws.order[atomicAdd(&s_bin[bin[k]], 1u)] = threadIdx.x + k * kOrderThreads;
+    if (threadIdx.x == 0) *ws.ntiles = total;
+}
+
+// The tile block b works on, or false when b is past the non-empty tiles.
+__device__ __forceinline__ bool tile_of(const SqeWs &ws, uint32_t &q, uint32_t &t)
+{
+    if (blockIdx.x >= *ws.ntiles) return false;
+    const uint32_t g = ws.order[blockIdx.x];
+    q = g / kTilesPerQueue;
+    t = g % kTilesPerQueue;
+    return true;
+}
+
+__global__ __launch_bounds__(kThreads) void k_sqe_count(SqeArgs a, SqeWs ws)
 {
     __shared__ uint32_t s_sum[kWaves];
-    const uint32_t t = blockIdx.x, q = blockIdx.y;
+    uint32_t q, t;
+    if (!tile_of(ws, q, t)) return;                    // uniform over the block
     const Window win = window_of(a, q);
     const uint32_t lo = t * kTile;
-    if (lo >= win.w) return;                           // uniform over the block
     const uint32_t cnt = win.w - lo < kTile ? win.w - lo : kTile;
     const uint32_t *__restrict__ pos = a.perm + win.start + lo;
 
@@ -99,28 +185,31 @@ __global__ __launch_bounds__(kThreads) void k_sqe_count(SqeArgs a, uint32_t *__r
         uint32_t s = 0;
 #pragma unroll
         for (int w = 0; w < kWaves; ++w) s += s_sum[w];
-        counts[(uint64_t)q * kTilesPerQueue + t] = s;
+        ws.counts[(uint64_t)q * kTilesPerQueue + t] = s;
     }
 }
 
-__global__ __launch_bounds__(kThreads) void k_sqe_emit(SqeArgs a, const uint32_t *__restrict__ counts)
+__global__ __launch_bounds__(kThreads) void k_sqe_emit(SqeArgs a, SqeWs ws)
 {
     __shared__ uint32_t s_cnt[kRounds][kWaves];
-    const uint32_t t = blockIdx.x, q = blockIdx.y;
+    uint32_t q, t;
+    if (!tile_of(ws, q, t)) return;                    // uniform over the block
     const Window win = window_of(a, q);
     const uint32_t lo = t * kTile;
-    if (lo >= win.w) return;                           // uniform over the block
     const uint32_t cnt = win.w - lo < kTile ? win.w - lo : kTile;
     const uint32_t *__restrict__ pos = a.perm + win.start + lo;
     const int w = wave(), ln = lane();
 
     // Placeable requests of the window before this tile (t < 64 tiles).
-    uint32_t before = (uint32_t)ln < t ? counts[(uint64_t)q * kTilesPerQueue + ln] : 0u;
+    uint32_t before = (uint32_t)ln < t ? ws.counts[(uint64_t)q * kTilesPerQueue + ln] : 0u;
     before = wave_sum(before);
 
+    // Every gather of the tile is issued before the first ring store: the
+    // compiler cannot prove that a ring aliases no input column, so a load
+    // placed after a store would wait for it.
     uint32_t idx[kRounds];
-    uint64_t len[kRounds];
-    bool ok[kRounds];
+    uint64_t len[kRounds], p1[kRounds], p2[kRounds], lba[kRounds];
+    uint8_t st[kRounds];
 #pragma unroll
     for (int k = 0; k < kRounds; ++k) {
         const uint32_t j = k * kThreads + threadIdx.x;
@@ -128,15 +217,18 @@ __global__ __launch_bounds__(kThreads) void k_sqe_emit(SqeArgs a, const uint32_t
     }
 #pragma unroll
     for (int k = 0; k < kRounds; ++k) {
-        const uint32_t i = idx[k];
-        const bool in = i < a.n;
+        const uint32_t i = idx[k] < a.n ? idx[k] : 0u;
+        const bool in = idx[k] < a.n;
+        st[k] = in ? a.status[i] : (uint8_t)0xFF;
         len[k] = in ? a.len[i] : 0;
-        ok[k] = in && placeable(a.status[i], len[k], a.lba_shift);
+        p1[k] = in ? a.prp1[i] : 0;
+        p2[k] = in ? a.prp2[i] : 0;
+        lba[k] = in ? a.slba[i] : 0;
     }
     uint64_t m[kRounds];
 #pragma unroll
     for (int k = 0; k < kRounds; ++k) {
-        m[k] = __ballot(ok[k]);
+        m[k] = __ballot(placeable(st[k], len[k], a.lba_shift));
         if (ln == 0) s_cnt[k][w] = (uint32_t)__popcll(m[k]);
     }
     __syncthreads();
@@ -153,31 +245,29 @@ __global__ __launch_bounds__(kThreads) void k_sqe_emit(SqeArgs a, const uint32_t
             wpre += v < w ? c : 0u;
             rtot += c;
         }
-        if (ok[k]) {
-            const uint32_t i = idx[k];
+        if ((m[k] >> ln) & 1u) {
             uint32_t s = win.tail + run + wpre + (uint32_t)__popcll(m[k] & below);
             if (s >= win.depth) s -= win.depth;        // tail < depth, rank < depth - 1
-            const uint64_t p1 = a.prp1[i], p2 = a.prp2[i], lba = a.slba[i];
             const uint32_t nlb0 = (uint32_t)(len[k] >> a.lba_shift) - 1u;
             uint4 *e = ring + (uint64_t)s * 4;
             e[0] = make_uint4(a.opcode | (s << 16), a.nsid, 0u, 0u);
-            e[1] = make_uint4(0u, 0u, (uint32_t)p1, (uint32_t)(p1 >> 32));
-            e[2] = make_uint4((uint32_t)p2, (uint32_t)(p2 >> 32), (uint32_t)lba,
-                              (uint32_t)(lba >> 32));
+            e[1] = make_uint4(0u, 0u, (uint32_t)p1[k], (uint32_t)(p1[k] >> 32));
+            e[2] = make_uint4((uint32_t)p2[k], (uint32_t)(p2[k] >> 32), (uint32_t)lba[k],
+                              (uint32_t)(lba[k] >> 32));
             e[3] = make_uint4(nlb0, 0u, 0u, 0u);
-            if (a.req_of_slot) a.req_of_slot[(uint64_t)q * DMADESC_SQ_MAX_DEPTH + s] = i;
+            if (a.req_of_slot) a.req_of_slot[(uint64_t)q * DMADESC_SQ_MAX_DEPTH + s] = idx[k];
         }
         run += rtot;
     }
 }
 
-__global__ __launch_bounds__(kThreads) void k_sqe_finish(SqeArgs a, const uint32_t *__restrict__ counts)
+__global__ __launch_bounds__(kThreads) void k_sqe_finish(SqeArgs a, SqeWs ws)
 {
     for (uint32_t q = threadIdx.x; q < a.nqueues; q += kThreads) {
         const Window win = window_of(a, q);
         const uint32_t tiles = (win.w + kTile - 1) / kTile;
         uint32_t placed = 0;
-        for (uint32_t t = 0; t < tiles; ++t) placed += counts[(uint64_t)q * kTilesPerQueue + t];
+        for (uint32_t t = 0; t < tiles; ++t) placed += ws.counts[(uint64_t)q * kTilesPerQueue + t];
         a.placed[q] = placed;
         if (win.w > 0) {
             uint32_t nt = win.tail + placed;
@@ -192,16 +282,21 @@ __global__ __launch_bounds__(kThreads) void k_sqe_finish(SqeArgs a, const uint32
 
 size_t ws_emit_sqe(uint32_t nq)
 {
-    return align256((uint64_t)nq * kTilesPerQueue * sizeof(uint32_t));
+    const uint64_t tiles = (uint64_t)nq * kTilesPerQueue * sizeof(uint32_t);
+    return 2 * align256(tiles) + 256;
 }
 
 hipError_t launch_emit_sqe(const SqeArgs &a, hipStream_t s)
 {
-    uint32_t *counts = static_cast<uint32_t *>(a.ws);
-    const dim3 grid(kTilesPerQueue, a.nqueues);
-    hipLaunchKernelGGL(k_sqe_count, grid, dim3(kThreads), 0, s, a, counts);
-    hipLaunchKernelGGL(k_sqe_emit, grid, dim3(kThreads), 0, s, a, counts);
-    hipLaunchKernelGGL(k_sqe_finish, dim3(1), dim3(kThreads), 0, s, a, counts);
+    char *base = static_cast<char *>(a.ws);
+    const uint64_t tiles = (uint64_t)a.nqueues * kTilesPerQueue;
+    SqeWs ws{reinterpret_cast<uint32_t *>(base),
+             reinterpret_cast<uint32_t *>(base + align256(tiles * sizeof(uint32_t))),
+             reinterpret_cast<uint32_t *>(base + 2 * align256(tiles * sizeof(uint32_t)))};
+    hipLaunchKernelGGL(k_sqe_order, dim3(1), dim3(kOrderThreads), 0, s, a, ws);
+    hipLaunchKernelGGL(k_sqe_count, dim3((unsigned)tiles), dim3(kThreads), 0, s, a, ws);
+    hipLaunchKernelGGL(k_sqe_emit, dim3((unsigned)tiles), dim3(kThreads), 0, s, a, ws);
+    hipLaunchKernelGGL(k_sqe_finish, dim3(1), dim3(kThreads), 0, s, a, ws);
     return hipGetLastError();
 }
 

@@ -82,16 +82,16 @@ def check_lookup(start, end, lkey, off, ln, va_base=0, page_shift=12, ctx=""):
 
 # -------------------------------------------------------------------- PRP ---
 
-def gpu_prp(lut, off, ln, bus, pool_pages):
-    """Runs dmadesc_build_prp on a canary-filled pool; returns (outputs as
-    numpy, the device pool)."""
+def gpu_prp(lut, off, ln, bus, pool_pages, packed=False):
+    """Runs dmadesc_build_prp (or its packed form) on a canary-filled pool;
+    returns (outputs as numpy, the device pool)."""
     pool = torch.empty((pool_pages, 512), dtype=torch.uint64, device="cuda")
     pool.view(torch.int64).fill_(CANARY_I64)
     n = len(off)
     ws = torch.full((max(dd.workspace_bytes(dd.OP_BUILD_PRP, n), 8),), 0xAB,
                     dtype=torch.uint8, device="cuda")
     out = dd.build_prp(dev(np.asarray(lut, np.uint64)), dev(np.asarray(off, np.uint64)),
-                       dev(np.asarray(ln, np.uint64)), bus, pool, ws=ws)
+                       dev(np.asarray(ln, np.uint64)), bus, pool, ws=ws, packed=packed)
     torch.cuda.synchronize()
     g = {k: host(v) for k, v in out.items()}
     g["total"] = int(g.pop("total_pages")[0])
@@ -111,15 +111,18 @@ def assert_prp_columns_equal(o, g, ctx=""):
     assert o["total"] == g["total"], (ctx, o["total"], g["total"])
 
 
-def check_prp_full(lut, off, ln, bus, pool_pages, ctx=""):
+def check_prp_full(lut, off, ln, bus, pool_pages, ctx="", packed=False):
     """Whole-pool comparison: both pools start as canary, so equal pools mean
-    the GPU wrote exactly the oracle's entries and nothing else."""
+    the GPU wrote exactly the oracle's entries and nothing else (the page
+    layout's padding words aside; the packed layout has none)."""
     o_pool = np.full((pool_pages, 512), CANARY, dtype=np.uint64)
-    o = oracle.build_prp(lut, off, ln, bus, pool_pages, pool=o_pool)
-    g, pool = gpu_prp(lut, off, ln, bus, pool_pages)
+    build = oracle.build_prp_packed if packed else oracle.build_prp
+    o = build(lut, off, ln, bus, pool_pages, pool=o_pool)
+    g, pool = gpu_prp(lut, off, ln, bus, pool_pages, packed=packed)
     assert_prp_columns_equal(o, g, ctx)
     gp = host(pool)
-    mask_padding(o_pool, gp, padding_spans(o["prp2"], o["status"], off, ln, bus))
+    if not packed:
+        mask_padding(o_pool, gp, padding_spans(o["prp2"], o["status"], off, ln, bus))
     if not np.array_equal(o_pool, gp):
         bad = np.argwhere(o_pool != gp)
         s, p = bad[0]

@@ -96,6 +96,21 @@ def test_build_prp_rejects_bad_arguments():
 
 
 @no_gpu_only
+def test_build_prp_packed_rejects_bad_arguments():
+    f = dd.lib().dmadesc_build_prp_packed
+    ok = [P, 16, P, P, 8, 0x10000, P, 4, P, P, P, P, P, 1 << 20, NULL]
+    for k, bad in [(5, 0x10008), (1, 1 << 48), (4, 1 << 32), (11, NULL), (0, NULL),
+                   (6, NULL), (6, P + 8), (2, NULL), (8, NULL), (12, NULL), (13, 8)]:
+        args = list(ok)
+        args[k] = bad
+        assert f(*args) == EINVAL, (k, bad)
+    # Slot counts must stay below 2^62: (16 * lut_entries + 2) * n.
+    args = list(ok)
+    args[1], args[4] = (1 << 44), (1 << 20)
+    assert f(*args) == EINVAL
+
+
+@no_gpu_only
 def test_partition_rejects_bad_arguments():
     f = dd.lib().dmadesc_partition_by_queue
     ok = [P, 100, 4, P, P, P, P, 1 << 20, NULL]
@@ -126,8 +141,8 @@ def test_empty_lookup_is_a_no_op():
              NULL, 0, NULL) == 0
 
 
-@pytest.mark.parametrize("name", ["mr_lookup", "build_prp", "partition_by_queue",
-                                  "emit_sqe"])
+@pytest.mark.parametrize("name", ["mr_lookup", "build_prp", "build_prp_packed",
+                                  "partition_by_queue", "emit_sqe"])
 def test_binding_names_match_abi(name):
     assert callable(getattr(dd, name))
     assert f"dmadesc_{name}" in _declared()
