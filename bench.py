@@ -2,15 +2,19 @@
 """Benchmark: batched DMA-descriptor building on one MI355X.
 
 One step = the whole hot path over one batch: page-rounded MR lookup, PRP
-build (PRP1/PRP2 + chained lists) and stable split by queue, three calls on
+build (PRP1/PRP2 + chained lists; packed lists by default, --layout page for
+one run of list pages per request) and stable split by queue, three calls on
 one stream, over the 16,777,216-request Mixed workload (256 GiB heap of
 4,194,304 GPU pages, 4,096 regions, log-uniform 512 B - 1 MiB requests,
 Zipf(1.1) over 64 queues). Inputs are resident in HBM before timing starts.
 
 Prints ONE JSON line. `value` is requests per second (millions) over the
-timed steps; `roofline` describes the dominant call (the PRP build):
+timed steps; `roofline` describes the dominant call (the PRP build of the
+step's layout; the other layout's build is timed alone beside it):
 algorithmic bytes of one launch / its mean duration from HIP events recorded
-on the stream it runs on. `cpu_baseline` times the single-threaded oracle on a
+on the stream it runs on. `emit_sqe` times the stage after the path (NVMe
+submission entries for the first window of every queue) on the step's outputs,
+outside the timed steps. `cpu_baseline` times the single-threaded oracle on a
 bounded sample of the same workload.
 """
 from __future__ import annotations
@@ -27,8 +31,11 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, AMD public specification
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_build_prp_mixed.json")
 PRP_SOURCES = ["build_prp.hip", "dd_device.hpp"]
+
+
+def traffic_file(layout: str, workload: str) -> str:
+    return os.path.join(ROOT, "profiles", f"traffic_build_prp_{layout}_{workload}.json")
 
 
 def parse():
@@ -38,11 +45,18 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="mixed",
                     choices=["tiny", "small", "large", "mixed"])
+    ap.add_argument("--layout", default="packed", choices=["packed", "page"],
+                    help="PRP list layout of the timed step: lists back to back "
+                         "(dmadesc_build_prp_packed) or one run of list pages per request "
+                         "(dmadesc_build_prp); the other layout's PRP build is timed too")
     ap.add_argument("--cpu-sample", type=int, default=1 << 21,
                     help="requests of the workload the oracle is timed on")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="minimum CPU time spent timing the oracle")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--emit-reps", type=int, default=20,
+                    help="launches of the submission-entry stage timed after the steps "
+                         "(0 = skip it)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a plain 1 GiB device copy (for counter scaling) and exit")
     ap.add_argument("--list-write-floor", action="store_true",
@@ -62,7 +76,9 @@ def prp_source_hash() -> str:
 def algorithmic_bytes(d, np):
     """Bytes each call must move, each column once (per-request figures:
     lookup 16 read + 25 written; PRP 16 read + 8 per GPU page touched, 17
-    written + 8 per list entry or chain pointer; split 4 read + 4 written)."""
+    written + 8 per list word; split 4 read + 4 written). List words: page
+    layout m + L - 1 per request (entries and chain pointers); packed layout
+    the whole dense range, E + floor(E / 511) words for E entries in all."""
     off, ln = d["off"], d["len"]
     n = off.shape[0]
     heap = np.uint64(d["lut_entries"]) * np.uint64(65536)
@@ -73,21 +89,78 @@ def algorithmic_bytes(d, np):
     m = np.where(lists, pages - 1, 0).astype(np.float64)
     lp = np.where(lists, (pages - 2 + 510) // 511, 0).astype(np.float64)
     entries = float((m + lp - np.where(lists, 1.0, 0.0)).sum())
+    e_total = int(m.sum())
+    packed_words = float(e_total + e_total // 511)
     lookup = n * (16 + 25) + d["regions"] * 20
-    prp = n * (16 + 17) + 8 * float(frames.sum()) + 8 * entries
+    base = n * (16 + 17) + 8 * float(frames.sum())
     split = n * 8
-    return dict(lookup=float(lookup), build_prp=float(prp), partition=float(split),
+    return dict(lookup=float(lookup), build_prp=base + 8 * entries,
+                build_prp_packed=base + 8 * packed_words, partition=float(split),
                 list_entries=entries, prp_entries=float(pages.astype(np.float64).sum()))
 
 
-def cpu_baseline(name, sample, min_seconds):
+def emit_stage(dd, d, np, torch, prp_out, sp_out, ln, reps):
+    """Times dmadesc_emit_sqe on the step's PRP and split outputs: every queue
+    gets a ring of 65536 entries with all but one slot free, tails from a
+    seeded draw, cursors at 0, so each launch consumes the first window of
+    every bucket. Algorithmic bytes: per consumed entry 4 (perm) + 1 (status)
+    + 8 (len); per placed entry 24 (slba, prp1, prp2) + 64 (the entry) + 4
+    (request map); per queue 48."""
+    import synth
+    dev = torch.device("cuda:0")
+    n, nq = d["n"], d["nqueues"]
+    depth = 65536
+    rings = torch.empty((nq, depth * 64), dtype=torch.uint8, device=dev)
+    ring = torch.tensor([rings[q].data_ptr() for q in range(nq)],
+                        dtype=torch.int64).view(torch.uint64).to(dev)
+    up = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)  # noqa: E731
+    depth_t = up(np.full(nq, depth, np.uint32))
+    free_t = up(np.full(nq, depth - 1, np.uint32))
+    tail0 = up(np.random.default_rng(1).integers(0, depth, nq).astype(np.uint32))
+    cursor0 = torch.zeros(nq, dtype=torch.uint64, device=dev)
+    tail, cursor = tail0.clone(), cursor0.clone()
+    placed = torch.empty(nq, dtype=torch.uint32, device=dev)
+    rid = torch.empty(nq * depth, dtype=torch.uint32, device=dev)
+    slba = up(synth.slba(d["name"], n))
+    ws = torch.empty(dd.workspace_bytes(dd.OP_EMIT_SQE, n, nq), dtype=torch.uint8, device=dev)
+
+    def call():
+        tail.copy_(tail0)
+        cursor.copy_(cursor0)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        dd.emit_sqe(sp_out["perm"], sp_out["qoff"], prp_out["status"], ln, slba,
+                    prp_out["prp1"], prp_out["prp2"], ring, depth_t, free_t, tail, cursor,
+                    placed=placed, req_of_slot=rid, ws=ws)
+        e1.record()
+        return e0, e1
+
+    for _ in range(3):
+        call()
+    torch.cuda.synchronize()
+    evs = [call() for _ in range(reps)]
+    torch.cuda.synchronize()
+    ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    consumed = int(cursor.cpu().numpy().astype(np.int64).sum())
+    n_placed = int(placed.cpu().numpy().astype(np.int64).sum())
+    nbytes = consumed * 13 + n_placed * (24 + 64 + 4) + nq * 48
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"kernels": "k_sqe_count + k_sqe_emit + k_sqe_finish", "ring_depth": depth,
+            "consumed": consumed, "placed": n_placed, "mean_launch_ms": round(ms, 4),
+            "algorithmic_bytes_per_launch": nbytes, "achieved_gbs": round(gbs, 1),
+            "frac": round(gbs / PEAK_HBM_GBS, 4),
+            "entries_per_s": round(n_placed / (ms * 1e-3), 1)}
+
+
+def cpu_baseline(name, sample, min_seconds, layout):
     import numpy as np
 
     import oracle
     import synth
     d = synth.generate(name, n=sample)
     bus = d["list_bus_base"]
-    total = oracle.build_prp(d["lut"], d["off"], d["len"], bus, 0)["total"]
+    build = oracle.build_prp_packed if layout == "packed" else oracle.build_prp
+    total = build(d["lut"], d["off"], d["len"], bus, 0)["total"]
     pool = np.ones((max(total, 1), 512), dtype=np.uint64)      # pre-faulted, reused
     old = os.sched_getaffinity(0)
     cpu = min(old)
@@ -99,7 +172,7 @@ def cpu_baseline(name, sample, min_seconds):
             if d["regions"]:
                 oracle.mr_lookup(d["rstart"], d["rend"], d["rlkey"], d["off"], d["len"],
                                  va_base=d["va_base"])
-            oracle.build_prp(d["lut"], d["off"], d["len"], bus, total, pool=pool)
+            build(d["lut"], d["off"], d["len"], bus, total, pool=pool)
             oracle.partition(d["qid"], d["nqueues"])
             spent += time.perf_counter() - t0
             reps += 1
@@ -108,7 +181,7 @@ def cpu_baseline(name, sample, min_seconds):
     return {"value": round(sample * reps / spent / 1e6, 4), "unit": "M req/s", "cores": 1,
             "kind": "oracle",
             "sample": (f"first {sample:,} requests of the {name} workload, lookup + PRP build "
-                       f"(lists into a pre-faulted host pool) + split, single thread pinned "
+                       f"({layout} lists into a pre-faulted host pool) + split, single thread pinned "
                        f"to one core, {reps} repetitions, {spent:.1f} s"),
             "host_cores": os.cpu_count()}
 
@@ -199,11 +272,16 @@ def main():
 
     # Capacity query: with an empty pool the call still reports the pages
     # the batch needs.
+    packed = args.layout == "packed"
     empty = torch.empty((0, 512), dtype=torch.uint64, device=dev)
-    probe = dd.build_prp(lut, off, ln, bus, empty)
-    torch.cuda.synchronize()
-    pool_pages = int(probe["total_pages"].cpu()[0])
-    pool = torch.empty((pool_pages, 512), dtype=torch.uint64, device=dev)
+
+    def pool_for(pk):
+        probe = dd.build_prp(lut, off, ln, bus, empty, packed=pk)
+        torch.cuda.synchronize()
+        pages = int(probe["total_pages"].cpu()[0])
+        return torch.empty((max(pages, 1), 512), dtype=torch.uint64, device=dev), pages
+
+    pool, pool_pages = pool_for(packed)
 
     lk_out = prp_out = sp_out = None
     ws_prp = torch.empty(max(dd.workspace_bytes(dd.OP_BUILD_PRP, n), 1), dtype=torch.uint8, device=dev)
@@ -217,7 +295,7 @@ def main():
         if d["regions"]:
             lk_out = dd.mr_lookup(rs, re_, rk, off, ln, va_base=d["va_base"], out=lk_out)
         ev[1].record()
-        prp_out = dd.build_prp(lut, off, ln, bus, pool, out=prp_out, ws=ws_prp)
+        prp_out = dd.build_prp(lut, off, ln, bus, pool, out=prp_out, ws=ws_prp, packed=packed)
         ev[2].record()
         if nq:
             sp_out = dd.partition_by_queue(qid, nq, out=sp_out, ws=ws_sp)
@@ -239,18 +317,40 @@ def main():
                 for k, c in enumerate(calls)}
     status = prp_out["status"].cpu().numpy()
     ab = algorithmic_bytes(d, np)
-    step_bytes = ab["lookup"] * bool(d["regions"]) + ab["build_prp"] + ab["partition"] * bool(nq)
+    prp_key = "build_prp_packed" if packed else "build_prp"
+    step_bytes = ab["lookup"] * bool(d["regions"]) + ab[prp_key] + ab["partition"] * bool(nq)
     ms = elapsed / args.steps * 1e3
     prp_ms = per_call["build_prp"]
-    achieved = ab["build_prp"] / (prp_ms * 1e-3) / 1e9
+    achieved = ab[prp_key] / (prp_ms * 1e-3) / 1e9
 
     traffic = None
-    if os.path.exists(TRAFFIC_FILE):
-        with open(TRAFFIC_FILE) as f:
+    tf = traffic_file(args.layout, args.workload)
+    if os.path.exists(tf):
+        with open(tf) as f:
             rec = json.load(f)
-        if rec.get("source_sha256") == prp_source_hash() and rec.get("workload") == args.workload:
+        if rec.get("source_sha256") == prp_source_hash():
             traffic = rec.get("traffic_bytes_per_launch")
 
+    # The other layout's PRP build, timed alone on the same inputs.
+    other = "page" if packed else "packed"
+    o_pool, o_pages = pool_for(not packed)
+    o_out = None
+    o_ev = []
+    for r in range(max(args.steps // 2, 3) + 3):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        o_out = dd.build_prp(lut, off, ln, bus, o_pool, out=o_out, ws=ws_prp, packed=not packed)
+        e1.record()
+        if r >= 3:
+            o_ev.append((e0, e1))
+    torch.cuda.synchronize()
+    o_ms = float(np.mean([a.elapsed_time(b) for a, b in o_ev]))
+    o_key = "build_prp" if packed else "build_prp_packed"
+    o_gbs = ab[o_key] / (o_ms * 1e-3) / 1e9
+    del o_pool
+
+    kernel = ("dmadesc_build_prp_packed" if packed else "dmadesc_build_prp") + \
+        " (k_prp_clear + k_prp_build)"
     result = {
         "metric": "descriptor requests/sec (M/s) + achieved HBM GB/s vs MI355X peak",
         "value": round(n * args.steps / elapsed / 1e6, 3),
@@ -265,22 +365,30 @@ def main():
         "dtype": "u64",
         "data": "synthetic",
         "config": {"workload": args.workload, "requests": n, "lut_entries": d["lut_entries"],
-                   "regions": d["regions"], "nqueues": nq, "list_pages": pool_pages,
-                   "calls": "mr_lookup + build_prp + partition_by_queue, one stream"},
-        "roofline": {"bound": "hbm", "kernel": "dmadesc_build_prp (k_prp_clear + k_prp_build)",
+                   "regions": d["regions"], "nqueues": nq, "prp_layout": args.layout,
+                   "list_pages": pool_pages,
+                   "calls": f"mr_lookup + {kernel.split()[0][8:]} + partition_by_queue, one stream"},
+        "roofline": {"bound": "hbm", "kernel": kernel,
                      "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
-                     "algorithmic_bytes_per_launch": ab["build_prp"],
+                     "algorithmic_bytes_per_launch": ab[prp_key],
                      "mean_launch_ms": round(prp_ms, 4)},
         "per_call_ms": {k: round(v, 4) for k, v in per_call.items()},
         "step_algorithmic_gbs": round(step_bytes / (ms * 1e-3) / 1e9, 1),
         "step_frac_of_peak": round(step_bytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
         "prp_entries_per_s": round(ab["prp_entries"] * args.steps / elapsed, 1),
         "refused_requests": int((status != 0).sum()),
+        f"{other}_layout_build_prp": {
+            "mean_launch_ms": round(o_ms, 4), "list_pages": o_pages,
+            "algorithmic_bytes_per_launch": ab[o_key], "achieved_gbs": round(o_gbs, 1),
+            "frac": round(o_gbs / PEAK_HBM_GBS, 4),
+            "refused_requests": int((o_out["status"].cpu().numpy() != 0).sum())},
     }
+    if nq and args.emit_reps > 0:
+        result["emit_sqe"] = emit_stage(dd, d, np, torch, prp_out, sp_out, ln, args.emit_reps)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(args.workload, min(args.cpu_sample, n),
-                                              args.cpu_seconds)
+                                              args.cpu_seconds, args.layout)
     print(json.dumps(result), flush=True)
 
 

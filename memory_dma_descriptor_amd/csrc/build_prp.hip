@@ -384,8 +384,8 @@ struct PackTab {
     T start[kWave + 1];         // first data slot of each request, - S (clamped to E - S)
     T foff[kWave + 1];          // exclusive prefix of staged GPU pages
     T m[kWave];                 // list entries (0: none)
-    uint64_t f0[kWave];         // GPU page holding data entry 0
-    uint32_t ph[kWave];         // 4 KiB page of data entry 0 within GPU page f0
+    uint64_t f0[kWave];         // GPU page of PRP1, the first staged page
+    uint32_t ph[kWave];         // 4 KiB page of data entry 0 counted from f0 (< 32)
     uint64_t lut[kTileFrames];
 };
 union PackLds {
@@ -393,98 +393,131 @@ union PackLds {
     PackTab<uint64_t> wide;
 };
 
-// Writes the aligned 4-word groups covering pool words [wlo, whi) of one
-// packed round; words outside the range belong to other rounds.
+// Value of pool word w of a packed round whose owner is request r (record
+// st, mm, f0, ph, fb; rel = the slot the word stands for, relative to S).
+template <typename T, bool kStaged>
+__device__ __forceinline__ uint64_t pack_word(const PackTab<T> &P, uint64_t w, T rel, T st,
+                                              T mm, uint64_t f0, uint32_t ph, T fb,
+                                              const uint64_t *__restrict__ lut, uint64_t bus)
+{
+    const uint32_t o = (uint32_t)(w & 511u);
+    const T j = rel - st;                                    // entry at this slot
+    T e = j;                                                 // entry to write, if any
+    if (o == 511u) {
+        const T rem = mm - j - 1;                            // entries after the slot
+        if (rem >= 2) return bus + (((w >> 9) + 1) << 12);   // chain pointer
+        if (rem == 0) return 0;                              // list ended in word 510
+        e = mm - 1;                                          // the final entry moves up
+    } else if (o == 0u && j > 0 && j == mm - 1) {
+        return 0;                                            // vacated by the final entry
+    }
+    const T t0 = (T)ph + e;
+    const T fi = t0 >> 4;
+    const uint64_t l = kStaged ? P.lut[fb + fi] : lut[f0 + fi];
+    return l + ((uint64_t)(t0 & 15u) << 12);
+}
+
+// Writes the aligned 2-word pairs covering pool words [wlo, whi) of one
+// packed round; words outside the range belong to other rounds. Each lane
+// takes kPairs pairs per step, pair c + 64 k + lane, so each of the wave's
+// 16-byte stores covers 1 KiB of the pool contiguously, and the pairs' owner
+// searches run in lockstep, so their LDS latencies overlap.
 template <typename T, bool kStaged>
 __device__ __forceinline__ void pack_groups(const PackTab<T> &P, uint64_t S, uint64_t wlo,
                                             uint64_t whi, const uint64_t *__restrict__ lut,
                                             uint64_t *__restrict__ pool, uint64_t bus)
 {
-    const uint64_t ghi = (whi + 3) >> 2;
-    for (uint64_t G = (wlo >> 2) + lane(); G < ghi; G += kWave) {
-        const uint64_t w0 = G << 2;
-        uint64_t v[4];
-        bool all = true;
-        int r = -1;
-        T st = 0, mm = 0;
-        uint64_t f0 = 0;
-        uint32_t ph = 0;
-        T fb = 0;
+    constexpr int kPairs = 4;
+    const uint64_t c0 = wlo >> 1, chi = (whi + 1) >> 1;
+    const T last = (T)(P.start[kWave] - 1);                  // last slot of the round
+    for (uint64_t c = c0; c < chi; c += kPairs * kWave) {
+        T key[kPairs];
+        int r[kPairs];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const uint64_t w = w0 + k;
-            v[k] = 0;
-            if (w < wlo || w >= whi) {
-                all = false;
-                continue;
-            }
-            const uint64_t pg = w >> 9;
+        for (int k = 0; k < kPairs; ++k) {
+            // The slot of the pair's first word inside the range (clamped).
+            uint64_t w = (c + (uint64_t)k * kWave + lane()) << 1;
+            w = w < wlo ? wlo : w;
             const uint32_t o = (uint32_t)(w & 511u);
-            // Word 511 is decided by the owner of the page's last slot.
-            const T rel = (T)(pg * 511 + (o == 511u ? 510u : o) - S);
-            const int r0 = r;
-            if (r < 0) r = owner_of<kWave>(P.start, rel);
-            else
-                while (P.start[r + 1] <= rel) ++r;
-            if (r != r0) {
-                st = P.start[r];
-                mm = P.m[r];
-                f0 = P.f0[r];
-                ph = P.ph[r];
-                fb = P.foff[r];
-            }
-            const T j = rel - st;                            // entry at this slot
-            T e = j;                                         // entry to write, if any
-            bool data = true;
-            if (o == 511u) {
-                const T rem = mm - j - 1;                    // entries after the slot
-                if (rem >= 2) {
-                    v[k] = bus + ((pg + 1) << 12);           // chain pointer
-                    data = false;
-                } else if (rem == 1) {
-                    e = mm - 1;                              // the final entry moves up
-                } else {
-                    data = false;                            // list ended in word 510
-                }
-            } else if (o == 0u && j > 0 && j == mm - 1) {
-                data = false;                                // vacated by the final entry
-            }
-            if (data) {
-                const T t0 = (T)ph + e;
-                const T fi = t0 >> 4;
-                const uint64_t l = kStaged ? P.lut[fb + fi] : lut[f0 + fi];
-                v[k] = l + ((uint64_t)(t0 & 15u) << 12);
-            }
+            const uint64_t d = (w >> 9) * 511 + (o == 511u ? 510u : o) - S;
+            key[k] = d < (uint64_t)last ? (T)d : last;
+            r[k] = 0;
         }
-        uint64_t *dst = pool + w0;
-        if (all) {
-            *reinterpret_cast<u64x2 *>(dst) = u64x2{v[0], v[1]};
-            *reinterpret_cast<u64x2 *>(dst + 2) = u64x2{v[2], v[3]};
-        } else {
 #pragma unroll
-            for (int k = 0; k < 4; ++k)
-                if (w0 + k >= wlo && w0 + k < whi) dst[k] = v[k];
+        for (int step = kWave / 2; step > 0; step >>= 1) {
+#pragma unroll
+            for (int k = 0; k < kPairs; ++k)
+                r[k] = (P.start[r[k] + step] <= key[k]) ? r[k] + step : r[k];
+        }
+#pragma unroll
+        for (int k = 0; k < kPairs; ++k) {
+            const uint64_t C = c + (uint64_t)k * kWave + lane();
+            if (C >= chi) continue;
+            const uint64_t w0 = C << 1;
+            int rr = r[k];
+            T st = P.start[rr], nx = P.start[rr + 1], mm = P.m[rr], fb = P.foff[rr];
+            uint64_t f0 = P.f0[rr];
+            uint32_t ph = P.ph[rr];
+            uint64_t v[2];
+            bool all = true;
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                const uint64_t w = w0 + q;
+                v[q] = 0;
+                if (w < wlo || w >= whi) {
+                    all = false;
+                    continue;
+                }
+                const uint32_t o = (uint32_t)(w & 511u);
+                const T rel = (T)((w >> 9) * 511 + (o == 511u ? 510u : o) - S);
+                if (nx <= rel) {                             // the pair's second word
+                    do {                                     // begins a later list
+                        ++rr;                                // (requests with no list
+                        st = nx;                             // own no slot: skip them)
+                        nx = P.start[rr + 1];
+                    } while (nx <= rel);
+                    mm = P.m[rr];
+                    fb = P.foff[rr];
+                    f0 = P.f0[rr];
+                    ph = P.ph[rr];
+                }
+                v[q] = pack_word<T, kStaged>(P, w, rel, st, mm, f0, ph, fb, lut, bus);
+            }
+            // Non-temporal: the list words are not read again by this kernel,
+            // and streaming them frees L2 for the table and the columns.
+            uint64_t *dst = pool + w0;
+            if (all) {
+                __builtin_nontemporal_store(u64x2{v[0], v[1]}, reinterpret_cast<u64x2 *>(dst));
+            } else {
+#pragma unroll
+                for (int q = 0; q < 2; ++q)
+                    if (w0 + q >= wlo && w0 + q < whi) __builtin_nontemporal_store(v[q], dst + q);
+            }
         }
     }
 }
 
 template <typename T>
 __device__ __forceinline__ void emit_packed_t(PackTab<T> &P, uint64_t d, uint64_t m,
-                                              uint64_t S, uint64_t E, uint64_t xb,
-                                              uint64_t last_frame,
+                                              uint64_t S, uint64_t E, uint64_t o, uint64_t xb,
+                                              uint64_t last_frame, uint64_t *prp1,
                                               const uint64_t *__restrict__ lut,
                                               uint64_t *__restrict__ pool, uint64_t bus)
 {
+    // A request's staged GPU pages run from PRP1's (o >> 16) to its last one;
+    // data entry e then lies in staged page (ph + e) >> 4, with ph < 32 the
+    // 4 KiB page of entry 0 counted from the start of PRP1's GPU page.
     const int ln = lane();
-    const uint64_t frames = m ? last_frame - (xb >> 16) + 1 : 0;
+    const uint64_t f0 = o >> 16;
+    const uint64_t frames = m ? last_frame - f0 + 1 : 0;
     const uint64_t finc = wave_incl_scan(frames);
     const uint64_t ftot = __shfl(finc, kWave - 1, kWave);
     const uint64_t rs = d - S < E - S ? d - S : E - S;       // d >= S for every lane
     P.start[ln] = (T)rs;
     P.foff[ln] = (T)(finc - frames);
     P.m[ln] = (T)m;
-    P.f0[ln] = xb >> 16;
-    P.ph[ln] = (uint32_t)((xb >> 12) & 15u);
+    P.f0[ln] = f0;
+    P.ph[ln] = (uint32_t)((xb >> 12) & 15u) + (uint32_t)(((xb >> 16) - f0) << 4);
     if (ln == kWave - 1) {
         P.start[kWave] = (T)(E - S);
         P.foff[kWave] = (T)finc;
@@ -508,17 +541,22 @@ __device__ __forceinline__ void emit_packed_t(PackTab<T> &P, uint64_t d, uint64_
             }
         }
         wave_sync_lds();
+        if (m && prp1)
+            __builtin_nontemporal_store(P.lut[P.foff[ln]] + (o & 0xFFFFu), prp1);
         pack_groups<T, true>(P, S, wlo, whi, lut, pool, bus);
     } else {
+        if (m && prp1) __builtin_nontemporal_store(lut[f0] + (o & 0xFFFFu), prp1);
         pack_groups<T, false>(P, S, wlo, whi, lut, pool, bus);
     }
     wave_sync_lds();                                         // the next round rewrites P
 }
 
 // Writes the packed words of the wave's 64 requests of one round (lane k: one
-// request with list entries m from data slot d; m == 0 for no list).
+// request at heap offset o with list entries m from data slot d; m == 0 for
+// no list), and PRP1 of each request with a list.
 __device__ __forceinline__ void emit_round_packed(PackLds &L, uint64_t d, uint64_t m,
-                                                  uint64_t xb, uint64_t last_frame,
+                                                  uint64_t o, uint64_t xb, uint64_t last_frame,
+                                                  uint64_t *prp1,
                                                   const uint64_t *__restrict__ lut,
                                                   uint64_t *__restrict__ pool, uint64_t bus)
 {
@@ -529,9 +567,9 @@ __device__ __forceinline__ void emit_round_packed(PackLds &L, uint64_t d, uint64
     const uint64_t S = __shfl(d, first, kWave);
     const uint64_t E = __shfl(d + m, last, kWave);
     if (E - S < (1ull << 31))
-        emit_packed_t<uint32_t>(L.fast, d, m, S, E, xb, last_frame, lut, pool, bus);
+        emit_packed_t<uint32_t>(L.fast, d, m, S, E, o, xb, last_frame, prp1, lut, pool, bus);
     else
-        emit_packed_t<uint64_t>(L.wide, d, m, S, E, xb, last_frame, lut, pool, bus);
+        emit_packed_t<uint64_t>(L.wide, d, m, S, E, o, xb, last_frame, prp1, lut, pool, bus);
 }
 
 template <bool kPacked>
@@ -543,7 +581,7 @@ __global__ __launch_bounds__(kThreads, 4) void k_prp_build(
     uint8_t *__restrict__ status, uint64_t *__restrict__ total,
     Header *__restrict__ hdr, uint64_t *__restrict__ bstat)
 {
-    __shared__ uint64_t s_red[kWaves];
+    __shared__ uint64_t s_red[kItems * kWaves];
     __shared__ uint64_t s_bid, s_excl;
     __shared__ typename std::conditional<kPacked, PackLds, RoundLds>::type s_round[kWaves];
 
@@ -558,8 +596,8 @@ __global__ __launch_bounds__(kThreads, 4) void k_prp_build(
 #pragma unroll
     for (int k = 0; k < kItems; ++k) {
         const uint64_t i = base + (uint64_t)k * kThreads + t;
-        o[k] = i < n ? off[i] : 0;
-        l[k] = i < n ? len[i] : 0;                   // len 0 decodes as invalid
+        o[k] = i < n ? __builtin_nontemporal_load(off + i) : 0;
+        l[k] = i < n ? __builtin_nontemporal_load(len + i) : 0;   // len 0 decodes as invalid
     }
     // PRP1, a two-page PRP2 and the status do not depend on the list pages,
     // so they are written before the scan and overlap it. A request later
@@ -573,7 +611,10 @@ __global__ __launch_bounds__(kThreads, 4) void k_prp_build(
             uint64_t pages;
             const uint8_t st = decode(o[k], l[k], heap, pages);
             const uint64_t x = (o[k] & ~4095ull) + 4096;
-            i1[k] = st == kOk ? o[k] >> 16 : 0;
+            // Packed lists stage their request's table entries from PRP1's
+            // GPU page on, so PRP1 of a list request is taken from there.
+            const bool staged_prp1 = kPacked && pages >= 3;
+            i1[k] = (st == kOk && !staged_prp1) ? o[k] >> 16 : 0;
             i2[k] = (st == kOk && pages == 2) ? x >> 16 : 0;
         }
 #pragma unroll
@@ -587,10 +628,14 @@ __global__ __launch_bounds__(kThreads, 4) void k_prp_build(
             uint64_t pages;
             const uint8_t st = decode(o[k], l[k], heap, pages);
             if (i < n) {
-                prp1[i] = st == kOk ? v1[k] + (o[k] & 0xFFFFu) : 0;
-                if (pages < 3) prp2[i] = (st == kOk && pages == 2) ?
-                    v2[k] + (((o[k] & ~4095ull) + 4096) & 0xFFFFu) : 0;
-                status[i] = st;
+                // Output columns and input columns are streamed (non-temporal):
+                // neither is read again by this kernel.
+                if (!(kPacked && st == kOk && pages >= 3))
+                    __builtin_nontemporal_store(st == kOk ? v1[k] + (o[k] & 0xFFFFu) : 0, prp1 + i);
+                if (pages < 3)
+                    __builtin_nontemporal_store((st == kOk && pages == 2) ?
+                        v2[k] + (((o[k] & ~4095ull) + 4096) & 0xFFFFu) : 0, prp2 + i);
+                __builtin_nontemporal_store(st, status + i);
             }
         }
     } else {
@@ -607,16 +652,31 @@ __global__ __launch_bounds__(kThreads, 4) void k_prp_build(
         }
     }
     // Scanned per request: list pages (page layout) or list entries (packed).
-    uint64_t agg = 0;
+    // Request order is (item, wave, lane): wave scans per item, then one
+    // barrier to combine the waves' totals.
 #pragma unroll
     for (int k = 0; k < kItems; ++k) {
         uint64_t pages;
         const uint8_t st = decode(o[k], l[k], heap, pages);
         const uint64_t cnt = (st == kOk && pages >= 3)
                                  ? (kPacked ? pages - 1 : (pages - 2 + 510) / 511) : 0;
-        uint64_t tot;
-        pre[k] = agg + block_excl_scan<kThreads>(cnt, s_red, &tot);
-        agg += tot;
+        const uint64_t inc = wave_incl_scan(cnt);
+        pre[k] = inc - cnt;
+        if (ln == kWave - 1) s_red[k * kWaves + w] = inc;
+    }
+    __syncthreads();
+    uint64_t agg = 0;
+#pragma unroll
+    for (int k = 0; k < kItems; ++k) {
+        uint64_t before = 0, all = 0;
+#pragma unroll
+        for (int v = 0; v < kWaves; ++v) {
+            const uint64_t x = s_red[k * kWaves + v];
+            before += v < w ? x : 0ull;
+            all += x;
+        }
+        pre[k] += agg + before;
+        agg += all;
     }
     if (w == 0) {
         uint64_t excl = 0;
@@ -657,7 +717,8 @@ __global__ __launch_bounds__(kThreads, 4) void k_prp_build(
         const uint64_t xb = (o[k] & ~4095ull) + 4096;
         const uint64_t last_frame = (o[k] + l[k] - 1) >> 16;
         if constexpr (kPacked)
-            emit_round_packed(s_round[w], slot, lists ? cnt : 0, xb, last_frame, lut, pool, bus);
+            emit_round_packed(s_round[w], slot, lists ? cnt : 0, o[k], xb, last_frame,
+                              i < n ? prp1 + i : nullptr, lut, pool, bus);
         else
             emit_round(s_round[w], xb, slot << 9, lists ? (pages - 1) + (cnt - 1) : 0,
                        lists ? cnt : 0, last_frame, lut, pool, bus);
