@@ -18,6 +18,8 @@ _SO = os.path.join(_HERE, "liboracle.so")
 
 MISS, EXACT, CONTAINED, INVALID = 0, 1, 2, 3
 OK, EINVAL, ERANGE, ENOSPC = 0, 1, 2, 3
+REG_INVALID, REG_HIT, REG_NEW, REG_HIT_NEW, REG_NOSPACE = 0, 1, 2, 3, 4
+DEREG_OK, DEREG_REMOVED, DEREG_STALE = 0, 1, 2
 
 
 def build() -> str:
@@ -74,6 +76,13 @@ def _lib():
         lib.orc_reg_capacity.restype = u64
         lib.orc_reg_export.argtypes = [ctypes.c_void_p, _u64p, _u64p, _u64p, u64]
         lib.orc_reg_export.restype = u64
+        lib.orc_reg_next_id.argtypes = [ctypes.c_void_p]
+        lib.orc_reg_next_id.restype = u64
+        lib.orc_reg_register_batch.argtypes = [ctypes.c_void_p, u64, _u64p, _u64p, u64,
+                                               _u64p, _u8p]
+        lib.orc_reg_register_batch.restype = u64
+        lib.orc_reg_deregister_batch.argtypes = [ctypes.c_void_p, _u64p, u64, _u8p]
+        lib.orc_reg_deregister_batch.restype = None
         _lib_handle = lib
     return _lib_handle
 
@@ -220,3 +229,29 @@ class Registry:
         s, e, h = (np.empty(k, np.uint64) for _ in range(3))
         _lib().orc_reg_export(self._h, _p(s, _u64p), _p(e, _u64p), _p(h, _u64p), k)
         return s, e, h
+
+    def next_id(self):
+        return int(_lib().orc_reg_next_id(self._h))
+
+    def register_batch(self, addr, size, capacity):
+        """O4b register batch; returns (handle u64[n], kind u8[n], needed capacity)."""
+        addr, size = _u64(addr), _u64(size)
+        n = addr.shape[0]
+        h, k = np.empty(n, np.uint64), np.empty(n, np.uint8)
+        need = _lib().orc_reg_register_batch(self._h, capacity, _p(addr, _u64p),
+                                             _p(size, _u64p), n, _p(h, _u64p), _p(k, _u8p))
+        return h, k, int(need)
+
+    def deregister_batch(self, handles):
+        """O4b deregister batch; returns status u8[n]."""
+        handles = _u64(handles)
+        st = np.empty(handles.shape[0], np.uint8)
+        _lib().orc_reg_deregister_batch(self._h, _p(handles, _u64p), handles.shape[0],
+                                        _p(st, _u8p))
+        return st
+
+    def records(self):
+        """(start, end, handle, refs) of the live records in sorted order."""
+        s, e, h = self.table()
+        refs = np.array([self.refs(int(x)) for x in h], dtype=np.int64)
+        return s, e, h, refs

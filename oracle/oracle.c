@@ -522,3 +522,78 @@ uint64_t orc_reg_export(const orc_registry *g, uint64_t *start, uint64_t *end,
     }
     return k;
 }
+
+/* ------------------------------------------------------------------------
+ * O4b  Registry batches.
+ *
+ * Each item is applied in order with O4's register/deregister, so a batch
+ * means exactly what the same calls made one after another mean ([NCCL-26]
+ * "Communicator User Registration Cache" and "IB Backend MR Cache"). The
+ * record table's room is the caller's: a register batch that would leave more
+ * records than the capacity is applied to a copy, found too large, and
+ * dropped, and the call reports the capacity O4's growth rule (0 -> 32, then
+ * doubling) reaches from the caller's.
+ *
+ * Pinned by: the register experiment of "真实 ncclCommRegister 语义实验" as
+ * one batch and as a deregister batch (the fourth deregister is stale), the
+ * 0 -> 32 -> 64 -> 128 growth, and a record-list model in Python replayed
+ * over random batches.
+ * ------------------------------------------------------------------------ */
+uint64_t orc_reg_next_id(const orc_registry *g) { return g->next_id; }
+
+static orc_registry *reg_clone(const orc_registry *g)
+{
+    orc_registry *c = (orc_registry *)calloc(1, sizeof(*c));
+    *c = *g;
+    c->rec = NULL;
+    if (g->capacity) {
+        c->rec = (orc_record *)malloc(g->capacity * sizeof(orc_record));
+        memcpy(c->rec, g->rec, g->count * sizeof(orc_record));
+    }
+    return c;
+}
+
+uint64_t orc_reg_register_batch(orc_registry *g, uint64_t capacity,
+                                const uint64_t *addr, const uint64_t *size, uint64_t n,
+                                uint64_t *handle, uint8_t *kind)
+{
+    orc_registry *c = reg_clone(g);
+    const uint64_t first_new = c->next_id;
+    for (uint64_t i = 0; i < n; ++i) {
+        const uint64_t before = c->count;
+        const uint64_t h = orc_reg_register(c, addr[i], size[i]);
+        handle[i] = h;
+        if (h == 0) kind[i] = ORC_REG_INVALID;
+        else if (h < first_new) kind[i] = ORC_REG_HIT;
+        else if (c->count > before) kind[i] = ORC_REG_NEW;
+        else kind[i] = ORC_REG_HIT_NEW;
+    }
+    uint64_t need = capacity;
+    while (need < c->count) need = need == 0 ? 32 : 2 * need;
+    if (c->count > capacity) {                      /* refused: keep g as it was */
+        for (uint64_t i = 0; i < n; ++i) {
+            handle[i] = 0;
+            kind[i] = ORC_REG_NOSPACE;
+        }
+        orc_reg_destroy(c);
+        return need;
+    }
+    free(g->rec);
+    *g = *c;                                        /* take the copy's records */
+    free(c);
+    return need;
+}
+
+void orc_reg_deregister_batch(orc_registry *g, const uint64_t *handle, uint64_t n,
+                              uint8_t *status)
+{
+    for (uint64_t i = 0; i < n; ++i) {
+        const int64_t refs = orc_reg_refs(g, handle[i]);
+        if (refs < 0) {
+            status[i] = ORC_DEREG_STALE;
+            continue;
+        }
+        orc_reg_deregister(g, handle[i]);
+        status[i] = refs == 1 ? ORC_DEREG_REMOVED : ORC_DEREG_OK;
+    }
+}

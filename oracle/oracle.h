@@ -127,6 +127,29 @@ uint64_t orc_reg_capacity(const orc_registry *g);
 uint64_t orc_reg_export(const orc_registry *g, uint64_t *start, uint64_t *end,
                         uint64_t *handle, uint64_t max);
 
+/*
+ * O4b: batches for the registry, each item applied in order as O4 does,
+ * against a caller capacity for the record table.
+ * register: kind[i] = INVALID (handle 0: zero length or wrap), HIT (a record
+ * that existed before the batch contains the range), NEW (this item inserted
+ * a record), HIT_NEW (a record inserted earlier in the same batch contains it).
+ * If the record count after the batch would exceed `capacity`, nothing is
+ * applied, every kind is NOSPACE and every handle 0. Returns the capacity the
+ * batch needs: `capacity` itself if it fits, else the capacity grown by O4's
+ * rule (0 -> 32, then doubling) until the count fits.
+ * deregister: status[i] = OK (count dropped), REMOVED (dropped to zero, record
+ * freed) or STALE (no live record has that handle).
+ */
+enum { ORC_REG_INVALID = 0, ORC_REG_HIT = 1, ORC_REG_NEW = 2, ORC_REG_HIT_NEW = 3,
+       ORC_REG_NOSPACE = 4 };
+enum { ORC_DEREG_OK = 0, ORC_DEREG_REMOVED = 1, ORC_DEREG_STALE = 2 };
+uint64_t orc_reg_next_id(const orc_registry *g);
+uint64_t orc_reg_register_batch(orc_registry *g, uint64_t capacity,
+                                const uint64_t *addr, const uint64_t *size, uint64_t n,
+                                uint64_t *handle, uint8_t *kind);
+void orc_reg_deregister_batch(orc_registry *g, const uint64_t *handle, uint64_t n,
+                              uint8_t *status);
+
 #ifdef __cplusplus
 }
 #endif

@@ -136,3 +136,42 @@ def queue_feed(qid, status, length, lba_shift, q):
         ok = int(status[i]) == 0 and ln > 0 and ln % block == 0 and ln // block <= 65536
         out.append((int(i), ok))
     return out
+
+
+class RecordList:
+    """Registration records as a plain Python list kept in start order: a
+    range is rounded to whole pages (floor / ceiling); the first record in list
+    order that contains it gains a reference, else a new record goes after
+    every record starting at or before it; a deregistration drops a reference
+    and removes the record at zero; a handle no record holds is stale."""
+
+    def __init__(self, page_shift=12):
+        self.page = 1 << page_shift
+        self.recs = []          # [start, end, handle, refs]
+        self.next = 1
+
+    def register(self, addr, size):
+        if size == 0 or addr + size > U64_MAX:
+            return 0, "invalid"
+        lo, hi = round_bounds(addr, size, self.page)
+        if hi > U64_MAX:
+            return 0, "invalid"
+        for r in self.recs:
+            if r[0] <= lo and hi <= r[1]:
+                r[3] += 1
+                return r[2], "hit"
+        pos = sum(1 for r in self.recs if r[0] <= lo)
+        h = self.next
+        self.next += 1
+        self.recs.insert(pos, [lo, hi, h, 1])
+        return h, "new"
+
+    def deregister(self, handle):
+        for k, r in enumerate(self.recs):
+            if r[2] == handle:
+                r[3] -= 1
+                if r[3] == 0:
+                    del self.recs[k]
+                    return "removed"
+                return "ok"
+        return "stale"
