@@ -14,7 +14,8 @@ step's layout; the other layout's build is timed alone beside it):
 algorithmic bytes of one launch / its mean duration from HIP events recorded
 on the stream it runs on. `emit_sqe` times the stage after the path (NVMe
 submission entries for the first window of every queue) on the step's outputs,
-outside the timed steps. `cpu_baseline` times the single-threaded oracle on a
+and `registry` a batch of registrations and deregistrations on the device
+registration table, both outside the timed steps. `cpu_baseline` times the single-threaded oracle on a
 bounded sample of the same workload.
 """
 from __future__ import annotations
@@ -150,6 +151,69 @@ def emit_stage(dd, d, np, torch, prp_out, sp_out, ln, reps):
             "algorithmic_bytes_per_launch": nbytes, "achieved_gbs": round(gbs, 1),
             "frac": round(gbs / PEAK_HBM_GBS, 4),
             "entries_per_s": round(n_placed / (ms * 1e-3), 1)}
+
+
+def registry_stage(dd, d, np, torch, reps):
+    """Times one register batch (65,536 calls) and one deregister batch on a
+    device registration table that starts as the workload's 4,096 regions:
+    half the calls fall inside a region (hit), a quarter are new ranges and a
+    quarter repeat those (hit on a record of the same batch); the deregister
+    batch names handles of the table, some beyond their references (stale).
+    The table is restored from a copy before each timed call."""
+    dev = torch.device("cuda:0")
+    rng = np.random.default_rng(7)
+    up = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)  # noqa: E731
+    reg = dd.DeviceRegistry(0)
+    rs, re_ = d["rstart"], d["rend"]
+    reg.register(up(rs), up(re_ - rs))
+    n = dd.REG_MAX_BATCH
+    pick = rng.integers(0, len(rs), n)
+    span = (re_ - rs)[pick]
+    off = rng.integers(0, 1 << 62, n).astype(np.uint64) % np.maximum(span // np.uint64(2), 1)
+    addr = rs[pick] + off
+    size = np.maximum((span - off) // np.uint64(4), np.uint64(1))
+    fresh = np.arange(n // 4, dtype=np.uint64)
+    addr[n // 2: 3 * n // 4] = np.uint64(1 << 46) + fresh * np.uint64(1 << 21)
+    size[n // 2: 3 * n // 4] = np.uint64(1 << 20)
+    addr[3 * n // 4:] = addr[n // 2: 3 * n // 4] + np.uint64(4096)
+    size[3 * n // 4:] = np.uint64(4096)
+    g_addr, g_size = up(addr), up(size)
+    reg.grow(32768)                                     # room for the batch's inserts
+    saved = {k: getattr(reg, k).clone() for k in ("start", "end", "id", "refs", "by_start",
+                                                  "state")}
+
+    def restore():
+        for k, t in saved.items():
+            getattr(reg, k).copy_(t)
+
+    def timed(fn):
+        out, ms = None, []
+        for r in range(reps + 2):
+            restore()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            out = fn()
+            e1.record()
+            torch.cuda.synchronize()
+            if r >= 2:
+                ms.append(e0.elapsed_time(e1))
+        return out, float(np.mean(ms))
+
+    out, reg_ms = timed(lambda: reg.register(g_addr, g_size, grow=False))
+    kinds = np.bincount(out["kind"].cpu().numpy(), minlength=5)
+    handles = saved["id"][:len(rs)].cpu().numpy()
+    dh = up(rng.choice(handles, n))
+    st, dereg_ms = timed(lambda: reg.deregister(dh))
+    sts = np.bincount(st.cpu().numpy(), minlength=3)
+    return {"table_records": int(len(rs)), "batch": n,
+            "register_batch_ms": round(reg_ms, 4), "deregister_batch_ms": round(dereg_ms, 4),
+            "registrations_per_s": round(n / (reg_ms * 1e-3), 1),
+            "deregistrations_per_s": round(n / (dereg_ms * 1e-3), 1),
+            "register_kinds": {"hit": int(kinds[1]), "new": int(kinds[2]),
+                               "hit_new": int(kinds[3]), "invalid": int(kinds[0])},
+            "deregister_status": {"ok": int(sts[0]), "removed": int(sts[1]),
+                                  "stale": int(sts[2])},
+            "note": "register timing includes the binding's read of the needed capacity"}
 
 
 def cpu_baseline(name, sample, min_seconds, layout):
@@ -386,6 +450,8 @@ def main():
     }
     if nq and args.emit_reps > 0:
         result["emit_sqe"] = emit_stage(dd, d, np, torch, prp_out, sp_out, ln, args.emit_reps)
+    if d["regions"] and args.emit_reps > 0:
+        result["registry"] = registry_stage(dd, d, np, torch, 10)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(args.workload, min(args.cpu_sample, n),
                                               args.cpu_seconds, args.layout)

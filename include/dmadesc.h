@@ -17,6 +17,11 @@
  *   dmadesc_emit_sqe           64-byte NVMe submission entries in per-queue
  *                              rings, one window of the split per call
  *
+ * and the registration cache kept on the device:
+ *
+ *   dmadesc_reg_register       batch of registrations (page-rounded, refcounted)
+ *   dmadesc_reg_deregister     batch of deregistrations
+ *
  * Sources (web pages, cited by title and section):
  *   [NCCL-26] "NCCL 专家课程 26：GPUDirect RDMA、DMA-BUF、MR 与注册缓存",
  *             sections "IB Backend MR Cache" and
@@ -86,7 +91,8 @@ enum dmadesc_op {
     DMADESC_OP_MR_LOOKUP = 1,
     DMADESC_OP_BUILD_PRP = 2,
     DMADESC_OP_PARTITION = 3,
-    DMADESC_OP_EMIT_SQE = 4
+    DMADESC_OP_EMIT_SQE = 4,
+    DMADESC_OP_REGISTRY = 5
 };
 
 /* Largest nqueues dmadesc_partition_by_queue and dmadesc_emit_sqe accept. */
@@ -295,8 +301,69 @@ int dmadesc_emit_sqe(const uint32_t *perm, const uint64_t *qoff, uint32_t nqueue
                      uint32_t *tail, uint64_t *cursor, uint32_t *placed,
                      uint32_t *req_of_slot, void *ws, size_t ws_bytes, void *stream);
 
+/* Registration cache limits and per-call outcomes. */
+#define DMADESC_REG_MAX_BATCH 65536u          /* calls per batch                  */
+#define DMADESC_REG_MAX_CAPACITY (1u << 24)   /* records a table may hold         */
+enum dmadesc_reg_kind {
+    DMADESC_REG_INVALID = 0,  /* zero length, or the range or its rounded end wraps  */
+    DMADESC_REG_HIT = 1,      /* a record present before the batch contains it       */
+    DMADESC_REG_NEW = 2,      /* this call inserted a record                          */
+    DMADESC_REG_HIT_NEW = 3,  /* a record inserted earlier in this batch contains it  */
+    DMADESC_REG_NOSPACE = 4   /* the batch did not fit the capacity; nothing applied  */
+};
+enum dmadesc_dereg_status {
+    DMADESC_DEREG_OK = 0,      /* one reference dropped                                */
+    DMADESC_DEREG_REMOVED = 1, /* the last reference dropped; the record is freed      */
+    DMADESC_DEREG_STALE = 2    /* no live record holds the handle (an error)           */
+};
+
+/*
+ * dmadesc_reg_register / dmadesc_reg_deregister - the registration cache.
+ *
+ * [NCCL-26] "Communicator User Registration Cache": a registration widens the
+ * range [addr, addr + size) to whole pages (floor of the start, ceiling of the
+ * end); if a record fully contains the widened range, that record gains a
+ * reference and its handle is returned, else a new record is inserted in
+ * start order. "IB Backend MR Cache": a deregistration drops a reference and
+ * frees the record at zero; a handle not in the cache is an error; the record
+ * array grows from 0 to 32 and then doubles. A batch means exactly what its
+ * calls made one after another, in index order, mean; among several records
+ * containing a range the first in start order is used, and a new record goes
+ * after the records with the same start.
+ *
+ * Table (caller-owned device memory; `capacity` <= DMADESC_REG_MAX_CAPACITY):
+ *   start, end  u64[capacity]  widened range of each record (end exclusive)
+ *   id          u64[capacity]  handle of each record (> 0, never reused)
+ *   refs        u32[capacity]  reference count
+ *     slots 0 .. count-1 hold the live records in increasing handle order
+ *   by_start    u32[capacity]  slots of the live records in (start, handle)
+ *                              order
+ *   state       u64[2]         count of live records, next handle; a new
+ *                              table is state = {0, 1}
+ * register: addr, size u64[n] (n <= DMADESC_REG_MAX_BATCH); page_shift 12..30.
+ *   Outputs handle u64[n] (0 for INVALID and NOSPACE), kind u8[n] (enum
+ *   dmadesc_reg_kind) and *needed (device u64): the capacity the batch needs,
+ *   equal to `capacity` when it fits, else `capacity` grown 0 -> 32 -> 64 ...
+ *   until it fits. A batch that does not fit changes nothing: the caller
+ *   copies the table into arrays of *needed entries and calls again.
+ * deregister: handle u64[n]; output status u8[n] (enum dmadesc_dereg_status).
+ *   Freed records leave the table; the others keep their order.
+ * Both: the table is updated in place; calls on one table must be ordered.
+ * Workspace: dmadesc_workspace_bytes(DMADESC_OP_REGISTRY, n, capacity).
+ */
+int dmadesc_reg_register(uint64_t *start, uint64_t *end, uint64_t *id, uint32_t *refs,
+                         uint32_t *by_start, uint64_t *state, uint64_t capacity,
+                         uint32_t page_shift, const uint64_t *addr, const uint64_t *size,
+                         uint64_t n, uint64_t *handle, uint8_t *kind, uint64_t *needed,
+                         void *ws, size_t ws_bytes, void *stream);
+int dmadesc_reg_deregister(uint64_t *start, uint64_t *end, uint64_t *id, uint32_t *refs,
+                           uint32_t *by_start, uint64_t *state, uint64_t capacity,
+                           const uint64_t *handle, uint64_t n, uint8_t *status,
+                           void *ws, size_t ws_bytes, void *stream);
+
 /* Workspace bytes needed by `op` for n requests (`param` = nqueues for
- * DMADESC_OP_PARTITION and DMADESC_OP_EMIT_SQE, ignored otherwise). Returns 0 for an unknown op or
+ * DMADESC_OP_PARTITION and DMADESC_OP_EMIT_SQE, the table capacity for
+ * DMADESC_OP_REGISTRY, ignored otherwise). Returns 0 for an unknown op or
  * for an op that needs none. Host-only; launches nothing. */
 size_t dmadesc_workspace_bytes(int op, uint64_t n, uint32_t param);
 

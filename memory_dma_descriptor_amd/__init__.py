@@ -15,7 +15,7 @@ import torch
 from . import _build
 
 __all__ = ["mr_lookup", "build_prp", "build_prp_packed", "partition_by_queue", "emit_sqe",
-           "ring_addresses",
+           "ring_addresses", "DeviceRegistry",
            "workspace_bytes", "DmadescError", "lib", "LIB_PATH", "MAX_QUEUES",
            "SQ_MAX_DEPTH",
            "MISS", "EXACT", "CONTAINED", "INVALID",
@@ -24,7 +24,10 @@ __all__ = ["mr_lookup", "build_prp", "build_prp_packed", "partition_by_queue", "
 LIB_PATH = _build.LIB
 MAX_QUEUES = 256
 SQ_MAX_DEPTH = 65536
-OP_MR_LOOKUP, OP_BUILD_PRP, OP_PARTITION, OP_EMIT_SQE = 1, 2, 3, 4
+OP_MR_LOOKUP, OP_BUILD_PRP, OP_PARTITION, OP_EMIT_SQE, OP_REGISTRY = 1, 2, 3, 4, 5
+REG_MAX_BATCH, REG_MAX_CAPACITY = 65536, 1 << 24
+REG_INVALID, REG_HIT, REG_NEW, REG_HIT_NEW, REG_NOSPACE = 0, 1, 2, 3, 4
+DEREG_OK, DEREG_REMOVED, DEREG_STALE = 0, 1, 2
 MISS, EXACT, CONTAINED, INVALID = 0, 1, 2, 3
 PRP_OK, PRP_EINVAL, PRP_ERANGE, PRP_ENOSPC = 0, 1, 2, 3
 
@@ -44,6 +47,10 @@ _EXPORTS = {
                                    ctypes.c_int),
     "dmadesc_emit_sqe": ([_P, _P, _U32, _P, _P, _P, _P, _P, _U64, _U32, _U32, _U32,
                           _P, _P, _P, _P, _P, _P, _P, _P, _SIZE, _P], ctypes.c_int),
+    "dmadesc_reg_register": ([_P, _P, _P, _P, _P, _P, _U64, _U32, _P, _P, _U64, _P, _P, _P,
+                              _P, _SIZE, _P], ctypes.c_int),
+    "dmadesc_reg_deregister": ([_P, _P, _P, _P, _P, _P, _U64, _P, _U64, _P, _P, _SIZE, _P],
+                               ctypes.c_int),
     "dmadesc_workspace_bytes": ([ctypes.c_int, _U64, _U32], _SIZE),
     "dmadesc_strerror": ([ctypes.c_int], ctypes.c_char_p),
     "dmadesc_version": ([], ctypes.c_int),
@@ -231,3 +238,97 @@ def emit_sqe(perm: torch.Tensor, qoff: torch.Tensor, status: torch.Tensor,
         rid, ws.data_ptr(), ws.numel(), _stream(dev, stream))
     _check("dmadesc_emit_sqe", rc)
     return dict(placed=placed, tail=tail, cursor=cursor, req_of_slot=req_of_slot)
+
+
+class DeviceRegistry:
+    """Registration cache kept in device memory (dmadesc_reg_register /
+    dmadesc_reg_deregister). The record arrays are torch tensors owned here;
+    when a register batch reports that it needs more room, the arrays are
+    copied into larger ones (the C calls never allocate) and the batch is
+    issued again."""
+
+    def __init__(self, capacity: int = 0, page_shift: int = 12, device="cuda"):
+        self.page_shift = page_shift
+        self.device = torch.device(device)
+        self.state = torch.tensor([0, 1], dtype=torch.int64).view(torch.uint64).to(self.device)
+        self.capacity = 0
+        self.start = self.end = self.id = self.refs = self.by_start = None
+        self._needed = torch.zeros(1, dtype=torch.uint64, device=self.device)
+        self.grow(capacity)
+
+    def grow(self, capacity: int) -> None:
+        if capacity > REG_MAX_CAPACITY:
+            raise ValueError(f"capacity above {REG_MAX_CAPACITY}")
+        if capacity <= self.capacity:
+            return
+        dev, c = self.device, capacity
+        new = dict(start=torch.empty(c, dtype=torch.uint64, device=dev),
+                   end=torch.empty(c, dtype=torch.uint64, device=dev),
+                   id=torch.empty(c, dtype=torch.uint64, device=dev),
+                   refs=torch.empty(c, dtype=torch.uint32, device=dev),
+                   by_start=torch.empty(c, dtype=torch.uint32, device=dev))
+        if self.capacity:
+            k = self.count()
+            for name, t in new.items():
+                t[:k] = getattr(self, name)[:k]
+        for name, t in new.items():
+            setattr(self, name, t)
+        self.capacity = capacity
+
+    def count(self) -> int:
+        return int(self.state.view(torch.int64)[0].item())
+
+    def next_id(self) -> int:
+        return int(self.state.view(torch.int64)[1].item())
+
+    def _table(self):
+        def ptr(t):
+            return t.data_ptr() if t is not None else 0
+        return (ptr(self.start), ptr(self.end), ptr(self.id), ptr(self.refs),
+                ptr(self.by_start), self.state.data_ptr(), self.capacity)
+
+    def register(self, addr: torch.Tensor, size: torch.Tensor, grow: bool = True,
+                 stream=None) -> dict:
+        """Returns dict(handle u64[n], kind u8[n], needed)."""
+        n = addr.numel()
+        dev = self.device
+        handle = torch.empty(n, dtype=torch.uint64, device=dev)
+        kind = torch.empty(n, dtype=torch.uint8, device=dev)
+        while True:
+            ws = _workspace(OP_REGISTRY, n, self.capacity, dev, None)
+            rc = lib().dmadesc_reg_register(
+                *self._table(), self.page_shift, _dev(addr, torch.uint64, "addr", n),
+                _dev(size, torch.uint64, "size", n), n, _dev(handle, torch.uint64, "handle", n),
+                _dev(kind, torch.uint8, "kind", n), self._needed.data_ptr(), ws.data_ptr(),
+                ws.numel(), _stream(dev, stream))
+            _check("dmadesc_reg_register", rc)
+            needed = int(self._needed.view(torch.int64)[0].item())
+            if needed <= self.capacity or not grow:
+                return dict(handle=handle, kind=kind, needed=needed)
+            self.grow(needed)
+
+    def deregister(self, handles: torch.Tensor, stream=None) -> torch.Tensor:
+        """Returns status u8[n]."""
+        n = handles.numel()
+        status = torch.empty(n, dtype=torch.uint8, device=self.device)
+        ws = _workspace(OP_REGISTRY, n, self.capacity, self.device, None)
+        rc = lib().dmadesc_reg_deregister(
+            *self._table(), _dev(handles, torch.uint64, "handle", n), n,
+            _dev(status, torch.uint8, "status", n), ws.data_ptr(), ws.numel(),
+            _stream(self.device, stream))
+        _check("dmadesc_reg_deregister", rc)
+        return status
+
+    def records(self):
+        """(start, end, handle, refs) of the live records in start order, and
+        the handles in storage order, as host numpy arrays."""
+        import numpy as np
+        k = self.count()
+        if k == 0:
+            z = np.zeros(0, np.uint64)
+            return (z, z, z, np.zeros(0, np.int64)), z
+        host = {name: getattr(self, name)[:k].cpu().numpy()
+                for name in ("start", "end", "id", "refs", "by_start")}
+        order = host["by_start"].astype(np.int64)
+        return ((host["start"][order], host["end"][order], host["id"][order],
+                 host["refs"][order].astype(np.int64)), host["id"])

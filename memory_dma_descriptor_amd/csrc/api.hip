@@ -65,6 +65,9 @@ size_t dmadesc_workspace_bytes(int op, uint64_t n, uint32_t param)
     case DMADESC_OP_EMIT_SQE:
         if (param == 0 || param > DMADESC_MAX_QUEUES) return 0;
         return dd::ws_emit_sqe(param);
+    case DMADESC_OP_REGISTRY:
+        if (n > DMADESC_REG_MAX_BATCH || param > DMADESC_REG_MAX_CAPACITY) return 0;
+        return dd::ws_registry(n, param);
     default: return 0;
     }
 }
@@ -141,6 +144,38 @@ int dmadesc_emit_sqe(const uint32_t *perm, const uint64_t *qoff, uint32_t nqueue
     dd::SqeArgs a{perm, qoff, nqueues, status, len, slba, prp1, prp2, n, opcode, nsid, lba_shift,
                   ring, depth, free_slots, tail, cursor, placed, req_of_slot, ws};
     return launched(dd::launch_emit_sqe(a, static_cast<hipStream_t>(stream)));
+}
+
+int dmadesc_reg_register(uint64_t *start, uint64_t *end, uint64_t *id, uint32_t *refs,
+                         uint32_t *by_start, uint64_t *state, uint64_t capacity,
+                         uint32_t page_shift, const uint64_t *addr, const uint64_t *size,
+                         uint64_t n, uint64_t *handle, uint8_t *kind, uint64_t *needed,
+                         void *ws, size_t ws_bytes, void *stream)
+{
+    if (page_shift < 12 || page_shift > 30) return -EINVAL;
+    if (n > DMADESC_REG_MAX_BATCH || capacity > DMADESC_REG_MAX_CAPACITY) return -EINVAL;
+    if (!state || !needed) return -EINVAL;
+    if (capacity > 0 && (!start || !end || !id || !refs || !by_start)) return -EINVAL;
+    if (n > 0 && (!addr || !size || !handle || !kind)) return -EINVAL;
+    if (!ws || ws_bytes < dd::ws_registry(n, capacity)) return -EINVAL;
+    dd::RegArgs a{start, end, id, refs, by_start, state, capacity, page_shift, addr, size,
+                  nullptr, n, handle, kind, needed, nullptr, ws};
+    return launched(dd::launch_reg_register(a, static_cast<hipStream_t>(stream)));
+}
+
+int dmadesc_reg_deregister(uint64_t *start, uint64_t *end, uint64_t *id, uint32_t *refs,
+                           uint32_t *by_start, uint64_t *state, uint64_t capacity,
+                           const uint64_t *handle, uint64_t n, uint8_t *status,
+                           void *ws, size_t ws_bytes, void *stream)
+{
+    if (n > DMADESC_REG_MAX_BATCH || capacity > DMADESC_REG_MAX_CAPACITY) return -EINVAL;
+    if (!state) return -EINVAL;
+    if (capacity > 0 && (!start || !end || !id || !refs || !by_start)) return -EINVAL;
+    if (n > 0 && (!handle || !status)) return -EINVAL;
+    if (!ws || ws_bytes < dd::ws_registry(n, capacity)) return -EINVAL;
+    dd::RegArgs a{start, end, id, refs, by_start, state, capacity, 12, nullptr, nullptr,
+                  handle, n, nullptr, nullptr, nullptr, status, ws};
+    return launched(dd::launch_reg_deregister(a, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -59,14 +59,33 @@ struct SqeArgs {
     void *ws;
 };
 
+struct RegArgs {
+    uint64_t *start, *end, *id;
+    uint32_t *refs, *by_start;
+    uint64_t *state;
+    uint64_t capacity;
+    uint32_t page_shift;
+    const uint64_t *addr, *size;      // register
+    const uint64_t *handle_in;        // deregister
+    uint64_t n;
+    uint64_t *handle;                 // register outputs
+    uint8_t *kind;
+    uint64_t *needed;
+    uint8_t *status;                  // deregister output
+    void *ws;
+};
+
 hipError_t launch_mr_lookup(const LookupArgs &a, hipStream_t s);
 hipError_t launch_build_prp(const PrpArgs &a, hipStream_t s);
 hipError_t launch_partition(const SplitArgs &a, hipStream_t s);
 hipError_t launch_emit_sqe(const SqeArgs &a, hipStream_t s);
+hipError_t launch_reg_register(const RegArgs &a, hipStream_t s);
+hipError_t launch_reg_deregister(const RegArgs &a, hipStream_t s);
 
 size_t ws_build_prp(uint64_t n);
 size_t ws_partition(uint64_t n, uint32_t nqueues);
 size_t ws_emit_sqe(uint32_t nqueues);
+size_t ws_registry(uint64_t n, uint64_t capacity);
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 

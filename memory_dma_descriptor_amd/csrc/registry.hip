@@ -1,0 +1,683 @@
+// registry.hip - the registration cache on the device: batches of register
+// and deregister calls applied to a refcounted record table, for gfx950.
+//
+// Method (NCCL GDR/MR course page, "Communicator User Registration Cache" and
+// "IB Backend MR Cache"): a registration widens its range to whole pages; a
+// record that fully contains the widened range gains a reference and its
+// handle is returned, otherwise a new record is inserted in start order; a
+// deregistration drops a reference and frees the record at zero, and a handle
+// no record holds is an error. The record table grows 0 -> 32 -> 64 -> ...
+//
+// A batch means what its calls made one after another mean. In parallel:
+//  * A range that some record of the table before the batch contains hits
+//    the first such record in start order: with PM[p] the running maximum of
+//    the records' ends in start order, that record is the first p with
+//    PM[p] >= end, provided its start is <= the range's start.
+//  * A miss is inserted exactly when no earlier miss of the batch contains
+//    it (an earlier miss either was inserted or was itself contained by an
+//    inserted record, which then contains this one too; an earlier hit's range
+//    lies inside an old record, so it never contains a miss). Every other
+//    range goes to the record that comes first in start order among the old
+//    record it hit (if any) and the earlier inserts that contain it: the
+//    insert with the smallest (start, batch index) wins over the old record
+//    only when its start is strictly smaller, since an insert goes after the
+//    records with the same start. These relations are found by comparing
+//    every pair of the batch in LDS tiles (a batch is at most
+//    DMADESC_REG_MAX_BATCH calls).
+//  * New records get handles next_id + their rank among the batch's inserts,
+//    take storage slots after the live records (storage is in handle order,
+//    so a handle is found by binary search), and are merged into the
+//    start-ordered index behind existing records with the same start.
+//  * A deregistration of a record with r references is stale when r earlier
+//    calls of the batch already named it; live records are compacted stably.
+// A register batch that would leave more records than the capacity applies
+// nothing and reports the capacity the growth rule reaches.
+#include "dd_device.hpp"
+#include "dd_internal.h"
+#include "dmadesc.h"
+
+namespace dd {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / kWave;
+constexpr int kPer = 4;                              // records per thread in scans
+constexpr uint32_t kChunk = kThreads * kPer;         // records per scan block
+constexpr int kTopThreads = 1024;
+constexpr uint32_t kMaxChunks = DMADESC_REG_MAX_CAPACITY / kChunk;   // 16384
+constexpr uint32_t kBatchPer = DMADESC_REG_MAX_BATCH / kTopThreads; // 64
+static_assert(kMaxChunks % kTopThreads == 0, "chunk totals scan in one block");
+
+enum : uint8_t { kInvalid = DMADESC_REG_INVALID, kHit = DMADESC_REG_HIT, kNew = DMADESC_REG_NEW,
+                 kHitNew = DMADESC_REG_HIT_NEW, kNospace = DMADESC_REG_NOSPACE };
+enum : uint8_t { kMiss = 5 };                        // internal class before inserts are known
+
+// Workspace pieces (pointers into the caller's workspace).
+struct RegWs {
+    // per batch item
+    uint64_t *base, *top;
+    uint8_t *cls;           // kInvalid / kHit / kMiss, then kNew / kHitNew
+    uint32_t *hit;          // storage slot of the hit record (kHit)
+    uint64_t *hstart;       // start of the hit record (kHit)
+    uint32_t *rank;         // rank among inserts (kNew)
+    uint32_t *brank;        // rank of an insert in (start, batch index) order
+    uint32_t *owner;        // batch index of the containing insert (kHitNew)
+    uint32_t *newrefs;      // references of each insert, by rank
+    uint64_t *newbase;      // start of each insert, by brank
+    // per record (capacity)
+    uint64_t *sstart;       // starts in start order
+    uint64_t *pm;           // running maximum of ends in start order
+    uint32_t *merged;       // next start-ordered index / kept flags
+    uint32_t *newslot;      // storage slot after compaction
+    uint64_t *tmp64a, *tmp64b, *tmp64c;
+    uint32_t *tmp32;
+    // per scan chunk
+    uint64_t *chunk;        // chunk totals, then exclusive prefixes
+    // scalars: [0] inserts, [1] fits, [2] live count after deregistration
+    uint64_t *scal;
+};
+
+struct RegState {
+    uint64_t *start, *end, *id;
+    uint32_t *refs, *by_start;
+    uint64_t *state;        // [0] live records, [1] next handle
+    uint64_t capacity;
+};
+
+// ---------------------------------------------------------------- scans ---
+
+template <bool kMax>
+__device__ __forceinline__ uint64_t combine(uint64_t a, uint64_t b)
+{
+    return kMax ? (a > b ? a : b) : a + b;
+}
+
+template <bool kMax, int kT>
+__device__ __forceinline__ uint64_t block_excl(uint64_t v, uint64_t *scr, uint64_t *total)
+{
+    constexpr int kW = kT / kWave;
+    uint64_t inc = v;
+    const int ln = lane();
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+        const uint64_t u = __shfl_up(inc, (unsigned)d, kWave);
+        if (ln >= d) inc = combine<kMax>(inc, u);
+    }
+    const int w = wave();
+    if (ln == kWave - 1) scr[w] = inc;
+    __syncthreads();
+    uint64_t before = 0, all = 0;
+#pragma unroll
+    for (int k = 0; k < kW; ++k) {
+        const uint64_t s = scr[k];
+        if (k < w) before = combine<kMax>(before, s);
+        all = combine<kMax>(all, s);
+    }
+    __syncthreads();
+    *total = all;
+    // exclusive: the wave-exclusive value combined with the earlier waves'
+    const uint64_t wex = __shfl_up(inc, 1u, kWave);
+    return combine<kMax>(before, ln ? wex : 0ull);
+}
+
+// Values of the records in start order, for the running maximum of ends.
+struct EndsInOrder {
+    const uint64_t *end;
+    const uint32_t *by_start;
+    __device__ uint64_t operator()(uint64_t p) const { return end[by_start[p]]; }
+};
+// Kept flags (refs > 0) of storage slots, for the compaction.
+struct KeptSlots {
+    const uint32_t *refs;
+    __device__ uint64_t operator()(uint64_t p) const { return refs[p] != 0; }
+};
+// Kept flags of the start-ordered index.
+struct KeptInOrder {
+    const uint32_t *refs;
+    const uint32_t *by_start;
+    __device__ uint64_t operator()(uint64_t p) const { return refs[by_start[p]] != 0; }
+};
+
+// Pass 1: per-chunk totals of f(p) for p < count.
+template <bool kMax, class F>
+__global__ __launch_bounds__(kThreads) void k_scan_chunks(F f, const uint64_t *state,
+                                                          uint64_t *chunk)
+{
+    __shared__ uint64_t scr[kWaves];
+    const uint64_t count = state[0];
+    const uint64_t p0 = (uint64_t)blockIdx.x * kChunk;
+    if (p0 >= count) return;                         // uniform over the block
+    uint64_t v = 0;
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+        const uint64_t p = p0 + (uint64_t)threadIdx.x * kPer + k;
+        if (p < count) v = combine<kMax>(v, f(p));
+    }
+    uint64_t tot;
+    block_excl<kMax, kThreads>(v, scr, &tot);
+    if (threadIdx.x == 0) chunk[blockIdx.x] = tot;
+}
+
+// Pass 2: one block turns the chunk totals into exclusive prefixes; the grand
+// total goes to *total.
+template <bool kMax>
+__global__ __launch_bounds__(kTopThreads) void k_scan_top(const uint64_t *state, uint64_t *chunk,
+                                                          uint64_t *total)
+{
+    __shared__ uint64_t scr[kTopThreads / kWave];
+    const uint64_t count = state[0];
+    const uint32_t nch = (uint32_t)((count + kChunk - 1) / kChunk);
+    constexpr uint32_t kEach = kMaxChunks / kTopThreads;
+    uint64_t v[kEach], s = 0;
+#pragma unroll
+    for (uint32_t k = 0; k < kEach; ++k) {
+        const uint32_t c = threadIdx.x * kEach + k;
+        v[k] = c < nch ? chunk[c] : 0;
+        s = combine<kMax>(s, v[k]);
+    }
+    uint64_t tot;
+    uint64_t run = block_excl<kMax, kTopThreads>(s, scr, &tot);
+#pragma unroll
+    for (uint32_t k = 0; k < kEach; ++k) {
+        const uint32_t c = threadIdx.x * kEach + k;
+        if (c < nch) chunk[c] = run;
+        run = combine<kMax>(run, v[k]);
+    }
+    if (threadIdx.x == 0 && total) *total = count ? tot : 0;
+}
+
+// Pass 3: out[p] = prefix of f over records before p (exclusive) or up to p
+// (inclusive).
+template <bool kMax, bool kIncl, class F>
+__global__ __launch_bounds__(kThreads) void k_scan_apply(F f, const uint64_t *state,
+                                                         const uint64_t *chunk, uint64_t *out)
+{
+    __shared__ uint64_t scr[kWaves];
+    const uint64_t count = state[0];
+    const uint64_t p0 = (uint64_t)blockIdx.x * kChunk;
+    if (p0 >= count) return;
+    uint64_t v[kPer], s = 0;
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+        const uint64_t p = p0 + (uint64_t)threadIdx.x * kPer + k;
+        v[k] = p < count ? f(p) : 0;
+        s = combine<kMax>(s, v[k]);
+    }
+    uint64_t tot;
+    uint64_t run = combine<kMax>(chunk[blockIdx.x], block_excl<kMax, kThreads>(s, scr, &tot));
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+        const uint64_t p = p0 + (uint64_t)threadIdx.x * kPer + k;
+        const uint64_t nxt = combine<kMax>(run, v[k]);
+        if (p < count) out[p] = kIncl ? nxt : run;
+        run = nxt;
+    }
+}
+
+template <bool kMax, bool kIncl, class F>
+void scan_records(F f, const uint64_t *state, uint64_t capacity, uint64_t *chunk, uint64_t *out,
+                  uint64_t *total, hipStream_t s)
+{
+    const unsigned nb = (unsigned)((capacity + kChunk - 1) / kChunk);
+    if (nb == 0) return;
+    hipLaunchKernelGGL((k_scan_chunks<kMax, F>), dim3(nb), dim3(kThreads), 0, s, f, state, chunk);
+    hipLaunchKernelGGL((k_scan_top<kMax>), dim3(1), dim3(kTopThreads), 0, s, state, chunk, total);
+    hipLaunchKernelGGL((k_scan_apply<kMax, kIncl, F>), dim3(nb), dim3(kThreads), 0, s, f, state,
+                       chunk, out);
+}
+
+// ------------------------------------------------------------- register ---
+
+__global__ __launch_bounds__(kThreads) void k_reg_starts(RegState g, RegWs w)
+{
+    const uint64_t count = g.state[0];
+    for (uint64_t p = (uint64_t)blockIdx.x * kThreads + threadIdx.x; p < count;
+         p += (uint64_t)gridDim.x * kThreads)
+        w.sstart[p] = g.start[g.by_start[p]];
+}
+
+// Rounding and the lookup in the table as it was before the batch.
+__global__ __launch_bounds__(kThreads) void k_reg_classify(RegState g, RegWs w, uint32_t shift,
+                                                           const uint64_t *addr, const uint64_t *size,
+                                                           uint32_t n)
+{
+    const uint32_t i = blockIdx.x * kThreads + threadIdx.x;
+    if (i >= n) return;
+    const uint64_t count = g.state[0];
+    const uint64_t a = addr[i], l = size[i];
+    const uint64_t page = 1ull << shift;
+    uint8_t c = kMiss;
+    uint64_t base = 0, top = 0;
+    if (l == 0 || l > ~a) {
+        c = kInvalid;
+    } else {
+        base = a & ~(page - 1);
+        const uint64_t last = a + l - 1;                  // no wrap: l <= ~a
+        const uint64_t lastp = last & ~(page - 1);
+        if (lastp > ~0ull - page) c = kInvalid;           // the rounded end would wrap
+        else top = lastp + page;
+    }
+    uint32_t hit = 0;
+    uint64_t hstart = 0;
+    if (c == kMiss && count) {
+        // First p with pm[p] >= top (pm is non-decreasing).
+        uint64_t lo = 0, hi = count;
+        while (lo < hi) {
+            const uint64_t mid = (lo + hi) >> 1;
+            if (w.pm[mid] >= top) hi = mid;
+            else lo = mid + 1;
+        }
+        if (lo < count && w.sstart[lo] <= base) {
+            c = kHit;
+            hit = g.by_start[lo];
+            hstart = w.sstart[lo];
+        }
+    }
+    w.hstart[i] = hstart;
+    w.base[i] = base;
+    w.top[i] = top;
+    w.cls[i] = c;
+    w.hit[i] = hit;
+}
+
+// inserted(i) = miss and no earlier miss contains it. Items i of this block
+// against every earlier item j, 256 at a time in LDS.
+__global__ __launch_bounds__(kThreads) void k_reg_inserted(RegWs w, uint32_t n)
+{
+    __shared__ uint64_t s_base[kThreads], s_top[kThreads];
+    __shared__ uint8_t s_miss[kThreads];
+    const uint32_t i = blockIdx.x * kThreads + threadIdx.x;
+    const bool me = i < n && w.cls[i] == kMiss;
+    const uint64_t b = me ? w.base[i] : 0, t = me ? w.top[i] : 0;
+    bool inside = false;
+    const uint32_t jend = blockIdx.x * kThreads + kThreads;   // j < i <= this bound
+    for (uint32_t j0 = 0; j0 < jend; j0 += kThreads) {
+        if (__syncthreads_or(me && !inside) == 0) break;  // every item here is decided
+        const uint32_t j = j0 + threadIdx.x;
+        // Other blocks mark their inserts kNew while this loop runs: a miss
+        // reads as kMiss or kNew, both mean "a miss of the old table".
+        const uint8_t cj = j < n ? w.cls[j] : kInvalid;
+        const bool jm = cj == kMiss || cj == kNew;
+        s_base[threadIdx.x] = jm ? w.base[j] : 0;
+        s_top[threadIdx.x] = jm ? w.top[j] : 0;
+        s_miss[threadIdx.x] = jm;
+        if (__syncthreads_or(jm) == 0) continue;         // no miss in this tile
+        if (me && !inside) {
+            const uint32_t lim = i - j0 < kThreads ? i - j0 : kThreads;   // j < i
+            for (uint32_t k = 0; k < lim; ++k)
+                if (s_miss[k] && s_base[k] <= b && t <= s_top[k]) {
+                    inside = true;
+                    break;
+                }
+        }
+        __syncthreads();
+    }
+    if (me && !inside) w.cls[i] = kNew;
+}
+
+// One block: ranks of the inserts in batch order, their count, and whether
+// the table has room; the needed capacity is reported either way.
+__global__ __launch_bounds__(kTopThreads) void k_reg_count(RegState g, RegWs w, uint32_t n,
+                                                           uint64_t *needed)
+{
+    __shared__ uint64_t scr[kTopThreads / kWave];
+    uint64_t s = 0;
+    for (uint32_t k = 0; k < kBatchPer; ++k) {
+        const uint32_t i = threadIdx.x * kBatchPer + k;
+        s += (i < n && w.cls[i] == kNew) ? 1u : 0u;
+    }
+    uint64_t tot;
+    uint64_t run = block_excl<false, kTopThreads>(s, scr, &tot);
+    for (uint32_t k = 0; k < kBatchPer; ++k) {
+        const uint32_t i = threadIdx.x * kBatchPer + k;
+        if (i < n) {
+            w.rank[i] = (uint32_t)run;
+            w.newrefs[i] = 1;                            // by rank; ranks < n
+            run += w.cls[i] == kNew;
+        }
+    }
+    if (threadIdx.x == 0) {
+        const uint64_t after = g.state[0] + tot;
+        uint64_t need = g.capacity;
+        while (need < after) need = need == 0 ? 32 : 2 * need;
+        *needed = need;
+        w.scal[0] = tot;
+        w.scal[1] = after <= g.capacity;
+    }
+}
+
+// For every range that is not inserted, the earlier insert with the smallest
+// (start, index) that contains it decides between that insert and the old
+// record it hit; and the (start, index) rank of each insert.
+__global__ __launch_bounds__(kThreads) void k_reg_owner(RegWs w, uint32_t n)
+{
+    __shared__ uint64_t s_base[kThreads], s_top[kThreads];
+    __shared__ uint8_t s_new[kThreads];
+    const uint32_t i = blockIdx.x * kThreads + threadIdx.x;
+    const uint8_t c = i < n ? w.cls[i] : kInvalid;
+    const bool look = c == kMiss || c == kHit;           // looks for a containing insert
+    const uint64_t b = look || c == kNew ? w.base[i] : 0;
+    const uint64_t t = look || c == kNew ? w.top[i] : 0;
+    uint32_t best = UINT32_MAX, brank = 0;
+    uint64_t bbase = 0;
+    const bool any = __syncthreads_or(look || c == kNew) != 0;
+    if (!any) return;                                    // uniform over the block
+    for (uint32_t j0 = 0; j0 < n; j0 += kThreads) {
+        const uint32_t j = j0 + threadIdx.x;
+        const bool jn = j < n && w.cls[j] == kNew;
+        s_base[threadIdx.x] = jn ? w.base[j] : 0;
+        s_top[threadIdx.x] = jn ? w.top[j] : 0;
+        s_new[threadIdx.x] = jn;
+        if (__syncthreads_or(jn) == 0) continue;         // no insert in this tile
+        const uint32_t lim = n - j0 < kThreads ? n - j0 : kThreads;
+        if (look) {
+            const uint32_t jl = i > j0 ? (i - j0 < lim ? i - j0 : lim) : 0;   // j < i
+            for (uint32_t k = 0; k < jl; ++k)
+                if (s_new[k] && s_base[k] <= b && t <= s_top[k] &&
+                    (best == UINT32_MAX || s_base[k] < bbase)) {
+                    best = j0 + k;
+                    bbase = s_base[k];
+                }
+        } else if (c == kNew) {
+            for (uint32_t k = 0; k < lim; ++k)
+                brank += s_new[k] && (s_base[k] < b || (s_base[k] == b && j0 + k < i));
+        }
+        __syncthreads();
+    }
+    if (c == kMiss || (c == kHit && best != UINT32_MAX && bbase < w.hstart[i])) {
+        w.owner[i] = best;                               // a miss always finds one
+        w.cls[i] = kHitNew;
+    } else if (c == kNew) {
+        w.brank[i] = brank;
+    }
+}
+
+// Handles, kinds and reference counts (or NOSPACE for every item).
+__global__ __launch_bounds__(kThreads) void k_reg_apply(RegState g, RegWs w, uint32_t n,
+                                                        uint64_t *handle, uint8_t *kind)
+{
+    const uint32_t i = blockIdx.x * kThreads + threadIdx.x;
+    if (i >= n) return;
+    const uint8_t c = w.cls[i];
+    if (!w.scal[1]) {
+        handle[i] = 0;
+        kind[i] = kNospace;
+        return;
+    }
+    const uint64_t next = g.state[1];
+    uint64_t h = 0;
+    if (c == kHit) {
+        h = g.id[w.hit[i]];
+        atomicAdd(&g.refs[w.hit[i]], 1u);
+    } else if (c == kNew) {
+        h = next + w.rank[i];
+        w.newbase[w.brank[i]] = w.base[i];
+    } else if (c == kHitNew) {
+        const uint32_t o = w.owner[i];
+        h = next + w.rank[o];
+        atomicAdd(&w.newrefs[w.rank[o]], 1u);
+    }
+    handle[i] = h;
+    kind[i] = c;
+}
+
+// New records in storage after the live ones, and the merged start order.
+__global__ __launch_bounds__(kThreads) void k_reg_insert(RegState g, RegWs w, uint32_t n)
+{
+    if (!w.scal[1]) return;
+    const uint64_t count = g.state[0], T = w.scal[0], next = g.state[1];
+    const uint64_t tid = (uint64_t)blockIdx.x * kThreads + threadIdx.x;
+    const uint64_t stride = (uint64_t)gridDim.x * kThreads;
+    // Existing records: shift by the inserts that start strictly before.
+    for (uint64_t p = tid; p < count; p += stride) {
+        const uint64_t st = w.sstart[p];
+        uint64_t lo = 0, hi = T;                         // inserts with start < st
+        while (lo < hi) {
+            const uint64_t mid = (lo + hi) >> 1;
+            if (w.newbase[mid] < st) lo = mid + 1;
+            else hi = mid;
+        }
+        w.merged[p + lo] = g.by_start[p];
+    }
+    // Inserts: after the existing records that start at or before them.
+    for (uint64_t i = tid; i < n; i += stride) {
+        if (w.cls[i] != kNew) continue;
+        const uint64_t b = w.base[i];
+        uint64_t lo = 0, hi = count;                     // existing with start <= b
+        while (lo < hi) {
+            const uint64_t mid = (lo + hi) >> 1;
+            if (w.sstart[mid] <= b) lo = mid + 1;
+            else hi = mid;
+        }
+        const uint64_t slot = count + w.rank[i];
+        w.merged[w.brank[i] + lo] = (uint32_t)slot;
+        g.start[slot] = b;
+        g.end[slot] = w.top[i];
+        g.id[slot] = next + w.rank[i];
+        g.refs[slot] = w.newrefs[w.rank[i]];
+    }
+}
+
+__global__ __launch_bounds__(kThreads) void k_reg_commit(RegState g, RegWs w)
+{
+    if (!w.scal[1]) return;
+    const uint64_t count = g.state[0] + w.scal[0];
+    for (uint64_t p = (uint64_t)blockIdx.x * kThreads + threadIdx.x; p < count;
+         p += (uint64_t)gridDim.x * kThreads)
+        g.by_start[p] = w.merged[p];
+}
+
+__global__ void k_reg_state(RegState g, RegWs w)
+{
+    if (threadIdx.x == 0 && w.scal[1]) {
+        g.state[0] += w.scal[0];
+        g.state[1] += w.scal[0];
+    }
+}
+
+// ----------------------------------------------------------- deregister ---
+
+__global__ __launch_bounds__(kThreads) void k_dereg_find(RegState g, RegWs w, const uint64_t *h,
+                                                         uint32_t n)
+{
+    const uint32_t i = blockIdx.x * kThreads + threadIdx.x;
+    if (i >= n) return;
+    const uint64_t count = g.state[0], key = h[i];
+    uint64_t lo = 0, hi = count;                         // storage is in handle order
+    while (lo < hi) {
+        const uint64_t mid = (lo + hi) >> 1;
+        if (g.id[mid] < key) lo = mid + 1;
+        else hi = mid;
+    }
+    w.hit[i] = (lo < count && g.id[lo] == key) ? (uint32_t)lo : UINT32_MAX;
+}
+
+// Calls before i naming the same record decide whether call i succeeds.
+__global__ __launch_bounds__(kThreads) void k_dereg_status(RegState g, RegWs w, uint32_t n,
+                                                           uint8_t *status)
+{
+    __shared__ uint32_t s_slot[kThreads];
+    const uint32_t i = blockIdx.x * kThreads + threadIdx.x;
+    const uint32_t me = i < n ? w.hit[i] : UINT32_MAX;
+    uint32_t before = 0;
+    const uint32_t jend = blockIdx.x * kThreads + kThreads;
+    for (uint32_t j0 = 0; j0 < jend; j0 += kThreads) {
+        const uint32_t j = j0 + threadIdx.x;
+        s_slot[threadIdx.x] = j < n ? w.hit[j] : UINT32_MAX;
+        __syncthreads();
+        if (me != UINT32_MAX) {
+            const uint32_t lim = i > j0 ? (i - j0 < kThreads ? i - j0 : kThreads) : 0;
+            for (uint32_t k = 0; k < lim; ++k) before += s_slot[k] == me;
+        }
+        __syncthreads();
+    }
+    if (i >= n) return;
+    uint8_t st = DMADESC_DEREG_STALE;
+    if (me != UINT32_MAX) {
+        const uint32_t r = g.refs[me];
+        if (before + 1 < r) st = DMADESC_DEREG_OK;
+        else if (before + 1 == r) st = DMADESC_DEREG_REMOVED;
+    }
+    status[i] = st;
+    w.cls[i] = st;
+}
+
+__global__ __launch_bounds__(kThreads) void k_dereg_drop(RegState g, RegWs w, uint32_t n)
+{
+    const uint32_t i = blockIdx.x * kThreads + threadIdx.x;
+    if (i < n && w.cls[i] != DMADESC_DEREG_STALE) atomicSub(&g.refs[w.hit[i]], 1u);
+}
+
+// Stable compaction: kept storage slots move to their exclusive prefix, and
+// the start-ordered index keeps its kept entries, renamed to the new slots.
+__global__ __launch_bounds__(kThreads) void k_dereg_gather(RegState g, RegWs w)
+{
+    const uint64_t count = g.state[0];
+    for (uint64_t p = (uint64_t)blockIdx.x * kThreads + threadIdx.x; p < count;
+         p += (uint64_t)gridDim.x * kThreads) {
+        w.tmp64a[p] = g.start[p];
+        w.tmp64b[p] = g.end[p];
+        w.tmp64c[p] = g.id[p];
+        w.tmp32[p] = g.refs[p];
+        w.merged[p] = g.by_start[p];
+    }
+}
+
+__global__ __launch_bounds__(kThreads) void k_dereg_scatter(RegState g, RegWs w,
+                                                            const uint64_t *slot_pre,
+                                                            const uint64_t *order_pre)
+{
+    const uint64_t count = g.state[0];
+    for (uint64_t p = (uint64_t)blockIdx.x * kThreads + threadIdx.x; p < count;
+         p += (uint64_t)gridDim.x * kThreads) {
+        if (w.tmp32[p] != 0) {
+            const uint64_t q = slot_pre[p];
+            g.start[q] = w.tmp64a[p];
+            g.end[q] = w.tmp64b[p];
+            g.id[q] = w.tmp64c[p];
+            g.refs[q] = w.tmp32[p];
+        }
+        const uint32_t s = w.merged[p];
+        if (w.tmp32[s] != 0) g.by_start[order_pre[p]] = (uint32_t)slot_pre[s];
+    }
+}
+
+__global__ void k_dereg_state(RegState g, RegWs w)
+{
+    if (threadIdx.x == 0) g.state[0] = w.scal[2];
+}
+
+// ------------------------------------------------------------ workspace ---
+
+struct Carver {
+    char *p;
+    template <typename T>
+    T *take(uint64_t count)
+    {
+        T *r = reinterpret_cast<T *>(p);
+        p += align256(count * sizeof(T));
+        return r;
+    }
+};
+
+RegWs carve(void *ws, uint64_t n, uint64_t cap)
+{
+    Carver c{static_cast<char *>(ws)};
+    RegWs w;
+    w.base = c.take<uint64_t>(n);
+    w.top = c.take<uint64_t>(n);
+    w.cls = c.take<uint8_t>(n);
+    w.hit = c.take<uint32_t>(n);
+    w.hstart = c.take<uint64_t>(n);
+    w.rank = c.take<uint32_t>(n);
+    w.brank = c.take<uint32_t>(n);
+    w.owner = c.take<uint32_t>(n);
+    w.newrefs = c.take<uint32_t>(n);
+    w.newbase = c.take<uint64_t>(n);
+    w.sstart = c.take<uint64_t>(cap);
+    w.pm = c.take<uint64_t>(cap);
+    w.merged = c.take<uint32_t>(cap + n);
+    w.newslot = c.take<uint32_t>(cap);
+    w.tmp64a = c.take<uint64_t>(cap);
+    w.tmp64b = c.take<uint64_t>(cap);
+    w.tmp64c = c.take<uint64_t>(cap);
+    w.tmp32 = c.take<uint32_t>(cap);
+    w.chunk = c.take<uint64_t>(kMaxChunks);
+    w.scal = c.take<uint64_t>(4);
+    return w;
+}
+
+uint64_t carve_bytes(uint64_t n, uint64_t cap)
+{
+    return 10 * align256(n * 8) + 4 * align256(cap * 8) + 3 * align256(cap * 4) +
+           align256((cap + n) * 4) + align256((uint64_t)kMaxChunks * 8) + 256;
+}
+
+}  // namespace
+
+size_t ws_registry(uint64_t n, uint64_t capacity)
+{
+    return carve_bytes(n < 1 ? 1 : n, capacity < 1 ? 1 : capacity);
+}
+
+hipError_t launch_reg_register(const RegArgs &a, hipStream_t s)
+{
+    const uint64_t cap = a.capacity;
+    RegState g{a.start, a.end, a.id, a.refs, a.by_start, a.state, cap};
+    RegWs w = carve(a.ws, a.n < 1 ? 1 : a.n, cap < 1 ? 1 : cap);
+    const uint32_t n = (uint32_t)a.n;
+    const unsigned nb = (n + kThreads - 1) / kThreads;
+    const unsigned rb = (unsigned)((cap + kThreads - 1) / kThreads < 4096 ? (cap + kThreads - 1) / kThreads : 4096);
+    if (rb) {
+        hipLaunchKernelGGL(k_reg_starts, dim3(rb), dim3(kThreads), 0, s, g, w);
+        scan_records<true, true>(EndsInOrder{a.end, a.by_start}, a.state, cap, w.chunk, w.pm,
+                                 nullptr, s);
+    }
+    if (nb) {
+        hipLaunchKernelGGL(k_reg_classify, dim3(nb), dim3(kThreads), 0, s, g, w, a.page_shift,
+                           a.addr, a.size, n);
+        hipLaunchKernelGGL(k_reg_inserted, dim3(nb), dim3(kThreads), 0, s, w, n);
+    }
+    hipLaunchKernelGGL(k_reg_count, dim3(1), dim3(kTopThreads), 0, s, g, w, n, a.needed);
+    if (nb) {
+        hipLaunchKernelGGL(k_reg_owner, dim3(nb), dim3(kThreads), 0, s, w, n);
+        hipLaunchKernelGGL(k_reg_apply, dim3(nb), dim3(kThreads), 0, s, g, w, n, a.handle,
+                           a.kind);
+        const unsigned ib = (unsigned)((cap + n + kThreads - 1) / kThreads < 4096
+                                           ? (cap + n + kThreads - 1) / kThreads : 4096);
+        hipLaunchKernelGGL(k_reg_insert, dim3(ib), dim3(kThreads), 0, s, g, w, n);
+        hipLaunchKernelGGL(k_reg_commit, dim3(ib), dim3(kThreads), 0, s, g, w);
+        hipLaunchKernelGGL(k_reg_state, dim3(1), dim3(64), 0, s, g, w);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_reg_deregister(const RegArgs &a, hipStream_t s)
+{
+    const uint64_t cap = a.capacity;
+    RegState g{a.start, a.end, a.id, a.refs, a.by_start, a.state, cap};
+    RegWs w = carve(a.ws, a.n < 1 ? 1 : a.n, cap < 1 ? 1 : cap);
+    const uint32_t n = (uint32_t)a.n;
+    const unsigned nb = (n + kThreads - 1) / kThreads;
+    if (nb == 0 || cap == 0) {
+        if (nb) {                                        // nothing is live: all stale
+            hipLaunchKernelGGL(k_dereg_find, dim3(nb), dim3(kThreads), 0, s, g, w, a.handle_in, n);
+            hipLaunchKernelGGL(k_dereg_status, dim3(nb), dim3(kThreads), 0, s, g, w, n, a.status);
+        }
+        return hipGetLastError();
+    }
+    const unsigned rb = (unsigned)((cap + kThreads - 1) / kThreads < 4096 ? (cap + kThreads - 1) / kThreads : 4096);
+    hipLaunchKernelGGL(k_dereg_find, dim3(nb), dim3(kThreads), 0, s, g, w, a.handle_in, n);
+    hipLaunchKernelGGL(k_dereg_status, dim3(nb), dim3(kThreads), 0, s, g, w, n, a.status);
+    hipLaunchKernelGGL(k_dereg_drop, dim3(nb), dim3(kThreads), 0, s, g, w, n);
+    // Prefixes of kept slots (storage) and kept entries (start order).
+    scan_records<false, false>(KeptSlots{a.refs}, a.state, cap, w.chunk, w.pm, &w.scal[2], s);
+    scan_records<false, false>(KeptInOrder{a.refs, a.by_start}, a.state, cap, w.chunk, w.sstart,
+                               nullptr, s);
+    hipLaunchKernelGGL(k_dereg_gather, dim3(rb), dim3(kThreads), 0, s, g, w);
+    hipLaunchKernelGGL(k_dereg_scatter, dim3(rb), dim3(kThreads), 0, s, g, w, w.pm, w.sstart);
+    hipLaunchKernelGGL(k_dereg_state, dim3(1), dim3(64), 0, s, g, w);
+    return hipGetLastError();
+}
+
+}  // namespace dd

@@ -26,7 +26,7 @@ def _declared():
 def test_exports_every_declared_symbol():
     names = _declared()
     assert {"dmadesc_mr_lookup", "dmadesc_build_prp", "dmadesc_partition_by_queue",
-            "dmadesc_emit_sqe"} <= names
+            "dmadesc_emit_sqe", "dmadesc_reg_register", "dmadesc_reg_deregister"} <= names
     lib = ctypes.CDLL(dd.LIB_PATH)
     for n in sorted(names):
         assert hasattr(lib, n), n
@@ -132,6 +132,32 @@ def test_emit_sqe_rejects_bad_arguments():
         args = list(ok)
         args[k] = bad
         assert f(*args) == EINVAL, (k, bad)
+
+
+@no_gpu_only
+def test_registry_rejects_bad_arguments():
+    f = dd.lib().dmadesc_reg_register
+    ok = [P, P, P, P, P, P, 64, 12, P, P, 8, P, P, P, P, 1 << 30, NULL]
+    for k, bad in [(7, 11), (7, 31), (10, 65537), (6, (1 << 24) + 1), (5, NULL), (13, NULL),
+                   (0, NULL), (4, NULL), (8, NULL), (11, NULL), (12, NULL), (14, NULL),
+                   (15, 16)]:
+        args = list(ok)
+        args[k] = bad
+        assert f(*args) == EINVAL, (k, bad)
+    g = dd.lib().dmadesc_reg_deregister
+    ok = [P, P, P, P, P, P, 64, P, 8, P, P, 1 << 30, NULL]
+    for k, bad in [(8, 65537), (6, (1 << 24) + 1), (5, NULL), (0, NULL), (7, NULL), (9, NULL),
+                   (10, NULL), (11, 16)]:
+        args = list(ok)
+        args[k] = bad
+        assert g(*args) == EINVAL, (k, bad)
+
+
+def test_registry_workspace_sizes():
+    ws = dd.workspace_bytes
+    assert ws(dd.OP_REGISTRY, 65537, 64) == 0 and ws(dd.OP_REGISTRY, 1, (1 << 24) + 1) == 0
+    a, b, c = ws(dd.OP_REGISTRY, 1, 64), ws(dd.OP_REGISTRY, 65536, 64), ws(dd.OP_REGISTRY, 1, 1 << 20)
+    assert 0 < a < b and a < c and all(x % 256 == 0 for x in (a, b, c))
 
 
 def test_empty_lookup_is_a_no_op():

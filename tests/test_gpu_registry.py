@@ -1,0 +1,154 @@
+"""GPU parity of the device registration cache (dmadesc_reg_register /
+dmadesc_reg_deregister) with the oracle's O4b: every handle, kind and status,
+the needed capacity, and the whole record table (start, end, handle,
+references, in start order; storage in handle order) after every batch."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import memory_dma_descriptor_amd as dd
+import oracle
+from tests import gpu_cases as gc
+
+pytestmark = pytest.mark.gpu
+
+M = 1 << 20
+
+
+def _compare_tables(dev_reg, ref, ctx):
+    (s, e, h, r), storage = dev_reg.records()
+    ws, we, wh, wr = ref.records()
+    for name, got, want in (("start", s, ws), ("end", e, we), ("handle", h, wh), ("refs", r, wr)):
+        if not np.array_equal(np.asarray(got, np.int64), np.asarray(want, np.int64)):
+            raise AssertionError(f"{ctx}: table column {name} differs "
+                                 f"({len(got)} vs {len(want)} records)")
+    assert (np.diff(storage.astype(np.int64)) > 0).all(), f"{ctx}: storage not in handle order"
+    assert dev_reg.next_id() == ref.next_id(), ctx
+
+
+class Pair:
+    """The device registry and the oracle registry, driven together."""
+
+    def __init__(self, page_shift=12, capacity=0):
+        self.dev = dd.DeviceRegistry(capacity, page_shift)
+        self.ref = oracle.Registry(page_shift)
+        self.cap = capacity
+
+    def register(self, addr, size, ctx, grow=True):
+        gc.say(f"registry register {ctx}: n={len(addr)} cap={self.dev.capacity}")
+        out = self.dev.register(gc.dev(np.asarray(addr, np.uint64)),
+                                gc.dev(np.asarray(size, np.uint64)), grow=grow)
+        torch.cuda.synchronize()
+        h, k, need = self.ref.register_batch(addr, size, self.dev.capacity if grow else self.cap)
+        if grow:
+            # The device call grew the table as often as the oracle's rule says;
+            # replay the oracle against the final capacity.
+            assert need <= self.dev.capacity
+        np.testing.assert_array_equal(gc.host(out["kind"]), k, err_msg=f"{ctx} kind")
+        np.testing.assert_array_equal(gc.host(out["handle"]), h, err_msg=f"{ctx} handle")
+        assert out["needed"] == need or grow, (ctx, out["needed"], need)
+        _compare_tables(self.dev, self.ref, ctx)
+        return h, k
+
+    def deregister(self, handles, ctx):
+        gc.say(f"registry deregister {ctx}: n={len(handles)}")
+        st = self.dev.deregister(gc.dev(np.asarray(handles, np.uint64)))
+        torch.cuda.synchronize()
+        want = self.ref.deregister_batch(handles)
+        np.testing.assert_array_equal(gc.host(st), want, err_msg=f"{ctx} status")
+        _compare_tables(self.dev, self.ref, ctx)
+
+
+def test_register_experiment_as_batches():
+    base = 0x7f00_0000_0000
+    p = Pair()
+    h, _ = p.register([base, base, base + 0x1000, base + 4 * M], [2 * M, 2 * M, M, 2 * M],
+                      "experiment")
+    assert p.dev.capacity == 32
+    p.deregister([h[0]] * 4, "experiment deregister")
+    p.deregister([h[0], 0, h[3], h[3]], "stale and repeated")
+    assert p.dev.count() == 0
+
+
+def test_capacity_grows_0_32_64_128_256():
+    p = Pair()
+    caps = []
+    for i in range(0, 160, 20):
+        p.register(np.arange(i, i + 20, dtype=np.uint64) * np.uint64(8 * M),
+                   np.full(20, M, np.uint64), f"grow {i}")
+        caps.append(p.dev.capacity)
+    assert caps == [32, 64, 64, 128, 128, 128, 256, 256]
+
+
+def test_refused_batch_changes_nothing():
+    p = Pair(capacity=4)
+    p.register([0, 16 * M], [M, M], "fill")
+    p.cap = 4
+    out = p.dev.register(gc.dev(np.array([32 * M, 48 * M, 64 * M], np.uint64)),
+                         gc.dev(np.full(3, M, np.uint64)), grow=False)
+    torch.cuda.synchronize()
+    h, k, need = p.ref.register_batch([32 * M, 48 * M, 64 * M], [M, M, M], 4)
+    assert out["needed"] == need == 8
+    np.testing.assert_array_equal(gc.host(out["kind"]), k)
+    assert (k == oracle.REG_NOSPACE).all() and (gc.host(out["handle"]) == 0).all()
+    _compare_tables(p.dev, p.ref, "refused")
+
+
+@pytest.mark.parametrize("page_shift", [12, 16])
+def test_invalid_and_rounding(page_shift):
+    p = Pair(page_shift)
+    top = (1 << 64) - 1
+    p.register([0, 5, 4095, top - 100, top - (1 << page_shift) + 1, 1 << 40, (1 << 40) + 1],
+               [0, 1, 2, 50, 1, 1 << page_shift, 3], f"edges shift={page_shift}")
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_random_batches(seed):
+    rng = np.random.default_rng(seed)
+    p = Pair()
+    live = []
+    for rnd in range(30):
+        n = int(rng.choice([1, 7, 255, 256, 257, 1000, 3000]))
+        if rng.random() < 0.6 or not live:
+            starts = rng.integers(0, 512, n).astype(np.uint64) * np.uint64(64 * 1024) + \
+                rng.integers(0, 4096, n).astype(np.uint64)
+            sizes = rng.choice([0, 1, 4096, 100_000, M, 3 * M, 9 * M], n).astype(np.uint64)
+            if rnd % 5 == 0:                            # repeats of earlier items
+                starts[n // 2:] = starts[:n - n // 2]
+                sizes[n // 2:] = sizes[:n - n // 2]
+            h, k = p.register(starts, sizes, f"seed {seed} round {rnd}")
+        else:
+            hs = rng.choice(live + [0, 10 ** 9], n).astype(np.uint64)
+            p.deregister(hs, f"seed {seed} round {rnd}")
+        (_, _, hh, _), _ = p.dev.records()
+        live = [int(x) for x in hh]
+
+
+def test_full_batch_on_a_large_table():
+    rng = np.random.default_rng(42)
+    p = Pair(capacity=2048)
+    # 1024 disjoint regions, then one full batch: repeats, contained ranges,
+    # nested new ranges and invalid ones.
+    base = np.arange(1024, dtype=np.uint64) * np.uint64(64 * M)
+    p.register(base, np.full(1024, 32 * M, np.uint64), "table")
+    n = dd.REG_MAX_BATCH
+    pick = rng.integers(0, 1024, n)
+    kind = rng.integers(0, 4, n)
+    starts = base[pick] + np.where(kind == 1, rng.integers(0, 16 * M, n), 0).astype(np.uint64)
+    starts = np.where(kind >= 2, base[pick] + np.uint64(40 * M) +
+                      rng.integers(0, 8, n).astype(np.uint64) * np.uint64(M), starts)
+    sizes = np.where(kind == 0, 32 * M, np.where(kind == 1, M, (8 - (starts - base[pick] - np.uint64(40 * M)) // np.uint64(M)) * np.uint64(M)))
+    sizes = np.where(kind >= 2, np.maximum(sizes.astype(np.int64), 1), sizes).astype(np.uint64)
+    sizes[rng.random(n) < 0.01] = 0
+    h, k = p.register(starts, sizes, "full batch")
+    assert (k == oracle.REG_HIT_NEW).sum() > 1000 and (k == oracle.REG_NEW).sum() > 1000
+    p.deregister(rng.choice(h[h > 0], n), "full deregister")
+
+
+def test_empty_batches_and_empty_table():
+    p = Pair()
+    p.register(np.zeros(0, np.uint64), np.zeros(0, np.uint64), "empty register")
+    p.deregister(np.array([1, 2, 0], np.uint64), "deregister on an empty table")
+    p.deregister(np.zeros(0, np.uint64), "empty deregister")
