@@ -60,6 +60,10 @@ def _lib():
                                      ctypes.POINTER(_u8p), _u32p, _u32p, _u32p, _u64p, _u32p,
                                      _u32p]
         lib.orc_emit_sqe.restype = None
+        lib.orc_build_put.argtypes = [_u64p, _u64p, _u64p, _u32p, u64, u64, u64, ctypes.c_uint,
+                                      _u32p, _u64p, _u32p, u32, ctypes.c_void_p, u64,
+                                      _u64p, _u32p, _u8p, _u64p]
+        lib.orc_build_put.restype = None
         lib.orc_reg_create.argtypes = [ctypes.c_uint]
         lib.orc_reg_create.restype = ctypes.c_void_p
         lib.orc_reg_destroy.argtypes = [ctypes.c_void_p]
@@ -196,6 +200,32 @@ def emit_sqe(perm, qoff, status, length, slba, prp1, prp2, rings, depth, free_sl
                         _p(free_slots, _u32p), _p(tail, _u32p), _p(cursor, _u64p),
                         _p(placed, _u32p), _p(req_of_slot, _u32p))
     return dict(tail=tail, cursor=cursor, placed=placed)
+
+
+PUT_DESC = np.dtype([("laddr", "<u8"), ("raddr", "<u8"), ("len", "<u4"), ("lkey", "<u4"),
+                     ("rkey", "<u4"), ("req", "<u4")])
+
+
+def build_put(src, dst, nbytes, pe, local_base, heap_bytes, chunk_shift, lkeys, peer_base,
+              rkeys, desc_cap, write=True):
+    """Runs O6; returns dict(desc (PUT_DESC[desc_cap] or None), first, count,
+    status, total)."""
+    src, dst, nbytes, pe = _u64(src), _u64(dst), _u64(nbytes), _u32(pe)
+    lkeys, peer_base, rkeys = _u32(lkeys), _u64(peer_base), _u32(rkeys)
+    n = src.shape[0]
+    desc = np.zeros(desc_cap, PUT_DESC) if write else None
+    out = dict(first=np.empty(n, np.uint64), count=np.empty(n, np.uint32),
+               status=np.empty(n, np.uint8))
+    total = np.zeros(1, np.uint64)
+    _lib().orc_build_put(_p(src, _u64p), _p(dst, _u64p), _p(nbytes, _u64p), _p(pe, _u32p), n,
+                         local_base, heap_bytes, chunk_shift, _p(lkeys, _u32p),
+                         _p(peer_base, _u64p), _p(rkeys, _u32p), peer_base.shape[0],
+                         desc.ctypes.data if write else None, desc_cap,
+                         _p(out["first"], _u64p), _p(out["count"], _u32p),
+                         _p(out["status"], _u8p), _p(total, _u64p))
+    out["desc"] = desc
+    out["total"] = int(total[0])
+    return out
 
 
 class Registry:

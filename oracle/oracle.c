@@ -410,6 +410,101 @@ void orc_emit_sqe(const uint32_t *perm, const uint64_t *qoff, uint32_t nqueues,
 }
 
 /* ------------------------------------------------------------------------
+ * O6  RDMA put descriptors for a symmetric heap.
+ *
+ * [MORI] thread-scope put: the remote address of a heap address is the peer's
+ * heap base plus the same offset. In a static heap one local key and one
+ * remote key per peer cover the whole heap and the whole remainder is sent at
+ * once. In a VMM heap each chunk has its own keys; every round the source
+ * chunk and the destination chunk are looked up, each giving the bytes left in
+ * that chunk and its key, and the round sends min(source chunk left,
+ * destination chunk left, remaining), so a key is always valid for what it
+ * covers.
+ *
+ * Readings: chunks are 2^chunk_shift bytes everywhere in the heap and on
+ * every PE; a piece never exceeds 2^31 bytes (the RDMA message limit; it only
+ * matters for a static heap); descriptors are laid out request after request
+ * from a running count that refused requests also advance.
+ *
+ * Pinned by: the closed-form piece count 1 + (source boundaries crossed) +
+ * (destination boundaries crossed) - (shared ones); a byte walk on tiny chunks
+ * (pieces are the maximal runs of bytes with one source chunk and one
+ * destination chunk); sum of lengths, contiguity, keys and addresses.
+ * ------------------------------------------------------------------------ */
+#define ORC_PUT_MAX_MSG (1ull << 31)
+
+void orc_build_put(const uint64_t *src, const uint64_t *dst, const uint64_t *bytes,
+                   const uint32_t *pe, uint64_t n, uint64_t local_base, uint64_t heap_bytes,
+                   unsigned chunk_shift, const uint32_t *lkeys, const uint64_t *peer_base,
+                   const uint32_t *rkeys, uint32_t npes, orc_put_desc *desc, uint64_t desc_cap,
+                   uint64_t *first, uint32_t *count, uint8_t *status, uint64_t *total)
+{
+    const int vmm = chunk_shift != 0;
+    const uint64_t chunk = vmm ? 1ull << chunk_shift : 0;
+    const uint64_t nchunks = vmm ? heap_bytes >> chunk_shift : 1;
+    uint64_t next = 0;
+    for (uint64_t i = 0; i < n; ++i) {
+        first[i] = next;
+        count[i] = 0;
+        status[i] = ORC_OK;
+        if (bytes[i] == 0 || pe[i] >= npes) {
+            status[i] = ORC_EINVAL;
+            continue;
+        }
+        if ((u128)src[i] + bytes[i] > heap_bytes || (u128)dst[i] + bytes[i] > heap_bytes) {
+            status[i] = ORC_ERANGE;
+            continue;
+        }
+        /* The rounds of the put loop, first only counted. */
+        uint64_t pieces = 0;
+        for (uint64_t x = 0; x < bytes[i];) {
+            uint64_t t = bytes[i] - x;
+            if (vmm) {
+                const uint64_t src_left = chunk - (src[i] + x) % chunk;
+                const uint64_t dst_left = chunk - (dst[i] + x) % chunk;
+                if (src_left < t) t = src_left;
+                if (dst_left < t) t = dst_left;
+            }
+            if (t > ORC_PUT_MAX_MSG) t = ORC_PUT_MAX_MSG;
+            x += t;
+            ++pieces;
+        }
+        count[i] = (uint32_t)pieces;
+        next += pieces;
+        if (first[i] + pieces > desc_cap) {
+            status[i] = ORC_ENOSPC;
+            continue;
+        }
+        if (desc == NULL) continue;
+        /* The same rounds, now writing one descriptor each. */
+        uint64_t k = first[i];
+        for (uint64_t x = 0; x < bytes[i];) {
+            uint64_t t = bytes[i] - x;
+            uint32_t lkey = lkeys[0], rkey = rkeys[pe[i]];
+            if (vmm) {
+                const uint64_t sc = (src[i] + x) >> chunk_shift, dc = (dst[i] + x) >> chunk_shift;
+                const uint64_t src_left = chunk - (src[i] + x) % chunk;
+                const uint64_t dst_left = chunk - (dst[i] + x) % chunk;
+                if (src_left < t) t = src_left;
+                if (dst_left < t) t = dst_left;
+                lkey = lkeys[sc];
+                rkey = rkeys[(uint64_t)pe[i] * nchunks + dc];
+            }
+            if (t > ORC_PUT_MAX_MSG) t = ORC_PUT_MAX_MSG;
+            desc[k].laddr = local_base + src[i] + x;
+            desc[k].raddr = peer_base[pe[i]] + dst[i] + x;
+            desc[k].len = (uint32_t)t;
+            desc[k].lkey = lkey;
+            desc[k].rkey = rkey;
+            desc[k].req = (uint32_t)i;
+            ++k;
+            x += t;
+        }
+    }
+    *total = next;
+}
+
+/* ------------------------------------------------------------------------
  * O4  Registration cache with reference counts.
  *
  * [NCCL-26] "Communicator User Registration Cache": register rounds the range

@@ -109,6 +109,31 @@ void orc_emit_sqe(const uint32_t *perm, const uint64_t *qoff, uint32_t nqueues,
                   uint32_t *tail, uint64_t *cursor, uint32_t *placed, uint32_t *req_of_slot);
 
 /*
+ * O6: RDMA put descriptors for a symmetric heap, static or VMM.
+ * Request i moves bytes[i] from heap offset src[i] to heap offset dst[i] of
+ * PE pe[i]. chunk_shift == 0: static heap, one local key lkeys[0] and one
+ * remote key rkeys[pe] per PE. Otherwise the heap is chunks of 2^chunk_shift
+ * bytes (nchunks = heap_bytes >> chunk_shift), chunk k has local key lkeys[k]
+ * and, on PE q, remote key rkeys[q * nchunks + k]. Each request is cut into
+ * pieces: transfer = min(bytes left in the source chunk, bytes left in the
+ * destination chunk, remaining, 2^31); each piece is a descriptor
+ * {laddr = local_base + src + x, raddr = peer_base[pe] + dst + x, len, lkey,
+ * rkey, req = i}. Descriptors of request i are desc[first[i] .. first[i] +
+ * count[i]), first = running count over requests (refused ones included).
+ * Status: EINVAL (zero bytes, pe >= npes), ERANGE (past the heap), ENOSPC
+ * (first + count > desc_cap). *total = descriptors the batch needs.
+ */
+typedef struct {
+    uint64_t laddr, raddr;
+    uint32_t len, lkey, rkey, req;
+} orc_put_desc;
+void orc_build_put(const uint64_t *src, const uint64_t *dst, const uint64_t *bytes,
+                   const uint32_t *pe, uint64_t n, uint64_t local_base, uint64_t heap_bytes,
+                   unsigned chunk_shift, const uint32_t *lkeys, const uint64_t *peer_base,
+                   const uint32_t *rkeys, uint32_t npes, orc_put_desc *desc, uint64_t desc_cap,
+                   uint64_t *first, uint32_t *count, uint8_t *status, uint64_t *total);
+
+/*
  * O4: host registration cache with reference counts ([NCCL-26]).
  * Handles are positive record ids, never reused; 0 is never a handle.
  */
