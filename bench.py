@@ -14,8 +14,9 @@ step's layout; the other layout's build is timed alone beside it):
 algorithmic bytes of one launch / its mean duration from HIP events recorded
 on the stream it runs on. `emit_sqe` times the stage after the path (NVMe
 submission entries for the first window of every queue) on the step's outputs,
-and `registry` a batch of registrations and deregistrations on the device
-registration table, both outside the timed steps. `cpu_baseline` times the single-threaded oracle on a
+`registry` a batch of registrations and deregistrations on the device
+registration table, and `build_put` RDMA put descriptors for a VMM heap, all
+outside the timed steps. `cpu_baseline` times the single-threaded oracle on a
 bounded sample of the same workload.
 """
 from __future__ import annotations
@@ -32,7 +33,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, AMD public specification
-PRP_SOURCES = ["build_prp.hip", "dd_device.hpp"]
+PRP_SOURCES = ["build_prp.hip", "dd_device.hpp", "dd_lookback.hpp"]
 
 
 def traffic_file(layout: str, workload: str) -> str:
@@ -151,6 +152,42 @@ def emit_stage(dd, d, np, torch, prp_out, sp_out, ln, reps):
             "algorithmic_bytes_per_launch": nbytes, "achieved_gbs": round(gbs, 1),
             "frac": round(gbs / PEAK_HBM_GBS, 4),
             "entries_per_s": round(n_placed / (ms * 1e-3), 1)}
+
+
+def put_stage(dd, np, torch, n, reps):
+    """Times dmadesc_build_put on n seeded puts against a 256 GiB VMM heap of
+    2 MiB chunks on 8 PEs (lengths as the Mixed requests). Algorithmic bytes:
+    per put 28 read (src, dst, bytes, pe) + 13 written (first, count, status);
+    per descriptor 32 written + 8 of keys read."""
+    import synth
+    dev = torch.device("cuda:0")
+    up = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)  # noqa: E731
+    b = synth.put_batch(n)
+    args = [up(b["src"]), up(b["dst"]), up(b["len"]), up(b["pe"]), b["local_base"], b["heap"],
+            b["chunk_shift"], up(b["lkeys"]), up(b["peer_base"]), up(b["rkeys"])]
+    probe = dd.build_put(*args, torch.empty((0, 4), dtype=torch.uint64, device=dev))
+    torch.cuda.synchronize()
+    total = int(probe["total"].cpu()[0])
+    desc = torch.empty((total, 4), dtype=torch.uint64, device=dev)
+    ws = torch.empty(max(dd.workspace_bytes(dd.OP_BUILD_PUT, n), 1), dtype=torch.uint8, device=dev)
+    out, ms = None, []
+    for r in range(reps + 3):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        out = dd.build_put(*args, desc, out=out, ws=ws)
+        e1.record()
+        if r >= 3:
+            ms.append((e0, e1))
+    torch.cuda.synchronize()
+    mean = float(np.mean([a.elapsed_time(c) for a, c in ms]))
+    nbytes = n * (28 + 13) + total * (32 + 8)
+    gbs = nbytes / (mean * 1e-3) / 1e9
+    return {"kernels": "k_ws_clear + k_put_build", "puts": n, "descriptors": total,
+            "heap": "256 GiB, 2 MiB chunks, 8 PEs", "mean_launch_ms": round(mean, 4),
+            "puts_per_s": round(n / (mean * 1e-3), 1),
+            "descriptors_per_s": round(total / (mean * 1e-3), 1),
+            "algorithmic_bytes_per_launch": nbytes, "achieved_gbs": round(gbs, 1),
+            "frac": round(gbs / PEAK_HBM_GBS, 4)}
 
 
 def registry_stage(dd, d, np, torch, reps):
@@ -414,7 +451,7 @@ def main():
     del o_pool
 
     kernel = ("dmadesc_build_prp_packed" if packed else "dmadesc_build_prp") + \
-        " (k_prp_clear + k_prp_build)"
+        " (k_ws_clear + k_prp_build)"
     result = {
         "metric": "descriptor requests/sec (M/s) + achieved HBM GB/s vs MI355X peak",
         "value": round(n * args.steps / elapsed / 1e6, 3),
@@ -452,6 +489,8 @@ def main():
         result["emit_sqe"] = emit_stage(dd, d, np, torch, prp_out, sp_out, ln, args.emit_reps)
     if d["regions"] and args.emit_reps > 0:
         result["registry"] = registry_stage(dd, d, np, torch, 10)
+    if args.emit_reps > 0:
+        result["build_put"] = put_stage(dd, np, torch, n, args.emit_reps)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(args.workload, min(args.cpu_sample, n),
                                               args.cpu_seconds, args.layout)

@@ -17,6 +17,11 @@
  *   dmadesc_emit_sqe           64-byte NVMe submission entries in per-queue
  *                              rings, one window of the split per call
  *
+ * a put-descriptor build for a symmetric heap:
+ *
+ *   dmadesc_build_put          RDMA put descriptors, one per chunk-bounded piece
+ *                              (static heap or VMM heap with per-chunk keys)
+ *
  * and the registration cache kept on the device:
  *
  *   dmadesc_reg_register       batch of registrations (page-rounded, refcounted)
@@ -92,7 +97,8 @@ enum dmadesc_op {
     DMADESC_OP_BUILD_PRP = 2,
     DMADESC_OP_PARTITION = 3,
     DMADESC_OP_EMIT_SQE = 4,
-    DMADESC_OP_REGISTRY = 5
+    DMADESC_OP_REGISTRY = 5,
+    DMADESC_OP_BUILD_PUT = 6
 };
 
 /* Largest nqueues dmadesc_partition_by_queue and dmadesc_emit_sqe accept. */
@@ -300,6 +306,52 @@ int dmadesc_emit_sqe(const uint32_t *perm, const uint64_t *qoff, uint32_t nqueue
                      const uint64_t *ring, const uint32_t *depth, const uint32_t *free_slots,
                      uint32_t *tail, uint64_t *cursor, uint32_t *placed,
                      uint32_t *req_of_slot, void *ws, size_t ws_bytes, void *stream);
+
+/* One RDMA put descriptor (32 bytes, little endian). */
+typedef struct dmadesc_put_desc {
+    uint64_t laddr;   /* local address: local_base + src + x      */
+    uint64_t raddr;   /* remote address: peer_base[pe] + dst + x  */
+    uint32_t len;     /* bytes of this piece (1 .. 2^31)          */
+    uint32_t lkey;    /* key of the source chunk                  */
+    uint32_t rkey;    /* key of the destination chunk on pe       */
+    uint32_t req;     /* request index                            */
+} dmadesc_put_desc;
+
+/*
+ * dmadesc_build_put - RDMA put descriptors for a symmetric heap.
+ *
+ * [MORI] thread-scope put and QueryRemoteAddr: the remote address of a heap
+ * offset is the peer's heap base plus the same offset. Static heap
+ * (chunk_shift == 0): one local key lkeys[0] and one remote key rkeys[pe] per
+ * peer; a put is one transfer. VMM heap (chunk_shift 12..31): the heap is
+ * chunks of 2^chunk_shift bytes with their own keys (lkeys[k]; on PE q,
+ * rkeys[q * nchunks + k], nchunks = heap_bytes >> chunk_shift); each transfer
+ * is min(bytes left in the source chunk, bytes left in the destination chunk,
+ * remaining), so every piece lies in one chunk on both sides. No piece exceeds
+ * 2^31 bytes (the RDMA message limit; it binds only for a static heap).
+ *   src, dst, bytes u64[n]  heap offsets (local source, remote destination)
+ *                           and length of each put
+ *   pe              u32[n]  destination PE (< npes, 1..65536)
+ *   local_base, peer_base[npes]  heap base addresses (host value / device)
+ *   heap_bytes      heap size; with VMM a multiple of the chunk size with
+ *                   fewer than 2^30 chunks
+ *   desc            dmadesc_put_desc[desc_cap] (16-byte aligned)
+ * Outputs: first u64[n] (slot of the first descriptor of put i: a running
+ * count over all puts, refused ones included), count u32[n] (its pieces; 0
+ * for EINVAL/ERANGE), status u8[n] (enum dmadesc_prp_status: EINVAL zero bytes
+ * or pe >= npes, ERANGE past the heap on either side, ENOSPC first + count >
+ * desc_cap, refused puts are a suffix), *total (device u64: descriptors the
+ * batch needs). Descriptors of refused puts are not written; no other
+ * descriptor slot is written. Extra check: n * (most pieces per put) >= 2^62
+ * -> -EINVAL.
+ * Workspace: dmadesc_workspace_bytes(DMADESC_OP_BUILD_PUT, n, 0).
+ */
+int dmadesc_build_put(const uint64_t *src, const uint64_t *dst, const uint64_t *bytes,
+                      const uint32_t *pe, uint64_t n, uint64_t local_base, uint64_t heap_bytes,
+                      uint32_t chunk_shift, const uint32_t *lkeys, const uint64_t *peer_base,
+                      const uint32_t *rkeys, uint32_t npes, dmadesc_put_desc *desc,
+                      uint64_t desc_cap, uint64_t *first, uint32_t *count, uint8_t *status,
+                      uint64_t *total, void *ws, size_t ws_bytes, void *stream);
 
 /* Registration cache limits and per-call outcomes. */
 #define DMADESC_REG_MAX_BATCH 65536u          /* calls per batch                  */

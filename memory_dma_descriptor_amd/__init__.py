@@ -15,7 +15,7 @@ import torch
 from . import _build
 
 __all__ = ["mr_lookup", "build_prp", "build_prp_packed", "partition_by_queue", "emit_sqe",
-           "ring_addresses", "DeviceRegistry",
+           "ring_addresses", "DeviceRegistry", "build_put",
            "workspace_bytes", "DmadescError", "lib", "LIB_PATH", "MAX_QUEUES",
            "SQ_MAX_DEPTH",
            "MISS", "EXACT", "CONTAINED", "INVALID",
@@ -24,7 +24,7 @@ __all__ = ["mr_lookup", "build_prp", "build_prp_packed", "partition_by_queue", "
 LIB_PATH = _build.LIB
 MAX_QUEUES = 256
 SQ_MAX_DEPTH = 65536
-OP_MR_LOOKUP, OP_BUILD_PRP, OP_PARTITION, OP_EMIT_SQE, OP_REGISTRY = 1, 2, 3, 4, 5
+OP_MR_LOOKUP, OP_BUILD_PRP, OP_PARTITION, OP_EMIT_SQE, OP_REGISTRY, OP_BUILD_PUT = 1, 2, 3, 4, 5, 6
 REG_MAX_BATCH, REG_MAX_CAPACITY = 65536, 1 << 24
 REG_INVALID, REG_HIT, REG_NEW, REG_HIT_NEW, REG_NOSPACE = 0, 1, 2, 3, 4
 DEREG_OK, DEREG_REMOVED, DEREG_STALE = 0, 1, 2
@@ -47,6 +47,8 @@ _EXPORTS = {
                                    ctypes.c_int),
     "dmadesc_emit_sqe": ([_P, _P, _U32, _P, _P, _P, _P, _P, _U64, _U32, _U32, _U32,
                           _P, _P, _P, _P, _P, _P, _P, _P, _SIZE, _P], ctypes.c_int),
+    "dmadesc_build_put": ([_P, _P, _P, _P, _U64, _U64, _U64, _U32, _P, _P, _P, _U32, _P, _U64,
+                           _P, _P, _P, _P, _P, _SIZE, _P], ctypes.c_int),
     "dmadesc_reg_register": ([_P, _P, _P, _P, _P, _P, _U64, _U32, _P, _P, _U64, _P, _P, _P,
                               _P, _SIZE, _P], ctypes.c_int),
     "dmadesc_reg_deregister": ([_P, _P, _P, _P, _P, _P, _U64, _P, _U64, _P, _P, _SIZE, _P],
@@ -238,6 +240,40 @@ def emit_sqe(perm: torch.Tensor, qoff: torch.Tensor, status: torch.Tensor,
         rid, ws.data_ptr(), ws.numel(), _stream(dev, stream))
     _check("dmadesc_emit_sqe", rc)
     return dict(placed=placed, tail=tail, cursor=cursor, req_of_slot=req_of_slot)
+
+
+def build_put(src: torch.Tensor, dst: torch.Tensor, nbytes: torch.Tensor, pe: torch.Tensor,
+              local_base: int, heap_bytes: int, chunk_shift: int, lkeys: torch.Tensor,
+              peer_base: torch.Tensor, rkeys: torch.Tensor, desc: torch.Tensor,
+              out: dict | None = None, ws: torch.Tensor | None = None, stream=None) -> dict:
+    """RDMA put descriptors into `desc` (u64[desc_cap, 4], one 32-byte
+    dmadesc_put_desc per row); returns dict(first, count, status, total)."""
+    n = src.numel()
+    dev = src.device
+    if desc.dim() != 2 or desc.shape[1] != 4:
+        raise ValueError("desc must have shape [desc_cap, 4]")
+    nchunks = heap_bytes >> chunk_shift if chunk_shift else 1
+    if lkeys.numel() < nchunks or rkeys.numel() < peer_base.numel() * nchunks:
+        raise ValueError("key tables smaller than the heap's chunks (lkeys[nchunks], "
+                         "rkeys[npes * nchunks])")
+    if out is None:
+        out = dict(first=torch.empty(n, dtype=torch.uint64, device=dev),
+                   count=torch.empty(n, dtype=torch.uint32, device=dev),
+                   status=torch.empty(n, dtype=torch.uint8, device=dev),
+                   total=torch.empty(1, dtype=torch.uint64, device=dev))
+    ws = _workspace(OP_BUILD_PUT, n, 0, dev, ws)
+    rc = lib().dmadesc_build_put(
+        _dev(src, torch.uint64, "src", n), _dev(dst, torch.uint64, "dst", n),
+        _dev(nbytes, torch.uint64, "bytes", n), _dev(pe, torch.uint32, "pe", n), n,
+        local_base, heap_bytes, chunk_shift, _dev(lkeys, torch.uint32, "lkeys"),
+        _dev(peer_base, torch.uint64, "peer_base"), _dev(rkeys, torch.uint32, "rkeys"),
+        peer_base.numel(), _dev(desc, torch.uint64, "desc"), desc.shape[0],
+        _dev(out["first"], torch.uint64, "first", n), _dev(out["count"], torch.uint32, "count", n),
+        _dev(out["status"], torch.uint8, "status", n),
+        _dev(out["total"], torch.uint64, "total", 1), ws.data_ptr(), ws.numel(),
+        _stream(dev, stream))
+    _check("dmadesc_build_put", rc)
+    return out
 
 
 class DeviceRegistry:

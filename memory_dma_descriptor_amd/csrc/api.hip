@@ -65,6 +65,7 @@ size_t dmadesc_workspace_bytes(int op, uint64_t n, uint32_t param)
     case DMADESC_OP_EMIT_SQE:
         if (param == 0 || param > DMADESC_MAX_QUEUES) return 0;
         return dd::ws_emit_sqe(param);
+    case DMADESC_OP_BUILD_PUT: return dd::ws_build_put(n);
     case DMADESC_OP_REGISTRY:
         if (n > DMADESC_REG_MAX_BATCH || param > DMADESC_REG_MAX_CAPACITY) return 0;
         return dd::ws_registry(n, param);
@@ -144,6 +145,34 @@ int dmadesc_emit_sqe(const uint32_t *perm, const uint64_t *qoff, uint32_t nqueue
     dd::SqeArgs a{perm, qoff, nqueues, status, len, slba, prp1, prp2, n, opcode, nsid, lba_shift,
                   ring, depth, free_slots, tail, cursor, placed, req_of_slot, ws};
     return launched(dd::launch_emit_sqe(a, static_cast<hipStream_t>(stream)));
+}
+
+int dmadesc_build_put(const uint64_t *src, const uint64_t *dst, const uint64_t *bytes,
+                      const uint32_t *pe, uint64_t n, uint64_t local_base, uint64_t heap_bytes,
+                      uint32_t chunk_shift, const uint32_t *lkeys, const uint64_t *peer_base,
+                      const uint32_t *rkeys, uint32_t npes, dmadesc_put_desc *desc,
+                      uint64_t desc_cap, uint64_t *first, uint32_t *count, uint8_t *status,
+                      uint64_t *total, void *ws, size_t ws_bytes, void *stream)
+{
+    if (n >= kMaxN || npes == 0 || npes > 65536) return -EINVAL;
+    if (chunk_shift != 0 && (chunk_shift < 12 || chunk_shift > 31)) return -EINVAL;
+    if (chunk_shift != 0 &&
+        ((heap_bytes & ((1ull << chunk_shift) - 1)) || (heap_bytes >> chunk_shift) >= (1ull << 30)))
+        return -EINVAL;
+    if (!lkeys || !peer_base || !rkeys || !total) return -EINVAL;
+    if (desc_cap > 0 && !desc) return -EINVAL;
+    if (reinterpret_cast<uintptr_t>(desc) & 15u) return -EINVAL;
+    if (desc_cap > (~0ull >> 5)) return -EINVAL;                 // byte size fits 64 bits
+    const unsigned __int128 most = chunk_shift ? 2 * (heap_bytes >> chunk_shift) + 1
+                                               : (heap_bytes >> 31) + 1;
+    if (most * n >= ((unsigned __int128)1 << 62)) return -EINVAL;
+    if (n > 0 && (!src || !dst || !bytes || !pe || !first || !count || !status)) return -EINVAL;
+    const size_t need = dd::ws_build_put(n);
+    if (need > 0 && (!ws || ws_bytes < need)) return -EINVAL;
+    dd::PutArgs a{src, dst, bytes, pe, n, local_base, heap_bytes, chunk_shift, npes, lkeys,
+                  peer_base, rkeys, reinterpret_cast<uint64_t *>(desc), desc_cap, first, count,
+                  status, total, ws};
+    return launched(dd::launch_build_put(a, static_cast<hipStream_t>(stream)));
 }
 
 int dmadesc_reg_register(uint64_t *start, uint64_t *end, uint64_t *id, uint32_t *refs,

@@ -48,6 +48,7 @@
 
 #include "dd_device.hpp"
 #include "dd_internal.h"
+#include "dd_lookback.hpp"
 
 namespace dd {
 namespace {
@@ -62,31 +63,7 @@ constexpr int kTile = kThreads * kItems;      // requests per block
 constexpr uint64_t kPadWords = 16;
 // GPU pages of the table staged in LDS per wave and round (4 KiB).
 constexpr int kTileFrames = 512;
-constexpr uint64_t kFlagAgg = 1ull << 62;     // status word: aggregate published
-constexpr uint64_t kFlagInc = 2ull << 62;     // status word: inclusive prefix published
-constexpr uint64_t kValue = (1ull << 62) - 1;
-constexpr uint32_t kMaxPolls = 1u << 22;      // bounded wait (about seconds)
-
 enum : uint8_t { kOk = 0, kEinval = 1, kErange = 2, kEnospc = 3 };
-
-// Workspace layout: a 256-byte header, then one status word per block.
-struct Header {
-    uint32_t ticket;     // next block order
-    uint32_t timeouts;   // look-back waits that hit the bound (never expected)
-};
-constexpr size_t kHeaderBytes = 256;
-
-typedef uint64_t u64x2 __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ uint64_t load_status(const uint64_t *p)
-{
-    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-__device__ __forceinline__ void store_status(uint64_t *p, uint64_t v)
-{
-    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
 
 // Status and 4 KiB page count of one request.
 __device__ __forceinline__ uint8_t decode(uint64_t o, uint64_t l, uint64_t heap,
@@ -97,43 +74,6 @@ __device__ __forceinline__ uint8_t decode(uint64_t o, uint64_t l, uint64_t heap,
     if (o + l > heap) return kErange;
     pages = ((o & 4095u) + l + 4095u) >> 12;
     return kOk;
-}
-
-// Exclusive prefix of the list pages of all blocks before `b` (called by one
-// whole wave; lane k inspects block b-1-k of the current window).
-__device__ uint64_t look_back(uint64_t *status, int64_t b, uint32_t *timeouts)
-{
-    const int ln = lane();
-    uint64_t excl = 0;
-    int64_t top = b - 1;
-    uint32_t polls = 0;
-    for (;;) {
-        const int64_t idx = top - ln;
-        uint64_t s = idx >= 0 ? load_status(status + idx) : kFlagInc;   // before block 0: 0
-        while (__ballot((s >> 62) == 0) != 0) {
-            if (++polls > kMaxPolls) {
-                if (ln == 0) atomicAdd(timeouts, 1u);
-                return excl;
-            }
-            __builtin_amdgcn_s_sleep(2);
-            if ((s >> 62) == 0) s = load_status(status + idx);
-        }
-        const uint64_t inc = __ballot((s >> 62) == 2);
-        if (inc != 0) {
-            const int first = __ffsll((unsigned long long)inc) - 1;   // nearest inclusive
-            excl += wave_sum(ln <= first ? (s & kValue) : 0ull);
-            return excl;
-        }
-        excl += wave_sum(s & kValue);
-        top -= kWave;
-    }
-}
-
-__global__ void k_prp_clear(uint64_t *ws_words, uint64_t words)
-{
-    for (uint64_t k = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; k < words;
-         k += (uint64_t)gridDim.x * blockDim.x)
-        ws_words[k] = 0;
 }
 
 // Per-wave table of one round of 64 requests, in LDS.
@@ -740,7 +680,7 @@ hipError_t launch_build_prp(const PrpArgs &a, hipStream_t s)
     const uint64_t nb = (a.n + kTile - 1) / kTile;
     if (nb == 0) {
         // Nothing to build; the batch needs no list pages.
-        hipLaunchKernelGGL(k_prp_clear, dim3(1), dim3(64), 0, s, a.total_pages, (uint64_t)1);
+        hipLaunchKernelGGL(k_ws_clear, dim3(1), dim3(64), 0, s, a.total_pages, (uint64_t)1);
         return hipGetLastError();
     }
     Header *hdr = static_cast<Header *>(a.ws);
@@ -748,7 +688,7 @@ hipError_t launch_build_prp(const PrpArgs &a, hipStream_t s)
     const uint64_t words = kHeaderBytes / sizeof(uint64_t) + nb;
     uint64_t cblocks = (words + 255) / 256;
     if (cblocks > 1024) cblocks = 1024;
-    hipLaunchKernelGGL(k_prp_clear, dim3((unsigned)cblocks), dim3(256), 0, s,
+    hipLaunchKernelGGL(k_ws_clear, dim3((unsigned)cblocks), dim3(256), 0, s,
                        static_cast<uint64_t *>(a.ws), words);
     if (a.packed)
         hipLaunchKernelGGL(k_prp_build<true>, dim3((unsigned)nb), dim3(kThreads), 0, s,

@@ -1,0 +1,250 @@
+// build_put.hip - RDMA put descriptors for a symmetric heap, static or VMM,
+// for gfx950.
+//
+// Method (MORI page, "mori通信库分析(一)", thread-scope put and QueryRemoteAddr):
+// the remote address of a heap offset is the peer's heap base plus the same
+// offset. In a static heap one local key and one remote key per peer cover the
+// heap and the whole remainder goes in one transfer. In a VMM heap every chunk
+// has its own keys, and each round of the put loop sends min(bytes left in the
+// source chunk, bytes left in the destination chunk, remaining), so that a key
+// always covers what it is used for. No transfer exceeds 2^31 bytes (the RDMA
+// message limit), which only binds for a static heap.
+//
+// The rounds have a closed form. With chunk size C, the source boundaries
+// after the start lie at a, a + C, ... (a = C - src % C) and the destination
+// ones at b, b + C, ...; both progressions have period C, so when a != b they
+// alternate: min(a, b), max(a, b), min(a, b) + C, ... Piece j ends at the j-th
+// boundary (or at the end of the request); the piece count is 1 + source
+// boundaries crossed + destination boundaries crossed - the shared ones (all
+// of them when a == b). Every descriptor is therefore computed on its own.
+//
+// One pass: 1,024 requests per block; the descriptor slots of a request are a
+// device-wide exclusive scan of the piece counts in request order (decoupled
+// look-back, dd_lookback.hpp); then each wave writes the descriptors of its 64
+// consecutive requests as one contiguous range, load-balanced over descriptors:
+// lane j of a step takes descriptor S + 64 j + lane and finds its request by a
+// 6-step search over the requests' first slots in LDS.
+#include "dd_device.hpp"
+#include "dd_internal.h"
+#include "dd_lookback.hpp"
+#include "dmadesc.h"
+
+namespace dd {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / kWave;
+constexpr int kItems = 4;
+constexpr int kTile = kThreads * kItems;
+constexpr uint32_t kMsgShift = 31;                   // largest transfer: 2^31 bytes
+
+enum : uint8_t { kOk = 0, kEinval = 1, kErange = 2, kEnospc = 3 };
+
+// Pieces of one put (shift 0: static heap).
+__device__ __forceinline__ uint64_t put_pieces(uint64_t s, uint64_t d, uint64_t b, uint32_t shift)
+{
+    if (shift == 0) return (b + (1ull << kMsgShift) - 1) >> kMsgShift;
+    const uint64_t cs = ((s + b - 1) >> shift) - (s >> shift);
+    const uint64_t cd = ((d + b - 1) >> shift) - (d >> shift);
+    const uint64_t common = ((s - d) & ((1ull << shift) - 1)) == 0 ? cs : 0;
+    return 1 + cs + cd - common;
+}
+
+// Offset (from the put's start) at which piece j ends, before clipping to the
+// put's length.
+__device__ __forceinline__ uint64_t put_boundary(uint64_t s, uint64_t d, uint32_t shift, uint64_t j)
+{
+    if (shift == 0) return (j + 1) << kMsgShift;
+    const uint64_t c = 1ull << shift, mask = c - 1;
+    const uint64_t a = c - (s & mask), bb = c - (d & mask);
+    if (a == bb) return a + (j << shift);
+    const uint64_t lo = a < bb ? a : bb, hi = a < bb ? bb : a;
+    return ((j & 1) ? hi : lo) + ((j >> 1) << shift);
+}
+
+struct PutTab {
+    uint64_t start[kWave + 1];   // first descriptor slot of each request ([64]: end)
+    uint64_t s[kWave], d[kWave], b[kWave];
+    uint32_t pe[kWave];
+    uint32_t req[kWave];
+};
+
+struct PutKeys {
+    const uint32_t *lkeys;
+    const uint64_t *peer_base;
+    const uint32_t *rkeys;
+    uint64_t local_base, nchunks;
+    uint32_t shift;
+};
+
+// Writes the descriptors of the wave's 64 requests of one round (lane k: one
+// request, m descriptors from slot first; m == 0 for none).
+__device__ __forceinline__ void emit_put_round(PutTab &T, uint64_t first, uint64_t m, uint64_t s,
+                                               uint64_t d, uint64_t b, uint32_t pe, uint32_t req,
+                                               const PutKeys &K, uint64_t *__restrict__ desc)
+{
+    const int ln = lane();
+    const uint64_t has = __ballot(m != 0);
+    if (has == 0) return;                                // uniform per wave
+    const int lo = __ffsll((unsigned long long)has) - 1;
+    const int hi = 63 - __clzll((unsigned long long)has);
+    const uint64_t S = __shfl(first, lo, kWave);
+    const uint64_t E = __shfl(first + m, hi, kWave);
+    // Requests before the first one with descriptors start at S; those after
+    // the last one (none, or refused) at E: the search never picks them.
+    T.start[ln] = first < S ? S : (first > E ? E : first);
+    if (ln == kWave - 1) T.start[kWave] = E;
+    T.s[ln] = s;
+    T.d[ln] = d;
+    T.b[ln] = b;
+    T.pe[ln] = pe;
+    T.req[ln] = req;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    for (uint64_t p = S + ln; p < E; p += kWave) {
+        const int r = owner_of<kWave>(T.start, p);
+        const uint64_t j = p - T.start[r];
+        const uint64_t rs = T.s[r], rd = T.d[r], rb = T.b[r];
+        const uint32_t rpe = T.pe[r];
+        const uint64_t x0 = j ? put_boundary(rs, rd, K.shift, j - 1) : 0;
+        uint64_t x1 = put_boundary(rs, rd, K.shift, j);
+        x1 = x1 < rb ? x1 : rb;
+        uint32_t lkey, rkey;
+        if (K.shift) {
+            lkey = K.lkeys[(rs + x0) >> K.shift];
+            rkey = K.rkeys[(uint64_t)rpe * K.nchunks + ((rd + x0) >> K.shift)];
+        } else {
+            lkey = K.lkeys[0];
+            rkey = K.rkeys[rpe];
+        }
+        const uint64_t w2 = (x1 - x0) | ((uint64_t)lkey << 32);
+        const uint64_t w3 = rkey | ((uint64_t)T.req[r] << 32);
+        uint64_t *dst = desc + 4 * p;
+        __builtin_nontemporal_store(u64x2{K.local_base + rs + x0, K.peer_base[rpe] + rd + x0},
+                                    reinterpret_cast<u64x2 *>(dst));
+        __builtin_nontemporal_store(u64x2{w2, w3}, reinterpret_cast<u64x2 *>(dst + 2));
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");   // the next round rewrites T
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+__global__ __launch_bounds__(kThreads) void k_put_build(
+    const uint64_t *__restrict__ src, const uint64_t *__restrict__ dst,
+    const uint64_t *__restrict__ bytes, const uint32_t *__restrict__ pe, uint64_t n,
+    uint64_t heap, uint32_t npes, PutKeys K, uint64_t *__restrict__ desc, uint64_t cap,
+    uint64_t *__restrict__ first_out, uint32_t *__restrict__ count_out,
+    uint8_t *__restrict__ status, uint64_t *__restrict__ total, uint64_t nblocks,
+    Header *__restrict__ hdr, uint64_t *__restrict__ bstat)
+{
+    __shared__ uint64_t s_red[kItems * kWaves];
+    __shared__ uint64_t s_bid, s_excl;
+    __shared__ PutTab s_tab[kWaves];
+    const int t = threadIdx.x, w = wave(), ln = lane();
+    if (t == 0) s_bid = atomicAdd(&hdr->ticket, 1u);
+    __syncthreads();
+    const uint64_t blk = s_bid;
+    const uint64_t base = blk * kTile;
+
+    uint64_t s[kItems], d[kItems], b[kItems], cnt[kItems], pre[kItems];
+    uint32_t q[kItems];
+    uint8_t st[kItems];
+#pragma unroll
+    for (int k = 0; k < kItems; ++k) {
+        const uint64_t i = base + (uint64_t)k * kThreads + t;
+        const bool in = i < n;
+        s[k] = in ? __builtin_nontemporal_load(src + i) : 0;
+        d[k] = in ? __builtin_nontemporal_load(dst + i) : 0;
+        b[k] = in ? __builtin_nontemporal_load(bytes + i) : 0;
+        q[k] = in ? __builtin_nontemporal_load(pe + i) : 0;
+    }
+#pragma unroll
+    for (int k = 0; k < kItems; ++k) {
+        st[k] = kOk;
+        if (b[k] == 0 || q[k] >= npes) st[k] = kEinval;
+        else if (b[k] > heap || s[k] > heap - b[k] || d[k] > heap - b[k]) st[k] = kErange;
+        cnt[k] = st[k] == kOk ? put_pieces(s[k], d[k], b[k], K.shift) : 0;
+        const uint64_t inc = wave_incl_scan(cnt[k]);
+        pre[k] = inc - cnt[k];
+        if (ln == kWave - 1) s_red[k * kWaves + w] = inc;
+    }
+    __syncthreads();
+    uint64_t agg = 0;
+#pragma unroll
+    for (int k = 0; k < kItems; ++k) {
+        uint64_t before = 0, all = 0;
+#pragma unroll
+        for (int v = 0; v < kWaves; ++v) {
+            const uint64_t x = s_red[k * kWaves + v];
+            before += v < w ? x : 0ull;
+            all += x;
+        }
+        pre[k] += agg + before;
+        agg += all;
+    }
+    if (w == 0) {
+        uint64_t excl = 0;
+        if (blk == 0) {
+            if (ln == 0) store_status(bstat, kFlagInc | agg);
+        } else {
+            if (ln == 0) store_status(bstat + blk, kFlagAgg | agg);
+            excl = look_back(bstat, (int64_t)blk, &hdr->timeouts);
+            if (ln == 0) store_status(bstat + blk, kFlagInc | (excl + agg));
+        }
+        if (ln == 0) {
+            s_excl = excl;
+            if (blk == nblocks - 1) *total = excl + agg;
+        }
+    }
+    __syncthreads();
+    const uint64_t excl = s_excl;
+
+#pragma unroll 1
+    for (int k = 0; k < kItems; ++k) {
+        const uint64_t i = base + (uint64_t)k * kThreads + t;
+        const uint64_t f = excl + pre[k];
+        uint8_t sk = st[k];
+        if (cnt[k] != 0 && f + cnt[k] > cap) sk = kEnospc;   // refused; its slots stay taken
+        if (i < n) {
+            __builtin_nontemporal_store(f, first_out + i);
+            __builtin_nontemporal_store((uint32_t)cnt[k], count_out + i);
+            __builtin_nontemporal_store(sk, status + i);
+        }
+        emit_put_round(s_tab[w], f, sk == kOk ? cnt[k] : 0, s[k], d[k], b[k], q[k],
+                       (uint32_t)i, K, desc);
+    }
+}
+
+}  // namespace
+
+size_t ws_build_put(uint64_t n)
+{
+    if (n == 0) return 0;
+    const uint64_t nb = (n + kTile - 1) / kTile;
+    return align256(kHeaderBytes + nb * sizeof(uint64_t));
+}
+
+hipError_t launch_build_put(const PutArgs &a, hipStream_t s)
+{
+    const uint64_t nb = (a.n + kTile - 1) / kTile;
+    if (nb == 0) {
+        hipLaunchKernelGGL(k_ws_clear, dim3(1), dim3(64), 0, s, a.total, (uint64_t)1);
+        return hipGetLastError();
+    }
+    Header *hdr = static_cast<Header *>(a.ws);
+    uint64_t *bstat = reinterpret_cast<uint64_t *>(static_cast<char *>(a.ws) + kHeaderBytes);
+    const uint64_t words = kHeaderBytes / sizeof(uint64_t) + nb;
+    uint64_t cblocks = (words + 255) / 256;
+    if (cblocks > 1024) cblocks = 1024;
+    hipLaunchKernelGGL(k_ws_clear, dim3((unsigned)cblocks), dim3(256), 0, s,
+                       static_cast<uint64_t *>(a.ws), words);
+    const PutKeys K{a.lkeys, a.peer_base, a.rkeys, a.local_base,
+                    a.chunk_shift ? a.heap_bytes >> a.chunk_shift : 1, a.chunk_shift};
+    hipLaunchKernelGGL(k_put_build, dim3((unsigned)nb), dim3(kThreads), 0, s, a.src, a.dst,
+                       a.bytes, a.pe, a.n, a.heap_bytes, a.npes, K, a.desc, a.desc_cap,
+                       a.first, a.count, a.status, a.total, nb, hdr, bstat);
+    return hipGetLastError();
+}
+
+}  // namespace dd

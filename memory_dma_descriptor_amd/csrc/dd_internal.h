@@ -75,16 +75,35 @@ struct RegArgs {
     void *ws;
 };
 
+struct PutArgs {
+    const uint64_t *src, *dst, *bytes;
+    const uint32_t *pe;
+    uint64_t n, local_base, heap_bytes;
+    uint32_t chunk_shift, npes;
+    const uint32_t *lkeys;
+    const uint64_t *peer_base;
+    const uint32_t *rkeys;
+    uint64_t *desc;             // 4 words per descriptor
+    uint64_t desc_cap;
+    uint64_t *first;
+    uint32_t *count;
+    uint8_t *status;
+    uint64_t *total;
+    void *ws;
+};
+
 hipError_t launch_mr_lookup(const LookupArgs &a, hipStream_t s);
 hipError_t launch_build_prp(const PrpArgs &a, hipStream_t s);
 hipError_t launch_partition(const SplitArgs &a, hipStream_t s);
 hipError_t launch_emit_sqe(const SqeArgs &a, hipStream_t s);
+hipError_t launch_build_put(const PutArgs &a, hipStream_t s);
 hipError_t launch_reg_register(const RegArgs &a, hipStream_t s);
 hipError_t launch_reg_deregister(const RegArgs &a, hipStream_t s);
 
 size_t ws_build_prp(uint64_t n);
 size_t ws_partition(uint64_t n, uint32_t nqueues);
 size_t ws_emit_sqe(uint32_t nqueues);
+size_t ws_build_put(uint64_t n);
 size_t ws_registry(uint64_t n, uint64_t capacity);
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }

@@ -207,13 +207,16 @@ PUT_DESC = np.dtype([("laddr", "<u8"), ("raddr", "<u8"), ("len", "<u4"), ("lkey"
 
 
 def build_put(src, dst, nbytes, pe, local_base, heap_bytes, chunk_shift, lkeys, peer_base,
-              rkeys, desc_cap, write=True):
+              rkeys, desc_cap, write=True, desc=None):
     """Runs O6; returns dict(desc (PUT_DESC[desc_cap] or None), first, count,
-    status, total)."""
+    status, total). `desc` may be a caller array of PUT_DESC[desc_cap]."""
     src, dst, nbytes, pe = _u64(src), _u64(dst), _u64(nbytes), _u32(pe)
     lkeys, peer_base, rkeys = _u32(lkeys), _u64(peer_base), _u32(rkeys)
     n = src.shape[0]
-    desc = np.zeros(desc_cap, PUT_DESC) if write else None
+    if desc is None:
+        desc = np.zeros(desc_cap, PUT_DESC) if write else None
+    else:
+        assert desc.dtype == PUT_DESC and desc.shape[0] >= desc_cap
     out = dict(first=np.empty(n, np.uint64), count=np.empty(n, np.uint32),
                status=np.empty(n, np.uint8))
     total = np.zeros(1, np.uint64)

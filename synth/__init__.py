@@ -126,3 +126,34 @@ def slba(name: str, n: int, seed: int = 0) -> np.ndarray:
     if _lib().synth_fill_slba(WORKLOADS[name], seed, n, _ptr(out, ctypes.c_uint64)) != 0:
         raise ValueError(name)
     return out
+
+
+PUT_HEAP = 256 << 30          # symmetric heap of the put workload
+PUT_CHUNK_SHIFT = 21          # 2 MiB chunks
+PUT_NPES = 8
+PUT_LOCAL_BASE = 0x0000600000000000
+PUT_STREAM = 0x9075_9075_9075_9075
+
+
+def put_batch(n: int, seed: int = 0, heap: int = PUT_HEAP, chunk_shift: int = PUT_CHUNK_SHIFT,
+              npes: int = PUT_NPES) -> dict:
+    """Seeded puts on a symmetric heap: lengths log-uniform 512 B .. 1 MiB in
+    512 B steps (as the Mixed requests), source and destination offsets
+    uniform and 4-byte aligned with room for the length, destination PE
+    uniform; random nonzero 32-bit keys per chunk (local, and per PE remote)
+    and one heap base per PE. Draws come from SplitMix64 streams."""
+    r = splitmix64((seed or PUT_STREAM) ^ PUT_STREAM, 4 * n)
+    u = (r[:n] >> np.uint64(11)).astype(np.float64) / float(1 << 53)
+    k = np.clip(np.floor(2049.0 ** u), 1, 2048).astype(np.uint64)
+    length = k * np.uint64(512)
+    room = np.uint64(heap) - length
+    src = ((r[n:2 * n] % (room // np.uint64(4) + np.uint64(1))) * np.uint64(4))
+    dst = ((r[2 * n:3 * n] % (room // np.uint64(4) + np.uint64(1))) * np.uint64(4))
+    pe = (r[3 * n:] % np.uint64(npes)).astype(np.uint32)
+    nchunks = heap >> chunk_shift if chunk_shift else 1
+    kr = splitmix64(((seed or PUT_STREAM) ^ PUT_STREAM) + 1, nchunks * (npes + 1))
+    keys = (kr >> np.uint64(32)).astype(np.uint32) | np.uint32(1)
+    peer_base = np.uint64(0x0000400000000000) + np.arange(npes, dtype=np.uint64) * np.uint64(1 << 40)
+    return dict(src=src, dst=dst, len=length, pe=pe, lkeys=keys[:nchunks],
+                rkeys=keys[nchunks:], peer_base=peer_base, local_base=PUT_LOCAL_BASE,
+                heap=heap, chunk_shift=chunk_shift, npes=npes)

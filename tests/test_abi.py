@@ -26,7 +26,8 @@ def _declared():
 def test_exports_every_declared_symbol():
     names = _declared()
     assert {"dmadesc_mr_lookup", "dmadesc_build_prp", "dmadesc_partition_by_queue",
-            "dmadesc_emit_sqe", "dmadesc_reg_register", "dmadesc_reg_deregister"} <= names
+            "dmadesc_emit_sqe", "dmadesc_reg_register", "dmadesc_reg_deregister",
+            "dmadesc_build_put"} <= names
     lib = ctypes.CDLL(dd.LIB_PATH)
     for n in sorted(names):
         assert hasattr(lib, n), n
@@ -129,6 +130,19 @@ def test_emit_sqe_rejects_bad_arguments():
                    (1, NULL), (12, NULL), (13, NULL), (14, NULL), (15, NULL), (16, NULL),
                    (17, NULL), (0, NULL), (3, NULL), (4, NULL), (5, NULL), (6, NULL),
                    (7, NULL), (19, NULL), (20, 16)]:
+        args = list(ok)
+        args[k] = bad
+        assert f(*args) == EINVAL, (k, bad)
+
+
+@no_gpu_only
+def test_build_put_rejects_bad_arguments():
+    f = dd.lib().dmadesc_build_put
+    ok = [P, P, P, P, 8, 0, 1 << 30, 21, P, P, P, 4, P, 64, P, P, P, P, P, 1 << 20, NULL]
+    for k, bad in [(4, 1 << 32), (11, 0), (11, 65537), (7, 11), (7, 32), (6, (1 << 30) + 5),
+                   (6, 1 << 52), (8, NULL), (9, NULL), (10, NULL), (17, NULL), (12, NULL),
+                   (12, P + 8), (0, NULL), (3, NULL), (14, NULL), (16, NULL), (18, NULL),
+                   (19, 16)]:
         args = list(ok)
         args[k] = bad
         assert f(*args) == EINVAL, (k, bad)
