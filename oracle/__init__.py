@@ -64,6 +64,8 @@ def _lib():
                                       _u32p, _u64p, _u32p, u32, ctypes.c_void_p, u64,
                                       _u64p, _u32p, _u8p, _u64p]
         lib.orc_build_put.restype = None
+        lib.orc_cq_drain.argtypes = [_u32p, _u32p, u32, u32, _u32p, _u32p, _u32p]
+        lib.orc_cq_drain.restype = u64
         lib.orc_reg_create.argtypes = [ctypes.c_uint]
         lib.orc_reg_create.restype = ctypes.c_void_p
         lib.orc_reg_destroy.argtypes = [ctypes.c_void_p]
@@ -229,6 +231,16 @@ def build_put(src, dst, nbytes, pe, local_base, heap_bytes, chunk_shift, lkeys, 
     out["desc"] = desc
     out["total"] = int(total[0])
     return out
+
+
+def cq_drain(src, dst, gen, head, phase, ack):
+    """Runs O7 on u32[depth, 4] arrays (dst updated in place); returns
+    (copied, head, phase, ack)."""
+    assert src.dtype == np.uint32 and dst.dtype == np.uint32 and src.flags["C_CONTIGUOUS"]
+    h, p, a = (np.array([v], np.uint32) for v in (head, phase, ack))
+    c = _lib().orc_cq_drain(_p(src, _u32p), _p(dst, _u32p), src.shape[0], gen, _p(h, _u32p),
+                            _p(p, _u32p), _p(a, _u32p))
+    return int(c), int(h[0]), int(p[0]), int(a[0])
 
 
 class Registry:

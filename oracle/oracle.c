@@ -505,6 +505,45 @@ void orc_build_put(const uint64_t *src, const uint64_t *dst, const uint64_t *byt
 }
 
 /* ------------------------------------------------------------------------
+ * O7  Completion-queue mirror, one drain.
+ *
+ * [UPCIE] "Memory Architecture" (the CQ mirror): a resident kernel watches
+ * each device-memory completion queue and copies completions into the host
+ * queue as their phase bit turns; per queue the host and the kernel share the
+ * two queue addresses, the depth, a generation (odd while attached) and an
+ * acknowledgement; a queue found with an even generation is acknowledged with
+ * the odd value before it. [NVMe] (not on the pages): a completion entry is 16
+ * bytes with the phase tag in bit 16 of its fourth dword; the controller
+ * writes the tag as 1 on its first pass through the queue and inverts it on
+ * every later pass.
+ *
+ * Readings: a drain copies every entry that carries the expected phase, in
+ * queue order, and stops at the first that does not; the slot keeps the next
+ * position and the expected phase across drains.
+ *
+ * Pinned by: a controller model that writes completions in passes with the
+ * phase inverted each pass; everything it wrote comes out once, in order.
+ * ------------------------------------------------------------------------ */
+uint64_t orc_cq_drain(const uint32_t *src, uint32_t *dst, uint32_t depth, uint32_t gen,
+                      uint32_t *head, uint32_t *phase, uint32_t *ack)
+{
+    if ((gen & 1u) == 0) {
+        *ack = gen - 1;
+        return 0;
+    }
+    uint64_t copied = 0;
+    while (((src[(uint64_t)*head * 4 + 3] >> 16) & 1u) == *phase) {
+        memcpy(&dst[(uint64_t)*head * 4], &src[(uint64_t)*head * 4], 16);
+        ++copied;
+        if (++*head == depth) {
+            *head = 0;
+            *phase ^= 1u;
+        }
+    }
+    return copied;
+}
+
+/* ------------------------------------------------------------------------
  * O4  Registration cache with reference counts.
  *
  * [NCCL-26] "Communicator User Registration Cache": register rounds the range

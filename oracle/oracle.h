@@ -134,6 +134,18 @@ void orc_build_put(const uint64_t *src, const uint64_t *dst, const uint64_t *byt
                    uint64_t *first, uint32_t *count, uint8_t *status, uint64_t *total);
 
 /*
+ * O7: one drain of a completion-queue mirror slot. src and dst are
+ * u32[depth][4] (16-byte NVMe completion entries; the phase tag is bit 16 of
+ * dword 3). If *gen is odd, entries are copied from src to dst starting at
+ * *head while their phase equals *phase; *head advances (mod depth) and
+ * *phase flips each time *head wraps to 0. If *gen is even, nothing is copied
+ * and *ack becomes *gen - 1 (a queue detached before it was drained). Returns
+ * the number of entries copied.
+ */
+uint64_t orc_cq_drain(const uint32_t *src, uint32_t *dst, uint32_t depth, uint32_t gen,
+                      uint32_t *head, uint32_t *phase, uint32_t *ack);
+
+/*
  * O4: host registration cache with reference counts ([NCCL-26]).
  * Handles are positive record ids, never reused; 0 is never a handle.
  */

@@ -175,3 +175,28 @@ class RecordList:
                     return "removed"
                 return "ok"
         return "stale"
+
+
+class CqController:
+    """A completion queue as the NVMe controller fills it: entries are written
+    in queue order, the phase tag (dword 3 bit 16) 1 on the first pass through
+    the queue and inverted on every pass after."""
+
+    def __init__(self, depth, seed=0):
+        self.depth = depth
+        self.cq = np.zeros((depth, 4), np.uint32)
+        self.tail = 0
+        self.phase = 1
+        self.rng = np.random.default_rng(seed)
+        self.log = []                       # every entry written, in order
+
+    def complete(self, count):
+        for _ in range(count):
+            e = self.rng.integers(0, 1 << 32, 4, dtype=np.uint64).astype(np.uint32)
+            e[3] = (e[3] & np.uint32(~(1 << 16) & 0xFFFFFFFF)) | np.uint32(self.phase << 16)
+            self.cq[self.tail] = e
+            self.log.append(e.copy())
+            self.tail += 1
+            if self.tail == self.depth:
+                self.tail = 0
+                self.phase ^= 1
