@@ -15,8 +15,9 @@ algorithmic bytes of one launch / its mean duration from HIP events recorded
 on the stream it runs on. `emit_sqe` times the stage after the path (NVMe
 submission entries for the first window of every queue) on the step's outputs,
 `registry` a batch of registrations and deregistrations on the device
-registration table, and `build_put` RDMA put descriptors for a VMM heap, all
-outside the timed steps. `cpu_baseline` times the single-threaded oracle on a
+registration table, `build_put` RDMA put descriptors for a VMM heap and
+`cq_mirror` the completion-queue mirror draining 64 full queues, all outside
+the timed steps. `cpu_baseline` times the single-threaded oracle on a
 bounded sample of the same workload.
 """
 from __future__ import annotations
@@ -188,6 +189,54 @@ def put_stage(dd, np, torch, n, reps):
             "descriptors_per_s": round(total / (mean * 1e-3), 1),
             "algorithmic_bytes_per_launch": nbytes, "achieved_gbs": round(gbs, 1),
             "frac": round(gbs / PEAK_HBM_GBS, 4)}
+
+
+def cq_stage(dd, np, torch, reps):
+    """Times dmadesc_cq_mirror draining 64 device-memory completion queues of
+    65,536 entries, each holding one full pass of completions when the call
+    starts (stop flag already set, so every wave leaves after its queue is
+    empty), into mirror queues in device memory and then in pinned host
+    memory (the host completion queues of the method). Slots are reset from a
+    copy before each timed call. Algorithmic bytes: per entry 16 read + 16
+    written."""
+    dev = torch.device("cuda:0")
+    nq, depth = dd.CQ_MAX_SLOTS, 65536
+    rng = np.random.default_rng(9)
+    e = rng.integers(0, 1 << 32, (nq, depth, 4), dtype=np.uint64).astype(np.uint32)
+    e[..., 3] |= np.uint32(1 << 16)                    # first pass: phase tag 1
+    src = torch.from_numpy(e.view(np.int32)).to(dev)
+    stop = torch.ones(1, dtype=torch.int32, device=dev).view(torch.uint32)
+    n = nq * depth
+    out = {"kernel": "k_cq_mirror", "queues": nq, "depth": depth, "entries_per_launch": n,
+           "algorithmic_bytes_per_launch": n * 32}
+    for where in ("device", "host"):
+        dst = (torch.zeros_like(src) if where == "device"
+               else torch.zeros(src.shape, dtype=torch.int32).pin_memory())
+        slots = dd.cq_slots(nq, dev)
+        for q in range(nq):
+            dd.cq_attach(slots, q, src[q], dst[q], depth, 1)
+        saved = slots.clone()
+        ms = []
+        for r in range(reps + 2):
+            slots.copy_(saved)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            dd.cq_mirror(slots, stop, idle_polls=1)
+            e1.record()
+            torch.cuda.synchronize()
+            if r >= 2:
+                ms.append(e0.elapsed_time(e1))
+        st = dd.cq_slot_state(slots)
+        ok = bool((st["copied"] == depth).all() and torch.equal(src.cpu(), dst.cpu()))
+        mean = float(np.mean(ms))
+        gbs = n * 32 / (mean * 1e-3) / 1e9
+        out[f"{where}_mirror"] = {
+            "mirrored_exactly": ok, "mean_launch_ms": round(mean, 4),
+            "entries_per_s": round(n / (mean * 1e-3), 1),
+            "us_per_poll": round(mean * 1e3 / (depth / 256), 3),
+            "achieved_gbs": round(gbs, 1), "frac": round(gbs / PEAK_HBM_GBS, 4)}
+        del dst
+    return out
 
 
 def registry_stage(dd, d, np, torch, reps):
@@ -491,6 +540,8 @@ def main():
         result["registry"] = registry_stage(dd, d, np, torch, 10)
     if args.emit_reps > 0:
         result["build_put"] = put_stage(dd, np, torch, n, args.emit_reps)
+    if args.emit_reps > 0:
+        result["cq_mirror"] = cq_stage(dd, np, torch, 10)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(args.workload, min(args.cpu_sample, n),
                                               args.cpu_seconds, args.layout)

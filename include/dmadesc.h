@@ -22,6 +22,12 @@
  *   dmadesc_build_put          RDMA put descriptors, one per chunk-bounded piece
  *                              (static heap or VMM heap with per-chunk keys)
  *
+ * the completion side:
+ *
+ *   dmadesc_cq_mirror          copy NVMe completions from device-memory
+ *                              completion queues to mirror queues as their
+ *                              phase bit turns (one wave per queue)
+ *
  * and the registration cache kept on the device:
  *
  *   dmadesc_reg_register       batch of registrations (page-rounded, refcounted)
@@ -352,6 +358,54 @@ int dmadesc_build_put(const uint64_t *src, const uint64_t *dst, const uint64_t *
                       const uint32_t *rkeys, uint32_t npes, dmadesc_put_desc *desc,
                       uint64_t desc_cap, uint64_t *first, uint32_t *count, uint8_t *status,
                       uint64_t *total, void *ws, size_t ws_bytes, void *stream);
+
+/* One mirrored completion queue (shared by host and device; 48 bytes). */
+#define DMADESC_CQ_MAX_SLOTS 64u
+#define DMADESC_CQ_MAX_DEPTH 65536u
+typedef struct dmadesc_cq_slot {
+    uint64_t src;          /* device address of the device-memory queue (16-byte aligned) */
+    uint64_t dst;          /* device-visible address of the mirror queue (16-byte aligned) */
+    uint32_t depth;        /* entries of 16 bytes, 2 .. 65536                          */
+    uint32_t generation;   /* host: odd while the queue is attached                    */
+    uint32_t ack;          /* mirror: generation it has finished with                  */
+    uint32_t head;         /* mirror state: next entry to copy (host sets 0 to attach)  */
+    uint32_t phase;        /* mirror state: phase the next entry carries (host sets 1)  */
+    uint32_t reserved;
+    uint64_t copied;       /* mirror: entries copied under the current attachment       */
+} dmadesc_cq_slot;
+
+/*
+ * dmadesc_cq_mirror - completion-queue mirror.
+ *
+ * [UPCIE] "Memory Architecture": one kernel serves every mirrored queue (up to
+ * 64) with one wave each and copies completions from the device-memory queue
+ * into the mirror queue as their phase bit turns (NVMe: phase tag = bit 16 of
+ * dword 3, 1 on the controller's first pass, inverted on each later pass).
+ * The host fills a slot (addresses, depth, head 0, phase 1, copied 0) and then
+ * raises its generation to an odd value; the wave copies until the generation
+ * changes, then writes the value it worked under to `ack`; a wave finding an
+ * even generation writes generation - 1. The host frees nothing of a queue
+ * before it sees that acknowledgement. A copied entry is first written whole
+ * with its old phase bit and only then, after a release, given dword 3 with
+ * the new one, so a consumer polling the mirror's phase bits never reads a
+ * partial entry; each poll's copies are released before the next poll.
+ *   slots       dmadesc_cq_slot[nslots] (device or host-mapped memory),
+ *               nslots 1..DMADESC_CQ_MAX_SLOTS
+ *   stop        u32 (device or host-mapped): nonzero asks the waves to leave
+ *               after one more drain
+ *   idle_polls  1..2^24: a wave also leaves after this many polls in a row
+ *               that copied nothing (a poll sleeps ~0.2 µs when idle)
+ * The call is one launch on `stream` that stays resident until every wave has
+ * left (at most 2^22 polls each); slots keep head, phase and copied, so the
+ * next call continues. A slot with an unusable description (depth, null or
+ * unaligned address, head >= depth) copies nothing and acknowledges nothing.
+ * Run it on a stream of its own: work on that stream waits for it, and so may
+ * work on a stream that shares its hardware queue. Errors: -EINVAL for a
+ * null or non-8-byte-aligned `slots`, a null `stop`, nslots or idle_polls out
+ * of range; -EIO if the launch fails.
+ */
+int dmadesc_cq_mirror(dmadesc_cq_slot *slots, uint32_t nslots, const uint32_t *stop,
+                      uint32_t idle_polls, void *stream);
 
 /* Registration cache limits and per-call outcomes. */
 #define DMADESC_REG_MAX_BATCH 65536u          /* calls per batch                  */

@@ -15,7 +15,8 @@ import torch
 from . import _build
 
 __all__ = ["mr_lookup", "build_prp", "build_prp_packed", "partition_by_queue", "emit_sqe",
-           "ring_addresses", "DeviceRegistry", "build_put",
+           "ring_addresses", "DeviceRegistry", "build_put", "cq_slots", "cq_attach",
+           "cq_mirror", "cq_slot_state",
            "workspace_bytes", "DmadescError", "lib", "LIB_PATH", "MAX_QUEUES",
            "SQ_MAX_DEPTH",
            "MISS", "EXACT", "CONTAINED", "INVALID",
@@ -49,6 +50,7 @@ _EXPORTS = {
                           _P, _P, _P, _P, _P, _P, _P, _P, _SIZE, _P], ctypes.c_int),
     "dmadesc_build_put": ([_P, _P, _P, _P, _U64, _U64, _U64, _U32, _P, _P, _P, _U32, _P, _U64,
                            _P, _P, _P, _P, _P, _SIZE, _P], ctypes.c_int),
+    "dmadesc_cq_mirror": ([_P, _U32, _P, _U32, _P], ctypes.c_int),
     "dmadesc_reg_register": ([_P, _P, _P, _P, _P, _P, _U64, _U32, _P, _P, _U64, _P, _P, _P,
                               _P, _SIZE, _P], ctypes.c_int),
     "dmadesc_reg_deregister": ([_P, _P, _P, _P, _P, _P, _U64, _P, _U64, _P, _P, _SIZE, _P],
@@ -274,6 +276,54 @@ def build_put(src: torch.Tensor, dst: torch.Tensor, nbytes: torch.Tensor, pe: to
         _stream(dev, stream))
     _check("dmadesc_build_put", rc)
     return out
+
+
+# dmadesc_cq_slot as 6 little-endian u64 words: src, dst, depth | generation
+# << 32, ack | head << 32, phase | reserved << 32, copied.
+CQ_SLOT_WORDS = 6
+CQ_MAX_SLOTS = 64
+
+
+def cq_slots(n: int, device="cuda") -> torch.Tensor:
+    """A zeroed table of n completion-queue mirror slots (u64[n, 6])."""
+    if not 1 <= n <= CQ_MAX_SLOTS:
+        raise ValueError(f"1..{CQ_MAX_SLOTS} slots")
+    return torch.zeros((n, CQ_SLOT_WORDS), dtype=torch.int64, device=device).view(torch.uint64)
+
+
+def cq_attach(slots: torch.Tensor, q: int, src: torch.Tensor, dst: torch.Tensor, depth: int,
+              generation: int, head: int = 0, phase: int = 1) -> None:
+    """Fills slot q (nothing copied; a fresh queue starts at head 0, phase 1)
+    and then raises its generation (odd), on the current stream. src/dst:
+    device tensors holding depth x 16 bytes."""
+    if generation % 2 != 1:
+        raise ValueError("an attached queue has an odd generation")
+    if src.numel() * src.element_size() < 16 * depth or dst.numel() * dst.element_size() < 16 * depth:
+        raise ValueError("src and dst must hold depth x 16 bytes")
+    words = torch.tensor([src.data_ptr(), dst.data_ptr(), depth, head << 32, phase, 0],
+                         dtype=torch.int64)
+    row = slots[q].view(torch.int64)
+    row.copy_(words.to(slots.device))
+    row[2:3].copy_(torch.tensor([depth | (generation << 32)], dtype=torch.int64).to(slots.device))
+
+
+def cq_mirror(slots: torch.Tensor, stop: torch.Tensor, idle_polls: int = 64, stream=None) -> None:
+    """One resident call of the completion-queue mirror over all slots."""
+    n = slots.shape[0]
+    if slots.dim() != 2 or slots.shape[1] != CQ_SLOT_WORDS:
+        raise ValueError("slots must be u64[n, 6]")
+    rc = lib().dmadesc_cq_mirror(_dev(slots, torch.uint64, "slots"), n,
+                                 _dev(stop, torch.uint32, "stop", 1), idle_polls,
+                                 _stream(slots.device, stream))
+    _check("dmadesc_cq_mirror", rc)
+
+
+def cq_slot_state(slots: torch.Tensor) -> dict:
+    """Host copy of every slot's generation, ack, head, phase and copied."""
+    w = slots.view(torch.int64).cpu().numpy().view("<u8")
+    return dict(depth=(w[:, 2] & 0xFFFFFFFF).astype("u4"), generation=(w[:, 2] >> 32).astype("u4"),
+                ack=(w[:, 3] & 0xFFFFFFFF).astype("u4"), head=(w[:, 3] >> 32).astype("u4"),
+                phase=(w[:, 4] & 0xFFFFFFFF).astype("u4"), copied=w[:, 5].copy())
 
 
 class DeviceRegistry:

@@ -175,6 +175,16 @@ int dmadesc_build_put(const uint64_t *src, const uint64_t *dst, const uint64_t *
     return launched(dd::launch_build_put(a, static_cast<hipStream_t>(stream)));
 }
 
+int dmadesc_cq_mirror(dmadesc_cq_slot *slots, uint32_t nslots, const uint32_t *stop,
+                      uint32_t idle_polls, void *stream)
+{
+    if (!slots || !stop || nslots == 0 || nslots > DMADESC_CQ_MAX_SLOTS) return -EINVAL;
+    if (idle_polls == 0 || idle_polls > (1u << 24)) return -EINVAL;
+    if (reinterpret_cast<uintptr_t>(slots) & 7u) return -EINVAL;
+    return launched(dd::launch_cq_mirror(slots, nslots, stop, idle_polls,
+                                         static_cast<hipStream_t>(stream)));
+}
+
 int dmadesc_reg_register(uint64_t *start, uint64_t *end, uint64_t *id, uint32_t *refs,
                          uint32_t *by_start, uint64_t *state, uint64_t capacity,
                          uint32_t page_shift, const uint64_t *addr, const uint64_t *size,

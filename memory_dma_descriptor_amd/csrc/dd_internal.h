@@ -6,6 +6,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "dmadesc.h"
+
 namespace dd {
 
 struct LookupArgs {
@@ -96,6 +98,8 @@ hipError_t launch_mr_lookup(const LookupArgs &a, hipStream_t s);
 hipError_t launch_build_prp(const PrpArgs &a, hipStream_t s);
 hipError_t launch_partition(const SplitArgs &a, hipStream_t s);
 hipError_t launch_emit_sqe(const SqeArgs &a, hipStream_t s);
+hipError_t launch_cq_mirror(dmadesc_cq_slot *slots, uint32_t nslots, const uint32_t *stop,
+                            uint32_t idle_polls, hipStream_t s);
 hipError_t launch_build_put(const PutArgs &a, hipStream_t s);
 hipError_t launch_reg_register(const RegArgs &a, hipStream_t s);
 hipError_t launch_reg_deregister(const RegArgs &a, hipStream_t s);

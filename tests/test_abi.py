@@ -167,6 +167,26 @@ def test_registry_rejects_bad_arguments():
         assert g(*args) == EINVAL, (k, bad)
 
 
+@no_gpu_only
+def test_cq_mirror_rejects_bad_arguments():
+    f = dd.lib().dmadesc_cq_mirror
+    ok = [P, 8, P, 64, NULL]
+    for k, bad in [(0, NULL), (0, P + 4), (1, 0), (1, 65), (2, NULL), (3, 0), (3, (1 << 24) + 1)]:
+        args = list(ok)
+        args[k] = bad
+        assert f(*args) == EINVAL, (k, bad)
+
+
+def test_cq_slot_layout():
+    # dmadesc_cq_slot is 48 bytes: two addresses, six u32 words, the count.
+    src = open(os.path.join(ROOT, "include", "dmadesc.h"), encoding="utf-8").read()
+    body = re.search(r"typedef struct dmadesc_cq_slot \{(.*?)\}", src, re.S).group(1)
+    fields = re.findall(r"(uint\d+)_t\s+(\w+);", body)
+    assert [n for _, n in fields] == ["src", "dst", "depth", "generation", "ack", "head",
+                                      "phase", "reserved", "copied"]
+    assert sum(int(t[4:]) // 8 for t, _ in fields) == 8 * dd.CQ_SLOT_WORDS
+
+
 def test_registry_workspace_sizes():
     ws = dd.workspace_bytes
     assert ws(dd.OP_REGISTRY, 65537, 64) == 0 and ws(dd.OP_REGISTRY, 1, (1 << 24) + 1) == 0
@@ -182,7 +202,8 @@ def test_empty_lookup_is_a_no_op():
 
 
 @pytest.mark.parametrize("name", ["mr_lookup", "build_prp", "build_prp_packed",
-                                  "partition_by_queue", "emit_sqe"])
+                                  "partition_by_queue", "emit_sqe", "build_put",
+                                  "cq_mirror"])
 def test_binding_names_match_abi(name):
     assert callable(getattr(dd, name))
     assert f"dmadesc_{name}" in _declared()
