@@ -326,6 +326,9 @@ struct PackTab {
     T m[kWave];                 // list entries (0: none)
     uint64_t f0[kWave];         // GPU page of PRP1, the first staged page
     uint32_t ph[kWave];         // 4 KiB page of data entry 0 counted from f0 (< 32)
+    uint4 rec[kWave];           // 32-bit rounds: {start, m, foff, ph} of each request
+    uint2 rec2[kWave];          // 32-bit rounds: {ph - start, foff} of each request
+    uint8_t mark[2 * kWave];    // 32-bit rounds: 1 + request whose list starts at a word
     uint64_t lut[kTileFrames];
 };
 union PackLds {
@@ -437,10 +440,107 @@ __device__ __forceinline__ void pack_groups(const PackTab<T> &P, uint64_t S, uin
     }
 }
 
+// Inclusive maximum over lanes 0..l of the wave (row shifts within rows of 16
+// lanes, then the row broadcasts of lanes 15 and 31).
+__device__ __forceinline__ uint32_t wave_incl_max(uint32_t x)
+{
+    x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xF, 0xF, false));
+    x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xF, 0xF, false));
+    x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xF, 0xF, false));
+    x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xF, 0xF, false));
+    x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xA, 0xF, false));
+    x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xC, 0xF, false));
+    return x;
+}
+
+// The value of lane l - 1 (0 in lane 0).
+__device__ __forceinline__ uint32_t wave_shr1(uint32_t x)
+{
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x138, 0xF, 0xF, false);
+}
+
+// Writes pool words [wlo, whi) of a packed round whose slots, relative to S,
+// fit 32 bits, in windows of 128 words: lane l writes words 2l and 2l + 1, so
+// each 16-byte store of the wave covers 1 KiB contiguously. A word's owner is
+// the last list that starts at or before it: every list marks its first word
+// in an LDS map of the window, and a prefix maximum across the wave (plus the
+// owner carried from the window before) hands each word its owner, with no
+// search. A non-511 word W holds slot W - W / 512, so entry t of its owner's
+// staged pages is (slot - S) + (ph - start). Word 511 (lane 63) and word 0
+// (lane 0) of a pool page get their special values in a branch taken only in
+// the windows that hold them. `wst` is the first word of this lane's list (a
+// value no window reaches when it has none); `first` is the first list lane.
+template <bool kStaged>
+__device__ __forceinline__ void pack_marks(PackTab<uint32_t> &P, uint64_t S, uint64_t wlo,
+                                           uint64_t whi, uint64_t wst, int first,
+                                           uint64_t lut_entries,
+                                           const uint64_t *__restrict__ lut,
+                                           uint64_t *__restrict__ pool, uint64_t bus)
+{
+    const uint32_t ln = (uint32_t)lane();
+    uint32_t carry = (uint32_t)first + 1;                    // owner mark before the window
+    uint16_t *mark16 = reinterpret_cast<uint16_t *>(P.mark);
+    for (uint64_t Wb = wlo & ~127ull; Wb < whi; Wb += 128) {
+        mark16[ln] = 0;
+        if (wst - Wb < 128) P.mark[wst - Wb] = (uint8_t)(ln + 1);
+        wave_sync_lds();
+        const uint32_t mk = mark16[ln];
+        const uint32_t m0 = mk & 0xFFu, m1 = mk >> 8;
+        const uint32_t pm = max(wave_incl_max(max(m0, m1)), carry);
+        const uint32_t o0 = max(max(wave_shr1(pm), carry), m0);   // owner mark of word 2l
+        const uint32_t o1 = max(o0, m1);                          // ... and of word 2l + 1
+        carry = (uint32_t)__builtin_amdgcn_readlane((int)pm, kWave - 1);
+        const int r0 = (int)o0 - 1, r1 = (int)o1 - 1;
+        const uint64_t W0 = Wb + 2 * ln, W1 = W0 + 1;
+        const bool in0 = W0 >= wlo && W0 < whi, in1 = W1 >= wlo && W1 < whi;
+        const uint2 a0 = P.rec2[r0], a1 = P.rec2[r1];
+        const uint32_t t0 = (uint32_t)(W0 - (W0 >> 9) - S) + a0.x;
+        const uint32_t t1 = (uint32_t)(W1 - (W1 >> 9) - S) + a1.x;
+        // Words outside the range are computed from entry 0 and never stored.
+        const uint32_t f0 = in0 ? t0 >> 4 : 0, f1 = in1 ? t1 >> 4 : 0;
+        uint64_t l0, l1;
+        if (kStaged) {
+            l0 = P.lut[(a0.y + f0) & (kTileFrames - 1)];
+            l1 = P.lut[(a1.y + f1) & (kTileFrames - 1)];
+        } else {
+            const uint64_t i0 = P.f0[r0] + f0, i1 = P.f0[r1] + f1;
+            l0 = lut[i0 < lut_entries ? i0 : 0];
+            l1 = lut[i1 < lut_entries ? i1 : 0];
+        }
+        uint64_t v0 = l0 + ((uint64_t)(t0 & 15u) << 12);
+        uint64_t v1 = l1 + ((uint64_t)(t1 & 15u) << 12);
+        if ((Wb & 511u) == 384u && ln == kWave - 1) {
+            // Word 511: the owner of slot 510 writes a chain pointer if two or
+            // more of its entries remain, its final entry if exactly one does
+            // (v1 is then that entry), else 0.
+            const uint4 R = P.rec[r1];
+            const uint32_t rem = R.y - ((uint32_t)(W1 - 1 - (W1 >> 9) - S) - R.x) - 1;
+            if (rem >= 2) v1 = bus + (((W1 >> 9) + 1) << 12);
+            else if (rem == 0) v1 = 0;
+        }
+        if ((Wb & 511u) == 0u && ln == 0) {
+            // Word 0: 0 when its slot's entry is its owner's final one, which
+            // then sits in word 511 of the page before.
+            const uint4 R = P.rec[r0];
+            const uint32_t j = (uint32_t)(W0 - (W0 >> 9) - S) - R.x;
+            if (j > 0 && j == R.y - 1) v0 = 0;
+        }
+        // Non-temporal: the list words are not read again by this kernel.
+        if (in0 && in1) {
+            __builtin_nontemporal_store(u64x2{v0, v1}, reinterpret_cast<u64x2 *>(pool + W0));
+        } else {
+            if (in0) __builtin_nontemporal_store(v0, pool + W0);
+            if (in1) __builtin_nontemporal_store(v1, pool + W1);
+        }
+        wave_sync_lds();                                     // the map is rewritten next
+    }
+}
+
 template <typename T>
 __device__ __forceinline__ void emit_packed_t(PackTab<T> &P, uint64_t d, uint64_t m,
-                                              uint64_t S, uint64_t E, uint64_t o, uint64_t xb,
-                                              uint64_t last_frame, uint64_t *prp1,
+                                              uint64_t S, uint64_t E, int first, uint64_t o,
+                                              uint64_t xb, uint64_t last_frame, uint64_t *prp1,
+                                              uint64_t lut_entries,
                                               const uint64_t *__restrict__ lut,
                                               uint64_t *__restrict__ pool, uint64_t bus)
 {
@@ -458,12 +558,18 @@ __device__ __forceinline__ void emit_packed_t(PackTab<T> &P, uint64_t d, uint64_
     P.m[ln] = (T)m;
     P.f0[ln] = f0;
     P.ph[ln] = (uint32_t)((xb >> 12) & 15u) + (uint32_t)(((xb >> 16) - f0) << 4);
+    if constexpr (std::is_same<T, uint32_t>::value) {
+        const uint32_t ph = (uint32_t)((xb >> 12) & 15u) + (uint32_t)(((xb >> 16) - f0) << 4);
+        P.rec[ln] = make_uint4((uint32_t)rs, (uint32_t)m, (uint32_t)(finc - frames), ph);
+        P.rec2[ln] = make_uint2(ph - (uint32_t)rs, (uint32_t)(finc - frames));
+    }
     if (ln == kWave - 1) {
         P.start[kWave] = (T)(E - S);
         P.foff[kWave] = (T)finc;
     }
     wave_sync_lds();
     const uint64_t wlo = S + S / 511, whi = E + E / 511;
+    const uint64_t wst = m ? d + d / 511 : ~0ull;            // first word of this lane's list
     if (ftot <= (uint64_t)kTileFrames) {
         for (uint32_t j0 = 0; j0 < (uint32_t)ftot; j0 += 4 * kWave) {
             uint64_t v[4];
@@ -483,10 +589,16 @@ __device__ __forceinline__ void emit_packed_t(PackTab<T> &P, uint64_t d, uint64_
         wave_sync_lds();
         if (m && prp1)
             __builtin_nontemporal_store(P.lut[P.foff[ln]] + (o & 0xFFFFu), prp1);
-        pack_groups<T, true>(P, S, wlo, whi, lut, pool, bus);
+        if constexpr (std::is_same<T, uint32_t>::value)
+            pack_marks<true>(P, S, wlo, whi, wst, first, lut_entries, lut, pool, bus);
+        else
+            pack_groups<T, true>(P, S, wlo, whi, lut, pool, bus);
     } else {
         if (m && prp1) __builtin_nontemporal_store(lut[f0] + (o & 0xFFFFu), prp1);
-        pack_groups<T, false>(P, S, wlo, whi, lut, pool, bus);
+        if constexpr (std::is_same<T, uint32_t>::value)
+            pack_marks<false>(P, S, wlo, whi, wst, first, lut_entries, lut, pool, bus);
+        else
+            pack_groups<T, false>(P, S, wlo, whi, lut, pool, bus);
     }
     wave_sync_lds();                                         // the next round rewrites P
 }
@@ -496,7 +608,7 @@ __device__ __forceinline__ void emit_packed_t(PackTab<T> &P, uint64_t d, uint64_
 // no list), and PRP1 of each request with a list.
 __device__ __forceinline__ void emit_round_packed(PackLds &L, uint64_t d, uint64_t m,
                                                   uint64_t o, uint64_t xb, uint64_t last_frame,
-                                                  uint64_t *prp1,
+                                                  uint64_t *prp1, uint64_t lut_entries,
                                                   const uint64_t *__restrict__ lut,
                                                   uint64_t *__restrict__ pool, uint64_t bus)
 {
@@ -507,9 +619,11 @@ __device__ __forceinline__ void emit_round_packed(PackLds &L, uint64_t d, uint64
     const uint64_t S = __shfl(d, first, kWave);
     const uint64_t E = __shfl(d + m, last, kWave);
     if (E - S < (1ull << 31))
-        emit_packed_t<uint32_t>(L.fast, d, m, S, E, o, xb, last_frame, prp1, lut, pool, bus);
+        emit_packed_t<uint32_t>(L.fast, d, m, S, E, first, o, xb, last_frame, prp1, lut_entries,
+                                lut, pool, bus);
     else
-        emit_packed_t<uint64_t>(L.wide, d, m, S, E, o, xb, last_frame, prp1, lut, pool, bus);
+        emit_packed_t<uint64_t>(L.wide, d, m, S, E, first, o, xb, last_frame, prp1, lut_entries,
+                                lut, pool, bus);
 }
 
 template <bool kPacked>
@@ -658,7 +772,7 @@ __global__ __launch_bounds__(kThreads, 4) void k_prp_build(
         const uint64_t last_frame = (o[k] + l[k] - 1) >> 16;
         if constexpr (kPacked)
             emit_round_packed(s_round[w], slot, lists ? cnt : 0, o[k], xb, last_frame,
-                              i < n ? prp1 + i : nullptr, lut, pool, bus);
+                              i < n ? prp1 + i : nullptr, heap >> 16, lut, pool, bus);
         else
             emit_round(s_round[w], xb, slot << 9, lists ? (pages - 1) + (cnt - 1) : 0,
                        lists ? cnt : 0, last_frame, lut, pool, bus);
