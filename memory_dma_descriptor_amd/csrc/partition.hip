@@ -19,7 +19,7 @@
 // read as kItems rounds of 64 consecutive requests, so equal ids meet in
 // (wave, round, lane) order -- request order.
 //
-// Kernels: k_split_hist (per-block bucket counts, block-major),
+// Kernels: k_split_hist (per-block bucket counts, bucket-major),
 // k_split_colscan (one block per bucket: exclusive scan over blocks),
 // k_split_scatter (ranks, a block-local stable sort in LDS, then perm written
 // as contiguous runs, one per bucket, so stores coalesce).
@@ -51,47 +51,78 @@ __device__ __forceinline__ uint32_t bucket_of(const uint32_t *__restrict__ qid, 
     return q < nq ? q : nq;
 }
 
+// Buckets of a thread's kItems requests base + 64 k. In a tile that lies
+// wholly inside the batch (every tile but the last) the loads carry no
+// condition, so all of them are in flight at once; a guarded load would wait
+// for each before issuing the next.
+__device__ __forceinline__ void load_buckets(const uint32_t *__restrict__ qid, uint64_t base,
+                                             uint64_t n, uint32_t nq, bool full,
+                                             uint32_t (&b)[kItems])
+{
+    if (full) {
+#pragma unroll
+        for (int k = 0; k < kItems; ++k) b[k] = qid[base + (uint64_t)k * kWave];
+#pragma unroll
+        for (int k = 0; k < kItems; ++k) b[k] = b[k] < nq ? b[k] : nq;
+    } else {
+#pragma unroll
+        for (int k = 0; k < kItems; ++k) b[k] = bucket_of(qid, base + (uint64_t)k * kWave, n, nq);
+    }
+}
+
+// Copies of the block histogram: lane l adds into copy l % kCopies, so the
+// lanes of a wave that share a popular queue spread over kCopies addresses
+// instead of serializing on one (the copies lie in different LDS banks).
+constexpr int kCopies = 8;
+
 __global__ __launch_bounds__(kThreads) void k_split_hist(
-    const uint32_t *__restrict__ qid, uint64_t n, uint32_t nq,
+    const uint32_t *__restrict__ qid, uint64_t n, uint32_t nq, uint64_t nb,
     uint32_t *__restrict__ counts)
 {
-    __shared__ uint32_t h[kMaxBuckets];
+    __shared__ uint32_t h[kCopies][kMaxBuckets];
     const uint32_t nbk = nq + 1;
-    for (uint32_t b = threadIdx.x; b < nbk; b += kThreads) h[b] = 0;
+    for (uint32_t b = threadIdx.x; b < kCopies * kMaxBuckets; b += kThreads) (&h[0][0])[b] = 0;
     __syncthreads();
-    // Counts only (no ranks), so plain LDS atomics suffice here.
+    // Counts only (no ranks), so LDS atomics suffice here.
     const uint64_t base = (uint64_t)blockIdx.x * kTile + (uint64_t)wave() * kWaveItems + lane();
+    uint32_t *hc = h[lane() % kCopies];
     uint32_t b[kItems];
-#pragma unroll
-    for (int k = 0; k < kItems; ++k) b[k] = bucket_of(qid, base + (uint64_t)k * kWave, n, nq);
+    load_buckets(qid, base, n, nq, (uint64_t)(blockIdx.x + 1) * kTile <= n, b);
 #pragma unroll
     for (int k = 0; k < kItems; ++k)
-        if (base + (uint64_t)k * kWave < n) atomicAdd(&h[b[k]], 1u);
+        if (base + (uint64_t)k * kWave < n) atomicAdd(&hc[b[k]], 1u);
     __syncthreads();
-    uint32_t *row = counts + (uint64_t)blockIdx.x * nbk;       // block-major
-    for (uint32_t k = threadIdx.x; k < nbk; k += kThreads) row[k] = h[k];
+    // Bucket-major: bucket k's counts over all blocks are contiguous.
+    for (uint32_t k = threadIdx.x; k < nbk; k += kThreads) {
+        uint32_t c = 0;
+#pragma unroll
+        for (int j = 0; j < kCopies; ++j) c += h[j][k];
+        counts[(uint64_t)k * nb + blockIdx.x] = c;
+    }
 }
 
 // One block per bucket: in-place exclusive scan of that bucket's per-block
-// counts (a column of the block-major matrix) and the bucket total.
+// counts (one contiguous row of the bucket-major matrix) and the bucket
+// total. Thread t takes a contiguous segment of the row; all its loads are
+// issued before the first is used.
 __global__ __launch_bounds__(kThreads) void k_split_colscan(
     uint32_t *__restrict__ counts, uint64_t nb, uint32_t nbk, uint64_t *__restrict__ total)
 {
     __shared__ uint64_t scratch[kWaves];
-    const uint32_t col = blockIdx.x;
+    uint32_t *row = counts + (uint64_t)blockIdx.x * nb;
     const uint64_t seg = (nb + kThreads - 1) / kThreads;
     const uint64_t b0 = (uint64_t)threadIdx.x * seg;
     const uint64_t b1 = (b0 + seg < nb) ? b0 + seg : nb;
     uint64_t s = 0;
-    for (uint64_t k = b0; k < b1; ++k) s += counts[k * nbk + col];
+    for (uint64_t k = b0; k < b1; ++k) s += row[k];
     uint64_t tot;
     uint64_t run = block_excl_scan<kThreads>(s, scratch, &tot);
     for (uint64_t k = b0; k < b1; ++k) {
-        const uint32_t c = counts[k * nbk + col];
-        counts[k * nbk + col] = (uint32_t)run;
+        const uint32_t c = row[k];
+        row[k] = (uint32_t)run;
         run += c;
     }
-    if (threadIdx.x == 0) total[col] = tot;
+    if (threadIdx.x == 0) total[blockIdx.x] = tot;
 }
 
 __global__ __launch_bounds__(kThreads) void k_split_scatter(
@@ -120,8 +151,7 @@ __global__ __launch_bounds__(kThreads) void k_split_scatter(
     const uint64_t base = tile + (uint64_t)w * kWaveItems + ln;
     const uint64_t below = __lanemask_lt();
     uint32_t b[kItems], rank[kItems];
-#pragma unroll
-    for (int k = 0; k < kItems; ++k) b[k] = bucket_of(qid, base + (uint64_t)k * kWave, n, nq);
+    load_buckets(qid, base, n, nq, (uint64_t)(blockIdx.x + 1) * kTile <= n, b);
 #pragma unroll
     for (int k = 0; k < kItems; ++k) {
         const bool on = base + (uint64_t)k * kWave < n;
@@ -163,7 +193,7 @@ __global__ __launch_bounds__(kThreads) void k_split_scatter(
         if (bk < nbk) {
             const uint64_t gbase = gex + (h ? pair_off[0] : 0);
             s_lstart[bk] = (uint32_t)(lex + (h ? pair_tot[0] : 0));
-            s_gpos[bk] = gbase + offs[(uint64_t)blockIdx.x * nbk + bk];
+            s_gpos[bk] = gbase + offs[(uint64_t)bk * gridDim.x + blockIdx.x];
             if (blockIdx.x == 0) qoff[bk] = gbase;
         }
     }
@@ -219,7 +249,7 @@ hipError_t launch_partition(const SplitArgs &a, hipStream_t s)
     uint64_t *total = reinterpret_cast<uint64_t *>(
         static_cast<char *>(a.ws) + align256((uint64_t)nbk * nb * sizeof(uint32_t)));
     hipLaunchKernelGGL(k_split_hist, dim3((unsigned)nb), dim3(kThreads), 0, s,
-                       a.qid, a.n, a.nqueues, counts);
+                       a.qid, a.n, a.nqueues, nb, counts);
     hipLaunchKernelGGL(k_split_colscan, dim3(nbk), dim3(kThreads), 0, s,
                        counts, nb, nbk, total);
     hipLaunchKernelGGL(k_split_scatter, dim3((unsigned)nb), dim3(kThreads), 0, s,
