@@ -172,12 +172,20 @@ __global__ __launch_bounds__(kThreads) void k_sqe_count(SqeArgs a, SqeWs ws)
         const uint32_t j = k * kThreads + threadIdx.x;
         idx[k] = j < cnt ? pos[j] : UINT32_MAX;
     }
-    uint32_t c = 0;
+    // Gathers from a clamped index, all issued before any is used (a load
+    // behind an i < n branch would wait for the one before it).
+    uint8_t st[kRounds];
+    uint64_t len[kRounds];
 #pragma unroll
     for (int k = 0; k < kRounds; ++k) {
-        const uint32_t i = idx[k];
-        if (i < a.n && placeable(a.status[i], a.len[i], a.lba_shift)) ++c;
+        const uint32_t i = idx[k] < a.n ? idx[k] : 0u;
+        st[k] = a.status[i];
+        len[k] = a.len[i];
     }
+    uint32_t c = 0;
+#pragma unroll
+    for (int k = 0; k < kRounds; ++k)
+        c += (idx[k] < a.n && placeable(st[k], len[k], a.lba_shift)) ? 1u : 0u;
     c = wave_sum(c);
     if (lane() == 0) s_sum[wave()] = c;
     __syncthreads();
