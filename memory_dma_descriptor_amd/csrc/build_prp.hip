@@ -653,61 +653,11 @@ __global__ __launch_bounds__(kThreads, 4) void k_prp_build(
         o[k] = i < n ? __builtin_nontemporal_load(off + i) : 0;
         l[k] = i < n ? __builtin_nontemporal_load(len + i) : 0;   // len 0 decodes as invalid
     }
-    // PRP1, a two-page PRP2 and the status do not depend on the list pages,
-    // so they are written before the scan and overlap it. A request later
-    // refused for lack of pool pages is rewritten below. The table reads are
-    // branch-free (index 0 stands in for a request that needs none) so that
-    // all of them are in flight together.
-    if (heap != 0) {
-        uint64_t i1[kItems], i2[kItems], v1[kItems], v2[kItems];
-#pragma unroll
-        for (int k = 0; k < kItems; ++k) {
-            uint64_t pages;
-            const uint8_t st = decode(o[k], l[k], heap, pages);
-            const uint64_t x = (o[k] & ~4095ull) + 4096;
-            // Packed lists stage their request's table entries from PRP1's
-            // GPU page on, so PRP1 of a list request is taken from there.
-            const bool staged_prp1 = kPacked && pages >= 3;
-            i1[k] = (st == kOk && !staged_prp1) ? o[k] >> 16 : 0;
-            i2[k] = (st == kOk && pages == 2) ? x >> 16 : 0;
-        }
-#pragma unroll
-        for (int k = 0; k < kItems; ++k) {
-            v1[k] = lut[i1[k]];
-            v2[k] = lut[i2[k]];
-        }
-#pragma unroll
-        for (int k = 0; k < kItems; ++k) {
-            const uint64_t i = base + (uint64_t)k * kThreads + t;
-            uint64_t pages;
-            const uint8_t st = decode(o[k], l[k], heap, pages);
-            if (i < n) {
-                // Output columns and input columns are streamed (non-temporal):
-                // neither is read again by this kernel.
-                if (!(kPacked && st == kOk && pages >= 3))
-                    __builtin_nontemporal_store(st == kOk ? v1[k] + (o[k] & 0xFFFFu) : 0, prp1 + i);
-                if (pages < 3)
-                    __builtin_nontemporal_store((st == kOk && pages == 2) ?
-                        v2[k] + (((o[k] & ~4095ull) + 4096) & 0xFFFFu) : 0, prp2 + i);
-                __builtin_nontemporal_store(st, status + i);
-            }
-        }
-    } else {
-#pragma unroll
-        for (int k = 0; k < kItems; ++k) {                  // no heap: every request is ERANGE
-            const uint64_t i = base + (uint64_t)k * kThreads + t;
-            uint64_t pages;
-            const uint8_t st = decode(o[k], l[k], heap, pages);
-            if (i < n) {
-                prp1[i] = 0;
-                prp2[i] = 0;
-                status[i] = st;
-            }
-        }
-    }
     // Scanned per request: list pages (page layout) or list entries (packed).
     // Request order is (item, wave, lane): wave scans per item, then one
-    // barrier to combine the waves' totals.
+    // barrier to combine the waves' totals. The scan needs only the request
+    // columns, so it comes first and the block's aggregate is published
+    // before any table read: blocks looking back at this one wait less.
 #pragma unroll
     for (int k = 0; k < kItems; ++k) {
         uint64_t pages;
@@ -732,18 +682,57 @@ __global__ __launch_bounds__(kThreads, 4) void k_prp_build(
         pre[k] += agg + before;
         agg += all;
     }
+    if (w == 0 && ln == 0) store_status(bstat + b, (b == 0 ? kFlagInc : kFlagAgg) | agg);
+
+    // PRP1, a two-page PRP2 and the status do not depend on the list pages.
+    // The table reads are branch-free (index 0 stands in for a request that
+    // needs none) so that all of them are in flight together; waves 1..3
+    // issue theirs before wave 0 looks back, wave 0 after (its look-back
+    // polls would otherwise wait for its table reads). A request later
+    // refused for lack of pool pages is rewritten below.
+    uint64_t v1[kItems], v2[kItems];
+    auto gather = [&]() {
+#pragma unroll
+        for (int k = 0; k < kItems; ++k) {
+            uint64_t pages;
+            const uint8_t st = decode(o[k], l[k], heap, pages);
+            const uint64_t x = (o[k] & ~4095ull) + 4096;
+            // Packed lists stage their request's table entries from PRP1's
+            // GPU page on, so PRP1 of a list request is taken from there.
+            const bool staged_prp1 = kPacked && pages >= 3;
+            const uint64_t i1 = (st == kOk && !staged_prp1) ? o[k] >> 16 : 0;
+            const uint64_t i2 = (st == kOk && pages == 2) ? x >> 16 : 0;
+            v1[k] = heap ? lut[i1] : 0;
+            v2[k] = heap ? lut[i2] : 0;
+        }
+    };
+    if (w != 0) gather();
     if (w == 0) {
         uint64_t excl = 0;
-        if (b == 0) {
-            if (ln == 0) store_status(bstat, kFlagInc | agg);
-        } else {
-            if (ln == 0) store_status(bstat + b, kFlagAgg | agg);
+        if (b != 0) {
             excl = look_back(bstat, (int64_t)b, &hdr->timeouts);
             if (ln == 0) store_status(bstat + b, kFlagInc | (excl + agg));
         }
         if (ln == 0) {
             s_excl = excl;
             if (b == nblocks - 1) *total = kPacked ? (excl + agg + 510) / 511 : excl + agg;
+        }
+        gather();
+    }
+#pragma unroll
+    for (int k = 0; k < kItems; ++k) {
+        const uint64_t i = base + (uint64_t)k * kThreads + t;
+        uint64_t pages;
+        const uint8_t st = decode(o[k], l[k], heap, pages);
+        if (i < n) {
+            // Output columns and input columns are streamed (non-temporal):
+            // neither is read again by this kernel.
+            if (!(kPacked && st == kOk && pages >= 3))
+                __builtin_nontemporal_store(st == kOk ? v1[k] + (o[k] & 0xFFFFu) : 0, prp1 + i);
+            if (pages < 3)
+                __builtin_nontemporal_store((st == kOk && pages == 2) ?
+                    v2[k] + (((o[k] & ~4095ull) + 4096) & 0xFFFFu) : 0, prp2 + i);
+            __builtin_nontemporal_store(st, status + i);
         }
     }
     __syncthreads();
