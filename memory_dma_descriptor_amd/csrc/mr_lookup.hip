@@ -9,11 +9,14 @@
 // Layout: one lane per request over structure-of-arrays columns, so each
 // column load/store of a wave is one contiguous 64-element run. Two kernels:
 //
-//  * k_lookup_lds, for tables that fit in LDS (20 bytes per region; MI355X
-//    has 160 KiB of LDS per CU): every block copies the whole table into
-//    LDS once and then answers requests in a grid-stride loop; the search
-//    and the start/end/lkey reads of the chosen region are all LDS reads, so
-//    no random global gathers reach the texture address unit.
+//  * k_lookup_lds, for tables of up to 4,096 regions (20 bytes per region;
+//    MI355X has 160 KiB of LDS per CU): one 1,024-thread block per CU copies
+//    the whole table into LDS once, builds a bucket index over the region
+//    starts, and then answers requests in a grid-stride loop. A query reads
+//    two index entries and searches only its bucket's run of regions (one or
+//    two on evenly spread tables) instead of the whole table: a wave's random
+//    LDS reads then collide in far fewer banks. All table reads are LDS
+//    reads, so no random global gathers reach the texture address unit.
 //  * k_lookup_split, for larger tables: every block stages every S-th
 //    region start (S a power of two, at most kMaxSplitters splitters = 64 KiB)
 //    in LDS; a lane searches the splitters in LDS, then the <= S starts of the
@@ -28,7 +31,8 @@ namespace dd {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kThreadsLds = 512;
+constexpr int kThreadsLds = 1024;            // one block per CU: 16 waves
+constexpr uint32_t kBuckets = 4096;          // bucket index over the region starts (LDS kernel)
 constexpr int kPerLane = 4;                  // requests per lane per trip (LDS kernel)
 
 typedef uint64_t u64x2 __attribute__((ext_vector_type(2)));
@@ -87,10 +91,42 @@ __global__ __launch_bounds__(kThreadsLds) void k_lookup_lds(
     uint64_t *s_start = lds;
     uint64_t *s_end = lds + nregions;
     uint32_t *s_key = reinterpret_cast<uint32_t *>(lds + 2 * (uint64_t)nregions);
+    uint16_t *s_idx = reinterpret_cast<uint16_t *>(s_key + nregions + (nregions & 1));
     for (uint32_t k = threadIdx.x; k < nregions; k += kThreadsLds) {
         s_start[k] = rs[k];
         s_end[k] = re[k];
         s_key[k] = rk[k];
+    }
+    __syncthreads();
+    // Bucket index: the starts' span [base, last start] cut into kBuckets
+    // buckets of 2^bs bytes; s_idx[b] = first region whose start is at or
+    // past bucket b. The last region starting at or before x then lies in
+    // [s_idx[b] - 1, s_idx[b + 1]) for x's bucket b: a query reads two index
+    // entries and searches that short run (usually one or two regions)
+    // instead of the whole table, so far fewer of a wave's random LDS reads
+    // collide in the same banks.
+    const uint64_t base = nregions ? s_start[0] : 0;
+    uint32_t bs = 0;
+    if (nregions) {
+        const uint64_t span = s_start[nregions - 1] - base;
+        while ((span >> bs) >= kBuckets) ++bs;
+        for (uint32_t b = threadIdx.x; b <= kBuckets; b += kThreadsLds) {
+            // Start of bucket b, saturating at 2^64 - 1 (then no region is past it).
+            const bool over = bs && ((uint64_t)b >> (64 - bs)) != 0;
+            const uint64_t width = over ? ~0ull : (uint64_t)b << bs;
+            const uint64_t x = width > ~base ? ~0ull : base + width;
+            uint32_t lo = 0, cnt = nregions;                  // first start >= x
+            while (cnt > 0) {
+                const uint32_t half = cnt >> 1;
+                if (s_start[lo + half] < x) {
+                    lo += half + 1;
+                    cnt -= half + 1;
+                } else {
+                    cnt = half;
+                }
+            }
+            s_idx[b] = (uint16_t)lo;
+        }
     }
     __syncthreads();
 
@@ -106,10 +142,11 @@ __global__ __launch_bounds__(kThreadsLds) void k_lookup_lds(
         const bool whole = aligned && i0 + kPerLane <= n;
         uint64_t o[kPerLane], l[kPerLane];
         if (whole) {
-            const u64x2 oa = *reinterpret_cast<const u64x2 *>(off + i0);
-            const u64x2 ob = *reinterpret_cast<const u64x2 *>(off + i0 + 2);
-            const u64x2 la = *reinterpret_cast<const u64x2 *>(len + i0);
-            const u64x2 lb = *reinterpret_cast<const u64x2 *>(len + i0 + 2);
+            // Columns are streamed (non-temporal): nothing reads them again.
+            const u64x2 oa = __builtin_nontemporal_load(reinterpret_cast<const u64x2 *>(off + i0));
+            const u64x2 ob = __builtin_nontemporal_load(reinterpret_cast<const u64x2 *>(off + i0 + 2));
+            const u64x2 la = __builtin_nontemporal_load(reinterpret_cast<const u64x2 *>(len + i0));
+            const u64x2 lb = __builtin_nontemporal_load(reinterpret_cast<const u64x2 *>(len + i0 + 2));
             o[0] = oa.x; o[1] = oa.y; o[2] = ob.x; o[3] = ob.y;
             l[0] = la.x; l[1] = la.y; l[2] = lb.x; l[3] = lb.y;
         } else {
@@ -129,8 +166,12 @@ __global__ __launch_bounds__(kThreadsLds) void k_lookup_lds(
             h[k] = -1;
             key[k] = 0;
             kd[k] = ok ? 0 : 3;                  // MISS : INVALID
-            if (ok && nregions > 0 && s_start[0] <= lo[k]) {
-                const uint32_t r = (uint32_t)last_le(s_start, nregions, lo[k]);
+            if (ok && nregions > 0 && base <= lo[k]) {
+                uint64_t b = (lo[k] - base) >> bs;
+                b = b < kBuckets ? b : kBuckets - 1;
+                const uint32_t i0 = s_idx[b], i1 = s_idx[b + 1];
+                const uint32_t first = i0 ? i0 - 1 : 0;
+                const uint32_t r = first + (uint32_t)last_le(s_start + first, i1 - first, lo[k]);
                 const uint64_t e = s_end[r];
                 if (hi[k] <= e) {
                     h[k] = (int32_t)r;
@@ -140,15 +181,17 @@ __global__ __launch_bounds__(kThreadsLds) void k_lookup_lds(
             }
         }
         if (whole) {
-            *reinterpret_cast<i32x4 *>(handle + i0) = i32x4{h[0], h[1], h[2], h[3]};
-            *reinterpret_cast<u32x4 *>(lkey + i0) = u32x4{key[0], key[1], key[2], key[3]};
-            *reinterpret_cast<uint32_t *>(kind + i0) =
-                (uint32_t)kd[0] | ((uint32_t)kd[1] << 8) | ((uint32_t)kd[2] << 16) |
-                ((uint32_t)kd[3] << 24);
-            *reinterpret_cast<u64x2 *>(rbase + i0) = u64x2{lo[0], lo[1]};
-            *reinterpret_cast<u64x2 *>(rbase + i0 + 2) = u64x2{lo[2], lo[3]};
-            *reinterpret_cast<u64x2 *>(rend + i0) = u64x2{hi[0], hi[1]};
-            *reinterpret_cast<u64x2 *>(rend + i0 + 2) = u64x2{hi[2], hi[3]};
+            __builtin_nontemporal_store(i32x4{h[0], h[1], h[2], h[3]},
+                                        reinterpret_cast<i32x4 *>(handle + i0));
+            __builtin_nontemporal_store(u32x4{key[0], key[1], key[2], key[3]},
+                                        reinterpret_cast<u32x4 *>(lkey + i0));
+            __builtin_nontemporal_store((uint32_t)kd[0] | ((uint32_t)kd[1] << 8) |
+                                            ((uint32_t)kd[2] << 16) | ((uint32_t)kd[3] << 24),
+                                        reinterpret_cast<uint32_t *>(kind + i0));
+            __builtin_nontemporal_store(u64x2{lo[0], lo[1]}, reinterpret_cast<u64x2 *>(rbase + i0));
+            __builtin_nontemporal_store(u64x2{lo[2], lo[3]}, reinterpret_cast<u64x2 *>(rbase + i0 + 2));
+            __builtin_nontemporal_store(u64x2{hi[0], hi[1]}, reinterpret_cast<u64x2 *>(rend + i0));
+            __builtin_nontemporal_store(u64x2{hi[2], hi[3]}, reinterpret_cast<u64x2 *>(rend + i0 + 2));
         } else {
 #pragma unroll
             for (int k = 0; k < kPerLane; ++k)
@@ -210,15 +253,17 @@ hipError_t launch_mr_lookup(const LookupArgs &a, hipStream_t s)
         e = hipDeviceGetAttribute(&lds_max, hipDeviceAttributeSharedMemPerBlockOptin, dev);
     if (e != hipSuccess) return e;
 
-    const size_t table_bytes = (size_t)a.nregions * 20;
-    if (table_bytes <= (size_t)lds_max / 2) {
-        // Two blocks per CU share its LDS; each answers a grid-stride share.
+    const size_t table_bytes = (size_t)a.nregions * 20 + (a.nregions & 1) * 4 +
+                               (size_t)(kBuckets + 1) * sizeof(uint16_t);
+    if (a.nregions <= 4096 && table_bytes <= (size_t)lds_max) {
+        // One 1,024-thread block per CU holds the table and its bucket index;
+        // each answers a grid-stride share.
         const size_t bytes = table_bytes;
         e = hipFuncSetAttribute(reinterpret_cast<const void *>(k_lookup_lds),
                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
         if (e != hipSuccess) return e;
         uint64_t blocks = (a.n + (uint64_t)kThreadsLds * kPerLane - 1) / ((uint64_t)kThreadsLds * kPerLane);
-        const uint64_t cap = 2ull * (uint64_t)cus;
+        const uint64_t cap = (uint64_t)cus;
         if (blocks > cap) blocks = cap;
         // Columns that allow 16-byte accesses (4-byte for kind) take the
         // vector path; any other alignment is served element by element.

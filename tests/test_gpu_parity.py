@@ -242,6 +242,75 @@ def test_lookup_tables(count, page_shift):
                     ctx=f"R={count} shift={page_shift}")
 
 
+def _spread_table(kind, count, rng):
+    """Tables whose starts span very different ranges: the LDS kernel buckets
+    the span between the first and the last start."""
+    if kind == "wide":            # starts spread over almost the whole 2^64 range
+        step = ((1 << 64) - (1 << 32)) // max(count, 1)
+        start = [4096 + i * (step & ~0xFFF) for i in range(count)]
+        size = [4096 * int(rng.integers(1, 64)) for _ in range(count)]
+    elif kind == "skewed":        # nearly all regions in one bucket, a few far away
+        start, cur = [], 0x1000
+        for i in range(count):
+            if i in (count // 3, 2 * count // 3, count - 1):
+                cur += 1 << 44
+            start.append(cur)
+            cur += 4096 * int(rng.integers(1, 4))
+        size = [4096] * count
+    else:                         # "even": one region per equal slot
+        start = [0x7000_0000_0000 + i * (1 << 26) + 4096 * int(rng.integers(0, 16))
+                 for i in range(count)]
+        size = [4096 * int(rng.integers(1, 1024)) for _ in range(count)]
+    start = np.array(start, np.uint64)
+    end = np.minimum(start.astype(object) + np.array(size, dtype=object), (1 << 64) - 4096)
+    return start, np.array(end, dtype=np.uint64)
+
+
+def _queries_u64(rng, start, end, n):
+    """Query mix of _queries in Python integers (addresses up to 2^64): whole
+    regions, ranges inside one, ranges across an edge, and ranges anywhere."""
+    top = (1 << 64) - (1 << 21)
+    off, ln = [], []
+    for _ in range(n):
+        r = int(rng.integers(0, len(start)))
+        s, e = int(start[r]), int(end[r])
+        c = int(rng.integers(0, 4))
+        if c == 0:
+            o, l = s, e - s
+        elif c == 1:
+            o = s + int(rng.random() * (e - s))
+            l = max(1, int(rng.random() * (e - o)))
+        elif c == 2:
+            edge = s if rng.random() < 0.5 else e
+            d1, d2 = int(rng.integers(1, 5000)), int(rng.integers(1, 5000))
+            o, l = max(edge - d1, 0), d1 + d2
+        else:
+            o, l = int(rng.random() * top), int(rng.integers(1, 1 << 20))
+        off.append(o)
+        ln.append(l)
+    return np.array(off, np.uint64), np.array(ln, np.uint64)
+
+
+@pytest.mark.parametrize("kind", ["wide", "skewed", "even"])
+@pytest.mark.parametrize("count", [1, 3, 1000, 4096])
+def test_lookup_bucket_spreads(kind, count):
+    rng = np.random.default_rng(count + len(kind))
+    start, end = _spread_table(kind, count, rng)
+    lkey = rng.integers(1, 1 << 32, size=count, dtype=np.uint64).astype(np.uint32)
+    off, ln = _queries_u64(rng, start, end, 20_011)
+    # Plus: below the first start, past the last, and at every bucket edge of
+    # a few regions (exact starts, one page before, the last page inside).
+    extra_off, extra_ln = [0, int(start[0]) - 4096 if start[0] >= 4096 else 0,
+                           int(end[-1]), (1 << 64) - 8192], [4096, 4096, 4096, 4096]
+    for r in rng.integers(0, count, size=min(count, 200)):
+        s, e = int(start[r]), int(end[r])
+        extra_off += [s, max(s - 4096, 0), e - 4096, e]
+        extra_ln += [e - s, 4096, 4096, 4096]
+    off = np.concatenate([off, np.array(extra_off, np.uint64)])
+    ln = np.concatenate([ln, np.array(extra_ln, np.uint64)])
+    gc.check_lookup(start, end, lkey, off, ln, ctx=f"{kind} R={count}")
+
+
 def test_lookup_invalid_and_va_base():
     start = np.array([0x1000, 0x9000], np.uint64)
     end = np.array([0x5000, 0xA000], np.uint64)
