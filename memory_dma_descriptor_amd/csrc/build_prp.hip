@@ -539,7 +539,7 @@ __device__ __forceinline__ void pack_marks(PackTab<uint32_t> &P, uint64_t S, uin
 template <typename T>
 __device__ __forceinline__ void emit_packed_t(PackTab<T> &P, uint64_t d, uint64_t m,
                                               uint64_t S, uint64_t E, int first, uint64_t o,
-                                              uint64_t xb, uint64_t last_frame, uint64_t *prp1,
+                                              uint64_t xb, uint64_t last_frame, uint64_t &p1,
                                               uint64_t lut_entries,
                                               const uint64_t *__restrict__ lut,
                                               uint64_t *__restrict__ pool, uint64_t bus)
@@ -587,14 +587,13 @@ __device__ __forceinline__ void emit_packed_t(PackTab<T> &P, uint64_t d, uint64_
             }
         }
         wave_sync_lds();
-        if (m && prp1)
-            __builtin_nontemporal_store(P.lut[P.foff[ln]] + (o & 0xFFFFu), prp1);
+        if (m) p1 = P.lut[P.foff[ln]] + (o & 0xFFFFu);
         if constexpr (std::is_same<T, uint32_t>::value)
             pack_marks<true>(P, S, wlo, whi, wst, first, lut_entries, lut, pool, bus);
         else
             pack_groups<T, true>(P, S, wlo, whi, lut, pool, bus);
     } else {
-        if (m && prp1) __builtin_nontemporal_store(lut[f0] + (o & 0xFFFFu), prp1);
+        if (m) p1 = lut[f0] + (o & 0xFFFFu);
         if constexpr (std::is_same<T, uint32_t>::value)
             pack_marks<false>(P, S, wlo, whi, wst, first, lut_entries, lut, pool, bus);
         else
@@ -605,10 +604,10 @@ __device__ __forceinline__ void emit_packed_t(PackTab<T> &P, uint64_t d, uint64_
 
 // Writes the packed words of the wave's 64 requests of one round (lane k: one
 // request at heap offset o with list entries m from data slot d; m == 0 for
-// no list), and PRP1 of each request with a list.
+// no list); sets p1 to PRP1 of each request with a list.
 __device__ __forceinline__ void emit_round_packed(PackLds &L, uint64_t d, uint64_t m,
                                                   uint64_t o, uint64_t xb, uint64_t last_frame,
-                                                  uint64_t *prp1, uint64_t lut_entries,
+                                                  uint64_t &p1, uint64_t lut_entries,
                                                   const uint64_t *__restrict__ lut,
                                                   uint64_t *__restrict__ pool, uint64_t bus)
 {
@@ -619,10 +618,10 @@ __device__ __forceinline__ void emit_round_packed(PackLds &L, uint64_t d, uint64
     const uint64_t S = __shfl(d, first, kWave);
     const uint64_t E = __shfl(d + m, last, kWave);
     if (E - S < (1ull << 31))
-        emit_packed_t<uint32_t>(L.fast, d, m, S, E, first, o, xb, last_frame, prp1, lut_entries,
+        emit_packed_t<uint32_t>(L.fast, d, m, S, E, first, o, xb, last_frame, p1, lut_entries,
                                 lut, pool, bus);
     else
-        emit_packed_t<uint64_t>(L.wide, d, m, S, E, first, o, xb, last_frame, prp1, lut_entries,
+        emit_packed_t<uint64_t>(L.wide, d, m, S, E, first, o, xb, last_frame, p1, lut_entries,
                                 lut, pool, bus);
 }
 
@@ -637,6 +636,7 @@ __global__ __launch_bounds__(kThreads, 4) void k_prp_build(
 {
     __shared__ uint64_t s_red[kItems * kWaves];
     __shared__ uint64_t s_bid, s_excl;
+    __shared__ uint64_t s_v2[kItems * kThreads];   // table entry of PRP2's page (two pages)
     __shared__ typename std::conditional<kPacked, PackLds, RoundLds>::type s_round[kWaves];
 
     const int t = threadIdx.x, w = wave(), ln = lane();
@@ -684,26 +684,30 @@ __global__ __launch_bounds__(kThreads, 4) void k_prp_build(
     }
     if (w == 0 && ln == 0) store_status(bstat + b, (b == 0 ? kFlagInc : kFlagAgg) | agg);
 
-    // PRP1, a two-page PRP2 and the status do not depend on the list pages.
-    // The table reads are branch-free (index 0 stands in for a request that
-    // needs none) so that all of them are in flight together; waves 1..3
-    // issue theirs before wave 0 looks back, wave 0 after (its look-back
-    // polls would otherwise wait for its table reads). A request later
-    // refused for lack of pool pages is rewritten below.
-    uint64_t v1[kItems], v2[kItems];
+    // PRP1, PRP2 and the status of a request are written once, in the list
+    // round of its item: every 64-request segment of the three columns goes
+    // out whole, in one pass, instead of in two passes with holes (a column
+    // written in parts costs whole-segment writes twice). The table reads for
+    // PRP1 and a two-page PRP2 are issued here, branch-free (index 0 stands
+    // in for a request that needs none) so that all of them are in flight
+    // together; waves 1..3 issue theirs before wave 0 looks back, wave 0
+    // after (its look-back polls would otherwise wait for its table reads).
+    // A packed list takes PRP1 from the table entries its round stages, so
+    // its table read is not repeated here. The second page's table entry of
+    // a two-page request waits in LDS (8 KiB per block), which keeps the
+    // packed build within 128 VGPRs, four blocks per CU.
+    uint64_t v1[kItems];
     auto gather = [&]() {
 #pragma unroll
         for (int k = 0; k < kItems; ++k) {
             uint64_t pages;
             const uint8_t st = decode(o[k], l[k], heap, pages);
             const uint64_t x = (o[k] & ~4095ull) + 4096;
-            // Packed lists stage their request's table entries from PRP1's
-            // GPU page on, so PRP1 of a list request is taken from there.
             const bool staged_prp1 = kPacked && pages >= 3;
             const uint64_t i1 = (st == kOk && !staged_prp1) ? o[k] >> 16 : 0;
             const uint64_t i2 = (st == kOk && pages == 2) ? x >> 16 : 0;
             v1[k] = heap ? lut[i1] : 0;
-            v2[k] = heap ? lut[i2] : 0;
+            s_v2[k * kThreads + t] = heap ? lut[i2] : 0;
         }
     };
     if (w != 0) gather();
@@ -719,22 +723,6 @@ __global__ __launch_bounds__(kThreads, 4) void k_prp_build(
         }
         gather();
     }
-#pragma unroll
-    for (int k = 0; k < kItems; ++k) {
-        const uint64_t i = base + (uint64_t)k * kThreads + t;
-        uint64_t pages;
-        const uint8_t st = decode(o[k], l[k], heap, pages);
-        if (i < n) {
-            // Output columns and input columns are streamed (non-temporal):
-            // neither is read again by this kernel.
-            if (!(kPacked && st == kOk && pages >= 3))
-                __builtin_nontemporal_store(st == kOk ? v1[k] + (o[k] & 0xFFFFu) : 0, prp1 + i);
-            if (pages < 3)
-                __builtin_nontemporal_store((st == kOk && pages == 2) ?
-                    v2[k] + (((o[k] & ~4095ull) + 4096) & 0xFFFFu) : 0, prp2 + i);
-            __builtin_nontemporal_store(st, status + i);
-        }
-    }
     __syncthreads();
     const uint64_t excl = s_excl;
 
@@ -748,23 +736,25 @@ __global__ __launch_bounds__(kThreads, 4) void k_prp_build(
                                  ? (kPacked ? pages - 1 : (pages - 2 + 510) / 511) : 0;
         const uint64_t slot = excl + pre[k];
         if (cnt != 0 && slot + cnt > cap) st = kEnospc;      // refused; its slots stay taken
-        if (i < n && cnt != 0) {
-            const uint64_t list = kPacked ? bus + 8 * (slot + slot / 511) : bus + (slot << 12);
-            prp2[i] = st == kOk ? list : 0;
-            if (st == kEnospc) {
-                prp1[i] = 0;
-                status[i] = kEnospc;
-            }
-        }
         const bool lists = (st == kOk) && cnt != 0;
         const uint64_t xb = (o[k] & ~4095ull) + 4096;
         const uint64_t last_frame = (o[k] + l[k] - 1) >> 16;
+        uint64_t p1 = v1[k] + (o[k] & 0xFFFFu);
         if constexpr (kPacked)
-            emit_round_packed(s_round[w], slot, lists ? cnt : 0, o[k], xb, last_frame,
-                              i < n ? prp1 + i : nullptr, heap >> 16, lut, pool, bus);
+            emit_round_packed(s_round[w], slot, lists ? cnt : 0, o[k], xb, last_frame, p1,
+                              heap >> 16, lut, pool, bus);
         else
             emit_round(s_round[w], xb, slot << 9, lists ? (pages - 1) + (cnt - 1) : 0,
                        lists ? cnt : 0, last_frame, lut, pool, bus);
+        if (i < n) {
+            const uint64_t list = kPacked ? bus + 8 * (slot + slot / 511) : bus + (slot << 12);
+            const uint64_t p2 = lists ? list : (pages == 2 ? s_v2[k * kThreads + t] + (xb & 0xFFFFu) : 0);
+            // Output columns and input columns are streamed (non-temporal):
+            // neither is read again by this kernel.
+            __builtin_nontemporal_store(st == kOk ? p1 : 0, prp1 + i);
+            __builtin_nontemporal_store(st == kOk ? p2 : 0, prp2 + i);
+            __builtin_nontemporal_store(st, status + i);
+        }
     }
 }
 
