@@ -6,8 +6,8 @@
 // range to whole pages, then a region that fully contains the widened range
 // is a hit (exact when both bounds coincide); partial overlap is a miss.
 //
-// Layout: one lane per request over structure-of-arrays columns, so each
-// column load/store of a wave is one contiguous 64-element run. Two kernels:
+// Layout: structure-of-arrays columns; every column load and store of a wave
+// covers one contiguous run. Two kernels:
 //
 //  * k_lookup_lds, for tables of up to 4,096 regions (20 bytes per region;
 //    MI355X has 160 KiB of LDS per CU): one 1,024-thread block per CU copies
@@ -34,6 +34,7 @@ constexpr int kThreads = 256;
 constexpr int kThreadsLds = 1024;            // one block per CU: 16 waves
 constexpr uint32_t kBuckets = 4096;          // bucket index over the region starts (LDS kernel)
 constexpr int kPerLane = 4;                  // requests per lane per trip (LDS kernel)
+static_assert(kPerLane % 2 == 0, "lanes take requests in pairs");
 
 typedef uint64_t u64x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -130,30 +131,40 @@ __global__ __launch_bounds__(kThreadsLds) void k_lookup_lds(
     }
     __syncthreads();
 
-    // Each lane takes kPerLane consecutive requests per trip, so every column
-    // moves through 16- to 32-byte accesses per lane (kind as one dword,
-    // handle and lkey as 16 bytes, rbase and rend as 32 bytes) while a wave's
-    // accesses stay contiguous; all loads are issued before any search.
+    // A wave takes 256 consecutive requests per trip; request k of a lane is
+    // wb + (k >> 1) * 128 + 2 * lane + (k & 1), so each of the wave's column
+    // loads and stores covers one contiguous run (1 KiB for the 8-byte
+    // columns, 16 bytes per lane) and every 64-byte segment is written whole
+    // by one instruction: a mapping whose store instruction fills only part
+    // of each segment (4 consecutive requests per lane: half of every
+    // 32 bytes of rbase) costs about 10 % more, 8 consecutive requests per
+    // lane 3x. All loads are issued before any search.
     const uint64_t in_page = (1ull << page_shift) - 1;
     const uint64_t span = (uint64_t)kThreadsLds * kPerLane;
+    const int ln = (int)(threadIdx.x & 63), wv = (int)(threadIdx.x >> 6);
     for (uint64_t c = (uint64_t)blockIdx.x * span; c < n; c += (uint64_t)gridDim.x * span) {
-        const uint64_t i0 = c + (uint64_t)threadIdx.x * kPerLane;
-        if (i0 >= n) break;
-        const bool whole = aligned && i0 + kPerLane <= n;
+        const uint64_t wb = c + (uint64_t)wv * (64 * kPerLane);     // the wave's requests
+        if (wb >= n) break;
+        const bool whole = aligned && wb + 64 * kPerLane <= n;      // uniform per wave
         uint64_t o[kPerLane], l[kPerLane];
         if (whole) {
             // Columns are streamed (non-temporal): nothing reads them again.
-            const u64x2 oa = __builtin_nontemporal_load(reinterpret_cast<const u64x2 *>(off + i0));
-            const u64x2 ob = __builtin_nontemporal_load(reinterpret_cast<const u64x2 *>(off + i0 + 2));
-            const u64x2 la = __builtin_nontemporal_load(reinterpret_cast<const u64x2 *>(len + i0));
-            const u64x2 lb = __builtin_nontemporal_load(reinterpret_cast<const u64x2 *>(len + i0 + 2));
-            o[0] = oa.x; o[1] = oa.y; o[2] = ob.x; o[3] = ob.y;
-            l[0] = la.x; l[1] = la.y; l[2] = lb.x; l[3] = lb.y;
+#pragma unroll
+            for (int p = 0; p < kPerLane / 2; ++p) {
+                const u64x2 oa = __builtin_nontemporal_load(reinterpret_cast<const u64x2 *>(off + wb + p * 128 + 2 * ln));
+                o[2 * p] = oa.x; o[2 * p + 1] = oa.y;
+            }
+#pragma unroll
+            for (int p = 0; p < kPerLane / 2; ++p) {
+                const u64x2 la = __builtin_nontemporal_load(reinterpret_cast<const u64x2 *>(len + wb + p * 128 + 2 * ln));
+                l[2 * p] = la.x; l[2 * p + 1] = la.y;
+            }
         } else {
 #pragma unroll
             for (int k = 0; k < kPerLane; ++k) {
-                o[k] = i0 + k < n ? off[i0 + k] : 0;
-                l[k] = i0 + k < n ? len[i0 + k] : 0;
+                const uint64_t i = wb + (k >> 1) * 128 + 2 * ln + (k & 1);
+                o[k] = i < n ? off[i] : 0;
+                l[k] = i < n ? len[i] : 0;
             }
         }
         int32_t h[kPerLane];
@@ -181,22 +192,41 @@ __global__ __launch_bounds__(kThreadsLds) void k_lookup_lds(
             }
         }
         if (whole) {
-            __builtin_nontemporal_store(i32x4{h[0], h[1], h[2], h[3]},
-                                        reinterpret_cast<i32x4 *>(handle + i0));
-            __builtin_nontemporal_store(u32x4{key[0], key[1], key[2], key[3]},
-                                        reinterpret_cast<u32x4 *>(lkey + i0));
-            __builtin_nontemporal_store((uint32_t)kd[0] | ((uint32_t)kd[1] << 8) |
-                                            ((uint32_t)kd[2] << 16) | ((uint32_t)kd[3] << 24),
-                                        reinterpret_cast<uint32_t *>(kind + i0));
-            __builtin_nontemporal_store(u64x2{lo[0], lo[1]}, reinterpret_cast<u64x2 *>(rbase + i0));
-            __builtin_nontemporal_store(u64x2{lo[2], lo[3]}, reinterpret_cast<u64x2 *>(rbase + i0 + 2));
-            __builtin_nontemporal_store(u64x2{hi[0], hi[1]}, reinterpret_cast<u64x2 *>(rend + i0));
-            __builtin_nontemporal_store(u64x2{hi[2], hi[3]}, reinterpret_cast<u64x2 *>(rend + i0 + 2));
+#pragma unroll
+            for (int p = 0; p < kPerLane / 2; ++p) {
+                const uint64_t i = wb + p * 128 + 2 * ln;
+                __builtin_nontemporal_store(u64x2{lo[2 * p], lo[2 * p + 1]}, reinterpret_cast<u64x2 *>(rbase + i));
+            }
+#pragma unroll
+            for (int p = 0; p < kPerLane / 2; ++p) {
+                const uint64_t i = wb + p * 128 + 2 * ln;
+                __builtin_nontemporal_store(u64x2{hi[2 * p], hi[2 * p + 1]}, reinterpret_cast<u64x2 *>(rend + i));
+            }
+#pragma unroll
+            for (int p = 0; p < kPerLane / 2; ++p) {
+                const uint64_t i = wb + p * 128 + 2 * ln;
+                __builtin_nontemporal_store(
+                    (uint64_t)(uint32_t)h[2 * p] | ((uint64_t)(uint32_t)h[2 * p + 1] << 32),
+                    reinterpret_cast<uint64_t *>(handle + i));
+            }
+#pragma unroll
+            for (int p = 0; p < kPerLane / 2; ++p) {
+                const uint64_t i = wb + p * 128 + 2 * ln;
+                __builtin_nontemporal_store((uint64_t)key[2 * p] | ((uint64_t)key[2 * p + 1] << 32),
+                                            reinterpret_cast<uint64_t *>(lkey + i));
+            }
+#pragma unroll
+            for (int p = 0; p < kPerLane / 2; ++p) {
+                const uint64_t i = wb + p * 128 + 2 * ln;
+                __builtin_nontemporal_store((uint16_t)(kd[2 * p] | (kd[2 * p + 1] << 8)),
+                                            reinterpret_cast<uint16_t *>(kind + i));
+            }
         } else {
 #pragma unroll
-            for (int k = 0; k < kPerLane; ++k)
-                if (i0 + k < n) put(i0 + k, h[k], key[k], kd[k], lo[k], hi[k], handle, lkey, kind,
-                                    rbase, rend);
+            for (int k = 0; k < kPerLane; ++k) {
+                const uint64_t i = wb + (k >> 1) * 128 + 2 * ln + (k & 1);
+                if (i < n) put(i, h[k], key[k], kd[k], lo[k], hi[k], handle, lkey, kind, rbase, rend);
+            }
         }
     }
 }
@@ -265,11 +295,12 @@ hipError_t launch_mr_lookup(const LookupArgs &a, hipStream_t s)
         uint64_t blocks = (a.n + (uint64_t)kThreadsLds * kPerLane - 1) / ((uint64_t)kThreadsLds * kPerLane);
         const uint64_t cap = (uint64_t)cus;
         if (blocks > cap) blocks = cap;
-        // Columns that allow 16-byte accesses (4-byte for kind) take the
-        // vector path; any other alignment is served element by element.
+        // Columns that allow the vector accesses (16 bytes for off, len,
+        // rbase and rend, 8 for handle and lkey, 2 for kind) take the vector
+        // path; any other alignment is served element by element.
         auto al = [](const void *p, uintptr_t m) { return (reinterpret_cast<uintptr_t>(p) & m) == 0; };
         const bool aligned = al(a.off, 15) && al(a.len, 15) && al(a.handle, 15) &&
-                             al(a.lkey, 15) && al(a.kind, 3) && al(a.rbase, 15) && al(a.rend, 15);
+                             al(a.lkey, 7) && al(a.kind, 1) && al(a.rbase, 15) && al(a.rend, 15);
         hipLaunchKernelGGL(k_lookup_lds, dim3((unsigned)blocks), dim3(kThreadsLds), bytes, s,
                            a.reg_start, a.reg_end, a.reg_lkey, a.nregions, a.page_shift,
                            a.off, a.len, a.n, a.va_base, a.handle, a.lkey, a.kind, a.rbase,
