@@ -20,9 +20,13 @@
 // (wave, round, lane) order -- request order.
 //
 // Kernels: k_split_hist (per-block bucket counts, bucket-major),
-// k_split_colscan (one block per bucket: exclusive scan over blocks),
-// k_split_scatter (ranks, a block-local stable sort in LDS, then perm written
-// as contiguous runs, one per bucket, so stores coalesce).
+// k_split_colscan (one block per bucket: exclusive scan over blocks), then a
+// scatter: ranks, a block-local stable sort in LDS, and perm written as
+// contiguous runs, one per bucket, so stores coalesce. Two scatters compute
+// the same ranks: k_split_scatter_cnt, for up to kCntQueues queues, counts
+// each thread's consecutive requests into a (bucket, thread) matrix of LDS
+// counters and scans it (a few VALU per request); k_split_scatter, for any
+// count, ranks with the per-bit ballots above (one per key bit per request).
 #include "dd_device.hpp"
 #include "dd_internal.h"
 #include "dmadesc.h"
@@ -221,6 +225,146 @@ __global__ __launch_bounds__(kThreads) void k_split_scatter(
     }
 }
 
+// Counter ranking. Thread t of a block owns the kItems consecutive requests
+// of chunk c(t) of the tile and counts them, in request order, into its own
+// column of a (bucket, chunk) matrix of 16-bit LDS counters: the count it
+// reads is the request's rank among the chunk's requests of its bucket. One
+// exclusive scan of the matrix in bucket-major order then gives (bucket b,
+// chunk c) the number of the tile's requests that sort before chunk c's
+// requests of bucket b -- those of lower buckets, and those of bucket b in
+// earlier chunks -- so scan value + rank is a request's place in the block's
+// stable order. Buckets are padded to a multiple of 8 (a thread scans whole
+// 16-byte rows) with at least one spare bucket, which takes the requests past
+// the end of the batch in the last tile.
+constexpr int kCntBuckets = 72;                 // padded bucket limit of the counter path
+constexpr uint32_t kCntQueues = kCntBuckets - 2;   // nq + 1 buckets + a spare fit
+static_assert(kCntBuckets % 8 == 0, "scan rows are 8 counters");
+static_assert(kTile * 3 <= kCntBuckets * kThreads * 2, "sorted tile fits over the counters");
+
+// Lanes l and l + 32 of a wave own adjacent chunks, so the 32 lanes an LDS
+// cycle serves touch 32 different dwords of a 16-bit counter row.
+__device__ __forceinline__ uint32_t chunk_of(int t)
+{
+    const int l = t & (kWave - 1), w = t / kWave;
+    return (uint32_t)(w * kWave + 2 * (l & 31) + (l >> 5));
+}
+
+__global__ __launch_bounds__(kThreads) void k_split_scatter_cnt(
+    const uint32_t *__restrict__ qid, uint64_t n, uint32_t nq, bool vec,
+    const uint32_t *__restrict__ offs, const uint64_t *__restrict__ total,
+    uint32_t *__restrict__ perm, uint64_t *__restrict__ qoff,
+    uint64_t *__restrict__ n_invalid)
+{
+    __shared__ uint32_t s_scr32[kWaves];
+    __shared__ uint64_t s_scr64[kWaves];
+    // Counters, then their bucket-major exclusive scan; at the end the sorted
+    // tile (16-bit request index inside the tile, then 8-bit bucket) over it.
+    __shared__ __align__(16) uint16_t s_cnt[kCntBuckets * kThreads];
+    __shared__ uint32_t s_lstart[kCntBuckets];         // bucket start in the sorted tile
+    __shared__ uint64_t s_gpos[kCntBuckets];           // bucket start in perm for this block
+
+    const uint32_t nbk = nq + 1;
+    const uint32_t nbp = (nbk + 8) & ~7u;              // padded, >= nbk + 1
+    const uint32_t rows = nbp / 8;                     // 16-byte scan rows per thread
+    const int t = threadIdx.x;
+    const uint32_t c = chunk_of(t);
+    const uint64_t tile = (uint64_t)blockIdx.x * kTile;
+    const uint64_t base = tile + (uint64_t)c * kItems;
+    uint4 *s4 = reinterpret_cast<uint4 *>(s_cnt);
+    for (uint32_t k = t; k < rows * kThreads; k += kThreads) s4[k] = make_uint4(0, 0, 0, 0);
+
+    // Buckets of the chunk's requests; past the batch: the spare bucket.
+    uint32_t b[kItems];
+    if (vec && tile + kTile <= n) {
+#pragma unroll
+        for (int q = 0; q < kItems / 4; ++q) {
+            const uint4 x = *reinterpret_cast<const uint4 *>(qid + base + 4 * q);
+            b[4 * q] = x.x;
+            b[4 * q + 1] = x.y;
+            b[4 * q + 2] = x.z;
+            b[4 * q + 3] = x.w;
+        }
+#pragma unroll
+        for (int k = 0; k < kItems; ++k) b[k] = b[k] < nq ? b[k] : nq;
+    } else {
+#pragma unroll
+        for (int k = 0; k < kItems; ++k)
+            b[k] = base + k < n ? bucket_of(qid, base + k, n, nq) : nbp - 1;
+    }
+    __syncthreads();
+
+    // Ranks inside the chunk: each request reads and bumps its own counter,
+    // in request order (LDS operations of a wave complete in order).
+    uint16_t *col = s_cnt + c;
+    uint32_t rank[kItems];
+#pragma unroll
+    for (int k = 0; k < kItems; ++k) {
+        const uint32_t r = col[b[k] * kThreads];
+        rank[k] = r;
+        col[b[k] * kThreads] = (uint16_t)(r + 1);
+    }
+    __syncthreads();
+
+    // Exclusive scan of the matrix, bucket-major: thread t scans counters
+    // [t * nbp, (t + 1) * nbp) of the flattened matrix. A chunk's count in a
+    // bucket is <= kItems, so the 16-bit halves of a dword sum without carry.
+    uint32_t sum = 0;
+    for (uint32_t q = 0; q < rows; ++q) {
+        const uint4 x = s4[t * rows + q];
+        const uint32_t s2 = x.x + x.y + x.z + x.w;
+        sum += (s2 & 0xFFFFu) + (s2 >> 16);
+    }
+    uint32_t tile_tot;
+    uint32_t run = block_excl_scan<kThreads>(sum, s_scr32, &tile_tot);
+    for (uint32_t q = 0; q < rows; ++q) {
+        uint4 x = s4[t * rows + q];
+        uint32_t *xw = &x.x;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const uint32_t lo = xw[j] & 0xFFFFu, hi = xw[j] >> 16;
+            xw[j] = run | ((run + lo) << 16);
+            run += lo + hi;
+        }
+        s4[t * rows + q] = x;
+    }
+    __syncthreads();
+
+    // Bucket starts: in the sorted tile (scan value of chunk 0), and in perm
+    // (all buckets' batch totals scanned, plus the blocks before this one).
+    const uint64_t gv = (uint32_t)t < nbk ? total[t] : 0;
+    uint64_t gtot;
+    const uint64_t gex = block_excl_scan<kThreads>(gv, s_scr64, &gtot);
+    if ((uint32_t)t < nbk) {
+        s_lstart[t] = s_cnt[t * kThreads];
+        s_gpos[t] = gex + offs[(uint64_t)t * gridDim.x + blockIdx.x];
+        if (blockIdx.x == 0) qoff[t] = gex;
+    }
+    if (blockIdx.x == 0 && t == 0) {
+        qoff[nbk] = n;
+        *n_invalid = total[nq];
+    }
+    uint32_t sidx[kItems];
+#pragma unroll
+    for (int k = 0; k < kItems; ++k) sidx[k] = col[b[k] * kThreads] + rank[k];
+    __syncthreads();
+
+    uint16_t *s_sorted = s_cnt;
+    uint8_t *s_sbkt = reinterpret_cast<uint8_t *>(s_cnt + kTile);
+#pragma unroll
+    for (int k = 0; k < kItems; ++k) {
+        if (base + k < n) {
+            s_sorted[sidx[k]] = (uint16_t)(c * kItems + k);
+            s_sbkt[sidx[k]] = (uint8_t)b[k];
+        }
+    }
+    __syncthreads();
+    const uint64_t cnt = n - tile < (uint64_t)kTile ? n - tile : (uint64_t)kTile;
+    for (uint32_t j = t; j < cnt; j += kThreads) {
+        const uint32_t bk = s_sbkt[j];
+        perm[s_gpos[bk] + (j - s_lstart[bk])] = (uint32_t)(tile + s_sorted[j]);
+    }
+}
+
 __global__ void k_split_empty(uint32_t nq, uint64_t *__restrict__ qoff, uint64_t *__restrict__ n_invalid)
 {
     for (uint32_t b = threadIdx.x; b < nq + 2; b += blockDim.x) qoff[b] = 0;
@@ -252,8 +396,15 @@ hipError_t launch_partition(const SplitArgs &a, hipStream_t s)
                        a.qid, a.n, a.nqueues, nb, counts);
     hipLaunchKernelGGL(k_split_colscan, dim3(nbk), dim3(kThreads), 0, s,
                        counts, nb, nbk, total);
-    hipLaunchKernelGGL(k_split_scatter, dim3((unsigned)nb), dim3(kThreads), 0, s,
-                       a.qid, a.n, a.nqueues, counts, total, a.perm, a.qoff, a.n_invalid);
+    if (a.nqueues <= kCntQueues) {
+        const bool vec = (reinterpret_cast<uintptr_t>(a.qid) & 15u) == 0;
+        hipLaunchKernelGGL(k_split_scatter_cnt, dim3((unsigned)nb), dim3(kThreads), 0, s,
+                           a.qid, a.n, a.nqueues, vec, counts, total, a.perm, a.qoff,
+                           a.n_invalid);
+    } else {
+        hipLaunchKernelGGL(k_split_scatter, dim3((unsigned)nb), dim3(kThreads), 0, s,
+                           a.qid, a.n, a.nqueues, counts, total, a.perm, a.qoff, a.n_invalid);
+    }
     return hipGetLastError();
 }
 

@@ -361,13 +361,30 @@ def test_lookup_register_sequence_table():
 
 # ----------------------------------------------------------- split edges ---
 
-@pytest.mark.parametrize("nq", [1, 2, 3, 16, 64, 65, 255, 256])
-@pytest.mark.parametrize("n", [1, 63, 64, 65, 2047, 2048, 2049, 70_001])
+# Up to 70 queues the scatter ranks by counters, from 71 on by ballots; a
+# block covers 4,096 requests.
+@pytest.mark.parametrize("nq", [1, 2, 3, 7, 8, 16, 64, 65, 70, 71, 255, 256])
+@pytest.mark.parametrize("n", [1, 63, 64, 65, 2047, 2048, 2049, 4096, 4097, 70_001])
 def test_split_sizes(nq, n):
     rng = np.random.default_rng(nq * 1000 + n)
     qid = rng.integers(0, nq + 2, size=n).astype(np.uint32)
     qid[rng.random(n) < 0.01] = np.uint32(0xFFFFFFFF)
     gc.check_split(qid, nq, ctx=f"nq={nq} n={n}")
+
+
+@pytest.mark.parametrize("nq", [64, 256])
+def test_split_unaligned_qid(nq):
+    """A queue-id column 4 bytes past a 16-byte boundary takes the scalar loads."""
+    rng = np.random.default_rng(nq + 11)
+    n = 3 * 4096 + 77
+    qid = rng.integers(0, nq + 1, size=n).astype(np.uint32)
+    buf = gc.dev(np.zeros(n + 1, np.uint32))
+    buf[1:].copy_(gc.dev(qid))
+    out = dd.partition_by_queue(buf[1:], nq)
+    torch.cuda.synchronize()
+    o = oracle.partition(qid, nq)
+    assert np.array_equal(gc.host(out["perm"]), o["perm"])
+    assert np.array_equal(gc.host(out["qoff"]), o["qoff"])
 
 
 def test_split_skewed_and_empty():
