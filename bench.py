@@ -12,7 +12,9 @@ Prints ONE JSON line. `value` is requests per second (millions) over the
 timed steps; `roofline` describes the dominant call (the PRP build of the
 step's layout; the other layout's build is timed alone beside it):
 algorithmic bytes of one launch / its mean duration from HIP events recorded
-on the stream it runs on. `emit_sqe` times the stage after the path (NVMe
+on the stream it runs on, on every 10th timed step (`per_call_ms` likewise;
+each event record is a queue marker that would add a few microseconds to
+every step). `emit_sqe` times the stage after the path (NVMe
 submission entries for the first window of every queue) on the step's outputs,
 `registry` a batch of registrations and deregistrations on the device
 registration table, `build_put` RDMA put descriptors for a VMM heap and
@@ -57,6 +59,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="minimum CPU time spent timing the oracle")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--event-every", type=int, default=10,
+                    help="record per-call HIP events on every k-th timed step (each event "
+                         "record is a queue marker that costs a few microseconds)")
     ap.add_argument("--emit-reps", type=int, default=20,
                     help="launches of the submission-entry stage timed after the steps "
                          "(0 = skip it)")
@@ -438,27 +443,32 @@ def main():
     ws_sp = torch.empty(max(dd.workspace_bytes(dd.OP_PARTITION, n, max(nq, 1)), 1),
                         dtype=torch.uint8, device=dev)
 
-    def step():
+    def step(timed_calls):
+        # The three calls are issued back to back on the current stream; on
+        # sampled steps HIP events bracket each call on that stream.
         nonlocal lk_out, prp_out, sp_out
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
-        ev[0].record()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)] if timed_calls else None
+        if ev: ev[0].record()
         if d["regions"]:
             lk_out = dd.mr_lookup(rs, re_, rk, off, ln, va_base=d["va_base"], out=lk_out)
-        ev[1].record()
+        if ev: ev[1].record()
         prp_out = dd.build_prp(lut, off, ln, bus, pool, out=prp_out, ws=ws_prp, packed=packed)
-        ev[2].record()
+        if ev: ev[2].record()
         if nq:
             sp_out = dd.partition_by_queue(qid, nq, out=sp_out, ws=ws_sp)
-        ev[3].record()
+        if ev: ev[3].record()
         return ev
 
     for _ in range(args.warmup):
-        step()
+        step(False)
     torch.cuda.synchronize()
     events = []
+    every = max(args.event_every, 1)
     t0 = time.perf_counter()
-    for _ in range(args.steps):
-        events.append(step())
+    for s_i in range(args.steps):
+        ev = step(s_i % every == every - 1 or (s_i == args.steps - 1 and not events))
+        if ev:
+            events.append(ev)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
 
@@ -524,6 +534,7 @@ def main():
                      "algorithmic_bytes_per_launch": ab[prp_key],
                      "mean_launch_ms": round(prp_ms, 4)},
         "per_call_ms": {k: round(v, 4) for k, v in per_call.items()},
+        "per_call_sampled_steps": len(events),
         "step_algorithmic_gbs": round(step_bytes / (ms * 1e-3) / 1e9, 1),
         "step_frac_of_peak": round(step_bytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
         "prp_entries_per_s": round(ab["prp_entries"] * args.steps / elapsed, 1),
