@@ -168,7 +168,7 @@ int dmadesc_mr_lookup(const uint64_t *reg_start, const uint64_t *reg_end,
  *                                  pages; page s has bus address
  *                                  list_bus_base + 4096*s. Entries the batch
  *                                  needs are written; after a request's last
- *                                  entry, words up to the next multiple of 16
+ *                                  entry, words up to the next multiple of 8
  *                                  words of its final list page may be
  *                                  written (with 0; a controller never reads
  *                                  them); every other word, and every page

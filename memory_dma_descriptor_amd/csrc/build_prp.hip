@@ -24,14 +24,16 @@
 //    the run is the chain pointer when q % 512 == 511 on a non-final page,
 //    else data entry j = q - q / 512. No division is needed anywhere.
 //  * List phase, per wave and per item round: the wave's 64 consecutive
-//    requests of that round are emitted in groups
-//    of 4 consecutive words (32 bytes), load-balanced over groups, not
-//    requests: lane k of each step takes group c + k, finds its request by a
-//    6-step search over the wave's group offsets in LDS, and writes its 4
-//    words with two 16-byte stores. Four consecutive 4 KiB pages lie in at
-//    most two 64 KiB GPU pages, so each group reads at most two table
-//    entries; a wave's 64 groups read one short run of the table per
-//    request, which the L1/L2 serve.
+//    requests of that round are emitted in pairs of consecutive words
+//    (16 bytes), load-balanced over pairs, not requests: lane k of each step
+//    takes pair c + k, finds its request by a 6-step search over the wave's
+//    pair offsets in LDS, and writes it with one non-temporal 16-byte store,
+//    so that each store instruction fills whole 64-byte segments (a lane
+//    writing 32 bytes as two stores would fill half of every 32 bytes per
+//    instruction). Two consecutive 4 KiB pages lie in at most two 64 KiB GPU
+//    pages, so each pair reads at most two table entries, staged in LDS.
+//    Rounds with a list of 2^24 words or more take a 64-bit path in groups
+//    of 4 words.
 //
 // Packed layout (the same kernel, kPacked = true): lists lie back to back in
 // data slots, 511 to a page (words 0..510); a request's list starts where the
@@ -59,8 +61,9 @@ constexpr int kItems = 4;                     // requests per thread
 constexpr int kTile = kThreads * kItems;      // requests per block
 // A request's list run is written in whole units of kPadWords words (a
 // multiple of 4 dividing 512, so padding never leaves the request's final
-// list page); words past the last entry are written as 0.
-constexpr uint64_t kPadWords = 16;
+// list page): whole 64-byte segments. Words past the last entry are
+// written as 0.
+constexpr uint64_t kPadWords = 8;
 // GPU pages of the table staged in LDS per wave and round (4 KiB).
 constexpr int kTileFrames = 512;
 enum : uint8_t { kOk = 0, kEinval = 1, kErange = 2, kEnospc = 3 };
@@ -99,7 +102,7 @@ struct ReqRec {                 // 32 bytes, read with two 16-byte LDS loads
     uint32_t ph;                // 4 KiB page of data entry 0 within GPU page f0
 };
 struct FastTable {
-    uint32_t goff[kWave + 1];   // exclusive prefix of 4-word groups
+    uint32_t goff[kWave + 1];   // exclusive prefix of 2-word pairs
     uint32_t foff[kWave + 1];   // exclusive prefix of staged GPU pages
     ReqRec rec[kWave];
     uint64_t lut[kTileFrames];
@@ -190,20 +193,22 @@ __device__ __forceinline__ void emit_round_wide(RoundTable &T, uint64_t xb, uint
     wave_sync_lds();                                         // the next round rewrites T
 }
 
-// Writes one group of a fast round. Data entry j of a request lies in GPU
-// page f0 + ((ph + j) >> 4) at in-page offset ((ph + j) & 15) * 4 KiB.
+// Writes one 2-word pair of a fast round (one 16-byte store: the lanes of a
+// wave write consecutive pairs, so each store instruction fills whole lines).
+// Data entry j of a request lies in GPU page f0 + ((ph + j) >> 4) at in-page
+// offset ((ph + j) & 15) * 4 KiB.
 template <bool kStaged>
 __device__ __forceinline__ void fast_group(const FastTable &T, uint32_t g, int r,
                                            const uint64_t *__restrict__ lut,
                                            uint64_t *__restrict__ pool, uint64_t bus)
 {
     const ReqRec R = T.rec[r];
-    const uint32_t q = (g - T.goff[r]) << 2;                 // first word of the group
+    const uint32_t q = (g - T.goff[r]) << 1;                 // first word of the pair
     const uint32_t page = q >> 9;
     const uint32_t j0 = q - page;                            // its data entry
-    const bool has_ptr = ((q & 511u) == 508u) && (q < R.plim);
-    const uint32_t left = R.ent > q ? R.ent - q : 0;         // 0 for a padding-only group
-    const uint32_t nd = has_ptr ? 3u : (left < 4u ? left : 4u);
+    const bool has_ptr = ((q & 511u) == 510u) && (q < R.plim);
+    const uint32_t left = R.ent > q ? R.ent - q : 0;         // 0 for a padding-only pair
+    const uint32_t nd = has_ptr ? 1u : (left < 2u ? left : 2u);
     const uint32_t t0 = R.ph + j0;
     const uint32_t fi = t0 >> 4, u = t0 & 15u;
     uint64_t l0 = 0, l1 = 0;
@@ -217,20 +222,20 @@ __device__ __forceinline__ void fast_group(const FastTable &T, uint32_t g, int r
             l1 = two ? lut[R.f0 + fi + 1] : l0;
         }
     }
-    uint64_t v[4];
+    uint64_t v[2];
 #pragma unroll
-    for (uint32_t k = 0; k < 4; ++k) {
+    for (uint32_t k = 0; k < 2; ++k) {
         const uint32_t wk = u + k;
         const uint64_t d = (wk >= 16u ? l1 : l0) + (uint64_t)((wk & 15u) << 12);
         v[k] = k < nd ? d : 0;                               // padding words are 0
     }
-    if (has_ptr) v[3] = bus + (((R.word >> 9) + page + 1) << 12);
-    uint64_t *dst = pool + R.word + q;
-    *reinterpret_cast<u64x2 *>(dst) = u64x2{v[0], v[1]};
-    *reinterpret_cast<u64x2 *>(dst + 2) = u64x2{v[2], v[3]};
+    if (has_ptr) v[1] = bus + (((R.word >> 9) + page + 1) << 12);
+    // Non-temporal: the list words are not read again by this kernel.
+    __builtin_nontemporal_store(u64x2{v[0], v[1]},
+                                reinterpret_cast<u64x2 *>(pool + R.word + q));
 }
 
-// Writes the groups of a fast round, two per lane per step: groups g and
+// Writes the pairs of a fast round, two per lane per step: pairs g and
 // g + 64 are searched in lockstep so that their LDS reads overlap.
 template <bool kStaged>
 __device__ __forceinline__ void fast_groups(const FastTable &T, uint32_t gtot,
@@ -261,7 +266,7 @@ __device__ __forceinline__ void emit_round_fast(FastTable &T, uint64_t xb, uint6
 {
     const int ln = lane();
     const uint32_t groups = ((ent + (uint32_t)kPadWords - 1) / (uint32_t)kPadWords) *
-                            (uint32_t)(kPadWords / 4);
+                            (uint32_t)(kPadWords / 2);
     const uint32_t ginc = wave_incl_scan(groups);
     const uint32_t gtot = __shfl(ginc, kWave - 1, kWave);
     if (gtot == 0) return;                                   // uniform per wave

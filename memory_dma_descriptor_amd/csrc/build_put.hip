@@ -23,7 +23,8 @@
 // look-back, dd_lookback.hpp); then each wave writes the descriptors of its 64
 // consecutive requests as one contiguous range, load-balanced over descriptors:
 // lane j of a step takes descriptor S + 64 j + lane and finds its request by a
-// 6-step search over the requests' first slots in LDS.
+// 6-step search over the requests' first slots in LDS; a step's 64
+// descriptors go out through LDS as two 1 KiB store instructions.
 #include "dd_device.hpp"
 #include "dd_internal.h"
 #include "dd_lookback.hpp"
@@ -67,6 +68,7 @@ struct PutTab {
     uint64_t s[kWave], d[kWave], b[kWave];
     uint32_t pe[kWave];
     uint32_t req[kWave];
+    u64x2 out[2 * kWave];        // one step's 64 descriptors, in order, for the stores
 };
 
 struct PutKeys {
@@ -102,7 +104,9 @@ __device__ __forceinline__ void emit_put_round(PutTab &T, uint64_t first, uint64
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    for (uint64_t p = S + ln; p < E; p += kWave) {
+    for (uint64_t c = S; c < E; c += kWave) {             // uniform per wave
+        // Lanes past the end compute the last descriptor again; not stored.
+        const uint64_t p = c + ln < E ? c + ln : E - 1;
         const int r = owner_of<kWave>(T.start, p);
         const uint64_t j = p - T.start[r];
         const uint64_t rs = T.s[r], rd = T.d[r], rb = T.b[r];
@@ -120,10 +124,22 @@ __device__ __forceinline__ void emit_put_round(PutTab &T, uint64_t first, uint64
         }
         const uint64_t w2 = (x1 - x0) | ((uint64_t)lkey << 32);
         const uint64_t w3 = rkey | ((uint64_t)T.req[r] << 32);
-        uint64_t *dst = desc + 4 * p;
-        __builtin_nontemporal_store(u64x2{K.local_base + rs + x0, K.peer_base[rpe] + rd + x0},
-                                    reinterpret_cast<u64x2 *>(dst));
-        __builtin_nontemporal_store(u64x2{w2, w3}, reinterpret_cast<u64x2 *>(dst + 2));
+        // Through LDS, so that each of the wave's two 16-byte store
+        // instructions covers 1 KiB contiguously (a lane storing its own
+        // 32-byte descriptor would fill half of every 32 bytes per
+        // instruction, which non-temporal stores pay for twice).
+        T.out[2 * ln] = u64x2{K.local_base + rs + x0, K.peer_base[rpe] + rd + x0};
+        T.out[2 * ln + 1] = u64x2{w2, w3};
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        const u64x2 h0 = T.out[ln], h1 = T.out[kWave + ln];
+        u64x2 *dst = reinterpret_cast<u64x2 *>(desc + 4 * c);
+        if (c + (ln >> 1) < E) __builtin_nontemporal_store(h0, dst + ln);
+        if (c + kWave / 2 + (ln >> 1) < E) __builtin_nontemporal_store(h1, dst + kWave + ln);
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");   // out is rewritten next
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");   // the next round rewrites T
     __builtin_amdgcn_wave_barrier();

@@ -13,7 +13,7 @@ CANARY_I64 = np.uint64(CANARY).astype(np.int64).item()
 # The library may write the words after a request's last list entry, up to
 # the next multiple of PAD_WORDS words inside that request's final list page
 # (their contents are unspecified); every other pool word it must leave alone.
-PAD_WORDS = 16
+PAD_WORDS = 8
 
 
 def padding_spans(prp2, status, off, ln, bus, slot_base=0):
