@@ -146,11 +146,16 @@ __global__ __launch_bounds__(kOrderThreads) void k_sqe_order(SqeArgs a, SqeWs ws
     if (threadIdx.x == 0) *ws.ntiles = total;
 }
 
-// The tile block b works on, or false when b is past the non-empty tiles.
+// The tile block b works on, or false when b has none. Blocks are dealt to
+// the 8 XCDs in turn; XCD x takes the x-th eighth of the tile order, so the
+// tiles that share an XCD's L2 cover neighbouring request ranges.
 __device__ __forceinline__ bool tile_of(const SqeWs &ws, uint32_t &q, uint32_t &t)
 {
-    if (blockIdx.x >= *ws.ntiles) return false;
-    const uint32_t g = ws.order[blockIdx.x];
+    const uint32_t nt = *ws.ntiles, per = (nt + 7) / 8;
+    const uint32_t x = blockIdx.x & 7, k = blockIdx.x >> 3;
+    const uint32_t idx = x * per + k;
+    if (k >= per || idx >= nt) return false;
+    const uint32_t g = ws.order[idx];
     q = g / kTilesPerQueue;
     t = g % kTilesPerQueue;
     return true;
