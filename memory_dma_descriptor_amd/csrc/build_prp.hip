@@ -10,7 +10,7 @@
 //
 // One pass, one kernel (after a small workspace-clearing kernel):
 //
-//  * Request phase, 2048 requests per block, item k of thread t being request
+//  * Request phase, 1024 requests per block, item k of thread t being request
 //    block_base + 256 k + t (so every column load is contiguous per wave):
 //    validity, 4 KiB page count, list pages L. List pages are handed out in
 //    request order by a device-wide exclusive scan done in the same pass
