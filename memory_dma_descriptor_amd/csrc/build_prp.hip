@@ -333,7 +333,9 @@ struct PackTab {
     uint32_t ph[kWave];         // 4 KiB page of data entry 0 counted from f0 (< 32)
     uint4 rec[kWave];           // 32-bit rounds: {start, m, foff, ph} of each request
     uint2 rec2[kWave];          // 32-bit rounds: {ph - start, foff} of each request
-    uint8_t mark[2 * kWave];    // 32-bit rounds: 1 + request whose list starts at a word
+    // 32-bit rounds: 1 + request whose list starts at a word of a 256-word
+    // window (the 64-bit rounds do not use it; their table is the larger).
+    uint8_t mark[sizeof(T) == 4 ? 4 * kWave : 2 * kWave];
     uint64_t lut[kTileFrames];
 };
 union PackLds {
@@ -465,16 +467,19 @@ __device__ __forceinline__ uint32_t wave_shr1(uint32_t x)
 }
 
 // Writes pool words [wlo, whi) of a packed round whose slots, relative to S,
-// fit 32 bits, in windows of 128 words: lane l writes words 2l and 2l + 1, so
-// each 16-byte store of the wave covers 1 KiB contiguously. A word's owner is
-// the last list that starts at or before it: every list marks its first word
-// in an LDS map of the window, and a prefix maximum across the wave (plus the
-// owner carried from the window before) hands each word its owner, with no
-// search. A non-511 word W holds slot W - W / 512, so entry t of its owner's
-// staged pages is (slot - S) + (ph - start). Word 511 (lane 63) and word 0
-// (lane 0) of a pool page get their special values in a branch taken only in
-// the windows that hold them. `wst` is the first word of this lane's list (a
-// value no window reaches when it has none); `first` is the first list lane.
+// fit 32 bits, in windows of 256 words, each two halves of 128: lane l writes
+// words 2l, 2l + 1 of each half, so each 16-byte store of the wave covers
+// 1 KiB contiguously, and the window's fixed work (the owner map below) is
+// shared by four words per lane. A word's owner is the last list that starts
+// at or before it: every list marks its first word in an LDS map of the
+// window, and a prefix maximum across the wave (plus the owner carried from
+// before) hands each word its owner, with no search. Every word of a window
+// lies in one pool page, so a non-511 word W holds slot W - W / 512, and its
+// entry is (slot - S) + (ph - start) of its owner's staged GPU pages. Word 511
+// (lane 63) and word 0 (lane 0) of a page get their special values in a
+// branch taken only in the windows that hold them. `wst` is the first word of
+// this lane's list (a value no window reaches when it has none); `first` is
+// the first list lane.
 template <bool kStaged>
 __device__ __forceinline__ void pack_marks(PackTab<uint32_t> &P, uint64_t S, uint64_t wlo,
                                            uint64_t whi, uint64_t wst, int first,
@@ -482,60 +487,82 @@ __device__ __forceinline__ void pack_marks(PackTab<uint32_t> &P, uint64_t S, uin
                                            const uint64_t *__restrict__ lut,
                                            uint64_t *__restrict__ pool, uint64_t bus)
 {
+    constexpr uint64_t kWin = 4 * kWave;
     const uint32_t ln = (uint32_t)lane();
     uint32_t carry = (uint32_t)first + 1;                    // owner mark before the window
-    uint16_t *mark16 = reinterpret_cast<uint16_t *>(P.mark);
-    for (uint64_t Wb = wlo & ~127ull; Wb < whi; Wb += 128) {
-        mark16[ln] = 0;
-        if (wst - Wb < 128) P.mark[wst - Wb] = (uint8_t)(ln + 1);
+    uint32_t *mark32 = reinterpret_cast<uint32_t *>(P.mark);
+    const uint16_t *mark16 = reinterpret_cast<const uint16_t *>(P.mark);
+    for (uint64_t Wb = wlo & ~(kWin - 1); Wb < whi; Wb += kWin) {
+        mark32[ln] = 0;
+        if (wst - Wb < kWin) P.mark[wst - Wb] = (uint8_t)(ln + 1);
         wave_sync_lds();
-        const uint32_t mk = mark16[ln];
-        const uint32_t m0 = mk & 0xFFu, m1 = mk >> 8;
-        const uint32_t pm = max(wave_incl_max(max(m0, m1)), carry);
-        const uint32_t o0 = max(max(wave_shr1(pm), carry), m0);   // owner mark of word 2l
-        const uint32_t o1 = max(o0, m1);                          // ... and of word 2l + 1
-        carry = (uint32_t)__builtin_amdgcn_readlane((int)pm, kWave - 1);
-        const int r0 = (int)o0 - 1, r1 = (int)o1 - 1;
-        const uint64_t W0 = Wb + 2 * ln, W1 = W0 + 1;
-        const bool in0 = W0 >= wlo && W0 < whi, in1 = W1 >= wlo && W1 < whi;
-        const uint2 a0 = P.rec2[r0], a1 = P.rec2[r1];
-        const uint32_t t0 = (uint32_t)(W0 - (W0 >> 9) - S) + a0.x;
-        const uint32_t t1 = (uint32_t)(W1 - (W1 >> 9) - S) + a1.x;
-        // Words outside the range are computed from entry 0 and never stored.
-        const uint32_t f0 = in0 ? t0 >> 4 : 0, f1 = in1 ? t1 >> 4 : 0;
-        uint64_t l0, l1;
-        if (kStaged) {
-            l0 = P.lut[(a0.y + f0) & (kTileFrames - 1)];
-            l1 = P.lut[(a1.y + f1) & (kTileFrames - 1)];
-        } else {
-            const uint64_t i0 = P.f0[r0] + f0, i1 = P.f0[r1] + f1;
-            l0 = lut[i0 < lut_entries ? i0 : 0];
-            l1 = lut[i1 < lut_entries ? i1 : 0];
+        const uint32_t ma = mark16[ln], mb = mark16[kWave + ln];
+        const uint32_t a0 = ma & 0xFFu, a1 = ma >> 8, b0 = mb & 0xFFu, b1 = mb >> 8;
+        // Prefix maxima of both halves side by side; the second half carries
+        // the first half's last owner.
+        const uint32_t pa = max(wave_incl_max(max(a0, a1)), carry);
+        const uint32_t pb0 = wave_incl_max(max(b0, b1));
+        const uint32_t ca = (uint32_t)__builtin_amdgcn_readlane((int)pa, kWave - 1);
+        const uint32_t pb = max(pb0, ca);
+        int r[4];
+        r[0] = (int)max(max(wave_shr1(pa), carry), a0) - 1;
+        r[1] = max(r[0], (int)a1 - 1);
+        r[2] = (int)max(max(wave_shr1(pb), ca), b0) - 1;
+        r[3] = max(r[2], (int)b1 - 1);
+        carry = (uint32_t)__builtin_amdgcn_readlane((int)pb, kWave - 1);
+        // Slot of this lane's first word, relative to S (mod 2^32; words
+        // outside the range compute anything and are not stored).
+        const uint32_t sb = (uint32_t)(Wb - (Wb >> 9) - S) + 2 * ln;
+        uint64_t v[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const uint2 a = P.rec2[r[k]];
+            const uint32_t t = sb + (uint32_t)((k >> 1) * 128 + (k & 1)) + a.x;
+            uint64_t l;
+            if (kStaged) {
+                l = P.lut[(a.y + (t >> 4)) & (kTileFrames - 1)];
+            } else {
+                const uint64_t i = P.f0[r[k]] + (t >> 4);
+                l = lut[i < lut_entries ? i : 0];
+            }
+            v[k] = l + ((uint64_t)(t & 15u) << 12);
         }
-        uint64_t v0 = l0 + ((uint64_t)(t0 & 15u) << 12);
-        uint64_t v1 = l1 + ((uint64_t)(t1 & 15u) << 12);
-        if ((Wb & 511u) == 384u && ln == kWave - 1) {
-            // Word 511: the owner of slot 510 writes a chain pointer if two or
-            // more of its entries remain, its final entry if exactly one does
-            // (v1 is then that entry), else 0.
-            const uint4 R = P.rec[r1];
-            const uint32_t rem = R.y - ((uint32_t)(W1 - 1 - (W1 >> 9) - S) - R.x) - 1;
-            if (rem >= 2) v1 = bus + (((W1 >> 9) + 1) << 12);
-            else if (rem == 0) v1 = 0;
+        if ((Wb & 511u) == 256u && ln == kWave - 1) {
+            // Word 511 (second half, second word of lane 63): the owner of
+            // slot 510 writes a chain pointer if two or more of its entries
+            // remain, its final entry if exactly one does (v[3] is then that
+            // entry), else 0.
+            const uint4 R = P.rec[r[3]];
+            const uint32_t rem = R.y - ((sb + 128u) - R.x) - 1u;
+            if (rem >= 2) v[3] = bus + ((((Wb + 255) >> 9) + 1) << 12);
+            else if (rem == 0) v[3] = 0;
         }
         if ((Wb & 511u) == 0u && ln == 0) {
             // Word 0: 0 when its slot's entry is its owner's final one, which
             // then sits in word 511 of the page before.
-            const uint4 R = P.rec[r0];
-            const uint32_t j = (uint32_t)(W0 - (W0 >> 9) - S) - R.x;
-            if (j > 0 && j == R.y - 1) v0 = 0;
+            const uint4 R = P.rec[r[0]];
+            const uint32_t j = sb - R.x;
+            if (j > 0 && j == R.y - 1) v[0] = 0;
         }
         // Non-temporal: the list words are not read again by this kernel.
-        if (in0 && in1) {
-            __builtin_nontemporal_store(u64x2{v0, v1}, reinterpret_cast<u64x2 *>(pool + W0));
+        if (Wb >= wlo && Wb + kWin <= whi) {
+            __builtin_nontemporal_store(u64x2{v[0], v[1]},
+                                        reinterpret_cast<u64x2 *>(pool + Wb + 2 * ln));
+            __builtin_nontemporal_store(u64x2{v[2], v[3]},
+                                        reinterpret_cast<u64x2 *>(pool + Wb + 128 + 2 * ln));
         } else {
-            if (in0) __builtin_nontemporal_store(v0, pool + W0);
-            if (in1) __builtin_nontemporal_store(v1, pool + W1);
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const uint64_t W0 = Wb + 2 * ln + 128 * h, W1 = W0 + 1;
+                const bool in0 = W0 >= wlo && W0 < whi, in1 = W1 >= wlo && W1 < whi;
+                if (in0 && in1) {
+                    __builtin_nontemporal_store(u64x2{v[2 * h], v[2 * h + 1]},
+                                                reinterpret_cast<u64x2 *>(pool + W0));
+                } else {
+                    if (in0) __builtin_nontemporal_store(v[2 * h], pool + W0);
+                    if (in1) __builtin_nontemporal_store(v[2 * h + 1], pool + W1);
+                }
+            }
         }
         wave_sync_lds();                                     // the map is rewritten next
     }
