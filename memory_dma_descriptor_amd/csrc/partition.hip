@@ -36,9 +36,12 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
-constexpr int kItems = 16;                      // requests per thread
-constexpr int kWaveItems = kWave * kItems;      // requests per wave
-constexpr int kTile = kThreads * kItems;        // requests per block
+// Requests per thread: 32 (8,192 per block) with the counter ranking, whose
+// registers allow it and whose per-bucket runs of perm get twice as long
+// (fewer partly written 64-byte segments); 16 with the ballot ranking,
+// which at 32 would need 225 VGPRs. The histogram uses the scatter's tile.
+constexpr int kItemsCnt = 32;
+constexpr int kItemsBallot = 16;
 constexpr int kMaxBuckets = DMADESC_MAX_QUEUES + 1;
 constexpr int kBucketSlots = 2 * kThreads;      // >= kMaxBuckets, two per thread
 
@@ -59,6 +62,7 @@ __device__ __forceinline__ uint32_t bucket_of(const uint32_t *__restrict__ qid, 
 // wholly inside the batch (every tile but the last) the loads carry no
 // condition, so all of them are in flight at once; a guarded load would wait
 // for each before issuing the next.
+template <int kItems>
 __device__ __forceinline__ void load_buckets(const uint32_t *__restrict__ qid, uint64_t base,
                                              uint64_t n, uint32_t nq, bool full,
                                              uint32_t (&b)[kItems])
@@ -79,10 +83,13 @@ __device__ __forceinline__ void load_buckets(const uint32_t *__restrict__ qid, u
 // instead of serializing on one (the copies lie in different LDS banks).
 constexpr int kCopies = 8;
 
+template <int kItems>
 __global__ __launch_bounds__(kThreads) void k_split_hist(
     const uint32_t *__restrict__ qid, uint64_t n, uint32_t nq, uint64_t nb,
     uint32_t *__restrict__ counts)
 {
+    constexpr int kWaveItems = kWave * kItems;          // requests per wave
+    constexpr int kTile = kThreads * kItems;            // requests per block
     __shared__ uint32_t h[kCopies][kMaxBuckets];
     const uint32_t nbk = nq + 1;
     for (uint32_t b = threadIdx.x; b < kCopies * kMaxBuckets; b += kThreads) (&h[0][0])[b] = 0;
@@ -129,12 +136,15 @@ __global__ __launch_bounds__(kThreads) void k_split_colscan(
     if (threadIdx.x == 0) total[blockIdx.x] = tot;
 }
 
+template <int kItems>
 __global__ __launch_bounds__(kThreads) void k_split_scatter(
     const uint32_t *__restrict__ qid, uint64_t n, uint32_t nq,
     const uint32_t *__restrict__ offs, const uint64_t *__restrict__ total,
     uint32_t *__restrict__ perm, uint64_t *__restrict__ qoff,
     uint64_t *__restrict__ n_invalid)
 {
+    constexpr int kWaveItems = kWave * kItems;          // requests per wave
+    constexpr int kTile = kThreads * kItems;            // requests per block
     __shared__ uint64_t s_scr[kWaves];
     __shared__ uint32_t s_wcnt[kWaves][kMaxBuckets];   // running, then prefix, per wave
     __shared__ uint32_t s_lstart[kBucketSlots];        // bucket start in the block's sorted tile
@@ -239,7 +249,8 @@ __global__ __launch_bounds__(kThreads) void k_split_scatter(
 constexpr int kCntBuckets = 72;                 // padded bucket limit of the counter path
 constexpr uint32_t kCntQueues = kCntBuckets - 2;   // nq + 1 buckets + a spare fit
 static_assert(kCntBuckets % 8 == 0, "scan rows are 8 counters");
-static_assert(kTile * 3 <= kCntBuckets * kThreads * 2, "sorted tile fits over the counters");
+static_assert(kThreads * kItemsCnt * 3 <= kCntBuckets * kThreads * 2,
+              "sorted tile fits over the counters");
 
 // Lanes l and l + 32 of a wave own adjacent chunks, so the 32 lanes an LDS
 // cycle serves touch 32 different dwords of a 16-bit counter row.
@@ -249,12 +260,15 @@ __device__ __forceinline__ uint32_t chunk_of(int t)
     return (uint32_t)(w * kWave + 2 * (l & 31) + (l >> 5));
 }
 
+template <int kItems>
 __global__ __launch_bounds__(kThreads) void k_split_scatter_cnt(
     const uint32_t *__restrict__ qid, uint64_t n, uint32_t nq, bool vec,
     const uint32_t *__restrict__ offs, const uint64_t *__restrict__ total,
     uint32_t *__restrict__ perm, uint64_t *__restrict__ qoff,
     uint64_t *__restrict__ n_invalid)
 {
+    constexpr int kWaveItems = kWave * kItems;          // requests per wave
+    constexpr int kTile = kThreads * kItems;            // requests per block
     __shared__ uint32_t s_scr32[kWaves];
     __shared__ uint64_t s_scr64[kWaves];
     // Counters, then their bucket-major exclusive scan; at the end the sorted
@@ -371,11 +385,18 @@ __global__ void k_split_empty(uint32_t nq, uint64_t *__restrict__ qoff, uint64_t
     if (threadIdx.x == 0) *n_invalid = 0;
 }
 
+// Requests per block of the split for nq queues (the ranking it uses).
+uint64_t split_tile(uint32_t nq)
+{
+    return (uint64_t)kThreads * (nq <= kCntQueues ? kItemsCnt : kItemsBallot);
+}
+
 }  // namespace
 
 size_t ws_partition(uint64_t n, uint32_t nq)
 {
-    const uint64_t nb = (n + kTile - 1) / kTile;
+    const uint64_t tile = split_tile(nq);
+    const uint64_t nb = (n + tile - 1) / tile;
     return align256((uint64_t)(nq + 1) * nb * sizeof(uint32_t)) +
            align256((uint64_t)(nq + 1) * sizeof(uint64_t));
 }
@@ -387,22 +408,28 @@ hipError_t launch_partition(const SplitArgs &a, hipStream_t s)
                            a.n_invalid);
         return hipGetLastError();
     }
-    const uint64_t nb = (a.n + kTile - 1) / kTile;
+    const uint64_t tile = split_tile(a.nqueues);
+    const uint64_t nb = (a.n + tile - 1) / tile;
     const uint32_t nbk = a.nqueues + 1;
+    const bool cnt_path = a.nqueues <= kCntQueues;
     uint32_t *counts = static_cast<uint32_t *>(a.ws);
     uint64_t *total = reinterpret_cast<uint64_t *>(
         static_cast<char *>(a.ws) + align256((uint64_t)nbk * nb * sizeof(uint32_t)));
-    hipLaunchKernelGGL(k_split_hist, dim3((unsigned)nb), dim3(kThreads), 0, s,
-                       a.qid, a.n, a.nqueues, nb, counts);
+    if (cnt_path)
+        hipLaunchKernelGGL(k_split_hist<kItemsCnt>, dim3((unsigned)nb), dim3(kThreads), 0, s,
+                           a.qid, a.n, a.nqueues, nb, counts);
+    else
+        hipLaunchKernelGGL(k_split_hist<kItemsBallot>, dim3((unsigned)nb), dim3(kThreads), 0, s,
+                           a.qid, a.n, a.nqueues, nb, counts);
     hipLaunchKernelGGL(k_split_colscan, dim3(nbk), dim3(kThreads), 0, s,
                        counts, nb, nbk, total);
-    if (a.nqueues <= kCntQueues) {
+    if (cnt_path) {
         const bool vec = (reinterpret_cast<uintptr_t>(a.qid) & 15u) == 0;
-        hipLaunchKernelGGL(k_split_scatter_cnt, dim3((unsigned)nb), dim3(kThreads), 0, s,
+        hipLaunchKernelGGL(k_split_scatter_cnt<kItemsCnt>, dim3((unsigned)nb), dim3(kThreads), 0, s,
                            a.qid, a.n, a.nqueues, vec, counts, total, a.perm, a.qoff,
                            a.n_invalid);
     } else {
-        hipLaunchKernelGGL(k_split_scatter, dim3((unsigned)nb), dim3(kThreads), 0, s,
+        hipLaunchKernelGGL(k_split_scatter<kItemsBallot>, dim3((unsigned)nb), dim3(kThreads), 0, s,
                            a.qid, a.n, a.nqueues, counts, total, a.perm, a.qoff, a.n_invalid);
     }
     return hipGetLastError();
