@@ -364,7 +364,8 @@ def test_lookup_register_sequence_table():
 # Up to 70 queues the scatter ranks by counters, from 71 on by ballots; a
 # block covers 4,096 requests.
 @pytest.mark.parametrize("nq", [1, 2, 3, 7, 8, 16, 64, 65, 70, 71, 255, 256])
-@pytest.mark.parametrize("n", [1, 63, 64, 65, 2047, 2048, 2049, 4096, 4097, 70_001])
+@pytest.mark.parametrize("n", [1, 63, 64, 65, 2047, 2048, 2049, 4096, 4097, 8191, 8192, 8193,
+                               16_385, 70_001])
 def test_split_sizes(nq, n):
     rng = np.random.default_rng(nq * 1000 + n)
     qid = rng.integers(0, nq + 2, size=n).astype(np.uint32)
