@@ -267,7 +267,6 @@ __global__ __launch_bounds__(kThreads) void k_split_scatter_cnt(
     uint32_t *__restrict__ perm, uint64_t *__restrict__ qoff,
     uint64_t *__restrict__ n_invalid)
 {
-    constexpr int kWaveItems = kWave * kItems;          // requests per wave
     constexpr int kTile = kThreads * kItems;            // requests per block
     __shared__ uint32_t s_scr32[kWaves];
     __shared__ uint64_t s_scr64[kWaves];

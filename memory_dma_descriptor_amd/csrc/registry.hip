@@ -52,6 +52,19 @@ enum : uint8_t { kInvalid = DMADESC_REG_INVALID, kHit = DMADESC_REG_HIT, kNew = 
                  kHitNew = DMADESC_REG_HIT_NEW, kNospace = DMADESC_REG_NOSPACE };
 enum : uint8_t { kMiss = 5 };                        // internal class before inserts are known
 
+// Pair kernels: items per block (one per lane of a wave), and entries of a
+// tile read from LDS before they are compared.
+constexpr uint32_t kPairItems = kWave;
+constexpr uint32_t kPairStep = 8;
+static_assert(kWave % (4 * kPairStep) == 0, "a wave's quarter is whole steps");
+
+// A rounded range in LDS; kNoRange contains nothing and sorts after every
+// valid start (a valid range has base < 2^64 - 1 and top > 0).
+struct alignas(16) Range {
+    uint64_t base, top;
+};
+constexpr Range kNoRange{~0ull, 0};
+
 // Workspace pieces (pointers into the caller's workspace).
 struct RegWs {
     // per batch item
@@ -280,39 +293,49 @@ __global__ __launch_bounds__(kThreads) void k_reg_classify(RegState g, RegWs w, 
     w.hit[i] = hit;
 }
 
-// inserted(i) = miss and no earlier miss contains it. Items i of this block
-// against every earlier item j, 256 at a time in LDS.
+// inserted(i) = miss and no earlier miss contains it. A block holds
+// kPairItems items; every earlier item j passes through LDS 256 at a time and
+// each wave compares the block's items with its own quarter of the tile.
+// s_done[l] turns 1 once some wave finds a miss containing item l.
 __global__ __launch_bounds__(kThreads) void k_reg_inserted(RegWs w, uint32_t n)
 {
-    __shared__ uint64_t s_base[kThreads], s_top[kThreads];
-    __shared__ uint8_t s_miss[kThreads];
-    const uint32_t i = blockIdx.x * kThreads + threadIdx.x;
+    __shared__ Range s_r[kThreads];
+    __shared__ uint32_t s_done[kPairItems];
+    const uint32_t ln = threadIdx.x % kWave, k0 = threadIdx.x / kWave * kWave;
+    const uint32_t i = blockIdx.x * kPairItems + ln;
     const bool me = i < n && w.cls[i] == kMiss;
     const uint64_t b = me ? w.base[i] : 0, t = me ? w.top[i] : 0;
-    bool inside = false;
-    const uint32_t jend = blockIdx.x * kThreads + kThreads;   // j < i <= this bound
+    if (k0 == 0) s_done[ln] = !me;
+    __syncthreads();
+    const uint32_t jend = blockIdx.x * kPairItems + kPairItems;   // j < i < this bound
     for (uint32_t j0 = 0; j0 < jend; j0 += kThreads) {
-        if (__syncthreads_or(me && !inside) == 0) break;  // every item here is decided
+        const bool open = s_done[ln] == 0;
+        if (__syncthreads_or(open) == 0) break;          // every item here is decided
         const uint32_t j = j0 + threadIdx.x;
         // Other blocks mark their inserts kNew while this loop runs: a miss
         // reads as kMiss or kNew, both mean "a miss of the old table".
         const uint8_t cj = j < n ? w.cls[j] : kInvalid;
         const bool jm = cj == kMiss || cj == kNew;
-        s_base[threadIdx.x] = jm ? w.base[j] : 0;
-        s_top[threadIdx.x] = jm ? w.top[j] : 0;
-        s_miss[threadIdx.x] = jm;
+        s_r[threadIdx.x] = jm ? Range{w.base[j], w.top[j]} : kNoRange;
         if (__syncthreads_or(jm) == 0) continue;         // no miss in this tile
-        if (me && !inside) {
-            const uint32_t lim = i - j0 < kThreads ? i - j0 : kThreads;   // j < i
-            for (uint32_t k = 0; k < lim; ++k)
-                if (s_miss[k] && s_base[k] <= b && t <= s_top[k]) {
-                    inside = true;
-                    break;
-                }
+        if (open) {
+            const uint32_t lim = i > j0 ? (i - j0 < kThreads ? i - j0 : kThreads) : 0;   // j < i
+            const uint32_t ke = lim < k0 + kWave ? lim : k0 + kWave;
+            bool in = false;
+            uint32_t k = k0;
+            for (; k + kPairStep <= ke && !in; k += kPairStep) {   // reads in flight together
+                Range r[kPairStep];
+#pragma unroll
+                for (uint32_t u = 0; u < kPairStep; ++u) r[u] = s_r[k + u];
+#pragma unroll
+                for (uint32_t u = 0; u < kPairStep; ++u) in |= r[u].base <= b && t <= r[u].top;
+            }
+            for (; k < ke && !in; ++k) in = s_r[k].base <= b && t <= s_r[k].top;
+            if (in) s_done[ln] = 1;
         }
         __syncthreads();
     }
-    if (me && !inside) w.cls[i] = kNew;
+    if (k0 == 0 && me && s_done[ln] == 0) w.cls[i] = kNew;
 }
 
 // One block: ranks of the inserts in batch order, their count, and whether
@@ -348,46 +371,88 @@ __global__ __launch_bounds__(kTopThreads) void k_reg_count(RegState g, RegWs w, 
 
 // For every range that is not inserted, the earlier insert with the smallest
 // (start, index) that contains it decides between that insert and the old
-// record it hit; and the (start, index) rank of each insert.
+// record it hit; and the (start, index) rank of each insert. Blocks of
+// kPairItems items as in k_reg_inserted; each wave keeps its own best
+// (start, index) or count over its quarters, merged at the end.
 __global__ __launch_bounds__(kThreads) void k_reg_owner(RegWs w, uint32_t n)
 {
-    __shared__ uint64_t s_base[kThreads], s_top[kThreads];
-    __shared__ uint8_t s_new[kThreads];
-    const uint32_t i = blockIdx.x * kThreads + threadIdx.x;
+    __shared__ Range s_r[kThreads];
+    __shared__ uint64_t s_bb[kThreads];
+    __shared__ uint32_t s_bj[kThreads];
+    const uint32_t ln = threadIdx.x % kWave, k0 = threadIdx.x / kWave * kWave;
+    const uint32_t i = blockIdx.x * kPairItems + ln;
     const uint8_t c = i < n ? w.cls[i] : kInvalid;
     const bool look = c == kMiss || c == kHit;           // looks for a containing insert
-    const uint64_t b = look || c == kNew ? w.base[i] : 0;
-    const uint64_t t = look || c == kNew ? w.top[i] : 0;
+    const bool ins = c == kNew;                          // ranks itself among inserts
+    const uint64_t b = look || ins ? w.base[i] : 0;
+    const uint64_t t = look || ins ? w.top[i] : 0;
     uint32_t best = UINT32_MAX, brank = 0;
     uint64_t bbase = 0;
-    const bool any = __syncthreads_or(look || c == kNew) != 0;
-    if (!any) return;                                    // uniform over the block
+    if (__syncthreads_or(look || ins) == 0) return;      // uniform over the block
     for (uint32_t j0 = 0; j0 < n; j0 += kThreads) {
         const uint32_t j = j0 + threadIdx.x;
         const bool jn = j < n && w.cls[j] == kNew;
-        s_base[threadIdx.x] = jn ? w.base[j] : 0;
-        s_top[threadIdx.x] = jn ? w.top[j] : 0;
-        s_new[threadIdx.x] = jn;
+        s_r[threadIdx.x] = jn ? Range{w.base[j], w.top[j]} : kNoRange;
         if (__syncthreads_or(jn) == 0) continue;         // no insert in this tile
         const uint32_t lim = n - j0 < kThreads ? n - j0 : kThreads;
         if (look) {
             const uint32_t jl = i > j0 ? (i - j0 < lim ? i - j0 : lim) : 0;   // j < i
-            for (uint32_t k = 0; k < jl; ++k)
-                if (s_new[k] && s_base[k] <= b && t <= s_top[k] &&
-                    (best == UINT32_MAX || s_base[k] < bbase)) {
+            const uint32_t ke = jl < k0 + kWave ? jl : k0 + kWave;
+            uint32_t k = k0;
+            for (; k + kPairStep <= ke; k += kPairStep) {
+                Range r[kPairStep];
+#pragma unroll
+                for (uint32_t u = 0; u < kPairStep; ++u) r[u] = s_r[k + u];
+#pragma unroll
+                for (uint32_t u = 0; u < kPairStep; ++u)
+                    if (r[u].base <= b && t <= r[u].top && (best == UINT32_MAX || r[u].base < bbase)) {
+                        best = j0 + k + u;
+                        bbase = r[u].base;
+                    }
+            }
+            for (; k < ke; ++k) {
+                const Range r = s_r[k];
+                if (r.base <= b && t <= r.top && (best == UINT32_MAX || r.base < bbase)) {
                     best = j0 + k;
-                    bbase = s_base[k];
+                    bbase = r.base;
                 }
-        } else if (c == kNew) {
-            for (uint32_t k = 0; k < lim; ++k)
-                brank += s_new[k] && (s_base[k] < b || (s_base[k] == b && j0 + k < i));
+            }
+        } else if (ins) {
+            const uint32_t ke = lim < k0 + kWave ? lim : k0 + kWave;
+            uint32_t k = k0;
+            for (; k + kPairStep <= ke; k += kPairStep) {
+                uint64_t rb[kPairStep];
+#pragma unroll
+                for (uint32_t u = 0; u < kPairStep; ++u) rb[u] = s_r[k + u].base;
+#pragma unroll
+                for (uint32_t u = 0; u < kPairStep; ++u) brank += rb[u] < b || (rb[u] == b && j0 + k + u < i);
+            }
+            for (; k < ke; ++k) {
+                const uint64_t rb = s_r[k].base;
+                brank += rb < b || (rb == b && j0 + k < i);
+            }
         }
         __syncthreads();
+    }
+    s_bb[threadIdx.x] = bbase;
+    s_bj[threadIdx.x] = look ? best : brank;
+    __syncthreads();
+    if (k0 != 0 || !(look || ins)) return;
+    for (uint32_t v = kWave; v < kThreads; v += kWave) {
+        const uint32_t oj = s_bj[v + ln];
+        const uint64_t ob = s_bb[v + ln];
+        if (ins) {
+            brank += oj;
+        } else if (oj != UINT32_MAX &&
+                   (best == UINT32_MAX || ob < bbase || (ob == bbase && oj < best))) {
+            best = oj;
+            bbase = ob;
+        }
     }
     if (c == kMiss || (c == kHit && best != UINT32_MAX && bbase < w.hstart[i])) {
         w.owner[i] = best;                               // a miss always finds one
         w.cls[i] = kHitNew;
-    } else if (c == kNew) {
+    } else if (ins) {
         w.brank[i] = brank;
     }
 }
@@ -493,25 +558,42 @@ __global__ __launch_bounds__(kThreads) void k_dereg_find(RegState g, RegWs w, co
 }
 
 // Calls before i naming the same record decide whether call i succeeds.
+// Blocks of kPairItems calls; each wave counts over its quarter of every tile.
 __global__ __launch_bounds__(kThreads) void k_dereg_status(RegState g, RegWs w, uint32_t n,
                                                            uint8_t *status)
 {
-    __shared__ uint32_t s_slot[kThreads];
-    const uint32_t i = blockIdx.x * kThreads + threadIdx.x;
+    __shared__ __align__(16) uint32_t s_slot[kThreads];
+    __shared__ uint32_t s_cnt[kThreads];
+    const uint32_t ln = threadIdx.x % kWave, k0 = threadIdx.x / kWave * kWave;
+    const uint32_t i = blockIdx.x * kPairItems + ln;
     const uint32_t me = i < n ? w.hit[i] : UINT32_MAX;
     uint32_t before = 0;
-    const uint32_t jend = blockIdx.x * kThreads + kThreads;
+    const uint32_t jend = blockIdx.x * kPairItems + kPairItems;
     for (uint32_t j0 = 0; j0 < jend; j0 += kThreads) {
         const uint32_t j = j0 + threadIdx.x;
         s_slot[threadIdx.x] = j < n ? w.hit[j] : UINT32_MAX;
         __syncthreads();
         if (me != UINT32_MAX) {
             const uint32_t lim = i > j0 ? (i - j0 < kThreads ? i - j0 : kThreads) : 0;
-            for (uint32_t k = 0; k < lim; ++k) before += s_slot[k] == me;
+            const uint32_t ke = lim < k0 + kWave ? lim : k0 + kWave;
+            uint32_t k = k0;
+            for (; k + 4 * kPairStep <= ke; k += 4 * kPairStep) {   // 16-byte reads in flight together
+                uint4 v[kPairStep];
+#pragma unroll
+                for (uint32_t u = 0; u < kPairStep; ++u)
+                    v[u] = *reinterpret_cast<const uint4 *>(&s_slot[k + 4 * u]);
+#pragma unroll
+                for (uint32_t u = 0; u < kPairStep; ++u)
+                    before += (v[u].x == me) + (v[u].y == me) + (v[u].z == me) + (v[u].w == me);
+            }
+            for (; k < ke; ++k) before += s_slot[k] == me;
         }
         __syncthreads();
     }
-    if (i >= n) return;
+    s_cnt[threadIdx.x] = before;
+    __syncthreads();
+    if (k0 != 0 || i >= n) return;
+    for (uint32_t v = kWave; v < kThreads; v += kWave) before += s_cnt[v + ln];
     uint8_t st = DMADESC_DEREG_STALE;
     if (me != UINT32_MAX) {
         const uint32_t r = g.refs[me];
@@ -627,6 +709,7 @@ hipError_t launch_reg_register(const RegArgs &a, hipStream_t s)
     RegWs w = carve(a.ws, a.n < 1 ? 1 : a.n, cap < 1 ? 1 : cap);
     const uint32_t n = (uint32_t)a.n;
     const unsigned nb = (n + kThreads - 1) / kThreads;
+    const unsigned pb = (n + kPairItems - 1) / kPairItems;
     const unsigned rb = (unsigned)((cap + kThreads - 1) / kThreads < 4096 ? (cap + kThreads - 1) / kThreads : 4096);
     if (rb) {
         hipLaunchKernelGGL(k_reg_starts, dim3(rb), dim3(kThreads), 0, s, g, w);
@@ -636,11 +719,11 @@ hipError_t launch_reg_register(const RegArgs &a, hipStream_t s)
     if (nb) {
         hipLaunchKernelGGL(k_reg_classify, dim3(nb), dim3(kThreads), 0, s, g, w, a.page_shift,
                            a.addr, a.size, n);
-        hipLaunchKernelGGL(k_reg_inserted, dim3(nb), dim3(kThreads), 0, s, w, n);
+        hipLaunchKernelGGL(k_reg_inserted, dim3(pb), dim3(kThreads), 0, s, w, n);
     }
     hipLaunchKernelGGL(k_reg_count, dim3(1), dim3(kTopThreads), 0, s, g, w, n, a.needed);
     if (nb) {
-        hipLaunchKernelGGL(k_reg_owner, dim3(nb), dim3(kThreads), 0, s, w, n);
+        hipLaunchKernelGGL(k_reg_owner, dim3(pb), dim3(kThreads), 0, s, w, n);
         hipLaunchKernelGGL(k_reg_apply, dim3(nb), dim3(kThreads), 0, s, g, w, n, a.handle,
                            a.kind);
         const unsigned ib = (unsigned)((cap + n + kThreads - 1) / kThreads < 4096
@@ -659,16 +742,17 @@ hipError_t launch_reg_deregister(const RegArgs &a, hipStream_t s)
     RegWs w = carve(a.ws, a.n < 1 ? 1 : a.n, cap < 1 ? 1 : cap);
     const uint32_t n = (uint32_t)a.n;
     const unsigned nb = (n + kThreads - 1) / kThreads;
+    const unsigned pb = (n + kPairItems - 1) / kPairItems;
     if (nb == 0 || cap == 0) {
         if (nb) {                                        // nothing is live: all stale
             hipLaunchKernelGGL(k_dereg_find, dim3(nb), dim3(kThreads), 0, s, g, w, a.handle_in, n);
-            hipLaunchKernelGGL(k_dereg_status, dim3(nb), dim3(kThreads), 0, s, g, w, n, a.status);
+            hipLaunchKernelGGL(k_dereg_status, dim3(pb), dim3(kThreads), 0, s, g, w, n, a.status);
         }
         return hipGetLastError();
     }
     const unsigned rb = (unsigned)((cap + kThreads - 1) / kThreads < 4096 ? (cap + kThreads - 1) / kThreads : 4096);
     hipLaunchKernelGGL(k_dereg_find, dim3(nb), dim3(kThreads), 0, s, g, w, a.handle_in, n);
-    hipLaunchKernelGGL(k_dereg_status, dim3(nb), dim3(kThreads), 0, s, g, w, n, a.status);
+    hipLaunchKernelGGL(k_dereg_status, dim3(pb), dim3(kThreads), 0, s, g, w, n, a.status);
     hipLaunchKernelGGL(k_dereg_drop, dim3(nb), dim3(kThreads), 0, s, g, w, n);
     // Prefixes of kept slots (storage) and kept entries (start order).
     scan_records<false, false>(KeptSlots{a.refs}, a.state, cap, w.chunk, w.pm, &w.scal[2], s);
