@@ -45,7 +45,6 @@ constexpr int kPer = 4;                              // records per thread in sc
 constexpr uint32_t kChunk = kThreads * kPer;         // records per scan block
 constexpr int kTopThreads = 1024;
 constexpr uint32_t kMaxChunks = DMADESC_REG_MAX_CAPACITY / kChunk;   // 16384
-constexpr uint32_t kBatchPer = DMADESC_REG_MAX_BATCH / kTopThreads; // 64
 static_assert(kMaxChunks % kTopThreads == 0, "chunk totals scan in one block");
 
 enum : uint8_t { kInvalid = DMADESC_REG_INVALID, kHit = DMADESC_REG_HIT, kNew = DMADESC_REG_NEW,
@@ -308,15 +307,28 @@ __global__ __launch_bounds__(kThreads) void k_reg_inserted(RegWs w, uint32_t n)
     if (k0 == 0) s_done[ln] = !me;
     __syncthreads();
     const uint32_t jend = blockIdx.x * kPairItems + kPairItems;   // j < i < this bound
+    // Tile columns are loaded one tile ahead, while the current tile is
+    // compared. Other blocks mark their inserts kNew while this loop runs: a
+    // miss reads as kMiss or kNew, both mean "a miss of the old table".
+    uint8_t cj = kInvalid;
+    uint64_t bj = 0, tj = 0;
+    if (threadIdx.x < n) {
+        cj = w.cls[threadIdx.x];
+        bj = w.base[threadIdx.x];
+        tj = w.top[threadIdx.x];
+    }
     for (uint32_t j0 = 0; j0 < jend; j0 += kThreads) {
         const bool open = s_done[ln] == 0;
         if (__syncthreads_or(open) == 0) break;          // every item here is decided
-        const uint32_t j = j0 + threadIdx.x;
-        // Other blocks mark their inserts kNew while this loop runs: a miss
-        // reads as kMiss or kNew, both mean "a miss of the old table".
-        const uint8_t cj = j < n ? w.cls[j] : kInvalid;
         const bool jm = cj == kMiss || cj == kNew;
-        s_r[threadIdx.x] = jm ? Range{w.base[j], w.top[j]} : kNoRange;
+        s_r[threadIdx.x] = jm ? Range{bj, tj} : kNoRange;
+        const uint32_t jn = j0 + kThreads + threadIdx.x;
+        cj = kInvalid;
+        if (j0 + kThreads < jend && jn < n) {
+            cj = w.cls[jn];
+            bj = w.base[jn];
+            tj = w.top[jn];
+        }
         if (__syncthreads_or(jm) == 0) continue;         // no miss in this tile
         if (open) {
             const uint32_t lim = i > j0 ? (i - j0 < kThreads ? i - j0 : kThreads) : 0;   // j < i
@@ -339,25 +351,42 @@ __global__ __launch_bounds__(kThreads) void k_reg_inserted(RegWs w, uint32_t n)
 }
 
 // One block: ranks of the inserts in batch order, their count, and whether
-// the table has room; the needed capacity is reported either way.
+// the table has room; the needed capacity is reported either way. Wave v
+// takes the v-th contiguous chunk of the batch, 64 items a round: one pass
+// counts, the other ranks by ballots after the earlier chunks' counts.
 __global__ __launch_bounds__(kTopThreads) void k_reg_count(RegState g, RegWs w, uint32_t n,
                                                            uint64_t *needed)
 {
-    __shared__ uint64_t scr[kTopThreads / kWave];
-    uint64_t s = 0;
-    for (uint32_t k = 0; k < kBatchPer; ++k) {
-        const uint32_t i = threadIdx.x * kBatchPer + k;
-        s += (i < n && w.cls[i] == kNew) ? 1u : 0u;
+    constexpr uint32_t kTopWaves = kTopThreads / kWave;
+    constexpr uint32_t kChunkItems = DMADESC_REG_MAX_BATCH / kTopWaves;
+    static_assert(kChunkItems % kWave == 0, "chunks are whole rounds");
+    __shared__ uint32_t s_tot[kTopWaves];
+    const uint32_t v = threadIdx.x / kWave, ln = threadIdx.x % kWave;
+    const uint32_t c0 = v * kChunkItems;
+    const uint32_t ce = n < c0 ? 0u : (n - c0 < kChunkItems ? n - c0 : kChunkItems);
+    uint32_t cnt = 0;
+    for (uint32_t r = 0; r < ce; r += kWave) {           // uniform over the wave
+        const uint32_t i = c0 + r + ln;
+        cnt += (uint32_t)__popcll(__ballot(r + ln < ce && w.cls[i] == kNew));
     }
-    uint64_t tot;
-    uint64_t run = block_excl<false, kTopThreads>(s, scr, &tot);
-    for (uint32_t k = 0; k < kBatchPer; ++k) {
-        const uint32_t i = threadIdx.x * kBatchPer + k;
-        if (i < n) {
-            w.rank[i] = (uint32_t)run;
+    if (ln == 0) s_tot[v] = cnt;
+    __syncthreads();
+    uint32_t run = 0, tot = 0;
+    for (uint32_t u = 0; u < kTopWaves; ++u) {
+        const uint32_t c = s_tot[u];
+        run += u < v ? c : 0u;
+        tot += c;
+    }
+    const uint64_t below = __lanemask_lt();
+    for (uint32_t r = 0; r < ce; r += kWave) {
+        const uint32_t i = c0 + r + ln;
+        const bool in = r + ln < ce;
+        const uint64_t m = __ballot(in && w.cls[i] == kNew);
+        if (in) {
+            w.rank[i] = run + (uint32_t)__popcll(m & below);
             w.newrefs[i] = 1;                            // by rank; ranks < n
-            run += w.cls[i] == kNew;
         }
+        run += (uint32_t)__popcll(m);
     }
     if (threadIdx.x == 0) {
         const uint64_t after = g.state[0] + tot;
@@ -389,10 +418,24 @@ __global__ __launch_bounds__(kThreads) void k_reg_owner(RegWs w, uint32_t n)
     uint32_t best = UINT32_MAX, brank = 0;
     uint64_t bbase = 0;
     if (__syncthreads_or(look || ins) == 0) return;      // uniform over the block
+    // Tile columns are loaded one tile ahead, while the current tile is compared.
+    uint8_t cj = kInvalid;
+    uint64_t bj = 0, tj = 0;
+    if (threadIdx.x < n) {
+        cj = w.cls[threadIdx.x];
+        bj = w.base[threadIdx.x];
+        tj = w.top[threadIdx.x];
+    }
     for (uint32_t j0 = 0; j0 < n; j0 += kThreads) {
-        const uint32_t j = j0 + threadIdx.x;
-        const bool jn = j < n && w.cls[j] == kNew;
-        s_r[threadIdx.x] = jn ? Range{w.base[j], w.top[j]} : kNoRange;
+        const bool jn = cj == kNew;
+        s_r[threadIdx.x] = jn ? Range{bj, tj} : kNoRange;
+        const uint32_t jx = j0 + kThreads + threadIdx.x;
+        cj = kInvalid;
+        if (jx < n) {
+            cj = w.cls[jx];
+            bj = w.base[jx];
+            tj = w.top[jx];
+        }
         if (__syncthreads_or(jn) == 0) continue;         // no insert in this tile
         const uint32_t lim = n - j0 < kThreads ? n - j0 : kThreads;
         if (look) {
@@ -558,25 +601,33 @@ __global__ __launch_bounds__(kThreads) void k_dereg_find(RegState g, RegWs w, co
 }
 
 // Calls before i naming the same record decide whether call i succeeds.
-// Blocks of kPairItems calls; each wave counts over its quarter of every tile.
+// Blocks of kPairItems calls; each wave counts over its quarter of every tile
+// and adds its count to s_before. A call that has seen as many earlier calls
+// as its record has references is stale whatever follows, so it stops there.
 __global__ __launch_bounds__(kThreads) void k_dereg_status(RegState g, RegWs w, uint32_t n,
                                                            uint8_t *status)
 {
     __shared__ __align__(16) uint32_t s_slot[kThreads];
-    __shared__ uint32_t s_cnt[kThreads];
+    __shared__ uint32_t s_before[kPairItems];
     const uint32_t ln = threadIdx.x % kWave, k0 = threadIdx.x / kWave * kWave;
     const uint32_t i = blockIdx.x * kPairItems + ln;
     const uint32_t me = i < n ? w.hit[i] : UINT32_MAX;
-    uint32_t before = 0;
+    const uint32_t r = me != UINT32_MAX ? g.refs[me] : 0u;
+    if (k0 == 0) s_before[ln] = 0;
+    __syncthreads();
     const uint32_t jend = blockIdx.x * kPairItems + kPairItems;
+    uint32_t hj = threadIdx.x < n ? w.hit[threadIdx.x] : UINT32_MAX;   // one tile ahead
     for (uint32_t j0 = 0; j0 < jend; j0 += kThreads) {
-        const uint32_t j = j0 + threadIdx.x;
-        s_slot[threadIdx.x] = j < n ? w.hit[j] : UINT32_MAX;
+        const bool open = me != UINT32_MAX && s_before[ln] < r;
+        if (__syncthreads_or(open) == 0) break;          // every call here is decided
+        s_slot[threadIdx.x] = hj;
+        const uint32_t jn = j0 + kThreads + threadIdx.x;
+        hj = j0 + kThreads < jend && jn < n ? w.hit[jn] : UINT32_MAX;
         __syncthreads();
-        if (me != UINT32_MAX) {
+        if (open) {
             const uint32_t lim = i > j0 ? (i - j0 < kThreads ? i - j0 : kThreads) : 0;
             const uint32_t ke = lim < k0 + kWave ? lim : k0 + kWave;
-            uint32_t k = k0;
+            uint32_t c = 0, k = k0;
             for (; k + 4 * kPairStep <= ke; k += 4 * kPairStep) {   // 16-byte reads in flight together
                 uint4 v[kPairStep];
 #pragma unroll
@@ -584,19 +635,17 @@ __global__ __launch_bounds__(kThreads) void k_dereg_status(RegState g, RegWs w, 
                     v[u] = *reinterpret_cast<const uint4 *>(&s_slot[k + 4 * u]);
 #pragma unroll
                 for (uint32_t u = 0; u < kPairStep; ++u)
-                    before += (v[u].x == me) + (v[u].y == me) + (v[u].z == me) + (v[u].w == me);
+                    c += (v[u].x == me) + (v[u].y == me) + (v[u].z == me) + (v[u].w == me);
             }
-            for (; k < ke; ++k) before += s_slot[k] == me;
+            for (; k < ke; ++k) c += s_slot[k] == me;
+            if (c) atomicAdd(&s_before[ln], c);
         }
         __syncthreads();
     }
-    s_cnt[threadIdx.x] = before;
-    __syncthreads();
     if (k0 != 0 || i >= n) return;
-    for (uint32_t v = kWave; v < kThreads; v += kWave) before += s_cnt[v + ln];
+    const uint32_t before = s_before[ln];                 // exact unless already >= r
     uint8_t st = DMADESC_DEREG_STALE;
     if (me != UINT32_MAX) {
-        const uint32_t r = g.refs[me];
         if (before + 1 < r) st = DMADESC_DEREG_OK;
         else if (before + 1 == r) st = DMADESC_DEREG_REMOVED;
     }
