@@ -61,15 +61,17 @@
  *  - Return value: 0 on success, or a negative errno value. On error nothing
  *    is launched and no output is touched:
  *      -EINVAL  null pointer where one is required, n >= 2^32, a parameter
- *               out of range (stated per call), workspace too small;
+ *               out of range (stated per call), workspace too small or not
+ *               256-byte aligned;
  *      -EIO     the HIP runtime refused a kernel launch.
  *    Errors in individual requests are not call errors: they are reported
  *    per request in an output column (stated per call).
  *  - All arithmetic is exact unsigned 64-bit integer arithmetic; outputs are
  *    bit-for-bit deterministic (no atomics decide any output position).
  *  - `ws` is a caller-owned device workspace of at least
- *    dmadesc_workspace_bytes(op, n, param) bytes (256-byte aligned). Its
- *    contents on entry are ignored and on return are unspecified.
+ *    dmadesc_workspace_bytes(op, n, param) bytes, 256-byte aligned (-EINVAL
+ *    otherwise). Its contents on entry are ignored and on return are
+ *    unspecified.
  */
 #ifndef DMADESC_H
 #define DMADESC_H

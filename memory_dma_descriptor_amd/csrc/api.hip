@@ -13,6 +13,13 @@ constexpr uint64_t kMaxLutEntries = 1ull << 48;  // heap < 2^64 bytes
 
 int launched(hipError_t e) { return e == hipSuccess ? 0 : -EIO; }
 
+// A workspace is present, at least `need` bytes and 256-byte aligned (the
+// kernels keep 64-bit atomics and 16-byte columns in it).
+bool ws_ok(const void *ws, size_t ws_bytes, size_t need)
+{
+    return ws && ws_bytes >= need && (reinterpret_cast<uintptr_t>(ws) & 255u) == 0;
+}
+
 int build_prp_common(const uint64_t *lut, uint64_t lut_entries, const uint64_t *off,
                      const uint64_t *len, uint64_t n, uint64_t list_bus_base,
                      uint64_t *list_pool, uint64_t pool_pages, uint64_t *prp1, uint64_t *prp2,
@@ -32,7 +39,7 @@ int build_prp_common(const uint64_t *lut, uint64_t lut_entries, const uint64_t *
         return -EINVAL;
     if (n > 0 && (!off || !len || !prp1 || !prp2 || !status)) return -EINVAL;
     const size_t need = dd::ws_build_prp(n);
-    if (need > 0 && (!ws || ws_bytes < need)) return -EINVAL;
+    if (need > 0 && !ws_ok(ws, ws_bytes, need)) return -EINVAL;
     dd::PrpArgs a{lut, lut_entries, off, len, n, list_bus_base, list_pool, pool_pages,
                   prp1, prp2, status, total_pages, ws, packed};
     return launched(dd::launch_build_prp(a, static_cast<hipStream_t>(stream)));
@@ -123,7 +130,7 @@ int dmadesc_partition_by_queue(const uint32_t *qid, uint64_t n, uint32_t nqueues
     if (!qoff || !n_invalid) return -EINVAL;
     if (n > 0 && (!qid || !perm)) return -EINVAL;
     const size_t need = dd::ws_partition(n, nqueues);
-    if (n > 0 && (!ws || ws_bytes < need)) return -EINVAL;
+    if (n > 0 && !ws_ok(ws, ws_bytes, need)) return -EINVAL;
     dd::SplitArgs a{qid, n, nqueues, perm, qoff, n_invalid, ws};
     return launched(dd::launch_partition(a, static_cast<hipStream_t>(stream)));
 }
@@ -141,7 +148,7 @@ int dmadesc_emit_sqe(const uint32_t *perm, const uint64_t *qoff, uint32_t nqueue
     if (!qoff || !ring || !depth || !free_slots || !tail || !cursor || !placed) return -EINVAL;
     if (n > 0 && (!perm || !status || !len || !slba || !prp1 || !prp2)) return -EINVAL;
     const size_t need = dd::ws_emit_sqe(nqueues);
-    if (!ws || ws_bytes < need) return -EINVAL;
+    if (!ws_ok(ws, ws_bytes, need)) return -EINVAL;
     dd::SqeArgs a{perm, qoff, nqueues, status, len, slba, prp1, prp2, n, opcode, nsid, lba_shift,
                   ring, depth, free_slots, tail, cursor, placed, req_of_slot, ws};
     return launched(dd::launch_emit_sqe(a, static_cast<hipStream_t>(stream)));
@@ -168,7 +175,7 @@ int dmadesc_build_put(const uint64_t *src, const uint64_t *dst, const uint64_t *
     if (most * n >= ((unsigned __int128)1 << 62)) return -EINVAL;
     if (n > 0 && (!src || !dst || !bytes || !pe || !first || !count || !status)) return -EINVAL;
     const size_t need = dd::ws_build_put(n);
-    if (need > 0 && (!ws || ws_bytes < need)) return -EINVAL;
+    if (need > 0 && !ws_ok(ws, ws_bytes, need)) return -EINVAL;
     dd::PutArgs a{src, dst, bytes, pe, n, local_base, heap_bytes, chunk_shift, npes, lkeys,
                   peer_base, rkeys, reinterpret_cast<uint64_t *>(desc), desc_cap, first, count,
                   status, total, ws};
@@ -196,7 +203,7 @@ int dmadesc_reg_register(uint64_t *start, uint64_t *end, uint64_t *id, uint32_t 
     if (!state || !needed) return -EINVAL;
     if (capacity > 0 && (!start || !end || !id || !refs || !by_start)) return -EINVAL;
     if (n > 0 && (!addr || !size || !handle || !kind)) return -EINVAL;
-    if (!ws || ws_bytes < dd::ws_registry(n, capacity)) return -EINVAL;
+    if (!ws_ok(ws, ws_bytes, dd::ws_registry(n, capacity))) return -EINVAL;
     dd::RegArgs a{start, end, id, refs, by_start, state, capacity, page_shift, addr, size,
                   nullptr, n, handle, kind, needed, nullptr, ws};
     return launched(dd::launch_reg_register(a, static_cast<hipStream_t>(stream)));
@@ -211,7 +218,7 @@ int dmadesc_reg_deregister(uint64_t *start, uint64_t *end, uint64_t *id, uint32_
     if (!state) return -EINVAL;
     if (capacity > 0 && (!start || !end || !id || !refs || !by_start)) return -EINVAL;
     if (n > 0 && (!handle || !status)) return -EINVAL;
-    if (!ws || ws_bytes < dd::ws_registry(n, capacity)) return -EINVAL;
+    if (!ws_ok(ws, ws_bytes, dd::ws_registry(n, capacity))) return -EINVAL;
     dd::RegArgs a{start, end, id, refs, by_start, state, capacity, 12, nullptr, nullptr,
                   handle, n, nullptr, nullptr, nullptr, status, ws};
     return launched(dd::launch_reg_deregister(a, static_cast<hipStream_t>(stream)));

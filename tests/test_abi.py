@@ -90,7 +90,8 @@ def test_build_prp_rejects_bad_arguments():
     f = dd.lib().dmadesc_build_prp
     ok = [P, 16, P, P, 8, 0x10000, P, 4, P, P, P, P, P, 1 << 20, NULL]
     for k, bad in [(5, 0x10008), (1, 1 << 48), (4, 1 << 32), (11, NULL), (0, NULL),
-                   (6, NULL), (6, P + 8), (2, NULL), (8, NULL), (12, NULL), (13, 8)]:
+                   (6, NULL), (6, P + 8), (2, NULL), (8, NULL), (12, NULL), (13, 8),
+                   (12, P + 8), (12, P + 128)]:
         args = list(ok)
         args[k] = bad
         assert f(*args) == EINVAL, (k, bad)
@@ -101,7 +102,8 @@ def test_build_prp_packed_rejects_bad_arguments():
     f = dd.lib().dmadesc_build_prp_packed
     ok = [P, 16, P, P, 8, 0x10000, P, 4, P, P, P, P, P, 1 << 20, NULL]
     for k, bad in [(5, 0x10008), (1, 1 << 48), (4, 1 << 32), (11, NULL), (0, NULL),
-                   (6, NULL), (6, P + 8), (2, NULL), (8, NULL), (12, NULL), (13, 8)]:
+                   (6, NULL), (6, P + 8), (2, NULL), (8, NULL), (12, NULL), (13, 8),
+                   (12, P + 8), (12, P + 128)]:
         args = list(ok)
         args[k] = bad
         assert f(*args) == EINVAL, (k, bad)
@@ -116,7 +118,7 @@ def test_partition_rejects_bad_arguments():
     f = dd.lib().dmadesc_partition_by_queue
     ok = [P, 100, 4, P, P, P, P, 1 << 20, NULL]
     for k, bad in [(2, 0), (2, 257), (1, 1 << 32), (4, NULL), (5, NULL), (0, NULL),
-                   (3, NULL), (6, NULL), (7, 16)]:
+                   (3, NULL), (6, NULL), (7, 16), (6, P + 64)]:
         args = list(ok)
         args[k] = bad
         assert f(*args) == EINVAL, (k, bad)
@@ -129,7 +131,7 @@ def test_emit_sqe_rejects_bad_arguments():
     for k, bad in [(2, 0), (2, 257), (8, 1 << 32), (9, 256), (11, 8), (11, 17),
                    (1, NULL), (12, NULL), (13, NULL), (14, NULL), (15, NULL), (16, NULL),
                    (17, NULL), (0, NULL), (3, NULL), (4, NULL), (5, NULL), (6, NULL),
-                   (7, NULL), (19, NULL), (20, 16)]:
+                   (7, NULL), (19, NULL), (20, 16), (19, P + 8)]:
         args = list(ok)
         args[k] = bad
         assert f(*args) == EINVAL, (k, bad)
@@ -142,7 +144,7 @@ def test_build_put_rejects_bad_arguments():
     for k, bad in [(4, 1 << 32), (11, 0), (11, 65537), (7, 11), (7, 32), (6, (1 << 30) + 5),
                    (6, 1 << 52), (8, NULL), (9, NULL), (10, NULL), (17, NULL), (12, NULL),
                    (12, P + 8), (0, NULL), (3, NULL), (14, NULL), (16, NULL), (18, NULL),
-                   (19, 16)]:
+                   (19, 16), (18, P + 8)]:
         args = list(ok)
         args[k] = bad
         assert f(*args) == EINVAL, (k, bad)
@@ -154,14 +156,14 @@ def test_registry_rejects_bad_arguments():
     ok = [P, P, P, P, P, P, 64, 12, P, P, 8, P, P, P, P, 1 << 30, NULL]
     for k, bad in [(7, 11), (7, 31), (10, 65537), (6, (1 << 24) + 1), (5, NULL), (13, NULL),
                    (0, NULL), (4, NULL), (8, NULL), (11, NULL), (12, NULL), (14, NULL),
-                   (15, 16)]:
+                   (15, 16), (14, P + 8)]:
         args = list(ok)
         args[k] = bad
         assert f(*args) == EINVAL, (k, bad)
     g = dd.lib().dmadesc_reg_deregister
     ok = [P, P, P, P, P, P, 64, P, 8, P, P, 1 << 30, NULL]
     for k, bad in [(8, 65537), (6, (1 << 24) + 1), (5, NULL), (0, NULL), (7, NULL), (9, NULL),
-                   (10, NULL), (11, 16)]:
+                   (10, NULL), (11, 16), (10, P + 8)]:
         args = list(ok)
         args[k] = bad
         assert g(*args) == EINVAL, (k, bad)
