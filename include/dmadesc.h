@@ -227,7 +227,8 @@ int dmadesc_build_prp(const uint64_t *lut, uint64_t lut_entries,
  *   extra check    (16 * lut_entries + 2) * n >= 2^62 -> -EINVAL
  * A batch's lists fill about (entries / 511) pages instead of one page or
  * more per list, and are written as one dense stream.
- * Workspace: dmadesc_workspace_bytes(DMADESC_OP_BUILD_PRP, n, 0).
+ * Workspace: dmadesc_workspace_bytes(DMADESC_OP_BUILD_PRP, n, 0), with the
+ * same 8-byte header on return as dmadesc_build_prp (blocks, expired waits).
  */
 int dmadesc_build_prp_packed(const uint64_t *lut, uint64_t lut_entries,
                              const uint64_t *off, const uint64_t *len, uint64_t n,
@@ -352,7 +353,9 @@ typedef struct dmadesc_put_desc {
  * batch needs). Descriptors of refused puts are not written; no other
  * descriptor slot is written. Extra check: n * (most pieces per put) >= 2^62
  * -> -EINVAL.
- * Workspace: dmadesc_workspace_bytes(DMADESC_OP_BUILD_PUT, n, 0).
+ * Workspace: dmadesc_workspace_bytes(DMADESC_OP_BUILD_PUT, n, 0); as for
+ * dmadesc_build_prp, its first 8 bytes hold on return a block counter and a
+ * count of bounded waits that expired (0 when blocks make progress).
  */
 int dmadesc_build_put(const uint64_t *src, const uint64_t *dst, const uint64_t *bytes,
                       const uint32_t *pe, uint64_t n, uint64_t local_base, uint64_t heap_bytes,

@@ -24,12 +24,20 @@ def check_put(src, dst, nbytes, pe, local_base, heap, shift, lkeys, peer_base, r
                          rkeys, cap, desc=want)
     desc = torch.full((max(cap, 1), 4), gc.CANARY_I64, dtype=torch.int64,
                       device="cuda").view(torch.uint64)
+    n = len(src)
+    ws = torch.full((max(dd.workspace_bytes(dd.OP_BUILD_PUT, n), 8),), 0xAB,
+                    dtype=torch.uint8, device="cuda")
     g = dd.build_put(gc.dev(np.asarray(src, np.uint64)), gc.dev(np.asarray(dst, np.uint64)),
                      gc.dev(np.asarray(nbytes, np.uint64)), gc.dev(np.asarray(pe, np.uint32)),
                      local_base, heap, shift, gc.dev(np.asarray(lkeys, np.uint32)),
                      gc.dev(np.asarray(peer_base, np.uint64)),
-                     gc.dev(np.asarray(rkeys, np.uint32)), desc[:cap] if cap else desc[:0])
+                     gc.dev(np.asarray(rkeys, np.uint32)), desc[:cap] if cap else desc[:0],
+                     ws=ws)
     torch.cuda.synchronize()
+    if n:
+        # workspace header: blocks that ran, and bounded waits that expired
+        blocks, timeouts = gc.host(ws[:8]).view(np.uint32)
+        assert 1 <= blocks <= n and timeouts == 0, (ctx, blocks, timeouts)
     for k in ("first", "count", "status"):
         got = gc.host(g[k])
         if not np.array_equal(got, o[k]):
