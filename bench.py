@@ -399,8 +399,9 @@ def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py: this build runs on exactly one GPU (requests are independent; "
-              "see the sharding design); use --gpus 1", file=sys.stderr, flush=True)
+        print("bench.py: the benchmark runs on one GPU only (requests are independent, so "
+              "a batch would shard by index range with no exchange); use --gpus 1",
+              file=sys.stderr, flush=True)
         sys.exit(2)
 
     import numpy as np
