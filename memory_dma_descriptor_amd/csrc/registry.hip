@@ -73,9 +73,10 @@ struct RegWs {
     uint64_t *hstart;       // start of the hit record (kHit)
     uint32_t *rank;         // rank among inserts (kNew)
     uint32_t *brank;        // rank of an insert in (start, batch index) order
-    uint32_t *owner;        // batch index of the containing insert (kHitNew)
+    uint32_t *owner;        // rank of the containing insert (kHitNew)
     uint32_t *newrefs;      // references of each insert, by rank
     uint64_t *newbase;      // start of each insert, by brank
+    uint64_t *ibase, *itop; // rounded range of each insert, by rank
     // per record (capacity)
     uint64_t *sstart;       // starts in start order
     uint64_t *pm;           // running maximum of ends in start order
@@ -381,10 +382,16 @@ __global__ __launch_bounds__(kTopThreads) void k_reg_count(RegState g, RegWs w, 
     for (uint32_t r = 0; r < ce; r += kWave) {
         const uint32_t i = c0 + r + ln;
         const bool in = r + ln < ce;
-        const uint64_t m = __ballot(in && w.cls[i] == kNew);
+        const bool nw = in && w.cls[i] == kNew;
+        const uint64_t m = __ballot(nw);
         if (in) {
-            w.rank[i] = run + (uint32_t)__popcll(m & below);
+            const uint32_t rk = run + (uint32_t)__popcll(m & below);
+            w.rank[i] = rk;
             w.newrefs[i] = 1;                            // by rank; ranks < n
+            if (nw) {                                    // the inserts' ranges, by rank
+                w.ibase[rk] = w.base[i];
+                w.itop[rk] = w.top[i];
+            }
         }
         run += (uint32_t)__popcll(m);
     }
@@ -400,14 +407,18 @@ __global__ __launch_bounds__(kTopThreads) void k_reg_count(RegState g, RegWs w, 
 
 // For every range that is not inserted, the earlier insert with the smallest
 // (start, index) that contains it decides between that insert and the old
-// record it hit; and the (start, index) rank of each insert. Blocks of
-// kPairItems items as in k_reg_inserted; each wave keeps its own best
-// (start, index) or count over its quarters, merged at the end.
+// record it hit; and the (start, index) rank of each insert. Both questions
+// are about inserts only, so they walk the inserts' ranges by rank (batch
+// order among inserts), 256 at a time through LDS: item i meets the rank[i]
+// inserts before it, an insert meets all of them, and (start, rank) orders
+// inserts as (start, index) does. Blocks of kPairItems items, each wave on a
+// quarter of every tile, partial answers merged at the end.
 __global__ __launch_bounds__(kThreads) void k_reg_owner(RegWs w, uint32_t n)
 {
     __shared__ Range s_r[kThreads];
     __shared__ uint64_t s_bb[kThreads];
     __shared__ uint32_t s_bj[kThreads];
+    __shared__ uint32_t s_jend;
     const uint32_t ln = threadIdx.x % kWave, k0 = threadIdx.x / kWave * kWave;
     const uint32_t i = blockIdx.x * kPairItems + ln;
     const uint8_t c = i < n ? w.cls[i] : kInvalid;
@@ -415,31 +426,26 @@ __global__ __launch_bounds__(kThreads) void k_reg_owner(RegWs w, uint32_t n)
     const bool ins = c == kNew;                          // ranks itself among inserts
     const uint64_t b = look || ins ? w.base[i] : 0;
     const uint64_t t = look || ins ? w.top[i] : 0;
+    const uint32_t ri = look || ins ? w.rank[i] : 0;     // inserts before item i
     uint32_t best = UINT32_MAX, brank = 0;
     uint64_t bbase = 0;
-    if (__syncthreads_or(look || ins) == 0) return;      // uniform over the block
-    // Tile columns are loaded one tile ahead, while the current tile is compared.
-    uint8_t cj = kInvalid;
-    uint64_t bj = 0, tj = 0;
-    if (threadIdx.x < n) {
-        cj = w.cls[threadIdx.x];
-        bj = w.base[threadIdx.x];
-        tj = w.top[threadIdx.x];
-    }
-    for (uint32_t j0 = 0; j0 < n; j0 += kThreads) {
-        const bool jn = cj == kNew;
-        s_r[threadIdx.x] = jn ? Range{bj, tj} : kNoRange;
-        const uint32_t jx = j0 + kThreads + threadIdx.x;
-        cj = kInvalid;
-        if (jx < n) {
-            cj = w.cls[jx];
-            bj = w.base[jx];
-            tj = w.top[jx];
-        }
-        if (__syncthreads_or(jn) == 0) continue;         // no insert in this tile
-        const uint32_t lim = n - j0 < kThreads ? n - j0 : kThreads;
+    // Inserts the block needs: all of them if it holds one, else those
+    // before its last looking item.
+    if (threadIdx.x == 0) s_jend = 0;
+    __syncthreads();
+    if (k0 == 0 && (look || ins)) atomicMax(&s_jend, ins ? (uint32_t)w.scal[0] : ri);
+    __syncthreads();
+    const uint32_t jend = s_jend;
+    if (jend == 0) return;                               // uniform over the block
+    Range nx = threadIdx.x < jend ? Range{w.ibase[threadIdx.x], w.itop[threadIdx.x]} : kNoRange;
+    for (uint32_t j0 = 0; j0 < jend; j0 += kThreads) {
+        s_r[threadIdx.x] = nx;
+        const uint32_t jx = j0 + kThreads + threadIdx.x;  // next tile, loaded while this one is used
+        nx = jx < jend ? Range{w.ibase[jx], w.itop[jx]} : kNoRange;
+        __syncthreads();
+        const uint32_t lim = jend - j0 < kThreads ? jend - j0 : kThreads;
         if (look) {
-            const uint32_t jl = i > j0 ? (i - j0 < lim ? i - j0 : lim) : 0;   // j < i
+            const uint32_t jl = ri > j0 ? (ri - j0 < lim ? ri - j0 : lim) : 0;   // rank < ri
             const uint32_t ke = jl < k0 + kWave ? jl : k0 + kWave;
             uint32_t k = k0;
             for (; k + kPairStep <= ke; k += kPairStep) {
@@ -468,11 +474,11 @@ __global__ __launch_bounds__(kThreads) void k_reg_owner(RegWs w, uint32_t n)
 #pragma unroll
                 for (uint32_t u = 0; u < kPairStep; ++u) rb[u] = s_r[k + u].base;
 #pragma unroll
-                for (uint32_t u = 0; u < kPairStep; ++u) brank += rb[u] < b || (rb[u] == b && j0 + k + u < i);
+                for (uint32_t u = 0; u < kPairStep; ++u) brank += rb[u] < b || (rb[u] == b && j0 + k + u < ri);
             }
             for (; k < ke; ++k) {
                 const uint64_t rb = s_r[k].base;
-                brank += rb < b || (rb == b && j0 + k < i);
+                brank += rb < b || (rb == b && j0 + k < ri);
             }
         }
         __syncthreads();
@@ -521,9 +527,9 @@ __global__ __launch_bounds__(kThreads) void k_reg_apply(RegState g, RegWs w, uin
         h = next + w.rank[i];
         w.newbase[w.brank[i]] = w.base[i];
     } else if (c == kHitNew) {
-        const uint32_t o = w.owner[i];
-        h = next + w.rank[o];
-        atomicAdd(&w.newrefs[w.rank[o]], 1u);
+        const uint32_t o = w.owner[i];                   // rank of the insert
+        h = next + o;
+        atomicAdd(&w.newrefs[o], 1u);
     }
     handle[i] = h;
     kind[i] = c;
@@ -725,6 +731,8 @@ RegWs carve(void *ws, uint64_t n, uint64_t cap)
     w.owner = c.take<uint32_t>(n);
     w.newrefs = c.take<uint32_t>(n);
     w.newbase = c.take<uint64_t>(n);
+    w.ibase = c.take<uint64_t>(n);
+    w.itop = c.take<uint64_t>(n);
     w.sstart = c.take<uint64_t>(cap);
     w.pm = c.take<uint64_t>(cap);
     w.merged = c.take<uint32_t>(cap + n);
@@ -740,7 +748,7 @@ RegWs carve(void *ws, uint64_t n, uint64_t cap)
 
 uint64_t carve_bytes(uint64_t n, uint64_t cap)
 {
-    return 10 * align256(n * 8) + 4 * align256(cap * 8) + 3 * align256(cap * 4) +
+    return 12 * align256(n * 8) + 4 * align256(cap * 8) + 3 * align256(cap * 4) +
            align256((cap + n) * 4) + align256((uint64_t)kMaxChunks * 8) + 256;
 }
 
