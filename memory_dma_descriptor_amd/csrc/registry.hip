@@ -77,6 +77,8 @@ struct RegWs {
     uint32_t *newrefs;      // references of each insert, by rank
     uint64_t *newbase;      // start of each insert, by brank
     uint64_t *ibase, *itop; // rounded range of each insert, by rank
+    uint64_t *mbase, *mtop; // rounded range of each miss, by miss rank
+    uint32_t *mrank;        // misses before each item
     // per record (capacity)
     uint64_t *sstart;       // starts in start order
     uint64_t *pm;           // running maximum of ends in start order
@@ -293,46 +295,74 @@ __global__ __launch_bounds__(kThreads) void k_reg_classify(RegState g, RegWs w, 
     w.hit[i] = hit;
 }
 
-// inserted(i) = miss and no earlier miss contains it. A block holds
-// kPairItems items; every earlier item j passes through LDS 256 at a time and
-// each wave compares the block's items with its own quarter of the tile.
-// s_done[l] turns 1 once some wave finds a miss containing item l.
+// One block: the misses in batch order. mrank[i] = misses before item i; the
+// misses' ranges go to their ranks. Wave v ranks the v-th contiguous chunk
+// of the batch by ballots after the earlier chunks' counts.
+__global__ __launch_bounds__(kTopThreads) void k_reg_misses(RegWs w, uint32_t n)
+{
+    constexpr uint32_t kTopWaves = kTopThreads / kWave;
+    constexpr uint32_t kChunkItems = DMADESC_REG_MAX_BATCH / kTopWaves;
+    static_assert(kChunkItems % kWave == 0, "chunks are whole rounds");
+    __shared__ uint32_t s_tot[kTopWaves];
+    const uint32_t v = threadIdx.x / kWave, ln = threadIdx.x % kWave;
+    const uint32_t c0 = v * kChunkItems;
+    const uint32_t ce = n < c0 ? 0u : (n - c0 < kChunkItems ? n - c0 : kChunkItems);
+    uint32_t cnt = 0;
+    for (uint32_t r = 0; r < ce; r += kWave)             // uniform over the wave
+        cnt += (uint32_t)__popcll(__ballot(r + ln < ce && w.cls[c0 + r + ln] == kMiss));
+    if (ln == 0) s_tot[v] = cnt;
+    __syncthreads();
+    uint32_t run = 0;
+    for (uint32_t u = 0; u < v; ++u) run += s_tot[u];
+    const uint64_t below = __lanemask_lt();
+    for (uint32_t r = 0; r < ce; r += kWave) {
+        const uint32_t i = c0 + r + ln;
+        const bool in = r + ln < ce;
+        const bool miss = in && w.cls[i] == kMiss;
+        const uint64_t m = __ballot(miss);
+        if (in) {
+            const uint32_t rk = run + (uint32_t)__popcll(m & below);
+            w.mrank[i] = rk;
+            if (miss) {
+                w.mbase[rk] = w.base[i];
+                w.mtop[rk] = w.top[i];
+            }
+        }
+        run += (uint32_t)__popcll(m);
+    }
+}
+
+// inserted(i) = miss and no earlier miss contains it. The earlier misses are
+// the mrank[i] first entries of the misses' ranges by rank; they pass through
+// LDS 256 at a time. A block holds kPairItems items and each wave compares
+// them with its own quarter of the tile. s_done[l] turns 1 once some wave
+// finds a miss containing item l.
 __global__ __launch_bounds__(kThreads) void k_reg_inserted(RegWs w, uint32_t n)
 {
     __shared__ Range s_r[kThreads];
     __shared__ uint32_t s_done[kPairItems];
+    __shared__ uint32_t s_jend;
     const uint32_t ln = threadIdx.x % kWave, k0 = threadIdx.x / kWave * kWave;
     const uint32_t i = blockIdx.x * kPairItems + ln;
     const bool me = i < n && w.cls[i] == kMiss;
     const uint64_t b = me ? w.base[i] : 0, t = me ? w.top[i] : 0;
+    const uint32_t mi = me ? w.mrank[i] : 0;             // misses before item i
+    if (threadIdx.x == 0) s_jend = 0;
     if (k0 == 0) s_done[ln] = !me;
     __syncthreads();
-    const uint32_t jend = blockIdx.x * kPairItems + kPairItems;   // j < i < this bound
-    // Tile columns are loaded one tile ahead, while the current tile is
-    // compared. Other blocks mark their inserts kNew while this loop runs: a
-    // miss reads as kMiss or kNew, both mean "a miss of the old table".
-    uint8_t cj = kInvalid;
-    uint64_t bj = 0, tj = 0;
-    if (threadIdx.x < n) {
-        cj = w.cls[threadIdx.x];
-        bj = w.base[threadIdx.x];
-        tj = w.top[threadIdx.x];
-    }
+    if (k0 == 0 && me) atomicMax(&s_jend, mi);
+    __syncthreads();
+    const uint32_t jend = s_jend;                        // misses the block needs
+    Range nx = threadIdx.x < jend ? Range{w.mbase[threadIdx.x], w.mtop[threadIdx.x]} : kNoRange;
     for (uint32_t j0 = 0; j0 < jend; j0 += kThreads) {
         const bool open = s_done[ln] == 0;
         if (__syncthreads_or(open) == 0) break;          // every item here is decided
-        const bool jm = cj == kMiss || cj == kNew;
-        s_r[threadIdx.x] = jm ? Range{bj, tj} : kNoRange;
-        const uint32_t jn = j0 + kThreads + threadIdx.x;
-        cj = kInvalid;
-        if (j0 + kThreads < jend && jn < n) {
-            cj = w.cls[jn];
-            bj = w.base[jn];
-            tj = w.top[jn];
-        }
-        if (__syncthreads_or(jm) == 0) continue;         // no miss in this tile
+        s_r[threadIdx.x] = nx;
+        const uint32_t jx = j0 + kThreads + threadIdx.x;  // next tile, loaded while this one is used
+        nx = jx < jend ? Range{w.mbase[jx], w.mtop[jx]} : kNoRange;
+        __syncthreads();
         if (open) {
-            const uint32_t lim = i > j0 ? (i - j0 < kThreads ? i - j0 : kThreads) : 0;   // j < i
+            const uint32_t lim = mi > j0 ? (mi - j0 < kThreads ? mi - j0 : kThreads) : 0;   // rank < mi
             const uint32_t ke = lim < k0 + kWave ? lim : k0 + kWave;
             bool in = false;
             uint32_t k = k0;
@@ -733,6 +763,9 @@ RegWs carve(void *ws, uint64_t n, uint64_t cap)
     w.newbase = c.take<uint64_t>(n);
     w.ibase = c.take<uint64_t>(n);
     w.itop = c.take<uint64_t>(n);
+    w.mbase = c.take<uint64_t>(n);
+    w.mtop = c.take<uint64_t>(n);
+    w.mrank = c.take<uint32_t>(n);
     w.sstart = c.take<uint64_t>(cap);
     w.pm = c.take<uint64_t>(cap);
     w.merged = c.take<uint32_t>(cap + n);
@@ -748,7 +781,7 @@ RegWs carve(void *ws, uint64_t n, uint64_t cap)
 
 uint64_t carve_bytes(uint64_t n, uint64_t cap)
 {
-    return 12 * align256(n * 8) + 4 * align256(cap * 8) + 3 * align256(cap * 4) +
+    return 15 * align256(n * 8) + 4 * align256(cap * 8) + 3 * align256(cap * 4) +
            align256((cap + n) * 4) + align256((uint64_t)kMaxChunks * 8) + 256;
 }
 
@@ -776,6 +809,7 @@ hipError_t launch_reg_register(const RegArgs &a, hipStream_t s)
     if (nb) {
         hipLaunchKernelGGL(k_reg_classify, dim3(nb), dim3(kThreads), 0, s, g, w, a.page_shift,
                            a.addr, a.size, n);
+        hipLaunchKernelGGL(k_reg_misses, dim3(1), dim3(kTopThreads), 0, s, w, n);
         hipLaunchKernelGGL(k_reg_inserted, dim3(pb), dim3(kThreads), 0, s, w, n);
     }
     hipLaunchKernelGGL(k_reg_count, dim3(1), dim3(kTopThreads), 0, s, g, w, n, a.needed);
