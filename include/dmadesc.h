@@ -52,7 +52,8 @@
  * ---------------------------------------
  *  - Every pointer argument is caller-owned DEVICE memory on the current HIP
  *    device unless marked "host". The library allocates nothing, keeps no
- *    state between calls and retains no pointer after returning.
+ *    state between calls (apart from the test bound set by
+ *    dmadesc_debug_wait_limit) and retains no pointer after returning.
  *  - Every call is asynchronous on `stream` (a hipStream_t; NULL = the
  *    device's null stream). Outputs are valid once the caller synchronizes
  *    that stream or orders later work behind it on the same stream
@@ -96,8 +97,16 @@ enum dmadesc_prp_status {
     DMADESC_PRP_OK = 0,
     DMADESC_PRP_EINVAL = 1, /* len == 0, off not a multiple of 4, or off+len wraps */
     DMADESC_PRP_ERANGE = 2, /* off + len > lut_entries * 64 KiB (past the heap)     */
-    DMADESC_PRP_ENOSPC = 3  /* the request's list pages pass pool_pages            */
+    DMADESC_PRP_ENOSPC = 3, /* the request's list pages pass pool_pages            */
+    DMADESC_PRP_EBUSY = 4   /* the slot scan of the request's block did not finish:
+                               a bounded wait expired (see dmadesc_debug_wait_limit);
+                               nothing was written for the request              */
 };
+
+/* Default bound on the polls of one wait of the device-wide slot scan (the
+ * decoupled look-back of dmadesc_build_prp, dmadesc_build_prp_packed and
+ * dmadesc_build_put); a poll sleeps about 0.1 us, so the default is seconds. */
+#define DMADESC_DEFAULT_WAIT_POLLS (1u << 22)
 
 /* Operation codes for dmadesc_workspace_bytes. */
 enum dmadesc_op {
@@ -130,7 +139,8 @@ enum dmadesc_op {
  * Region table (device arrays, `nregions` entries, nregions < 2^31): sorted
  * by start, non-overlapping (end[r] <= start[r+1]), start[r] < end[r]; end is
  * exclusive. Abutting regions are allowed. A table that breaks these rules
- * gives unspecified (but memory-safe) results.
+ * gives unspecified (but memory-safe) results; dmadesc_mr_table_check tells
+ * the two apart.
  *   reg_start  u64[nregions]   region start address
  *   reg_end    u64[nregions]   region end address (exclusive)
  *   reg_lkey   u32[nregions]   local key returned on a hit
@@ -151,6 +161,28 @@ int dmadesc_mr_lookup(const uint64_t *reg_start, const uint64_t *reg_end,
                       int32_t *handle, uint32_t *lkey, uint8_t *kind,
                       uint64_t *rbase, uint64_t *rend,
                       void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * dmadesc_mr_table_check - validation of a region table (the debug mode of
+ * dmadesc_mr_lookup).
+ *
+ * [NCCL-26] "IB Backend MR Cache" lets overlapping records stand side by side
+ * after partial-overlap registrations, which leaves the containing record of
+ * a range ambiguous; the lookup therefore takes sorted, non-overlapping,
+ * page-aligned tables only. This call checks a table on the device: region r
+ * is at fault when start[r] >= end[r], a bound is not a multiple of
+ * 2^page_shift, or end[r] > start[r+1].
+ *   scratch     device u64 the check writes (8-byte aligned)
+ *   first_bad   host u64 or NULL: the smallest faulty index, UINT64_MAX when
+ *               there is none
+ * Returns 0 for a valid table, -EINVAL for a faulty one (or for bad
+ * arguments: page_shift outside 12..30, nregions >= 2^31, null or unaligned
+ * scratch, null arrays with nregions > 0), -EIO if the runtime fails. Unlike
+ * every other call it synchronizes `stream` before it returns.
+ */
+int dmadesc_mr_table_check(const uint64_t *reg_start, const uint64_t *reg_end,
+                           uint32_t nregions, uint32_t page_shift, uint64_t *scratch,
+                           uint64_t *first_bad, void *stream);
 
 /*
  * dmadesc_build_prp - GPU-page table -> NVMe PRP1/PRP2 and chained PRP lists.
@@ -189,10 +221,16 @@ int dmadesc_mr_lookup(const uint64_t *reg_start, const uint64_t *reg_end,
  *                                  *total_pages pages serves them all.
  * Per request, with pages p = ((off & 4095) + len + 4095) >> 12, entries
  * m = p - 1 and, for p >= 3, list pages L = ceil((m - 1) / 511).
+ * Slot scan: list pages are handed out by a one-pass device-wide scan over
+ * blocks of 1,024 requests whose waits are bounded. A block whose wait
+ * expires (never at the default bound while blocks make progress) refuses
+ * its list requests with DMADESC_PRP_EBUSY (prp1 = prp2 = 0, no list
+ * entries); every other request is built exactly as above, and if the
+ * batch's last block expired *total_pages is UINT64_MAX.
  * Workspace: dmadesc_workspace_bytes(DMADESC_OP_BUILD_PRP, n, 0); its
- * first 8 bytes hold, on return, a block counter and a count of bounded
- * waits that expired (always 0 when blocks make progress; read it after
- * synchronizing to check).
+ * first 8 bytes hold, on return, a block counter (u32) and the count of
+ * blocks whose wait expired (u32; read it after synchronizing: nonzero
+ * means some requests carry DMADESC_PRP_EBUSY).
  */
 int dmadesc_build_prp(const uint64_t *lut, uint64_t lut_entries,
                       const uint64_t *off, const uint64_t *len, uint64_t n,
@@ -228,7 +266,9 @@ int dmadesc_build_prp(const uint64_t *lut, uint64_t lut_entries,
  * A batch's lists fill about (entries / 511) pages instead of one page or
  * more per list, and are written as one dense stream.
  * Workspace: dmadesc_workspace_bytes(DMADESC_OP_BUILD_PRP, n, 0), with the
- * same 8-byte header on return as dmadesc_build_prp (blocks, expired waits).
+ * same 8-byte header on return as dmadesc_build_prp (blocks, expired waits);
+ * an expired wait refuses the block's list requests with DMADESC_PRP_EBUSY,
+ * as in dmadesc_build_prp.
  */
 int dmadesc_build_prp_packed(const uint64_t *lut, uint64_t lut_entries,
                              const uint64_t *off, const uint64_t *len, uint64_t n,
@@ -349,13 +389,15 @@ typedef struct dmadesc_put_desc {
  * count over all puts, refused ones included), count u32[n] (its pieces; 0
  * for EINVAL/ERANGE), status u8[n] (enum dmadesc_prp_status: EINVAL zero bytes
  * or pe >= npes, ERANGE past the heap on either side, ENOSPC first + count >
- * desc_cap, refused puts are a suffix), *total (device u64: descriptors the
- * batch needs). Descriptors of refused puts are not written; no other
- * descriptor slot is written. Extra check: n * (most pieces per put) >= 2^62
- * -> -EINVAL.
+ * desc_cap, refused puts are a suffix; EBUSY: the slot scan of the put's
+ * block did not finish, first = UINT64_MAX), *total (device u64: descriptors
+ * the batch needs; UINT64_MAX if the last block's scan did not finish).
+ * Descriptors of refused puts are not written; no other descriptor slot is
+ * written. Extra check: n * (most pieces per put) >= 2^62 -> -EINVAL.
  * Workspace: dmadesc_workspace_bytes(DMADESC_OP_BUILD_PUT, n, 0); as for
- * dmadesc_build_prp, its first 8 bytes hold on return a block counter and a
- * count of bounded waits that expired (0 when blocks make progress).
+ * dmadesc_build_prp, its first 8 bytes hold on return a block counter and
+ * the count of blocks whose bounded wait expired (0 when blocks make
+ * progress; nonzero means some puts carry DMADESC_PRP_EBUSY).
  */
 int dmadesc_build_put(const uint64_t *src, const uint64_t *dst, const uint64_t *bytes,
                       const uint32_t *pe, uint64_t n, uint64_t local_base, uint64_t heap_bytes,
@@ -483,6 +525,13 @@ const char *dmadesc_strerror(int err);
 
 /* Library ABI version (host-only). */
 int dmadesc_version(void);
+
+/* Sets the process-wide bound on the polls of one wait of the slot scan
+ * (DMADESC_DEFAULT_WAIT_POLLS at load; 0 makes a wait give up at the first
+ * poll that finds a predecessor not yet published) for calls launched
+ * afterwards, and returns the previous bound. For tests of the refusal path
+ * (DMADESC_PRP_EBUSY): every kernel still ends normally at any bound. */
+uint32_t dmadesc_debug_wait_limit(uint32_t polls);
 
 #ifdef __cplusplus
 }

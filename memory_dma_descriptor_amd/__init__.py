@@ -17,10 +17,11 @@ from . import _build
 __all__ = ["mr_lookup", "build_prp", "build_prp_packed", "partition_by_queue", "emit_sqe",
            "ring_addresses", "DeviceRegistry", "build_put", "cq_slots", "cq_attach",
            "cq_mirror", "cq_slot_state",
-           "workspace_bytes", "DmadescError", "lib", "LIB_PATH", "MAX_QUEUES",
+           "workspace_bytes", "DmadescError", "DmadescRefused", "lib", "LIB_PATH", "MAX_QUEUES",
            "SQ_MAX_DEPTH",
+           "mr_table_check", "debug_wait_limit", "DEFAULT_WAIT_POLLS",
            "MISS", "EXACT", "CONTAINED", "INVALID",
-           "PRP_OK", "PRP_EINVAL", "PRP_ERANGE", "PRP_ENOSPC"]
+           "PRP_OK", "PRP_EINVAL", "PRP_ERANGE", "PRP_ENOSPC", "PRP_EBUSY"]
 
 LIB_PATH = _build.LIB
 MAX_QUEUES = 256
@@ -30,7 +31,8 @@ REG_MAX_BATCH, REG_MAX_CAPACITY = 65536, 1 << 24
 REG_INVALID, REG_HIT, REG_NEW, REG_HIT_NEW, REG_NOSPACE = 0, 1, 2, 3, 4
 DEREG_OK, DEREG_REMOVED, DEREG_STALE = 0, 1, 2
 MISS, EXACT, CONTAINED, INVALID = 0, 1, 2, 3
-PRP_OK, PRP_EINVAL, PRP_ERANGE, PRP_ENOSPC = 0, 1, 2, 3
+PRP_OK, PRP_EINVAL, PRP_ERANGE, PRP_ENOSPC, PRP_EBUSY = 0, 1, 2, 3, 4
+DEFAULT_WAIT_POLLS = 1 << 22
 
 _P = ctypes.c_void_p
 _U64 = ctypes.c_uint64
@@ -40,6 +42,7 @@ _SIZE = ctypes.c_size_t
 _EXPORTS = {
     "dmadesc_mr_lookup": ([_P, _P, _P, _U32, _U32, _P, _P, _U64, _U64,
                            _P, _P, _P, _P, _P, _P, _SIZE, _P], ctypes.c_int),
+    "dmadesc_mr_table_check": ([_P, _P, _U32, _U32, _P, _P, _P], ctypes.c_int),
     "dmadesc_build_prp": ([_P, _U64, _P, _P, _U64, _U64, _P, _U64,
                            _P, _P, _P, _P, _P, _SIZE, _P], ctypes.c_int),
     "dmadesc_build_prp_packed": ([_P, _U64, _P, _P, _U64, _U64, _P, _U64,
@@ -58,6 +61,7 @@ _EXPORTS = {
     "dmadesc_workspace_bytes": ([ctypes.c_int, _U64, _U32], _SIZE),
     "dmadesc_strerror": ([ctypes.c_int], ctypes.c_char_p),
     "dmadesc_version": ([], ctypes.c_int),
+    "dmadesc_debug_wait_limit": ([_U32], _U32),
 }
 
 _lib = None
@@ -79,10 +83,37 @@ def lib() -> ctypes.CDLL:
 
 
 class DmadescError(RuntimeError):
-    def __init__(self, func: str, rc: int):
+    def __init__(self, func: str, rc: int, detail: str = ""):
         msg = lib().dmadesc_strerror(rc).decode()
-        super().__init__(f"{func} returned {rc}: {msg}")
+        super().__init__(f"{func} returned {rc}: {msg}" + (f" ({detail})" if detail else ""))
         self.rc = rc
+
+
+class DmadescRefused(RuntimeError):
+    """A call succeeded but refused part of its batch in a way the caller must
+    act on: a slot-scan wait that expired (requests with PRP_EBUSY), or queue
+    ids outside the queues (the split's overflow bucket). Raised after the
+    stream is synchronized when the call was made with check=True; the
+    outputs are complete and attached as `out`."""
+
+    def __init__(self, msg: str, out: dict):
+        super().__init__(msg)
+        self.out = out
+
+
+def _u32_at(t: torch.Tensor, byte: int) -> int:
+    return int(t[byte:byte + 4].view(torch.int32).item()) & 0xFFFFFFFF
+
+
+def _check_scan(func: str, ws: torch.Tensor, stream_dev, stream, out: dict) -> None:
+    """After synchronizing, raises DmadescRefused when the slot scan's header
+    (workspace bytes 4..7) counts blocks whose wait expired."""
+    s = stream if stream is not None else torch.cuda.current_stream(stream_dev)
+    s.synchronize()
+    expired = _u32_at(ws, 4)
+    if expired:
+        raise DmadescRefused(f"{func}: the slot-scan wait of {expired} block(s) expired; "
+                             "their requests carry PRP_EBUSY", out)
 
 
 def _check(func: str, rc: int) -> None:
@@ -114,12 +145,16 @@ def workspace_bytes(op: int, n: int, param: int = 0) -> int:
 
 
 def _workspace(op: int, n: int, param: int, device, ws):
+    """(tensor, pointer, bytes) of a device workspace for `op`: the caller's
+    `ws` (a contiguous uint8 device tensor, checked) or a new one."""
     need = workspace_bytes(op, n, param)
     if ws is None:
         ws = torch.empty(max(need, 1), dtype=torch.uint8, device=device)
-    if ws.numel() < need:
-        raise ValueError(f"workspace needs {need} bytes, got {ws.numel()}")
-    return ws
+    ptr = _dev(ws, torch.uint8, "ws")
+    nbytes = ws.numel() * ws.element_size()
+    if nbytes < need:
+        raise ValueError(f"workspace needs {need} bytes, got {nbytes}")
+    return ws, ptr, nbytes
 
 
 def mr_lookup(reg_start: torch.Tensor, reg_end: torch.Tensor, reg_lkey: torch.Tensor,
@@ -145,12 +180,40 @@ def mr_lookup(reg_start: torch.Tensor, reg_end: torch.Tensor, reg_lkey: torch.Te
     return out
 
 
+def mr_table_check(reg_start: torch.Tensor, reg_end: torch.Tensor, page_shift: int = 12,
+                   stream=None) -> None:
+    """Raises DmadescError(-EINVAL) naming the first faulty region unless the
+    table is sorted, non-overlapping and page-aligned (dmadesc_mr_table_check;
+    synchronizes the stream)."""
+    r = reg_start.numel()
+    dev = reg_start.device
+    scratch = torch.empty(1, dtype=torch.uint64, device=dev)
+    bad = ctypes.c_uint64(0)
+    rc = lib().dmadesc_mr_table_check(
+        _dev(reg_start, torch.uint64, "reg_start", r), _dev(reg_end, torch.uint64, "reg_end", r),
+        r, page_shift, scratch.data_ptr(), ctypes.addressof(bad), _stream(dev, stream))
+    if rc != 0:
+        detail = f"region {bad.value} is empty, unaligned or overlaps the next" \
+            if bad.value != (1 << 64) - 1 else ""
+        raise DmadescError("dmadesc_mr_table_check", rc, detail)
+
+
+def debug_wait_limit(polls: int) -> int:
+    """Sets the bound on slot-scan waits for later calls (tests of the
+    PRP_EBUSY path); returns the previous bound."""
+    return int(lib().dmadesc_debug_wait_limit(polls))
+
+
 def build_prp(lut: torch.Tensor, off: torch.Tensor, length: torch.Tensor,
               list_bus_base: int, pool: torch.Tensor, out: dict | None = None,
-              ws: torch.Tensor | None = None, stream=None, packed: bool = False) -> dict:
+              ws: torch.Tensor | None = None, stream=None, packed: bool = False,
+              check: bool = True) -> dict:
     """GPU-page table -> PRP1/PRP2/status and chained lists in `pool`
     (u64[pool_pages, 512]); returns dict(prp1, prp2, status, total_pages).
-    packed=True calls dmadesc_build_prp_packed (lists back to back)."""
+    packed=True calls dmadesc_build_prp_packed (lists back to back).
+    check=True synchronizes the stream and raises DmadescRefused if a
+    slot-scan wait expired (check=False leaves the call asynchronous; the
+    caller then reads workspace bytes 4..7 itself)."""
     n = off.numel()
     dev = off.device
     if pool.dim() != 2 or pool.shape[1] != 512:
@@ -169,22 +232,28 @@ def build_prp(lut: torch.Tensor, off: torch.Tensor, length: torch.Tensor,
         _dev(out["prp1"], torch.uint64, "prp1", n), _dev(out["prp2"], torch.uint64, "prp2", n),
         _dev(out["status"], torch.uint8, "status", n),
         _dev(out["total_pages"], torch.uint64, "total_pages", 1),
-        ws.data_ptr(), ws.numel(), _stream(dev, stream))
-    _check("dmadesc_build_prp_packed" if packed else "dmadesc_build_prp", rc)
+        *ws[1:], _stream(dev, stream))
+    name = "dmadesc_build_prp_packed" if packed else "dmadesc_build_prp"
+    _check(name, rc)
+    if check and n:
+        _check_scan(name, ws[0], dev, stream, out)
     return out
 
 
 def build_prp_packed(lut: torch.Tensor, off: torch.Tensor, length: torch.Tensor,
                      list_bus_base: int, pool: torch.Tensor, out: dict | None = None,
-                     ws: torch.Tensor | None = None, stream=None) -> dict:
+                     ws: torch.Tensor | None = None, stream=None, check: bool = True) -> dict:
     """dmadesc_build_prp_packed: the same PRP entries, lists back to back."""
     return build_prp(lut, off, length, list_bus_base, pool, out=out, ws=ws, stream=stream,
-                     packed=True)
+                     packed=True, check=check)
 
 
 def partition_by_queue(qid: torch.Tensor, nqueues: int, out: dict | None = None,
-                       ws: torch.Tensor | None = None, stream=None) -> dict:
-    """Stable split by queue id; returns dict(perm, qoff, n_invalid)."""
+                       ws: torch.Tensor | None = None, stream=None, check: bool = True) -> dict:
+    """Stable split by queue id; returns dict(perm, qoff, n_invalid).
+    check=True synchronizes the stream and raises DmadescRefused when some
+    queue ids are >= nqueues (they sit, stably, in the overflow bucket);
+    check=False leaves the call asynchronous."""
     n = qid.numel()
     dev = qid.device
     if out is None:
@@ -197,8 +266,14 @@ def partition_by_queue(qid: torch.Tensor, nqueues: int, out: dict | None = None,
         _dev(out["perm"], torch.uint32, "perm", n),
         _dev(out["qoff"], torch.uint64, "qoff", nqueues + 2),
         _dev(out["n_invalid"], torch.uint64, "n_invalid", 1),
-        ws.data_ptr(), ws.numel(), _stream(dev, stream))
+        *ws[1:], _stream(dev, stream))
     _check("dmadesc_partition_by_queue", rc)
+    if check:
+        (stream if stream is not None else torch.cuda.current_stream(dev)).synchronize()
+        bad = int(out["n_invalid"].view(torch.int64)[0].item())
+        if bad:
+            raise DmadescRefused(f"dmadesc_partition_by_queue: {bad} request(s) name a queue "
+                                 f">= nqueues ({nqueues}); they are in the overflow bucket", out)
     return out
 
 
@@ -239,7 +314,7 @@ def emit_sqe(perm: torch.Tensor, qoff: torch.Tensor, status: torch.Tensor,
         _dev(ring, torch.uint64, "ring", nq), _dev(depth, torch.uint32, "depth", nq),
         _dev(free_slots, torch.uint32, "free_slots", nq), _dev(tail, torch.uint32, "tail", nq),
         _dev(cursor, torch.uint64, "cursor", nq), _dev(placed, torch.uint32, "placed", nq),
-        rid, ws.data_ptr(), ws.numel(), _stream(dev, stream))
+        rid, *ws[1:], _stream(dev, stream))
     _check("dmadesc_emit_sqe", rc)
     return dict(placed=placed, tail=tail, cursor=cursor, req_of_slot=req_of_slot)
 
@@ -247,9 +322,12 @@ def emit_sqe(perm: torch.Tensor, qoff: torch.Tensor, status: torch.Tensor,
 def build_put(src: torch.Tensor, dst: torch.Tensor, nbytes: torch.Tensor, pe: torch.Tensor,
               local_base: int, heap_bytes: int, chunk_shift: int, lkeys: torch.Tensor,
               peer_base: torch.Tensor, rkeys: torch.Tensor, desc: torch.Tensor,
-              out: dict | None = None, ws: torch.Tensor | None = None, stream=None) -> dict:
+              out: dict | None = None, ws: torch.Tensor | None = None, stream=None,
+              check: bool = True) -> dict:
     """RDMA put descriptors into `desc` (u64[desc_cap, 4], one 32-byte
-    dmadesc_put_desc per row); returns dict(first, count, status, total)."""
+    dmadesc_put_desc per row); returns dict(first, count, status, total).
+    check=True synchronizes and raises DmadescRefused if a slot-scan wait
+    expired."""
     n = src.numel()
     dev = src.device
     if desc.dim() != 2 or desc.shape[1] != 4:
@@ -272,9 +350,10 @@ def build_put(src: torch.Tensor, dst: torch.Tensor, nbytes: torch.Tensor, pe: to
         peer_base.numel(), _dev(desc, torch.uint64, "desc"), desc.shape[0],
         _dev(out["first"], torch.uint64, "first", n), _dev(out["count"], torch.uint32, "count", n),
         _dev(out["status"], torch.uint8, "status", n),
-        _dev(out["total"], torch.uint64, "total", 1), ws.data_ptr(), ws.numel(),
-        _stream(dev, stream))
+        _dev(out["total"], torch.uint64, "total", 1), *ws[1:], _stream(dev, stream))
     _check("dmadesc_build_put", rc)
+    if check and n:
+        _check_scan("dmadesc_build_put", ws[0], dev, stream, out)
     return out
 
 
@@ -385,8 +464,7 @@ class DeviceRegistry:
             rc = lib().dmadesc_reg_register(
                 *self._table(), self.page_shift, _dev(addr, torch.uint64, "addr", n),
                 _dev(size, torch.uint64, "size", n), n, _dev(handle, torch.uint64, "handle", n),
-                _dev(kind, torch.uint8, "kind", n), self._needed.data_ptr(), ws.data_ptr(),
-                ws.numel(), _stream(dev, stream))
+                _dev(kind, torch.uint8, "kind", n), self._needed.data_ptr(), *ws[1:], _stream(dev, stream))
             _check("dmadesc_reg_register", rc)
             needed = int(self._needed.view(torch.int64)[0].item())
             if needed <= self.capacity or not grow:
@@ -400,8 +478,7 @@ class DeviceRegistry:
         ws = _workspace(OP_REGISTRY, n, self.capacity, self.device, None)
         rc = lib().dmadesc_reg_deregister(
             *self._table(), _dev(handles, torch.uint64, "handle", n), n,
-            _dev(status, torch.uint8, "status", n), ws.data_ptr(), ws.numel(),
-            _stream(self.device, stream))
+            _dev(status, torch.uint8, "status", n), *ws[1:], _stream(self.device, stream))
         _check("dmadesc_reg_deregister", rc)
         return status
 

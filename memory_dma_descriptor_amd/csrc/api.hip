@@ -3,10 +3,15 @@
 // launched, so a rejected call touches no memory and needs no GPU.
 #include <errno.h>
 
+#include <atomic>
+
 #include "dd_internal.h"
 #include "dmadesc.h"
 
 namespace {
+
+// Bound on the polls of one look-back wait (about seconds at the default).
+std::atomic<uint32_t> g_wait_polls{DMADESC_DEFAULT_WAIT_POLLS};
 
 constexpr uint64_t kMaxN = 1ull << 32;           // indices are u32
 constexpr uint64_t kMaxLutEntries = 1ull << 48;  // heap < 2^64 bytes
@@ -47,9 +52,18 @@ int build_prp_common(const uint64_t *lut, uint64_t lut_entries, const uint64_t *
 
 }  // namespace
 
+namespace dd {
+uint32_t wait_limit() { return g_wait_polls.load(std::memory_order_relaxed); }
+}  // namespace dd
+
 extern "C" {
 
 int dmadesc_version(void) { return 1; }
+
+uint32_t dmadesc_debug_wait_limit(uint32_t polls)
+{
+    return g_wait_polls.exchange(polls);
+}
 
 const char *dmadesc_strerror(int err)
 {
@@ -97,6 +111,22 @@ int dmadesc_mr_lookup(const uint64_t *reg_start, const uint64_t *reg_end,
     dd::LookupArgs a{reg_start, reg_end, reg_lkey, nregions, page_shift, off, len, n, va_base,
                      handle, lkey, kind, rbase, rend};
     return launched(dd::launch_mr_lookup(a, static_cast<hipStream_t>(stream)));
+}
+
+int dmadesc_mr_table_check(const uint64_t *reg_start, const uint64_t *reg_end,
+                           uint32_t nregions, uint32_t page_shift, uint64_t *scratch,
+                           uint64_t *first_bad, void *stream)
+{
+    if (first_bad) *first_bad = ~0ull;
+    if (page_shift < 12 || page_shift > 30 || nregions >= (1u << 31) || !scratch) return -EINVAL;
+    if (reinterpret_cast<uintptr_t>(scratch) & 7u) return -EINVAL;
+    if (nregions > 0 && (!reg_start || !reg_end)) return -EINVAL;
+    uint64_t bad = ~0ull;
+    if (dd::launch_table_check(reg_start, reg_end, nregions, page_shift, scratch, &bad,
+                               static_cast<hipStream_t>(stream)) != hipSuccess)
+        return -EIO;
+    if (first_bad) *first_bad = bad;
+    return bad == ~0ull ? 0 : -EINVAL;
 }
 
 int dmadesc_build_prp(const uint64_t *lut, uint64_t lut_entries,

@@ -66,7 +66,7 @@ constexpr int kTile = kThreads * kItems;      // requests per block
 constexpr uint64_t kPadWords = 8;
 // GPU pages of the table staged in LDS per wave and round (4 KiB).
 constexpr int kTileFrames = 512;
-enum : uint8_t { kOk = 0, kEinval = 1, kErange = 2, kEnospc = 3 };
+enum : uint8_t { kOk = 0, kEinval = 1, kErange = 2, kEnospc = 3, kEbusy = 4 };
 
 // Status and 4 KiB page count of one request.
 __device__ __forceinline__ uint8_t decode(uint64_t o, uint64_t l, uint64_t heap,
@@ -664,10 +664,11 @@ __global__ __launch_bounds__(kThreads, 4) void k_prp_build(
     uint64_t nblocks, uint64_t bus, uint64_t *__restrict__ pool, uint64_t pool_pages,
     uint64_t *__restrict__ prp1, uint64_t *__restrict__ prp2,
     uint8_t *__restrict__ status, uint64_t *__restrict__ total,
-    Header *__restrict__ hdr, uint64_t *__restrict__ bstat)
+    Header *__restrict__ hdr, uint64_t *__restrict__ bstat, uint32_t max_polls)
 {
     __shared__ uint64_t s_red[kItems * kWaves];
     __shared__ uint64_t s_bid, s_excl;
+    __shared__ uint32_t s_dead;
     __shared__ uint64_t s_v2[kItems * kThreads];   // table entry of PRP2's page (two pages)
     __shared__ typename std::conditional<kPacked, PackLds, RoundLds>::type s_round[kWaves];
 
@@ -745,18 +746,24 @@ __global__ __launch_bounds__(kThreads, 4) void k_prp_build(
     if (w != 0) gather();
     if (w == 0) {
         uint64_t excl = 0;
+        bool dead = false;
         if (b != 0) {
-            excl = look_back(bstat, (int64_t)b, &hdr->timeouts);
-            if (ln == 0) store_status(bstat + b, kFlagInc | (excl + agg));
+            excl = look_back(bstat, (int64_t)b, &hdr->timeouts, max_polls, dead);
+            // An expired wait leaves the aggregate published, so later blocks
+            // still find their prefixes; this block's list requests are refused.
+            if (ln == 0 && !dead) store_status(bstat + b, kFlagInc | (excl + agg));
         }
         if (ln == 0) {
             s_excl = excl;
-            if (b == nblocks - 1) *total = kPacked ? (excl + agg + 510) / 511 : excl + agg;
+            s_dead = dead;
+            if (b == nblocks - 1)
+                *total = dead ? ~0ull : (kPacked ? (excl + agg + 510) / 511 : excl + agg);
         }
         gather();
     }
     __syncthreads();
     const uint64_t excl = s_excl;
+    const bool dead = s_dead != 0;
 
     const uint64_t cap = kPacked ? pool_pages * 511 : pool_pages;   // slots of the pool
 #pragma unroll 1
@@ -767,7 +774,8 @@ __global__ __launch_bounds__(kThreads, 4) void k_prp_build(
         const uint64_t cnt = (st == kOk && pages >= 3)
                                  ? (kPacked ? pages - 1 : (pages - 2 + 510) / 511) : 0;
         const uint64_t slot = excl + pre[k];
-        if (cnt != 0 && slot + cnt > cap) st = kEnospc;      // refused; its slots stay taken
+        if (cnt != 0 && dead) st = kEbusy;                   // its slots are unknown
+        else if (cnt != 0 && slot + cnt > cap) st = kEnospc; // refused; its slots stay taken
         const bool lists = (st == kOk) && cnt != 0;
         const uint64_t xb = (o[k] & ~4095ull) + 4096;
         const uint64_t last_frame = (o[k] + l[k] - 1) >> 16;
@@ -818,11 +826,13 @@ hipError_t launch_build_prp(const PrpArgs &a, hipStream_t s)
     if (a.packed)
         hipLaunchKernelGGL(k_prp_build<true>, dim3((unsigned)nb), dim3(kThreads), 0, s,
                            a.lut, heap, a.off, a.len, a.n, nb, a.list_bus_base, a.pool,
-                           a.pool_pages, a.prp1, a.prp2, a.status, a.total_pages, hdr, bstat);
+                           a.pool_pages, a.prp1, a.prp2, a.status, a.total_pages, hdr, bstat,
+                           wait_limit());
     else
         hipLaunchKernelGGL(k_prp_build<false>, dim3((unsigned)nb), dim3(kThreads), 0, s,
                            a.lut, heap, a.off, a.len, a.n, nb, a.list_bus_base, a.pool,
-                           a.pool_pages, a.prp1, a.prp2, a.status, a.total_pages, hdr, bstat);
+                           a.pool_pages, a.prp1, a.prp2, a.status, a.total_pages, hdr, bstat,
+                           wait_limit());
     return hipGetLastError();
 }
 

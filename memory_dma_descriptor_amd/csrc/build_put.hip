@@ -39,7 +39,7 @@ constexpr int kItems = 4;
 constexpr int kTile = kThreads * kItems;
 constexpr uint32_t kMsgShift = 31;                   // largest transfer: 2^31 bytes
 
-enum : uint8_t { kOk = 0, kEinval = 1, kErange = 2, kEnospc = 3 };
+enum : uint8_t { kOk = 0, kEinval = 1, kErange = 2, kEnospc = 3, kEbusy = 4 };
 
 // Pieces of one put (shift 0: static heap).
 __device__ __forceinline__ uint64_t put_pieces(uint64_t s, uint64_t d, uint64_t b, uint32_t shift)
@@ -152,10 +152,11 @@ __global__ __launch_bounds__(kThreads) void k_put_build(
     uint64_t heap, uint32_t npes, PutKeys K, uint64_t *__restrict__ desc, uint64_t cap,
     uint64_t *__restrict__ first_out, uint32_t *__restrict__ count_out,
     uint8_t *__restrict__ status, uint64_t *__restrict__ total, uint64_t nblocks,
-    Header *__restrict__ hdr, uint64_t *__restrict__ bstat)
+    Header *__restrict__ hdr, uint64_t *__restrict__ bstat, uint32_t max_polls)
 {
     __shared__ uint64_t s_red[kItems * kWaves];
     __shared__ uint64_t s_bid, s_excl;
+    __shared__ uint32_t s_dead;
     __shared__ PutTab s_tab[kWaves];
     const int t = threadIdx.x, w = wave(), ln = lane();
     if (t == 0) s_bid = atomicAdd(&hdr->ticket, 1u);
@@ -201,27 +202,37 @@ __global__ __launch_bounds__(kThreads) void k_put_build(
     }
     if (w == 0) {
         uint64_t excl = 0;
+        bool dead = false;
         if (blk == 0) {
             if (ln == 0) store_status(bstat, kFlagInc | agg);
         } else {
             if (ln == 0) store_status(bstat + blk, kFlagAgg | agg);
-            excl = look_back(bstat, (int64_t)blk, &hdr->timeouts);
-            if (ln == 0) store_status(bstat + blk, kFlagInc | (excl + agg));
+            excl = look_back(bstat, (int64_t)blk, &hdr->timeouts, max_polls, dead);
+            // An expired wait leaves the aggregate published (later blocks
+            // still find their prefixes); this block's puts are refused.
+            if (ln == 0 && !dead) store_status(bstat + blk, kFlagInc | (excl + agg));
         }
         if (ln == 0) {
             s_excl = excl;
-            if (blk == nblocks - 1) *total = excl + agg;
+            s_dead = dead;
+            if (blk == nblocks - 1) *total = dead ? ~0ull : excl + agg;
         }
     }
     __syncthreads();
     const uint64_t excl = s_excl;
+    const bool dead = s_dead != 0;
 
 #pragma unroll 1
     for (int k = 0; k < kItems; ++k) {
         const uint64_t i = base + (uint64_t)k * kThreads + t;
-        const uint64_t f = excl + pre[k];
+        uint64_t f = excl + pre[k];
         uint8_t sk = st[k];
-        if (cnt[k] != 0 && f + cnt[k] > cap) sk = kEnospc;   // refused; its slots stay taken
+        if (cnt[k] != 0 && dead) {
+            sk = kEbusy;                                      // its slots are unknown
+            f = ~0ull;
+        } else if (cnt[k] != 0 && f + cnt[k] > cap) {
+            sk = kEnospc;                                     // refused; its slots stay taken
+        }
         if (i < n) {
             __builtin_nontemporal_store(f, first_out + i);
             __builtin_nontemporal_store((uint32_t)cnt[k], count_out + i);
@@ -259,7 +270,7 @@ hipError_t launch_build_put(const PutArgs &a, hipStream_t s)
                     a.chunk_shift ? a.heap_bytes >> a.chunk_shift : 1, a.chunk_shift};
     hipLaunchKernelGGL(k_put_build, dim3((unsigned)nb), dim3(kThreads), 0, s, a.src, a.dst,
                        a.bytes, a.pe, a.n, a.heap_bytes, a.npes, K, a.desc, a.desc_cap,
-                       a.first, a.count, a.status, a.total, nb, hdr, bstat);
+                       a.first, a.count, a.status, a.total, nb, hdr, bstat, wait_limit());
     return hipGetLastError();
 }
 

@@ -95,6 +95,9 @@ struct PutArgs {
 };
 
 hipError_t launch_mr_lookup(const LookupArgs &a, hipStream_t s);
+hipError_t launch_table_check(const uint64_t *rs, const uint64_t *re, uint32_t nregions,
+                              uint32_t page_shift, uint64_t *scratch, uint64_t *host_result,
+                              hipStream_t s);
 hipError_t launch_build_prp(const PrpArgs &a, hipStream_t s);
 hipError_t launch_partition(const SplitArgs &a, hipStream_t s);
 hipError_t launch_emit_sqe(const SqeArgs &a, hipStream_t s);
@@ -109,6 +112,10 @@ size_t ws_partition(uint64_t n, uint32_t nqueues);
 size_t ws_emit_sqe(uint32_t nqueues);
 size_t ws_build_put(uint64_t n);
 size_t ws_registry(uint64_t n, uint64_t capacity);
+
+// Polls a look-back wait may take before it gives up (process-wide; set by
+// dmadesc_debug_wait_limit, default 2^22).
+uint32_t wait_limit();
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 

@@ -3,7 +3,11 @@
 // order: each block publishes its aggregate, then reads its predecessors'
 // published values until it meets an inclusive prefix. Block order comes from
 // an atomic ticket in the workspace header, so a block only ever waits on
-// blocks that are already running; waits are bounded and counted.
+// blocks that are already running. Waits are bounded: a block whose wait
+// runs out does not know its prefix, counts itself in the header and
+// reports it to its caller, which then refuses the outputs that need the
+// prefix (a distinct status), so an expired wait is never silent. Blocks
+// after it still find their own prefixes, since its aggregate is published.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -17,12 +21,12 @@ namespace {
 constexpr uint64_t kFlagAgg = 1ull << 62;     // status word: aggregate published
 constexpr uint64_t kFlagInc = 2ull << 62;     // status word: inclusive prefix published
 constexpr uint64_t kValue = (1ull << 62) - 1;
-constexpr uint32_t kMaxPolls = 1u << 22;      // bounded wait (about seconds)
 
 // Workspace layout: a 256-byte header, then one status word per block.
 struct Header {
     uint32_t ticket;     // next block order
-    uint32_t timeouts;   // look-back waits that hit the bound (never expected)
+    uint32_t timeouts;   // blocks whose look-back wait hit the bound (never
+                         // expected at the default bound)
 };
 constexpr size_t kHeaderBytes = 256;
 
@@ -39,20 +43,25 @@ __device__ __forceinline__ void store_status(uint64_t *p, uint64_t v)
 }
 
 // Exclusive prefix of the values of all blocks before `b` (called by one
-// whole wave; lane k inspects block b-1-k of the current window).
-__device__ uint64_t look_back(uint64_t *status, int64_t b, uint32_t *timeouts)
+// whole wave; lane k inspects block b-1-k of the current window). When a
+// wait takes more than max_polls polls, `expired` is set (in every lane) and
+// the value returned is meaningless.
+__device__ uint64_t look_back(uint64_t *status, int64_t b, uint32_t *timeouts,
+                              uint32_t max_polls, bool &expired)
 {
     const int ln = lane();
     uint64_t excl = 0;
     int64_t top = b - 1;
     uint32_t polls = 0;
+    expired = false;
     for (;;) {
         const int64_t idx = top - ln;
         uint64_t s = idx >= 0 ? load_status(status + idx) : kFlagInc;   // before block 0: 0
         while (__ballot((s >> 62) == 0) != 0) {
-            if (++polls > kMaxPolls) {
+            if (++polls > max_polls) {
                 if (ln == 0) atomicAdd(timeouts, 1u);
-                return excl;
+                expired = true;
+                return 0;
             }
             __builtin_amdgcn_s_sleep(2);
             if ((s >> 62) == 0) s = load_status(status + idx);

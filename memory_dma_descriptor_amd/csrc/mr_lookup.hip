@@ -272,7 +272,44 @@ __global__ __launch_bounds__(kThreads) void k_lookup_split(
     }
 }
 
+// Region r breaks the table rules when it is empty, a bound is not a page
+// multiple, or it overlaps region r + 1 (or starts before it ends). The
+// smallest such r lands in *first_bad (a minimum is order-independent).
+__global__ __launch_bounds__(kThreads) void k_table_check(
+    const uint64_t *__restrict__ rs, const uint64_t *__restrict__ re, uint32_t nregions,
+    uint64_t in_page, unsigned long long *__restrict__ first_bad)
+{
+    for (uint64_t r = (uint64_t)blockIdx.x * kThreads + threadIdx.x; r < nregions;
+         r += (uint64_t)gridDim.x * kThreads) {
+        const uint64_t s0 = rs[r], e0 = re[r];
+        bool bad = s0 >= e0 || ((s0 | e0) & in_page) != 0;
+        if (r + 1 < nregions) bad = bad || e0 > rs[r + 1];
+        if (bad) atomicMin(first_bad, (unsigned long long)r);
+    }
+}
+
+__global__ void k_set_u64(unsigned long long *p, unsigned long long v) { *p = v; }
+
 }  // namespace
+
+hipError_t launch_table_check(const uint64_t *rs, const uint64_t *re, uint32_t nregions,
+                              uint32_t page_shift, uint64_t *scratch, uint64_t *host_result,
+                              hipStream_t s)
+{
+    auto *fb = reinterpret_cast<unsigned long long *>(scratch);
+    hipLaunchKernelGGL(k_set_u64, dim3(1), dim3(1), 0, s, fb, ~0ull);
+    if (nregions > 0) {
+        uint64_t blocks = ((uint64_t)nregions + kThreads - 1) / kThreads;
+        if (blocks > 1024) blocks = 1024;
+        hipLaunchKernelGGL(k_table_check, dim3((unsigned)blocks), dim3(kThreads), 0, s, rs, re,
+                           nregions, (1ull << page_shift) - 1, fb);
+    }
+    hipError_t e = hipGetLastError();
+    if (e == hipSuccess) e = hipMemcpyAsync(host_result, scratch, sizeof(uint64_t),
+                                            hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    return e;
+}
 
 hipError_t launch_mr_lookup(const LookupArgs &a, hipStream_t s)
 {

@@ -737,19 +737,24 @@ __global__ void k_dereg_state(RegState g, RegWs w)
 // ------------------------------------------------------------ workspace ---
 
 struct Carver {
-    char *p;
+    // Walks the layout by offset, so the same walk both sizes the workspace
+    // (base == nullptr) and hands out its pieces.
+    char *base;
+    size_t off;
     template <typename T>
     T *take(uint64_t count)
     {
-        T *r = reinterpret_cast<T *>(p);
-        p += align256(count * sizeof(T));
+        T *r = base ? reinterpret_cast<T *>(base + off) : nullptr;
+        off += align256(count * sizeof(T));
         return r;
     }
 };
 
-RegWs carve(void *ws, uint64_t n, uint64_t cap)
+// Lays the workspace out for a batch of n items and a table of cap records;
+// *bytes receives the end of the walk, which is what the workspace must hold.
+RegWs carve(void *ws, uint64_t n, uint64_t cap, size_t *bytes = nullptr)
 {
-    Carver c{static_cast<char *>(ws)};
+    Carver c{static_cast<char *>(ws), 0};
     RegWs w;
     w.base = c.take<uint64_t>(n);
     w.top = c.take<uint64_t>(n);
@@ -776,13 +781,15 @@ RegWs carve(void *ws, uint64_t n, uint64_t cap)
     w.tmp32 = c.take<uint32_t>(cap);
     w.chunk = c.take<uint64_t>(kMaxChunks);
     w.scal = c.take<uint64_t>(4);
+    if (bytes) *bytes = c.off;
     return w;
 }
 
-uint64_t carve_bytes(uint64_t n, uint64_t cap)
+size_t carve_bytes(uint64_t n, uint64_t cap)
 {
-    return 15 * align256(n * 8) + 4 * align256(cap * 8) + 3 * align256(cap * 4) +
-           align256((cap + n) * 4) + align256((uint64_t)kMaxChunks * 8) + 256;
+    size_t bytes = 0;
+    carve(nullptr, n, cap, &bytes);
+    return bytes;
 }
 
 }  // namespace

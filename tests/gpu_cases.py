@@ -171,8 +171,8 @@ def check_prp_sampled(lut, off, ln, bus, pool_pages, sample, ctx=""):
 
 # ------------------------------------------------------------------ split ---
 
-def gpu_split(qid, nq):
-    out = dd.partition_by_queue(dev(np.asarray(qid, np.uint32)), nq)
+def gpu_split(qid, nq, check=False):
+    out = dd.partition_by_queue(dev(np.asarray(qid, np.uint32)), nq, check=check)
     torch.cuda.synchronize()
     g = {k: host(v) for k, v in out.items()}
     g["n_invalid"] = int(g["n_invalid"][0])
@@ -188,6 +188,14 @@ def check_split(qid, nq, ctx=""):
             raise AssertionError(f"{ctx} split column {k}: {bad.size} mismatches, first at "
                                  f"{bad[0]}: oracle {o[k][bad[0]]} gpu {g[k][bad[0]]}")
     assert o["n_invalid"] == g["n_invalid"], ctx
+    if o["n_invalid"]:
+        # The checked call reports the overflow bucket after synchronizing.
+        try:
+            gpu_split(qid, nq, check=True)
+        except dd.DmadescRefused as e:
+            assert np.array_equal(host(e.out["perm"]), o["perm"]), ctx
+        else:
+            raise AssertionError(f"{ctx}: overflow ids were not reported")
     return o, g
 
 

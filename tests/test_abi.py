@@ -179,6 +179,36 @@ def test_cq_mirror_rejects_bad_arguments():
         assert f(*args) == EINVAL, (k, bad)
 
 
+@no_gpu_only
+def test_table_check_rejects_bad_arguments():
+    f = dd.lib().dmadesc_mr_table_check
+    bad = ctypes.c_uint64(0)
+    ok = [P, P, 4, 12, P, ctypes.addressof(bad), NULL]
+    for k, v in [(3, 11), (3, 31), (2, 1 << 31), (4, NULL), (4, P + 4), (0, NULL), (1, NULL)]:
+        args = list(ok)
+        args[k] = v
+        bad.value = 5
+        assert f(*args) == EINVAL, (k, v)
+        assert bad.value == (1 << 64) - 1, (k, v)     # no faulty region named
+
+
+def test_wait_limit_round_trip():
+    # The bound is host state only: set, read back through the next call,
+    # restore the default.
+    assert dd.debug_wait_limit(7) == dd.DEFAULT_WAIT_POLLS
+    assert dd.debug_wait_limit(0) == 7
+    assert dd.debug_wait_limit(dd.DEFAULT_WAIT_POLLS) == 0
+
+
+def test_status_codes_match_the_header():
+    src = open(os.path.join(ROOT, "include", "dmadesc.h"), encoding="utf-8").read()
+    for name in ("OK", "EINVAL", "ERANGE", "ENOSPC", "EBUSY"):
+        v = int(re.search(rf"DMADESC_PRP_{name} = (\d+)", src).group(1))
+        assert getattr(dd, f"PRP_{name}") == v, name
+    polls = re.search(r"#define DMADESC_DEFAULT_WAIT_POLLS \(1u << (\d+)\)", src).group(1)
+    assert dd.DEFAULT_WAIT_POLLS == 1 << int(polls)
+
+
 def test_cq_slot_layout():
     # dmadesc_cq_slot is 48 bytes: two addresses, six u32 words, the count.
     src = open(os.path.join(ROOT, "include", "dmadesc.h"), encoding="utf-8").read()
@@ -194,6 +224,26 @@ def test_registry_workspace_sizes():
     assert ws(dd.OP_REGISTRY, 65537, 64) == 0 and ws(dd.OP_REGISTRY, 1, (1 << 24) + 1) == 0
     a, b, c = ws(dd.OP_REGISTRY, 1, 64), ws(dd.OP_REGISTRY, 65536, 64), ws(dd.OP_REGISTRY, 1, 1 << 20)
     assert 0 < a < b and a < c and all(x % 256 == 0 for x in (a, b, c))
+
+
+def _a256(x):
+    return (x + 255) // 256 * 256
+
+
+@pytest.mark.parametrize("n", [1, 20, 64, 1000, 65536])
+@pytest.mark.parametrize("cap", [1, 32, 256, 4096, 65536, 1 << 20, 1 << 24])
+def test_registry_workspace_holds_every_piece(n, cap):
+    # The registry kernels keep, each in a 256-byte-aligned piece: per batch
+    # item six u64 columns (rounded base and top, hit start, new base, insert
+    # base and top), two more (miss base and top), one u8 class and six u32
+    # columns (hit slot, rank, start rank, owner, new references, miss rank);
+    # per record five u64 columns (starts, running maximum, three scratch)
+    # and two u32 (new slot, scratch), the merged index over records and
+    # items (u32), 16,384 chunk totals and four scalars. A workspace of
+    # dmadesc_workspace_bytes must hold all of them.
+    need = (8 * _a256(8 * n) + _a256(n) + 6 * _a256(4 * n) + 5 * _a256(8 * cap)
+            + 2 * _a256(4 * cap) + _a256(4 * (cap + n)) + _a256(8 * 16384) + _a256(32))
+    assert dd.workspace_bytes(dd.OP_REGISTRY, n, cap) >= need, (n, cap)
 
 
 def test_empty_lookup_is_a_no_op():

@@ -381,7 +381,7 @@ def test_split_unaligned_qid(nq):
     qid = rng.integers(0, nq + 1, size=n).astype(np.uint32)
     buf = gc.dev(np.zeros(n + 1, np.uint32))
     buf[1:].copy_(gc.dev(qid))
-    out = dd.partition_by_queue(buf[1:], nq)
+    out = dd.partition_by_queue(buf[1:], nq, check=False)
     torch.cuda.synchronize()
     o = oracle.partition(qid, nq)
     assert np.array_equal(gc.host(out["perm"]), o["perm"])

@@ -152,3 +152,35 @@ def test_empty_batches_and_empty_table():
     p.register(np.zeros(0, np.uint64), np.zeros(0, np.uint64), "empty register")
     p.deregister(np.array([1, 2, 0], np.uint64), "deregister on an empty table")
     p.deregister(np.zeros(0, np.uint64), "empty deregister")
+
+
+def test_workspace_of_exact_size_keeps_its_neighbour_intact():
+    # A workspace of exactly dmadesc_workspace_bytes inside a larger buffer
+    # whose tail holds a canary: a small batch on a large table must write
+    # nothing past the workspace, for a register and a deregister batch.
+    cap, n = 65536, 20
+    reg = dd.DeviceRegistry(cap)
+    need = dd.workspace_bytes(dd.OP_REGISTRY, n, cap)
+    tail = 1 << 20
+    buf = torch.full((need + tail,), 0xA5, dtype=torch.uint8, device="cuda")
+    addr = gc.dev(np.arange(n, dtype=np.uint64) * np.uint64(8 * M))
+    size = gc.dev(np.full(n, M, np.uint64))
+    handle = torch.empty(n, dtype=torch.uint64, device="cuda")
+    kind = torch.empty(n, dtype=torch.uint8, device="cuda")
+    needed = torch.zeros(1, dtype=torch.uint64, device="cuda")
+    s = torch.cuda.current_stream().cuda_stream
+    gc.say(f"registry exact workspace: n={n} cap={cap} ws={need}")
+    rc = dd.lib().dmadesc_reg_register(*reg._table(), 12, addr.data_ptr(), size.data_ptr(), n,
+                                       handle.data_ptr(), kind.data_ptr(), needed.data_ptr(),
+                                       buf.data_ptr(), need, s)
+    assert rc == 0
+    torch.cuda.synchronize()
+    assert (gc.host(kind) == oracle.REG_NEW).all() and reg.count() == n
+    assert bool((buf[need:] == 0xA5).all()), "register wrote past its workspace"
+    status = torch.empty(n, dtype=torch.uint8, device="cuda")
+    rc = dd.lib().dmadesc_reg_deregister(*reg._table(), handle.data_ptr(), n,
+                                         status.data_ptr(), buf.data_ptr(), need, s)
+    assert rc == 0
+    torch.cuda.synchronize()
+    assert (gc.host(status) == oracle.DEREG_REMOVED).all() and reg.count() == 0
+    assert bool((buf[need:] == 0xA5).all()), "deregister wrote past its workspace"

@@ -32,7 +32,7 @@ def _columns(rng, n, nq, lba_shift=9, bad_p=0.1, max_blocks=300):
 def _inputs(qid, nq, status, ln, slba, prp1, prp2):
     """Oracle inputs from the oracle's split, GPU inputs from the GPU's split."""
     o_split = oracle.partition(qid, nq)
-    g_split = dd.partition_by_queue(gc.dev(qid), nq)
+    g_split = dd.partition_by_queue(gc.dev(qid), nq, check=False)
     o, _ = gc.sqe_inputs(o_split["perm"], o_split["qoff"], status, ln, slba, prp1, prp2)
     _, g = gc.sqe_inputs(o_split["perm"], o_split["qoff"], status, ln, slba, prp1, prp2)
     g["perm"], g["qoff"] = g_split["perm"], g_split["qoff"]
@@ -163,7 +163,7 @@ def _path_inputs(name, n=None):
     g_prp = dd.build_prp(g_lut, g_off, g_len, d["list_bus_base"], pool)
     assert int(gc.host(g_prp["total_pages"])[0]) == total
     o_split = oracle.partition(d["qid"], nq)
-    g_split = dd.partition_by_queue(gc.dev(d["qid"]), nq)
+    g_split = dd.partition_by_queue(gc.dev(d["qid"]), nq, check=False)
     o = dict(perm=o_split["perm"], qoff=o_split["qoff"], status=o_prp["status"],
              len=d["len"], slba=slba, prp1=o_prp["prp1"], prp2=o_prp["prp2"])
     g = dict(perm=g_split["perm"], qoff=g_split["qoff"], status=g_prp["status"], len=g_len,
