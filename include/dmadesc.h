@@ -278,6 +278,32 @@ int dmadesc_build_prp_packed(const uint64_t *lut, uint64_t lut_entries,
                              void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * dmadesc_build_prp_packed_noalloc - dmadesc_build_prp_packed without a
+ * caller workspace.
+ *
+ * For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc. Arguments,
+ * outputs, statuses and errors are those of dmadesc_build_prp_packed; the
+ * slot scan's workspace is instead a static device array of the library
+ * (256 + 8 * DMADESC_NOALLOC_MAX_N / 1024 bytes, about 1 MiB) that every GPU
+ * holds until the process ends; it is cleared by a kernel at the start of
+ * each call. The call allocates nothing (no hipMalloc, hipFree or allocating
+ * library routine). The first call on a device looks the array's device
+ * address up once (hipGetSymbolAddress) with that device current.
+ *   n > DMADESC_NOALLOC_MAX_N -> -E2BIG (nothing launched)
+ * Every call on one GPU shares that GPU's array: calls that overlap in time
+ * on one GPU (on different streams or from different threads) race and give
+ * unspecified results; order them on one stream. The array's header (blocks,
+ * expired waits) is not returned: refusals show as DMADESC_PRP_EBUSY.
+ */
+#define DMADESC_NOALLOC_MAX_N (1u << 27)
+int dmadesc_build_prp_packed_noalloc(const uint64_t *lut, uint64_t lut_entries,
+                                     const uint64_t *off, const uint64_t *len, uint64_t n,
+                                     uint64_t list_bus_base, uint64_t *list_pool,
+                                     uint64_t pool_pages, uint64_t *prp1, uint64_t *prp2,
+                                     uint8_t *status, uint64_t *total_pages, void *stream);
+
+/*
  * dmadesc_partition_by_queue - stable split of request indices by queue id.
  *
  * [MORI] groups a wave's lanes by destination with ballot / find-first-set /

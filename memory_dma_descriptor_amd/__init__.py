@@ -14,7 +14,8 @@ import torch
 
 from . import _build
 
-__all__ = ["mr_lookup", "build_prp", "build_prp_packed", "partition_by_queue", "emit_sqe",
+__all__ = ["mr_lookup", "build_prp", "build_prp_packed", "build_prp_packed_noalloc",
+           "partition_by_queue", "emit_sqe",
            "ring_addresses", "DeviceRegistry", "build_put", "cq_slots", "cq_attach",
            "cq_mirror", "cq_slot_state",
            "workspace_bytes", "DmadescError", "DmadescRefused", "lib", "LIB_PATH", "MAX_QUEUES",
@@ -47,6 +48,8 @@ _EXPORTS = {
                            _P, _P, _P, _P, _P, _SIZE, _P], ctypes.c_int),
     "dmadesc_build_prp_packed": ([_P, _U64, _P, _P, _U64, _U64, _P, _U64,
                                   _P, _P, _P, _P, _P, _SIZE, _P], ctypes.c_int),
+    "dmadesc_build_prp_packed_noalloc": ([_P, _U64, _P, _P, _U64, _U64, _P, _U64,
+                                          _P, _P, _P, _P, _P], ctypes.c_int),
     "dmadesc_partition_by_queue": ([_P, _U64, _U32, _P, _P, _P, _P, _SIZE, _P],
                                    ctypes.c_int),
     "dmadesc_emit_sqe": ([_P, _P, _U32, _P, _P, _P, _P, _P, _U64, _U32, _U32, _U32,
@@ -246,6 +249,30 @@ def build_prp_packed(lut: torch.Tensor, off: torch.Tensor, length: torch.Tensor,
     """dmadesc_build_prp_packed: the same PRP entries, lists back to back."""
     return build_prp(lut, off, length, list_bus_base, pool, out=out, ws=ws, stream=stream,
                      packed=True, check=check)
+
+
+NOALLOC_MAX_N = 1 << 27
+
+
+def build_prp_packed_noalloc(lut: torch.Tensor, off: torch.Tensor, length: torch.Tensor,
+                             list_bus_base: int, pool: torch.Tensor, out: dict,
+                             stream=None) -> dict:
+    """dmadesc_build_prp_packed_noalloc: the packed build with the library's
+    static scratch in place of a workspace. `out` (prp1, prp2, status,
+    total_pages) is required, so that nothing is allocated here either."""
+    n = off.numel()
+    dev = off.device
+    if pool.dim() != 2 or pool.shape[1] != 512:
+        raise ValueError("pool must have shape [pool_pages, 512]")
+    rc = lib().dmadesc_build_prp_packed_noalloc(
+        _dev(lut, torch.uint64, "lut"), lut.numel(),
+        _dev(off, torch.uint64, "off", n), _dev(length, torch.uint64, "len", n), n,
+        list_bus_base, _dev(pool, torch.uint64, "pool"), pool.shape[0],
+        _dev(out["prp1"], torch.uint64, "prp1", n), _dev(out["prp2"], torch.uint64, "prp2", n),
+        _dev(out["status"], torch.uint8, "status", n),
+        _dev(out["total_pages"], torch.uint64, "total_pages", 1), _stream(dev, stream))
+    _check("dmadesc_build_prp_packed_noalloc", rc)
+    return out
 
 
 def partition_by_queue(qid: torch.Tensor, nqueues: int, out: dict | None = None,

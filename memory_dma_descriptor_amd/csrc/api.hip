@@ -71,6 +71,7 @@ const char *dmadesc_strerror(int err)
     case 0: return "success";
     case -EINVAL: return "invalid argument (null pointer, size or parameter out of range, or workspace too small)";
     case -EIO: return "the HIP runtime refused a kernel launch";
+    case -E2BIG: return "batch larger than the allocation-free entry point's scratch allows";
     default: return "unknown error";
     }
 }
@@ -147,6 +148,20 @@ int dmadesc_build_prp_packed(const uint64_t *lut, uint64_t lut_entries,
                              uint64_t *total_pages,
                              void *ws, size_t ws_bytes, void *stream)
 {
+    return build_prp_common(lut, lut_entries, off, len, n, list_bus_base, list_pool, pool_pages,
+                            prp1, prp2, status, total_pages, ws, ws_bytes, stream, true);
+}
+
+int dmadesc_build_prp_packed_noalloc(const uint64_t *lut, uint64_t lut_entries,
+                                     const uint64_t *off, const uint64_t *len, uint64_t n,
+                                     uint64_t list_bus_base, uint64_t *list_pool,
+                                     uint64_t pool_pages, uint64_t *prp1, uint64_t *prp2,
+                                     uint8_t *status, uint64_t *total_pages, void *stream)
+{
+    if (n > DMADESC_NOALLOC_MAX_N) return -E2BIG;
+    void *ws = nullptr;
+    size_t ws_bytes = 0;
+    if (dd::noalloc_scratch(&ws, &ws_bytes) != hipSuccess) return -EIO;
     return build_prp_common(lut, lut_entries, off, len, n, list_bus_base, list_pool, pool_pages,
                             prp1, prp2, status, total_pages, ws, ws_bytes, stream, true);
 }

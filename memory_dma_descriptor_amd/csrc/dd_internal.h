@@ -113,6 +113,10 @@ size_t ws_emit_sqe(uint32_t nqueues);
 size_t ws_build_put(uint64_t n);
 size_t ws_registry(uint64_t n, uint64_t capacity);
 
+// Device address and size of the allocation-free entry point's scratch on
+// the current device (looked up on the first call on each device).
+hipError_t noalloc_scratch(void **ptr, size_t *bytes);
+
 // Polls a look-back wait may take before it gives up (process-wide; set by
 // dmadesc_debug_wait_limit, default 2^22).
 uint32_t wait_limit();
