@@ -8,19 +8,25 @@ one stream, over the 16,777,216-request Mixed workload (256 GiB heap of
 4,194,304 GPU pages, 4,096 regions, log-uniform 512 B - 1 MiB requests,
 Zipf(1.1) over 64 queues). Inputs are resident in HBM before timing starts.
 
-Prints ONE JSON line. `value` is requests per second (millions) over the
-timed steps; `roofline` describes the dominant call (the PRP build of the
-step's layout; the other layout's build is timed alone beside it):
-algorithmic bytes of one launch / its mean duration from HIP events recorded
-on the stream it runs on, on every 10th timed step (`per_call_ms` likewise;
-each event record is a queue marker that would add a few microseconds to
-every step). `emit_sqe` times the stage after the path (NVMe
-submission entries for the first window of every queue) on the step's outputs,
-`registry` a batch of registrations and deregistrations on the device
-registration table, `build_put` RDMA put descriptors for a VMM heap and
-`cq_mirror` the completion-queue mirror draining 64 full queues, all outside
-the timed steps. `cpu_baseline` times the single-threaded oracle on a
-bounded sample of the same workload.
+Prints ONE JSON line:
+  value        requests per second (millions) over the K timed steps (wall
+               clock between two synchronizations)
+  step         median/min/p95 of one step from HIP events around each of
+               >= 20 further steps; algorithmic bytes with every column
+               counted once (and the per-call sum beside it)
+  roofline     the dominant call (the PRP build of the step's layout):
+               algorithmic bytes of one launch / its mean duration from HIP
+               events recorded on its stream around every call of >= 10
+               sampled timed steps (per_call_ms likewise)
+  batch_call   dmadesc_build_batch (lookup, PRP build and split in one call
+               that reads the request columns once) on the same batch
+  per_config   Tiny, Small-I/O, Large/chaining and MR-heavy, each with its own
+               functions, median/min/p95 over >= 20 iterations (>= 200 for
+               Tiny and Small)
+  emit_sqe, registry, build_put, cq_mirror: the stages beside the path,
+               timed after the steps
+  cpu_baseline the single-threaded oracle, per function and end to end,
+               median of 3 runs on one pinned core
 """
 from __future__ import annotations
 
@@ -49,19 +55,21 @@ def parse():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="mixed",
-                    choices=["tiny", "small", "large", "mixed"])
+                    choices=["tiny", "small", "large", "mrheavy", "mixed"])
     ap.add_argument("--layout", default="packed", choices=["packed", "page"],
                     help="PRP list layout of the timed step: lists back to back "
                          "(dmadesc_build_prp_packed) or one run of list pages per request "
                          "(dmadesc_build_prp); the other layout's PRP build is timed too")
-    ap.add_argument("--cpu-sample", type=int, default=1 << 21,
+    ap.add_argument("--cpu-sample", type=int, default=1 << 24,
                     help="requests of the workload the oracle is timed on")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0,
-                    help="minimum CPU time spent timing the oracle")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--event-every", type=int, default=10,
-                    help="record per-call HIP events on every k-th timed step (each event "
-                         "record is a queue marker that costs a few microseconds)")
+    ap.add_argument("--sampled-steps", type=int, default=10,
+                    help="timed steps that carry per-call HIP events (at least 10; each "
+                         "event record is a queue marker that costs a few microseconds)")
+    ap.add_argument("--dist-steps", type=int, default=30,
+                    help="steps timed one by one with HIP events for median/min/p95")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the per-config lines of the other workloads")
     ap.add_argument("--emit-reps", type=int, default=20,
                     help="launches of the submission-entry stage timed after the steps "
                          "(0 = skip it)")
@@ -82,11 +90,14 @@ def prp_source_hash() -> str:
 
 
 def algorithmic_bytes(d, np):
-    """Bytes each call must move, each column once (per-request figures:
-    lookup 16 read + 25 written; PRP 16 read + 8 per GPU page touched, 17
-    written + 8 per list word; split 4 read + 4 written). List words: page
-    layout m + L - 1 per request (entries and chain pointers); packed layout
-    the whole dense range, E + floor(E / 511) words for E entries in all."""
+    """Bytes each call must move, each column once (per request: lookup 16
+    read + 25 written; PRP 16 read + 8 per GPU page touched, 17 written + 8
+    per list word; split 4 read + 4 written; the region table 20 per region).
+    List words: page layout m + L - 1 per request (entries and chain
+    pointers); packed layout the whole dense range, E + floor(E / 511) words
+    for E entries in all. `step_*` count every column of the step once: off
+    and len are read once although both the lookup and the PRP build take
+    them."""
     off, ln = d["off"], d["len"]
     n = off.shape[0]
     heap = np.uint64(d["lut_entries"]) * np.uint64(65536)
@@ -100,11 +111,185 @@ def algorithmic_bytes(d, np):
     e_total = int(m.sum())
     packed_words = float(e_total + e_total // 511)
     lookup = n * (16 + 25) + d["regions"] * 20
-    base = n * (16 + 17) + 8 * float(frames.sum())
+    prp_base = n * (16 + 17) + 8 * float(frames.sum())
     split = n * 8
-    return dict(lookup=float(lookup), build_prp=base + 8 * entries,
-                build_prp_packed=base + 8 * packed_words, partition=float(split),
-                list_entries=entries, prp_entries=float(pages.astype(np.float64).sum()))
+    out = dict(lookup=float(lookup), build_prp=prp_base + 8 * entries,
+               build_prp_packed=prp_base + 8 * packed_words, partition=float(split),
+               list_entries=entries, prp_entries=float(pages.astype(np.float64).sum()))
+    # The step, each column once: off/len read once, whatever reads them.
+    for layout, key in (("page", "build_prp"), ("packed", "build_prp_packed")):
+        b = 0.0
+        if d["regions"]:
+            b += out["lookup"]
+        if d["lut_entries"]:
+            b += out[key] - (n * 16 if d["regions"] else 0)
+        if d["nqueues"]:
+            b += split
+        out[f"step_{layout}"] = b
+        out[f"step_sum_{layout}"] = (out["lookup"] if d["regions"] else 0) + \
+            (out[key] if d["lut_entries"] else 0) + (split if d["nqueues"] else 0)
+    return out
+
+
+def dist(np, ms):
+    """median, min and p95 of a list of milliseconds."""
+    a = np.asarray(ms, dtype=np.float64)
+    return {"median_ms": round(float(np.median(a)), 5), "min_ms": round(float(a.min()), 5),
+            "p95_ms": round(float(np.percentile(a, 95)), 5), "iterations": int(a.size)}
+
+
+def timed_iters(torch, np, fn, reps, warm=3):
+    """Runs fn warm + reps times, each bracketed by HIP events on the current
+    stream; returns the reps durations in ms."""
+    for _ in range(warm):
+        fn()
+    torch.cuda.synchronize()
+    evs = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        fn()
+        e1.record()
+        evs.append((e0, e1))
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in evs]
+
+
+class Step:
+    """The path's calls over one uploaded workload: lookup (if it has
+    regions), PRP build (if it has a heap) and split (if it has queues), in
+    that order on the current stream, with outputs and workspaces reused."""
+
+    def __init__(self, dd, torch, np, d, packed):
+        self.dd, self.torch, self.d, self.packed = dd, torch, d, packed
+        dev = torch.device("cuda:0")
+        up = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)  # noqa: E731
+        self.n, self.nq, self.bus = d["n"], d["nqueues"], d["list_bus_base"]
+        self.rs, self.re, self.rk = up(d["rstart"]), up(d["rend"]), up(d["rlkey"])
+        self.off, self.ln, self.qid, self.lut = up(d["off"]), up(d["len"]), up(d["qid"]), up(d["lut"])
+        self.lk = self.pr = self.sp = self.bt = None
+        self.pool = self.pool_pages = None
+        if d["lut_entries"]:
+            self.pool, self.pool_pages = self.pool_for(packed)
+            self.ws_prp = torch.empty(max(dd.workspace_bytes(dd.OP_BUILD_PRP, self.n), 1),
+                                      dtype=torch.uint8, device=dev)
+        if self.nq:
+            self.ws_sp = torch.empty(max(dd.workspace_bytes(dd.OP_PARTITION, self.n, self.nq), 1),
+                                     dtype=torch.uint8, device=dev)
+
+    def pool_for(self, packed):
+        """A pool of exactly the pages the batch needs (asked of the library
+        itself: with an empty pool the call still reports them)."""
+        torch, dev = self.torch, self.torch.device("cuda:0")
+        empty = torch.empty((0, 512), dtype=torch.uint64, device=dev)
+        probe = self.dd.build_prp(self.lut, self.off, self.ln, self.bus, empty, packed=packed)
+        pages = int(probe["total_pages"].cpu()[0])
+        return torch.empty((max(pages, 1), 512), dtype=torch.uint64, device=dev), pages
+
+    def calls(self):
+        out = []
+        if self.d["regions"]:
+            out.append("mr_lookup")
+        if self.d["lut_entries"]:
+            out.append("build_prp_packed" if self.packed else "build_prp")
+        if self.nq:
+            out.append("partition_by_queue")
+        return out
+
+    def run(self, ev=None):
+        """One step; with `ev` (a list of len(calls) + 1 events) each call is
+        bracketed on the stream it runs on."""
+        dd, d = self.dd, self.d
+        k = 0
+        if ev:
+            ev[0].record()
+        if d["regions"]:
+            self.lk = dd.mr_lookup(self.rs, self.re, self.rk, self.off, self.ln,
+                                   va_base=d["va_base"], out=self.lk)
+            k += 1
+            if ev:
+                ev[k].record()
+        if d["lut_entries"]:
+            self.pr = dd.build_prp(self.lut, self.off, self.ln, self.bus, self.pool, out=self.pr,
+                                   ws=self.ws_prp, packed=self.packed, check=False)
+            k += 1
+            if ev:
+                ev[k].record()
+        if self.nq:
+            self.sp = dd.partition_by_queue(self.qid, self.nq, out=self.sp, ws=self.ws_sp,
+                                            check=False)
+            k += 1
+            if ev:
+                ev[k].record()
+
+    def batch(self):
+        """The same step as one dmadesc_build_batch call."""
+        d = self.d
+        if self.bt is None:
+            self.ws_bt = self.torch.empty(
+                self.dd.batch_workspace_bytes(self.n, self.nq, d["regions"]),
+                dtype=self.torch.uint8, device=self.torch.device("cuda:0"))
+        self.bt = self.dd.build_batch(self.lut, self.off, self.ln, self.qid, self.nq, self.bus,
+                                      self.pool, self.rs, self.re, self.rk, va_base=d["va_base"],
+                                      packed=self.packed, lookup=bool(d["regions"]), out=self.bt,
+                                      ws=self.ws_bt, check=False)
+
+    def check_outputs(self, np):
+        """After the timed work: no refused requests beyond those the
+        workload itself makes, no expired slot-scan wait, no overflow ids."""
+        res = {}
+        if self.pr is not None:
+            st = self.pr["status"].cpu().numpy()
+            res["refused_requests"] = int((st != 0).sum())
+            res["expired_waits"] = int(self.ws_prp[4:8].view(self.torch.int32).item())
+            if res["expired_waits"] or (st == self.dd.PRP_EBUSY).any():
+                raise RuntimeError("a slot-scan wait expired during the benchmark")
+        if self.sp is not None:
+            res["overflow_ids"] = int(self.sp["n_invalid"].view(self.torch.int64)[0].item())
+        return res
+
+
+def run_config(dd, torch, np, name, reps, packed=True):
+    """One workload with its own functions (lookup, PRP build, split as it
+    has them): median/min/p95 of reps steps, per-call medians, rates."""
+    import synth
+    d = synth.generate(name)
+    ab = algorithmic_bytes(d, np)
+    st = Step(dd, torch, np, d, packed)
+    layout = "packed" if packed else "page"
+    step_ms = timed_iters(torch, np, st.run, reps)
+    calls = st.calls()
+    ev_ms = {c: [] for c in calls}
+    for _ in range(min(reps, 50)):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)]
+        st.run(ev)
+        torch.cuda.synchronize()
+        for k, c in enumerate(calls):
+            ev_ms[c].append(ev[k].elapsed_time(ev[k + 1]))
+    med = float(np.median(step_ms))
+    nbytes = ab[f"step_{layout}"]
+    out = {"workload": name, "requests": d["n"], "functions": calls,
+           "requests_per_s": round(d["n"] / (med * 1e-3), 1),
+           "step": dist(np, step_ms),
+           "step_algorithmic_bytes": nbytes,
+           "step_algorithmic_gbs": round(nbytes / (med * 1e-3) / 1e9, 1),
+           "step_frac_of_peak": round(nbytes / (med * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+           "per_call_median_ms": {c: round(float(np.median(v)), 5) for c, v in ev_ms.items()}}
+    if d["lut_entries"]:
+        key = "build_prp_packed" if packed else "build_prp"
+        pm = float(np.median(ev_ms[key]))
+        out.update(prp_layout=layout, list_pages=st.pool_pages,
+                   prp_entries_per_s=round(ab["prp_entries"] / (med * 1e-3), 1),
+                   prp_call={"algorithmic_bytes": ab[key],
+                             "gbs": round(ab[key] / (pm * 1e-3) / 1e9, 1),
+                             "frac": round(ab[key] / (pm * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)})
+    if d["regions"]:
+        lm = float(np.median(ev_ms["mr_lookup"]))
+        out["lookup_call"] = {"regions": d["regions"], "algorithmic_bytes": ab["lookup"],
+                              "gbs": round(ab["lookup"] / (lm * 1e-3) / 1e9, 1),
+                              "frac": round(ab["lookup"] / (lm * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+    out.update(st.check_outputs(np))
+    return out
 
 
 def emit_stage(dd, d, np, torch, prp_out, sp_out, ln, reps):
@@ -307,38 +492,70 @@ def registry_stage(dd, d, np, torch, reps):
             "note": "register timing includes the binding's read of the needed capacity"}
 
 
-def cpu_baseline(name, sample, min_seconds, layout):
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(name, sample, layout):
+    """The single-threaded oracle (lookup, PRP build of the step's layout
+    with lists into a pre-faulted host pool, split) on the first `sample`
+    requests of the workload, pinned to one core: each function timed 3
+    times (1 if a run passes 20 s), medians reported; end to end = the sum
+    of the medians."""
     import numpy as np
 
     import oracle
     import synth
     d = synth.generate(name, n=sample)
-    bus = d["list_bus_base"]
+    n, bus = d["n"], d["list_bus_base"]
     build = oracle.build_prp_packed if layout == "packed" else oracle.build_prp
-    total = build(d["lut"], d["off"], d["len"], bus, 0)["total"]
-    pool = np.ones((max(total, 1), 512), dtype=np.uint64)      # pre-faulted, reused
+    fns = {}
+    if d["regions"]:
+        fns["mr_lookup"] = lambda: oracle.mr_lookup(d["rstart"], d["rend"], d["rlkey"], d["off"],
+                                                    d["len"], va_base=d["va_base"])
+    pool = None
+    if d["lut_entries"]:
+        total = build(d["lut"], d["off"], d["len"], bus, 0)["total"]
+        pool = np.ones((max(total, 1), 512), dtype=np.uint64)      # pre-faulted, reused
+        fns["build_prp"] = lambda: build(d["lut"], d["off"], d["len"], bus, total, pool=pool)
+    if d["nqueues"]:
+        fns["partition_by_queue"] = lambda: oracle.partition(d["qid"], d["nqueues"])
     old = os.sched_getaffinity(0)
     cpu = min(old)
     os.sched_setaffinity(0, {cpu})
+    times = {k: [] for k in fns}
     try:
-        reps, spent = 0, 0.0
-        while spent < min_seconds:
-            t0 = time.perf_counter()
-            if d["regions"]:
-                oracle.mr_lookup(d["rstart"], d["rend"], d["rlkey"], d["off"], d["len"],
-                                 va_base=d["va_base"])
-            build(d["lut"], d["off"], d["len"], bus, total, pool=pool)
-            oracle.partition(d["qid"], d["nqueues"])
-            spent += time.perf_counter() - t0
-            reps += 1
+        for r in range(3):
+            for k, fn in fns.items():
+                t0 = time.perf_counter()
+                fn()
+                times[k].append(time.perf_counter() - t0)
+            if max(v[-1] for v in times.values()) > 20.0:
+                break
     finally:
         os.sched_setaffinity(0, old)
-    return {"value": round(sample * reps / spent / 1e6, 4), "unit": "M req/s", "cores": 1,
-            "kind": "oracle",
-            "sample": (f"first {sample:,} requests of the {name} workload, lookup + PRP build "
-                       f"({layout} lists into a pre-faulted host pool) + split, single thread pinned "
-                       f"to one core, {reps} repetitions, {spent:.1f} s"),
-            "host_cores": os.cpu_count()}
+    med = {k: float(np.median(v)) for k, v in times.items()}
+    e2e = sum(med.values())
+    ab = algorithmic_bytes(d, np)
+    per = {k: {"median_s": round(v, 4), "requests_per_s": round(n / v, 1), "runs": len(times[k])}
+           for k, v in med.items()}
+    if "build_prp" in per:
+        per["build_prp"]["prp_entries_per_s"] = round(ab["prp_entries"] / med["build_prp"], 1)
+    return {"value": round(n / e2e / 1e6, 4), "unit": "M req/s", "cores": 1, "kind": "oracle",
+            "sample": (f"first {n:,} requests of the {name} workload: "
+                       + " + ".join(fns) + f" ({layout} lists into a pre-faulted host pool), "
+                       "single thread pinned to one core, median of 3 runs per function, "
+                       f"{sum(sum(v) for v in times.values()):.1f} s in all"),
+            "per_function": per,
+            "prp_entries_per_s": round(ab["prp_entries"] / e2e, 1) if pool is not None else None,
+            "host_cores": os.cpu_count(), "cpu_model": cpu_model()}
 
 
 def copy_calibration():
@@ -421,103 +638,92 @@ def main():
     torch.cuda.set_device(dev)
     d = synth.generate(args.workload)
     n, nq = d["n"], d["nqueues"]
-    bus = d["list_bus_base"]
-    up = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)  # noqa: E731
-    rs, re_, rk = up(d["rstart"]), up(d["rend"]), up(d["rlkey"])
-    off, ln, qid, lut = up(d["off"]), up(d["len"]), up(d["qid"]), up(d["lut"])
-
-    # Capacity query: with an empty pool the call still reports the pages
-    # the batch needs.
     packed = args.layout == "packed"
-    empty = torch.empty((0, 512), dtype=torch.uint64, device=dev)
-
-    def pool_for(pk):
-        probe = dd.build_prp(lut, off, ln, bus, empty, packed=pk)
-        torch.cuda.synchronize()
-        pages = int(probe["total_pages"].cpu()[0])
-        return torch.empty((max(pages, 1), 512), dtype=torch.uint64, device=dev), pages
-
-    pool, pool_pages = pool_for(packed)
-
-    lk_out = prp_out = sp_out = None
-    ws_prp = torch.empty(max(dd.workspace_bytes(dd.OP_BUILD_PRP, n), 1), dtype=torch.uint8, device=dev)
-    ws_sp = torch.empty(max(dd.workspace_bytes(dd.OP_PARTITION, n, max(nq, 1)), 1),
-                        dtype=torch.uint8, device=dev)
-
-    def step(timed_calls):
-        # The three calls are issued back to back on the current stream; on
-        # sampled steps HIP events bracket each call on that stream.
-        nonlocal lk_out, prp_out, sp_out
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)] if timed_calls else None
-        if ev: ev[0].record()
-        if d["regions"]:
-            lk_out = dd.mr_lookup(rs, re_, rk, off, ln, va_base=d["va_base"], out=lk_out)
-        if ev: ev[1].record()
-        prp_out = dd.build_prp(lut, off, ln, bus, pool, out=prp_out, ws=ws_prp, packed=packed,
-                               check=False)
-        if ev: ev[2].record()
-        if nq:
-            sp_out = dd.partition_by_queue(qid, nq, out=sp_out, ws=ws_sp, check=False)
-        if ev: ev[3].record()
-        return ev
-
+    layout = args.layout
     ab = algorithmic_bytes(d, np)
+    st = Step(dd, torch, np, d, packed)
+    calls = st.calls()
+    prp_key = "build_prp_packed" if packed else "build_prp"
+    dominant = prp_key if d["lut_entries"] else "mr_lookup"
+    dom_bytes = ab[prp_key] if d["lut_entries"] else ab["lookup"]
+
     # The other layout's PRP build, timed alone on the same inputs. It runs
     # before the warm-up steps, so the timed steps find the GPU at its
     # steady clocks (the first few dozen steps otherwise run about 1 % slow).
-    other = "page" if packed else "packed"
-    o_pool, o_pages = pool_for(not packed)
-    o_out = None
-    o_ev = []
-    for r in range(max(args.steps // 2, 3) + 3):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        o_out = dd.build_prp(lut, off, ln, bus, o_pool, out=o_out, ws=ws_prp, packed=not packed,
-                             check=False)
-        e1.record()
-        if r >= 3:
-            o_ev.append((e0, e1))
-    torch.cuda.synchronize()
-    o_ms = float(np.mean([a.elapsed_time(b) for a, b in o_ev]))
-    o_key = "build_prp" if packed else "build_prp_packed"
-    o_gbs = ab[o_key] / (o_ms * 1e-3) / 1e9
-    o_refused = int((o_out["status"].cpu().numpy() != 0).sum())
-    del o_pool, o_out
+    other = None
+    if d["lut_entries"]:
+        o_pool, o_pages = st.pool_for(not packed)
+        o_key = "build_prp" if packed else "build_prp_packed"
+        o_out = [None]
+
+        def o_call():
+            o_out[0] = dd.build_prp(st.lut, st.off, st.ln, st.bus, o_pool, out=o_out[0],
+                                    ws=st.ws_prp, packed=not packed, check=False)
+        o_ms = timed_iters(torch, np, o_call, max(args.steps // 2, 20))
+        o_med = float(np.median(o_ms))
+        o_gbs = ab[o_key] / (o_med * 1e-3) / 1e9
+        other = {"list_pages": o_pages, "algorithmic_bytes_per_launch": ab[o_key],
+                 **dist(np, o_ms), "achieved_gbs": round(o_gbs, 1),
+                 "frac": round(o_gbs / PEAK_HBM_GBS, 4),
+                 "refused_requests": int((o_out[0]["status"].cpu().numpy() != 0).sum())}
+        del o_pool, o_out
 
     for _ in range(args.warmup):
-        step(False)
+        st.run()
     torch.cuda.synchronize()
+    # Timed steps; per-call events on >= 10 of them, spread evenly.
+    k_sampled = min(args.steps, max(10, args.sampled_steps))
+    sampled = set(np.linspace(0, args.steps - 1, k_sampled).round().astype(int).tolist())
     events = []
-    every = max(args.event_every, 1)
     t0 = time.perf_counter()
     for s_i in range(args.steps):
-        ev = step(s_i % every == every - 1 or (s_i == args.steps - 1 and not events))
-        if ev:
+        ev = None
+        if s_i in sampled:
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)]
             events.append(ev)
+        st.run(ev)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-
-    calls = ["mr_lookup", "build_prp", "partition_by_queue"]
+    ms = elapsed / args.steps * 1e3
     per_call = {c: float(np.mean([e[k].elapsed_time(e[k + 1]) for e in events]))
                 for k, c in enumerate(calls)}
-    status = prp_out["status"].cpu().numpy()
-    prp_key = "build_prp_packed" if packed else "build_prp"
-    step_bytes = ab["lookup"] * bool(d["regions"]) + ab[prp_key] + ab["partition"] * bool(nq)
-    ms = elapsed / args.steps * 1e3
-    prp_ms = per_call["build_prp"]
-    achieved = ab[prp_key] / (prp_ms * 1e-3) / 1e9
+    checks = st.check_outputs(np)
 
+    # Step-time distribution: steps timed one by one.
+    step_ms = timed_iters(torch, np, st.run, max(args.dist_steps, 20), warm=0)
+    step_bytes, step_sum = ab[f"step_{layout}"], ab[f"step_sum_{layout}"]
+    step_med = float(np.median(step_ms))
+
+    # The same step as one dmadesc_build_batch call, checked against the
+    # separate calls' outputs (which are those of the last step).
+    batch = None
+    if d["lut_entries"] and nq:
+        ref = {}
+        for o in (st.lk, st.pr, st.sp):
+            if o:
+                ref.update({k: v.clone() for k, v in o.items()})
+        b_ms = timed_iters(torch, np, st.batch, 20)
+        same = all(torch.equal(st.bt[k], v) for k, v in ref.items())
+        b_med = float(np.median(b_ms))
+        batch = {"call": "dmadesc_build_batch", **dist(np, b_ms),
+                 "requests_per_s": round(n / (b_med * 1e-3), 1),
+                 "algorithmic_gbs": round(step_bytes / (b_med * 1e-3) / 1e9, 1),
+                 "frac": round(step_bytes / (b_med * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                 "same_outputs_as_the_calls": bool(same)}
+        del ref
+
+    dom_ms = per_call[dominant]
+    achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
     traffic = None
-    tf = traffic_file(args.layout, args.workload)
-    if os.path.exists(tf):
+    tf = traffic_file(layout, args.workload)
+    if d["lut_entries"] and os.path.exists(tf):
         with open(tf) as f:
             rec = json.load(f)
         if rec.get("source_sha256") == prp_source_hash():
             traffic = rec.get("traffic_bytes_per_launch")
-
-
-    kernel = ("dmadesc_build_prp_packed" if packed else "dmadesc_build_prp") + \
-        " (k_ws_clear + k_prp_build)"
+    kernel = {"build_prp_packed": "dmadesc_build_prp_packed (k_ws_clear + k_prp_build)",
+              "build_prp": "dmadesc_build_prp (k_ws_clear + k_prp_build)",
+              "mr_lookup": "dmadesc_mr_lookup"}[dominant]
     result = {
         "metric": "descriptor requests/sec (M/s) + achieved HBM GB/s vs MI355X peak",
         "value": round(n * args.steps / elapsed / 1e6, 3),
@@ -532,28 +738,40 @@ def main():
         "dtype": "u64",
         "data": "synthetic",
         "config": {"workload": args.workload, "requests": n, "lut_entries": d["lut_entries"],
-                   "regions": d["regions"], "nqueues": nq, "prp_layout": args.layout,
-                   "list_pages": pool_pages,
-                   "calls": f"mr_lookup + {kernel.split()[0][8:]} + partition_by_queue, one stream"},
+                   "regions": d["regions"], "nqueues": nq, "prp_layout": layout,
+                   "list_pages": st.pool_pages,
+                   "calls": " + ".join(calls) + ", one stream"},
         "roofline": {"bound": "hbm", "kernel": kernel,
                      "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
-                     "algorithmic_bytes_per_launch": ab[prp_key],
-                     "mean_launch_ms": round(prp_ms, 4)},
+                     "algorithmic_bytes_per_launch": dom_bytes,
+                     "mean_launch_ms": round(dom_ms, 4), "sampled_launches": len(events)},
+        "step": {**dist(np, step_ms),
+                 "algorithmic_bytes": step_bytes,
+                 "algorithmic_bytes_per_call_sum": step_sum,
+                 "algorithmic_gbs": round(step_bytes / (step_med * 1e-3) / 1e9, 1),
+                 "frac_of_peak": round(step_bytes / (step_med * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                 "timed_region_gbs": round(step_bytes / (ms * 1e-3) / 1e9, 1),
+                 "timed_region_frac": round(step_bytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
         "per_call_ms": {k: round(v, 4) for k, v in per_call.items()},
         "per_call_sampled_steps": len(events),
-        "step_algorithmic_gbs": round(step_bytes / (ms * 1e-3) / 1e9, 1),
-        "step_frac_of_peak": round(step_bytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
         "prp_entries_per_s": round(ab["prp_entries"] * args.steps / elapsed, 1),
-        "refused_requests": int((status != 0).sum()),
-        f"{other}_layout_build_prp": {
-            "mean_launch_ms": round(o_ms, 4), "list_pages": o_pages,
-            "algorithmic_bytes_per_launch": ab[o_key], "achieved_gbs": round(o_gbs, 1),
-            "frac": round(o_gbs / PEAK_HBM_GBS, 4),
-            "refused_requests": o_refused},
+        "checks": checks,
     }
-    if nq and args.emit_reps > 0:
-        result["emit_sqe"] = emit_stage(dd, d, np, torch, prp_out, sp_out, ln, args.emit_reps)
+    if batch:
+        result["batch_call"] = batch
+    if other:
+        result[f"{'page' if packed else 'packed'}_layout_build_prp"] = other
+    if not args.no_configs:
+        result["per_config"] = {}
+        for name, reps in (("tiny", 200), ("small", 200), ("large", 20), ("mrheavy", 20),
+                           ("mixed", 20)):
+            if name == args.workload:
+                continue
+            result["per_config"][name] = run_config(dd, torch, np, name, reps, packed)
+            torch.cuda.empty_cache()
+    if nq and d["lut_entries"] and args.emit_reps > 0:
+        result["emit_sqe"] = emit_stage(dd, d, np, torch, st.pr, st.sp, st.ln, args.emit_reps)
     if d["regions"] and args.emit_reps > 0:
         result["registry"] = registry_stage(dd, d, np, torch, 10)
     if args.emit_reps > 0:
@@ -561,8 +779,7 @@ def main():
     if args.emit_reps > 0:
         result["cq_mirror"] = cq_stage(dd, np, torch, 10)
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(args.workload, min(args.cpu_sample, n),
-                                              args.cpu_seconds, args.layout)
+        result["cpu_baseline"] = cpu_baseline(args.workload, min(args.cpu_sample, n), layout)
     print(json.dumps(result), flush=True)
 
 

@@ -11,6 +11,7 @@
  *   dmadesc_build_prp_packed   the same entries with the lists packed back to
  *                              back (qword-offset list pointers)
  *   dmadesc_partition_by_queue stable split of the requests by destination queue
+ *   dmadesc_build_batch        all three in one call (one read of the requests)
  *
  * and one stage after them:
  *
@@ -222,7 +223,8 @@ int dmadesc_mr_table_check(const uint64_t *reg_start, const uint64_t *reg_end,
  * Per request, with pages p = ((off & 4095) + len + 4095) >> 12, entries
  * m = p - 1 and, for p >= 3, list pages L = ceil((m - 1) / 511).
  * Slot scan: list pages are handed out by a one-pass device-wide scan over
- * blocks of 1,024 requests whose waits are bounded. A block whose wait
+ * blocks of 1,024 requests (256 for batches of at most 2^19 requests) whose
+ * waits are bounded. A block whose wait
  * expires (never at the default bound while blocks make progress) refuses
  * its list requests with DMADESC_PRP_EBUSY (prp1 = prp2 = 0, no list
  * entries); every other request is built exactly as above, and if the
@@ -322,6 +324,51 @@ int dmadesc_build_prp_packed_noalloc(const uint64_t *lut, uint64_t lut_entries,
 int dmadesc_partition_by_queue(const uint32_t *qid, uint64_t n, uint32_t nqueues,
                                uint32_t *perm, uint64_t *qoff, uint64_t *n_invalid,
                                void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * dmadesc_build_batch - the whole path for one batch in one call: the
+ * page-rounded region lookup, the PRP build and the stable split by queue,
+ * reading off, len and qid once.
+ *
+ * The three steps belong to one request's way to the device:
+ * [NCCL-26] "IB Backend MR Cache" (the containment lookup of the rounded
+ * range, returning the region's handle and key), [UPCIE] introduction (PRP
+ * entries from the GPU-page table when the command is built) and [MORI] the
+ * thread-scope put (requests grouped by destination queue). Its outputs are
+ * exactly those of dmadesc_mr_lookup, dmadesc_build_prp (flags 0) or
+ * dmadesc_build_prp_packed (flags DMADESC_BATCH_PACKED) and
+ * dmadesc_partition_by_queue called on the same arguments: the three column
+ * groups are independent (a lookup miss still gets its PRPs and its queue
+ * slot), and each keeps the errors, statuses and EBUSY refusals of its call.
+ *   reg_start, reg_end, reg_lkey, nregions, page_shift, va_base
+ *                 as dmadesc_mr_lookup; the lookup outputs handle, lkey,
+ *                 kind, rbase, rend are either all given or all NULL (then
+ *                 no lookup runs and the table arguments are ignored)
+ *   lut, lut_entries, list_bus_base, list_pool, pool_pages, prp1, prp2,
+ *   status, total_pages   as dmadesc_build_prp
+ *   qid, nqueues, perm, qoff, n_invalid   as dmadesc_partition_by_queue
+ *   off, len, n   the requests, shared by all three
+ *   flags         DMADESC_BATCH_PACKED or 0; other bits -EINVAL
+ * Workspace: dmadesc_batch_workspace_bytes(n, nqueues, nregions) bytes
+ * (nregions 0 when no lookup runs); its first 8 bytes hold, on return, the
+ * slot scan's block counter and count of expired waits, as in
+ * dmadesc_build_prp.
+ */
+#define DMADESC_BATCH_PACKED 1u
+int dmadesc_build_batch(const uint64_t *reg_start, const uint64_t *reg_end,
+                        const uint32_t *reg_lkey, uint32_t nregions, uint32_t page_shift,
+                        uint64_t va_base, const uint64_t *lut, uint64_t lut_entries,
+                        const uint64_t *off, const uint64_t *len, const uint32_t *qid,
+                        uint64_t n, uint32_t nqueues, uint64_t list_bus_base,
+                        uint64_t *list_pool, uint64_t pool_pages, uint32_t flags,
+                        int32_t *handle, uint32_t *lkey, uint8_t *kind, uint64_t *rbase,
+                        uint64_t *rend, uint64_t *prp1, uint64_t *prp2, uint8_t *status,
+                        uint64_t *total_pages, uint32_t *perm, uint64_t *qoff,
+                        uint64_t *n_invalid, void *ws, size_t ws_bytes, void *stream);
+
+/* Workspace bytes of dmadesc_build_batch (0 for nqueues outside
+ * 1..DMADESC_MAX_QUEUES, n >= 2^32 or nregions >= 2^31). Host-only. */
+size_t dmadesc_batch_workspace_bytes(uint64_t n, uint32_t nqueues, uint32_t nregions);
 
 /*
  * dmadesc_emit_sqe - NVMe submission entries per queue, one window per call.

@@ -15,6 +15,7 @@ import torch
 from . import _build
 
 __all__ = ["mr_lookup", "build_prp", "build_prp_packed", "build_prp_packed_noalloc",
+           "build_batch", "batch_workspace_bytes", "BATCH_PACKED",
            "partition_by_queue", "emit_sqe",
            "ring_addresses", "DeviceRegistry", "build_put", "cq_slots", "cq_attach",
            "cq_mirror", "cq_slot_state",
@@ -61,6 +62,10 @@ _EXPORTS = {
                               _P, _SIZE, _P], ctypes.c_int),
     "dmadesc_reg_deregister": ([_P, _P, _P, _P, _P, _P, _U64, _P, _U64, _P, _P, _SIZE, _P],
                                ctypes.c_int),
+    "dmadesc_build_batch": ([_P, _P, _P, _U32, _U32, _U64, _P, _U64, _P, _P, _P, _U64, _U32,
+                             _U64, _P, _U64, _U32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                             _P, _P, _SIZE, _P], ctypes.c_int),
+    "dmadesc_batch_workspace_bytes": ([_U64, _U32, _U32], _SIZE),
     "dmadesc_workspace_bytes": ([ctypes.c_int, _U64, _U32], _SIZE),
     "dmadesc_strerror": ([ctypes.c_int], ctypes.c_char_p),
     "dmadesc_version": ([], ctypes.c_int),
@@ -301,6 +306,82 @@ def partition_by_queue(qid: torch.Tensor, nqueues: int, out: dict | None = None,
         if bad:
             raise DmadescRefused(f"dmadesc_partition_by_queue: {bad} request(s) name a queue "
                                  f">= nqueues ({nqueues}); they are in the overflow bucket", out)
+    return out
+
+
+BATCH_PACKED = 1
+
+
+def batch_workspace_bytes(n: int, nqueues: int, nregions: int) -> int:
+    return int(lib().dmadesc_batch_workspace_bytes(n, nqueues, nregions))
+
+
+def build_batch(lut: torch.Tensor, off: torch.Tensor, length: torch.Tensor,
+                qid: torch.Tensor, nqueues: int, list_bus_base: int, pool: torch.Tensor,
+                reg_start: torch.Tensor | None = None, reg_end: torch.Tensor | None = None,
+                reg_lkey: torch.Tensor | None = None, va_base: int = 0, page_shift: int = 12,
+                packed: bool = True, lookup: bool = True, out: dict | None = None,
+                ws: torch.Tensor | None = None, stream=None, check: bool = True) -> dict:
+    """dmadesc_build_batch: lookup (when lookup=True and a table is given),
+    PRP build and split in one call. Returns one dict with the columns of
+    mr_lookup, build_prp and partition_by_queue. check=True synchronizes and
+    raises DmadescRefused on expired slot-scan waits or queue ids >= nqueues."""
+    n = off.numel()
+    dev = off.device
+    if pool.dim() != 2 or pool.shape[1] != 512:
+        raise ValueError("pool must have shape [pool_pages, 512]")
+    lookup = lookup and reg_start is not None
+    r = reg_start.numel() if lookup else 0
+    if out is None:
+        out = dict(prp1=torch.empty(n, dtype=torch.uint64, device=dev),
+                   prp2=torch.empty(n, dtype=torch.uint64, device=dev),
+                   status=torch.empty(n, dtype=torch.uint8, device=dev),
+                   total_pages=torch.empty(1, dtype=torch.uint64, device=dev),
+                   perm=torch.empty(n, dtype=torch.uint32, device=dev),
+                   qoff=torch.empty(nqueues + 2, dtype=torch.uint64, device=dev),
+                   n_invalid=torch.empty(1, dtype=torch.uint64, device=dev))
+        if lookup:
+            out.update(handle=torch.empty(n, dtype=torch.int32, device=dev),
+                       lkey=torch.empty(n, dtype=torch.uint32, device=dev),
+                       kind=torch.empty(n, dtype=torch.uint8, device=dev),
+                       rbase=torch.empty(n, dtype=torch.uint64, device=dev),
+                       rend=torch.empty(n, dtype=torch.uint64, device=dev))
+    need = batch_workspace_bytes(n, nqueues, r)
+    if ws is None:
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    wptr = _dev(ws, torch.uint8, "ws")
+    if ws.numel() < need:
+        raise ValueError(f"workspace needs {need} bytes, got {ws.numel()}")
+    if lookup:
+        tbl = (_dev(reg_start, torch.uint64, "reg_start", r), _dev(reg_end, torch.uint64, "reg_end", r),
+               _dev(reg_lkey, torch.uint32, "reg_lkey", r))
+        lk = (_dev(out["handle"], torch.int32, "handle", n), _dev(out["lkey"], torch.uint32, "lkey", n),
+              _dev(out["kind"], torch.uint8, "kind", n), _dev(out["rbase"], torch.uint64, "rbase", n),
+              _dev(out["rend"], torch.uint64, "rend", n))
+    else:
+        tbl, lk = (None, None, None), (None,) * 5
+    rc = lib().dmadesc_build_batch(
+        *tbl, r, page_shift, va_base, _dev(lut, torch.uint64, "lut"), lut.numel(),
+        _dev(off, torch.uint64, "off", n), _dev(length, torch.uint64, "len", n),
+        _dev(qid, torch.uint32, "qid", n), n, nqueues, list_bus_base,
+        _dev(pool, torch.uint64, "pool"), pool.shape[0], BATCH_PACKED if packed else 0, *lk,
+        _dev(out["prp1"], torch.uint64, "prp1", n), _dev(out["prp2"], torch.uint64, "prp2", n),
+        _dev(out["status"], torch.uint8, "status", n),
+        _dev(out["total_pages"], torch.uint64, "total_pages", 1),
+        _dev(out["perm"], torch.uint32, "perm", n),
+        _dev(out["qoff"], torch.uint64, "qoff", nqueues + 2),
+        _dev(out["n_invalid"], torch.uint64, "n_invalid", 1), wptr, ws.numel(),
+        _stream(dev, stream))
+    _check("dmadesc_build_batch", rc)
+    if check:
+        if n:
+            _check_scan("dmadesc_build_batch", ws, dev, stream, out)
+        else:
+            (stream if stream is not None else torch.cuda.current_stream(dev)).synchronize()
+        bad = int(out["n_invalid"].view(torch.int64)[0].item())
+        if bad:
+            raise DmadescRefused(f"dmadesc_build_batch: {bad} request(s) name a queue >= "
+                                 f"nqueues ({nqueues})", out)
     return out
 
 

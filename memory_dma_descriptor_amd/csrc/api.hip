@@ -25,24 +25,48 @@ bool ws_ok(const void *ws, size_t ws_bytes, size_t need)
     return ws && ws_bytes >= need && (reinterpret_cast<uintptr_t>(ws) & 255u) == 0;
 }
 
+// Arguments of a PRP build (both layouts), checked on the host.
+bool prp_args_ok(const uint64_t *lut, uint64_t lut_entries, const uint64_t *off,
+                 const uint64_t *len, uint64_t n, uint64_t list_bus_base, uint64_t *list_pool,
+                 uint64_t pool_pages, uint64_t *prp1, uint64_t *prp2, uint8_t *status,
+                 uint64_t *total_pages, bool packed)
+{
+    if (n >= kMaxN || lut_entries >= kMaxLutEntries) return false;
+    if (list_bus_base & 4095u) return false;
+    if (!total_pages) return false;
+    if (lut_entries > 0 && !lut) return false;
+    if (pool_pages > 0 && !list_pool) return false;
+    if (reinterpret_cast<uintptr_t>(list_pool) & 15u) return false;   // 16-byte stores
+    if (pool_pages > (~0ull >> 12)) return false;        // pool byte size fits 64 bits
+    // The scan carries 62-bit counts: every request has at most 16 lut_entries
+    // + 1 list entries, so n of them must stay below 2^62.
+    if (packed && (unsigned __int128)(lut_entries * 16 + 2) * n >= ((unsigned __int128)1 << 62))
+        return false;
+    if (n > 0 && (!off || !len || !prp1 || !prp2 || !status)) return false;
+    return true;
+}
+
+// The fused batch's workspace: the PRP slot scan, the split's counts and
+// totals, and the lookup's bucket index, each 256-byte aligned.
+size_t batch_ws(uint64_t n, uint32_t nqueues, uint32_t nregions, size_t *split_at,
+                size_t *index_at)
+{
+    const size_t a = dd::align256(dd::ws_build_prp(n));
+    const size_t b = dd::align256(dd::ws_partition(n, nqueues));
+    if (split_at) *split_at = a;
+    if (index_at) *index_at = a + b;
+    return a + b + dd::ws_batch_index(nregions);
+}
+
 int build_prp_common(const uint64_t *lut, uint64_t lut_entries, const uint64_t *off,
                      const uint64_t *len, uint64_t n, uint64_t list_bus_base,
                      uint64_t *list_pool, uint64_t pool_pages, uint64_t *prp1, uint64_t *prp2,
                      uint8_t *status, uint64_t *total_pages, void *ws, size_t ws_bytes,
                      void *stream, bool packed)
 {
-    if (n >= kMaxN || lut_entries >= kMaxLutEntries) return -EINVAL;
-    if (list_bus_base & 4095u) return -EINVAL;
-    if (!total_pages) return -EINVAL;
-    if (lut_entries > 0 && !lut) return -EINVAL;
-    if (pool_pages > 0 && !list_pool) return -EINVAL;
-    if (reinterpret_cast<uintptr_t>(list_pool) & 15u) return -EINVAL;    // 16-byte stores
-    if (pool_pages > (~0ull >> 12)) return -EINVAL;          // pool byte size fits 64 bits
-    // The scan carries 62-bit counts: every request has at most 16 lut_entries
-    // + 1 list entries, so n of them must stay below 2^62.
-    if (packed && (unsigned __int128)(lut_entries * 16 + 2) * n >= ((unsigned __int128)1 << 62))
+    if (!prp_args_ok(lut, lut_entries, off, len, n, list_bus_base, list_pool, pool_pages, prp1,
+                     prp2, status, total_pages, packed))
         return -EINVAL;
-    if (n > 0 && (!off || !len || !prp1 || !prp2 || !status)) return -EINVAL;
     const size_t need = dd::ws_build_prp(n);
     if (need > 0 && !ws_ok(ws, ws_bytes, need)) return -EINVAL;
     dd::PrpArgs a{lut, lut_entries, off, len, n, list_bus_base, list_pool, pool_pages,
@@ -150,6 +174,53 @@ int dmadesc_build_prp_packed(const uint64_t *lut, uint64_t lut_entries,
 {
     return build_prp_common(lut, lut_entries, off, len, n, list_bus_base, list_pool, pool_pages,
                             prp1, prp2, status, total_pages, ws, ws_bytes, stream, true);
+}
+
+size_t dmadesc_batch_workspace_bytes(uint64_t n, uint32_t nqueues, uint32_t nregions)
+{
+    if (nqueues == 0 || nqueues > DMADESC_MAX_QUEUES || n >= kMaxN || nregions >= (1u << 31))
+        return 0;
+    return batch_ws(n, nqueues, nregions, nullptr, nullptr);
+}
+
+int dmadesc_build_batch(const uint64_t *reg_start, const uint64_t *reg_end,
+                        const uint32_t *reg_lkey, uint32_t nregions, uint32_t page_shift,
+                        uint64_t va_base, const uint64_t *lut, uint64_t lut_entries,
+                        const uint64_t *off, const uint64_t *len, const uint32_t *qid,
+                        uint64_t n, uint32_t nqueues, uint64_t list_bus_base,
+                        uint64_t *list_pool, uint64_t pool_pages, uint32_t flags,
+                        int32_t *handle, uint32_t *lkey, uint8_t *kind, uint64_t *rbase,
+                        uint64_t *rend, uint64_t *prp1, uint64_t *prp2, uint8_t *status,
+                        uint64_t *total_pages, uint32_t *perm, uint64_t *qoff,
+                        uint64_t *n_invalid, void *ws, size_t ws_bytes, void *stream)
+{
+    if (flags & ~(uint32_t)DMADESC_BATCH_PACKED) return -EINVAL;
+    const bool packed = (flags & DMADESC_BATCH_PACKED) != 0;
+    if (!prp_args_ok(lut, lut_entries, off, len, n, list_bus_base, list_pool, pool_pages, prp1,
+                     prp2, status, total_pages, packed))
+        return -EINVAL;
+    if (nqueues == 0 || nqueues > DMADESC_MAX_QUEUES || !qoff || !n_invalid) return -EINVAL;
+    if (n > 0 && (!qid || !perm)) return -EINVAL;
+    // The lookup columns come all or none (none: the batch has no region table).
+    const int given = !!handle + !!lkey + !!kind + !!rbase + !!rend;
+    if (given != 0 && given != 5) return -EINVAL;
+    const bool lookup = given == 5;
+    if (lookup) {
+        if (page_shift < 12 || page_shift > 30 || nregions >= (1u << 31)) return -EINVAL;
+        if (nregions > 0 && (!reg_start || !reg_end || !reg_lkey)) return -EINVAL;
+    }
+    const uint32_t nreg = lookup ? nregions : 0;
+    size_t split_at = 0, index_at = 0;
+    const size_t need = batch_ws(n, nqueues, nreg, &split_at, &index_at);
+    if (!ws_ok(ws, ws_bytes, need)) return -EINVAL;
+    char *w = static_cast<char *>(ws);
+    dd::LookupArgs lk{reg_start, reg_end, reg_lkey, nreg, page_shift, off, len, n, va_base,
+                      lookup ? handle : nullptr, lkey, kind, rbase, rend};
+    dd::PrpArgs a{lut, lut_entries, off, len, n, list_bus_base, list_pool, pool_pages,
+                  prp1, prp2, status, total_pages, ws, packed};
+    dd::SplitArgs sp{qid, n, nqueues, perm, qoff, n_invalid, w + split_at};
+    return launched(dd::launch_build_batch(lk, a, sp, w + index_at,
+                                           static_cast<hipStream_t>(stream)));
 }
 
 int dmadesc_build_prp_packed_noalloc(const uint64_t *lut, uint64_t lut_entries,

@@ -10,8 +10,10 @@
 //
 // One pass, one kernel (after a small workspace-clearing kernel):
 //
-//  * Request phase, 1024 requests per block, item k of thread t being request
-//    block_base + 256 k + t (so every column load is contiguous per wave):
+//  * Request phase, 1024 requests per block (256 for batches of at most
+//    2^19 requests, so that they still make enough blocks), item k of thread
+//    t being request block_base + 256 k + t (so every column load is
+//    contiguous per wave):
 //    validity, 4 KiB page count, list pages L. List pages are handed out in
 //    request order by a device-wide exclusive scan done in the same pass
 //    with decoupled look-back: each block publishes its aggregate, then
@@ -57,8 +59,13 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
-constexpr int kItems = 4;                     // requests per thread
-constexpr int kTile = kThreads * kItems;      // requests per block
+// Requests per thread: 4 (1,024 per block) for large batches; 1 (256 per
+// block) for batches of at most kSmallBatch requests, whose blocks would
+// otherwise be too few to fill the chip (a 262,144-request batch of long
+// lists makes 256 blocks of 1,024: one block, four waves, per CU).
+constexpr int kItemsLarge = 4;
+constexpr int kItemsSmall = 1;
+constexpr uint64_t kSmallBatch = 1ull << 19;
 // A request's list run is written in whole units of kPadWords words (a
 // multiple of 4 dividing 512, so padding never leaves the request's final
 // list page): whole 64-byte segments. Words past the last entry are
@@ -67,6 +74,182 @@ constexpr uint64_t kPadWords = 8;
 // GPU pages of the table staged in LDS per wave and round (4 KiB).
 constexpr int kTileFrames = 512;
 enum : uint8_t { kOk = 0, kEinval = 1, kErange = 2, kEnospc = 3, kEbusy = 4 };
+
+// ---- the fused batch (dmadesc_build_batch) --------------------------------
+// The region lookup and the queue histogram of the split ride along the PRP
+// build's request phase, so off, len and qid are read once. The region table
+// stays in global memory: a bucket index over the region starts (built by
+// k_batch_prep) holds, per bucket, the first two regions that can contain an
+// address of the bucket, so on evenly spread tables one 48-byte record read
+// answers a lookup; longer runs are searched in the table.
+struct IndexHdr {
+    uint64_t base;                // start of region 0: bucket 0 begins here
+    uint32_t bs;                  // log2 of the bucket width in bytes
+    uint32_t pad;
+};
+// Bucket b of the index: the regions that can hold the last start at or
+// before an address in the bucket are [at, at + cnt) (at = the last region
+// starting before the bucket, or 0); the first two of them are copied in, so
+// a lookup whose run has one or two candidates reads one record.
+struct alignas(16) BucketRec {
+    uint64_t s0, e0;              // region at: start, end
+    uint64_t s1, e1;              // region at + 1 (cnt >= 2)
+    uint32_t k0, k1;              // their keys
+    uint32_t at, cnt;
+};
+static_assert(sizeof(BucketRec) == 48, "three 16-byte loads");
+struct Fuse {
+    const uint64_t *rs, *re;      // region table (nregions entries)
+    const uint32_t *rk;
+    uint32_t nregions, nbuckets;
+    const IndexHdr *ihdr;
+    const BucketRec *idx;
+    uint64_t in_page, va_base;
+    int32_t *handle;              // lookup columns; handle == nullptr: no lookup
+    uint32_t *lkey;
+    uint8_t *kind;
+    uint64_t *rbase, *rend;
+    const uint32_t *qid;          // queue id of each request
+    uint32_t nq;                  // queues; bucket nq takes ids >= nq
+    uint32_t tile_shift;          // log2 of the split's requests per tile
+    uint64_t ntiles;              // split tiles: the row length of counts
+    uint32_t *counts;             // bucket-major per-tile counts, zeroed
+};
+constexpr int kHistCopies = 4;                    // lane l counts into copy l % 4
+constexpr int kHistStride = DMADESC_MAX_QUEUES + 1;
+
+// Looks up kN requests of this thread (items k0 .. k0 + kN - 1, item k being
+// request base + k * kThreads + t) and writes the five lookup columns. Every
+// load of one stage is issued for all kN items before any is used.
+// Looks one request up (item k of this thread: request i) and writes the
+// five lookup columns. Only a range at or past the first region's start can
+// have a containing region, and only such a range reads the index, whose
+// records exist only when the table has regions.
+__device__ __forceinline__ void fused_lookup(const Fuse &F, const IndexHdr &H, uint64_t o,
+                                             uint64_t l, uint64_t i, uint64_t n)
+{
+    typedef uint64_t u64x2v __attribute__((ext_vector_type(2)));
+    uint64_t lo, hi;
+    const bool valid = page_round(F.va_base, o, l, F.in_page, lo, hi);
+    const bool cand = valid && F.nregions > 0 && lo >= H.base;
+    u64x2v a = u64x2v{0, 0}, c = u64x2v{0, 0};
+    uint4 m = make_uint4(0, 0, 0, 0);
+    if (cand) {
+        uint64_t bkt = (lo - H.base) >> H.bs;
+        bkt = bkt < F.nbuckets ? bkt : F.nbuckets - 1;
+        const u64x2v *rec = reinterpret_cast<const u64x2v *>(F.idx + bkt);
+        a = rec[0];
+        c = rec[1];
+        m = reinterpret_cast<const uint4 *>(rec)[2];
+    }
+    // One or two candidates: the record decides. More: search the table's
+    // starts over [at, at + cnt), then read the region (rare on spread
+    // tables; at + cnt <= nregions).
+    uint32_t r = 0, key = 0;
+    uint64_t s0 = 0, e0 = 0;
+    if (cand && m.w <= 2) {
+        const bool second = m.w == 2 && c.x <= lo;
+        r = m.z + (second ? 1u : 0u);
+        s0 = second ? c.x : a.x;
+        e0 = second ? c.y : a.y;
+        key = second ? m.y : m.x;
+    } else if (cand) {
+        uint32_t at = m.z, cnt = m.w;
+        while (cnt > 1) {
+            const uint32_t half = cnt >> 1;
+            at = (F.rs[at + half] <= lo) ? at + half : at;
+            cnt -= half;
+        }
+        r = at;
+        s0 = F.rs[r];
+        e0 = F.re[r];
+        key = F.rk[r];
+    }
+    const bool hit = cand && hi <= e0;
+    const uint8_t kd = !valid ? 3 : !hit ? 0 : (lo == s0 && hi == e0) ? 1 : 2;
+    if (i < n) {
+        // Streamed: nothing reads the lookup columns again here.
+        __builtin_nontemporal_store(hit ? (int32_t)r : -1, F.handle + i);
+        __builtin_nontemporal_store(hit ? key : 0u, F.lkey + i);
+        __builtin_nontemporal_store(kd, F.kind + i);
+        __builtin_nontemporal_store(lo, F.rbase + i);
+        __builtin_nontemporal_store(hi, F.rend + i);
+    }
+}
+
+// The lookups of this thread's kItems requests, one after another (one
+// record and its answer live at a time).
+template <int kItems>
+__device__ __forceinline__ void fused_lookups(const Fuse &F, const uint64_t (&o)[kItems],
+                                              const uint64_t (&l)[kItems], uint64_t base, int t,
+                                              uint64_t n)
+{
+    const IndexHdr H = *F.ihdr;
+#pragma unroll
+    for (int k = 0; k < kItems; ++k)
+        fused_lookup(F, H, o[k], l[k], base + (uint64_t)k * kThreads + t, n);
+}
+
+// First region whose start is at or past bucket b (b may be nbuckets).
+__device__ __forceinline__ uint32_t first_at_or_past(const uint64_t *__restrict__ rs,
+                                                     uint32_t nregions, uint64_t base,
+                                                     uint32_t bs, uint64_t b)
+{
+    const bool over = bs && (b >> (64 - bs)) != 0;
+    const uint64_t width = over ? ~0ull : b << bs;
+    const uint64_t x = width > ~base ? ~0ull : base + width;   // saturating
+    uint32_t lo = 0, cnt = nregions;
+    while (cnt > 0) {
+        const uint32_t half = cnt >> 1;
+        if (rs[lo + half] < x) {
+            lo += half + 1;
+            cnt -= half + 1;
+        } else {
+            cnt = half;
+        }
+    }
+    return lo;
+}
+
+// Before the fused kernel: clears the slot scan's header and status words
+// and the split's per-tile counts, and builds the bucket index over the
+// region starts (span from region 0's start to the last start, nbuckets
+// buckets of 2^bs bytes; the last bucket also takes everything past it).
+__global__ __launch_bounds__(256) void k_batch_prep(
+    uint64_t *__restrict__ scan_words, uint64_t nscan, uint32_t *__restrict__ counts,
+    uint64_t ncounts, const uint64_t *__restrict__ rs, uint32_t nregions, uint32_t nbuckets,
+    const uint64_t *__restrict__ re, const uint32_t *__restrict__ rk,
+    IndexHdr *__restrict__ ihdr, BucketRec *__restrict__ idx)
+{
+    const uint64_t g = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
+    for (uint64_t k = g; k < nscan; k += stride) scan_words[k] = 0;
+    for (uint64_t k = g; k < ncounts; k += stride) counts[k] = 0;
+    if (nregions == 0) return;
+    const uint64_t base = rs[0], span = rs[nregions - 1] - base;
+    uint32_t bs = 0;
+    while (bs < 63 && (span >> bs) >= nbuckets) ++bs;
+    if (g == 0) *ihdr = IndexHdr{base, bs, 0};
+    for (uint64_t b = g; b < nbuckets; b += stride) {
+        const uint32_t x = first_at_or_past(rs, nregions, base, bs, b);
+        const uint32_t y = b + 1 == nbuckets ? nregions
+                                             : first_at_or_past(rs, nregions, base, bs, b + 1);
+        // The last region starting at or before an address of this bucket
+        // lies in [x - 1, y) (region x - 1 starts before the bucket).
+        const uint32_t at = x ? x - 1 : 0;
+        const uint32_t nx = at + 1 < nregions ? at + 1 : at;
+        BucketRec R;
+        R.s0 = rs[at];
+        R.e0 = re[at];
+        R.k0 = rk[at];
+        R.s1 = rs[nx];
+        R.e1 = re[nx];
+        R.k1 = rk[nx];
+        R.at = at;
+        R.cnt = y - at;
+        idx[b] = R;
+    }
+}
 
 // Status and 4 KiB page count of one request.
 __device__ __forceinline__ uint8_t decode(uint64_t o, uint64_t l, uint64_t heap,
@@ -130,7 +313,9 @@ __device__ __forceinline__ void emit_round_wide(RoundTable &T, uint64_t xb, uint
     const uint64_t groups = ((ent + kPadWords - 1) / kPadWords) * (kPadWords / 4);
     const uint64_t ginc = wave_incl_scan(groups);
     const uint64_t gtot = __shfl(ginc, kWave - 1, kWave);
-    if (gtot == 0) return;                                   // uniform per wave
+    if (gtot == 0) {                                         // uniform per wave
+        return;
+    }
     const uint64_t frames = ent ? last_frame - (xb >> 16) + 1 : 0;
     const uint64_t finc = wave_incl_scan(frames);
     const uint64_t ftot = __shfl(finc, kWave - 1, kWave);
@@ -269,7 +454,9 @@ __device__ __forceinline__ void emit_round_fast(FastTable &T, uint64_t xb, uint6
                             (uint32_t)(kPadWords / 2);
     const uint32_t ginc = wave_incl_scan(groups);
     const uint32_t gtot = __shfl(ginc, kWave - 1, kWave);
-    if (gtot == 0) return;                                   // uniform per wave
+    if (gtot == 0) {                                         // uniform per wave
+        return;
+    }
     const uint64_t f0 = xb >> 16;
     const uint32_t frames = ent ? (uint32_t)(last_frame - f0 + 1) : 0;
     const uint32_t finc = wave_incl_scan(frames);
@@ -644,7 +831,9 @@ __device__ __forceinline__ void emit_round_packed(PackLds &L, uint64_t d, uint64
                                                   uint64_t *__restrict__ pool, uint64_t bus)
 {
     const uint64_t has = __ballot(m != 0);
-    if (has == 0) return;                                    // uniform per wave
+    if (has == 0) {                                          // uniform per wave
+        return;
+    }
     const int first = __ffsll((unsigned long long)has) - 1;
     const int last = 63 - __clzll((unsigned long long)has);
     const uint64_t S = __shfl(d, first, kWave);
@@ -657,34 +846,58 @@ __device__ __forceinline__ void emit_round_packed(PackLds &L, uint64_t d, uint64
                                 lut, pool, bus);
 }
 
-template <bool kPacked>
+template <bool kPacked, bool kFused, int kItems>
 __global__ __launch_bounds__(kThreads, 4) void k_prp_build(
     const uint64_t *__restrict__ lut, uint64_t heap,
     const uint64_t *__restrict__ off, const uint64_t *__restrict__ len, uint64_t n,
     uint64_t nblocks, uint64_t bus, uint64_t *__restrict__ pool, uint64_t pool_pages,
     uint64_t *__restrict__ prp1, uint64_t *__restrict__ prp2,
     uint8_t *__restrict__ status, uint64_t *__restrict__ total,
-    Header *__restrict__ hdr, uint64_t *__restrict__ bstat, uint32_t max_polls)
+    Header *__restrict__ hdr, uint64_t *__restrict__ bstat, uint32_t max_polls, Fuse F)
 {
+    using RoundT = typename std::conditional<kPacked, PackLds, RoundLds>::type;
     __shared__ uint64_t s_red[kItems * kWaves];
     __shared__ uint64_t s_bid, s_excl;
     __shared__ uint32_t s_dead;
     __shared__ uint64_t s_v2[kItems * kThreads];   // table entry of PRP2's page (two pages)
-    __shared__ typename std::conditional<kPacked, PackLds, RoundLds>::type s_round[kWaves];
+    __shared__ RoundT s_round[kWaves];
+    // The fused split's block histogram lives in the round tables' memory,
+    // which the list rounds only use after the request phase.
+    static_assert(sizeof(RoundT) * kWaves >= kHistCopies * kHistStride * sizeof(uint32_t),
+                  "the histogram fits in the round tables");
+    uint32_t *hist = reinterpret_cast<uint32_t *>(&s_round[0]);
 
     const int t = threadIdx.x, w = wave(), ln = lane();
+    if constexpr (kFused) {
+        for (int k = t; k < kHistCopies * kHistStride; k += kThreads) hist[k] = 0;
+    }
     if (t == 0) s_bid = atomicAdd(&hdr->ticket, 1u);
     __syncthreads();
     const uint64_t b = s_bid;
+    constexpr int kTile = kThreads * kItems;       // requests per block
     const uint64_t base = b * kTile;
 
     // ---- request phase: item k of thread t is request base + k*256 + t ----
     uint64_t o[kItems], l[kItems], pre[kItems];
+    uint32_t q[kItems];
 #pragma unroll
     for (int k = 0; k < kItems; ++k) {
         const uint64_t i = base + (uint64_t)k * kThreads + t;
         o[k] = i < n ? __builtin_nontemporal_load(off + i) : 0;
         l[k] = i < n ? __builtin_nontemporal_load(len + i) : 0;   // len 0 decodes as invalid
+        // Clamped, not guarded: a guarded load is a branch whose result the
+        // compiler waits for before the next item's loads are issued.
+        if constexpr (kFused) q[k] = __builtin_nontemporal_load(F.qid + (i < n ? i : n - 1));
+    }
+    if constexpr (kFused) {
+        // Queue histogram of the block (LDS atomics; counts only, so their
+        // order does not matter).
+        uint32_t *hc = hist + (ln % kHistCopies) * kHistStride;
+#pragma unroll
+        for (int k = 0; k < kItems; ++k) {
+            const uint64_t i = base + (uint64_t)k * kThreads + t;
+            if (i < n) atomicAdd(&hc[q[k] < F.nq ? q[k] : F.nq], 1u);
+        }
     }
     // Scanned per request: list pages (page layout) or list entries (packed).
     // Request order is (item, wave, lane): wave scans per item, then one
@@ -743,7 +956,21 @@ __global__ __launch_bounds__(kThreads, 4) void k_prp_build(
             s_v2[k * kThreads + t] = heap ? lut[i2] : 0;
         }
     };
-    if (w != 0) gather();
+    if (w != 0) {
+        gather();
+        if constexpr (kFused) {
+            // Waves 1..3 add the block histogram to its split tile's counts
+            // while wave 0 looks back, then look their requests up.
+            const uint64_t tile = base >> F.tile_shift;
+            for (uint32_t bk = t - kWave; bk <= F.nq; bk += kThreads - kWave) {
+                uint32_t c = 0;
+#pragma unroll
+                for (int j = 0; j < kHistCopies; ++j) c += hist[j * kHistStride + bk];
+                if (c) atomicAdd(F.counts + (uint64_t)bk * F.ntiles + tile, c);
+            }
+            if (F.handle) fused_lookups(F, o, l, base, t, n);
+        }
+    }
     if (w == 0) {
         uint64_t excl = 0;
         bool dead = false;
@@ -760,6 +987,9 @@ __global__ __launch_bounds__(kThreads, 4) void k_prp_build(
                 *total = dead ? ~0ull : (kPacked ? (excl + agg + 510) / 511 : excl + agg);
         }
         gather();
+        if constexpr (kFused) {
+            if (F.handle) fused_lookups(F, o, l, base, t, n);
+        }
     }
     __syncthreads();
     const uint64_t excl = s_excl;
@@ -800,17 +1030,113 @@ __global__ __launch_bounds__(kThreads, 4) void k_prp_build(
 
 }  // namespace
 
+// Buckets of the fused lookup's index: two per region (rounded up to a
+// power of two), at least 4,096 and at most 2^21 (96 MiB of records).
+// Requests per block of the PRP build for a batch of n (the launch and the
+// workspace size agree on it).
+uint64_t prp_tile(uint64_t n)
+{
+    return (uint64_t)kThreads * (n <= kSmallBatch ? kItemsSmall : kItemsLarge);
+}
+
+// Launches the k_prp_build instantiation for the layout and the batch size.
+template <bool kFused>
+void launch_prp_kernel(const PrpArgs &a, uint64_t nb, Header *hdr, uint64_t *bstat,
+                       const Fuse &F, hipStream_t s)
+{
+    const uint64_t heap = a.lut_entries << 16;
+    const bool small = a.n <= kSmallBatch;
+#define DD_PRP_LAUNCH(P, I)                                                                   \
+    hipLaunchKernelGGL((k_prp_build<P, kFused, I>), dim3((unsigned)nb), dim3(kThreads), 0, s,  \
+                       a.lut, heap, a.off, a.len, a.n, nb, a.list_bus_base, a.pool,            \
+                       a.pool_pages, a.prp1, a.prp2, a.status, a.total_pages, hdr, bstat,     \
+                       wait_limit(), F)
+    if (a.packed) {
+        if (small) DD_PRP_LAUNCH(true, kItemsSmall);
+        else DD_PRP_LAUNCH(true, kItemsLarge);
+    } else {
+        if (small) DD_PRP_LAUNCH(false, kItemsSmall);
+        else DD_PRP_LAUNCH(false, kItemsLarge);
+    }
+#undef DD_PRP_LAUNCH
+}
+
+uint32_t index_buckets(uint32_t nregions)
+{
+    uint64_t b = 4096;
+    while (b < 2ull * nregions && b < (1ull << 21)) b <<= 1;
+    return (uint32_t)b;
+}
+
+size_t ws_batch_index(uint32_t nregions)
+{
+    return align256(sizeof(IndexHdr)) +
+           align256((uint64_t)index_buckets(nregions) * sizeof(BucketRec));
+}
+
+hipError_t launch_build_batch(const LookupArgs &lk, const PrpArgs &a, const SplitArgs &sp,
+                              void *index_ws, hipStream_t s)
+{
+    const uint64_t nb = (a.n + prp_tile(a.n) - 1) / prp_tile(a.n);
+    if (nb == 0) {
+        hipLaunchKernelGGL(k_ws_clear, dim3(1), dim3(64), 0, s, a.total_pages, (uint64_t)1);
+        return launch_partition(sp, s);                   // an empty split
+    }
+    Header *hdr = static_cast<Header *>(a.ws);
+    uint64_t *bstat = reinterpret_cast<uint64_t *>(static_cast<char *>(a.ws) + kHeaderBytes);
+    const uint64_t words = kHeaderBytes / sizeof(uint64_t) + nb;
+    const uint32_t shift = split_tile_shift(sp.nqueues);
+    const uint64_t ntiles = (a.n + (1ull << shift) - 1) >> shift;
+    uint32_t *counts = static_cast<uint32_t *>(sp.ws);
+    const uint64_t ncounts = (uint64_t)(sp.nqueues + 1) * ntiles;
+    const uint32_t nbuckets = index_buckets(lk.nregions);
+    IndexHdr *ihdr = static_cast<IndexHdr *>(index_ws);
+    BucketRec *idx = reinterpret_cast<BucketRec *>(static_cast<char *>(index_ws) +
+                                                   align256(sizeof(IndexHdr)));
+    const bool lookup = lk.handle != nullptr;
+    uint64_t pb = (words > ncounts ? words : ncounts);
+    if (lookup && nbuckets > pb) pb = nbuckets;
+    pb = (pb + 255) / 256;
+    if (pb > 1024) pb = 1024;
+    hipLaunchKernelGGL(k_batch_prep, dim3((unsigned)pb), dim3(256), 0, s,
+                       static_cast<uint64_t *>(a.ws), words, counts, ncounts, lk.reg_start,
+                       lookup ? lk.nregions : 0u, nbuckets, lk.reg_end, lk.reg_lkey, ihdr, idx);
+    Fuse F{};
+    F.rs = lk.reg_start;
+    F.re = lk.reg_end;
+    F.rk = lk.reg_lkey;
+    F.nregions = lk.nregions;
+    F.nbuckets = nbuckets;
+    F.ihdr = ihdr;
+    F.idx = idx;
+    F.in_page = (1ull << lk.page_shift) - 1;
+    F.va_base = lk.va_base;
+    F.handle = lk.handle;
+    F.lkey = lk.lkey;
+    F.kind = lk.kind;
+    F.rbase = lk.rbase;
+    F.rend = lk.rend;
+    F.qid = sp.qid;
+    F.nq = sp.nqueues;
+    F.tile_shift = shift;
+    F.ntiles = ntiles;
+    F.counts = counts;
+    launch_prp_kernel<true>(a, nb, hdr, bstat, F, s);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return launch_partition_counted(sp, s);
+}
+
 size_t ws_build_prp(uint64_t n)
 {
     if (n == 0) return 0;
-    const uint64_t nb = (n + kTile - 1) / kTile;
+    const uint64_t nb = (n + prp_tile(n) - 1) / prp_tile(n);
     return align256(kHeaderBytes + nb * sizeof(uint64_t));
 }
 
 hipError_t launch_build_prp(const PrpArgs &a, hipStream_t s)
 {
-    const uint64_t heap = a.lut_entries << 16;
-    const uint64_t nb = (a.n + kTile - 1) / kTile;
+    const uint64_t nb = (a.n + prp_tile(a.n) - 1) / prp_tile(a.n);
     if (nb == 0) {
         // Nothing to build; the batch needs no list pages.
         hipLaunchKernelGGL(k_ws_clear, dim3(1), dim3(64), 0, s, a.total_pages, (uint64_t)1);
@@ -823,16 +1149,7 @@ hipError_t launch_build_prp(const PrpArgs &a, hipStream_t s)
     if (cblocks > 1024) cblocks = 1024;
     hipLaunchKernelGGL(k_ws_clear, dim3((unsigned)cblocks), dim3(256), 0, s,
                        static_cast<uint64_t *>(a.ws), words);
-    if (a.packed)
-        hipLaunchKernelGGL(k_prp_build<true>, dim3((unsigned)nb), dim3(kThreads), 0, s,
-                           a.lut, heap, a.off, a.len, a.n, nb, a.list_bus_base, a.pool,
-                           a.pool_pages, a.prp1, a.prp2, a.status, a.total_pages, hdr, bstat,
-                           wait_limit());
-    else
-        hipLaunchKernelGGL(k_prp_build<false>, dim3((unsigned)nb), dim3(kThreads), 0, s,
-                           a.lut, heap, a.off, a.len, a.n, nb, a.list_bus_base, a.pool,
-                           a.pool_pages, a.prp1, a.prp2, a.status, a.total_pages, hdr, bstat,
-                           wait_limit());
+    launch_prp_kernel<false>(a, nb, hdr, bstat, Fuse{}, s);
     return hipGetLastError();
 }
 

@@ -12,6 +12,22 @@ constexpr int kWave = 64;
 __device__ __forceinline__ int lane() { return (int)__lane_id(); }
 __device__ __forceinline__ int wave() { return (int)(threadIdx.x / kWave); }
 
+// Page rounding of one request range (NCCL course page, "IB Backend MR
+// Cache": floor of the start to the page, cover of the end): the absolute
+// start a = va_base + o widened to [lo, hi) of whole pages (in_page = page
+// size - 1). Returns false, with lo = hi = 0, for an empty range or one
+// whose start, end or rounded end wraps 2^64.
+__device__ __forceinline__ bool page_round(uint64_t va_base, uint64_t o, uint64_t l,
+                                           uint64_t in_page, uint64_t &lo, uint64_t &hi)
+{
+    const uint64_t a = va_base + o;
+    const uint64_t last = a + l - 1;
+    const bool bad = (l == 0) | (a < va_base) | (l > ~a) | ((last | in_page) == ~0ull);
+    lo = bad ? 0 : (a & ~in_page);             // page floor of the start
+    hi = bad ? 0 : (last | in_page) + 1;       // page cover of the end
+    return !bad;
+}
+
 // Inclusive prefix sum across the 64 lanes of a wave.
 template <typename T>
 __device__ __forceinline__ T wave_incl_scan(T v)

@@ -100,6 +100,17 @@ hipError_t launch_table_check(const uint64_t *rs, const uint64_t *re, uint32_t n
                               hipStream_t s);
 hipError_t launch_build_prp(const PrpArgs &a, hipStream_t s);
 hipError_t launch_partition(const SplitArgs &a, hipStream_t s);
+// The split's column scan and scatter, with the per-tile counts (bucket
+// major, a row of ceil(n / 2^split_tile_shift) tiles per bucket) already in
+// the first part of a.ws.
+hipError_t launch_partition_counted(const SplitArgs &a, hipStream_t s);
+uint32_t split_tile_shift(uint32_t nq);
+// The fused batch: lookup (lk.handle == nullptr: none), PRP build (a.packed
+// selects the layout) and split; a.ws, sp.ws and index_ws are the three
+// parts of the call's workspace.
+hipError_t launch_build_batch(const LookupArgs &lk, const PrpArgs &a, const SplitArgs &sp,
+                              void *index_ws, hipStream_t s);
+size_t ws_batch_index(uint32_t nregions);
 hipError_t launch_emit_sqe(const SqeArgs &a, hipStream_t s);
 hipError_t launch_cq_mirror(dmadesc_cq_slot *slots, uint32_t nslots, const uint32_t *stop,
                             uint32_t idle_polls, hipStream_t s);

@@ -17,12 +17,12 @@
 //    two on evenly spread tables) instead of the whole table: a wave's random
 //    LDS reads then collide in far fewer banks. All table reads are LDS
 //    reads, so no random global gathers reach the texture address unit.
-//  * k_lookup_split, for larger tables: every block stages every S-th
-//    region start (S a power of two, at most kMaxSplitters splitters = 64 KiB)
-//    in LDS; a lane searches the splitters in LDS, then the <= S starts of the
-//    selected run in global memory (the table is L2-resident).
+//  * k_lookup_big, for larger tables: every block stages every 8th region
+//    start in LDS (at most kMaxSplitters splitters = 64 KiB, with a bucket
+//    index over them); a lane finds its splitter in LDS, then reads the 8
+//    starts of that run in one 64-byte read (the table is L2-resident).
 //
-// Both searches are branch-free: the trip count depends only on the length
+// The searches are branch-free: the trip count depends only on the length
 // searched, so lanes of a wave never diverge in them.
 #include "dd_device.hpp"
 #include "dd_internal.h"
@@ -52,19 +52,6 @@ __device__ __forceinline__ uint64_t last_le(Ptr a, uint64_t cnt, uint64_t key)
         cnt -= half;
     }
     return idx;
-}
-
-// Validity and page-rounded bounds of one request; returns false for
-// INVALID (empty, start wraps, end wraps, or rounded end wraps).
-__device__ __forceinline__ bool round_range(uint64_t va_base, uint64_t o, uint64_t l,
-                                            uint64_t in_page, uint64_t &lo, uint64_t &hi)
-{
-    const uint64_t a = va_base + o;
-    const uint64_t last = a + l - 1;
-    const bool bad = (l == 0) | (a < va_base) | (l > ~a) | ((last | in_page) == ~0ull);
-    lo = bad ? 0 : (a & ~in_page);             // page floor of the start
-    hi = bad ? 0 : (last | in_page) + 1;       // page cover of the end
-    return !bad;
 }
 
 __device__ __forceinline__ void put(uint64_t i, int32_t h, uint32_t key, uint8_t kd,
@@ -173,7 +160,7 @@ __global__ __launch_bounds__(kThreadsLds) void k_lookup_lds(
         uint64_t lo[kPerLane], hi[kPerLane];
 #pragma unroll
         for (int k = 0; k < kPerLane; ++k) {
-            const bool ok = round_range(va_base, o[k], l[k], in_page, lo[k], hi[k]);
+            const bool ok = page_round(va_base, o[k], l[k], in_page, lo[k], hi[k]);
             h[k] = -1;
             key[k] = 0;
             kd[k] = ok ? 0 : 3;                  // MISS : INVALID
@@ -231,44 +218,188 @@ __global__ __launch_bounds__(kThreadsLds) void k_lookup_lds(
     }
 }
 
-__global__ __launch_bounds__(kThreads) void k_lookup_split(
+// Larger tables (k_lookup_big): the region starts do not fit LDS, so LDS
+// holds every 8th start ("splitters", up to kMaxSplitters = 64 KiB) and a
+// bucket index over them; a request finds its splitter c in LDS, then reads
+// the 8 starts of run c as one 64-byte read (four 16-byte loads), counts
+// those at or below its rounded base, and reads the end and key of that
+// region. Three dependent global rounds per request (columns, run, region),
+// four requests per lane in flight, columns read and written as in
+// k_lookup_lds. Tables with more than 8 * kMaxSplitters regions put every
+// 2^s-th start in LDS and narrow the run by a global binary search first.
+constexpr uint32_t kRun = 8;                 // starts read per request in one go
+
+__device__ __forceinline__ uint32_t count_le(const uint64_t (&t)[kRun], uint64_t key)
+{
+    uint32_t c = 0;
+#pragma unroll
+    for (int j = 0; j < (int)kRun; ++j) c += t[j] <= key ? 1u : 0u;
+    return c;
+}
+
+__global__ __launch_bounds__(kThreadsLds) void k_lookup_big(
     const uint64_t *__restrict__ rs, const uint64_t *__restrict__ re,
-    const uint32_t *__restrict__ rk, uint32_t nregions,
-    uint32_t split_shift, uint32_t nsplit, uint32_t page_shift,
+    const uint32_t *__restrict__ rk, uint32_t nregions, uint32_t split_shift,
+    uint32_t nsplit, uint32_t page_shift,
     const uint64_t *__restrict__ off, const uint64_t *__restrict__ len,
     uint64_t n, uint64_t va_base,
     int32_t *__restrict__ handle, uint32_t *__restrict__ lkey,
     uint8_t *__restrict__ kind, uint64_t *__restrict__ rbase,
-    uint64_t *__restrict__ rend)
+    uint64_t *__restrict__ rend, bool aligned)
 {
-    extern __shared__ uint64_t spl[];
-    for (uint32_t k = threadIdx.x; k < nsplit; k += kThreads)
+    extern __shared__ uint64_t lds[];
+    uint64_t *spl = lds;                                          // nsplit starts
+    uint16_t *s_idx = reinterpret_cast<uint16_t *>(lds + nsplit); // kBuckets + 1
+    for (uint32_t k = threadIdx.x; k < nsplit; k += kThreadsLds)
         spl[k] = rs[(uint64_t)k << split_shift];
+    __syncthreads();
+    // Bucket index over the splitters, as k_lookup_lds builds over starts:
+    // s_idx[b] = first splitter at or past bucket b of the splitters' span.
+    const uint64_t base = spl[0];
+    uint32_t bs = 0;
+    {
+        const uint64_t span = spl[nsplit - 1] - base;
+        while ((span >> bs) >= kBuckets) ++bs;
+        for (uint32_t b = threadIdx.x; b <= kBuckets; b += kThreadsLds) {
+            const bool over = bs && ((uint64_t)b >> (64 - bs)) != 0;
+            const uint64_t width = over ? ~0ull : (uint64_t)b << bs;
+            const uint64_t x = width > ~base ? ~0ull : base + width;
+            uint32_t lo = 0, cnt = nsplit;
+            while (cnt > 0) {
+                const uint32_t half = cnt >> 1;
+                if (spl[lo + half] < x) {
+                    lo += half + 1;
+                    cnt -= half + 1;
+                } else {
+                    cnt = half;
+                }
+            }
+            s_idx[b] = (uint16_t)lo;
+        }
+    }
     __syncthreads();
 
     const uint64_t in_page = (1ull << page_shift) - 1;
-    const uint64_t run = 1ull << split_shift;
-    const uint64_t stride = (uint64_t)gridDim.x * kThreads;
-    for (uint64_t i = (uint64_t)blockIdx.x * kThreads + threadIdx.x; i < n; i += stride) {
-        uint64_t lo, hi;
-        const bool ok = round_range(va_base, off[i], len[i], in_page, lo, hi);
-        int32_t h = -1;
-        uint32_t key = 0;
-        uint8_t kd = ok ? 0 : 3;                 // MISS : INVALID
-        if (ok && nsplit > 0 && spl[0] <= lo) {
-            const uint64_t c = last_le(spl, nsplit, lo);         // splitter run
-            const uint64_t b0 = c << split_shift;
-            const uint64_t left = (uint64_t)nregions - b0;
-            const uint64_t cnt = left < run ? left : run;
-            const uint64_t r = b0 + last_le(rs + b0, cnt, lo);   // last start <= lo
-            const uint64_t e = re[r];
-            if (hi <= e) {
-                h = (int32_t)r;
-                key = rk[r];
-                kd = (lo == rs[r] && hi == e) ? 1 : 2;   // EXACT : CONTAINED
+    const uint64_t span = (uint64_t)kThreadsLds * kPerLane;
+    const uint64_t runlen = 1ull << split_shift;                  // starts per splitter
+    const int ln = (int)(threadIdx.x & 63), wv = (int)(threadIdx.x >> 6);
+    for (uint64_t c0 = (uint64_t)blockIdx.x * span; c0 < n; c0 += (uint64_t)gridDim.x * span) {
+        const uint64_t wb = c0 + (uint64_t)wv * (64 * kPerLane);
+        if (wb >= n) break;
+        const bool whole = aligned && wb + 64 * kPerLane <= n;   // uniform per wave
+        uint64_t o[kPerLane], l[kPerLane];
+        if (whole) {
+#pragma unroll
+            for (int p = 0; p < kPerLane / 2; ++p) {
+                const u64x2 oa = __builtin_nontemporal_load(reinterpret_cast<const u64x2 *>(off + wb + p * 128 + 2 * ln));
+                o[2 * p] = oa.x; o[2 * p + 1] = oa.y;
+            }
+#pragma unroll
+            for (int p = 0; p < kPerLane / 2; ++p) {
+                const u64x2 la = __builtin_nontemporal_load(reinterpret_cast<const u64x2 *>(len + wb + p * 128 + 2 * ln));
+                l[2 * p] = la.x; l[2 * p + 1] = la.y;
+            }
+        } else {
+#pragma unroll
+            for (int k = 0; k < kPerLane; ++k) {
+                const uint64_t i = wb + (k >> 1) * 128 + 2 * ln + (k & 1);
+                o[k] = i < n ? off[i] : 0;
+                l[k] = i < n ? len[i] : 0;
             }
         }
-        put(i, h, key, kd, lo, hi, handle, lkey, kind, rbase, rend);
+        uint64_t lo[kPerLane], hi[kPerLane], at[kPerLane];
+        bool valid[kPerLane], cand[kPerLane];
+#pragma unroll
+        for (int k = 0; k < kPerLane; ++k) {
+            valid[k] = page_round(va_base, o[k], l[k], in_page, lo[k], hi[k]);
+            cand[k] = valid[k] && lo[k] >= base;
+            // Splitter c: the last splitter at or before lo (LDS).
+            uint32_t c = 0;
+            if (cand[k]) {
+                uint64_t b = (lo[k] - base) >> bs;
+                b = b < kBuckets ? b : kBuckets - 1;
+                const uint32_t i0 = s_idx[b], i1 = s_idx[b + 1];
+                const uint32_t first = i0 ? i0 - 1 : 0;
+                c = first + (uint32_t)last_le(spl + first, i1 - first, lo[k]);
+            }
+            at[k] = (uint64_t)c << split_shift;
+            // Runs of more than kRun starts: narrow to kRun by a search over
+            // every kRun-th start of the run in global memory.
+            uint64_t cnt = (uint64_t)nregions - at[k];
+            cnt = cnt < runlen ? cnt : runlen;
+            if (cand[k] && runlen > kRun) {
+                uint64_t step_at = 0, m = (cnt + kRun - 1) / kRun;
+                while (m > 1) {
+                    const uint64_t half = m >> 1;
+                    step_at = rs[at[k] + (step_at + half) * kRun] <= lo[k] ? step_at + half : step_at;
+                    m -= half;
+                }
+                at[k] += step_at * kRun;
+            }
+        }
+        // The kRun starts from `at` (past the table: never at or below lo).
+        uint32_t r[kPerLane];
+        uint64_t s0[kPerLane];
+#pragma unroll
+        for (int k = 0; k < kPerLane; ++k) {
+            uint64_t t[kRun];
+            if (cand[k] && at[k] + kRun <= nregions && aligned) {
+                const u64x2 *q = reinterpret_cast<const u64x2 *>(rs + at[k]);
+#pragma unroll
+                for (int j = 0; j < (int)kRun / 2; ++j) {
+                    const u64x2 v = q[j];
+                    t[2 * j] = v.x;
+                    t[2 * j + 1] = v.y;
+                }
+            } else {
+#pragma unroll
+                for (int j = 0; j < (int)kRun; ++j)
+                    t[j] = cand[k] && at[k] + j < nregions ? rs[at[k] + j] : ~0ull;
+            }
+            const uint32_t c = cand[k] ? count_le(t, lo[k]) : 1u;   // >= 1: t[0] <= lo
+            r[k] = (uint32_t)at[k] + c - 1;
+            uint64_t sel = t[0];
+#pragma unroll
+            for (int j = 1; j < (int)kRun; ++j) sel = (uint32_t)j == c - 1 ? t[j] : sel;
+            s0[k] = sel;
+        }
+        int32_t h[kPerLane];
+        uint32_t key[kPerLane];
+        uint8_t kd[kPerLane];
+        uint64_t e0[kPerLane];
+#pragma unroll
+        for (int k = 0; k < kPerLane; ++k) {
+            e0[k] = cand[k] ? re[r[k]] : 0;
+            key[k] = cand[k] ? rk[r[k]] : 0;
+        }
+#pragma unroll
+        for (int k = 0; k < kPerLane; ++k) {
+            const bool hit = cand[k] && hi[k] <= e0[k];
+            h[k] = hit ? (int32_t)r[k] : -1;
+            key[k] = hit ? key[k] : 0;
+            kd[k] = !valid[k] ? 3 : !hit ? 0 : (lo[k] == s0[k] && hi[k] == e0[k]) ? 1 : 2;
+        }
+        if (whole) {
+#pragma unroll
+            for (int p = 0; p < kPerLane / 2; ++p) {
+                const uint64_t i = wb + p * 128 + 2 * ln;
+                __builtin_nontemporal_store(u64x2{lo[2 * p], lo[2 * p + 1]}, reinterpret_cast<u64x2 *>(rbase + i));
+                __builtin_nontemporal_store(u64x2{hi[2 * p], hi[2 * p + 1]}, reinterpret_cast<u64x2 *>(rend + i));
+                __builtin_nontemporal_store(
+                    (uint64_t)(uint32_t)h[2 * p] | ((uint64_t)(uint32_t)h[2 * p + 1] << 32),
+                    reinterpret_cast<uint64_t *>(handle + i));
+                __builtin_nontemporal_store((uint64_t)key[2 * p] | ((uint64_t)key[2 * p + 1] << 32),
+                                            reinterpret_cast<uint64_t *>(lkey + i));
+                __builtin_nontemporal_store((uint16_t)(kd[2 * p] | (kd[2 * p + 1] << 8)),
+                                            reinterpret_cast<uint16_t *>(kind + i));
+            }
+        } else {
+#pragma unroll
+            for (int k = 0; k < kPerLane; ++k) {
+                const uint64_t i = wb + (k >> 1) * 128 + 2 * ln + (k & 1);
+                if (i < n) put(i, h[k], key[k], kd[k], lo[k], hi[k], handle, lkey, kind, rbase, rend);
+            }
+        }
     }
 }
 
@@ -344,16 +475,23 @@ hipError_t launch_mr_lookup(const LookupArgs &a, hipStream_t s)
                            a.rend, aligned);
         return hipGetLastError();
     }
-    uint32_t shift = 0;
+    // Every 2^shift-th start in LDS (at least every kRun-th).
+    uint32_t shift = 3;
     while (((uint64_t)a.nregions + (1ull << shift) - 1) >> shift > kMaxSplitters) ++shift;
     const uint32_t nsplit = (uint32_t)(((uint64_t)a.nregions + (1ull << shift) - 1) >> shift);
-    uint64_t blocks = (a.n + kThreads - 1) / kThreads;
-    if (blocks > 2048) blocks = 2048;
-    hipLaunchKernelGGL(k_lookup_split, dim3((unsigned)blocks), dim3(kThreads),
-                       (size_t)nsplit * sizeof(uint64_t), s,
+    const size_t bytes = (size_t)nsplit * sizeof(uint64_t) + (size_t)(kBuckets + 1) * sizeof(uint16_t);
+    e = hipFuncSetAttribute(reinterpret_cast<const void *>(k_lookup_big),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+    if (e != hipSuccess) return e;
+    uint64_t blocks = (a.n + (uint64_t)kThreadsLds * kPerLane - 1) / ((uint64_t)kThreadsLds * kPerLane);
+    if (blocks > (uint64_t)cus) blocks = (uint64_t)cus;
+    auto al = [](const void *p, uintptr_t m) { return (reinterpret_cast<uintptr_t>(p) & m) == 0; };
+    const bool aligned = al(a.off, 15) && al(a.len, 15) && al(a.handle, 15) && al(a.lkey, 7) &&
+                         al(a.kind, 1) && al(a.rbase, 15) && al(a.rend, 15) && al(a.reg_start, 15);
+    hipLaunchKernelGGL(k_lookup_big, dim3((unsigned)blocks), dim3(kThreadsLds), bytes, s,
                        a.reg_start, a.reg_end, a.reg_lkey, a.nregions, shift, nsplit,
                        a.page_shift, a.off, a.len, a.n, a.va_base,
-                       a.handle, a.lkey, a.kind, a.rbase, a.rend);
+                       a.handle, a.lkey, a.kind, a.rbase, a.rend, aligned);
     return hipGetLastError();
 }
 

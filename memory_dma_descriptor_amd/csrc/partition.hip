@@ -389,6 +389,8 @@ uint64_t split_tile(uint32_t nq)
 {
     return (uint64_t)kThreads * (nq <= kCntQueues ? kItemsCnt : kItemsBallot);
 }
+static_assert(kThreads * kItemsCnt == 1 << 13 && kThreads * kItemsBallot == 1 << 12,
+              "split_tile_shift matches split_tile");
 
 }  // namespace
 
@@ -400,6 +402,11 @@ size_t ws_partition(uint64_t n, uint32_t nq)
            align256((uint64_t)(nq + 1) * sizeof(uint64_t));
 }
 
+uint32_t split_tile_shift(uint32_t nq)
+{
+    return nq <= kCntQueues ? 13 : 12;
+}
+
 hipError_t launch_partition(const SplitArgs &a, hipStream_t s)
 {
     if (a.n == 0) {
@@ -409,17 +416,27 @@ hipError_t launch_partition(const SplitArgs &a, hipStream_t s)
     }
     const uint64_t tile = split_tile(a.nqueues);
     const uint64_t nb = (a.n + tile - 1) / tile;
-    const uint32_t nbk = a.nqueues + 1;
-    const bool cnt_path = a.nqueues <= kCntQueues;
     uint32_t *counts = static_cast<uint32_t *>(a.ws);
-    uint64_t *total = reinterpret_cast<uint64_t *>(
-        static_cast<char *>(a.ws) + align256((uint64_t)nbk * nb * sizeof(uint32_t)));
-    if (cnt_path)
+    if (a.nqueues <= kCntQueues)
         hipLaunchKernelGGL(k_split_hist<kItemsCnt>, dim3((unsigned)nb), dim3(kThreads), 0, s,
                            a.qid, a.n, a.nqueues, nb, counts);
     else
         hipLaunchKernelGGL(k_split_hist<kItemsBallot>, dim3((unsigned)nb), dim3(kThreads), 0, s,
                            a.qid, a.n, a.nqueues, nb, counts);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return launch_partition_counted(a, s);
+}
+
+hipError_t launch_partition_counted(const SplitArgs &a, hipStream_t s)
+{
+    const uint64_t tile = split_tile(a.nqueues);
+    const uint64_t nb = (a.n + tile - 1) / tile;
+    const uint32_t nbk = a.nqueues + 1;
+    const bool cnt_path = a.nqueues <= kCntQueues;
+    uint32_t *counts = static_cast<uint32_t *>(a.ws);
+    uint64_t *total = reinterpret_cast<uint64_t *>(
+        static_cast<char *>(a.ws) + align256((uint64_t)nbk * nb * sizeof(uint32_t)));
     hipLaunchKernelGGL(k_split_colscan, dim3(nbk), dim3(kThreads), 0, s,
                        counts, nb, nbk, total);
     if (cnt_path) {

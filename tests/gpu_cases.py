@@ -16,6 +16,13 @@ CANARY_I64 = np.uint64(CANARY).astype(np.int64).item()
 PAD_WORDS = 8
 
 
+def prp_tile(n):
+    """Requests per block of the PRP build's slot scan: 256 for batches of at
+    most 2^19 requests, 1,024 above (the library's choice, stated in
+    dmadesc_build_prp's header comment)."""
+    return 256 if n <= (1 << 19) else 1024
+
+
 def padding_spans(prp2, status, off, ln, bus, slot_base=0):
     """(page, first word, end word) of the words after each list's last entry
     that the library may write, from the oracle's PRP2 and status."""

@@ -180,6 +180,35 @@ def test_cq_mirror_rejects_bad_arguments():
 
 
 @no_gpu_only
+def test_build_batch_rejects_bad_arguments():
+    f = dd.lib().dmadesc_build_batch
+    need = dd.batch_workspace_bytes(8, 4, 4)
+    #     rs re rk nr ps  va lut lutn off len qid n  nq bus    pool pp flags
+    ok = [P, P, P, 4, 12, 0, P, 16, P, P, P, 8, 4, 0x10000, P, 4, 1,
+          P, P, P, P, P, P, P, P, P, P, P, P, P, need, NULL]
+    for k, bad in [(16, 2), (16, 3), (12, 0), (12, 257), (11, 1 << 32), (13, 0x10008),
+                   (1, NULL), (4, 11), (4, 31), (3, 1 << 31), (17, NULL), (21, NULL),
+                   (6, NULL), (14, NULL), (14, P + 8), (8, NULL), (10, NULL), (22, NULL),
+                   (25, NULL), (26, NULL), (27, NULL), (28, NULL), (29, NULL),
+                   (30, need - 256), (29, P + 64), (7, 1 << 48)]:
+        args = list(ok)
+        args[k] = bad
+        assert f(*args) == EINVAL, (k, bad)
+
+
+def test_batch_workspace_sizes():
+    ws = dd.batch_workspace_bytes
+    assert ws(100, 0, 10) == 0 and ws(100, 257, 10) == 0 and ws(1 << 32, 64, 10) == 0
+    assert ws(100, 64, 1 << 31) == 0
+    a, b = ws(1 << 24, 64, 4096), ws(1 << 24, 64, 65536)
+    assert 0 < a < b and a % 256 == 0 and b % 256 == 0
+    # at least the PRP scan's and the split's own workspaces
+    assert a >= dd.workspace_bytes(dd.OP_BUILD_PRP, 1 << 24) + \
+        dd.workspace_bytes(dd.OP_PARTITION, 1 << 24, 64)
+    assert ws(0, 64, 0) > 0
+
+
+@no_gpu_only
 def test_table_check_rejects_bad_arguments():
     f = dd.lib().dmadesc_mr_table_check
     bad = ctypes.c_uint64(0)
@@ -254,8 +283,9 @@ def test_empty_lookup_is_a_no_op():
 
 
 @pytest.mark.parametrize("name", ["mr_lookup", "build_prp", "build_prp_packed",
+                                  "build_prp_packed_noalloc", "build_batch",
                                   "partition_by_queue", "emit_sqe", "build_put",
-                                  "cq_mirror"])
+                                  "cq_mirror", "mr_table_check"])
 def test_binding_names_match_abi(name):
     assert callable(getattr(dd, name))
     assert f"dmadesc_{name}" in _declared()

@@ -18,7 +18,6 @@ from tests import gpu_cases as gc
 pytestmark = pytest.mark.gpu
 
 BUS = synth.LIST_BUS_BASE
-TILE = 1024                       # requests per block of the slot scan
 
 
 class tight_waits:
@@ -61,7 +60,7 @@ def _run_expired(packed, d, pool_pages, tries=4):
                                ws=ws, packed=packed, check=False)
         torch.cuda.synchronize()
         blocks, expired = gc.host(ws[:8]).view(np.uint32)
-        assert blocks == (n + TILE - 1) // TILE
+        assert blocks == -(-n // gc.prp_tile(n))
         if expired:
             return {k: gc.host(v) for k, v in out.items()}, pool, int(expired), ws
     pytest.fail(f"no look-back wait expired in {tries} runs at the tightest bound")
@@ -83,10 +82,11 @@ def test_expired_wait_refuses_only_list_requests_of_its_block(packed):
     assert (o["status"][busy] == 0).all() and (pages[busy] >= 3).all()
     assert (g["prp1"][busy] == 0).all() and (g["prp2"][busy] == 0).all()
     # They come in whole blocks: every list request of a refused block is refused.
-    blk = np.unique(np.nonzero(busy)[0] // TILE)
+    tile = gc.prp_tile(d["n"])
+    blk = np.unique(np.nonzero(busy)[0] // tile)
     assert len(blk) <= expired
     for b in blk:
-        sl = slice(b * TILE, (b + 1) * TILE)
+        sl = slice(b * tile, (b + 1) * tile)
         assert (busy[sl] == ((o["status"][sl] == 0) & (pages[sl] >= 3))).all()
     # Everything else is exact.
     for k in ("prp1", "prp2", "status"):
@@ -95,7 +95,7 @@ def test_expired_wait_refuses_only_list_requests_of_its_block(packed):
     # that block's wait expired (certainly so when it refused requests).
     total = int(g["total_pages"][0])
     assert total in (o["total"], 2 ** 64 - 1)
-    if busy[(d["n"] - 1) // TILE * TILE:].any():
+    if busy[(d["n"] - 1) // tile * tile:].any():
         assert total == 2 ** 64 - 1
     gp = gc.host(pool)
     if not packed:
