@@ -70,6 +70,9 @@ def parse():
                     help="steps timed one by one with HIP events for median/min/p95")
     ap.add_argument("--no-configs", action="store_true",
                     help="skip the per-config lines of the other workloads")
+    ap.add_argument("--quick", action="store_true",
+                    help="warm-up and timed steps only (for profiler passes): no other "
+                         "layout, step distribution, batch call, configs, stages or CPU baseline")
     ap.add_argument("--emit-reps", type=int, default=20,
                     help="launches of the submission-entry stage timed after the steps "
                          "(0 = skip it)")
@@ -651,7 +654,7 @@ def main():
     # before the warm-up steps, so the timed steps find the GPU at its
     # steady clocks (the first few dozen steps otherwise run about 1 % slow).
     other = None
-    if d["lut_entries"]:
+    if d["lut_entries"] and not args.quick:
         o_pool, o_pages = st.pool_for(not packed)
         o_key = "build_prp" if packed else "build_prp_packed"
         o_out = [None]
@@ -690,14 +693,15 @@ def main():
     checks = st.check_outputs(np)
 
     # Step-time distribution: steps timed one by one.
-    step_ms = timed_iters(torch, np, st.run, max(args.dist_steps, 20), warm=0)
+    step_ms = timed_iters(torch, np, st.run, 3 if args.quick else max(args.dist_steps, 20),
+                          warm=0)
     step_bytes, step_sum = ab[f"step_{layout}"], ab[f"step_sum_{layout}"]
     step_med = float(np.median(step_ms))
 
     # The same step as one dmadesc_build_batch call, checked against the
     # separate calls' outputs (which are those of the last step).
     batch = None
-    if d["lut_entries"] and nq:
+    if d["lut_entries"] and nq and not args.quick:
         ref = {}
         for o in (st.lk, st.pr, st.sp):
             if o:
@@ -762,6 +766,8 @@ def main():
         result["batch_call"] = batch
     if other:
         result[f"{'page' if packed else 'packed'}_layout_build_prp"] = other
+    if args.quick:
+        args.no_configs, args.emit_reps, args.no_cpu_baseline = True, 0, True
     if not args.no_configs:
         result["per_config"] = {}
         for name, reps in (("tiny", 200), ("small", 200), ("large", 20), ("mrheavy", 20),

@@ -39,6 +39,7 @@
  *             sections "IB Backend MR Cache" and
  *             "Communicator User Registration Cache".
  *   [UPCIE]   xNVMe "uPCIe CUDA" backend: introduction, "Memory Architecture",
+ *             "Completions in device memory",
  *             "Choosing the GPU and Heap Sizes", "GPU-Resident Queue API",
  *             "Limitations".
  *   [MORI]    "mori通信库分析(一)——对称内存RDMA数据发送过程": the thread-scope
@@ -497,7 +498,7 @@ typedef struct dmadesc_cq_slot {
 /*
  * dmadesc_cq_mirror - completion-queue mirror.
  *
- * [UPCIE] "Memory Architecture": one kernel serves every mirrored queue (up to
+ * [UPCIE] "Completions in device memory": one kernel serves every mirrored queue (up to
  * 64) with one wave each and copies completions from the device-memory queue
  * into the mirror queue as their phase bit turns (NVMe: phase tag = bit 16 of
  * dword 3, 1 on the controller's first pass, inverted on each later pass).

@@ -2,7 +2,7 @@
 // completions from device-memory completion queues into mirror queues as their
 // phase bit turns, for gfx950.
 //
-// Method (xNVMe "uPCIe CUDA" page, "Memory Architecture", the CQ mirror): one
+// Method (xNVMe "uPCIe CUDA" page, "Completions in device memory"): one
 // kernel serves every mirrored queue (up to 64), one warp -- here one wave --
 // per queue; it copies completions into the host queue as their phase bit
 // turns. Host and kernel share a slot per queue holding the two queue

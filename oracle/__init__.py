@@ -14,7 +14,13 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
-_SO = os.path.join(_HERE, "liboracle.so")
+# ORACLE_SANITIZE=1 selects a build with AddressSanitizer and
+# UndefinedBehaviorSanitizer (any report aborts); the process must then be
+# started with the ASan runtime preloaded (LD_PRELOAD=$(gcc
+# -print-file-name=libasan.so), ASAN_OPTIONS=detect_leaks=0), as
+# tests/test_oracle_sanitized.py does.
+SANITIZE = os.environ.get("ORACLE_SANITIZE") == "1"
+_SO = os.path.join(_HERE, "liboracle_san.so" if SANITIZE else "liboracle.so")
 
 MISS, EXACT, CONTAINED, INVALID = 0, 1, 2, 3
 OK, EINVAL, ERANGE, ENOSPC = 0, 1, 2, 3
@@ -22,12 +28,17 @@ REG_INVALID, REG_HIT, REG_NEW, REG_HIT_NEW, REG_NOSPACE = 0, 1, 2, 3, 4
 DEREG_OK, DEREG_REMOVED, DEREG_STALE = 0, 1, 2
 
 
-def build() -> str:
-    """Compile liboracle.so with the host C compiler (single-threaded, -O2)."""
-    cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-Wall", "-Wextra",
-           "-o", _SO, _SRC]
+def build(sanitize: bool | None = None) -> str:
+    """Compile the oracle with the host C compiler (single-threaded, -O2), or
+    with ASan + UBSan (-O1, every report fatal) when sanitize is set (default:
+    ORACLE_SANITIZE=1 in the environment)."""
+    san = SANITIZE if sanitize is None else sanitize
+    so = os.path.join(_HERE, "liboracle_san.so" if san else "liboracle.so")
+    opt = (["-O1", "-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
+            "-fno-sanitize-recover=all"] if san else ["-O2"])
+    cmd = ["gcc", *opt, "-std=c11", "-fPIC", "-shared", "-Wall", "-Wextra", "-o", so, _SRC]
     subprocess.run(cmd, check=True)
-    return _SO
+    return so
 
 
 _lib_handle = None

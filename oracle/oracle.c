@@ -507,7 +507,7 @@ void orc_build_put(const uint64_t *src, const uint64_t *dst, const uint64_t *byt
 /* ------------------------------------------------------------------------
  * O7  Completion-queue mirror, one drain.
  *
- * [UPCIE] "Memory Architecture" (the CQ mirror): a resident kernel watches
+ * [UPCIE] "Completions in device memory": a resident kernel watches
  * each device-memory completion queue and copies completions into the host
  * queue as their phase bit turns; per queue the host and the kernel share the
  * two queue addresses, the depth, a generation (odd while attached) and an

@@ -13,7 +13,8 @@
  *              "Communicator User Registration Cache" and
  *              "真实 ncclCommRegister 语义实验".
  *   [UPCIE]    xNVMe "uPCIe CUDA" backend (xnvme.io), introduction,
- *              "Memory Architecture" and "Limitations".
+ *              "Memory Architecture", "Completions in device memory" and
+ *              "Limitations".
  *   [MORI]     "mori通信库分析(一)——对称内存RDMA数据发送过程", the
  *              thread-scope put kernel and the warp-level WQE reservation.
  *   [NVMe]     NVM Express Base Specification, PRP entry / PRP list rules

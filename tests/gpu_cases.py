@@ -24,30 +24,34 @@ def prp_tile(n):
 
 
 def padding_spans(prp2, status, off, ln, bus, slot_base=0):
-    """(page, first word, end word) of the words after each list's last entry
-    that the library may write, from the oracle's PRP2 and status."""
+    """(page, first word, end word) arrays of the words after each list's last
+    entry that the library may write, from the oracle's PRP2 and status."""
     off = np.asarray(off, np.uint64)
     ln = np.asarray(ln, np.uint64)
     pages = ((off & np.uint64(4095)) + ln + np.uint64(4095)) >> np.uint64(12)
-    sel = np.nonzero((status == 0) & (pages >= 3))[0]
-    spans = []
-    for i in sel:
-        m = int(pages[i]) - 1
-        lp = (m - 1 + 510) // 511
-        final_words = m - 511 * (lp - 1)
-        end = min(512, -(-final_words // PAD_WORDS) * PAD_WORDS)
-        if end > final_words:
-            page = (int(prp2[i]) - bus) // 4096 + lp - 1 - slot_base
-            spans.append((page, final_words, end))
-    return spans
+    sel = np.nonzero((np.asarray(status) == 0) & (pages >= 3))[0]
+    m = pages[sel].astype(np.int64) - 1
+    lp = (m - 1 + 510) // 511
+    final_words = m - 511 * (lp - 1)
+    end = np.minimum(512, -(-final_words // PAD_WORDS) * PAD_WORDS)
+    page = ((np.asarray(prp2)[sel] - np.uint64(bus)) // np.uint64(4096)).astype(np.int64) \
+        + lp - 1 - slot_base
+    keep = end > final_words
+    return page[keep], final_words[keep], end[keep]
 
 
 def mask_padding(a, b, spans):
     """Makes the padding words of both pools equal before they are compared."""
-    for page, lo, hi in spans:
-        if 0 <= page < a.shape[0]:
-            a[page, lo:hi] = 0
-            b[page, lo:hi] = 0
+    page, lo, hi = spans
+    ok = (page >= 0) & (page < a.shape[0])
+    page, lo, hi = page[ok], lo[ok], hi[ok]
+    width = hi - lo
+    if width.size == 0:
+        return
+    rows = np.repeat(page, width)
+    cols = np.repeat(lo, width) + (np.arange(int(width.sum())) - np.repeat(np.cumsum(width) - width, width))
+    a[rows, cols] = 0
+    b[rows, cols] = 0
 
 
 def dev(a: np.ndarray) -> torch.Tensor:
@@ -138,42 +142,44 @@ def check_prp_full(lut, off, ln, bus, pool_pages, ctx="", packed=False):
     return o, g
 
 
-def check_prp_sampled(lut, off, ln, bus, pool_pages, sample, ctx=""):
-    """Full-size check: every PRP1/PRP2/status and the total against the
-    oracle run without a pool; list pages of `sample` requests against the
-    oracle run on each request alone at its slot; pool pages past the total
-    untouched."""
+def check_prp_chunked(lut, off, ln, bus, pool_pages, ctx="", chunk=1 << 20):
+    """Full-size check of the page layout, every list page included: every
+    PRP1/PRP2/status and the total against the oracle run without a pool;
+    then, chunk by chunk of requests, the oracle run on the chunk alone at
+    its slot offset (the oracle's own page count of the requests before it)
+    writes the chunk's list pages, which must equal the GPU pool's pages at
+    that offset (padding words masked); pool pages past the total untouched."""
     o = oracle.build_prp(lut, off, ln, bus, pool_pages, pool=None)
     g, pool = gpu_prp(lut, off, ln, bus, pool_pages)
     assert_prp_columns_equal(o, g, ctx)
-    lists = [int(i) for i in sample
-             if g["status"][i] == 0 and g["prp2"][i] >= bus
-             and (g["prp2"][i] - bus) // 4096 < min(pool_pages, g["total"])
-             and (ln[i] + (off[i] % 4096) + 4095) // 4096 >= 3]
-    slots, want, spans = [], [], []
-    for i in lists:
-        slot = (int(g["prp2"][i]) - bus) // 4096
-        one = oracle.build_prp(lut, off[i:i + 1], ln[i:i + 1], bus + slot * 4096,
-                               pool_pages - slot, pool=None)
-        lp = one["total"]
-        page = np.full((lp, 512), CANARY, dtype=np.uint64)
-        oracle.build_prp(lut, off[i:i + 1], ln[i:i + 1], bus + slot * 4096, lp, pool=page)
-        spans += [(pg + len(slots), lo, hi) for pg, lo, hi in
-                  padding_spans(one["prp2"], one["status"], off[i:i + 1], ln[i:i + 1],
-                                bus + slot * 4096)]
-        slots.extend(range(slot, slot + lp))
-        want.append(page)
-    if slots:
-        idx = torch.tensor(slots, dtype=torch.int64, device="cuda")
-        got = host(pool.view(torch.int64)[idx]).view(np.uint64)
-        want = np.concatenate(want)
-        mask_padding(got, want, spans)
-        if not np.array_equal(got, want):
-            bad = np.argwhere(got != want)
-            raise AssertionError(f"{ctx} sampled list pages: {len(bad)} mismatches")
+    n = len(off)
+    slot0 = 0
+    compared = 0
+    for i0 in range(0, n, chunk):
+        i1 = min(n, i0 + chunk)
+        o_off, o_ln = off[i0:i1], ln[i0:i1]
+        base = bus + slot0 * 4096
+        need = oracle.build_prp(lut, o_off, o_ln, base, pool_pages - slot0, pool=None)["total"]
+        want = np.full((max(need, 1), 512), CANARY, dtype=np.uint64)
+        part = oracle.build_prp(lut, o_off, o_ln, base, need, pool=want)
+        # The chunk run places its requests exactly as the whole run does.
+        for k in ("prp1", "prp2", "status"):
+            assert np.array_equal(part[k], o[k][i0:i1]), (ctx, i0, k)
+        if need:
+            got = host(pool[slot0:slot0 + need])
+            mask_padding(got, want, padding_spans(part["prp2"], part["status"], o_off, o_ln,
+                                                  bus, slot_base=slot0))
+            if not np.array_equal(got, want[:need]):
+                bad = np.argwhere(got != want[:need])
+                raise AssertionError(f"{ctx} list pages of requests [{i0}, {i1}): {len(bad)} "
+                                     f"words differ, first at page {slot0 + bad[0][0]} "
+                                     f"word {bad[0][1]}")
+        compared += need
+        slot0 += need
+    assert slot0 == o["total"] == compared, (ctx, slot0, o["total"])
     tail = pool.view(torch.int64)[min(g["total"], pool_pages):]
     assert bool((tail == CANARY_I64).all()), f"{ctx}: pool pages past the total were written"
-    return o, g, len(lists)
+    return o, g, compared
 
 
 # ------------------------------------------------------------------ split ---
