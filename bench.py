@@ -172,6 +172,8 @@ class Step:
         self.off, self.ln, self.qid, self.lut = up(d["off"]), up(d["len"]), up(d["qid"]), up(d["lut"])
         self.lk = self.pr = self.sp = self.bt = None
         self.pool = self.pool_pages = None
+        need = dd.workspace_bytes(dd.OP_MR_LOOKUP, self.n, d["regions"])
+        self.ws_lk = torch.empty(need, dtype=torch.uint8, device=dev) if need else None
         if d["lut_entries"]:
             self.pool, self.pool_pages = self.pool_for(packed)
             self.ws_prp = torch.empty(max(dd.workspace_bytes(dd.OP_BUILD_PRP, self.n), 1),
@@ -208,7 +210,7 @@ class Step:
             ev[0].record()
         if d["regions"]:
             self.lk = dd.mr_lookup(self.rs, self.re, self.rk, self.off, self.ln,
-                                   va_base=d["va_base"], out=self.lk)
+                                   va_base=d["va_base"], out=self.lk, ws=self.ws_lk)
             k += 1
             if ev:
                 ev[k].record()

@@ -155,7 +155,13 @@ enum dmadesc_op {
  *                region's bounds
  *   rbase   u64  rounded base (0 when INVALID)
  *   rend    u64  rounded end, exclusive (0 when INVALID)
- * Workspace: none (ws may be NULL).
+ * Workspace (optional): for tables of more than 4,096 regions,
+ *   dmadesc_workspace_bytes(DMADESC_OP_MR_LOOKUP, n, nregions) bytes
+ *   (64 per run of 4 regions, 256-byte aligned) let the call copy the table
+ *   into one record per run and answer each request from one cache line of
+ *   it; the call overwrites the workspace. ws NULL takes the path without
+ *   records (same results, slower on large tables); a workspace given too
+ *   small or misaligned is -EINVAL. Smaller tables need none (0 bytes).
  */
 int dmadesc_mr_lookup(const uint64_t *reg_start, const uint64_t *reg_end,
                       const uint32_t *reg_lkey, uint32_t nregions, uint32_t page_shift,
@@ -590,7 +596,8 @@ int dmadesc_reg_deregister(uint64_t *start, uint64_t *end, uint64_t *id, uint32_
 
 /* Workspace bytes needed by `op` for n requests (`param` = nqueues for
  * DMADESC_OP_PARTITION and DMADESC_OP_EMIT_SQE, the table capacity for
- * DMADESC_OP_REGISTRY, ignored otherwise). Returns 0 for an unknown op or
+ * DMADESC_OP_REGISTRY, nregions for DMADESC_OP_MR_LOOKUP (its optional
+ * record workspace), ignored otherwise). Returns 0 for an unknown op or
  * for an op that needs none. Host-only; launches nothing. */
 size_t dmadesc_workspace_bytes(int op, uint64_t n, uint32_t param);
 

@@ -167,10 +167,16 @@ def _workspace(op: int, n: int, param: int, device, ws):
 
 def mr_lookup(reg_start: torch.Tensor, reg_end: torch.Tensor, reg_lkey: torch.Tensor,
               off: torch.Tensor, length: torch.Tensor, va_base: int = 0,
-              page_shift: int = 12, out: dict | None = None, stream=None) -> dict:
-    """Page-rounded containment lookup; returns dict(handle, lkey, kind, rbase, rend)."""
+              page_shift: int = 12, out: dict | None = None, stream=None,
+              ws: torch.Tensor | None = None, records: bool = True) -> dict:
+    """Page-rounded containment lookup; returns dict(handle, lkey, kind, rbase, rend).
+    Tables of more than 4,096 regions take the record path through a
+    workspace (`ws`, or a new one); records=False passes none."""
     n, r = off.numel(), reg_start.numel()
     dev = off.device
+    ws_ptr, ws_bytes = None, 0
+    if records and workspace_bytes(OP_MR_LOOKUP, n, r) > 0:
+        ws, ws_ptr, ws_bytes = _workspace(OP_MR_LOOKUP, n, r, dev, ws)
     if out is None:
         out = dict(handle=torch.empty(n, dtype=torch.int32, device=dev),
                    lkey=torch.empty(n, dtype=torch.uint32, device=dev),
@@ -183,7 +189,7 @@ def mr_lookup(reg_start: torch.Tensor, reg_end: torch.Tensor, reg_lkey: torch.Te
         _dev(off, torch.uint64, "off", n), _dev(length, torch.uint64, "len", n), n, va_base,
         _dev(out["handle"], torch.int32, "handle", n), _dev(out["lkey"], torch.uint32, "lkey", n),
         _dev(out["kind"], torch.uint8, "kind", n), _dev(out["rbase"], torch.uint64, "rbase", n),
-        _dev(out["rend"], torch.uint64, "rend", n), None, 0, _stream(dev, stream))
+        _dev(out["rend"], torch.uint64, "rend", n), ws_ptr, ws_bytes, _stream(dev, stream))
     _check("dmadesc_mr_lookup", rc)
     return out
 

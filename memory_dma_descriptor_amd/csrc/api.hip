@@ -103,7 +103,7 @@ const char *dmadesc_strerror(int err)
 size_t dmadesc_workspace_bytes(int op, uint64_t n, uint32_t param)
 {
     switch (op) {
-    case DMADESC_OP_MR_LOOKUP: return 0;
+    case DMADESC_OP_MR_LOOKUP: return dd::ws_mr_lookup(param);
     case DMADESC_OP_BUILD_PRP: return dd::ws_build_prp(n);
     case DMADESC_OP_PARTITION:
         if (param == 0 || param > DMADESC_MAX_QUEUES) return 0;
@@ -126,15 +126,16 @@ int dmadesc_mr_lookup(const uint64_t *reg_start, const uint64_t *reg_end,
                       uint64_t *rbase, uint64_t *rend,
                       void *ws, size_t ws_bytes, void *stream)
 {
-    (void)ws;
-    (void)ws_bytes;
     if (page_shift < 12 || page_shift > 30) return -EINVAL;
     if (n >= kMaxN || nregions >= (1u << 31)) return -EINVAL;
     if (nregions > 0 && (!reg_start || !reg_end || !reg_lkey)) return -EINVAL;
+    const size_t need = dd::ws_mr_lookup(nregions);
+    if (ws && need > 0 && !ws_ok(ws, ws_bytes, need)) return -EINVAL;
     if (n == 0) return 0;
     if (!off || !len || !handle || !lkey || !kind || !rbase || !rend) return -EINVAL;
     dd::LookupArgs a{reg_start, reg_end, reg_lkey, nregions, page_shift, off, len, n, va_base,
                      handle, lkey, kind, rbase, rend};
+    if (ws && need > 0) a.rec = static_cast<uint64_t *>(ws);
     return launched(dd::launch_mr_lookup(a, static_cast<hipStream_t>(stream)));
 }
 

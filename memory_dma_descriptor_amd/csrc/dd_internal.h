@@ -20,6 +20,7 @@ struct LookupArgs {
     uint32_t *lkey;
     uint8_t *kind;
     uint64_t *rbase, *rend;
+    uint64_t *rec = nullptr;   // record copy of a large table (workspace), or none
 };
 
 struct PrpArgs {
@@ -118,6 +119,7 @@ hipError_t launch_build_put(const PutArgs &a, hipStream_t s);
 hipError_t launch_reg_register(const RegArgs &a, hipStream_t s);
 hipError_t launch_reg_deregister(const RegArgs &a, hipStream_t s);
 
+size_t ws_mr_lookup(uint32_t nregions);
 size_t ws_build_prp(uint64_t n);
 size_t ws_partition(uint64_t n, uint32_t nqueues);
 size_t ws_emit_sqe(uint32_t nqueues);

@@ -21,6 +21,13 @@
 //    start in LDS (at most kMaxSplitters splitters = 64 KiB, with a bucket
 //    index over them); a lane finds its splitter in LDS, then reads the 8
 //    starts of that run in one 64-byte read (the table is L2-resident).
+//    With a workspace, k_rec_build first writes one 64-byte record per run
+//    of 4 regions (the other three starts as page deltas from the first, the
+//    four ends and the four keys), LDS holds every 4th start, and a request
+//    is answered from its run's record in one round of four independent
+//    16-byte loads. The time of this kernel goes to dependent rounds of
+//    gathers (each waits behind the column stream's HBM misses in the vector
+//    memory pipeline), not to the number of loads in a round.
 //
 // The searches are branch-free: the trip count depends only on the length
 // searched, so lanes of a wave never diverge in them.
@@ -40,6 +47,10 @@ typedef uint64_t u64x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 constexpr uint32_t kMaxSplitters = 8192;   // 64 KiB of LDS
+constexpr uint32_t kMaxRecSplitters = 16384;   // 128 KiB of LDS (record path)
+constexpr uint32_t kRecRun = 4;              // regions per 64-byte record
+constexpr uint32_t kRecBytes = 64;
+constexpr uint32_t kLdsRegions = 4096;       // largest table k_lookup_lds holds
 
 // Index of the last element <= key in a[0..cnt), given a[0] <= key.
 template <typename Ptr>
@@ -237,6 +248,55 @@ __device__ __forceinline__ uint32_t count_le(const uint64_t (&t)[kRun], uint64_t
     return c;
 }
 
+// Record copy of the table for k_lookup_big<true>. With P = 2^page_shift
+// and B = ceil(start[4j] / P), record j (64 bytes) describes regions
+// 4j .. 4j + 3:
+//   u32 d[1..3]  ceil(start[4j + i] / P) - B: for a page-aligned rounded base
+//                lo, start <= lo exactly when its d <= lo / P - B.
+//                0xFFFFFFFF past the table (never at or below a base).
+//   u32 flags    bit i: start[4j + i] is a multiple of P (with d equal to
+//                lo / P - B this makes start == lo: an EXACT bound); bit 4
+//                ("wide"): some delta does not fit 32 bits, and the lookup
+//                reads that run's starts from the table instead.
+//   u64 end[0..3], then u32 key[0..3] (0 past the table).
+// One thread per record.
+constexpr uint32_t kWide = 16u;
+
+__global__ __launch_bounds__(kThreads) void k_rec_build(
+    const uint64_t *__restrict__ rs, const uint64_t *__restrict__ re,
+    const uint32_t *__restrict__ rk, uint32_t nregions, uint32_t page_shift,
+    uint32_t *__restrict__ rec)
+{
+    const uint64_t nrec = ((uint64_t)nregions + kRecRun - 1) / kRecRun;
+    const uint64_t in_page = (1ull << page_shift) - 1;
+    for (uint64_t j = (uint64_t)blockIdx.x * kThreads + threadIdx.x; j < nrec;
+         j += (uint64_t)gridDim.x * kThreads) {
+        const uint64_t r0 = j * kRecRun;
+        uint64_t e[kRecRun];
+        uint32_t k[kRecRun], d[kRecRun], flags = 0;
+        const uint64_t s0 = rs[r0];
+        const uint64_t base = (s0 >> page_shift) + ((s0 & in_page) != 0);
+#pragma unroll
+        for (uint32_t i = 0; i < kRecRun; ++i) {
+            const bool in = r0 + i < nregions;
+            const uint64_t st = in ? rs[r0 + i] : 0;
+            e[i] = in ? re[r0 + i] : 0;
+            k[i] = in ? rk[r0 + i] : 0;
+            const uint64_t up = (st >> page_shift) + ((st & in_page) != 0);
+            const uint64_t delta = up - base;      // wraps on an unsorted table: then "wide"
+            d[i] = !in ? 0xFFFFFFFFu : delta >= 0xFFFFFFFFull ? 0xFFFFFFFFu : (uint32_t)delta;
+            if (in && delta >= 0xFFFFFFFFull) flags |= kWide;
+            if (in && (st & in_page) == 0) flags |= 1u << i;
+        }
+        u32x4 *q = reinterpret_cast<u32x4 *>(rec + j * (kRecBytes / 4));
+        q[0] = u32x4{d[1], d[2], d[3], flags};
+        reinterpret_cast<u64x2 *>(q)[1] = u64x2{e[0], e[1]};
+        reinterpret_cast<u64x2 *>(q)[2] = u64x2{e[2], e[3]};
+        q[3] = u32x4{k[0], k[1], k[2], k[3]};
+    }
+}
+
+template <bool kRec>
 __global__ __launch_bounds__(kThreadsLds) void k_lookup_big(
     const uint64_t *__restrict__ rs, const uint64_t *__restrict__ re,
     const uint32_t *__restrict__ rk, uint32_t nregions, uint32_t split_shift,
@@ -245,8 +305,9 @@ __global__ __launch_bounds__(kThreadsLds) void k_lookup_big(
     uint64_t n, uint64_t va_base,
     int32_t *__restrict__ handle, uint32_t *__restrict__ lkey,
     uint8_t *__restrict__ kind, uint64_t *__restrict__ rbase,
-    uint64_t *__restrict__ rend, bool aligned)
+    uint64_t *__restrict__ rend, bool aligned, const uint32_t *__restrict__ rec)
 {
+    constexpr uint32_t kNarrow = kRec ? kRecRun : kRun;   // run length after narrowing
     extern __shared__ uint64_t lds[];
     uint64_t *spl = lds;                                          // nsplit starts
     uint16_t *s_idx = reinterpret_cast<uint16_t *>(lds + nsplit); // kBuckets + 1
@@ -307,7 +368,7 @@ __global__ __launch_bounds__(kThreadsLds) void k_lookup_big(
                 l[k] = i < n ? len[i] : 0;
             }
         }
-        uint64_t lo[kPerLane], hi[kPerLane], at[kPerLane];
+        uint64_t lo[kPerLane], hi[kPerLane], at[kPerLane], sat[kPerLane];
         bool valid[kPerLane], cand[kPerLane];
 #pragma unroll
         for (int k = 0; k < kPerLane; ++k) {
@@ -323,61 +384,113 @@ __global__ __launch_bounds__(kThreadsLds) void k_lookup_big(
                 c = first + (uint32_t)last_le(spl + first, i1 - first, lo[k]);
             }
             at[k] = (uint64_t)c << split_shift;
-            // Runs of more than kRun starts: narrow to kRun by a search over
-            // every kRun-th start of the run in global memory.
+            sat[k] = spl[c];                      // start of region at[k]
+            // Runs of more than kNarrow starts: narrow to kNarrow by a search
+            // over every kNarrow-th start of the run in global memory.
             uint64_t cnt = (uint64_t)nregions - at[k];
             cnt = cnt < runlen ? cnt : runlen;
-            if (cand[k] && runlen > kRun) {
-                uint64_t step_at = 0, m = (cnt + kRun - 1) / kRun;
+            if (cand[k] && runlen > kNarrow) {
+                uint64_t step_at = 0, m = (cnt + kNarrow - 1) / kNarrow;
                 while (m > 1) {
                     const uint64_t half = m >> 1;
-                    step_at = rs[at[k] + (step_at + half) * kRun] <= lo[k] ? step_at + half : step_at;
+                    const uint64_t v = rs[at[k] + (step_at + half) * kNarrow];
+                    if (v <= lo[k]) {
+                        step_at += half;
+                        sat[k] = v;
+                    }
                     m -= half;
                 }
-                at[k] += step_at * kRun;
+                at[k] += step_at * kNarrow;
             }
-        }
-        // The kRun starts from `at` (past the table: never at or below lo).
-        uint32_t r[kPerLane];
-        uint64_t s0[kPerLane];
-#pragma unroll
-        for (int k = 0; k < kPerLane; ++k) {
-            uint64_t t[kRun];
-            if (cand[k] && at[k] + kRun <= nregions && aligned) {
-                const u64x2 *q = reinterpret_cast<const u64x2 *>(rs + at[k]);
-#pragma unroll
-                for (int j = 0; j < (int)kRun / 2; ++j) {
-                    const u64x2 v = q[j];
-                    t[2 * j] = v.x;
-                    t[2 * j + 1] = v.y;
-                }
-            } else {
-#pragma unroll
-                for (int j = 0; j < (int)kRun; ++j)
-                    t[j] = cand[k] && at[k] + j < nregions ? rs[at[k] + j] : ~0ull;
-            }
-            const uint32_t c = cand[k] ? count_le(t, lo[k]) : 1u;   // >= 1: t[0] <= lo
-            r[k] = (uint32_t)at[k] + c - 1;
-            uint64_t sel = t[0];
-#pragma unroll
-            for (int j = 1; j < (int)kRun; ++j) sel = (uint32_t)j == c - 1 ? t[j] : sel;
-            s0[k] = sel;
         }
         int32_t h[kPerLane];
         uint32_t key[kPerLane];
         uint8_t kd[kPerLane];
-        uint64_t e0[kPerLane];
+        if constexpr (kRec) {
+            // One round: the run's whole record (a non-candidate reads record
+            // 0, so the loads stay unconditional).
+            u32x4 hd[kPerLane], kk[kPerLane];
+            u64x2 ea[kPerLane], eb[kPerLane];
 #pragma unroll
-        for (int k = 0; k < kPerLane; ++k) {
-            e0[k] = cand[k] ? re[r[k]] : 0;
-            key[k] = cand[k] ? rk[r[k]] : 0;
-        }
+            for (int k = 0; k < kPerLane; ++k) {
+                const u32x4 *q = reinterpret_cast<const u32x4 *>(
+                    rec + (cand[k] ? at[k] / kRecRun : 0) * (kRecBytes / 4));
+                hd[k] = q[0];
+                ea[k] = reinterpret_cast<const u64x2 *>(q)[1];
+                eb[k] = reinterpret_cast<const u64x2 *>(q)[2];
+                kk[k] = q[3];
+            }
 #pragma unroll
-        for (int k = 0; k < kPerLane; ++k) {
-            const bool hit = cand[k] && hi[k] <= e0[k];
-            h[k] = hit ? (int32_t)r[k] : -1;
-            key[k] = hit ? key[k] : 0;
-            kd[k] = !valid[k] ? 3 : !hit ? 0 : (lo[k] == s0[k] && hi[k] == e0[k]) ? 1 : 2;
+            for (int k = 0; k < kPerLane; ++k) {
+                const uint64_t base_pg = (sat[k] >> page_shift) + ((sat[k] & in_page) != 0);
+                const uint64_t qd = (lo[k] >> page_shift) - base_pg;     // >= 0: sat <= lo
+                const uint32_t q32 = qd < 0xFFFFFFFEull ? (uint32_t)qd : 0xFFFFFFFEu;
+                uint32_t c = (hd[k].x <= q32 ? 1u : 0u) + (hd[k].y <= q32 ? 1u : 0u) +
+                             (hd[k].z <= q32 ? 1u : 0u);
+                const uint32_t dc = c == 0 ? 0u : c == 1 ? hd[k].x : c == 2 ? hd[k].y : hd[k].z;
+                bool exact_lo = ((hd[k].w >> c) & 1u) && (uint64_t)dc == qd;
+                if (cand[k] && (hd[k].w & kWide)) {
+                    // Deltas beyond 32 bits: count the run's starts exactly.
+                    uint64_t sc = sat[k];
+                    c = 0;
+#pragma unroll
+                    for (uint32_t i = 1; i < kRecRun; ++i) {
+                        const bool in = at[k] + i < nregions;
+                        const uint64_t v = in ? rs[at[k] + i] : ~0ull;
+                        if (in && v <= lo[k]) {
+                            c = i;
+                            sc = v;
+                        }
+                    }
+                    exact_lo = lo[k] == sc;
+                }
+                const uint64_t e = c == 0 ? ea[k].x : c == 1 ? ea[k].y : c == 2 ? eb[k].x : eb[k].y;
+                const uint32_t kv = c == 0 ? kk[k].x : c == 1 ? kk[k].y : c == 2 ? kk[k].z : kk[k].w;
+                const bool hit = cand[k] && hi[k] <= e;
+                h[k] = hit ? (int32_t)(at[k] + c) : -1;
+                key[k] = hit ? kv : 0;
+                kd[k] = !valid[k] ? 3 : !hit ? 0 : (exact_lo && hi[k] == e) ? 1 : 2;
+            }
+        } else {
+            // The kRun starts from `at` (past the table: never at or below lo).
+            uint32_t r[kPerLane];
+            uint64_t s0[kPerLane];
+#pragma unroll
+            for (int k = 0; k < kPerLane; ++k) {
+                uint64_t t[kRun];
+                if (cand[k] && at[k] + kRun <= nregions && aligned) {
+                    const u64x2 *q = reinterpret_cast<const u64x2 *>(rs + at[k]);
+#pragma unroll
+                    for (int j = 0; j < (int)kRun / 2; ++j) {
+                        const u64x2 v = q[j];
+                        t[2 * j] = v.x;
+                        t[2 * j + 1] = v.y;
+                    }
+                } else {
+#pragma unroll
+                    for (int j = 0; j < (int)kRun; ++j)
+                        t[j] = cand[k] && at[k] + j < nregions ? rs[at[k] + j] : ~0ull;
+                }
+                const uint32_t c = cand[k] ? count_le(t, lo[k]) : 1u;   // >= 1: t[0] <= lo
+                r[k] = (uint32_t)at[k] + c - 1;
+                uint64_t sel = t[0];
+#pragma unroll
+                for (int j = 1; j < (int)kRun; ++j) sel = (uint32_t)j == c - 1 ? t[j] : sel;
+                s0[k] = sel;
+            }
+            uint64_t e0[kPerLane];
+#pragma unroll
+            for (int k = 0; k < kPerLane; ++k) {
+                e0[k] = cand[k] ? re[r[k]] : 0;
+                key[k] = cand[k] ? rk[r[k]] : 0;
+            }
+#pragma unroll
+            for (int k = 0; k < kPerLane; ++k) {
+                const bool hit = cand[k] && hi[k] <= e0[k];
+                h[k] = hit ? (int32_t)r[k] : -1;
+                key[k] = hit ? key[k] : 0;
+                kd[k] = !valid[k] ? 3 : !hit ? 0 : (lo[k] == s0[k] && hi[k] == e0[k]) ? 1 : 2;
+            }
         }
         if (whole) {
 #pragma unroll
@@ -453,7 +566,7 @@ hipError_t launch_mr_lookup(const LookupArgs &a, hipStream_t s)
 
     const size_t table_bytes = (size_t)a.nregions * 20 + (a.nregions & 1) * 4 +
                                (size_t)(kBuckets + 1) * sizeof(uint16_t);
-    if (a.nregions <= 4096 && table_bytes <= (size_t)lds_max) {
+    if (a.nregions <= kLdsRegions && table_bytes <= (size_t)lds_max) {
         // One 1,024-thread block per CU holds the table and its bucket index;
         // each answers a grid-stride share.
         const size_t bytes = table_bytes;
@@ -475,24 +588,55 @@ hipError_t launch_mr_lookup(const LookupArgs &a, hipStream_t s)
                            a.rend, aligned);
         return hipGetLastError();
     }
+    auto al = [](const void *p, uintptr_t m) { return (reinterpret_cast<uintptr_t>(p) & m) == 0; };
+    const bool cols_aligned = al(a.off, 15) && al(a.len, 15) && al(a.handle, 15) &&
+                              al(a.lkey, 7) && al(a.kind, 1) && al(a.rbase, 15) && al(a.rend, 15);
+    uint64_t blocks = (a.n + (uint64_t)kThreadsLds * kPerLane - 1) / ((uint64_t)kThreadsLds * kPerLane);
+    if (blocks > (uint64_t)cus) blocks = (uint64_t)cus;
+    // Record path: every 2^shift-th start in LDS (at least every 4th).
+    uint32_t rshift = 2;
+    while (((uint64_t)a.nregions + (1ull << rshift) - 1) >> rshift > kMaxRecSplitters) ++rshift;
+    const uint32_t rsplit = (uint32_t)(((uint64_t)a.nregions + (1ull << rshift) - 1) >> rshift);
+    const size_t rbytes = (size_t)rsplit * sizeof(uint64_t) + (size_t)(kBuckets + 1) * sizeof(uint16_t);
+    if (a.rec && rbytes <= (size_t)lds_max) {
+        const uint32_t shift = rshift, nsplit = rsplit;
+        const size_t bytes = rbytes;
+        e = hipFuncSetAttribute(reinterpret_cast<const void *>(k_lookup_big<true>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+        if (e != hipSuccess) return e;
+        const uint64_t nrec = ((uint64_t)a.nregions + kRecRun - 1) / kRecRun;
+        uint64_t rb = (nrec + kThreads - 1) / kThreads;
+        if (rb > 1024) rb = 1024;
+        auto *rec = reinterpret_cast<uint32_t *>(a.rec);
+        hipLaunchKernelGGL(k_rec_build, dim3((unsigned)rb), dim3(kThreads), 0, s,
+                           a.reg_start, a.reg_end, a.reg_lkey, a.nregions, a.page_shift, rec);
+        hipLaunchKernelGGL(k_lookup_big<true>, dim3((unsigned)blocks), dim3(kThreadsLds), bytes, s,
+                           a.reg_start, a.reg_end, a.reg_lkey, a.nregions, shift, nsplit,
+                           a.page_shift, a.off, a.len, a.n, a.va_base,
+                           a.handle, a.lkey, a.kind, a.rbase, a.rend, cols_aligned,
+                           (const uint32_t *)rec);
+        return hipGetLastError();
+    }
     // Every 2^shift-th start in LDS (at least every kRun-th).
     uint32_t shift = 3;
     while (((uint64_t)a.nregions + (1ull << shift) - 1) >> shift > kMaxSplitters) ++shift;
     const uint32_t nsplit = (uint32_t)(((uint64_t)a.nregions + (1ull << shift) - 1) >> shift);
     const size_t bytes = (size_t)nsplit * sizeof(uint64_t) + (size_t)(kBuckets + 1) * sizeof(uint16_t);
-    e = hipFuncSetAttribute(reinterpret_cast<const void *>(k_lookup_big),
+    e = hipFuncSetAttribute(reinterpret_cast<const void *>(k_lookup_big<false>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
     if (e != hipSuccess) return e;
-    uint64_t blocks = (a.n + (uint64_t)kThreadsLds * kPerLane - 1) / ((uint64_t)kThreadsLds * kPerLane);
-    if (blocks > (uint64_t)cus) blocks = (uint64_t)cus;
-    auto al = [](const void *p, uintptr_t m) { return (reinterpret_cast<uintptr_t>(p) & m) == 0; };
-    const bool aligned = al(a.off, 15) && al(a.len, 15) && al(a.handle, 15) && al(a.lkey, 7) &&
-                         al(a.kind, 1) && al(a.rbase, 15) && al(a.rend, 15) && al(a.reg_start, 15);
-    hipLaunchKernelGGL(k_lookup_big, dim3((unsigned)blocks), dim3(kThreadsLds), bytes, s,
+    const bool aligned = cols_aligned && al(a.reg_start, 15);
+    hipLaunchKernelGGL(k_lookup_big<false>, dim3((unsigned)blocks), dim3(kThreadsLds), bytes, s,
                        a.reg_start, a.reg_end, a.reg_lkey, a.nregions, shift, nsplit,
                        a.page_shift, a.off, a.len, a.n, a.va_base,
-                       a.handle, a.lkey, a.kind, a.rbase, a.rend, aligned);
+                       a.handle, a.lkey, a.kind, a.rbase, a.rend, aligned,
+                       (const uint32_t *)nullptr);
     return hipGetLastError();
+}
+
+size_t ws_mr_lookup(uint32_t nregions)
+{
+    return nregions > kLdsRegions ? ((size_t)nregions + kRecRun - 1) / kRecRun * kRecBytes : 0;
 }
 
 }  // namespace dd

@@ -3,7 +3,8 @@
 //
 // The packed PRP build needs a workspace (a 256-byte header with the block
 // ticket and the count of expired waits, then one look-back status word per
-// block of 1,024 requests). Callers that cannot allocate device memory use
+// block: 256 requests per block up to 2^19 requests, 1,024 above, so 8 bytes
+// per 1,024 requests bound it either way). Callers that cannot allocate device memory use
 // this file-scope array instead: every GPU the library runs on holds one
 // copy, at its own address, until the process ends. Host code never passes
 // the array's name to a kernel (in host code it is a stand-in, not a device

@@ -68,11 +68,19 @@ def say(msg: str) -> None:
 
 # ----------------------------------------------------------------- lookup ---
 
-def gpu_lookup(start, end, lkey, off, ln, va_base=0, page_shift=12):
+def gpu_lookup(start, end, lkey, off, ln, va_base=0, page_shift=12, records=True):
+    ws = None
+    if records and len(start) > 4096:
+        # A canary after the record workspace: the kernels stay inside it.
+        need = dd.workspace_bytes(dd.OP_MR_LOOKUP, len(off), len(start))
+        ws = torch.full((need + 4096,), 0x5A, dtype=torch.uint8, device="cuda")
     out = dd.mr_lookup(dev(np.asarray(start, np.uint64)), dev(np.asarray(end, np.uint64)),
                        dev(np.asarray(lkey, np.uint32)), dev(np.asarray(off, np.uint64)),
-                       dev(np.asarray(ln, np.uint64)), va_base=va_base, page_shift=page_shift)
+                       dev(np.asarray(ln, np.uint64)), va_base=va_base, page_shift=page_shift,
+                       ws=None if ws is None else ws[:need], records=records)
     torch.cuda.synchronize()
+    if ws is not None:
+        assert (host(ws[need:]) == 0x5A).all(), "lookup wrote past its record workspace"
     return {k: host(v) for k, v in out.items()}
 
 
@@ -84,9 +92,10 @@ def assert_lookup_equal(o, g, ctx=""):
                                  f"{bad[0]}: oracle {o[k][bad[0]]} gpu {g[k][bad[0]]}")
 
 
-def check_lookup(start, end, lkey, off, ln, va_base=0, page_shift=12, ctx=""):
+def check_lookup(start, end, lkey, off, ln, va_base=0, page_shift=12, ctx="", records=True):
     o = oracle.mr_lookup(start, end, lkey, off, ln, va_base=va_base, page_shift=page_shift)
-    g = gpu_lookup(start, end, lkey, off, ln, va_base=va_base, page_shift=page_shift)
+    g = gpu_lookup(start, end, lkey, off, ln, va_base=va_base, page_shift=page_shift,
+                   records=records)
     assert_lookup_equal(o, g, ctx)
     return o, g
 

@@ -42,7 +42,12 @@ def test_version_and_strerror():
 
 def test_workspace_sizes():
     ws = dd.workspace_bytes
-    assert ws(dd.OP_MR_LOOKUP, 1 << 20) == 0
+    # Lookup: no workspace up to 4,096 regions (the LDS kernel), then one
+    # 64-byte record per run of 4 regions.
+    assert ws(dd.OP_MR_LOOKUP, 1 << 20) == 0 and ws(dd.OP_MR_LOOKUP, 1 << 20, 4096) == 0
+    assert ws(dd.OP_MR_LOOKUP, 1 << 20, 4097) == 1025 * 64
+    assert ws(dd.OP_MR_LOOKUP, 0, 65536) == 16384 * 64
+    assert ws(dd.OP_MR_LOOKUP, 5, (1 << 31) - 1) == (1 << 29) * 64
     assert ws(dd.OP_BUILD_PRP, 0) == 0
     assert ws(dd.OP_PARTITION, 100, 0) == 0            # nqueues 0 is invalid
     assert ws(dd.OP_PARTITION, 100, 257) == 0          # above the maximum
@@ -83,6 +88,13 @@ def test_lookup_rejects_bad_arguments():
         args = list(ok)
         args[k] = bad
         assert f(*args) == EINVAL, (k, bad)
+    # A record workspace given for a large table must be big enough and
+    # 256-byte aligned (even for an empty batch); none at all is allowed.
+    need = dd.workspace_bytes(dd.OP_MR_LOOKUP, 0, 5000)
+    big = [P, P, P, 5000, 12, P, P, 0, 0, P, P, P, P, P]
+    assert f(*big, P, need - 1, NULL) == EINVAL
+    assert f(*big, P + 8, need, NULL) == EINVAL
+    assert f(*big, P, need, NULL) == 0 and f(*big, NULL, 0, NULL) == 0
 
 
 @no_gpu_only

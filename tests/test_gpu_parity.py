@@ -231,15 +231,39 @@ def _queries(rng, start, end, n):
     return np.asarray(off).astype(np.uint64), np.asarray(ln).astype(np.uint64)
 
 
-@pytest.mark.parametrize("count", [0, 1, 2, 63, 64, 65, 4096, 8192, 8193, 65536, 100_000])
+@pytest.mark.parametrize("count", [0, 1, 2, 63, 64, 65, 4096, 4097, 8192, 8193, 65536, 65537,
+                                   100_000, 262_147])
 @pytest.mark.parametrize("page_shift", [12, 16])
 def test_lookup_tables(count, page_shift):
+    # Above 4,096 regions both large-table paths: the record copy in a
+    # workspace (every 4th start in LDS up to 65,536 regions, then every
+    # 8th, 16th ... with a global narrowing step) and no workspace.
     rng = np.random.default_rng(count * 3 + page_shift)
     start, end = _table(rng, count)
     lkey = rng.integers(1, 1 << 32, size=count, dtype=np.uint64).astype(np.uint32)
     off, ln = _queries(rng, start, end, 30_011)
-    gc.check_lookup(start, end, lkey, off, ln, page_shift=page_shift,
-                    ctx=f"R={count} shift={page_shift}")
+    for records in ((True, False) if count > 4096 else (True,)):
+        gc.check_lookup(start, end, lkey, off, ln, page_shift=page_shift, records=records,
+                        ctx=f"R={count} shift={page_shift} records={records}")
+
+
+@pytest.mark.parametrize("page_shift", [13, 21, 30])
+def test_lookup_large_table_coarse_pages(page_shift):
+    # Pages larger than most regions: many starts share a page and few are
+    # page multiples, which the record path's page deltas and alignment bits
+    # must resolve exactly as the plain search does.
+    rng = np.random.default_rng(page_shift)
+    start, end = _table(rng, 20_000)
+    lkey = rng.integers(1, 1 << 32, size=20_000, dtype=np.uint64).astype(np.uint32)
+    off, ln = _queries(rng, start, end, 20_011)
+    p = 1 << page_shift
+    # Plus ranges that round exactly onto regions whose bounds are page multiples.
+    al = np.nonzero(((start % p) == 0) & ((end % p) == 0))[0]
+    off = np.concatenate([off, start[al], start[al] + np.uint64(1)])
+    ln = np.concatenate([ln, end[al] - start[al], np.maximum(end[al] - start[al] - 2, 1)])
+    for records in (True, False):
+        gc.check_lookup(start, end, lkey, off, ln, page_shift=page_shift, records=records,
+                        ctx=f"shift={page_shift} records={records}")
 
 
 def _spread_table(kind, count, rng):
@@ -292,7 +316,7 @@ def _queries_u64(rng, start, end, n):
 
 
 @pytest.mark.parametrize("kind", ["wide", "skewed", "even"])
-@pytest.mark.parametrize("count", [1, 3, 1000, 4096])
+@pytest.mark.parametrize("count", [1, 3, 1000, 4096, 20_001])
 def test_lookup_bucket_spreads(kind, count):
     rng = np.random.default_rng(count + len(kind))
     start, end = _spread_table(kind, count, rng)
@@ -308,7 +332,9 @@ def test_lookup_bucket_spreads(kind, count):
         extra_ln += [e - s, 4096, 4096, 4096]
     off = np.concatenate([off, np.array(extra_off, np.uint64)])
     ln = np.concatenate([ln, np.array(extra_ln, np.uint64)])
-    gc.check_lookup(start, end, lkey, off, ln, ctx=f"{kind} R={count}")
+    for records in ((True, False) if count > 4096 else (True,)):
+        gc.check_lookup(start, end, lkey, off, ln, records=records,
+                        ctx=f"{kind} R={count} records={records}")
 
 
 def test_lookup_invalid_and_va_base():
@@ -323,12 +349,14 @@ def test_lookup_invalid_and_va_base():
     gc.check_lookup(start, end, lkey, off, ln, page_shift=30, ctx="shift30")
 
 
-def test_lookup_unaligned_columns():
+@pytest.mark.parametrize("count", [1000, 20_000])
+def test_lookup_unaligned_columns(count):
     """Columns that start 8 bytes (1 byte for kind) past an aligned address take
-    the element-by-element path and must give the same answers."""
+    the element-by-element path and must give the same answers (LDS table and
+    record path)."""
     rng = np.random.default_rng(41)
-    start, end = _table(rng, 1000)
-    lkey = rng.integers(1, 1 << 32, size=1000, dtype=np.uint64).astype(np.uint32)
+    start, end = _table(rng, count)
+    lkey = rng.integers(1, 1 << 32, size=count, dtype=np.uint64).astype(np.uint32)
     off, ln = _queries(rng, start, end, 5003)
     n = off.shape[0]
     o = oracle.mr_lookup(start, end, lkey, off, ln)
