@@ -23,6 +23,8 @@ Prints ONE JSON line:
   per_config   Tiny, Small-I/O, Large/chaining and MR-heavy, each with its own
                functions, median/min/p95 over >= 20 iterations (>= 200 for
                Tiny and Small)
+  split_alone  dmadesc_partition_by_queue alone over 64 and 256 Zipf queues
+               (the two rankings)
   emit_sqe, registry, build_put, cq_mirror: the stages beside the path,
                timed after the steps
   cpu_baseline the single-threaded oracle, per function and end to end,
@@ -348,6 +350,34 @@ def emit_stage(dd, d, np, torch, prp_out, sp_out, ln, reps):
             "algorithmic_bytes_per_launch": nbytes, "achieved_gbs": round(gbs, 1),
             "frac": round(gbs / PEAK_HBM_GBS, 4),
             "entries_per_s": round(n_placed / (ms * 1e-3), 1)}
+
+
+def split_stage(dd, np, torch, n, reps):
+    """Times dmadesc_partition_by_queue alone on n requests with Zipf(1.1)
+    queue ids over 64 queues (LDS-counter ranking, as in the step) and over
+    256 queues (ballot ranking); algorithmic bytes: qid read, perm written,
+    the offsets."""
+    import synth
+    out = {}
+    for nq in (64, 256):
+        qid = torch.from_numpy(synth.queue_ids(n, nq, seed=nq)).to("cuda")
+        ws = torch.empty(dd.workspace_bytes(dd.OP_PARTITION, n, nq), dtype=torch.uint8,
+                         device="cuda")
+        res = {"o": None}
+
+        def call():
+            res["o"] = dd.partition_by_queue(qid, nq, out=res["o"], ws=ws, check=False)
+        ms = timed_iters(torch, np, call, reps)
+        d = dist(np, ms)
+        nbytes = 8 * n + 8 * (nq + 2)
+        out[f"nq{nq}"] = {"ranking": "lds_counters" if nq <= 70 else "ballots",
+                          "requests": n, **d,
+                          "requests_per_s": round(n / (d["median_ms"] * 1e-3), 1),
+                          "algorithmic_bytes": nbytes,
+                          "achieved_gbs": round(nbytes / (d["median_ms"] * 1e-3) / 1e9, 1),
+                          "frac": round(nbytes / (d["median_ms"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+        del qid, ws
+    return out
 
 
 def put_stage(dd, np, torch, n, reps):
@@ -782,6 +812,8 @@ def main():
         result["emit_sqe"] = emit_stage(dd, d, np, torch, st.pr, st.sp, st.ln, args.emit_reps)
     if d["regions"] and args.emit_reps > 0:
         result["registry"] = registry_stage(dd, d, np, torch, 10)
+    if nq and args.emit_reps > 0:
+        result["split_alone"] = split_stage(dd, np, torch, n, max(args.emit_reps, 20))
     if args.emit_reps > 0:
         result["build_put"] = put_stage(dd, np, torch, n, args.emit_reps)
     if args.emit_reps > 0:

@@ -128,6 +128,20 @@ def slba(name: str, n: int, seed: int = 0) -> np.ndarray:
     return out
 
 
+QID_STREAM = 0x51D_51D_51D_51D
+
+
+def queue_ids(n: int, nqueues: int, seed: int = 0, exponent: float = 1.1) -> np.ndarray:
+    """Seeded destination queues for `n` requests: Zipf over `nqueues` queues
+    with the given exponent (the Mixed workload's 1.1 over 64), drawn by
+    inverting the cumulative weights with SplitMix64 uniforms."""
+    w = np.arange(1, nqueues + 1, dtype=np.float64) ** -exponent
+    cdf = np.cumsum(w) / w.sum()
+    u = (splitmix64((seed or QID_STREAM) ^ QID_STREAM, n) >> np.uint64(11)).astype(np.float64) \
+        / float(1 << 53)
+    return np.minimum(np.searchsorted(cdf, u, side="right"), nqueues - 1).astype(np.uint32)
+
+
 PUT_HEAP = 256 << 30          # symmetric heap of the put workload
 PUT_CHUNK_SHIFT = 21          # 2 MiB chunks
 PUT_NPES = 8

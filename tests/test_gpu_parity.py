@@ -401,6 +401,16 @@ def test_split_sizes(nq, n):
     gc.check_split(qid, nq, ctx=f"nq={nq} n={n}")
 
 
+@pytest.mark.parametrize("nq", [71, 256])
+def test_split_full_size_ballot_path(nq):
+    # The ballot ranking (above 70 queues) at the Mixed batch size, Zipf ids
+    # (a few dense buckets, many sparse ones) and some overflow ids.
+    n = synth.shape("mixed")["n"]
+    qid = synth.queue_ids(n, nq, seed=nq)
+    qid[::100_003] = np.uint32(nq + 5)
+    gc.check_split(qid, nq, ctx=f"full size nq={nq}")
+
+
 @pytest.mark.parametrize("nq", [64, 256])
 def test_split_unaligned_qid(nq):
     """A queue-id column 4 bytes past a 16-byte boundary takes the scalar loads."""
