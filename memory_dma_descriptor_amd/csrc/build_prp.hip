@@ -302,6 +302,19 @@ __device__ __forceinline__ void wave_sync_lds()
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// Reads through explicitly typed pointers. Where a branch chooses between a
+// staged (LDS) copy of the table and the table itself, plain reads let the
+// compiler merge both into one generic-pointer (flat) load, which also counts
+// against the LDS counter; loads of different address spaces cannot merge.
+__device__ __forceinline__ uint64_t lds_read(const uint64_t *p)
+{
+    return *(const __attribute__((address_space(3))) uint64_t *)p;
+}
+__device__ __forceinline__ uint64_t global_read(const uint64_t *p)
+{
+    return *(const __attribute__((address_space(1))) uint64_t *)p;
+}
+
 // Writes the list runs of the wave's 64 requests of one round. Lane k's
 // request is described by (xb, word, ent, lp); ent == 0 for no list.
 __device__ __forceinline__ void emit_round_wide(RoundTable &T, uint64_t xb, uint64_t word, uint64_t ent,
@@ -356,11 +369,11 @@ __device__ __forceinline__ void emit_round_wide(RoundTable &T, uint64_t xb, uint
         if (nd) {
             if (staged) {
                 const uint64_t fs = T.foff[r] + f - (xr >> 16);
-                l0 = T.lut[fs];
-                l1 = two ? T.lut[fs + 1] : l0;
+                l0 = lds_read(&T.lut[fs]);
+                l1 = two ? lds_read(&T.lut[fs + 1]) : l0;
             } else {
-                l0 = lut[f];
-                l1 = two ? lut[f + 1] : l0;
+                l0 = global_read(&lut[f]);
+                l1 = two ? global_read(&lut[f + 1]) : l0;
             }
         }
         uint64_t v[4];
@@ -400,11 +413,11 @@ __device__ __forceinline__ void fast_group(const FastTable &T, uint32_t g, int r
     if (nd) {
         const bool two = (u + nd - 1u) >= 16u;
         if (kStaged) {
-            l0 = T.lut[R.fbase + fi];
-            l1 = two ? T.lut[R.fbase + fi + 1] : l0;
+            l0 = lds_read(&T.lut[R.fbase + fi]);
+            l1 = two ? lds_read(&T.lut[R.fbase + fi + 1]) : l0;
         } else {
-            l0 = lut[R.f0 + fi];
-            l1 = two ? lut[R.f0 + fi + 1] : l0;
+            l0 = global_read(&lut[R.f0 + fi]);
+            l1 = two ? global_read(&lut[R.f0 + fi + 1]) : l0;
         }
     }
     uint64_t v[2];

@@ -205,6 +205,8 @@ __global__ __launch_bounds__(kThreads) void k_sqe_count(SqeArgs a, SqeWs ws)
 __global__ __launch_bounds__(kThreads) void k_sqe_emit(SqeArgs a, SqeWs ws)
 {
     __shared__ uint32_t s_cnt[kRounds][kWaves];
+    // A wave's entries of one round, by rank: 64 x 64 bytes per wave.
+    __shared__ uint4 s_ent[kWaves][kWave * 4];
     uint32_t q, t;
     if (!tile_of(ws, q, t)) return;                    // uniform over the block
     const Window win = window_of(a, q);
@@ -246,9 +248,22 @@ __global__ __launch_bounds__(kThreads) void k_sqe_emit(SqeArgs a, SqeWs ws)
     }
     __syncthreads();
 
+    // Each round: the wave's placeable requests take consecutive slots (from
+    // s0, wrapping at the ring's end) in lane order. A lane builds its entry
+    // in the wave's LDS area at its rank; then lane l copies 16-byte quarter
+    // l % 4 of entries l / 4, l / 4 + 16, ... to the ring, so each store
+    // instruction writes 16 whole entries (1 KiB) back to back instead of
+    // one quarter of 64 entries 64 bytes apart.
     const uint64_t below = __lanemask_lt();
     uint32_t run = before;                             // placeable before round k
-    uint4 *ring = reinterpret_cast<uint4 *>(win.ring);
+    // The ring address comes from memory, so the compiler cannot infer its
+    // address space; as a generic pointer its stores would be flat stores,
+    // which also count against the LDS counter and so make every staging
+    // read wait for them. Rings are device (global) memory.
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(1))) u32x4 global_u32x4;
+    global_u32x4 *ring = (global_u32x4 *)(uintptr_t)win.ring;
+    uint4 *ent = s_ent[w];
 #pragma unroll
     for (int k = 0; k < kRounds; ++k) {
         uint32_t wpre = 0, rtot = 0;
@@ -258,11 +273,14 @@ __global__ __launch_bounds__(kThreads) void k_sqe_emit(SqeArgs a, SqeWs ws)
             wpre += v < w ? c : 0u;
             rtot += c;
         }
+        uint32_t s0 = win.tail + run + wpre;           // slot of the wave's rank 0
+        if (s0 >= win.depth) s0 -= win.depth;          // tail < depth, rank < depth - 1
         if ((m[k] >> ln) & 1u) {
-            uint32_t s = win.tail + run + wpre + (uint32_t)__popcll(m[k] & below);
-            if (s >= win.depth) s -= win.depth;        // tail < depth, rank < depth - 1
+            const uint32_t r = (uint32_t)__popcll(m[k] & below);
+            uint32_t s = s0 + r;
+            if (s >= win.depth) s -= win.depth;
             const uint32_t nlb0 = (uint32_t)(len[k] >> a.lba_shift) - 1u;
-            uint4 *e = ring + (uint64_t)s * 4;
+            uint4 *e = ent + r * 4;
             e[0] = make_uint4(a.opcode | (s << 16), a.nsid, 0u, 0u);
             e[1] = make_uint4(0u, 0u, (uint32_t)p1[k], (uint32_t)(p1[k] >> 32));
             e[2] = make_uint4((uint32_t)p2[k], (uint32_t)(p2[k] >> 32), (uint32_t)lba[k],
@@ -270,6 +288,24 @@ __global__ __launch_bounds__(kThreads) void k_sqe_emit(SqeArgs a, SqeWs ws)
             e[3] = make_uint4(nlb0, 0u, 0u, 0u);
             if (a.req_of_slot) a.req_of_slot[(uint64_t)q * DMADESC_SQ_MAX_DEPTH + s] = idx[k];
         }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        const uint32_t cw = (uint32_t)__popcll(m[k]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const uint32_t r = (uint32_t)(ln >> 2) + 16u * j;
+            if (r < cw) {
+                uint32_t s = s0 + r;
+                if (s >= win.depth) s -= win.depth;
+                const uint4 x = ent[r * 4 + (ln & 3)];
+                ring[(uint64_t)s * 4 + (ln & 3)] = u32x4{x.x, x.y, x.z, x.w};
+            }
+        }
+        // The next round reuses the area: its writes wait for these reads.
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         run += rtot;
     }
 }
