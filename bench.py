@@ -20,9 +20,12 @@ Prints ONE JSON line:
                sampled timed steps (per_call_ms likewise)
   batch_call   dmadesc_build_batch (lookup, PRP build and split in one call
                that reads the request columns once) on the same batch
+  graph_step   the step's calls captured once in a HIP graph and replayed
+               (median/min/p95 of replays): the device time without the
+               host's per-call launch cost
   per_config   Tiny, Small-I/O, Large/chaining and MR-heavy, each with its own
                functions, median/min/p95 over >= 20 iterations (>= 200 for
-               Tiny and Small)
+               Tiny and Small), eager and as graph replays
   split_alone  dmadesc_partition_by_queue alone over 64 and 256 Zipf queues
                (the two rankings)
   emit_sqe, registry, build_put, cq_mirror: the stages beside the path,
@@ -256,6 +259,23 @@ class Step:
         return res
 
 
+def graph_step(torch, np, st, reps):
+    """The step's calls captured once in a HIP graph and replayed reps times
+    (each replay bracketed by events): the device time of the step without
+    the host's per-call launch cost, which dominates small batches."""
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        st.run()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        st.run()
+    ms = timed_iters(torch, np, g.replay, reps)
+    return g, ms
+
+
 def run_config(dd, torch, np, name, reps, packed=True):
     """One workload with its own functions (lookup, PRP build, split as it
     has them): median/min/p95 of reps steps, per-call medians, rates."""
@@ -295,6 +315,12 @@ def run_config(dd, torch, np, name, reps, packed=True):
         out["lookup_call"] = {"regions": d["regions"], "algorithmic_bytes": ab["lookup"],
                               "gbs": round(ab["lookup"] / (lm * 1e-3) / 1e9, 1),
                               "frac": round(ab["lookup"] / (lm * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+    g, gms = graph_step(torch, np, st, reps)
+    gmed = float(np.median(gms))
+    out["graph_step"] = {**dist(np, gms), "requests_per_s": round(d["n"] / (gmed * 1e-3), 1),
+                         "algorithmic_gbs": round(nbytes / (gmed * 1e-3) / 1e9, 1),
+                         "frac_of_peak": round(nbytes / (gmed * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+    del g
     out.update(st.check_outputs(np))
     return out
 
@@ -730,6 +756,16 @@ def main():
     step_bytes, step_sum = ab[f"step_{layout}"], ab[f"step_sum_{layout}"]
     step_med = float(np.median(step_ms))
 
+    # The same calls captured in a HIP graph and replayed.
+    graph = None
+    if not args.quick:
+        g, gms = graph_step(torch, np, st, max(args.dist_steps, 20))
+        g_med = float(np.median(gms))
+        graph = {**dist(np, gms), "requests_per_s": round(n / (g_med * 1e-3), 1),
+                 "algorithmic_gbs": round(step_bytes / (g_med * 1e-3) / 1e9, 1),
+                 "frac_of_peak": round(step_bytes / (g_med * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+        del g
+
     # The same step as one dmadesc_build_batch call, checked against the
     # separate calls' outputs (which are those of the last step).
     batch = None
@@ -794,6 +830,8 @@ def main():
         "prp_entries_per_s": round(ab["prp_entries"] * args.steps / elapsed, 1),
         "checks": checks,
     }
+    if graph:
+        result["graph_step"] = graph
     if batch:
         result["batch_call"] = batch
     if other:
