@@ -315,6 +315,14 @@ def run_config(dd, torch, np, name, reps, packed=True):
         out["lookup_call"] = {"regions": d["regions"], "algorithmic_bytes": ab["lookup"],
                               "gbs": round(ab["lookup"] / (lm * 1e-3) / 1e9, 1),
                               "frac": round(ab["lookup"] / (lm * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+    if d["lut_entries"] and d["nqueues"]:
+        # The same step as one dmadesc_build_batch call (four kernels
+        # instead of six: the difference that matters for small batches).
+        bms = timed_iters(torch, np, st.batch, reps)
+        bmed = float(np.median(bms))
+        out["batch_call"] = {**dist(np, bms), "requests_per_s": round(d["n"] / (bmed * 1e-3), 1),
+                             "algorithmic_gbs": round(nbytes / (bmed * 1e-3) / 1e9, 1),
+                             "frac_of_peak": round(nbytes / (bmed * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
     g, gms = graph_step(torch, np, st, reps)
     gmed = float(np.median(gms))
     out["graph_step"] = {**dist(np, gms), "requests_per_s": round(d["n"] / (gmed * 1e-3), 1),
