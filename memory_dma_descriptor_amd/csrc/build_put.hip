@@ -18,13 +18,16 @@
 // boundaries crossed + destination boundaries crossed - the shared ones (all
 // of them when a == b). Every descriptor is therefore computed on its own.
 //
-// One pass: 1,024 requests per block; the descriptor slots of a request are a
-// device-wide exclusive scan of the piece counts in request order (decoupled
-// look-back, dd_lookback.hpp); then each wave writes the descriptors of its 64
-// consecutive requests as one contiguous range, load-balanced over descriptors:
-// lane j of a step takes descriptor S + 64 j + lane and finds its request by a
-// 6-step search over the requests' first slots in LDS; a step's 64
-// descriptors go out through LDS as two 1 KiB store instructions.
+// One pass: 1,024 requests per block, 256 consecutive ones per wave; the
+// descriptor slots of a request are a device-wide exclusive scan of the piece
+// counts in request order (decoupled look-back, dd_lookback.hpp); then each
+// wave writes the descriptors of its requests in two halves of 128, each one
+// contiguous range, load-balanced over descriptors: lane j of a step takes
+// descriptor S + 64 j + lane and finds its request by a 7-step search over
+// the requests' first slots in LDS. The key reads of up to kSub steps are
+// issued before any of them is used, so a half waits about one gather round
+// trip, not one per step; a step's 64 descriptors go out through LDS as two
+// 1 KiB store instructions.
 #include "dd_device.hpp"
 #include "dd_internal.h"
 #include "dd_lookback.hpp"
@@ -63,11 +66,13 @@ __device__ __forceinline__ uint64_t put_boundary(uint64_t s, uint64_t d, uint32_
     return ((j & 1) ? hi : lo) + ((j >> 1) << shift);
 }
 
+constexpr int kHalf = 2 * kWave;          // requests per emission table
+constexpr int kSub = 4;                   // descriptor steps whose key reads fly together
+
 struct PutTab {
-    uint64_t start[kWave + 1];   // first descriptor slot of each request ([64]: end)
-    uint64_t s[kWave], d[kWave], b[kWave];
-    uint32_t pe[kWave];
-    uint32_t req[kWave];
+    uint64_t start[kHalf + 1];   // first descriptor slot of each request ([kHalf]: end)
+    uint64_t s[kHalf], d[kHalf], b[kHalf];
+    uint32_t pe[kHalf];
     u64x2 out[2 * kWave];        // one step's 64 descriptors, in order, for the stores
 };
 
@@ -79,71 +84,91 @@ struct PutKeys {
     uint32_t shift;
 };
 
-// Writes the descriptors of the wave's 64 requests of one round (lane k: one
-// request, m descriptors from slot first; m == 0 for none).
-__device__ __forceinline__ void emit_put_round(PutTab &T, uint64_t first, uint64_t m, uint64_t s,
-                                               uint64_t d, uint64_t b, uint32_t pe, uint32_t req,
-                                               const PutKeys &K, uint64_t *__restrict__ desc)
+__device__ __forceinline__ void wave_fence()
 {
-    const int ln = lane();
-    const uint64_t has = __ballot(m != 0);
-    if (has == 0) return;                                // uniform per wave
-    const int lo = __ffsll((unsigned long long)has) - 1;
-    const int hi = 63 - __clzll((unsigned long long)has);
-    const uint64_t S = __shfl(first, lo, kWave);
-    const uint64_t E = __shfl(first + m, hi, kWave);
-    // Requests before the first one with descriptors start at S; those after
-    // the last one (none, or refused) at E: the search never picks them.
-    T.start[ln] = first < S ? S : (first > E ? E : first);
-    if (ln == kWave - 1) T.start[kWave] = E;
-    T.s[ln] = s;
-    T.d[ln] = d;
-    T.b[ln] = b;
-    T.pe[ln] = pe;
-    T.req[ln] = req;
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    for (uint64_t c = S; c < E; c += kWave) {             // uniform per wave
-        // Lanes past the end compute the last descriptor again; not stored.
-        const uint64_t p = c + ln < E ? c + ln : E - 1;
-        const int r = owner_of<kWave>(T.start, p);
-        const uint64_t j = p - T.start[r];
-        const uint64_t rs = T.s[r], rd = T.d[r], rb = T.b[r];
-        const uint32_t rpe = T.pe[r];
-        const uint64_t x0 = j ? put_boundary(rs, rd, K.shift, j - 1) : 0;
-        uint64_t x1 = put_boundary(rs, rd, K.shift, j);
-        x1 = x1 < rb ? x1 : rb;
-        uint32_t lkey, rkey;
-        if (K.shift) {
-            lkey = K.lkeys[(rs + x0) >> K.shift];
-            rkey = K.rkeys[(uint64_t)rpe * K.nchunks + ((rd + x0) >> K.shift)];
-        } else {
-            lkey = K.lkeys[0];
-            rkey = K.rkeys[rpe];
-        }
-        const uint64_t w2 = (x1 - x0) | ((uint64_t)lkey << 32);
-        const uint64_t w3 = rkey | ((uint64_t)T.req[r] << 32);
-        // Through LDS, so that each of the wave's two 16-byte store
-        // instructions covers 1 KiB contiguously (a lane storing its own
-        // 32-byte descriptor would fill half of every 32 bytes per
-        // instruction, which non-temporal stores pay for twice).
-        T.out[2 * ln] = u64x2{K.local_base + rs + x0, K.peer_base[rpe] + rd + x0};
-        T.out[2 * ln + 1] = u64x2{w2, w3};
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        const u64x2 h0 = T.out[ln], h1 = T.out[kWave + ln];
-        u64x2 *dst = reinterpret_cast<u64x2 *>(desc + 4 * c);
-        if (c + (ln >> 1) < E) __builtin_nontemporal_store(h0, dst + ln);
-        if (c + kWave / 2 + (ln >> 1) < E) __builtin_nontemporal_store(h1, dst + kWave + ln);
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");   // out is rewritten next
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Writes the descriptors of 128 consecutive requests, request r = 64 h + lane
+// for h = 0, 1 (first[h], m[h] descriptors from slot first[h]; m == 0 for
+// none); req0 is the index of request 0.
+__device__ __forceinline__ void emit_put_half(PutTab &T, const uint64_t (&first)[2],
+                                              const uint64_t (&m)[2], const uint64_t (&s)[2],
+                                              const uint64_t (&d)[2], const uint64_t (&b)[2],
+                                              const uint32_t (&pe)[2], uint64_t req0,
+                                              const PutKeys &K, uint64_t *__restrict__ desc)
+{
+    const int ln = lane();
+    const uint64_t has0 = __ballot(m[0] != 0), has1 = __ballot(m[1] != 0);
+    if ((has0 | has1) == 0) return;                      // uniform per wave
+    const uint64_t S = has0 ? __shfl(first[0], __ffsll((unsigned long long)has0) - 1, kWave)
+                            : __shfl(first[1], __ffsll((unsigned long long)has1) - 1, kWave);
+    const uint64_t E = has1 ? __shfl(first[1] + m[1], 63 - __clzll((unsigned long long)has1), kWave)
+                            : __shfl(first[0] + m[0], 63 - __clzll((unsigned long long)has0), kWave);
+    // Requests before the first one with descriptors start at S; those after
+    // the last one (none, or refused) at E: the search never picks them.
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int r = h * kWave + ln;
+        T.start[r] = first[h] < S ? S : (first[h] > E ? E : first[h]);
+        T.s[r] = s[h];
+        T.d[r] = d[h];
+        T.b[r] = b[h];
+        T.pe[r] = pe[h];
     }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");   // the next round rewrites T
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    if (ln == kWave - 1) T.start[kHalf] = E;
+    wave_fence();
+    for (uint64_t c = S; c < E; c += (uint64_t)kSub * kWave) {   // uniform per wave
+        // Every step's descriptor and key reads first (lanes past the end
+        // compute the last descriptor again; not stored).
+        int r[kSub];
+        uint64_t x0[kSub], x1[kSub], pb[kSub];
+        uint32_t lkey[kSub], rkey[kSub];
+#pragma unroll
+        for (int u = 0; u < kSub; ++u) {
+            const uint64_t pu = c + (uint64_t)u * kWave + ln;
+            const uint64_t p = pu < E ? pu : E - 1;
+            r[u] = owner_of<kHalf>(T.start, p);
+            const uint64_t j = p - T.start[r[u]];
+            const uint64_t rs = T.s[r[u]], rd = T.d[r[u]], rb = T.b[r[u]];
+            const uint32_t rpe = T.pe[r[u]];
+            x0[u] = j ? put_boundary(rs, rd, K.shift, j - 1) : 0;
+            const uint64_t e = put_boundary(rs, rd, K.shift, j);
+            x1[u] = e < rb ? e : rb;
+            // Key indices without a branch (a static heap has one local key
+            // and one remote key per PE: nchunks is 1 and the chunk is 0),
+            // so all of the steps' reads are in flight together; behind a
+            // branch each join waited for every read issued before it.
+            const uint64_t lc = K.shift ? (rs + x0[u]) >> K.shift : 0;
+            const uint64_t rc = K.shift ? (rd + x0[u]) >> K.shift : 0;
+            lkey[u] = K.lkeys[lc];
+            rkey[u] = K.rkeys[(uint64_t)rpe * K.nchunks + rc];
+            pb[u] = K.peer_base[rpe];
+        }
+#pragma unroll
+        for (int u = 0; u < kSub; ++u) {
+            const uint64_t cu = c + (uint64_t)u * kWave;
+            if (cu >= E) break;                              // uniform per wave
+            const uint64_t rs = T.s[r[u]], rd = T.d[r[u]];
+            const uint64_t w2 = (x1[u] - x0[u]) | ((uint64_t)lkey[u] << 32);
+            const uint64_t w3 = rkey[u] | ((req0 + (uint64_t)r[u]) << 32);
+            // Through LDS, so that each of the wave's two 16-byte store
+            // instructions covers 1 KiB contiguously (a lane storing its own
+            // 32-byte descriptor would fill half of every 32 bytes per
+            // instruction, which non-temporal stores pay for twice).
+            T.out[2 * ln] = u64x2{K.local_base + rs + x0[u], pb[u] + rd + x0[u]};
+            T.out[2 * ln + 1] = u64x2{w2, w3};
+            wave_fence();
+            const u64x2 h0 = T.out[ln], h1 = T.out[kWave + ln];
+            u64x2 *dst = reinterpret_cast<u64x2 *>(desc + 4 * cu);
+            if (cu + (ln >> 1) < E) __builtin_nontemporal_store(h0, dst + ln);
+            if (cu + kWave / 2 + (ln >> 1) < E) __builtin_nontemporal_store(h1, dst + kWave + ln);
+            wave_fence();                                    // out is rewritten next
+        }
+    }
+    wave_fence();                                            // the next half rewrites T
 }
 
 __global__ __launch_bounds__(kThreads) void k_put_build(
@@ -154,7 +179,7 @@ __global__ __launch_bounds__(kThreads) void k_put_build(
     uint8_t *__restrict__ status, uint64_t *__restrict__ total, uint64_t nblocks,
     Header *__restrict__ hdr, uint64_t *__restrict__ bstat, uint32_t max_polls)
 {
-    __shared__ uint64_t s_red[kItems * kWaves];
+    __shared__ uint64_t s_red[kWaves];
     __shared__ uint64_t s_bid, s_excl;
     __shared__ uint32_t s_dead;
     __shared__ PutTab s_tab[kWaves];
@@ -163,19 +188,37 @@ __global__ __launch_bounds__(kThreads) void k_put_build(
     __syncthreads();
     const uint64_t blk = s_bid;
     const uint64_t base = blk * kTile;
+    // Wave w owns requests wbase .. wbase + 255; item k of a lane is request
+    // wbase + 64 k + lane (request order is (wave, item, lane) order).
+    const uint64_t wbase = base + (uint64_t)w * (kWave * kItems);
+    const bool full = base + kTile <= n;                 // uniform per block
 
     uint64_t s[kItems], d[kItems], b[kItems], cnt[kItems], pre[kItems];
     uint32_t q[kItems];
     uint8_t st[kItems];
+    if (full) {
+        // Every load in flight at once (a guarded load would wait for the
+        // one before it).
 #pragma unroll
-    for (int k = 0; k < kItems; ++k) {
-        const uint64_t i = base + (uint64_t)k * kThreads + t;
-        const bool in = i < n;
-        s[k] = in ? __builtin_nontemporal_load(src + i) : 0;
-        d[k] = in ? __builtin_nontemporal_load(dst + i) : 0;
-        b[k] = in ? __builtin_nontemporal_load(bytes + i) : 0;
-        q[k] = in ? __builtin_nontemporal_load(pe + i) : 0;
+        for (int k = 0; k < kItems; ++k) {
+            const uint64_t i = wbase + (uint64_t)k * kWave + ln;
+            s[k] = __builtin_nontemporal_load(src + i);
+            d[k] = __builtin_nontemporal_load(dst + i);
+            b[k] = __builtin_nontemporal_load(bytes + i);
+            q[k] = __builtin_nontemporal_load(pe + i);
+        }
+    } else {
+#pragma unroll
+        for (int k = 0; k < kItems; ++k) {
+            const uint64_t i = wbase + (uint64_t)k * kWave + ln;
+            const bool in = i < n;
+            s[k] = in ? src[i] : 0;
+            d[k] = in ? dst[i] : 0;
+            b[k] = in ? bytes[i] : 0;
+            q[k] = in ? pe[i] : 0;
+        }
     }
+    uint64_t carry = 0;                                  // the wave's pieces before item k
 #pragma unroll
     for (int k = 0; k < kItems; ++k) {
         st[k] = kOk;
@@ -183,22 +226,17 @@ __global__ __launch_bounds__(kThreads) void k_put_build(
         else if (b[k] > heap || s[k] > heap - b[k] || d[k] > heap - b[k]) st[k] = kErange;
         cnt[k] = st[k] == kOk ? put_pieces(s[k], d[k], b[k], K.shift) : 0;
         const uint64_t inc = wave_incl_scan(cnt[k]);
-        pre[k] = inc - cnt[k];
-        if (ln == kWave - 1) s_red[k * kWaves + w] = inc;
+        pre[k] = carry + inc - cnt[k];
+        carry += __shfl(inc, kWave - 1, kWave);
     }
+    if (ln == 0) s_red[w] = carry;
     __syncthreads();
-    uint64_t agg = 0;
+    uint64_t agg = 0, wpre = 0;
 #pragma unroll
-    for (int k = 0; k < kItems; ++k) {
-        uint64_t before = 0, all = 0;
-#pragma unroll
-        for (int v = 0; v < kWaves; ++v) {
-            const uint64_t x = s_red[k * kWaves + v];
-            before += v < w ? x : 0ull;
-            all += x;
-        }
-        pre[k] += agg + before;
-        agg += all;
+    for (int v = 0; v < kWaves; ++v) {
+        const uint64_t x = s_red[v];
+        wpre += v < w ? x : 0ull;
+        agg += x;
     }
     if (w == 0) {
         uint64_t excl = 0;
@@ -219,27 +257,35 @@ __global__ __launch_bounds__(kThreads) void k_put_build(
         }
     }
     __syncthreads();
-    const uint64_t excl = s_excl;
+    const uint64_t excl = s_excl + wpre;
     const bool dead = s_dead != 0;
 
-#pragma unroll 1
+    uint64_t f[kItems], m[kItems];
+#pragma unroll
     for (int k = 0; k < kItems; ++k) {
-        const uint64_t i = base + (uint64_t)k * kThreads + t;
-        uint64_t f = excl + pre[k];
+        const uint64_t i = wbase + (uint64_t)k * kWave + ln;
+        f[k] = excl + pre[k];
         uint8_t sk = st[k];
         if (cnt[k] != 0 && dead) {
             sk = kEbusy;                                      // its slots are unknown
-            f = ~0ull;
-        } else if (cnt[k] != 0 && f + cnt[k] > cap) {
+            f[k] = ~0ull;
+        } else if (cnt[k] != 0 && f[k] + cnt[k] > cap) {
             sk = kEnospc;                                     // refused; its slots stay taken
         }
+        m[k] = sk == kOk ? cnt[k] : 0;
         if (i < n) {
-            __builtin_nontemporal_store(f, first_out + i);
+            __builtin_nontemporal_store(f[k], first_out + i);
             __builtin_nontemporal_store((uint32_t)cnt[k], count_out + i);
             __builtin_nontemporal_store(sk, status + i);
         }
-        emit_put_round(s_tab[w], f, sk == kOk ? cnt[k] : 0, s[k], d[k], b[k], q[k],
-                       (uint32_t)i, K, desc);
+    }
+#pragma unroll 1
+    for (int h = 0; h < kItems / 2; ++h) {
+        const uint64_t fh[2] = {f[2 * h], f[2 * h + 1]}, mh[2] = {m[2 * h], m[2 * h + 1]};
+        const uint64_t sh[2] = {s[2 * h], s[2 * h + 1]}, dh[2] = {d[2 * h], d[2 * h + 1]};
+        const uint64_t bh[2] = {b[2 * h], b[2 * h + 1]};
+        const uint32_t qh[2] = {q[2 * h], q[2 * h + 1]};
+        emit_put_half(s_tab[w], fh, mh, sh, dh, bh, qh, wbase + (uint64_t)h * kHalf, K, desc);
     }
 }
 
