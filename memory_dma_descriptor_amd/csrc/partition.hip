@@ -260,7 +260,10 @@ __device__ __forceinline__ uint32_t chunk_of(int t)
     return (uint32_t)(w * kWave + 2 * (l & 31) + (l >> 5));
 }
 
-template <int kItems>
+// kSingle: the whole batch is this one tile (the histogram and column scan
+// are then not launched): the bucket totals and their starts in perm are the
+// tile's own, from its counter scan.
+template <int kItems, bool kSingle>
 __global__ __launch_bounds__(kThreads) void k_split_scatter_cnt(
     const uint32_t *__restrict__ qid, uint64_t n, uint32_t nq, bool vec,
     const uint32_t *__restrict__ offs, const uint64_t *__restrict__ total,
@@ -344,17 +347,32 @@ __global__ __launch_bounds__(kThreads) void k_split_scatter_cnt(
 
     // Bucket starts: in the sorted tile (scan value of chunk 0), and in perm
     // (all buckets' batch totals scanned, plus the blocks before this one).
-    const uint64_t gv = (uint32_t)t < nbk ? total[t] : 0;
-    uint64_t gtot;
-    const uint64_t gex = block_excl_scan<kThreads>(gv, s_scr64, &gtot);
-    if ((uint32_t)t < nbk) {
-        s_lstart[t] = s_cnt[t * kThreads];
-        s_gpos[t] = gex + offs[(uint64_t)t * gridDim.x + blockIdx.x];
-        if (blockIdx.x == 0) qoff[t] = gex;
-    }
-    if (blockIdx.x == 0 && t == 0) {
-        qoff[nbk] = n;
-        *n_invalid = total[nq];
+    if constexpr (kSingle) {
+        // One tile: a bucket starts in perm where it starts in the tile; the
+        // spare bucket (past the batch) starts at n.
+        if ((uint32_t)t < nbk) {
+            const uint32_t st = s_cnt[t * kThreads];
+            s_lstart[t] = st;
+            s_gpos[t] = st;
+            qoff[t] = st;
+        }
+        if (t == 0) {
+            qoff[nbk] = n;
+            *n_invalid = n - (uint64_t)s_cnt[nq * kThreads];
+        }
+    } else {
+        const uint64_t gv = (uint32_t)t < nbk ? total[t] : 0;
+        uint64_t gtot;
+        const uint64_t gex = block_excl_scan<kThreads>(gv, s_scr64, &gtot);
+        if ((uint32_t)t < nbk) {
+            s_lstart[t] = s_cnt[t * kThreads];
+            s_gpos[t] = gex + offs[(uint64_t)t * gridDim.x + blockIdx.x];
+            if (blockIdx.x == 0) qoff[t] = gex;
+        }
+        if (blockIdx.x == 0 && t == 0) {
+            qoff[nbk] = n;
+            *n_invalid = total[nq];
+        }
     }
     uint32_t sidx[kItems];
 #pragma unroll
@@ -417,6 +435,14 @@ hipError_t launch_partition(const SplitArgs &a, hipStream_t s)
     const uint64_t tile = split_tile(a.nqueues);
     const uint64_t nb = (a.n + tile - 1) / tile;
     uint32_t *counts = static_cast<uint32_t *>(a.ws);
+    if (nb == 1 && a.nqueues <= kCntQueues) {
+        // One tile: the scatter alone (no histogram, no column scan).
+        const bool vec = (reinterpret_cast<uintptr_t>(a.qid) & 15u) == 0;
+        hipLaunchKernelGGL((k_split_scatter_cnt<kItemsCnt, true>), dim3(1), dim3(kThreads), 0, s,
+                           a.qid, a.n, a.nqueues, vec, counts, nullptr, a.perm, a.qoff,
+                           a.n_invalid);
+        return hipGetLastError();
+    }
     if (a.nqueues <= kCntQueues)
         hipLaunchKernelGGL(k_split_hist<kItemsCnt>, dim3((unsigned)nb), dim3(kThreads), 0, s,
                            a.qid, a.n, a.nqueues, nb, counts);
@@ -441,7 +467,7 @@ hipError_t launch_partition_counted(const SplitArgs &a, hipStream_t s)
                        counts, nb, nbk, total);
     if (cnt_path) {
         const bool vec = (reinterpret_cast<uintptr_t>(a.qid) & 15u) == 0;
-        hipLaunchKernelGGL(k_split_scatter_cnt<kItemsCnt>, dim3((unsigned)nb), dim3(kThreads), 0, s,
+        hipLaunchKernelGGL((k_split_scatter_cnt<kItemsCnt, false>), dim3((unsigned)nb), dim3(kThreads), 0, s,
                            a.qid, a.n, a.nqueues, vec, counts, total, a.perm, a.qoff,
                            a.n_invalid);
     } else {
