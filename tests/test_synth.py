@@ -65,3 +65,17 @@ def test_large_lengths():
     ln = d["len"]
     assert ln.min() >= 32 * 4096 and ln.max() <= 2048 * 4096 and (ln % 4096 == 0).all()
     assert (d["qid"] < 16).all()
+
+
+@pytest.mark.parametrize("nq", [1, 64, 71, 256])
+def test_queue_ids_zipf(nq):
+    # Seeded Zipf(1.1) queue ids (the split timed alone and tested at full
+    # size over 71 and 256 queues): in range, reproducible, and with each
+    # queue's share near its weight.
+    q = synth.queue_ids(400_000, nq, seed=nq)
+    assert q.dtype == np.uint32 and (q < nq).all()
+    assert np.array_equal(q, synth.queue_ids(400_000, nq, seed=nq))
+    assert not np.array_equal(q, synth.queue_ids(400_000, nq, seed=nq + 1)) or nq == 1
+    w = np.arange(1, nq + 1, dtype=float) ** -1.1
+    share = np.bincount(q, minlength=nq) / q.size
+    assert np.abs(share - w / w.sum()).max() < 0.004
