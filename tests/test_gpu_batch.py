@@ -197,3 +197,45 @@ def test_batch_rejects_bad_arguments():
     small = torch.empty(16, dtype=torch.uint8, device="cuda")
     with pytest.raises(ValueError):
         dd.build_batch(*args, 64, BUS, pool, ws=small)
+
+
+def _tiled_table(rng, va, span, count):
+    """`count` sorted, non-overlapping regions over [va, va + span), bounds on
+    64 KiB multiples (valid for every page size tested), random gaps."""
+    if count == 0:
+        z = np.zeros(0, np.uint64)
+        return z, z.copy(), np.zeros(0, np.uint32)
+    slot = max((span // count) & ~0xFFFF, 1 << 17)
+    k = np.arange(count, dtype=np.uint64)
+    start = np.uint64(va) + k * np.uint64(slot) + \
+        (rng.integers(0, 2, count).astype(np.uint64) << np.uint64(16))
+    size = rng.integers(1, slot >> 16, count).astype(np.uint64) << np.uint64(16)
+    end = np.minimum(start + size, np.uint64(va) + (k + np.uint64(1)) * np.uint64(slot))
+    lkey = rng.integers(1, 1 << 32, count, dtype=np.uint64).astype(np.uint32)
+    return start, end, lkey
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_shapes(seed):
+    """Seeded random batches: sizes, table sizes on both sides of the LDS
+    limit, queue counts on both sides of the ranking switch, page sizes and
+    both list layouts; the batch call and (for the same table) the lookup's
+    record and plain paths against the oracle."""
+    rng = np.random.default_rng(7000 + seed)
+    name = ("small", "mixed")[seed % 2]
+    n = int(rng.integers(1, 60_000))
+    d = synth.generate(name, n=n, seed=seed + 1)
+    R = int(rng.choice([0, 1, 17, 1000, 4096, 4097, 9000, 20_000]))
+    heap = d["lut_entries"] << 16
+    rs, re_, rk = _tiled_table(rng, d["va_base"], heap, R)
+    nq = int(rng.choice([1, 5, 64, 70, 71, 200, 256]))
+    qid = synth.queue_ids(n, nq, seed=seed + 3)
+    qid[rng.random(n) < 0.01] = np.uint32(nq + 1)
+    ps = int(rng.choice([12, 13, 16]))
+    packed = bool(rng.integers(0, 2))
+    d.update(rstart=rs, rend=re_, rlkey=rk)
+    check_batch(d, nq, packed=packed, qid=qid, page_shift=ps,
+                ctx=f"seed={seed} {name} n={n} R={R} nq={nq} shift={ps} packed={packed}")
+    for records in ((True, False) if R > 4096 else (True,)):
+        gc.check_lookup(rs, re_, rk, d["off"], d["len"], va_base=d["va_base"], page_shift=ps,
+                        records=records, ctx=f"seed={seed} lookup R={R} records={records}")
