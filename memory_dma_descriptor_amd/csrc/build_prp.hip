@@ -113,7 +113,8 @@ struct Fuse {
     uint32_t nq;                  // queues; bucket nq takes ids >= nq
     uint32_t tile_shift;          // log2 of the split's requests per tile
     uint64_t ntiles;              // split tiles: the row length of counts
-    uint32_t *counts;             // bucket-major per-tile counts, zeroed
+    uint32_t *counts;             // bucket-major per-tile counts, zeroed; nullptr: the
+                                  // split counts its single tile itself
 };
 constexpr int kHistCopies = 4;                    // lane l counts into copy l % 4
 constexpr int kHistStride = DMADESC_MAX_QUEUES + 1;
@@ -881,7 +882,8 @@ __global__ __launch_bounds__(kThreads, 4) void k_prp_build(
     uint32_t *hist = reinterpret_cast<uint32_t *>(&s_round[0]);
 
     const int t = threadIdx.x, w = wave(), ln = lane();
-    if constexpr (kFused) {
+    const bool split_hist = kFused && F.counts != nullptr;
+    if (split_hist) {
         for (int k = t; k < kHistCopies * kHistStride; k += kThreads) hist[k] = 0;
     }
     if (t == 0) s_bid = atomicAdd(&hdr->ticket, 1u);
@@ -900,9 +902,9 @@ __global__ __launch_bounds__(kThreads, 4) void k_prp_build(
         l[k] = i < n ? __builtin_nontemporal_load(len + i) : 0;   // len 0 decodes as invalid
         // Clamped, not guarded: a guarded load is a branch whose result the
         // compiler waits for before the next item's loads are issued.
-        if constexpr (kFused) q[k] = __builtin_nontemporal_load(F.qid + (i < n ? i : n - 1));
+        if (split_hist) q[k] = __builtin_nontemporal_load(F.qid + (i < n ? i : n - 1));
     }
-    if constexpr (kFused) {
+    if (split_hist) {
         // Queue histogram of the block (LDS atomics; counts only, so their
         // order does not matter).
         uint32_t *hc = hist + (ln % kHistCopies) * kHistStride;
@@ -975,7 +977,7 @@ __global__ __launch_bounds__(kThreads, 4) void k_prp_build(
             // Waves 1..3 add the block histogram to its split tile's counts
             // while wave 0 looks back, then look their requests up.
             const uint64_t tile = base >> F.tile_shift;
-            for (uint32_t bk = t - kWave; bk <= F.nq; bk += kThreads - kWave) {
+            for (uint32_t bk = t - kWave; split_hist && bk <= F.nq; bk += kThreads - kWave) {
                 uint32_t c = 0;
 #pragma unroll
                 for (int j = 0; j < kHistCopies; ++j) c += hist[j * kHistStride + bk];
@@ -1133,11 +1135,14 @@ hipError_t launch_build_batch(const LookupArgs &lk, const PrpArgs &a, const Spli
     F.nq = sp.nqueues;
     F.tile_shift = shift;
     F.ntiles = ntiles;
-    F.counts = counts;
+    // A batch of one split tile is ranked by the split's own one-tile kernel
+    // (it counts its tile itself): the build then adds no histogram.
+    const bool single = split_single(sp.n, sp.nqueues);
+    F.counts = single ? nullptr : counts;
     launch_prp_kernel<true>(a, nb, hdr, bstat, F, s);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    return launch_partition_counted(sp, s);
+    return single ? launch_partition(sp, s) : launch_partition_counted(sp, s);
 }
 
 size_t ws_build_prp(uint64_t n)

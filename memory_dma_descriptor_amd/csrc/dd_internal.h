@@ -106,6 +106,9 @@ hipError_t launch_partition(const SplitArgs &a, hipStream_t s);
 // the first part of a.ws.
 hipError_t launch_partition_counted(const SplitArgs &a, hipStream_t s);
 uint32_t split_tile_shift(uint32_t nq);
+// The batch is one split tile ranked by the counter path: the split runs its
+// one-tile kernel alone (no histogram, no column scan).
+bool split_single(uint64_t n, uint32_t nq);
 // The fused batch: lookup (lk.handle == nullptr: none), PRP build (a.packed
 // selects the layout) and split; a.ws, sp.ws and index_ws are the three
 // parts of the call's workspace.

@@ -420,6 +420,11 @@ size_t ws_partition(uint64_t n, uint32_t nq)
            align256((uint64_t)(nq + 1) * sizeof(uint64_t));
 }
 
+bool split_single(uint64_t n, uint32_t nq)
+{
+    return n > 0 && n <= split_tile(nq) && nq <= kCntQueues;
+}
+
 uint32_t split_tile_shift(uint32_t nq)
 {
     return nq <= kCntQueues ? 13 : 12;
@@ -435,7 +440,7 @@ hipError_t launch_partition(const SplitArgs &a, hipStream_t s)
     const uint64_t tile = split_tile(a.nqueues);
     const uint64_t nb = (a.n + tile - 1) / tile;
     uint32_t *counts = static_cast<uint32_t *>(a.ws);
-    if (nb == 1 && a.nqueues <= kCntQueues) {
+    if (split_single(a.n, a.nqueues)) {
         // One tile: the scatter alone (no histogram, no column scan).
         const bool vec = (reinterpret_cast<uintptr_t>(a.qid) & 15u) == 0;
         hipLaunchKernelGGL((k_split_scatter_cnt<kItemsCnt, true>), dim3(1), dim3(kThreads), 0, s,
