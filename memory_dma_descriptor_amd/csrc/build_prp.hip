@@ -900,9 +900,10 @@ __global__ __launch_bounds__(kThreads, 4) void k_prp_build(
         const uint64_t i = base + (uint64_t)k * kThreads + t;
         o[k] = i < n ? __builtin_nontemporal_load(off + i) : 0;
         l[k] = i < n ? __builtin_nontemporal_load(len + i) : 0;   // len 0 decodes as invalid
-        // Clamped, not guarded: a guarded load is a branch whose result the
-        // compiler waits for before the next item's loads are issued.
-        if (split_hist) q[k] = __builtin_nontemporal_load(F.qid + (i < n ? i : n - 1));
+        // Clamped, not guarded, and loaded even when the split counts its
+        // one tile itself: a load behind a condition is a branch whose result
+        // the compiler waits for before the next item's loads are issued.
+        if constexpr (kFused) q[k] = __builtin_nontemporal_load(F.qid + (i < n ? i : n - 1));
     }
     if (split_hist) {
         // Queue histogram of the block (LDS atomics; counts only, so their
