@@ -55,7 +55,9 @@
  *  - Every pointer argument is caller-owned DEVICE memory on the current HIP
  *    device unless marked "host". The library allocates nothing, keeps no
  *    state between calls (apart from the test bound set by
- *    dmadesc_debug_wait_limit) and retains no pointer after returning.
+ *    dmadesc_debug_wait_limit and the static per-device scratch of
+ *    dmadesc_build_prp_packed_noalloc) and retains no pointer after
+ *    returning.
  *  - Every call is asynchronous on `stream` (a hipStream_t; NULL = the
  *    device's null stream). Outputs are valid once the caller synchronizes
  *    that stream or orders later work behind it on the same stream
@@ -66,7 +68,9 @@
  *      -EINVAL  null pointer where one is required, n >= 2^32, a parameter
  *               out of range (stated per call), workspace too small or not
  *               256-byte aligned;
- *      -EIO     the HIP runtime refused a kernel launch.
+ *      -EIO     the HIP runtime refused a kernel launch;
+ *      -E2BIG   (dmadesc_build_prp_packed_noalloc only) a batch larger than
+ *               its static scratch allows.
  *    Errors in individual requests are not call errors: they are reported
  *    per request in an output column (stated per call).
  *  - All arithmetic is exact unsigned 64-bit integer arithmetic; outputs are
