@@ -123,3 +123,45 @@ def test_empty_batch():
     z = np.zeros(0, np.uint64)
     check_put(z, z, z, np.zeros(0, np.uint32), b["local_base"], b["heap"], b["chunk_shift"],
               b["lkeys"], b["peer_base"], b["rkeys"], 4, "empty")
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_random_parameters(seed):
+    """Seeded draws over the call's whole parameter space: chunk shift (0 =
+    static heap, else 12..31), heap size, PE count, batch size (around the
+    4,096-put block too), lengths from a byte to many chunks, invalid and
+    out-of-heap puts, random key tables and bases, and a capacity below or
+    at the total."""
+    rng = np.random.default_rng(1000 + seed)
+    shift = 0 if seed % 5 == 0 else int(rng.integers(12, 32))
+    if shift:
+        nch = int(rng.integers(1, min(1 << 12, (1 << 40) >> shift) + 1))
+        heap = nch << shift
+    else:
+        nch, heap = 1, int(rng.integers(1 << 20, 1 << 41))
+    npes = int(rng.integers(1, 17))
+    n = [int(rng.integers(0, 300)), 4095, 4096, 4097, int(rng.integers(5000, 40_000))][seed % 5]
+    unit = 1 << (shift if shift else 31)
+    kind = rng.integers(0, 3, n)
+    nbytes = np.where(kind == 0, rng.integers(1, 65, n),
+                      np.where(kind == 1, rng.integers(1, unit + 1, n),
+                               rng.integers(1, 4 * unit + 1, n))).astype(np.uint64)
+    nbytes = np.minimum(nbytes, np.uint64(heap))
+    src = (rng.random(n) * (heap - nbytes.astype(np.float64) + 1)).astype(np.uint64)
+    dst = (rng.random(n) * (heap - nbytes.astype(np.float64) + 1)).astype(np.uint64)
+    src = np.minimum(src, np.uint64(heap) - nbytes)
+    dst = np.minimum(dst, np.uint64(heap) - nbytes)
+    pe = rng.integers(0, npes, n).astype(np.uint32)
+    if n:
+        bad = rng.random(n)
+        nbytes[bad < 0.01] = 0                                    # EINVAL
+        pe[(bad >= 0.01) & (bad < 0.02)] = np.uint32(npes)        # EINVAL
+        src[(bad >= 0.02) & (bad < 0.03)] = np.uint64(heap)       # ERANGE (a byte past)
+    lk = rng.integers(0, 1 << 32, nch, dtype=np.uint64).astype(np.uint32)
+    rk = rng.integers(0, 1 << 32, npes * nch, dtype=np.uint64).astype(np.uint32)
+    pb = rng.integers(0, 1 << 56, npes, dtype=np.uint64)
+    local_base = int(rng.integers(0, 1 << 56))
+    o = oracle.build_put(src, dst, nbytes, pe, local_base, heap, shift, lk, pb, rk, 0, write=False)
+    cap = int(o["total"]) if seed % 3 else int(o["total"] * rng.uniform(0.3, 1.0))
+    check_put(src, dst, nbytes, pe, local_base, heap, shift, lk, pb, rk, cap,
+              f"random seed={seed} shift={shift} heap={heap} npes={npes} n={n}")
