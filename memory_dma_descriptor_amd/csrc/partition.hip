@@ -50,14 +50,6 @@ __device__ __forceinline__ int key_bits(uint32_t nq)
     return 32 - __clz(nq);                       // bits of the largest bucket id
 }
 
-__device__ __forceinline__ uint32_t bucket_of(const uint32_t *__restrict__ qid, uint64_t i,
-                                              uint64_t n, uint32_t nq)
-{
-    if (i >= n) return 0;
-    const uint32_t q = qid[i];
-    return q < nq ? q : nq;
-}
-
 // Buckets of a thread's kItems requests base + 64 k. In a tile that lies
 // wholly inside the batch (every tile but the last) the loads carry no
 // condition, so all of them are in flight at once; a guarded load would wait
@@ -73,8 +65,14 @@ __device__ __forceinline__ void load_buckets(const uint32_t *__restrict__ qid, u
 #pragma unroll
         for (int k = 0; k < kItems; ++k) b[k] = b[k] < nq ? b[k] : nq;
     } else {
+        // Clamped, not guarded (requests past the batch take bucket 0; their
+        // callers skip them).
 #pragma unroll
-        for (int k = 0; k < kItems; ++k) b[k] = bucket_of(qid, base + (uint64_t)k * kWave, n, nq);
+        for (int k = 0; k < kItems; ++k) {
+            const uint64_t i = base + (uint64_t)k * kWave;
+            const uint32_t v = qid[i < n ? i : n - 1];
+            b[k] = i < n ? (v < nq ? v : nq) : 0u;
+        }
     }
 }
 
@@ -302,10 +300,27 @@ __global__ __launch_bounds__(kThreads) void k_split_scatter_cnt(
         }
 #pragma unroll
         for (int k = 0; k < kItems; ++k) b[k] = b[k] < nq ? b[k] : nq;
-    } else {
+    } else if (vec && base + kItems <= n) {
+        // A chunk wholly inside the batch (in the last, partial tile).
 #pragma unroll
-        for (int k = 0; k < kItems; ++k)
-            b[k] = base + k < n ? bucket_of(qid, base + k, n, nq) : nbp - 1;
+        for (int q = 0; q < kItems / 4; ++q) {
+            const uint4 x = *reinterpret_cast<const uint4 *>(qid + base + 4 * q);
+            b[4 * q] = x.x;
+            b[4 * q + 1] = x.y;
+            b[4 * q + 2] = x.z;
+            b[4 * q + 3] = x.w;
+        }
+#pragma unroll
+        for (int k = 0; k < kItems; ++k) b[k] = b[k] < nq ? b[k] : nq;
+    } else {
+        // Clamped, not guarded, so that all of the chunk's loads are in
+        // flight at once (a one-tile batch: 10.3 -> 8.0 us for 4,096 requests).
+#pragma unroll
+        for (int k = 0; k < kItems; ++k) {
+            const uint64_t i = base + k;
+            const uint32_t v = qid[i < n ? i : n - 1];
+            b[k] = i < n ? (v < nq ? v : nq) : nbp - 1;
+        }
     }
     __syncthreads();
 
