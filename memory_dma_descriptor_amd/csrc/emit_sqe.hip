@@ -29,9 +29,12 @@
 // affects speed: a slot depends on the per-tile counts, never on which block
 // ran first.
 //
-// Kernels: k_sqe_order (tile order), k_sqe_count (placeable requests per
-// tile), k_sqe_emit (slots, entries, request map), k_sqe_finish (placed
-// counts, tails and cursors).
+// Kernels: k_sqe_order (tile order, one record per tile and per queue),
+// k_sqe_count (placeable requests per tile), k_sqe_emit (slots, entries,
+// request map), k_sqe_finish (placed counts, tails and cursors). The records
+// spare the two passes the chain of dependent reads (tile, queue state,
+// bucket bounds, cursor, free slots) that finding a tile's window takes:
+// a block reads its record and starts its gathers.
 #include "dd_device.hpp"
 #include "dd_internal.h"
 #include "dmadesc.h"
@@ -50,10 +53,27 @@ constexpr uint32_t kBins = 4096;                 // tile-order buckets over the 
 constexpr int kBinsPerThread = kBins / kOrderThreads;
 constexpr int kMaxTiles = DMADESC_MAX_QUEUES * kTilesPerQueue;
 
-// Workspace: per-tile counts, the tile order, and the number of non-empty tiles.
+// A non-empty tile in schedule order: where its entries start in perm, how
+// many there are, and its id g = 64 q + t.
+struct TileRec {
+    uint64_t pos;
+    uint32_t cnt, g;
+};
+static_assert(sizeof(TileRec) == 16, "one 16-byte load");
+
+// A queue's ring as this call sees it.
+struct QueueRec {
+    uint64_t ring;
+    uint32_t tail, depth;
+};
+static_assert(sizeof(QueueRec) == 16, "one 16-byte load");
+
+// Workspace: per-tile counts, the tile records in schedule order, the queue
+// records, and the number of non-empty tiles.
 struct SqeWs {
-    uint32_t *counts;     // [nq * 64]
-    uint32_t *order;      // [nq * 64]
+    uint32_t *counts;     // [nq * 64], by tile id
+    TileRec *tiles;       // [nq * 64], the first *ntiles in schedule order
+    QueueRec *queues;     // [nq]
     uint32_t *ntiles;     // scalar
 };
 
@@ -105,23 +125,36 @@ __global__ __launch_bounds__(kOrderThreads) void k_sqe_order(SqeArgs a, SqeWs ws
         const Window win = window_of(a, q);
         s_start[q] = win.start;
         s_w[q] = win.w;
+        ws.queues[q] = QueueRec{win.ring, win.tail, win.depth};
     }
     for (uint32_t b = threadIdx.x; b < kBins; b += kOrderThreads) s_bin[b] = 0;
     __syncthreads();
-    // Each thread owns tiles threadIdx.x + k * kOrderThreads.
+    // Each thread owns tiles threadIdx.x + k * kOrderThreads. The first
+    // entries of all of them are read at once, from a clamped position (a
+    // read behind a condition would wait for the one before it); with an
+    // empty batch no tile is non-empty and nothing is read.
     constexpr int kPer = kMaxTiles / kOrderThreads;
     uint32_t bin[kPer];
+    bool live[kPer];
+    uint64_t first[kPer];
 #pragma unroll
     for (int k = 0; k < kPer; ++k) {
         const uint32_t g = threadIdx.x + k * kOrderThreads;
+        const uint32_t q = g < ntile ? g / kTilesPerQueue : 0u;
+        const uint32_t lo = (g % kTilesPerQueue) * kTile;
+        live[k] = g < ntile && lo < s_w[q];
+        first[k] = live[k] ? s_start[q] + lo : 0;
+    }
+    if (a.n != 0) {
+#pragma unroll
+        for (int k = 0; k < kPer; ++k) first[k] = a.perm[first[k]];
+    }
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
         bin[k] = UINT32_MAX;
-        if (g < ntile) {
-            const uint32_t q = g / kTilesPerQueue, lo = (g % kTilesPerQueue) * kTile;
-            if (lo < s_w[q]) {
-                const uint64_t first = a.perm[s_start[q] + lo];
-                bin[k] = (uint32_t)(first * kBins / a.n);   // first < n, so bin < kBins
-                atomicAdd(&s_bin[bin[k]], 1u);
-            }
+        if (live[k]) {
+            bin[k] = (uint32_t)(first[k] * kBins / a.n);     // first < n, so bin < kBins
+            atomicAdd(&s_bin[bin[k]], 1u);
         }
     }
     __syncthreads();
@@ -141,35 +174,35 @@ __global__ __launch_bounds__(kOrderThreads) void k_sqe_order(SqeArgs a, SqeWs ws
     __syncthreads();
 #pragma unroll
     for (int k = 0; k < kPer; ++k)
-        if (bin[k] != UINT32_MAX)
-            ws.order[atomicAdd(&s_bin[bin[k]], 1u)] = threadIdx.x + k * kOrderThreads;
+        if (bin[k] != UINT32_MAX) {
+            const uint32_t g = threadIdx.x + k * kOrderThreads;
+            const uint32_t q = g / kTilesPerQueue, lo = (g % kTilesPerQueue) * kTile;
+            const uint32_t cnt = s_w[q] - lo < kTile ? s_w[q] - lo : kTile;
+            ws.tiles[atomicAdd(&s_bin[bin[k]], 1u)] = TileRec{s_start[q] + lo, cnt, g};
+        }
     if (threadIdx.x == 0) *ws.ntiles = total;
 }
 
 // The tile block b works on, or false when b has none. Blocks are dealt to
 // the 8 XCDs in turn; XCD x takes the x-th eighth of the tile order, so the
 // tiles that share an XCD's L2 cover neighbouring request ranges.
-__device__ __forceinline__ bool tile_of(const SqeWs &ws, uint32_t &q, uint32_t &t)
+__device__ __forceinline__ bool tile_of(const SqeWs &ws, TileRec &r)
 {
     const uint32_t nt = *ws.ntiles, per = (nt + 7) / 8;
     const uint32_t x = blockIdx.x & 7, k = blockIdx.x >> 3;
     const uint32_t idx = x * per + k;
     if (k >= per || idx >= nt) return false;
-    const uint32_t g = ws.order[idx];
-    q = g / kTilesPerQueue;
-    t = g % kTilesPerQueue;
+    r = ws.tiles[idx];
     return true;
 }
 
 __global__ __launch_bounds__(kThreads) void k_sqe_count(SqeArgs a, SqeWs ws)
 {
     __shared__ uint32_t s_sum[kWaves];
-    uint32_t q, t;
-    if (!tile_of(ws, q, t)) return;                    // uniform over the block
-    const Window win = window_of(a, q);
-    const uint32_t lo = t * kTile;
-    const uint32_t cnt = win.w - lo < kTile ? win.w - lo : kTile;
-    const uint32_t *__restrict__ pos = a.perm + win.start + lo;
+    TileRec r;
+    if (!tile_of(ws, r)) return;                       // uniform over the block
+    const uint32_t cnt = r.cnt;
+    const uint32_t *__restrict__ pos = a.perm + r.pos;
 
     uint32_t idx[kRounds];
 #pragma unroll
@@ -198,7 +231,7 @@ __global__ __launch_bounds__(kThreads) void k_sqe_count(SqeArgs a, SqeWs ws)
         uint32_t s = 0;
 #pragma unroll
         for (int w = 0; w < kWaves; ++w) s += s_sum[w];
-        ws.counts[(uint64_t)q * kTilesPerQueue + t] = s;
+        ws.counts[r.g] = s;
     }
 }
 
@@ -207,12 +240,12 @@ __global__ __launch_bounds__(kThreads) void k_sqe_emit(SqeArgs a, SqeWs ws)
     __shared__ uint32_t s_cnt[kRounds][kWaves];
     // A wave's entries of one round, by rank: 64 x 64 bytes per wave.
     __shared__ uint4 s_ent[kWaves][kWave * 4];
-    uint32_t q, t;
-    if (!tile_of(ws, q, t)) return;                    // uniform over the block
-    const Window win = window_of(a, q);
-    const uint32_t lo = t * kTile;
-    const uint32_t cnt = win.w - lo < kTile ? win.w - lo : kTile;
-    const uint32_t *__restrict__ pos = a.perm + win.start + lo;
+    TileRec r;
+    if (!tile_of(ws, r)) return;                       // uniform over the block
+    const uint32_t q = r.g / kTilesPerQueue, t = r.g % kTilesPerQueue;
+    const QueueRec win = ws.queues[q];
+    const uint32_t cnt = r.cnt;
+    const uint32_t *__restrict__ pos = a.perm + r.pos;
     const int w = wave(), ln = lane();
 
     // Placeable requests of the window before this tile (t < 64 tiles).
@@ -310,13 +343,17 @@ __global__ __launch_bounds__(kThreads) void k_sqe_emit(SqeArgs a, SqeWs ws)
     }
 }
 
+// One wave per queue: lane t adds tile t's count (64 tiles cover a window).
 __global__ __launch_bounds__(kThreads) void k_sqe_finish(SqeArgs a, SqeWs ws)
 {
-    for (uint32_t q = threadIdx.x; q < a.nqueues; q += kThreads) {
-        const Window win = window_of(a, q);
-        const uint32_t tiles = (win.w + kTile - 1) / kTile;
-        uint32_t placed = 0;
-        for (uint32_t t = 0; t < tiles; ++t) placed += ws.counts[(uint64_t)q * kTilesPerQueue + t];
+    const uint32_t q = blockIdx.x * kWaves + wave();
+    if (q >= a.nqueues) return;                         // uniform per wave
+    const Window win = window_of(a, q);
+    const uint32_t tiles = (win.w + kTile - 1) / kTile;
+    const uint32_t ln = lane();
+    uint32_t placed = ln < tiles ? ws.counts[(uint64_t)q * kTilesPerQueue + ln] : 0u;
+    placed = wave_sum(placed);
+    if (ln == 0) {
         a.placed[q] = placed;
         if (win.w > 0) {
             uint32_t nt = win.tail + placed;
@@ -331,21 +368,26 @@ __global__ __launch_bounds__(kThreads) void k_sqe_finish(SqeArgs a, SqeWs ws)
 
 size_t ws_emit_sqe(uint32_t nq)
 {
-    const uint64_t tiles = (uint64_t)nq * kTilesPerQueue * sizeof(uint32_t);
-    return 2 * align256(tiles) + 256;
+    const uint64_t tiles = (uint64_t)nq * kTilesPerQueue;
+    return align256(tiles * sizeof(uint32_t)) + align256(tiles * sizeof(TileRec)) +
+           align256((uint64_t)nq * sizeof(QueueRec)) + 256;
 }
 
 hipError_t launch_emit_sqe(const SqeArgs &a, hipStream_t s)
 {
     char *base = static_cast<char *>(a.ws);
     const uint64_t tiles = (uint64_t)a.nqueues * kTilesPerQueue;
-    SqeWs ws{reinterpret_cast<uint32_t *>(base),
-             reinterpret_cast<uint32_t *>(base + align256(tiles * sizeof(uint32_t))),
-             reinterpret_cast<uint32_t *>(base + 2 * align256(tiles * sizeof(uint32_t)))};
+    const uint64_t at_tiles = align256(tiles * sizeof(uint32_t));
+    const uint64_t at_queues = at_tiles + align256(tiles * sizeof(TileRec));
+    const uint64_t at_count = at_queues + align256((uint64_t)a.nqueues * sizeof(QueueRec));
+    SqeWs ws{reinterpret_cast<uint32_t *>(base), reinterpret_cast<TileRec *>(base + at_tiles),
+             reinterpret_cast<QueueRec *>(base + at_queues),
+             reinterpret_cast<uint32_t *>(base + at_count)};
     hipLaunchKernelGGL(k_sqe_order, dim3(1), dim3(kOrderThreads), 0, s, a, ws);
     hipLaunchKernelGGL(k_sqe_count, dim3((unsigned)tiles), dim3(kThreads), 0, s, a, ws);
     hipLaunchKernelGGL(k_sqe_emit, dim3((unsigned)tiles), dim3(kThreads), 0, s, a, ws);
-    hipLaunchKernelGGL(k_sqe_finish, dim3(1), dim3(kThreads), 0, s, a, ws);
+    hipLaunchKernelGGL(k_sqe_finish, dim3((a.nqueues + kWaves - 1) / kWaves), dim3(kThreads), 0,
+                       s, a, ws);
     return hipGetLastError();
 }
 
