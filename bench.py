@@ -54,6 +54,20 @@ def traffic_file(layout: str, workload: str) -> str:
     return os.path.join(ROOT, "profiles", f"traffic_build_prp_{layout}_{workload}.json")
 
 
+def recorded_traffic(layout: str, workload: str):
+    """HBM bytes per launch of the PRP build from the counter record in
+    profiles/, or None when there is none or the kernel sources changed
+    since the counters were taken."""
+    tf = traffic_file(layout, workload)
+    if not os.path.exists(tf):
+        return None
+    with open(tf) as f:
+        rec = json.load(f)
+    if rec.get("source_sha256") != prp_source_hash():
+        return None
+    return rec.get("traffic_bytes_per_launch")
+
+
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -734,6 +748,7 @@ def main():
         other = {"list_pages": o_pages, "algorithmic_bytes_per_launch": ab[o_key],
                  **dist(np, o_ms), "achieved_gbs": round(o_gbs, 1),
                  "frac": round(o_gbs / PEAK_HBM_GBS, 4),
+                 "traffic": recorded_traffic("packed" if not packed else "page", args.workload),
                  "refused_requests": int((o_out[0]["status"].cpu().numpy() != 0).sum())}
         del o_pool, o_out
 
@@ -794,13 +809,7 @@ def main():
 
     dom_ms = per_call[dominant]
     achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
-    traffic = None
-    tf = traffic_file(layout, args.workload)
-    if d["lut_entries"] and os.path.exists(tf):
-        with open(tf) as f:
-            rec = json.load(f)
-        if rec.get("source_sha256") == prp_source_hash():
-            traffic = rec.get("traffic_bytes_per_launch")
+    traffic = recorded_traffic(layout, args.workload) if d["lut_entries"] else None
     kernel = {"build_prp_packed": "dmadesc_build_prp_packed (k_ws_clear + k_prp_build)",
               "build_prp": "dmadesc_build_prp (k_ws_clear + k_prp_build)",
               "mr_lookup": "dmadesc_mr_lookup"}[dominant]

@@ -319,11 +319,12 @@ __device__ __forceinline__ uint64_t global_read(const uint64_t *p)
 // Writes the list runs of the wave's 64 requests of one round. Lane k's
 // request is described by (xb, word, ent, lp); ent == 0 for no list.
 __device__ __forceinline__ void emit_round_wide(RoundTable &T, uint64_t xb, uint64_t word, uint64_t ent,
-                                           uint64_t lp, uint64_t last_frame,
-                                           const uint64_t *__restrict__ lut,
+                                           uint64_t lp, uint64_t last_frame, uint64_t o,
+                                           uint64_t &p1, const uint64_t *__restrict__ lut,
                                            uint64_t *__restrict__ pool, uint64_t bus)
 {
     const int ln = lane();
+    if (ent) p1 = global_read(&lut[o >> 16]) + (o & 0xFFFFu);
     const uint64_t groups = ((ent + kPadWords - 1) / kPadWords) * (kPadWords / 4);
     const uint64_t ginc = wave_incl_scan(groups);
     const uint64_t gtot = __shfl(ginc, kWave - 1, kWave);
@@ -460,6 +461,7 @@ __device__ __forceinline__ void fast_groups(const FastTable &T, uint32_t gtot,
 
 __device__ __forceinline__ void emit_round_fast(FastTable &T, uint64_t xb, uint64_t word,
                                                 uint32_t ent, uint64_t lp, uint64_t last_frame,
+                                                uint64_t o, uint64_t &p1,
                                                 const uint64_t *__restrict__ lut,
                                                 uint64_t *__restrict__ pool, uint64_t bus)
 {
@@ -471,7 +473,9 @@ __device__ __forceinline__ void emit_round_fast(FastTable &T, uint64_t xb, uint6
     if (gtot == 0) {                                         // uniform per wave
         return;
     }
-    const uint64_t f0 = xb >> 16;
+    // Staged from PRP1's GPU page, so that PRP1 comes from the tile too; data
+    // entry 0 then lies in 4 KiB page ph (< 32) counted from that GPU page.
+    const uint64_t f0 = o >> 16;
     const uint32_t frames = ent ? (uint32_t)(last_frame - f0 + 1) : 0;
     const uint32_t finc = wave_incl_scan(frames);
     const uint32_t ftot = __shfl(finc, kWave - 1, kWave);
@@ -482,7 +486,7 @@ __device__ __forceinline__ void emit_round_fast(FastTable &T, uint64_t xb, uint6
         T.foff[kWave] = finc;
     }
     T.rec[ln] = ReqRec{word, f0, ent, lp ? (uint32_t)((lp - 1) << 9) : 0u, finc - frames,
-                       (uint32_t)((xb >> 12) & 15u)};
+                       (uint32_t)((xb >> 12) & 15u) + (uint32_t)(((xb >> 16) - f0) << 4)};
     wave_sync_lds();
     if (ftot <= (uint32_t)kTileFrames) {
         // Four reads in flight per lane before any lands in LDS.
@@ -502,8 +506,10 @@ __device__ __forceinline__ void emit_round_fast(FastTable &T, uint64_t xb, uint6
             }
         }
         wave_sync_lds();
+        if (ent) p1 = lds_read(&T.lut[finc - frames]) + (o & 0xFFFFu);
         fast_groups<true>(T, gtot, lut, pool, bus);
     } else {
+        if (ent) p1 = global_read(&lut[f0]) + (o & 0xFFFFu);
         fast_groups<false>(T, gtot, lut, pool, bus);
     }
     wave_sync_lds();                                         // the next round rewrites T
@@ -511,15 +517,16 @@ __device__ __forceinline__ void emit_round_fast(FastTable &T, uint64_t xb, uint6
 
 // Writes the list runs of the wave's 64 requests of one round (lane k: one
 // request; ent == 0 for no list).
+// Sets p1 to PRP1 of each request with a list.
 __device__ __forceinline__ void emit_round(RoundLds &T, uint64_t xb, uint64_t word, uint64_t ent,
-                                           uint64_t lp, uint64_t last_frame,
-                                           const uint64_t *__restrict__ lut,
+                                           uint64_t lp, uint64_t last_frame, uint64_t o,
+                                           uint64_t &p1, const uint64_t *__restrict__ lut,
                                            uint64_t *__restrict__ pool, uint64_t bus)
 {
     if (__ballot(ent >= kFastWords) == 0)
-        emit_round_fast(T.fast, xb, word, (uint32_t)ent, lp, last_frame, lut, pool, bus);
+        emit_round_fast(T.fast, xb, word, (uint32_t)ent, lp, last_frame, o, p1, lut, pool, bus);
     else
-        emit_round_wide(T.wide, xb, word, ent, lp, last_frame, lut, pool, bus);
+        emit_round_wide(T.wide, xb, word, ent, lp, last_frame, o, p1, lut, pool, bus);
 }
 
 // Per-wave table of one round of 64 requests for the packed layout. T holds
@@ -954,8 +961,8 @@ __global__ __launch_bounds__(kThreads, 4) void k_prp_build(
     // in for a request that needs none) so that all of them are in flight
     // together; waves 1..3 issue theirs before wave 0 looks back, wave 0
     // after (its look-back polls would otherwise wait for its table reads).
-    // A packed list takes PRP1 from the table entries its round stages, so
-    // its table read is not repeated here. The second page's table entry of
+    // A list (either layout) takes PRP1 from the table entries its round
+    // stages, so its table read is not repeated here. The second page's table entry of
     // a two-page request waits in LDS (8 KiB per block), which keeps the
     // packed build within 128 VGPRs, four blocks per CU.
     uint64_t v1[kItems];
@@ -965,7 +972,7 @@ __global__ __launch_bounds__(kThreads, 4) void k_prp_build(
             uint64_t pages;
             const uint8_t st = decode(o[k], l[k], heap, pages);
             const uint64_t x = (o[k] & ~4095ull) + 4096;
-            const bool staged_prp1 = kPacked && pages >= 3;
+            const bool staged_prp1 = pages >= 3;
             const uint64_t i1 = (st == kOk && !staged_prp1) ? o[k] >> 16 : 0;
             const uint64_t i2 = (st == kOk && pages == 2) ? x >> 16 : 0;
             v1[k] = heap ? lut[i1] : 0;
@@ -1031,7 +1038,7 @@ __global__ __launch_bounds__(kThreads, 4) void k_prp_build(
                               heap >> 16, lut, pool, bus);
         else
             emit_round(s_round[w], xb, slot << 9, lists ? (pages - 1) + (cnt - 1) : 0,
-                       lists ? cnt : 0, last_frame, lut, pool, bus);
+                       lists ? cnt : 0, last_frame, o[k], p1, lut, pool, bus);
         if (i < n) {
             const uint64_t list = kPacked ? bus + 8 * (slot + slot / 511) : bus + (slot << 12);
             const uint64_t p2 = lists ? list : (pages == 2 ? s_v2[k * kThreads + t] + (xb & 0xFFFFu) : 0);
