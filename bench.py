@@ -32,6 +32,10 @@ Prints ONE JSON line:
                timed after the steps
   cpu_baseline the single-threaded oracle, per function and end to end,
                median of 3 runs on one pinned core
+
+Profiler passes use --quick (the warm-up and timed steps only),
+--stage-emit-sqe (the submission-entry stage alone), --copy-calibration (a
+1 GiB device copy, for counter scales) and --list-write-floor.
 """
 from __future__ import annotations
 
@@ -100,6 +104,10 @@ def parse():
     ap.add_argument("--list-write-floor", action="store_true",
                     help="time a library scatter that writes the same 128-byte list lines "
                          "as the PRP build (its layout's write floor) and exit")
+    ap.add_argument("--stage-emit-sqe", action="store_true",
+                    help="run the step's calls once, then time only the submission-entry "
+                         "stage on their outputs (--emit-reps launches; for profiler passes) "
+                         "and exit")
     return ap.parse_args()
 
 
@@ -393,7 +401,7 @@ def emit_stage(dd, d, np, torch, prp_out, sp_out, ln, reps):
     n_placed = int(placed.cpu().numpy().astype(np.int64).sum())
     nbytes = consumed * 13 + n_placed * (24 + 64 + 4) + nq * 48
     gbs = nbytes / (ms * 1e-3) / 1e9
-    return {"kernels": "k_sqe_count + k_sqe_emit + k_sqe_finish", "ring_depth": depth,
+    return {"kernels": "k_sqe_order + k_sqe_count + k_sqe_emit + k_sqe_finish", "ring_depth": depth,
             "consumed": consumed, "placed": n_placed, "mean_launch_ms": round(ms, 4),
             "algorithmic_bytes_per_launch": nbytes, "achieved_gbs": round(gbs, 1),
             "frac": round(gbs / PEAK_HBM_GBS, 4),
@@ -716,6 +724,18 @@ def main():
 
     import memory_dma_descriptor_amd as dd
     import synth
+
+    if args.stage_emit_sqe:
+        d = synth.generate(args.workload)
+        if not (d["lut_entries"] and d["nqueues"]):
+            raise SystemExit("bench.py: the submission-entry stage needs a workload with a "
+                             "heap and queues")
+        st = Step(dd, torch, np, d, args.layout == "packed")
+        st.run()
+        torch.cuda.synchronize()
+        r = emit_stage(dd, d, np, torch, st.pr, st.sp, st.ln, max(args.emit_reps, 1))
+        print(json.dumps({"emit_sqe": r, "workload": args.workload}), flush=True)
+        return
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)

@@ -72,6 +72,8 @@ static_assert(sizeof(QueueRec) == 16, "one 16-byte load");
 // records, and the number of non-empty tiles.
 struct SqeWs {
     uint32_t *counts;     // [nq * 64], by tile id
+    uint64_t *mask;       // [nq * 64 * kRounds * kWaves]: placeable lanes of each
+                          // (tile, round, wave), by tile id
     TileRec *tiles;       // [nq * 64], the first *ntiles in schedule order
     QueueRec *queues;     // [nq]
     uint32_t *ntiles;     // scalar
@@ -220,11 +222,15 @@ __global__ __launch_bounds__(kThreads) void k_sqe_count(SqeArgs a, SqeWs ws)
         st[k] = a.status[i];
         len[k] = a.len[i];
     }
+    // The placeable lanes of each round, kept for the emit pass (which then
+    // gathers no status) and counted.
     uint32_t c = 0;
 #pragma unroll
-    for (int k = 0; k < kRounds; ++k)
-        c += (idx[k] < a.n && placeable(st[k], len[k], a.lba_shift)) ? 1u : 0u;
-    c = wave_sum(c);
+    for (int k = 0; k < kRounds; ++k) {
+        const uint64_t mk = __ballot(idx[k] < a.n && placeable(st[k], len[k], a.lba_shift));
+        if (lane() == 0) ws.mask[((uint64_t)r.g * kRounds + k) * kWaves + wave()] = mk;
+        c += (uint32_t)__popcll(mk);
+    }
     if (lane() == 0) s_sum[wave()] = c;
     __syncthreads();
     if (threadIdx.x == 0) {
@@ -257,7 +263,6 @@ __global__ __launch_bounds__(kThreads) void k_sqe_emit(SqeArgs a, SqeWs ws)
     // placed after a store would wait for it.
     uint32_t idx[kRounds];
     uint64_t len[kRounds], p1[kRounds], p2[kRounds], lba[kRounds];
-    uint8_t st[kRounds];
 #pragma unroll
     for (int k = 0; k < kRounds; ++k) {
         const uint32_t j = k * kThreads + threadIdx.x;
@@ -267,7 +272,6 @@ __global__ __launch_bounds__(kThreads) void k_sqe_emit(SqeArgs a, SqeWs ws)
     for (int k = 0; k < kRounds; ++k) {
         const uint32_t i = idx[k] < a.n ? idx[k] : 0u;
         const bool in = idx[k] < a.n;
-        st[k] = in ? a.status[i] : (uint8_t)0xFF;
         len[k] = in ? a.len[i] : 0;
         p1[k] = in ? a.prp1[i] : 0;
         p2[k] = in ? a.prp2[i] : 0;
@@ -276,7 +280,7 @@ __global__ __launch_bounds__(kThreads) void k_sqe_emit(SqeArgs a, SqeWs ws)
     uint64_t m[kRounds];
 #pragma unroll
     for (int k = 0; k < kRounds; ++k) {
-        m[k] = __ballot(placeable(st[k], len[k], a.lba_shift));
+        m[k] = ws.mask[((uint64_t)r.g * kRounds + k) * kWaves + w];   // the count pass's
         if (ln == 0) s_cnt[k][w] = (uint32_t)__popcll(m[k]);
     }
     __syncthreads();
@@ -369,18 +373,20 @@ __global__ __launch_bounds__(kThreads) void k_sqe_finish(SqeArgs a, SqeWs ws)
 size_t ws_emit_sqe(uint32_t nq)
 {
     const uint64_t tiles = (uint64_t)nq * kTilesPerQueue;
-    return align256(tiles * sizeof(uint32_t)) + align256(tiles * sizeof(TileRec)) +
-           align256((uint64_t)nq * sizeof(QueueRec)) + 256;
+    return align256(tiles * sizeof(uint32_t)) + align256(tiles * kRounds * kWaves * 8) +
+           align256(tiles * sizeof(TileRec)) + align256((uint64_t)nq * sizeof(QueueRec)) + 256;
 }
 
 hipError_t launch_emit_sqe(const SqeArgs &a, hipStream_t s)
 {
     char *base = static_cast<char *>(a.ws);
     const uint64_t tiles = (uint64_t)a.nqueues * kTilesPerQueue;
-    const uint64_t at_tiles = align256(tiles * sizeof(uint32_t));
+    const uint64_t at_mask = align256(tiles * sizeof(uint32_t));
+    const uint64_t at_tiles = at_mask + align256(tiles * kRounds * kWaves * 8);
     const uint64_t at_queues = at_tiles + align256(tiles * sizeof(TileRec));
     const uint64_t at_count = at_queues + align256((uint64_t)a.nqueues * sizeof(QueueRec));
-    SqeWs ws{reinterpret_cast<uint32_t *>(base), reinterpret_cast<TileRec *>(base + at_tiles),
+    SqeWs ws{reinterpret_cast<uint32_t *>(base), reinterpret_cast<uint64_t *>(base + at_mask),
+             reinterpret_cast<TileRec *>(base + at_tiles),
              reinterpret_cast<QueueRec *>(base + at_queues),
              reinterpret_cast<uint32_t *>(base + at_count)};
     hipLaunchKernelGGL(k_sqe_order, dim3(1), dim3(kOrderThreads), 0, s, a, ws);
