@@ -74,6 +74,8 @@ struct SqeWs {
     uint32_t *counts;     // [nq * 64], by tile id
     uint64_t *mask;       // [nq * 64 * kRounds * kWaves]: placeable lanes of each
                           // (tile, round, wave), by tile id
+    uint16_t *nlb;        // [schedule index * kTile + position]: blocks - 1 of each
+                          // placeable position of a tile
     TileRec *tiles;       // [nq * 64], the first *ntiles in schedule order
     QueueRec *queues;     // [nq]
     uint32_t *ntiles;     // scalar
@@ -188,11 +190,11 @@ __global__ __launch_bounds__(kOrderThreads) void k_sqe_order(SqeArgs a, SqeWs ws
 // The tile block b works on, or false when b has none. Blocks are dealt to
 // the 8 XCDs in turn; XCD x takes the x-th eighth of the tile order, so the
 // tiles that share an XCD's L2 cover neighbouring request ranges.
-__device__ __forceinline__ bool tile_of(const SqeWs &ws, TileRec &r)
+__device__ __forceinline__ bool tile_of(const SqeWs &ws, TileRec &r, uint32_t &idx)
 {
     const uint32_t nt = *ws.ntiles, per = (nt + 7) / 8;
     const uint32_t x = blockIdx.x & 7, k = blockIdx.x >> 3;
-    const uint32_t idx = x * per + k;
+    idx = x * per + k;
     if (k >= per || idx >= nt) return false;
     r = ws.tiles[idx];
     return true;
@@ -202,7 +204,8 @@ __global__ __launch_bounds__(kThreads) void k_sqe_count(SqeArgs a, SqeWs ws)
 {
     __shared__ uint32_t s_sum[kWaves];
     TileRec r;
-    if (!tile_of(ws, r)) return;                       // uniform over the block
+    uint32_t ti;
+    if (!tile_of(ws, r, ti)) return;                   // uniform over the block
     const uint32_t cnt = r.cnt;
     const uint32_t *__restrict__ pos = a.perm + r.pos;
 
@@ -230,6 +233,12 @@ __global__ __launch_bounds__(kThreads) void k_sqe_count(SqeArgs a, SqeWs ws)
         const uint64_t mk = __ballot(idx[k] < a.n && placeable(st[k], len[k], a.lba_shift));
         if (lane() == 0) ws.mask[((uint64_t)r.g * kRounds + k) * kWaves + wave()] = mk;
         c += (uint32_t)__popcll(mk);
+        // The block count field of each position, stored contiguously for
+        // the emit pass (which then gathers no length either).
+        const uint32_t j = k * kThreads + threadIdx.x;
+        if (j < cnt)
+            ws.nlb[(uint64_t)ti * kTile + j] =
+                (mk >> lane()) & 1u ? (uint16_t)((len[k] >> a.lba_shift) - 1u) : (uint16_t)0;
     }
     if (lane() == 0) s_sum[wave()] = c;
     __syncthreads();
@@ -247,7 +256,8 @@ __global__ __launch_bounds__(kThreads) void k_sqe_emit(SqeArgs a, SqeWs ws)
     // A wave's entries of one round, by rank: 64 x 64 bytes per wave.
     __shared__ uint4 s_ent[kWaves][kWave * 4];
     TileRec r;
-    if (!tile_of(ws, r)) return;                       // uniform over the block
+    uint32_t ti;
+    if (!tile_of(ws, r, ti)) return;                   // uniform over the block
     const uint32_t q = r.g / kTilesPerQueue, t = r.g % kTilesPerQueue;
     const QueueRec win = ws.queues[q];
     const uint32_t cnt = r.cnt;
@@ -262,7 +272,8 @@ __global__ __launch_bounds__(kThreads) void k_sqe_emit(SqeArgs a, SqeWs ws)
     // compiler cannot prove that a ring aliases no input column, so a load
     // placed after a store would wait for it.
     uint32_t idx[kRounds];
-    uint64_t len[kRounds], p1[kRounds], p2[kRounds], lba[kRounds];
+    uint64_t p1[kRounds], p2[kRounds], lba[kRounds];
+    uint32_t nlb[kRounds];
 #pragma unroll
     for (int k = 0; k < kRounds; ++k) {
         const uint32_t j = k * kThreads + threadIdx.x;
@@ -272,7 +283,8 @@ __global__ __launch_bounds__(kThreads) void k_sqe_emit(SqeArgs a, SqeWs ws)
     for (int k = 0; k < kRounds; ++k) {
         const uint32_t i = idx[k] < a.n ? idx[k] : 0u;
         const bool in = idx[k] < a.n;
-        len[k] = in ? a.len[i] : 0;
+        const uint32_t j = k * kThreads + threadIdx.x;
+        nlb[k] = ws.nlb[(uint64_t)ti * kTile + (j < cnt ? j : 0u)];
         p1[k] = in ? a.prp1[i] : 0;
         p2[k] = in ? a.prp2[i] : 0;
         lba[k] = in ? a.slba[i] : 0;
@@ -316,7 +328,7 @@ __global__ __launch_bounds__(kThreads) void k_sqe_emit(SqeArgs a, SqeWs ws)
             const uint32_t r = (uint32_t)__popcll(m[k] & below);
             uint32_t s = s0 + r;
             if (s >= win.depth) s -= win.depth;
-            const uint32_t nlb0 = (uint32_t)(len[k] >> a.lba_shift) - 1u;
+            const uint32_t nlb0 = nlb[k];
             uint4 *e = ent + r * 4;
             e[0] = make_uint4(a.opcode | (s << 16), a.nsid, 0u, 0u);
             e[1] = make_uint4(0u, 0u, (uint32_t)p1[k], (uint32_t)(p1[k] >> 32));
@@ -370,11 +382,16 @@ __global__ __launch_bounds__(kThreads) void k_sqe_finish(SqeArgs a, SqeWs ws)
 
 }  // namespace
 
+// Per (queue, tile): a count, the masks and a record, and the block counts
+// of its positions (2 bytes per ring slot a call can fill, 64 tiles per
+// queue whatever qoff holds, so every schedule index stays in bounds); per
+// queue a record. Under 1/16 of the rings the call can fill.
 size_t ws_emit_sqe(uint32_t nq)
 {
     const uint64_t tiles = (uint64_t)nq * kTilesPerQueue;
     return align256(tiles * sizeof(uint32_t)) + align256(tiles * kRounds * kWaves * 8) +
-           align256(tiles * sizeof(TileRec)) + align256((uint64_t)nq * sizeof(QueueRec)) + 256;
+           align256(tiles * kTile * sizeof(uint16_t)) + align256(tiles * sizeof(TileRec)) +
+           align256((uint64_t)nq * sizeof(QueueRec)) + 256;
 }
 
 hipError_t launch_emit_sqe(const SqeArgs &a, hipStream_t s)
@@ -382,11 +399,12 @@ hipError_t launch_emit_sqe(const SqeArgs &a, hipStream_t s)
     char *base = static_cast<char *>(a.ws);
     const uint64_t tiles = (uint64_t)a.nqueues * kTilesPerQueue;
     const uint64_t at_mask = align256(tiles * sizeof(uint32_t));
-    const uint64_t at_tiles = at_mask + align256(tiles * kRounds * kWaves * 8);
+    const uint64_t at_nlb = at_mask + align256(tiles * kRounds * kWaves * 8);
+    const uint64_t at_tiles = at_nlb + align256(tiles * kTile * sizeof(uint16_t));
     const uint64_t at_queues = at_tiles + align256(tiles * sizeof(TileRec));
     const uint64_t at_count = at_queues + align256((uint64_t)a.nqueues * sizeof(QueueRec));
     SqeWs ws{reinterpret_cast<uint32_t *>(base), reinterpret_cast<uint64_t *>(base + at_mask),
-             reinterpret_cast<TileRec *>(base + at_tiles),
+             reinterpret_cast<uint16_t *>(base + at_nlb), reinterpret_cast<TileRec *>(base + at_tiles),
              reinterpret_cast<QueueRec *>(base + at_queues),
              reinterpret_cast<uint32_t *>(base + at_count)};
     hipLaunchKernelGGL(k_sqe_order, dim3(1), dim3(kOrderThreads), 0, s, a, ws);

@@ -59,11 +59,14 @@ def test_workspace_sizes():
         assert sizes[-1] < 1 << 32, sizes                 # small next to the batch itself
     assert ws(dd.OP_PARTITION, 1 << 20, 256) > ws(dd.OP_PARTITION, 1 << 20, 1)
     # Submission entries: per (queue, tile) a count, the placeable-lane masks
-    # (128 bytes) and a record, per queue a record; independent of the batch.
+    # (128 bytes), a record and the block counts of its 1,024 positions (2
+    # bytes each), per queue a record; independent of the batch, and under
+    # 1/16 of the rings a call can fill (64 bytes per entry).
     assert ws(dd.OP_EMIT_SQE, 100, 0) == 0 and ws(dd.OP_EMIT_SQE, 100, 257) == 0
     e = [ws(dd.OP_EMIT_SQE, n, q) for q in (1, 64, 256) for n in (0, 1 << 24)]
     assert all(x % 256 == 0 and x > 0 for x in e) and e[0] == e[1] and e[2] < e[4]
-    assert e[-1] <= 4 << 20
+    for q, x in zip((1, 64, 256), e[::2]):
+        assert x <= q * 65536 * 64 // 16, (q, x)
 
 
 EINVAL = -errno.EINVAL
