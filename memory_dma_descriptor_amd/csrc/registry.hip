@@ -45,6 +45,8 @@ constexpr int kPer = 4;                              // records per thread in sc
 constexpr uint32_t kChunk = kThreads * kPer;         // records per scan block
 constexpr int kTopThreads = 1024;
 constexpr uint32_t kMaxChunks = DMADESC_REG_MAX_CAPACITY / kChunk;   // 16384
+constexpr uint32_t kItemChunks = DMADESC_REG_MAX_BATCH / kChunk;      // 64
+static_assert(kItemChunks <= kThreads, "item chunk totals scan in one block");
 static_assert(kMaxChunks % kTopThreads == 0, "chunk totals scan in one block");
 
 enum : uint8_t { kInvalid = DMADESC_REG_INVALID, kHit = DMADESC_REG_HIT, kNew = DMADESC_REG_NEW,
@@ -88,6 +90,7 @@ struct RegWs {
     uint32_t *tmp32;
     // per scan chunk
     uint64_t *chunk;        // chunk totals, then exclusive prefixes
+    uint64_t *ichunk;       // the same for batch items (ranking misses, inserts)
     // scalars: [0] inserts, [1] fits, [2] live count after deregistration
     uint64_t *scal;
 };
@@ -295,40 +298,97 @@ __global__ __launch_bounds__(kThreads) void k_reg_classify(RegState g, RegWs w, 
     w.hit[i] = hit;
 }
 
-// One block: the misses in batch order. mrank[i] = misses before item i; the
-// misses' ranges go to their ranks. Wave v ranks the v-th contiguous chunk
-// of the batch by ballots after the earlier chunks' counts.
-__global__ __launch_bounds__(kTopThreads) void k_reg_misses(RegWs w, uint32_t n)
+// Ranking batch items of one class (misses, then inserts) in batch order: a
+// device-wide exclusive scan over chunks of kChunk items in three kernels
+// (count per chunk, scan of the chunk counts in one block, ranks and
+// scatter), so that no wave walks a long chunk round by round. Thread t of a
+// block takes the 4 consecutive items p0 + 4t .. p0 + 4t + 3.
+template <uint8_t kCls>
+__device__ __forceinline__ void item_flags(const RegWs &w, uint32_t n, uint32_t p, uint32_t (&f)[kPer])
 {
-    constexpr uint32_t kTopWaves = kTopThreads / kWave;
-    constexpr uint32_t kChunkItems = DMADESC_REG_MAX_BATCH / kTopWaves;
-    static_assert(kChunkItems % kWave == 0, "chunks are whole rounds");
-    __shared__ uint32_t s_tot[kTopWaves];
-    const uint32_t v = threadIdx.x / kWave, ln = threadIdx.x % kWave;
-    const uint32_t c0 = v * kChunkItems;
-    const uint32_t ce = n < c0 ? 0u : (n - c0 < kChunkItems ? n - c0 : kChunkItems);
-    uint32_t cnt = 0;
-    for (uint32_t r = 0; r < ce; r += kWave)             // uniform over the wave
-        cnt += (uint32_t)__popcll(__ballot(r + ln < ce && w.cls[c0 + r + ln] == kMiss));
-    if (ln == 0) s_tot[v] = cnt;
-    __syncthreads();
-    uint32_t run = 0;
-    for (uint32_t u = 0; u < v; ++u) run += s_tot[u];
-    const uint64_t below = __lanemask_lt();
-    for (uint32_t r = 0; r < ce; r += kWave) {
-        const uint32_t i = c0 + r + ln;
-        const bool in = r + ln < ce;
-        const bool miss = in && w.cls[i] == kMiss;
-        const uint64_t m = __ballot(miss);
-        if (in) {
-            const uint32_t rk = run + (uint32_t)__popcll(m & below);
-            w.mrank[i] = rk;
-            if (miss) {
-                w.mbase[rk] = w.base[i];
-                w.mtop[rk] = w.top[i];
+    if (p + kPer <= n) {
+        const uint32_t c4 = *reinterpret_cast<const uint32_t *>(w.cls + p);
+#pragma unroll
+        for (int k = 0; k < kPer; ++k) f[k] = ((c4 >> (8 * k)) & 0xFFu) == kCls;
+    } else {
+#pragma unroll
+        for (int k = 0; k < kPer; ++k) f[k] = p + k < n && w.cls[p + k] == kCls;
+    }
+}
+
+template <uint8_t kCls>
+__global__ __launch_bounds__(kThreads) void k_rank_chunks(RegWs w, uint32_t n)
+{
+    __shared__ uint64_t scr[kWaves];
+    const uint32_t p = blockIdx.x * kChunk + threadIdx.x * kPer;
+    uint32_t f[kPer];
+    item_flags<kCls>(w, n, p, f);
+    uint64_t tot;
+    block_excl<false, kThreads>((uint64_t)(f[0] + f[1] + f[2] + f[3]), scr, &tot);
+    if (threadIdx.x == 0) w.ichunk[blockIdx.x] = tot;
+}
+
+// One block: the chunk counts become exclusive prefixes. For the inserts
+// (kCount) it also records their number, whether the table has room, and the
+// capacity the growth rule reaches (reported either way).
+template <bool kCount>
+__global__ __launch_bounds__(kThreads) void k_rank_top(RegState g, RegWs w, uint32_t n,
+                                                       uint64_t *needed)
+{
+    __shared__ uint64_t scr[kWaves];
+    const uint32_t nch = (n + kChunk - 1) / kChunk;
+    const uint64_t v = threadIdx.x < nch ? w.ichunk[threadIdx.x] : 0;
+    uint64_t tot;
+    const uint64_t ex = block_excl<false, kThreads>(v, scr, &tot);
+    if (threadIdx.x < nch) w.ichunk[threadIdx.x] = ex;
+    if (kCount && threadIdx.x == 0) {
+        const uint64_t after = g.state[0] + tot;
+        uint64_t need = g.capacity;
+        while (need < after) need = need == 0 ? 32 : 2 * need;
+        *needed = need;
+        w.scal[0] = tot;
+        w.scal[1] = after <= g.capacity;
+    }
+}
+
+// Ranks and scatter. Misses: mrank[i] = misses before item i, and each
+// miss's range goes to its rank. Inserts: rank[i] = inserts before item i,
+// newrefs[i] = 1 (by rank; ranks < n), and each insert's range goes to its
+// rank.
+template <uint8_t kCls>
+__global__ __launch_bounds__(kThreads) void k_rank_apply(RegWs w, uint32_t n)
+{
+    __shared__ uint64_t scr[kWaves];
+    const uint32_t p = blockIdx.x * kChunk + threadIdx.x * kPer;
+    uint32_t f[kPer];
+    item_flags<kCls>(w, n, p, f);
+    // The ranges of all four items, read at once (clamped, not guarded).
+    uint64_t b[kPer], t[kPer];
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+        const uint32_t i = p + k < n ? p + k : 0u;
+        b[k] = w.base[i];
+        t[k] = w.top[i];
+    }
+    uint64_t tot;
+    uint32_t run = (uint32_t)(w.ichunk[blockIdx.x] +
+                              block_excl<false, kThreads>((uint64_t)(f[0] + f[1] + f[2] + f[3]),
+                                                          scr, &tot));
+    uint32_t *rk_out = kCls == kMiss ? w.mrank : w.rank;
+    uint64_t *ob = kCls == kMiss ? w.mbase : w.ibase;
+    uint64_t *ot = kCls == kMiss ? w.mtop : w.itop;
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+        const uint32_t i = p + k;
+        if (i < n) {
+            rk_out[i] = run;
+            if (kCls == kNew) w.newrefs[i] = 1;
+            if (f[k]) {
+                ob[run] = b[k];
+                ot[run] = t[k];
             }
         }
-        run += (uint32_t)__popcll(m);
+        run += f[k];
     }
 }
 
@@ -379,60 +439,6 @@ __global__ __launch_bounds__(kThreads) void k_reg_inserted(RegWs w, uint32_t n)
         __syncthreads();
     }
     if (k0 == 0 && me && s_done[ln] == 0) w.cls[i] = kNew;
-}
-
-// One block: ranks of the inserts in batch order, their count, and whether
-// the table has room; the needed capacity is reported either way. Wave v
-// takes the v-th contiguous chunk of the batch, 64 items a round: one pass
-// counts, the other ranks by ballots after the earlier chunks' counts.
-__global__ __launch_bounds__(kTopThreads) void k_reg_count(RegState g, RegWs w, uint32_t n,
-                                                           uint64_t *needed)
-{
-    constexpr uint32_t kTopWaves = kTopThreads / kWave;
-    constexpr uint32_t kChunkItems = DMADESC_REG_MAX_BATCH / kTopWaves;
-    static_assert(kChunkItems % kWave == 0, "chunks are whole rounds");
-    __shared__ uint32_t s_tot[kTopWaves];
-    const uint32_t v = threadIdx.x / kWave, ln = threadIdx.x % kWave;
-    const uint32_t c0 = v * kChunkItems;
-    const uint32_t ce = n < c0 ? 0u : (n - c0 < kChunkItems ? n - c0 : kChunkItems);
-    uint32_t cnt = 0;
-    for (uint32_t r = 0; r < ce; r += kWave) {           // uniform over the wave
-        const uint32_t i = c0 + r + ln;
-        cnt += (uint32_t)__popcll(__ballot(r + ln < ce && w.cls[i] == kNew));
-    }
-    if (ln == 0) s_tot[v] = cnt;
-    __syncthreads();
-    uint32_t run = 0, tot = 0;
-    for (uint32_t u = 0; u < kTopWaves; ++u) {
-        const uint32_t c = s_tot[u];
-        run += u < v ? c : 0u;
-        tot += c;
-    }
-    const uint64_t below = __lanemask_lt();
-    for (uint32_t r = 0; r < ce; r += kWave) {
-        const uint32_t i = c0 + r + ln;
-        const bool in = r + ln < ce;
-        const bool nw = in && w.cls[i] == kNew;
-        const uint64_t m = __ballot(nw);
-        if (in) {
-            const uint32_t rk = run + (uint32_t)__popcll(m & below);
-            w.rank[i] = rk;
-            w.newrefs[i] = 1;                            // by rank; ranks < n
-            if (nw) {                                    // the inserts' ranges, by rank
-                w.ibase[rk] = w.base[i];
-                w.itop[rk] = w.top[i];
-            }
-        }
-        run += (uint32_t)__popcll(m);
-    }
-    if (threadIdx.x == 0) {
-        const uint64_t after = g.state[0] + tot;
-        uint64_t need = g.capacity;
-        while (need < after) need = need == 0 ? 32 : 2 * need;
-        *needed = need;
-        w.scal[0] = tot;
-        w.scal[1] = after <= g.capacity;
-    }
 }
 
 // For every range that is not inserted, the earlier insert with the smallest
@@ -780,6 +786,7 @@ RegWs carve(void *ws, uint64_t n, uint64_t cap, size_t *bytes = nullptr)
     w.tmp64c = c.take<uint64_t>(cap);
     w.tmp32 = c.take<uint32_t>(cap);
     w.chunk = c.take<uint64_t>(kMaxChunks);
+    w.ichunk = c.take<uint64_t>(kItemChunks);
     w.scal = c.take<uint64_t>(4);
     if (bytes) *bytes = c.off;
     return w;
@@ -807,6 +814,7 @@ hipError_t launch_reg_register(const RegArgs &a, hipStream_t s)
     const uint32_t n = (uint32_t)a.n;
     const unsigned nb = (n + kThreads - 1) / kThreads;
     const unsigned pb = (n + kPairItems - 1) / kPairItems;
+    const unsigned cb = (n + kChunk - 1) / kChunk;       // item chunks of the rankings
     const unsigned rb = (unsigned)((cap + kThreads - 1) / kThreads < 4096 ? (cap + kThreads - 1) / kThreads : 4096);
     if (rb) {
         hipLaunchKernelGGL(k_reg_starts, dim3(rb), dim3(kThreads), 0, s, g, w);
@@ -816,10 +824,14 @@ hipError_t launch_reg_register(const RegArgs &a, hipStream_t s)
     if (nb) {
         hipLaunchKernelGGL(k_reg_classify, dim3(nb), dim3(kThreads), 0, s, g, w, a.page_shift,
                            a.addr, a.size, n);
-        hipLaunchKernelGGL(k_reg_misses, dim3(1), dim3(kTopThreads), 0, s, w, n);
+        hipLaunchKernelGGL(k_rank_chunks<kMiss>, dim3(cb), dim3(kThreads), 0, s, w, n);
+        hipLaunchKernelGGL(k_rank_top<false>, dim3(1), dim3(kThreads), 0, s, g, w, n, a.needed);
+        hipLaunchKernelGGL(k_rank_apply<kMiss>, dim3(cb), dim3(kThreads), 0, s, w, n);
         hipLaunchKernelGGL(k_reg_inserted, dim3(pb), dim3(kThreads), 0, s, w, n);
+        hipLaunchKernelGGL(k_rank_chunks<kNew>, dim3(cb), dim3(kThreads), 0, s, w, n);
     }
-    hipLaunchKernelGGL(k_reg_count, dim3(1), dim3(kTopThreads), 0, s, g, w, n, a.needed);
+    hipLaunchKernelGGL(k_rank_top<true>, dim3(1), dim3(kThreads), 0, s, g, w, n, a.needed);
+    if (nb) hipLaunchKernelGGL(k_rank_apply<kNew>, dim3(cb), dim3(kThreads), 0, s, w, n);
     if (nb) {
         hipLaunchKernelGGL(k_reg_owner, dim3(pb), dim3(kThreads), 0, s, w, n);
         hipLaunchKernelGGL(k_reg_apply, dim3(nb), dim3(kThreads), 0, s, g, w, n, a.handle,
