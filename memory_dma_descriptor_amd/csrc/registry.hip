@@ -639,28 +639,49 @@ __global__ __launch_bounds__(kThreads) void k_dereg_find(RegState g, RegWs w, co
         if (g.id[mid] < key) lo = mid + 1;
         else hi = mid;
     }
-    w.hit[i] = (lo < count && g.id[lo] == key) ? (uint32_t)lo : UINT32_MAX;
+    const bool found = lo < count && g.id[lo] == key;
+    w.hit[i] = found ? (uint32_t)lo : UINT32_MAX;
+    if (found) w.tmp32[lo] = UINT32_MAX;                 // its first call, set next
 }
 
-// Calls before i naming the same record decide whether call i succeeds.
-// Blocks of kPairItems calls; each wave counts over its quarter of every tile
-// and adds its count to s_before. A call that has seen as many earlier calls
+// The first call of the batch on each named record (tmp32 by storage slot).
+__global__ __launch_bounds__(kThreads) void k_dereg_first(RegWs w, uint32_t n)
+{
+    const uint32_t i = blockIdx.x * kThreads + threadIdx.x;
+    if (i >= n) return;
+    const uint32_t me = w.hit[i];
+    if (me != UINT32_MAX) atomicMin(&w.tmp32[me], i);
+}
+
+// Calls before i naming the same record decide whether call i succeeds. No
+// call before the record's first call of the batch names it, so the first
+// call has none before it, and a later call on a record of one reference
+// has at least one: neither counts. The others count the calls in [first,
+// i): blocks of kPairItems calls, each wave over its quarter of every tile,
+// adding its count to s_before; a call that has seen as many earlier calls
 // as its record has references is stale whatever follows, so it stops there.
 __global__ __launch_bounds__(kThreads) void k_dereg_status(RegState g, RegWs w, uint32_t n,
                                                            uint8_t *status)
 {
     __shared__ __align__(16) uint32_t s_slot[kThreads];
     __shared__ uint32_t s_before[kPairItems];
+    __shared__ uint32_t s_from;
     const uint32_t ln = threadIdx.x % kWave, k0 = threadIdx.x / kWave * kWave;
     const uint32_t i = blockIdx.x * kPairItems + ln;
     const uint32_t me = i < n ? w.hit[i] : UINT32_MAX;
     const uint32_t r = me != UINT32_MAX ? g.refs[me] : 0u;
-    if (k0 == 0) s_before[ln] = 0;
+    const uint32_t first = me != UINT32_MAX ? w.tmp32[me] : i;
+    const bool counts = me != UINT32_MAX && first < i && r > 1;
+    if (threadIdx.x == 0) s_from = UINT32_MAX;
+    if (k0 == 0) s_before[ln] = first < i ? (r > 1 ? 0u : 1u) : 0u;
+    __syncthreads();
+    if (k0 == 0 && counts) atomicMin(&s_from, first);
     __syncthreads();
     const uint32_t jend = blockIdx.x * kPairItems + kPairItems;
-    uint32_t hj = threadIdx.x < n ? w.hit[threadIdx.x] : UINT32_MAX;   // one tile ahead
-    for (uint32_t j0 = 0; j0 < jend; j0 += kThreads) {
-        const bool open = me != UINT32_MAX && s_before[ln] < r;
+    const uint32_t jfrom = s_from == UINT32_MAX ? jend : s_from / kThreads * kThreads;
+    uint32_t hj = jfrom + threadIdx.x < n ? w.hit[jfrom + threadIdx.x] : UINT32_MAX;   // one tile ahead
+    for (uint32_t j0 = jfrom; j0 < jend; j0 += kThreads) {
+        const bool open = counts && s_before[ln] < r;
         if (__syncthreads_or(open) == 0) break;          // every call here is decided
         s_slot[threadIdx.x] = hj;
         const uint32_t jn = j0 + kThreads + threadIdx.x;
@@ -862,6 +883,7 @@ hipError_t launch_reg_deregister(const RegArgs &a, hipStream_t s)
     }
     const unsigned rb = (unsigned)((cap + kThreads - 1) / kThreads < 4096 ? (cap + kThreads - 1) / kThreads : 4096);
     hipLaunchKernelGGL(k_dereg_find, dim3(nb), dim3(kThreads), 0, s, g, w, a.handle_in, n);
+    hipLaunchKernelGGL(k_dereg_first, dim3(nb), dim3(kThreads), 0, s, w, n);
     hipLaunchKernelGGL(k_dereg_status, dim3(pb), dim3(kThreads), 0, s, g, w, n, a.status);
     hipLaunchKernelGGL(k_dereg_drop, dim3(nb), dim3(kThreads), 0, s, g, w, n);
     // Prefixes of kept slots (storage) and kept entries (start order).
