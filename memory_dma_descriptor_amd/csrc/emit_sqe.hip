@@ -30,11 +30,15 @@
 // ran first.
 //
 // Kernels: k_sqe_order (tile order, one record per tile and per queue),
-// k_sqe_count (placeable requests per tile), k_sqe_emit (slots, entries,
-// request map), k_sqe_finish (placed counts, tails and cursors). The records
-// spare the two passes the chain of dependent reads (tile, queue state,
-// bucket bounds, cursor, free slots) that finding a tile's window takes:
-// a block reads its record and starts its gathers.
+// k_sqe_count (placeable requests per tile; it gathers status and length and
+// keeps, for the next pass, each round's placeable lanes and each position's
+// block-count field), k_sqe_emit (slots, entries, request map; it gathers
+// only PRP1, PRP2 and the starting block, since every gathered column costs
+// a cache line per entry of a sparse queue), k_sqe_finish (placed counts,
+// tails and cursors). The records spare the two passes the chain of
+// dependent reads (tile, queue state, bucket bounds, cursor, free slots) that
+// finding a tile's window takes: a block reads its record and starts its
+// gathers.
 #include "dd_device.hpp"
 #include "dd_internal.h"
 #include "dmadesc.h"
@@ -68,8 +72,9 @@ struct QueueRec {
 };
 static_assert(sizeof(QueueRec) == 16, "one 16-byte load");
 
-// Workspace: per-tile counts, the tile records in schedule order, the queue
-// records, and the number of non-empty tiles.
+// Workspace: per-tile counts and placeable masks, the block-count fields,
+// the tile records in schedule order, the queue records, and the number of
+// non-empty tiles.
 struct SqeWs {
     uint32_t *counts;     // [nq * 64], by tile id
     uint64_t *mask;       // [nq * 64 * kRounds * kWaves]: placeable lanes of each
