@@ -247,7 +247,7 @@ __global__ __launch_bounds__(kThreads) void k_split_scatter(
 constexpr int kCntBuckets = 72;                 // padded bucket limit of the counter path
 constexpr uint32_t kCntQueues = kCntBuckets - 2;   // nq + 1 buckets + a spare fit
 static_assert(kCntBuckets % 8 == 0, "scan rows are 8 counters");
-static_assert(kThreads * kItemsCnt * 3 <= kCntBuckets * kThreads * 2,
+static_assert(kThreads * kItemsCnt * 4 <= kCntBuckets * kThreads * 2,
               "sorted tile fits over the counters");
 
 // Lanes l and l + 32 of a wave own adjacent chunks, so the 32 lanes an LDS
@@ -324,16 +324,20 @@ __global__ __launch_bounds__(kThreads) void k_split_scatter_cnt(
     }
     __syncthreads();
 
-    // Ranks inside the chunk: each request reads and bumps its own counter,
-    // in request order (LDS operations of a wave complete in order).
+    // Ranks inside the chunk: each request bumps its own counter with an LDS
+    // atomic add that returns the old value. The counters of chunks 2m and
+    // 2m + 1 share a dword, so the add goes to this chunk's half; a chunk
+    // counts at most kItems per bucket, so no carry reaches the other half.
+    // A wave's LDS operations complete in order, so the ranks follow request
+    // order, and the adds need not wait for each other (a load and a store
+    // per request made a dependent round trip each).
     uint16_t *col = s_cnt + c;
+    uint32_t *col32 = reinterpret_cast<uint32_t *>(s_cnt) + (c >> 1);
+    const uint32_t half = (c & 1u) * 16u;
     uint32_t rank[kItems];
 #pragma unroll
-    for (int k = 0; k < kItems; ++k) {
-        const uint32_t r = col[b[k] * kThreads];
-        rank[k] = r;
-        col[b[k] * kThreads] = (uint16_t)(r + 1);
-    }
+    for (int k = 0; k < kItems; ++k)
+        rank[k] = (atomicAdd(col32 + b[k] * (kThreads / 2), 1u << half) >> half) & 0xFFFFu;
     __syncthreads();
 
     // Exclusive scan of the matrix, bucket-major: thread t scans counters
@@ -393,21 +397,38 @@ __global__ __launch_bounds__(kThreads) void k_split_scatter_cnt(
 #pragma unroll
     for (int k = 0; k < kItems; ++k) sidx[k] = col[b[k] * kThreads] + rank[k];
     __syncthreads();
+    // Where the tile's place j of bucket bk goes in perm: s_gpos[bk] - s_lstart[bk] + j.
+    if ((uint32_t)t < nbk) s_gpos[t] -= s_lstart[t];
 
-    uint16_t *s_sorted = s_cnt;
-    uint8_t *s_sbkt = reinterpret_cast<uint8_t *>(s_cnt + kTile);
+    // The sorted tile: one dword per place, (bucket << 16) | request index in
+    // the tile. Requests past the batch (spare bucket, sorted last) land past
+    // its count, where nothing reads them, so no request needs a guard.
+    uint32_t *s_sorted = reinterpret_cast<uint32_t *>(s_cnt);
 #pragma unroll
-    for (int k = 0; k < kItems; ++k) {
-        if (base + k < n) {
-            s_sorted[sidx[k]] = (uint16_t)(c * kItems + k);
-            s_sbkt[sidx[k]] = (uint8_t)b[k];
-        }
-    }
+    for (int k = 0; k < kItems; ++k) s_sorted[sidx[k]] = (b[k] << 16) | (c * kItems + k);
     __syncthreads();
     const uint64_t cnt = n - tile < (uint64_t)kTile ? n - tile : (uint64_t)kTile;
-    for (uint32_t j = t; j < cnt; j += kThreads) {
-        const uint32_t bk = s_sbkt[j];
-        perm[s_gpos[bk] + (j - s_lstart[bk])] = (uint32_t)(tile + s_sorted[j]);
+    if (cnt == (uint64_t)kTile) {
+        // Eight places per lane at a time: their LDS reads are in flight
+        // together instead of one dependent pair per place.
+        constexpr int kU = 8;
+#pragma unroll 1
+        for (int m0 = 0; m0 < kItems; m0 += kU) {
+            uint32_t e[kU];
+            uint64_t d[kU];
+#pragma unroll
+            for (int u = 0; u < kU; ++u) e[u] = s_sorted[t + (m0 + u) * kThreads];
+#pragma unroll
+            for (int u = 0; u < kU; ++u) d[u] = s_gpos[e[u] >> 16];
+#pragma unroll
+            for (int u = 0; u < kU; ++u)
+                perm[d[u] + (uint32_t)(t + (m0 + u) * kThreads)] = (uint32_t)(tile + (e[u] & 0xFFFFu));
+        }
+    } else {
+        for (uint32_t j = t; j < cnt; j += kThreads) {
+            const uint32_t e = s_sorted[j];
+            perm[s_gpos[e >> 16] + j] = (uint32_t)(tile + (e & 0xFFFFu));
+        }
     }
 }
 
