@@ -34,8 +34,9 @@ Prints ONE JSON line:
                median of 3 runs on one pinned core
 
 Profiler passes use --quick (the warm-up and timed steps only),
---stage-emit-sqe (the submission-entry stage alone), --copy-calibration (a
-1 GiB device copy, for counter scales) and --list-write-floor.
+--stage-emit-sqe (the submission-entry stage alone), --stage-registry (the
+registry's two batches alone), --copy-calibration (a 1 GiB device copy, for
+counter scales) and --list-write-floor.
 """
 from __future__ import annotations
 
@@ -108,6 +109,9 @@ def parse():
                     help="run the step's calls once, then time only the submission-entry "
                          "stage on their outputs (--emit-reps launches; for profiler passes) "
                          "and exit")
+    ap.add_argument("--stage-registry", action="store_true",
+                    help="time only the registry's register and deregister batches "
+                         "(10 calls each; for profiler passes) and exit")
     return ap.parse_args()
 
 
@@ -735,6 +739,13 @@ def main():
         torch.cuda.synchronize()
         r = emit_stage(dd, d, np, torch, st.pr, st.sp, st.ln, max(args.emit_reps, 1))
         print(json.dumps({"emit_sqe": r, "workload": args.workload}), flush=True)
+        return
+    if args.stage_registry:
+        d = synth.generate(args.workload)
+        if not d["regions"]:
+            raise SystemExit("bench.py: the registry stage needs a workload with regions")
+        r = registry_stage(dd, d, np, torch, 10)
+        print(json.dumps({"registry": r, "workload": args.workload}), flush=True)
         return
 
     dev = torch.device("cuda:0")

@@ -21,9 +21,12 @@
 //    record it hit (if any) and the earlier inserts that contain it: the
 //    insert with the smallest (start, batch index) wins over the old record
 //    only when its start is strictly smaller, since an insert goes after the
-//    records with the same start. These relations are found by comparing
-//    every pair of the batch in LDS tiles (a batch is at most
-//    DMADESC_REG_MAX_BATCH calls).
+//    records with the same start. These relations are found through a
+//    bucketed index of the batch's ranges (a containing range that is no
+//    longer than a bucket lies in one of two buckets), and by comparing
+//    every pair in LDS tiles only for the ranges that are longer than a
+//    bucket or overflow theirs (a batch is at most DMADESC_REG_MAX_BATCH
+//    calls).
 //  * New records get handles next_id + their rank among the batch's inserts,
 //    take storage slots after the live records (storage is in handle order,
 //    so a handle is found by binary search), and are merged into the
@@ -66,6 +69,26 @@ struct alignas(16) Range {
 };
 constexpr Range kNoRange{~0ull, 0};
 
+// Range index of the batch's misses, and one of its inserts: buckets of
+// width W = 2^shift over [lo, hi], the smallest and largest start among the
+// misses (inserts are misses, so the same buckets serve both), each bucket
+// holding up to kSlots ranges inline. A range longer than W, or one that
+// finds its bucket full, goes to the long list instead. A range of length
+// at most W that contains [b, t) starts in [b + 1 - W, b], so a query reads
+// at most two buckets, plus the long list (which the pair kernels walk
+// through LDS in tiles, as they walked every earlier range before).
+constexpr uint32_t kSlots = 8;
+constexpr uint32_t kMinBuckets = 64, kMaxBuckets = 16384;
+static_assert((kMaxBuckets & (kMaxBuckets - 1)) == 0, "bucket counts are powers of two");
+
+struct RIdx {
+    uint32_t *cnt;          // ranges placed in each bucket (past kSlots: in the long list)
+    Range *rec;             // [bucket * kSlots + s]: a range of the bucket
+    uint32_t *key;          // [bucket * kSlots + s]: its rank (miss rank or insert rank)
+    uint32_t *lng;          // long list: ranks
+    uint32_t *pre;          // inserts only: in-table ranges of the earlier buckets
+};
+
 // Workspace pieces (pointers into the caller's workspace).
 struct RegWs {
     // per batch item
@@ -81,6 +104,11 @@ struct RegWs {
     uint64_t *ibase, *itop; // rounded range of each insert, by rank
     uint64_t *mbase, *mtop; // rounded range of each miss, by miss rank
     uint32_t *mrank;        // misses before each item
+    // range indexes (misses, inserts); rinfo = {lo, hi}; rcnt = long-list lengths
+    RIdx xm, xi;
+    uint64_t *rinfo;
+    uint32_t *rcnt;
+    uint32_t nbk;           // buckets per index (a power of two)
     // per record (capacity)
     uint64_t *sstart;       // starts in start order
     uint64_t *pm;           // running maximum of ends in start order
@@ -244,6 +272,116 @@ void scan_records(F f, const uint64_t *state, uint64_t capacity, uint64_t *chunk
                        chunk, out);
 }
 
+// ---------------------------------------------------------- range index ---
+
+// The smallest shift s with (hi - lo) >> s < nbk (nbk a power of two).
+__device__ __forceinline__ uint32_t idx_shift(uint64_t lo, uint64_t hi, uint32_t nbk)
+{
+    const uint64_t span = hi > lo ? hi - lo : 0;
+    const uint32_t bl = span ? 64u - (uint32_t)__clzll((long long)span) : 0u;
+    const uint32_t lb = 31u - (uint32_t)__clz((int)nbk);
+    return bl > lb ? bl - lb : 0u;
+}
+
+// Files range [b, t) (b in [lo, hi]) of rank r into index X.
+__device__ __forceinline__ void idx_put(const RIdx &X, uint32_t *nlong, uint64_t lo,
+                                        uint32_t shift, uint64_t b, uint64_t t, uint32_t r)
+{
+    if (t - b <= (1ull << shift)) {
+        const uint32_t c = (uint32_t)((b - lo) >> shift);
+        const uint32_t s = atomicAdd(&X.cnt[c], 1u);
+        if (s < kSlots) {
+            X.rec[(uint64_t)c * kSlots + s] = Range{b, t};
+            X.key[(uint64_t)c * kSlots + s] = r;
+            return;
+        }
+    }
+    X.lng[atomicAdd(nlong, 1u)] = r;
+}
+
+// Buckets [c0, c1] of index X that can hold a range of length <= 2^shift
+// containing a range starting at b; c0 > c1 when there are none.
+__device__ __forceinline__ void idx_window(uint64_t lo, uint64_t hi, uint32_t shift, uint64_t b,
+                                          uint32_t &c0, uint32_t &c1)
+{
+    const uint64_t wd = 1ull << shift;
+    uint64_t xlo = b + 1 >= wd ? b + 1 - wd : 0;       // b is a page start: b + 1 does not wrap
+    if (xlo < lo) xlo = lo;
+    const uint64_t xhi = b < hi ? b : hi;
+    if (xlo > xhi) {
+        c0 = 1;
+        c1 = 0;
+        return;
+    }
+    c0 = (uint32_t)((xlo - lo) >> shift);
+    c1 = (uint32_t)((xhi - lo) >> shift);
+}
+
+// Clears both indexes' bucket counts and long lists, and sets lo / hi for
+// the bounds the classification then narrows.
+__global__ __launch_bounds__(kThreads) void k_ridx_clear(RegWs w)
+{
+    const uint32_t g = blockIdx.x * kThreads + threadIdx.x;
+    if (g < w.nbk) {
+        w.xm.cnt[g] = 0;
+        w.xi.cnt[g] = 0;
+    }
+    if (g == 0) {
+        w.rinfo[0] = ~0ull;
+        w.rinfo[1] = 0;
+        w.rcnt[0] = 0;
+        w.rcnt[1] = 0;
+    }
+}
+
+// One block: pre[c] = in-table inserts of buckets before c. Thread t takes
+// buckets [16t, 16t + 16) (nbk is a multiple of 64, so a thread's buckets
+// are all inside or all past the index) as four 16-byte loads issued
+// together.
+__global__ __launch_bounds__(kTopThreads) void k_ridx_scan(RegWs w)
+{
+    __shared__ uint64_t scr[kTopThreads / kWave];
+    constexpr uint32_t kEach = kMaxBuckets / kTopThreads;
+    static_assert(kEach == 16 && kMinBuckets % kEach == 0, "whole 16-byte rows per thread");
+    const uint32_t c0 = threadIdx.x * kEach;
+    const bool mine = c0 < w.nbk;
+    uint32_t v[kEach], sum = 0;
+    if (mine) {
+        uint4 x[kEach / 4];
+#pragma unroll
+        for (uint32_t q = 0; q < kEach / 4; ++q) x[q] = reinterpret_cast<const uint4 *>(w.xi.cnt + c0)[q];
+#pragma unroll
+        for (uint32_t q = 0; q < kEach / 4; ++q) {
+            v[4 * q] = x[q].x;
+            v[4 * q + 1] = x[q].y;
+            v[4 * q + 2] = x[q].z;
+            v[4 * q + 3] = x[q].w;
+        }
+    } else {
+#pragma unroll
+        for (uint32_t k = 0; k < kEach; ++k) v[k] = 0;
+    }
+#pragma unroll
+    for (uint32_t k = 0; k < kEach; ++k) {
+        v[k] = v[k] < kSlots ? v[k] : kSlots;
+        sum += v[k];
+    }
+    uint64_t tot;
+    uint32_t run = (uint32_t)block_excl<false, kTopThreads>(sum, scr, &tot);
+    if (mine) {
+        uint4 y[kEach / 4];
+#pragma unroll
+        for (uint32_t q = 0; q < kEach / 4; ++q) {
+            y[q].x = run; run += v[4 * q];
+            y[q].y = run; run += v[4 * q + 1];
+            y[q].z = run; run += v[4 * q + 2];
+            y[q].w = run; run += v[4 * q + 3];
+        }
+#pragma unroll
+        for (uint32_t q = 0; q < kEach / 4; ++q) reinterpret_cast<uint4 *>(w.xi.pre + c0)[q] = y[q];
+    }
+}
+
 // ------------------------------------------------------------- register ---
 
 __global__ __launch_bounds__(kThreads) void k_reg_starts(RegState g, RegWs w)
@@ -254,48 +392,79 @@ __global__ __launch_bounds__(kThreads) void k_reg_starts(RegState g, RegWs w)
         w.sstart[p] = g.start[g.by_start[p]];
 }
 
-// Rounding and the lookup in the table as it was before the batch.
+// Rounding and the lookup in the table as it was before the batch; the
+// smallest and largest start among the misses narrow the range indexes'
+// bounds (one atomic pair per block).
 __global__ __launch_bounds__(kThreads) void k_reg_classify(RegState g, RegWs w, uint32_t shift,
                                                            const uint64_t *addr, const uint64_t *size,
                                                            uint32_t n)
 {
+    __shared__ uint64_t s_lo[kWaves], s_hi[kWaves];
     const uint32_t i = blockIdx.x * kThreads + threadIdx.x;
-    if (i >= n) return;
-    const uint64_t count = g.state[0];
-    const uint64_t a = addr[i], l = size[i];
-    const uint64_t page = 1ull << shift;
-    uint8_t c = kMiss;
-    uint64_t base = 0, top = 0;
-    if (l == 0 || l > ~a) {
-        c = kInvalid;
-    } else {
-        base = a & ~(page - 1);
-        const uint64_t last = a + l - 1;                  // no wrap: l <= ~a
-        const uint64_t lastp = last & ~(page - 1);
-        if (lastp > ~0ull - page) c = kInvalid;           // the rounded end would wrap
-        else top = lastp + page;
-    }
-    uint32_t hit = 0;
-    uint64_t hstart = 0;
-    if (c == kMiss && count) {
-        // First p with pm[p] >= top (pm is non-decreasing).
-        uint64_t lo = 0, hi = count;
-        while (lo < hi) {
-            const uint64_t mid = (lo + hi) >> 1;
-            if (w.pm[mid] >= top) hi = mid;
-            else lo = mid + 1;
+    uint64_t mlo = ~0ull, mhi = 0;
+    if (i < n) {
+        const uint64_t count = g.state[0];
+        const uint64_t a = addr[i], l = size[i];
+        const uint64_t page = 1ull << shift;
+        uint8_t c = kMiss;
+        uint64_t base = 0, top = 0;
+        if (l == 0 || l > ~a) {
+            c = kInvalid;
+        } else {
+            base = a & ~(page - 1);
+            const uint64_t last = a + l - 1;              // no wrap: l <= ~a
+            const uint64_t lastp = last & ~(page - 1);
+            if (lastp > ~0ull - page) c = kInvalid;       // the rounded end would wrap
+            else top = lastp + page;
         }
-        if (lo < count && w.sstart[lo] <= base) {
-            c = kHit;
-            hit = g.by_start[lo];
-            hstart = w.sstart[lo];
+        uint32_t hit = 0;
+        uint64_t hstart = 0;
+        if (c == kMiss && count) {
+            // First p with pm[p] >= top (pm is non-decreasing).
+            uint64_t lo = 0, hi = count;
+            while (lo < hi) {
+                const uint64_t mid = (lo + hi) >> 1;
+                if (w.pm[mid] >= top) hi = mid;
+                else lo = mid + 1;
+            }
+            if (lo < count && w.sstart[lo] <= base) {
+                c = kHit;
+                hit = g.by_start[lo];
+                hstart = w.sstart[lo];
+            }
+        }
+        w.hstart[i] = hstart;
+        w.base[i] = base;
+        w.top[i] = top;
+        w.cls[i] = c;
+        w.hit[i] = hit;
+        if (c == kMiss) {
+            mlo = base;
+            mhi = base;
         }
     }
-    w.hstart[i] = hstart;
-    w.base[i] = base;
-    w.top[i] = top;
-    w.cls[i] = c;
-    w.hit[i] = hit;
+#pragma unroll
+    for (int d = kWave / 2; d >= 1; d >>= 1) {
+        const uint64_t a = __shfl_xor(mlo, d, kWave), b = __shfl_xor(mhi, d, kWave);
+        mlo = a < mlo ? a : mlo;
+        mhi = b > mhi ? b : mhi;
+    }
+    if (lane() == 0) {
+        s_lo[wave()] = mlo;
+        s_hi[wave()] = mhi;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+#pragma unroll
+        for (int k = 1; k < kWaves; ++k) {
+            mlo = s_lo[k] < mlo ? s_lo[k] : mlo;
+            mhi = s_hi[k] > mhi ? s_hi[k] : mhi;
+        }
+        if (mlo <= mhi) {                                // the block holds a miss
+            atomicMin(reinterpret_cast<unsigned long long *>(&w.rinfo[0]), (unsigned long long)mlo);
+            atomicMax(reinterpret_cast<unsigned long long *>(&w.rinfo[1]), (unsigned long long)mhi);
+        }
+    }
 }
 
 // Ranking batch items of one class (misses, then inserts) in batch order: a
@@ -352,9 +521,9 @@ __global__ __launch_bounds__(kThreads) void k_rank_top(RegState g, RegWs w, uint
 }
 
 // Ranks and scatter. Misses: mrank[i] = misses before item i, and each
-// miss's range goes to its rank. Inserts: rank[i] = inserts before item i,
-// newrefs[i] = 1 (by rank; ranks < n), and each insert's range goes to its
-// rank.
+// miss's range goes to its rank and into the misses' index. Inserts:
+// rank[i] = inserts before item i, newrefs[i] = 1 (by rank; ranks < n), and
+// each insert's range goes to its rank and into the inserts' index.
 template <uint8_t kCls>
 __global__ __launch_bounds__(kThreads) void k_rank_apply(RegWs w, uint32_t n)
 {
@@ -377,6 +546,10 @@ __global__ __launch_bounds__(kThreads) void k_rank_apply(RegWs w, uint32_t n)
     uint32_t *rk_out = kCls == kMiss ? w.mrank : w.rank;
     uint64_t *ob = kCls == kMiss ? w.mbase : w.ibase;
     uint64_t *ot = kCls == kMiss ? w.mtop : w.itop;
+    const RIdx &X = kCls == kMiss ? w.xm : w.xi;
+    uint32_t *nlong = w.rcnt + (kCls == kMiss ? 0 : 1);
+    const uint64_t lo = w.rinfo[0];
+    const uint32_t sh = idx_shift(lo, w.rinfo[1], w.nbk);
 #pragma unroll
     for (int k = 0; k < kPer; ++k) {
         const uint32_t i = p + k;
@@ -386,54 +559,108 @@ __global__ __launch_bounds__(kThreads) void k_rank_apply(RegWs w, uint32_t n)
             if (f[k]) {
                 ob[run] = b[k];
                 ot[run] = t[k];
+                idx_put(X, nlong, lo, sh, b[k], t[k], run);
             }
         }
         run += f[k];
     }
 }
 
-// inserted(i) = miss and no earlier miss contains it. The earlier misses are
-// the mrank[i] first entries of the misses' ranges by rank; they pass through
-// LDS 256 at a time. A block holds kPairItems items and each wave compares
-// them with its own quarter of the tile. s_done[l] turns 1 once some wave
-// finds a miss containing item l.
+// Reads the in-table ranges of bucket c of index X (all kSlots slots at
+// once; those past the bucket's count are not used) and calls f(range, rank)
+// for each one the bucket holds.
+template <class F>
+__device__ __forceinline__ void idx_bucket(const RIdx &X, uint32_t c, F f)
+{
+    const uint32_t m = X.cnt[c] < kSlots ? X.cnt[c] : kSlots;
+    Range r[kSlots];
+    uint32_t q[kSlots];
+#pragma unroll
+    for (uint32_t s = 0; s < kSlots; ++s) {
+        r[s] = X.rec[(uint64_t)c * kSlots + s];
+        q[s] = X.key[(uint64_t)c * kSlots + s];
+    }
+#pragma unroll
+    for (uint32_t s = 0; s < kSlots; ++s)
+        if (s < m) f(r[s], q[s]);
+}
+
+// Loads entry j of a long list (rank, then the range by rank), or nothing
+// past its end.
+__device__ __forceinline__ void long_entry(const uint32_t *lng, const uint64_t *rb,
+                                           const uint64_t *rt, uint32_t j, uint32_t nl,
+                                           Range &r, uint32_t &k)
+{
+    if (j < nl) {
+        k = lng[j];
+        r = Range{rb[k], rt[k]};
+    } else {
+        k = UINT32_MAX;
+        r = kNoRange;
+    }
+}
+
+// inserted(i) = miss and no earlier miss contains it. A containing earlier
+// miss is either in the buckets of the misses' index that can hold it,
+// which wave 0 reads for the block's kPairItems items, or in the long list,
+// which passes through LDS 256 at a time, each wave comparing the items with
+// its own quarter of the tile. s_done[l] turns 1 once some wave finds a miss
+// containing item l.
 __global__ __launch_bounds__(kThreads) void k_reg_inserted(RegWs w, uint32_t n)
 {
     __shared__ Range s_r[kThreads];
+    __shared__ uint32_t s_k[kThreads];
     __shared__ uint32_t s_done[kPairItems];
-    __shared__ uint32_t s_jend;
     const uint32_t ln = threadIdx.x % kWave, k0 = threadIdx.x / kWave * kWave;
     const uint32_t i = blockIdx.x * kPairItems + ln;
     const bool me = i < n && w.cls[i] == kMiss;
     const uint64_t b = me ? w.base[i] : 0, t = me ? w.top[i] : 0;
     const uint32_t mi = me ? w.mrank[i] : 0;             // misses before item i
-    if (threadIdx.x == 0) s_jend = 0;
-    if (k0 == 0) s_done[ln] = !me;
+    if (k0 == 0) {
+        bool in = false;
+        if (me) {
+            const uint64_t lo = w.rinfo[0], hi = w.rinfo[1];
+            const uint32_t sh = idx_shift(lo, hi, w.nbk);
+            uint32_t c0, c1;
+            idx_window(lo, hi, sh, b, c0, c1);
+            for (uint32_t c = c0; c <= c1; ++c)
+                idx_bucket(w.xm, c, [&](const Range &r, uint32_t q) {
+                    in |= q < mi && r.base <= b && t <= r.top;
+                });
+        }
+        s_done[ln] = !me || in;
+    }
+    const uint32_t nl = w.rcnt[0];                       // long misses
+    Range nx;
+    uint32_t nk;
+    long_entry(w.xm.lng, w.mbase, w.mtop, threadIdx.x, nl, nx, nk);
     __syncthreads();
-    if (k0 == 0 && me) atomicMax(&s_jend, mi);
-    __syncthreads();
-    const uint32_t jend = s_jend;                        // misses the block needs
-    Range nx = threadIdx.x < jend ? Range{w.mbase[threadIdx.x], w.mtop[threadIdx.x]} : kNoRange;
-    for (uint32_t j0 = 0; j0 < jend; j0 += kThreads) {
+    for (uint32_t j0 = 0; j0 < nl; j0 += kThreads) {
         const bool open = s_done[ln] == 0;
         if (__syncthreads_or(open) == 0) break;          // every item here is decided
         s_r[threadIdx.x] = nx;
-        const uint32_t jx = j0 + kThreads + threadIdx.x;  // next tile, loaded while this one is used
-        nx = jx < jend ? Range{w.mbase[jx], w.mtop[jx]} : kNoRange;
+        s_k[threadIdx.x] = nk;
+        // The next tile, loaded while this one is used.
+        long_entry(w.xm.lng, w.mbase, w.mtop, j0 + kThreads + threadIdx.x, nl, nx, nk);
         __syncthreads();
         if (open) {
-            const uint32_t lim = mi > j0 ? (mi - j0 < kThreads ? mi - j0 : kThreads) : 0;   // rank < mi
+            const uint32_t lim = nl - j0 < kThreads ? nl - j0 : kThreads;
             const uint32_t ke = lim < k0 + kWave ? lim : k0 + kWave;
             bool in = false;
             uint32_t k = k0;
             for (; k + kPairStep <= ke && !in; k += kPairStep) {   // reads in flight together
                 Range r[kPairStep];
+                uint32_t q[kPairStep];
 #pragma unroll
-                for (uint32_t u = 0; u < kPairStep; ++u) r[u] = s_r[k + u];
+                for (uint32_t u = 0; u < kPairStep; ++u) {
+                    r[u] = s_r[k + u];
+                    q[u] = s_k[k + u];
+                }
 #pragma unroll
-                for (uint32_t u = 0; u < kPairStep; ++u) in |= r[u].base <= b && t <= r[u].top;
+                for (uint32_t u = 0; u < kPairStep; ++u)
+                    in |= q[u] < mi && r[u].base <= b && t <= r[u].top;
             }
-            for (; k < ke && !in; ++k) in = s_r[k].base <= b && t <= s_r[k].top;
+            for (; k < ke && !in; ++k) in = s_k[k] < mi && s_r[k].base <= b && t <= s_r[k].top;
             if (in) s_done[ln] = 1;
         }
         __syncthreads();
@@ -442,19 +669,20 @@ __global__ __launch_bounds__(kThreads) void k_reg_inserted(RegWs w, uint32_t n)
 }
 
 // For every range that is not inserted, the earlier insert with the smallest
-// (start, index) that contains it decides between that insert and the old
-// record it hit; and the (start, index) rank of each insert. Both questions
-// are about inserts only, so they walk the inserts' ranges by rank (batch
-// order among inserts), 256 at a time through LDS: item i meets the rank[i]
-// inserts before it, an insert meets all of them, and (start, rank) orders
-// inserts as (start, index) does. Blocks of kPairItems items, each wave on a
-// quarter of every tile, partial answers merged at the end.
+// (start, rank) that contains it decides between that insert and the old
+// record it hit; and the (start, rank) rank of each insert. Both questions
+// are about inserts only: wave 0 reads the buckets of the inserts' index
+// that can hold a containing insert (or, for an insert, its own bucket, the
+// earlier buckets being counted by the index's prefix), and the long list
+// passes through LDS 256 at a time, each wave on a quarter of every tile,
+// partial answers merged at the end. (start, rank) orders inserts as
+// (start, batch index) does.
 __global__ __launch_bounds__(kThreads) void k_reg_owner(RegWs w, uint32_t n)
 {
     __shared__ Range s_r[kThreads];
+    __shared__ uint32_t s_k[kThreads];
     __shared__ uint64_t s_bb[kThreads];
     __shared__ uint32_t s_bj[kThreads];
-    __shared__ uint32_t s_jend;
     const uint32_t ln = threadIdx.x % kWave, k0 = threadIdx.x / kWave * kWave;
     const uint32_t i = blockIdx.x * kPairItems + ln;
     const uint8_t c = i < n ? w.cls[i] : kInvalid;
@@ -465,73 +693,81 @@ __global__ __launch_bounds__(kThreads) void k_reg_owner(RegWs w, uint32_t n)
     const uint32_t ri = look || ins ? w.rank[i] : 0;     // inserts before item i
     uint32_t best = UINT32_MAX, brank = 0;
     uint64_t bbase = 0;
-    // Inserts the block needs: all of them if it holds one, else those
-    // before its last looking item.
-    if (threadIdx.x == 0) s_jend = 0;
-    __syncthreads();
-    if (k0 == 0 && (look || ins)) atomicMax(&s_jend, ins ? (uint32_t)w.scal[0] : ri);
-    __syncthreads();
-    const uint32_t jend = s_jend;
-    if (jend == 0) return;                               // uniform over the block
-    Range nx = threadIdx.x < jend ? Range{w.ibase[threadIdx.x], w.itop[threadIdx.x]} : kNoRange;
-    for (uint32_t j0 = 0; j0 < jend; j0 += kThreads) {
-        s_r[threadIdx.x] = nx;
-        const uint32_t jx = j0 + kThreads + threadIdx.x;  // next tile, loaded while this one is used
-        nx = jx < jend ? Range{w.ibase[jx], w.itop[jx]} : kNoRange;
-        __syncthreads();
-        const uint32_t lim = jend - j0 < kThreads ? jend - j0 : kThreads;
+    // Takes insert q (range r) if it contains item i and comes first so far.
+    auto consider = [&](const Range &r, uint32_t q) {
+        if (q < ri && r.base <= b && t <= r.top &&
+            (best == UINT32_MAX || r.base < bbase || (r.base == bbase && q < best))) {
+            best = q;
+            bbase = r.base;
+        }
+    };
+    auto before = [&](const Range &r, uint32_t q) -> uint32_t {
+        return r.base < b || (r.base == b && q < ri);
+    };
+    if (k0 == 0 && (look || ins)) {
+        const uint64_t lo = w.rinfo[0], hi = w.rinfo[1];
+        const uint32_t sh = idx_shift(lo, hi, w.nbk);
         if (look) {
-            const uint32_t jl = ri > j0 ? (ri - j0 < lim ? ri - j0 : lim) : 0;   // rank < ri
-            const uint32_t ke = jl < k0 + kWave ? jl : k0 + kWave;
-            uint32_t k = k0;
-            for (; k + kPairStep <= ke; k += kPairStep) {
-                Range r[kPairStep];
+            uint32_t c0, c1;
+            idx_window(lo, hi, sh, b, c0, c1);
+            for (uint32_t cb = c0; cb <= c1; ++cb) idx_bucket(w.xi, cb, consider);
+        } else {
+            const uint32_t cb = (uint32_t)((b - lo) >> sh);   // an insert's start is in [lo, hi]
+            brank = w.xi.pre[cb];
+            idx_bucket(w.xi, cb, [&](const Range &r, uint32_t q) { brank += before(r, q); });
+        }
+    }
+    const uint32_t nl = w.rcnt[1];                       // long inserts
+    if (nl != 0) {                                       // uniform over the block
+        Range nx;
+        uint32_t nk;
+        long_entry(w.xi.lng, w.ibase, w.itop, threadIdx.x, nl, nx, nk);
+        for (uint32_t j0 = 0; j0 < nl; j0 += kThreads) {
+            s_r[threadIdx.x] = nx;
+            s_k[threadIdx.x] = nk;
+            long_entry(w.xi.lng, w.ibase, w.itop, j0 + kThreads + threadIdx.x, nl, nx, nk);
+            __syncthreads();
+            const uint32_t lim = nl - j0 < kThreads ? nl - j0 : kThreads;
+            const uint32_t ke = lim < k0 + kWave ? lim : k0 + kWave;
+            if (look || ins) {
+                uint32_t k = k0;
+                for (; k + kPairStep <= ke; k += kPairStep) {
+                    Range r[kPairStep];
+                    uint32_t q[kPairStep];
 #pragma unroll
-                for (uint32_t u = 0; u < kPairStep; ++u) r[u] = s_r[k + u];
-#pragma unroll
-                for (uint32_t u = 0; u < kPairStep; ++u)
-                    if (r[u].base <= b && t <= r[u].top && (best == UINT32_MAX || r[u].base < bbase)) {
-                        best = j0 + k + u;
-                        bbase = r[u].base;
+                    for (uint32_t u = 0; u < kPairStep; ++u) {
+                        r[u] = s_r[k + u];
+                        q[u] = s_k[k + u];
                     }
-            }
-            for (; k < ke; ++k) {
-                const Range r = s_r[k];
-                if (r.base <= b && t <= r.top && (best == UINT32_MAX || r.base < bbase)) {
-                    best = j0 + k;
-                    bbase = r.base;
+#pragma unroll
+                    for (uint32_t u = 0; u < kPairStep; ++u) {
+                        if (look) consider(r[u], q[u]);
+                        else brank += before(r[u], q[u]);
+                    }
+                }
+                for (; k < ke; ++k) {
+                    if (look) consider(s_r[k], s_k[k]);
+                    else brank += before(s_r[k], s_k[k]);
                 }
             }
-        } else if (ins) {
-            const uint32_t ke = lim < k0 + kWave ? lim : k0 + kWave;
-            uint32_t k = k0;
-            for (; k + kPairStep <= ke; k += kPairStep) {
-                uint64_t rb[kPairStep];
-#pragma unroll
-                for (uint32_t u = 0; u < kPairStep; ++u) rb[u] = s_r[k + u].base;
-#pragma unroll
-                for (uint32_t u = 0; u < kPairStep; ++u) brank += rb[u] < b || (rb[u] == b && j0 + k + u < ri);
-            }
-            for (; k < ke; ++k) {
-                const uint64_t rb = s_r[k].base;
-                brank += rb < b || (rb == b && j0 + k < ri);
-            }
+            __syncthreads();
         }
+        s_bb[threadIdx.x] = bbase;
+        s_bj[threadIdx.x] = look ? best : brank;
         __syncthreads();
     }
-    s_bb[threadIdx.x] = bbase;
-    s_bj[threadIdx.x] = look ? best : brank;
-    __syncthreads();
     if (k0 != 0 || !(look || ins)) return;
-    for (uint32_t v = kWave; v < kThreads; v += kWave) {
-        const uint32_t oj = s_bj[v + ln];
-        const uint64_t ob = s_bb[v + ln];
-        if (ins) {
-            brank += oj;
-        } else if (oj != UINT32_MAX &&
-                   (best == UINT32_MAX || ob < bbase || (ob == bbase && oj < best))) {
-            best = oj;
-            bbase = ob;
+    if (nl != 0) {
+        for (uint32_t v = kWave; v < kThreads; v += kWave) {
+            const uint32_t oj = s_bj[v + ln];
+            const uint64_t ob = s_bb[v + ln];
+            if (ins) {
+                brank += oj;
+            } else if (oj != UINT32_MAX &&
+                       (best == UINT32_MAX || ob < bbase || (ob == bbase && oj < best))) {
+                best = oj;
+                bbase = ob;
+            }
         }
     }
     if (c == kMiss || (c == kHit && best != UINT32_MAX && bbase < w.hstart[i])) {
@@ -777,6 +1013,14 @@ struct Carver {
     }
 };
 
+// Buckets of the range indexes for a batch of n: a power of two near n / 4.
+uint32_t reg_buckets(uint64_t n)
+{
+    uint32_t b = kMinBuckets;
+    while (b < n / 4 && b < kMaxBuckets) b <<= 1;
+    return b;
+}
+
 // Lays the workspace out for a batch of n items and a table of cap records;
 // *bytes receives the end of the walk, which is what the workspace must hold.
 RegWs carve(void *ws, uint64_t n, uint64_t cap, size_t *bytes = nullptr)
@@ -798,6 +1042,17 @@ RegWs carve(void *ws, uint64_t n, uint64_t cap, size_t *bytes = nullptr)
     w.mbase = c.take<uint64_t>(n);
     w.mtop = c.take<uint64_t>(n);
     w.mrank = c.take<uint32_t>(n);
+    w.nbk = reg_buckets(n);
+    for (RIdx *x : {&w.xm, &w.xi}) {
+        x->cnt = c.take<uint32_t>(w.nbk);
+        x->rec = c.take<Range>((uint64_t)w.nbk * kSlots);
+        x->key = c.take<uint32_t>((uint64_t)w.nbk * kSlots);
+        x->lng = c.take<uint32_t>(n);
+    }
+    w.xm.pre = nullptr;
+    w.xi.pre = c.take<uint32_t>(w.nbk);
+    w.rinfo = c.take<uint64_t>(2);
+    w.rcnt = c.take<uint32_t>(2);
     w.sstart = c.take<uint64_t>(cap);
     w.pm = c.take<uint64_t>(cap);
     w.merged = c.take<uint32_t>(cap + n);
@@ -843,6 +1098,8 @@ hipError_t launch_reg_register(const RegArgs &a, hipStream_t s)
                                  nullptr, s);
     }
     if (nb) {
+        hipLaunchKernelGGL(k_ridx_clear, dim3((w.nbk + kThreads - 1) / kThreads), dim3(kThreads),
+                           0, s, w);
         hipLaunchKernelGGL(k_reg_classify, dim3(nb), dim3(kThreads), 0, s, g, w, a.page_shift,
                            a.addr, a.size, n);
         hipLaunchKernelGGL(k_rank_chunks<kMiss>, dim3(cb), dim3(kThreads), 0, s, w, n);
@@ -854,6 +1111,7 @@ hipError_t launch_reg_register(const RegArgs &a, hipStream_t s)
     hipLaunchKernelGGL(k_rank_top<true>, dim3(1), dim3(kThreads), 0, s, g, w, n, a.needed);
     if (nb) hipLaunchKernelGGL(k_rank_apply<kNew>, dim3(cb), dim3(kThreads), 0, s, w, n);
     if (nb) {
+        hipLaunchKernelGGL(k_ridx_scan, dim3(1), dim3(kTopThreads), 0, s, w);
         hipLaunchKernelGGL(k_reg_owner, dim3(pb), dim3(kThreads), 0, s, w, n);
         hipLaunchKernelGGL(k_reg_apply, dim3(nb), dim3(kThreads), 0, s, g, w, n, a.handle,
                            a.kind);

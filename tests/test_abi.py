@@ -284,10 +284,20 @@ def test_registry_workspace_holds_every_piece(n, cap):
     # columns (hit slot, rank, start rank, owner, new references, miss rank);
     # per record five u64 columns (starts, running maximum, three scratch)
     # and two u32 (new slot, scratch), the merged index over records and
-    # items (u32), 16,384 chunk totals and four scalars. A workspace of
-    # dmadesc_workspace_bytes must hold all of them.
+    # items (u32), 16,384 chunk totals and four scalars; and two range
+    # indexes over the batch (misses, inserts), each with nbk buckets (a power
+    # of two near n / 4, 64..16,384) of a u32 count and 8 inline ranges
+    # (16 bytes) with their u32 ranks, and a u32 long list per item, plus the
+    # inserts' bucket prefixes (u32 per bucket), the bounds (two u64) and the
+    # two long-list lengths. A workspace of dmadesc_workspace_bytes must hold
+    # all of them.
+    nbk = 64
+    while nbk < n // 4 and nbk < 16384:
+        nbk *= 2
+    index = 2 * (_a256(4 * nbk) + _a256(16 * 8 * nbk) + _a256(4 * 8 * nbk) + _a256(4 * n))
     need = (8 * _a256(8 * n) + _a256(n) + 6 * _a256(4 * n) + 5 * _a256(8 * cap)
-            + 2 * _a256(4 * cap) + _a256(4 * (cap + n)) + _a256(8 * 16384) + _a256(32))
+            + 2 * _a256(4 * cap) + _a256(4 * (cap + n)) + _a256(8 * 16384) + _a256(32)
+            + index + _a256(4 * nbk) + _a256(16) + _a256(8))
     assert dd.workspace_bytes(dd.OP_REGISTRY, n, cap) >= need, (n, cap)
 
 

@@ -147,6 +147,69 @@ def test_full_batch_on_a_large_table():
     p.deregister(rng.choice(h[h > 0], n), "full deregister")
 
 
+def _pages(x):
+    return np.asarray(x, np.uint64) * np.uint64(4096)
+
+
+def test_crowded_buckets_long_ranges_and_a_wide_span():
+    # The batch relations go through a bucketed index of the batch's ranges:
+    # a bucket holds a few ranges inline and sends the rest, and ranges longer
+    # than a bucket, to a list every query walks. These batches crowd one
+    # bucket far past its inline slots (identical and nested small ranges),
+    # mix in ranges longer than a bucket, repeats and hits, and then spread
+    # starts over the whole 64-bit space.
+    rng = np.random.default_rng(7)
+    p = Pair()
+    table = _pages(np.arange(64, dtype=np.uint64) << np.uint64(22))      # 64 regions, 16 GiB apart
+    p.register(table, np.full(64, 4 * M, np.uint64), "table")
+    n = 20_000
+    hot = np.uint64(0x50_0000_0000)
+    k = rng.integers(0, 10, n)
+    starts = np.zeros(n, np.uint64)
+    sizes = np.zeros(n, np.uint64)
+    crowd = k < 3                                   # the same few pages
+    starts[crowd] = hot + _pages(rng.integers(0, 4, crowd.sum()))
+    sizes[crowd] = 4096
+    nest = (k >= 3) & (k < 5)                       # ranges around the crowd
+    m = int(nest.sum())
+    starts[nest] = hot - _pages(rng.integers(0, 8, m))
+    sizes[nest] = _pages(rng.integers(1, 24, m))
+    long_ = k == 5                                  # longer than a bucket
+    m = int(long_.sum())
+    starts[long_] = _pages(rng.integers(1 << 29, 1 << 30, m))
+    sizes[long_] = _pages(rng.integers(1 << 17, 1 << 21, m))
+    short = k == 6
+    m = int(short.sum())
+    starts[short] = _pages(rng.integers(1 << 28, 1 << 29, m)) + rng.integers(0, 4096, m).astype(np.uint64)
+    sizes[short] = rng.integers(1, 1 << 20, m).astype(np.uint64)
+    hits = k == 7                                   # inside the table's regions
+    m = int(hits.sum())
+    starts[hits] = table[rng.integers(0, 64, m)] + _pages(rng.integers(0, 512, m))
+    sizes[hits] = _pages(rng.integers(1, 256, m))
+    rep = k >= 8                                    # repeats of earlier items
+    idx = np.nonzero(rep)[0]
+    own = np.nonzero(~rep)[0]
+    src = own[(rng.random(len(idx)) * np.searchsorted(own, idx)).astype(np.int64)]
+    starts[idx] = starts[src]
+    sizes[idx] = sizes[src]
+    sizes[rng.random(n) < 0.005] = 0
+    h, kd = p.register(starts, sizes, "crowded")
+    assert (kd == oracle.REG_HIT_NEW).sum() > 1000 and (kd == oracle.REG_NEW).sum() > 1000
+    live = h[h > 0]
+    p.deregister(rng.choice(live, 4000), "crowded deregister")
+    # Starts over the whole space, with ranges at both ends of it.
+    n = 8192
+    starts = rng.integers(0, 1 << 63, n, dtype=np.uint64) * np.uint64(2) + \
+        rng.integers(0, 2, n).astype(np.uint64)
+    sizes = rng.integers(1, 1 << 30, n).astype(np.uint64)
+    starts[:16] = np.arange(16, dtype=np.uint64) * np.uint64(4096)
+    starts[16:32] = np.uint64((1 << 64) - (1 << 24)) + _pages(np.arange(16))
+    sizes[16:32] = 4096
+    starts[32:4096] = starts[rng.integers(0, 32, 4064)]
+    sizes[32:4096] = sizes[rng.integers(0, 32, 4064)]
+    p.register(starts, sizes, "wide span")
+
+
 def test_empty_batches_and_empty_table():
     p = Pair()
     p.register(np.zeros(0, np.uint64), np.zeros(0, np.uint64), "empty register")
