@@ -73,21 +73,24 @@ constexpr Range kNoRange{~0ull, 0};
 // width W = 2^shift over [lo, hi], the smallest and largest start among the
 // misses (inserts are misses, so the same buckets serve both), each bucket
 // holding up to kSlots ranges inline. A range longer than W, or one that
-// finds its bucket full, goes to the long list instead. A range of length
-// at most W that contains [b, t) starts in [b + 1 - W, b], so a query reads
-// at most two buckets, plus the long list (which the pair kernels walk
-// through LDS in tiles, as they walked every earlier range before).
+// finds its bucket full, is flagged long instead. A range of length at most
+// W that contains [b, t) starts in [b + 1 - W, b], so a query reads at most
+// two buckets, plus the long ranges, which the pair kernels walk in rank
+// order through LDS tiles as they walked every earlier range before,
+// skipping the 256-rank tiles that hold none.
 constexpr uint32_t kSlots = 8;
 constexpr uint32_t kMinBuckets = 64, kMaxBuckets = 16384;
 static_assert((kMaxBuckets & (kMaxBuckets - 1)) == 0, "bucket counts are powers of two");
 
 struct RIdx {
-    uint32_t *cnt;          // ranges placed in each bucket (past kSlots: in the long list)
+    uint32_t *cnt;          // ranges filed to each bucket (past kSlots: flagged long)
     Range *rec;             // [bucket * kSlots + s]: a range of the bucket
     uint32_t *key;          // [bucket * kSlots + s]: its rank (miss rank or insert rank)
-    uint32_t *lng;          // long list: ranks
+    uint8_t *lflag;         // by rank: 1 if the range is long (not in a bucket)
+    uint32_t *tlong;        // long ranges per 256-rank tile
     uint32_t *pre;          // inserts only: in-table ranges of the earlier buckets
 };
+constexpr uint32_t kRankTiles = DMADESC_REG_MAX_BATCH / 256;
 
 // Workspace pieces (pointers into the caller's workspace).
 struct RegWs {
@@ -104,9 +107,11 @@ struct RegWs {
     uint64_t *ibase, *itop; // rounded range of each insert, by rank
     uint64_t *mbase, *mtop; // rounded range of each miss, by miss rank
     uint32_t *mrank;        // misses before each item
-    // range indexes (misses, inserts); rinfo = {lo, hi}; rcnt = long-list lengths
+    // range indexes (misses, inserts); rinfo = {lo, hi}; rcnt = long ranges
+    // of each index
     RIdx xm, xi;
     uint64_t *rinfo;
+    uint64_t *bmin, *bmax;  // per classification block: smallest / largest miss start
     uint32_t *rcnt;
     uint32_t nbk;           // buckets per index (a power of two)
     // per record (capacity)
@@ -283,9 +288,11 @@ __device__ __forceinline__ uint32_t idx_shift(uint64_t lo, uint64_t hi, uint32_t
     return bl > lb ? bl - lb : 0u;
 }
 
-// Files range [b, t) (b in [lo, hi]) of rank r into index X.
-__device__ __forceinline__ void idx_put(const RIdx &X, uint32_t *nlong, uint64_t lo,
-                                        uint32_t shift, uint64_t b, uint64_t t, uint32_t r)
+// Files range [b, t) (b in [lo, hi]) of rank r into index X; true if it is
+// long (the caller counts those per tile and in all, a few atomics per wave:
+// one word that every long range of the launch added to would serialize).
+__device__ __forceinline__ bool idx_put(const RIdx &X, uint64_t lo, uint32_t shift, uint64_t b,
+                                        uint64_t t, uint32_t r)
 {
     if (t - b <= (1ull << shift)) {
         const uint32_t c = (uint32_t)((b - lo) >> shift);
@@ -293,10 +300,12 @@ __device__ __forceinline__ void idx_put(const RIdx &X, uint32_t *nlong, uint64_t
         if (s < kSlots) {
             X.rec[(uint64_t)c * kSlots + s] = Range{b, t};
             X.key[(uint64_t)c * kSlots + s] = r;
-            return;
+            X.lflag[r] = 0;
+            return false;
         }
     }
-    X.lng[atomicAdd(nlong, 1u)] = r;
+    X.lflag[r] = 1;
+    return true;
 }
 
 // Buckets [c0, c1] of index X that can hold a range of length <= 2^shift
@@ -317,8 +326,7 @@ __device__ __forceinline__ void idx_window(uint64_t lo, uint64_t hi, uint32_t sh
     c1 = (uint32_t)((xhi - lo) >> shift);
 }
 
-// Clears both indexes' bucket counts and long lists, and sets lo / hi for
-// the bounds the classification then narrows.
+// Clears both indexes' bucket counts, long-tile counts and long counts.
 __global__ __launch_bounds__(kThreads) void k_ridx_clear(RegWs w)
 {
     const uint32_t g = blockIdx.x * kThreads + threadIdx.x;
@@ -326,9 +334,11 @@ __global__ __launch_bounds__(kThreads) void k_ridx_clear(RegWs w)
         w.xm.cnt[g] = 0;
         w.xi.cnt[g] = 0;
     }
+    if (g < kRankTiles) {
+        w.xm.tlong[g] = 0;
+        w.xi.tlong[g] = 0;
+    }
     if (g == 0) {
-        w.rinfo[0] = ~0ull;
-        w.rinfo[1] = 0;
         w.rcnt[0] = 0;
         w.rcnt[1] = 0;
     }
@@ -392,9 +402,9 @@ __global__ __launch_bounds__(kThreads) void k_reg_starts(RegState g, RegWs w)
         w.sstart[p] = g.start[g.by_start[p]];
 }
 
-// Rounding and the lookup in the table as it was before the batch; the
-// smallest and largest start among the misses narrow the range indexes'
-// bounds (one atomic pair per block).
+// Rounding and the lookup in the table as it was before the batch; each
+// block also stores the smallest and largest start among its misses, which
+// the misses' ranking kernel reduces to the range indexes' bounds.
 __global__ __launch_bounds__(kThreads) void k_reg_classify(RegState g, RegWs w, uint32_t shift,
                                                            const uint64_t *addr, const uint64_t *size,
                                                            uint32_t n)
@@ -460,10 +470,8 @@ __global__ __launch_bounds__(kThreads) void k_reg_classify(RegState g, RegWs w, 
             mlo = s_lo[k] < mlo ? s_lo[k] : mlo;
             mhi = s_hi[k] > mhi ? s_hi[k] : mhi;
         }
-        if (mlo <= mhi) {                                // the block holds a miss
-            atomicMin(reinterpret_cast<unsigned long long *>(&w.rinfo[0]), (unsigned long long)mlo);
-            atomicMax(reinterpret_cast<unsigned long long *>(&w.rinfo[1]), (unsigned long long)mhi);
-        }
+        w.bmin[blockIdx.x] = mlo;                        // ~0 and 0 for a block without misses
+        w.bmax[blockIdx.x] = mhi;
     }
 }
 
@@ -497,8 +505,10 @@ __global__ __launch_bounds__(kThreads) void k_rank_chunks(RegWs w, uint32_t n)
     if (threadIdx.x == 0) w.ichunk[blockIdx.x] = tot;
 }
 
-// One block: the chunk counts become exclusive prefixes. For the inserts
-// (kCount) it also records their number, whether the table has room, and the
+// One block: the chunk counts become exclusive prefixes. For the misses it
+// also reduces the classification blocks' start bounds to the range
+// indexes' [lo, hi] (lo > hi when there is no miss); for the inserts
+// (kCount) it records their number, whether the table has room, and the
 // capacity the growth rule reaches (reported either way).
 template <bool kCount>
 __global__ __launch_bounds__(kThreads) void k_rank_top(RegState g, RegWs w, uint32_t n,
@@ -510,6 +520,18 @@ __global__ __launch_bounds__(kThreads) void k_rank_top(RegState g, RegWs w, uint
     uint64_t tot;
     const uint64_t ex = block_excl<false, kThreads>(v, scr, &tot);
     if (threadIdx.x < nch) w.ichunk[threadIdx.x] = ex;
+    if (!kCount) {
+        const uint32_t ncb = (n + kThreads - 1) / kThreads;        // classification blocks
+        const uint64_t nlo = threadIdx.x < ncb ? ~w.bmin[threadIdx.x] : 0;   // min as ~max(~x)
+        const uint64_t mhi = threadIdx.x < ncb ? w.bmax[threadIdx.x] : 0;
+        uint64_t a, b;
+        block_excl<true, kThreads>(nlo, scr, &a);
+        block_excl<true, kThreads>(mhi, scr, &b);
+        if (threadIdx.x == 0) {
+            w.rinfo[0] = ~a;
+            w.rinfo[1] = b;
+        }
+    }
     if (kCount && threadIdx.x == 0) {
         const uint64_t after = g.state[0] + tot;
         uint64_t need = g.capacity;
@@ -550,6 +572,10 @@ __global__ __launch_bounds__(kThreads) void k_rank_apply(RegWs w, uint32_t n)
     uint32_t *nlong = w.rcnt + (kCls == kMiss ? 0 : 1);
     const uint64_t lo = w.rinfo[0];
     const uint32_t sh = idx_shift(lo, w.rinfo[1], w.nbk);
+    // The wave's ranks are at most 256 consecutive ones from lane 0's first:
+    // they fall in 256-rank tile bt or bt + 1.
+    const uint32_t bt = __shfl(run, 0, kWave) / 256;
+    uint32_t l0 = 0, l1 = 0;
 #pragma unroll
     for (int k = 0; k < kPer; ++k) {
         const uint32_t i = p + k;
@@ -559,10 +585,19 @@ __global__ __launch_bounds__(kThreads) void k_rank_apply(RegWs w, uint32_t n)
             if (f[k]) {
                 ob[run] = b[k];
                 ot[run] = t[k];
-                idx_put(X, nlong, lo, sh, b[k], t[k], run);
+                if (idx_put(X, lo, sh, b[k], t[k], run)) {
+                    if (run / 256 == bt) ++l0;
+                    else ++l1;
+                }
             }
         }
         run += f[k];
+    }
+    const uint32_t w0 = wave_sum(l0), w1 = wave_sum(l1);
+    if (lane() == 0) {
+        if (w0 + w1) atomicAdd(nlong, w0 + w1);
+        if (w0) atomicAdd(&X.tlong[bt], w0);
+        if (w1) atomicAdd(&X.tlong[bt + 1], w1);
     }
 }
 
@@ -585,37 +620,79 @@ __device__ __forceinline__ void idx_bucket(const RIdx &X, uint32_t c, F f)
         if (s < m) f(r[s], q[s]);
 }
 
-// Loads entry j of a long list (rank, then the range by rank), or nothing
-// past its end.
-__device__ __forceinline__ void long_entry(const uint32_t *lng, const uint64_t *rb,
-                                           const uint64_t *rt, uint32_t j, uint32_t nl,
-                                           Range &r, uint32_t &k)
+// Range of rank r for a tile of the long walk: the range itself if it is
+// flagged long, else one that contains nothing (its bucket already answered
+// for it). r is clamped, not guarded, so the three loads go out together.
+__device__ __forceinline__ Range long_range(const RIdx &X, const uint64_t *rb, const uint64_t *rt,
+                                            uint32_t r, uint32_t jend)
 {
-    if (j < nl) {
-        k = lng[j];
-        r = Range{rb[k], rt[k]};
-    } else {
-        k = UINT32_MAX;
-        r = kNoRange;
+    const uint32_t q = r < jend ? r : jend - 1;
+    const uint8_t f = X.lflag[q];
+    const Range x{rb[q], rt[q]};
+    return r < jend && f ? x : kNoRange;
+}
+static_assert(kRankTiles == kThreads, "one long-tile count per thread");
+
+// The 256-rank tiles that hold a long range, listed in rank order so that the
+// walks visit only those: thread t tests tile t; part 1 counts each wave's
+// tiles (a ballot), part 2 (after a barrier) writes the list and returns its
+// length.
+struct TileList {
+    uint32_t list[kRankTiles];
+    uint32_t wcnt[kWaves];
+};
+__device__ __forceinline__ uint64_t tiles_part1(TileList &L, const uint32_t *tlong)
+{
+    const uint64_t bal = __ballot(tlong[threadIdx.x] != 0);
+    if (lane() == 0) L.wcnt[wave()] = (uint32_t)__popcll(bal);
+    return bal;
+}
+// Listed tiles that start before rank jend (the list is in rank order).
+__device__ __forceinline__ uint32_t tiles_before(const TileList &L, uint32_t ntl, uint32_t jend)
+{
+    uint32_t lo = 0, hi = ntl;
+    while (lo < hi) {
+        const uint32_t mid = (lo + hi) >> 1;
+        if (L.list[mid] * kThreads < jend) lo = mid + 1;
+        else hi = mid;
     }
+    return lo;
+}
+__device__ __forceinline__ uint32_t tiles_part2(TileList &L, uint64_t bal)
+{
+    uint32_t off = 0, all = 0;
+#pragma unroll
+    for (int v = 0; v < kWaves; ++v) {
+        off += v < wave() ? L.wcnt[v] : 0u;
+        all += L.wcnt[v];
+    }
+    const uint64_t below = lane() ? (~0ull >> (64 - lane())) : 0ull;
+    if ((bal >> lane()) & 1ull) L.list[off + (uint32_t)__popcll(bal & below)] = threadIdx.x;
+    return all;
 }
 
 // inserted(i) = miss and no earlier miss contains it. A containing earlier
 // miss is either in the buckets of the misses' index that can hold it,
-// which wave 0 reads for the block's kPairItems items, or in the long list,
-// which passes through LDS 256 at a time, each wave comparing the items with
-// its own quarter of the tile. s_done[l] turns 1 once some wave finds a miss
-// containing item l.
+// which wave 0 reads for the block's kPairItems items, or long; the long
+// ones are walked in rank order through LDS 256 ranks at a time (tiles
+// without one are skipped), each wave comparing the items still open with
+// its own quarter of the tile, up to the largest miss rank among them.
+// s_done[l] turns 1 once item l is decided.
 __global__ __launch_bounds__(kThreads) void k_reg_inserted(RegWs w, uint32_t n)
 {
     __shared__ Range s_r[kThreads];
-    __shared__ uint32_t s_k[kThreads];
     __shared__ uint32_t s_done[kPairItems];
+    __shared__ TileList s_tl;
+    __shared__ uint32_t s_jend;
     const uint32_t ln = threadIdx.x % kWave, k0 = threadIdx.x / kWave * kWave;
     const uint32_t i = blockIdx.x * kPairItems + ln;
     const bool me = i < n && w.cls[i] == kMiss;
     const uint64_t b = me ? w.base[i] : 0, t = me ? w.top[i] : 0;
     const uint32_t mi = me ? w.mrank[i] : 0;             // misses before item i
+    const bool walk = w.rcnt[0] != 0;                    // any long miss (uniform)
+    if (!walk && k0 != 0) return;                        // the buckets alone decide
+    if (threadIdx.x == 0) s_jend = 0;
+    const uint64_t bal = walk ? tiles_part1(s_tl, w.xm.tlong) : 0;
     if (k0 == 0) {
         bool in = false;
         if (me) {
@@ -628,39 +705,41 @@ __global__ __launch_bounds__(kThreads) void k_reg_inserted(RegWs w, uint32_t n)
                     in |= q < mi && r.base <= b && t <= r.top;
                 });
         }
+        if (!walk) {
+            if (me && !in) w.cls[i] = kNew;
+            return;
+        }
         s_done[ln] = !me || in;
     }
-    const uint32_t nl = w.rcnt[0];                       // long misses
-    Range nx;
-    uint32_t nk;
-    long_entry(w.xm.lng, w.mbase, w.mtop, threadIdx.x, nl, nx, nk);
     __syncthreads();
-    for (uint32_t j0 = 0; j0 < nl; j0 += kThreads) {
+    const uint32_t ntl = tiles_part2(s_tl, bal);
+    if (k0 == 0 && s_done[ln] == 0) atomicMax(&s_jend, mi);
+    __syncthreads();
+    const uint32_t jend = s_jend;                        // ranks the open items need
+    const uint32_t nt = tiles_before(s_tl, ntl, jend);   // tiles to walk
+    Range nx = nt ? long_range(w.xm, w.mbase, w.mtop, s_tl.list[0] * kThreads + threadIdx.x, jend)
+                  : kNoRange;
+    for (uint32_t u = 0; u < nt; ++u) {
+        const uint32_t j0 = s_tl.list[u] * kThreads;     // a tile holding a long miss
         const bool open = s_done[ln] == 0;
         if (__syncthreads_or(open) == 0) break;          // every item here is decided
         s_r[threadIdx.x] = nx;
-        s_k[threadIdx.x] = nk;
-        // The next tile, loaded while this one is used.
-        long_entry(w.xm.lng, w.mbase, w.mtop, j0 + kThreads + threadIdx.x, nl, nx, nk);
+        if (u + 1 < nt)                                  // the next tile, loaded while this one is used
+            nx = long_range(w.xm, w.mbase, w.mtop, s_tl.list[u + 1] * kThreads + threadIdx.x, jend);
         __syncthreads();
         if (open) {
-            const uint32_t lim = nl - j0 < kThreads ? nl - j0 : kThreads;
+            const uint32_t lim = mi > j0 ? (mi - j0 < kThreads ? mi - j0 : kThreads) : 0;   // rank < mi
             const uint32_t ke = lim < k0 + kWave ? lim : k0 + kWave;
             bool in = false;
             uint32_t k = k0;
             for (; k + kPairStep <= ke && !in; k += kPairStep) {   // reads in flight together
                 Range r[kPairStep];
-                uint32_t q[kPairStep];
 #pragma unroll
-                for (uint32_t u = 0; u < kPairStep; ++u) {
-                    r[u] = s_r[k + u];
-                    q[u] = s_k[k + u];
-                }
+                for (uint32_t u = 0; u < kPairStep; ++u) r[u] = s_r[k + u];
 #pragma unroll
-                for (uint32_t u = 0; u < kPairStep; ++u)
-                    in |= q[u] < mi && r[u].base <= b && t <= r[u].top;
+                for (uint32_t u = 0; u < kPairStep; ++u) in |= r[u].base <= b && t <= r[u].top;
             }
-            for (; k < ke && !in; ++k) in = s_k[k] < mi && s_r[k].base <= b && t <= s_r[k].top;
+            for (; k < ke && !in; ++k) in = s_r[k].base <= b && t <= s_r[k].top;
             if (in) s_done[ln] = 1;
         }
         __syncthreads();
@@ -673,16 +752,19 @@ __global__ __launch_bounds__(kThreads) void k_reg_inserted(RegWs w, uint32_t n)
 // record it hit; and the (start, rank) rank of each insert. Both questions
 // are about inserts only: wave 0 reads the buckets of the inserts' index
 // that can hold a containing insert (or, for an insert, its own bucket, the
-// earlier buckets being counted by the index's prefix), and the long list
-// passes through LDS 256 at a time, each wave on a quarter of every tile,
-// partial answers merged at the end. (start, rank) orders inserts as
-// (start, batch index) does.
+// earlier buckets being counted by the index's prefix), and the long
+// inserts are walked in rank order through LDS 256 ranks at a time (tiles
+// without one are skipped), each wave on a quarter of every tile, partial
+// answers merged at the end: item i meets the rank[i] inserts before it, an
+// insert meets all of them. (start, rank) orders inserts as (start, batch
+// index) does.
 __global__ __launch_bounds__(kThreads) void k_reg_owner(RegWs w, uint32_t n)
 {
     __shared__ Range s_r[kThreads];
-    __shared__ uint32_t s_k[kThreads];
     __shared__ uint64_t s_bb[kThreads];
     __shared__ uint32_t s_bj[kThreads];
+    __shared__ TileList s_tl;
+    __shared__ uint32_t s_jend;
     const uint32_t ln = threadIdx.x % kWave, k0 = threadIdx.x / kWave * kWave;
     const uint32_t i = blockIdx.x * kPairItems + ln;
     const uint8_t c = i < n ? w.cls[i] : kInvalid;
@@ -701,9 +783,15 @@ __global__ __launch_bounds__(kThreads) void k_reg_owner(RegWs w, uint32_t n)
             bbase = r.base;
         }
     };
+    // Whether insert q (range r) comes before this insert in (start, rank)
+    // order; a range that contains nothing never does.
     auto before = [&](const Range &r, uint32_t q) -> uint32_t {
         return r.base < b || (r.base == b && q < ri);
     };
+    const bool walk = w.rcnt[1] != 0;                    // any long insert (uniform)
+    if (!walk && k0 != 0) return;                        // wave 0's buckets alone decide
+    if (threadIdx.x == 0) s_jend = 0;
+    const uint64_t bal = walk ? tiles_part1(s_tl, w.xi.tlong) : 0;
     if (k0 == 0 && (look || ins)) {
         const uint64_t lo = w.rinfo[0], hi = w.rinfo[1];
         const uint32_t sh = idx_shift(lo, hi, w.nbk);
@@ -717,47 +805,60 @@ __global__ __launch_bounds__(kThreads) void k_reg_owner(RegWs w, uint32_t n)
             idx_bucket(w.xi, cb, [&](const Range &r, uint32_t q) { brank += before(r, q); });
         }
     }
-    const uint32_t nl = w.rcnt[1];                       // long inserts
-    if (nl != 0) {                                       // uniform over the block
-        Range nx;
-        uint32_t nk;
-        long_entry(w.xi.lng, w.ibase, w.itop, threadIdx.x, nl, nx, nk);
-        for (uint32_t j0 = 0; j0 < nl; j0 += kThreads) {
+    bool walked = false;                                 // uniform over the block
+    if (walk) {                                          // the long inserts, in rank order
+        __syncthreads();
+        const uint32_t ntl = tiles_part2(s_tl, bal);
+        // Inserts the block needs: all of them if it holds one, else those
+        // before its last looking item.
+        if (k0 == 0 && (look || ins)) atomicMax(&s_jend, ins ? (uint32_t)w.scal[0] : ri);
+        __syncthreads();
+        const uint32_t jend = s_jend;
+        const uint32_t nt = tiles_before(s_tl, ntl, jend);   // tiles to walk
+        Range nx = nt ? long_range(w.xi, w.ibase, w.itop, s_tl.list[0] * kThreads + threadIdx.x, jend)
+                      : kNoRange;
+        for (uint32_t u = 0; u < nt; ++u) {
+            const uint32_t j0 = s_tl.list[u] * kThreads;     // a tile holding a long insert
+            walked = true;
             s_r[threadIdx.x] = nx;
-            s_k[threadIdx.x] = nk;
-            long_entry(w.xi.lng, w.ibase, w.itop, j0 + kThreads + threadIdx.x, nl, nx, nk);
+            if (u + 1 < nt)                              // the next tile, loaded while this one is used
+                nx = long_range(w.xi, w.ibase, w.itop, s_tl.list[u + 1] * kThreads + threadIdx.x, jend);
             __syncthreads();
-            const uint32_t lim = nl - j0 < kThreads ? nl - j0 : kThreads;
-            const uint32_t ke = lim < k0 + kWave ? lim : k0 + kWave;
-            if (look || ins) {
+            const uint32_t lim = jend - j0 < kThreads ? jend - j0 : kThreads;
+            if (look) {
+                const uint32_t jl = ri > j0 ? (ri - j0 < lim ? ri - j0 : lim) : 0;   // rank < ri
+                const uint32_t ke = jl < k0 + kWave ? jl : k0 + kWave;
                 uint32_t k = k0;
                 for (; k + kPairStep <= ke; k += kPairStep) {
                     Range r[kPairStep];
-                    uint32_t q[kPairStep];
-#pragma unroll
-                    for (uint32_t u = 0; u < kPairStep; ++u) {
-                        r[u] = s_r[k + u];
-                        q[u] = s_k[k + u];
-                    }
-#pragma unroll
-                    for (uint32_t u = 0; u < kPairStep; ++u) {
-                        if (look) consider(r[u], q[u]);
-                        else brank += before(r[u], q[u]);
-                    }
+    #pragma unroll
+                    for (uint32_t u = 0; u < kPairStep; ++u) r[u] = s_r[k + u];
+    #pragma unroll
+                    for (uint32_t u = 0; u < kPairStep; ++u) consider(r[u], j0 + k + u);
                 }
-                for (; k < ke; ++k) {
-                    if (look) consider(s_r[k], s_k[k]);
-                    else brank += before(s_r[k], s_k[k]);
+                for (; k < ke; ++k) consider(s_r[k], j0 + k);
+            } else if (ins) {
+                const uint32_t ke = lim < k0 + kWave ? lim : k0 + kWave;
+                uint32_t k = k0;
+                for (; k + kPairStep <= ke; k += kPairStep) {
+                    uint64_t rb[kPairStep];
+    #pragma unroll
+                    for (uint32_t u = 0; u < kPairStep; ++u) rb[u] = s_r[k + u].base;
+    #pragma unroll
+                    for (uint32_t u = 0; u < kPairStep; ++u) brank += before(Range{rb[u], 0}, j0 + k + u);
                 }
+                for (; k < ke; ++k) brank += before(s_r[k], j0 + k);
             }
             __syncthreads();
         }
-        s_bb[threadIdx.x] = bbase;
-        s_bj[threadIdx.x] = look ? best : brank;
-        __syncthreads();
+        if (walked) {
+            s_bb[threadIdx.x] = bbase;
+            s_bj[threadIdx.x] = look ? best : brank;
+            __syncthreads();
+        }
     }
     if (k0 != 0 || !(look || ins)) return;
-    if (nl != 0) {
+    if (walked) {
         for (uint32_t v = kWave; v < kThreads; v += kWave) {
             const uint32_t oj = s_bj[v + ln];
             const uint64_t ob = s_bb[v + ln];
@@ -799,9 +900,9 @@ __global__ __launch_bounds__(kThreads) void k_reg_apply(RegState g, RegWs w, uin
         h = next + w.rank[i];
         w.newbase[w.brank[i]] = w.base[i];
     } else if (c == kHitNew) {
-        const uint32_t o = w.owner[i];                   // rank of the insert
+        const uint32_t o = w.owner[i];                   // rank of the insert (< n)
         h = next + o;
-        atomicAdd(&w.newrefs[o], 1u);
+        if (o < n) atomicAdd(&w.newrefs[o], 1u);
     }
     handle[i] = h;
     kind[i] = c;
@@ -1047,11 +1148,14 @@ RegWs carve(void *ws, uint64_t n, uint64_t cap, size_t *bytes = nullptr)
         x->cnt = c.take<uint32_t>(w.nbk);
         x->rec = c.take<Range>((uint64_t)w.nbk * kSlots);
         x->key = c.take<uint32_t>((uint64_t)w.nbk * kSlots);
-        x->lng = c.take<uint32_t>(n);
+        x->lflag = c.take<uint8_t>(n);
+        x->tlong = c.take<uint32_t>(kRankTiles);
     }
     w.xm.pre = nullptr;
     w.xi.pre = c.take<uint32_t>(w.nbk);
     w.rinfo = c.take<uint64_t>(2);
+    w.bmin = c.take<uint64_t>(kRankTiles);
+    w.bmax = c.take<uint64_t>(kRankTiles);
     w.rcnt = c.take<uint32_t>(2);
     w.sstart = c.take<uint64_t>(cap);
     w.pm = c.take<uint64_t>(cap);
@@ -1098,8 +1202,9 @@ hipError_t launch_reg_register(const RegArgs &a, hipStream_t s)
                                  nullptr, s);
     }
     if (nb) {
-        hipLaunchKernelGGL(k_ridx_clear, dim3((w.nbk + kThreads - 1) / kThreads), dim3(kThreads),
-                           0, s, w);
+        const uint32_t cl = w.nbk > kRankTiles ? w.nbk : kRankTiles;
+        hipLaunchKernelGGL(k_ridx_clear, dim3((cl + kThreads - 1) / kThreads), dim3(kThreads), 0,
+                           s, w);
         hipLaunchKernelGGL(k_reg_classify, dim3(nb), dim3(kThreads), 0, s, g, w, a.page_shift,
                            a.addr, a.size, n);
         hipLaunchKernelGGL(k_rank_chunks<kMiss>, dim3(cb), dim3(kThreads), 0, s, w, n);

@@ -287,17 +287,20 @@ def test_registry_workspace_holds_every_piece(n, cap):
     # items (u32), 16,384 chunk totals and four scalars; and two range
     # indexes over the batch (misses, inserts), each with nbk buckets (a power
     # of two near n / 4, 64..16,384) of a u32 count and 8 inline ranges
-    # (16 bytes) with their u32 ranks, and a u32 long list per item, plus the
-    # inserts' bucket prefixes (u32 per bucket), the bounds (two u64) and the
-    # two long-list lengths. A workspace of dmadesc_workspace_bytes must hold
-    # all of them.
+    # (16 bytes) with their u32 ranks, a u8 long flag per item and a u32
+    # long count per 256-item tile of the largest batch, plus the inserts'
+    # bucket prefixes (u32 per bucket), the bounds (two u64), each
+    # classification block's smallest and largest start (u64, 256 blocks at
+    # most) and the two long counts. A workspace of dmadesc_workspace_bytes
+    # must hold all of them.
     nbk = 64
     while nbk < n // 4 and nbk < 16384:
         nbk *= 2
-    index = 2 * (_a256(4 * nbk) + _a256(16 * 8 * nbk) + _a256(4 * 8 * nbk) + _a256(4 * n))
+    index = 2 * (_a256(4 * nbk) + _a256(16 * 8 * nbk) + _a256(4 * 8 * nbk) + _a256(n)
+                 + _a256(4 * 256))
     need = (8 * _a256(8 * n) + _a256(n) + 6 * _a256(4 * n) + 5 * _a256(8 * cap)
             + 2 * _a256(4 * cap) + _a256(4 * (cap + n)) + _a256(8 * 16384) + _a256(32)
-            + index + _a256(4 * nbk) + _a256(16) + _a256(8))
+            + index + _a256(4 * nbk) + _a256(16) + 2 * _a256(8 * 256) + _a256(8))
     assert dd.workspace_bytes(dd.OP_REGISTRY, n, cap) >= need, (n, cap)
 
 
