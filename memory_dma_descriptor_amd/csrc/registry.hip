@@ -879,33 +879,70 @@ __global__ __launch_bounds__(kThreads) void k_reg_owner(RegWs w, uint32_t n)
     }
 }
 
+// Atomic update (add, subtract or minimum) of word base[idx] by v for every
+// lane with `on`, made once per wave, with the wave's total (or minimum), when
+// all such lanes of the wave name the same word: a record that every call
+// of a batch names would otherwise take one atomic per call, all on one
+// word, one after another. Every lane of the wave must call it.
+enum class Upd { kAdd, kSub, kMin };
+template <Upd kOp>
+__device__ __forceinline__ void wave_update(uint32_t *base, uint32_t idx, bool on, uint32_t v)
+{
+    const uint64_t act = __ballot(on);
+    if (act == 0) return;
+    const int first = __ffsll((unsigned long long)act) - 1;
+    const uint32_t i0 = __shfl(idx, first, kWave);
+    if (__ballot(on && idx != i0) == 0) {
+        uint32_t x = on ? v : (kOp == Upd::kMin ? UINT32_MAX : 0u);
+#pragma unroll
+        for (int d = kWave / 2; d > 0; d >>= 1) {
+            const uint32_t y = __shfl_xor(x, d, kWave);
+            x = kOp == Upd::kMin ? (y < x ? y : x) : x + y;
+        }
+        if (lane() == first) {
+            if (kOp == Upd::kAdd) atomicAdd(base + i0, x);
+            else if (kOp == Upd::kSub) atomicSub(base + i0, x);
+            else atomicMin(base + i0, x);
+        }
+    } else if (on) {
+        if (kOp == Upd::kAdd) atomicAdd(base + idx, v);
+        else if (kOp == Upd::kSub) atomicSub(base + idx, v);
+        else atomicMin(base + idx, v);
+    }
+}
+
 // Handles, kinds and reference counts (or NOSPACE for every item).
 __global__ __launch_bounds__(kThreads) void k_reg_apply(RegState g, RegWs w, uint32_t n,
                                                         uint64_t *handle, uint8_t *kind)
 {
     const uint32_t i = blockIdx.x * kThreads + threadIdx.x;
-    if (i >= n) return;
-    const uint8_t c = w.cls[i];
-    if (!w.scal[1]) {
-        handle[i] = 0;
-        kind[i] = kNospace;
+    const bool valid = i < n;
+    const uint8_t c = valid ? w.cls[i] : kInvalid;
+    if (!w.scal[1]) {                                    // uniform: the batch did not fit
+        if (valid) {
+            handle[i] = 0;
+            kind[i] = kNospace;
+        }
         return;
     }
     const uint64_t next = g.state[1];
     uint64_t h = 0;
+    const uint32_t hs = c == kHit ? w.hit[i] : 0u;       // storage slot of the hit record
+    const uint32_t o = c == kHitNew ? w.owner[i] : 0u;   // rank of the containing insert (< n)
     if (c == kHit) {
-        h = g.id[w.hit[i]];
-        atomicAdd(&g.refs[w.hit[i]], 1u);
+        h = g.id[hs];
     } else if (c == kNew) {
         h = next + w.rank[i];
         w.newbase[w.brank[i]] = w.base[i];
     } else if (c == kHitNew) {
-        const uint32_t o = w.owner[i];                   // rank of the insert (< n)
         h = next + o;
-        if (o < n) atomicAdd(&w.newrefs[o], 1u);
     }
-    handle[i] = h;
-    kind[i] = c;
+    wave_update<Upd::kAdd>(g.refs, hs, c == kHit, 1u);
+    wave_update<Upd::kAdd>(w.newrefs, o, c == kHitNew && o < n, 1u);
+    if (valid) {
+        handle[i] = h;
+        kind[i] = c;
+    }
 }
 
 // New records in storage after the live ones, and the merged start order.
@@ -985,9 +1022,8 @@ __global__ __launch_bounds__(kThreads) void k_dereg_find(RegState g, RegWs w, co
 __global__ __launch_bounds__(kThreads) void k_dereg_first(RegWs w, uint32_t n)
 {
     const uint32_t i = blockIdx.x * kThreads + threadIdx.x;
-    if (i >= n) return;
-    const uint32_t me = w.hit[i];
-    if (me != UINT32_MAX) atomicMin(&w.tmp32[me], i);
+    const uint32_t me = i < n ? w.hit[i] : UINT32_MAX;
+    wave_update<Upd::kMin>(w.tmp32, me, me != UINT32_MAX, i);
 }
 
 // Calls before i naming the same record decide whether call i succeeds. No
@@ -1056,7 +1092,8 @@ __global__ __launch_bounds__(kThreads) void k_dereg_status(RegState g, RegWs w, 
 __global__ __launch_bounds__(kThreads) void k_dereg_drop(RegState g, RegWs w, uint32_t n)
 {
     const uint32_t i = blockIdx.x * kThreads + threadIdx.x;
-    if (i < n && w.cls[i] != DMADESC_DEREG_STALE) atomicSub(&g.refs[w.hit[i]], 1u);
+    const bool on = i < n && w.cls[i] != DMADESC_DEREG_STALE;
+    wave_update<Upd::kSub>(g.refs, on ? w.hit[i] : 0u, on, 1u);
 }
 
 // Stable compaction: kept storage slots move to their exclusive prefix, and

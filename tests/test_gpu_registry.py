@@ -210,6 +210,23 @@ def test_crowded_buckets_long_ranges_and_a_wide_span():
     p.register(starts, sizes, "wide span")
 
 
+def test_whole_batches_on_one_record():
+    # Every call of a full batch names one record: hits on one old record,
+    # repeats of one new range, then deregistrations of one handle (its
+    # references drop one by one, the rest are stale). The reference updates
+    # of such a batch all land on one word.
+    p = Pair(capacity=64)
+    p.register(np.array([1 << 40], np.uint64), np.array([1 << 30], np.uint64), "one region")
+    n = dd.REG_MAX_BATCH
+    h, _ = p.register(np.full(n, (1 << 40) + 4096, np.uint64), np.full(n, M, np.uint64),
+                      "hits on one record")
+    h2, k2 = p.register(np.full(n - 1, 1 << 44, np.uint64), np.full(n - 1, M, np.uint64),
+                        "repeats of one new range")
+    assert (k2 == oracle.REG_NEW).sum() == 1
+    p.deregister(np.full(n, h2[0], np.uint64), "one handle, every call")
+    p.deregister(np.full(n, h[0], np.uint64), "the old record, every call")
+
+
 def test_empty_batches_and_empty_table():
     p = Pair()
     p.register(np.zeros(0, np.uint64), np.zeros(0, np.uint64), "empty register")
