@@ -288,9 +288,10 @@ __device__ __forceinline__ uint32_t idx_shift(uint64_t lo, uint64_t hi, uint32_t
     return bl > lb ? bl - lb : 0u;
 }
 
-// Files range [b, t) (b in [lo, hi]) of rank r into index X; true if it is
-// long (the caller counts those per tile and in all, a few atomics per wave:
-// one word that every long range of the launch added to would serialize).
+// Files range [b, t) (b in [lo, hi]) of rank r into index X, or flags it
+// long; returns whether it is long. The caller counts long ranges per
+// 256-rank tile and in all with a few atomics per wave (an atomic per long
+// range on one shared word would serialize).
 __device__ __forceinline__ bool idx_put(const RIdx &X, uint64_t lo, uint32_t shift, uint64_t b,
                                         uint64_t t, uint32_t r)
 {
@@ -308,8 +309,9 @@ __device__ __forceinline__ bool idx_put(const RIdx &X, uint64_t lo, uint32_t shi
     return true;
 }
 
-// Buckets [c0, c1] of index X that can hold a range of length <= 2^shift
-// containing a range starting at b; c0 > c1 when there are none.
+// Buckets [c0, c1] (of either index: both share lo, hi and shift) that can
+// hold a range of length <= 2^shift containing a range starting at b;
+// c0 > c1 when there are none.
 __device__ __forceinline__ void idx_window(uint64_t lo, uint64_t hi, uint32_t shift, uint64_t b,
                                           uint32_t &c0, uint32_t &c1)
 {
