@@ -57,8 +57,6 @@
 namespace dd {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kWaves = kThreads / kWave;
 // Requests per thread: 4 (1,024 per block) for large batches; 1 (256 per
 // block) for batches of at most kSmallBatch requests, whose blocks would
 // otherwise be too few to fill the chip (a 262,144-request batch of long
@@ -120,7 +118,7 @@ constexpr int kHistCopies = 4;                    // lane l counts into copy l %
 constexpr int kHistStride = DMADESC_MAX_QUEUES + 1;
 
 // Looks up kN requests of this thread (items k0 .. k0 + kN - 1, item k being
-// request base + k * kThreads + t) and writes the five lookup columns. Every
+// request base + k * (threads per block) + t) and writes the five lookup columns. Every
 // load of one stage is issued for all kN items before any is used.
 // Looks one request up (item k of this thread: request i) and writes the
 // five lookup columns. Only a range at or past the first region's start can
@@ -180,7 +178,7 @@ __device__ __forceinline__ void fused_lookup(const Fuse &F, const IndexHdr &H, u
 
 // The lookups of this thread's kItems requests, one after another (one
 // record and its answer live at a time).
-template <int kItems>
+template <int kItems, int kT>
 __device__ __forceinline__ void fused_lookups(const Fuse &F, const uint64_t (&o)[kItems],
                                               const uint64_t (&l)[kItems], uint64_t base, int t,
                                               uint64_t n)
@@ -188,7 +186,7 @@ __device__ __forceinline__ void fused_lookups(const Fuse &F, const uint64_t (&o)
     const IndexHdr H = *F.ihdr;
 #pragma unroll
     for (int k = 0; k < kItems; ++k)
-        fused_lookup(F, H, o[k], l[k], base + (uint64_t)k * kThreads + t, n);
+        fused_lookup(F, H, o[k], l[k], base + (uint64_t)k * kT + t, n);
 }
 
 // First region whose start is at or past bucket b (b may be nbuckets).
@@ -867,8 +865,8 @@ __device__ __forceinline__ void emit_round_packed(PackLds &L, uint64_t d, uint64
                                 lut, pool, bus);
 }
 
-template <bool kPacked, bool kFused, int kItems>
-__global__ __launch_bounds__(kThreads, 4) void k_prp_build(
+template <bool kPacked, bool kFused, int kItems, int kT>
+__global__ __launch_bounds__(kT, 4) void k_prp_build(
     const uint64_t *__restrict__ lut, uint64_t heap,
     const uint64_t *__restrict__ off, const uint64_t *__restrict__ len, uint64_t n,
     uint64_t nblocks, uint64_t bus, uint64_t *__restrict__ pool, uint64_t pool_pages,
@@ -876,27 +874,28 @@ __global__ __launch_bounds__(kThreads, 4) void k_prp_build(
     uint8_t *__restrict__ status, uint64_t *__restrict__ total,
     Header *__restrict__ hdr, uint64_t *__restrict__ bstat, uint32_t max_polls, Fuse F)
 {
+    constexpr int kWv = kT / kWave;                  // waves per block
     using RoundT = typename std::conditional<kPacked, PackLds, RoundLds>::type;
-    __shared__ uint64_t s_red[kItems * kWaves];
+    __shared__ uint64_t s_red[kItems * kWv];
     __shared__ uint64_t s_bid, s_excl;
     __shared__ uint32_t s_dead;
-    __shared__ uint64_t s_v2[kItems * kThreads];   // table entry of PRP2's page (two pages)
-    __shared__ RoundT s_round[kWaves];
+    __shared__ uint64_t s_v2[kItems * kT];   // table entry of PRP2's page (two pages)
+    __shared__ RoundT s_round[kWv];
     // The fused split's block histogram lives in the round tables' memory,
     // which the list rounds only use after the request phase.
-    static_assert(sizeof(RoundT) * kWaves >= kHistCopies * kHistStride * sizeof(uint32_t),
+    static_assert(sizeof(RoundT) * kWv >= kHistCopies * kHistStride * sizeof(uint32_t),
                   "the histogram fits in the round tables");
     uint32_t *hist = reinterpret_cast<uint32_t *>(&s_round[0]);
 
     const int t = threadIdx.x, w = wave(), ln = lane();
     const bool split_hist = kFused && F.counts != nullptr;
     if (split_hist) {
-        for (int k = t; k < kHistCopies * kHistStride; k += kThreads) hist[k] = 0;
+        for (int k = t; k < kHistCopies * kHistStride; k += kT) hist[k] = 0;
     }
     if (t == 0) s_bid = atomicAdd(&hdr->ticket, 1u);
     __syncthreads();
     const uint64_t b = s_bid;
-    constexpr int kTile = kThreads * kItems;       // requests per block
+    constexpr int kTile = kT * kItems;       // requests per block
     const uint64_t base = b * kTile;
 
     // ---- request phase: item k of thread t is request base + k*256 + t ----
@@ -911,7 +910,7 @@ __global__ __launch_bounds__(kThreads, 4) void k_prp_build(
     uint32_t q[kItems];
 #pragma unroll
     for (int k = 0; k < kItems; ++k) {
-        const uint64_t i = base + (uint64_t)k * kThreads + t;
+        const uint64_t i = base + (uint64_t)k * kT + t;
         o[k] = i < n ? __builtin_nontemporal_load(off + i) : 0;
         l[k] = i < n ? __builtin_nontemporal_load(len + i) : 0;   // len 0 decodes as invalid
         // Clamped, not guarded, and loaded even when the split counts its
@@ -925,7 +924,7 @@ __global__ __launch_bounds__(kThreads, 4) void k_prp_build(
         uint32_t *hc = hist + (ln % kHistCopies) * kHistStride;
 #pragma unroll
         for (int k = 0; k < kItems; ++k) {
-            const uint64_t i = base + (uint64_t)k * kThreads + t;
+            const uint64_t i = base + (uint64_t)k * kT + t;
             if (i < n) atomicAdd(&hc[q[k] < F.nq ? q[k] : F.nq], 1u);
         }
     }
@@ -942,7 +941,7 @@ __global__ __launch_bounds__(kThreads, 4) void k_prp_build(
                                  ? (kPacked ? pages - 1 : (pages - 2 + 510) / 511) : 0;
         const uint64_t inc = wave_incl_scan(cnt);
         pre[k] = inc - cnt;
-        if (ln == kWave - 1) s_red[k * kWaves + w] = inc;
+        if (ln == kWave - 1) s_red[k * kWv + w] = inc;
     }
     __syncthreads();
     uint64_t agg = 0;
@@ -950,8 +949,8 @@ __global__ __launch_bounds__(kThreads, 4) void k_prp_build(
     for (int k = 0; k < kItems; ++k) {
         uint64_t before = 0, all = 0;
 #pragma unroll
-        for (int v = 0; v < kWaves; ++v) {
-            const uint64_t x = s_red[k * kWaves + v];
+        for (int v = 0; v < kWv; ++v) {
+            const uint64_t x = s_red[k * kWv + v];
             before += v < w ? x : 0ull;
             all += x;
         }
@@ -983,7 +982,7 @@ __global__ __launch_bounds__(kThreads, 4) void k_prp_build(
             const uint64_t i1 = (st == kOk && !staged_prp1) ? o[k] >> 16 : 0;
             const uint64_t i2 = (st == kOk && pages == 2) ? x >> 16 : 0;
             v1[k] = heap ? lut[i1] : 0;
-            s_v2[k * kThreads + t] = heap ? lut[i2] : 0;
+            s_v2[k * kT + t] = heap ? lut[i2] : 0;
         }
     };
     if (w != 0) {
@@ -992,13 +991,13 @@ __global__ __launch_bounds__(kThreads, 4) void k_prp_build(
             // Waves 1..3 add the block histogram to its split tile's counts
             // while wave 0 looks back, then look their requests up.
             const uint64_t tile = base >> F.tile_shift;
-            for (uint32_t bk = t - kWave; split_hist && bk <= F.nq; bk += kThreads - kWave) {
+            for (uint32_t bk = t - kWave; split_hist && bk <= F.nq; bk += kT - kWave) {
                 uint32_t c = 0;
 #pragma unroll
                 for (int j = 0; j < kHistCopies; ++j) c += hist[j * kHistStride + bk];
                 if (c) atomicAdd(F.counts + (uint64_t)bk * F.ntiles + tile, c);
             }
-            if (F.handle) fused_lookups(F, o, l, base, t, n);
+            if (F.handle) fused_lookups<kItems, kT>(F, o, l, base, t, n);
         }
     }
     if (w == 0) {
@@ -1018,7 +1017,7 @@ __global__ __launch_bounds__(kThreads, 4) void k_prp_build(
         }
         gather();
         if constexpr (kFused) {
-            if (F.handle) fused_lookups(F, o, l, base, t, n);
+            if (F.handle) fused_lookups<kItems, kT>(F, o, l, base, t, n);
         }
     }
     __syncthreads();
@@ -1029,7 +1028,7 @@ __global__ __launch_bounds__(kThreads, 4) void k_prp_build(
     const uint64_t cap = kPacked ? pool_pages * 511 : pool_pages;   // slots of the pool
 #pragma unroll 1
     for (int k = 0; k < kItems; ++k) {
-        const uint64_t i = base + (uint64_t)k * kThreads + t;
+        const uint64_t i = base + (uint64_t)k * kT + t;
         uint64_t pages;
         uint8_t st = decode(o[k], l[k], heap, pages);
         const uint64_t cnt = (st == kOk && pages >= 3)
@@ -1049,7 +1048,7 @@ __global__ __launch_bounds__(kThreads, 4) void k_prp_build(
                        lists ? cnt : 0, last_frame, o[k], p1, lut, pool, bus);
         if (i < n) {
             const uint64_t list = kPacked ? bus + 8 * (slot + slot / 511) : bus + (slot << 12);
-            const uint64_t p2 = lists ? list : (pages == 2 ? s_v2[k * kThreads + t] + (xb & 0xFFFFu) : 0);
+            const uint64_t p2 = lists ? list : (pages == 2 ? s_v2[k * kT + t] + (xb & 0xFFFFu) : 0);
             // Output columns and input columns are streamed (non-temporal):
             // neither is read again by this kernel.
             __builtin_nontemporal_store(st == kOk ? p1 : 0, prp1 + i);
@@ -1065,9 +1064,25 @@ __global__ __launch_bounds__(kThreads, 4) void k_prp_build(
 // power of two), at least 4,096 and at most 2^21 (96 MiB of records).
 // Requests per block of the PRP build for a batch of n (the launch and the
 // workspace size agree on it).
+// Block shape of the build for a batch of n (threads per block, requests per
+// thread): one request per thread for small batches, four otherwise, in
+// 512-thread blocks for mid-size batches (half as many blocks take tickets
+// from the one ticket word than with 256 threads, which the launch's first
+// round of blocks otherwise takes one after another: 1,048,576 requests
+// 36 -> 30 us) and 256-thread blocks above (a 512-thread block's scan
+// spills a few registers, which large batches pay in every block).
+constexpr uint64_t kMidBatch = 1ull << 22;
+void prp_shape(uint64_t n, int &threads, int &items)
+{
+    threads = n > kSmallBatch && n <= kMidBatch ? 512 : 256;
+    items = n <= kSmallBatch ? kItemsSmall : kItemsLarge;
+}
+
 uint64_t prp_tile(uint64_t n)
 {
-    return (uint64_t)kThreads * (n <= kSmallBatch ? kItemsSmall : kItemsLarge);
+    int threads = 0, items = 0;
+    prp_shape(n, threads, items);
+    return (uint64_t)threads * (uint64_t)items;
 }
 
 // Launches the k_prp_build instantiation for the layout and the batch size.
@@ -1076,18 +1091,21 @@ void launch_prp_kernel(const PrpArgs &a, uint64_t nb, Header *hdr, uint64_t *bst
                        const Fuse &F, hipStream_t s)
 {
     const uint64_t heap = a.lut_entries << 16;
-    const bool small = a.n <= kSmallBatch;
-#define DD_PRP_LAUNCH(P, I)                                                                   \
-    hipLaunchKernelGGL((k_prp_build<P, kFused, I>), dim3((unsigned)nb), dim3(kThreads), 0, s,  \
+    int threads = 0, items = 0;
+    prp_shape(a.n, threads, items);
+#define DD_PRP_LAUNCH(P, I, T)                                                                \
+    hipLaunchKernelGGL((k_prp_build<P, kFused, I, T>), dim3((unsigned)nb), dim3(T), 0, s,      \
                        a.lut, heap, a.off, a.len, a.n, nb, a.list_bus_base, a.pool,            \
                        a.pool_pages, a.prp1, a.prp2, a.status, a.total_pages, hdr, bstat,     \
                        wait_limit(), F)
     if (a.packed) {
-        if (small) DD_PRP_LAUNCH(true, kItemsSmall);
-        else DD_PRP_LAUNCH(true, kItemsLarge);
+        if (items == kItemsSmall) DD_PRP_LAUNCH(true, kItemsSmall, 256);
+        else if (threads == 512) DD_PRP_LAUNCH(true, kItemsLarge, 512);
+        else DD_PRP_LAUNCH(true, kItemsLarge, 256);
     } else {
-        if (small) DD_PRP_LAUNCH(false, kItemsSmall);
-        else DD_PRP_LAUNCH(false, kItemsLarge);
+        if (items == kItemsSmall) DD_PRP_LAUNCH(false, kItemsSmall, 256);
+        else if (threads == 512) DD_PRP_LAUNCH(false, kItemsLarge, 512);
+        else DD_PRP_LAUNCH(false, kItemsLarge, 256);
     }
 #undef DD_PRP_LAUNCH
 }
