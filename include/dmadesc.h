@@ -234,8 +234,9 @@ int dmadesc_mr_table_check(const uint64_t *reg_start, const uint64_t *reg_end,
  * Per request, with pages p = ((off & 4095) + len + 4095) >> 12, entries
  * m = p - 1 and, for p >= 3, list pages L = ceil((m - 1) / 511).
  * Slot scan: list pages are handed out by a one-pass device-wide scan over
- * blocks of 1,024 requests (256 for batches of at most 2^19 requests, 2,048
- * for batches of more than 2^19 and at most 2^22) whose waits are bounded. A block whose wait
+ * blocks of 1,024 requests (256 for batches of at most 2^16 requests, 512
+ * for more than 2^16 and at most 2^19, 2,048 for more than 2^19 and at most
+ * 2^22) whose waits are bounded. A block whose wait
  * expires (never at the default bound while blocks make progress) refuses
  * its list requests with DMADESC_PRP_EBUSY (prp1 = prp2 = 0, no list
  * entries); every other request is built exactly as above, and if the

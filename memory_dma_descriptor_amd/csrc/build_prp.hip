@@ -1065,16 +1065,17 @@ __global__ __launch_bounds__(kT, 4) void k_prp_build(
 // Requests per block of the PRP build for a batch of n (the launch and the
 // workspace size agree on it).
 // Block shape of the build for a batch of n (threads per block, requests per
-// thread): one request per thread for small batches, four otherwise, in
-// 512-thread blocks for mid-size batches (half as many blocks take tickets
-// from the one ticket word than with 256 threads, which the launch's first
-// round of blocks otherwise takes one after another: 1,048,576 requests
-// 36 -> 30 us) and 256-thread blocks above (a 512-thread block's scan
-// spills a few registers, which large batches pay in every block).
+// thread): one request per thread up to 2^19 requests, four above; 512-thread
+// blocks from 2^16 to 2^22 requests (half as many blocks take tickets from
+// the one ticket word than with 256 threads, which the launch's first round
+// of blocks otherwise takes one after another: 1,048,576 requests 36 -> 30
+// us, 262,144 large ones 0.487 -> 0.482 ms), 256-thread blocks outside that
+// (a 512-thread block's scan spills a few registers, which large batches pay
+// in every block; tiny ones want more blocks).
 constexpr uint64_t kMidBatch = 1ull << 22;
 void prp_shape(uint64_t n, int &threads, int &items)
 {
-    threads = n > kSmallBatch && n <= kMidBatch ? 512 : 256;
+    threads = n > (1ull << 16) && n <= kMidBatch ? 512 : 256;
     items = n <= kSmallBatch ? kItemsSmall : kItemsLarge;
 }
 
@@ -1099,11 +1100,13 @@ void launch_prp_kernel(const PrpArgs &a, uint64_t nb, Header *hdr, uint64_t *bst
                        a.pool_pages, a.prp1, a.prp2, a.status, a.total_pages, hdr, bstat,     \
                        wait_limit(), F)
     if (a.packed) {
-        if (items == kItemsSmall) DD_PRP_LAUNCH(true, kItemsSmall, 256);
+        if (items == kItemsSmall && threads == 512) DD_PRP_LAUNCH(true, kItemsSmall, 512);
+        else if (items == kItemsSmall) DD_PRP_LAUNCH(true, kItemsSmall, 256);
         else if (threads == 512) DD_PRP_LAUNCH(true, kItemsLarge, 512);
         else DD_PRP_LAUNCH(true, kItemsLarge, 256);
     } else {
-        if (items == kItemsSmall) DD_PRP_LAUNCH(false, kItemsSmall, 256);
+        if (items == kItemsSmall && threads == 512) DD_PRP_LAUNCH(false, kItemsSmall, 512);
+        else if (items == kItemsSmall) DD_PRP_LAUNCH(false, kItemsSmall, 256);
         else if (threads == 512) DD_PRP_LAUNCH(false, kItemsLarge, 512);
         else DD_PRP_LAUNCH(false, kItemsLarge, 256);
     }

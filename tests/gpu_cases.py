@@ -18,9 +18,11 @@ PAD_WORDS = 8
 
 def prp_tile(n):
     """Requests per block of the PRP build's slot scan: 256 for batches of at
-    most 2^19 requests, 2,048 up to 2^22, 1,024 above (the library's choice,
-    stated in dmadesc_build_prp's header comment)."""
-    return 256 if n <= (1 << 19) else 2048 if n <= (1 << 22) else 1024
+    most 2^16 requests, 512 up to 2^19, 2,048 up to 2^22, 1,024 above (the
+    library's choice, stated in dmadesc_build_prp's header comment)."""
+    if n <= (1 << 16):
+        return 256
+    return 512 if n <= (1 << 19) else 2048 if n <= (1 << 22) else 1024
 
 
 def padding_spans(prp2, status, off, ln, bus, slot_base=0):
