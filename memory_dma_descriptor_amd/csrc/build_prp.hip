@@ -10,10 +10,10 @@
 //
 // One pass, one kernel (after a small workspace-clearing kernel):
 //
-//  * Request phase, 1024 requests per block (256 for batches of at most
-//    2^19 requests, so that they still make enough blocks), item k of thread
-//    t being request block_base + 256 k + t (so every column load is
-//    contiguous per wave):
+//  * Request phase, T threads per block and one or four requests per thread
+//    (prp_shape below: 256-1,024 requests per block by batch size), item k
+//    of thread t being request block_base + T k + t (so every column load
+//    is contiguous per wave):
 //    validity, 4 KiB page count, list pages L. List pages are handed out in
 //    request order by a device-wide exclusive scan done in the same pass
 //    with decoupled look-back: each block publishes its aggregate, then
@@ -57,10 +57,10 @@
 namespace dd {
 namespace {
 
-// Requests per thread: 4 (1,024 per block) for large batches; 1 (256 per
-// block) for batches of at most kSmallBatch requests, whose blocks would
-// otherwise be too few to fill the chip (a 262,144-request batch of long
-// lists makes 256 blocks of 1,024: one block, four waves, per CU).
+// Requests per thread: 4 for large batches; 1 for batches of at most
+// kSmallBatch requests, whose blocks would otherwise be too few to fill the
+// chip (a 262,144-request batch of long lists makes 256 blocks of 1,024:
+// one block, four waves, per CU).
 constexpr int kItemsLarge = 4;
 constexpr int kItemsSmall = 1;
 constexpr uint64_t kSmallBatch = 1ull << 19;
@@ -969,8 +969,8 @@ __global__ __launch_bounds__(kT, 4) void k_prp_build(
     // after (its look-back polls would otherwise wait for its table reads).
     // A list (either layout) takes PRP1 from the table entries its round
     // stages, so its table read is not repeated here. The second page's table entry of
-    // a two-page request waits in LDS (8 KiB per block), which keeps the
-    // packed build within 128 VGPRs, four blocks per CU.
+    // a two-page request waits in LDS (8 bytes per request), which keeps the
+    // packed build within 128 VGPRs, four waves per SIMD.
     uint64_t v1[kItems];
     auto gather = [&]() {
 #pragma unroll
